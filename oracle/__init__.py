@@ -1,0 +1,164 @@
+"""CPU oracle for the lossless BF16 codec -- TEST INFRASTRUCTURE ONLY.
+
+A thin ctypes/numpy wrapper around ``ciera_oracle.c``: plain scalar C that
+encodes and decodes one value at a time, in element order.  It defines what
+the HIP library must produce byte for byte.  Only ``tests/``,
+``__graft_entry__.smoke()`` and the CPU-baseline leg of ``bench.py`` may
+import this package; the product library never does.
+
+Parity pins (see the tests under ``tests/``): exhaustive round trips over all
+65,536 BF16 bit patterns, the ZipCCL digest's Figure 2 binade shares and
+97.5 % window share, the optimum u = 0.0172 and x_opt = log2(sigma) - 5.36
+(ZipCCL research digest, section 3.1), the block reuse law (1-c)^B (CIERA
+page, section 2), the closed-form stream size, exact-rational variance on
+small inputs, and a second, independent pure-Python encoder.  The byte layout
+itself is a reading of the pages (they print no encoded bytes); it is pinned
+by the size identity and by that second implementation only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "ciera_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "libciera_oracle.so")
+
+OK, ERR_ARG, ERR_CAPACITY, ERR_FORMAT, ERR_NOMEM = 0, 1, 2, 5, 6
+CHUNK = 65536
+
+_lib = None
+
+
+class OracleError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"oracle {what} failed with status {status}")
+        self.status = status
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc into ``oracle/libciera_oracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp"
+        cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared",
+               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        build(force=True)
+    lib = ctypes.CDLL(_LIB_PATH)
+    u64, u32, vp, i32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
+    lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
+    lib.orc_bf16_value.restype = ctypes.c_double
+    lib.orc_variance.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(u64)]
+    lib.orc_variance.restype = None
+    lib.orc_window_base.argtypes = [ctypes.c_double, u64]
+    lib.orc_window_base.restype = i32
+    lib.orc_choose_e0.argtypes = [vp, u64]
+    lib.orc_choose_e0.restype = i32
+    lib.orc_max_encoded_size.argtypes = [u64, u32]
+    lib.orc_max_encoded_size.restype = u64
+    lib.orc_encode.argtypes = [vp, u64, u32, vp, i32, vp, u64, ctypes.POINTER(u64), vp]
+    lib.orc_encode.restype = i32
+    lib.orc_decode.argtypes = [vp, u64, vp, u64, u32, vp]
+    lib.orc_decode.restype = i32
+    _lib = lib
+    return lib
+
+
+def _u16(x) -> np.ndarray:
+    x = np.ascontiguousarray(x)
+    if x.dtype != np.uint16:
+        raise TypeError("BF16 data must be passed as a uint16 bit-pattern array")
+    return x.reshape(-1)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.c_void_p) if a.size else None
+
+
+def bf16_value(bits: int) -> float:
+    return _load().orc_bf16_value(bits)
+
+
+def variance(x) -> tuple[float, int]:
+    """(sample variance of the finite values, number of finite values)."""
+    x = _u16(x)
+    var, nf = ctypes.c_double(), ctypes.c_uint64()
+    _load().orc_variance(_ptr(x), x.size, ctypes.byref(var), ctypes.byref(nf))
+    return var.value, nf.value
+
+
+def window_base(var: float, nfinite: int) -> int:
+    return _load().orc_window_base(var, nfinite)
+
+
+def choose_e0(x) -> int:
+    x = _u16(x)
+    return _load().orc_choose_e0(_ptr(x), x.size)
+
+
+def max_encoded_size(n: int, B: int = 0) -> int:
+    return _load().orc_max_encoded_size(n, B)
+
+
+def encode(x, B: int = 0, cache: np.ndarray | None = None, e0_override: int = -1):
+    """Encode ``x`` (uint16 BF16 patterns).  ``B = 0`` is zip3 mode; otherwise
+    ciera mode with block size ``B`` and the sender cache ``cache`` (uint8,
+    len(x), updated in place).  Returns (stream bytes as uint8 array,
+    {"E0", "changed_blocks", "escapes"})."""
+    x = _u16(x)
+    n = x.size
+    if B:
+        if cache is None or cache.dtype != np.uint8 or cache.size != n or not cache.flags.c_contiguous:
+            raise ValueError("ciera mode needs a contiguous uint8 cache of len(x)")
+    cap = max_encoded_size(n, B)
+    out = np.zeros(cap, dtype=np.uint8)
+    size = ctypes.c_uint64()
+    stats = np.zeros(3, dtype=np.uint64)
+    st = _load().orc_encode(_ptr(x), n, B, _ptr(cache) if B else None, e0_override,
+                            _ptr(out), cap, ctypes.byref(size), _ptr(stats))
+    if st != OK:
+        raise OracleError(st, "encode")
+    return out[: size.value].copy(), {"E0": int(stats[0]), "changed_blocks": int(stats[1]),
+                                      "escapes": int(stats[2])}
+
+
+def decode(stream, n: int, B: int = 0, cache: np.ndarray | None = None) -> np.ndarray:
+    """Decode a stream back to n uint16 BF16 patterns (ciera mode updates
+    ``cache`` in place)."""
+    stream = np.ascontiguousarray(stream, dtype=np.uint8).reshape(-1)
+    y = np.zeros(n, dtype=np.uint16)
+    if B:
+        if cache is None or cache.dtype != np.uint8 or cache.size != n or not cache.flags.c_contiguous:
+            raise ValueError("ciera mode needs a contiguous uint8 cache of n bytes")
+    st = _load().orc_decode(_ptr(stream), stream.size, _ptr(y), n, B, _ptr(cache) if B else None)
+    if st != OK:
+        raise OracleError(st, "decode")
+    return y
+
+
+def zip3_encode(x, e0_override: int = -1):
+    return encode(x, 0, None, e0_override)
+
+
+def zip3_decode(stream, n: int) -> np.ndarray:
+    return decode(stream, n, 0, None)
+
+
+def ciera_encode(x, B: int, cache: np.ndarray, e0_override: int = -1):
+    return encode(x, B, cache, e0_override)
+
+
+def ciera_decode(stream, n: int, B: int, cache: np.ndarray) -> np.ndarray:
+    return decode(stream, n, B, cache)

@@ -1,0 +1,435 @@
+/*
+ * ciera_oracle.c -- CPU oracle for the lossless BF16 codec.
+ *
+ * TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, scalar reference
+ * that the HIP library is checked against.  Only the tests, the smoke check
+ * and the benchmark's CPU-baseline leg load it.  The HIP library never
+ * includes, links or calls anything here, and nothing here comes from the
+ * HIP sources: the two sides share no code, header, table or constant.
+ *
+ * What it computes (every step in element order, one value at a time):
+ *
+ *  - Field split.  A BF16 value is 1 sign bit, 8 exponent bits and 7 mantissa
+ *    bits.  Sign and mantissa stay together as one raw byte (sign in bit 7);
+ *    the exponent is handled on its own.  ZipCCL research digest, section 3.1
+ *    (first paragraph); CIERA page, section 3.1 (the sender splits every value
+ *    into exponent bits and sign-plus-mantissa bits).
+ *
+ *  - Window.  sigma comes from the tensor's standard deviation (sample
+ *    variance, correction 1, over the finite values).  The 7-binade window
+ *    starts at the integer nearest x_opt = log2(sigma) + 0.5*log2(14 ln2 /
+ *    16383).  ZipCCL digest, section 3.1, the P_win equation, the x_opt
+ *    equation and Figure 2.  Written as a comparison of the variance with the
+ *    thresholds K0 * 4^k, K0 = 16383 / (28 ln 2), so no logarithm is taken:
+ *    k = floor(x_opt + 1/2)  <=>  var >= K0 * 4^k.
+ *
+ *  - 3-bit code.  An exponent E in [E0, E0+6] gets code E-E0+1 (1..7); any
+ *    other exponent gets code 0 and its full 8 bits go to the escape list, in
+ *    element order.  ZipCCL digest, section 3.1 (codes 001..111, code 000 plus
+ *    the full exponent in a separate zero-point list).
+ *
+ *  - Exponent reuse (ciera mode only).  The shard is cut into blocks of B
+ *    values counted from the shard start.  A block is "changed" when any of
+ *    its exponents differs from the sender's exponent cache (the exponents
+ *    sent for the previous iteration).  Only changed blocks send exponents; a
+ *    one-bit-per-block bitmap marks them; sign+mantissa of every value is sent.
+ *    The receiver takes unchanged blocks' exponents from its own cache.  CIERA
+ *    page, section 3.1 (bitmap, sender and receiver caches) and section 3.2
+ *    (payload S_{s+m} + S_bm + q S_e).  The cache here holds the exponents
+ *    themselves, compared exactly, in place of the page's per-block hash.
+ *
+ *  - Packing.  The stream is cut into chunks of 65,536 input values; each
+ *    chunk is written as a self-contained segment whose sections start on
+ *    128-byte boundaries, and the three code bits go to three 1-bit arrays.
+ *    ZipCCL digest, section 3.1 (last paragraph: chunks padded to 128 bytes,
+ *    codes as three aligned 1-bit arrays) and Figure 1 (codec writes the
+ *    collective's chunk layout; only a size exchange is added).
+ *
+ * Byte layout (all integers little-endian, all unnamed bytes zero):
+ *
+ *   header, 128 bytes:
+ *     0  char[4] magic "ZIP3" (zip3 mode) or "CIER" (ciera mode)
+ *     4  u16 version = 1
+ *     6  u8  mode (0 zip3, 1 ciera)
+ *     7  u8  E0 (window base; codes 1..7 mean E0..E0+6)
+ *     8  u64 n (values)
+ *     16 u32 B (0 in zip3 mode)
+ *     20 u32 C = 65536 (values per chunk)
+ *     24 u64 nchunks = ceil(n / C)
+ *     32 u64 total_bytes
+ *     40 u64 n_changed_blocks (ciera; in zip3 mode 0)
+ *     48 u64 n_escapes
+ *   chunk table at byte 128: nchunks+1 u64 absolute offsets (the last one is
+ *     total_bytes), zero-padded to a 128-byte multiple.
+ *   chunk c (values [cC, min(cC+C, n)), n_c of them), each section padded to
+ *   a multiple of 128 bytes with zeros:
+ *     1. sm:     n_c bytes, sm = (sign << 7) | mantissa
+ *     2. bitmap: ciera only, ceil(nb_c / 8) bytes, nb_c = ceil(n_c / B);
+ *                bit (j & 7) of byte (j >> 3) set when block j of the chunk
+ *                is changed
+ *     3. planes: three arrays of P_c bytes; plane b holds bit b of the code
+ *                of slot t in bit (t & 7) of byte (t >> 3).  zip3: slot t is
+ *                value t of the chunk, P_c = ceil(n_c / 8).  ciera: the r-th
+ *                changed block of the chunk owns slots rB .. rB+B-1, slot
+ *                rB+s is value s of that block (0 past the end of the data),
+ *                P_c = (changed blocks of the chunk) * B / 8.
+ *     4. escapes: one byte (the raw exponent) per code-0 slot that holds a
+ *                value, in slot order.
+ *
+ * Floating point: the variance is computed in FP64 (the precision the GPU
+ * kernels use for the same statistic) with one-pass sums shifted by the
+ * first value (0 if it is not finite), summed in element order.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum {
+  ORC_OK = 0,
+  ORC_ERR_ARG = 1,
+  ORC_ERR_CAPACITY = 2,
+  ORC_ERR_FORMAT = 5,
+  ORC_ERR_NOMEM = 6
+};
+
+#define ORC_CHUNK 65536ull
+#define ORC_HEADER 128ull
+#define ORC_MAX_N (1ull << 40)
+
+/* 16383 / (28 ln 2), rounded to the nearest double. */
+static const double ORC_K0 = 0x1.a610ca4a234eep+9;
+
+static uint64_t pad128(uint64_t x) { return (x + 127ull) / 128ull * 128ull; }
+static uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+static unsigned exp_field(uint16_t v) { return (v >> 7) & 0xFFu; }
+static unsigned sm_field(uint16_t v) { return ((unsigned)(v >> 15) << 7) | (v & 0x7Fu); }
+static uint16_t join_fields(unsigned sm, unsigned e) {
+  return (uint16_t)(((sm >> 7) << 15) | (e << 7) | (sm & 0x7Fu));
+}
+
+static void put_u16(uint8_t* p, unsigned v) {
+  p[0] = (uint8_t)v;
+  p[1] = (uint8_t)(v >> 8);
+}
+static void put_u32(uint8_t* p, uint32_t v) {
+  for (int i = 0; i < 4; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+static void put_u64(uint8_t* p, uint64_t v) {
+  for (int i = 0; i < 8; i++) p[i] = (uint8_t)(v >> (8 * i));
+}
+static unsigned get_u16(const uint8_t* p) { return (unsigned)p[0] | ((unsigned)p[1] << 8); }
+static uint32_t get_u32(const uint8_t* p) {
+  uint32_t v = 0;
+  for (int i = 3; i >= 0; i--) v = (v << 8) | p[i];
+  return v;
+}
+static uint64_t get_u64(const uint8_t* p) {
+  uint64_t v = 0;
+  for (int i = 7; i >= 0; i--) v = (v << 8) | p[i];
+  return v;
+}
+
+/* Exact value of a finite BF16 bit pattern.  Normal: (128+m) * 2^(E-134);
+ * subnormal (E = 0): m * 2^-133.  Both are exact in double. */
+double orc_bf16_value(uint16_t v) {
+  unsigned e = exp_field(v);
+  unsigned m = v & 0x7Fu;
+  double mag = (e == 0) ? ldexp((double)m, -133) : ldexp((double)(128u + m), (int)e - 134);
+  return (v & 0x8000u) ? -mag : mag;
+}
+
+/* Sample variance (correction 1) of the finite values of x; NaN and +-Inf
+ * (exponent field 255) are left out.  ZipCCL digest, section 3.1: sigma from
+ * one standard-deviation call. */
+void orc_variance(const uint16_t* x, uint64_t n, double* var_out, uint64_t* nfinite_out) {
+  double shift = 0.0;
+  if (n > 0 && exp_field(x[0]) != 255u) shift = orc_bf16_value(x[0]);
+  uint64_t nf = 0;
+  double s1 = 0.0, s2 = 0.0;
+  for (uint64_t i = 0; i < n; i++) {
+    if (exp_field(x[i]) == 255u) continue;
+    double d = orc_bf16_value(x[i]) - shift;
+    s1 += d;
+    s2 += d * d;
+    nf++;
+  }
+  double var = 0.0;
+  if (nf >= 2) {
+    var = (s2 - s1 * s1 / (double)nf) / (double)(nf - 1);
+    if (!(var > 0.0)) var = 0.0;
+  }
+  *var_out = var;
+  *nfinite_out = nf;
+}
+
+/* Window base E0 from the variance.  x_opt = 0.5 log2(var) + 0.5 log2(14 ln2 /
+ * 16383); the window's first unbiased exponent is k = floor(x_opt + 1/2),
+ * i.e. the largest k with var >= K0 * 4^k.  E0 = 127 + k, clamped to
+ * [0, 249] so that E0+6 stays a valid 8-bit field.  No finite spread
+ * (fewer than two finite values, or zero variance) gives E0 = 0. */
+int orc_window_base(double var, uint64_t nfinite) {
+  if (nfinite < 2 || !(var > 0.0)) return 0;
+  int e0 = 0;
+  for (int k = -127; k <= 122; k++) {
+    if (var >= ldexp(ORC_K0, 2 * k)) e0 = 127 + k;
+  }
+  return e0;
+}
+
+int orc_choose_e0(const uint16_t* x, uint64_t n) {
+  double var;
+  uint64_t nf;
+  orc_variance(x, n, &var, &nf);
+  return orc_window_base(var, nf);
+}
+
+static unsigned code_of(unsigned e, unsigned e0) {
+  return (e >= e0 && e <= e0 + 6u) ? e - e0 + 1u : 0u;
+}
+
+static int valid_block_size(uint32_t B) {
+  return B >= 64u && B <= (uint32_t)ORC_CHUNK && (B & (B - 1u)) == 0u;
+}
+
+/* Largest stream encode can produce for n values (every block changed, every
+ * value an escape).  B = 0 selects zip3 mode. */
+uint64_t orc_max_encoded_size(uint64_t n, uint32_t B) {
+  uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+  uint64_t size = ORC_HEADER + pad128(8ull * (nchunks + 1ull));
+  for (uint64_t c = 0; c < nchunks; c++) {
+    uint64_t nc = (n - c * ORC_CHUNK < ORC_CHUNK) ? n - c * ORC_CHUNK : ORC_CHUNK;
+    size += pad128(nc);
+    uint64_t plane;
+    if (B != 0) {
+      uint64_t nb = ceil_div(nc, B);
+      size += pad128(ceil_div(nb, 8));
+      plane = nb * B / 8;
+    } else {
+      plane = ceil_div(nc, 8);
+    }
+    size += 3ull * pad128(plane);
+    size += pad128(nc);
+  }
+  return size;
+}
+
+/* Encode.  B = 0: zip3 mode (every value coded, cache unused and may be
+ * NULL).  B != 0: ciera mode; cache holds n exponent bytes from the previous
+ * iteration (all zero before the first) and is overwritten with x's
+ * exponents.  e0_override in [0, 249] forces the window base, -1 derives it
+ * from the variance.  stats (may be NULL) receives {E0, changed blocks,
+ * escapes}. */
+int orc_encode(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, int e0_override,
+               uint8_t* out, uint64_t capacity, uint64_t* out_size, uint64_t* stats) {
+  const int ciera = (B != 0);
+  if (n > ORC_MAX_N) return ORC_ERR_ARG;
+  if (ciera && !valid_block_size(B)) return ORC_ERR_ARG;
+  if (ciera && n > 0 && cache == NULL) return ORC_ERR_ARG;
+  if (n > 0 && x == NULL) return ORC_ERR_ARG;
+  if (e0_override < -1 || e0_override > 249) return ORC_ERR_ARG;
+  const uint64_t need = orc_max_encoded_size(n, B);
+  if (out == NULL || capacity < need) return ORC_ERR_CAPACITY;
+  memset(out, 0, need);
+
+  const unsigned e0 = (e0_override >= 0) ? (unsigned)e0_override : (unsigned)orc_choose_e0(x, n);
+  const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+
+  /* Block change flags against the sender cache. */
+  uint8_t* changed = NULL;
+  uint64_t nblocks = 0;
+  if (ciera) {
+    nblocks = ceil_div(n, B);
+    changed = (uint8_t*)calloc(nblocks ? nblocks : 1, 1);
+    if (!changed) return ORC_ERR_NOMEM;
+    for (uint64_t i = 0; i < n; i++) {
+      if (exp_field(x[i]) != cache[i]) changed[i / B] = 1;
+    }
+  }
+
+  uint64_t pos = ORC_HEADER + pad128(8ull * (nchunks + 1ull));
+  uint64_t total_changed = 0, total_esc = 0;
+  for (uint64_t c = 0; c < nchunks; c++) {
+    const uint64_t start = c * ORC_CHUNK;
+    const uint64_t nc = (n - start < ORC_CHUNK) ? n - start : ORC_CHUNK;
+    put_u64(out + ORC_HEADER + 8ull * c, pos);
+
+    /* 1. sign+mantissa bytes of every value */
+    for (uint64_t t = 0; t < nc; t++) out[pos + t] = (uint8_t)sm_field(x[start + t]);
+    pos += pad128(nc);
+
+    /* 2. bitmap of changed blocks */
+    uint64_t nch = 0, nb = 0;
+    if (ciera) {
+      nb = ceil_div(nc, B);
+      for (uint64_t j = 0; j < nb; j++) {
+        if (changed[start / B + j]) {
+          out[pos + j / 8] |= (uint8_t)(1u << (j % 8));
+          nch++;
+        }
+      }
+      pos += pad128(ceil_div(nb, 8));
+    }
+
+    /* 3./4. code planes and escapes, slot by slot */
+    const uint64_t plane_bytes = ciera ? nch * B / 8 : ceil_div(nc, 8);
+    const uint64_t plane_pos[3] = {pos, pos + pad128(plane_bytes), pos + 2 * pad128(plane_bytes)};
+    const uint64_t esc_pos = pos + 3 * pad128(plane_bytes);
+    uint64_t nesc = 0;
+    uint64_t slot = 0;
+    if (!ciera) {
+      for (uint64_t t = 0; t < nc; t++, slot++) {
+        unsigned e = exp_field(x[start + t]);
+        unsigned code = code_of(e, e0);
+        for (int b = 0; b < 3; b++)
+          if ((code >> b) & 1u) out[plane_pos[b] + slot / 8] |= (uint8_t)(1u << (slot % 8));
+        if (code == 0) out[esc_pos + nesc++] = (uint8_t)e;
+      }
+    } else {
+      for (uint64_t j = 0; j < nb; j++) {
+        if (!changed[start / B + j]) continue;
+        for (uint64_t s = 0; s < B; s++, slot++) {
+          uint64_t t = j * B + s;
+          if (t >= nc) continue; /* slot past the end of the data: stays 0 */
+          unsigned e = exp_field(x[start + t]);
+          unsigned code = code_of(e, e0);
+          for (int b = 0; b < 3; b++)
+            if ((code >> b) & 1u) out[plane_pos[b] + slot / 8] |= (uint8_t)(1u << (slot % 8));
+          if (code == 0) out[esc_pos + nesc++] = (uint8_t)e;
+        }
+      }
+    }
+    pos = esc_pos + pad128(nesc);
+    total_changed += nch;
+    total_esc += nesc;
+  }
+  put_u64(out + ORC_HEADER + 8ull * nchunks, pos);
+
+  memcpy(out, ciera ? "CIER" : "ZIP3", 4);
+  put_u16(out + 4, 1);
+  out[6] = (uint8_t)(ciera ? 1 : 0);
+  out[7] = (uint8_t)e0;
+  put_u64(out + 8, n);
+  put_u32(out + 16, B);
+  put_u32(out + 20, (uint32_t)ORC_CHUNK);
+  put_u64(out + 24, nchunks);
+  put_u64(out + 32, pos);
+  put_u64(out + 40, total_changed);
+  put_u64(out + 48, total_esc);
+
+  if (ciera) {
+    for (uint64_t i = 0; i < n; i++) cache[i] = (uint8_t)exp_field(x[i]);
+    free(changed);
+  }
+  *out_size = pos;
+  if (stats) {
+    stats[0] = e0;
+    stats[1] = total_changed;
+    stats[2] = total_esc;
+  }
+  return ORC_OK;
+}
+
+/* Decode.  B = 0 expects a zip3 stream; B != 0 a ciera stream with that B,
+ * and cache holds the receiver's exponents of the previous iteration (updated
+ * in place).  Every header field, table entry and section size is checked
+ * against the layout above; any mismatch returns ORC_ERR_FORMAT. */
+int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uint32_t B,
+               uint8_t* cache) {
+  const int ciera = (B != 0);
+  if (n > ORC_MAX_N) return ORC_ERR_ARG;
+  if (ciera && !valid_block_size(B)) return ORC_ERR_ARG;
+  if (n > 0 && (y == NULL || (ciera && cache == NULL))) return ORC_ERR_ARG;
+  if (in == NULL || in_size < ORC_HEADER) return ORC_ERR_FORMAT;
+
+  const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+  const uint64_t base = ORC_HEADER + pad128(8ull * (nchunks + 1ull));
+  if (memcmp(in, ciera ? "CIER" : "ZIP3", 4) != 0) return ORC_ERR_FORMAT;
+  if (get_u16(in + 4) != 1u) return ORC_ERR_FORMAT;
+  if (in[6] != (ciera ? 1 : 0)) return ORC_ERR_FORMAT;
+  const unsigned e0 = in[7];
+  if (e0 > 249u) return ORC_ERR_FORMAT;
+  if (get_u64(in + 8) != n) return ORC_ERR_FORMAT;
+  if (get_u32(in + 16) != B) return ORC_ERR_FORMAT;
+  if (get_u32(in + 20) != (uint32_t)ORC_CHUNK) return ORC_ERR_FORMAT;
+  if (get_u64(in + 24) != nchunks) return ORC_ERR_FORMAT;
+  const uint64_t total = get_u64(in + 32);
+  if (total > in_size || base > in_size) return ORC_ERR_FORMAT;
+  for (uint64_t i = 56; i < ORC_HEADER; i++)
+    if (in[i] != 0) return ORC_ERR_FORMAT;
+  if (get_u64(in + ORC_HEADER) != base) return ORC_ERR_FORMAT;
+  if (get_u64(in + ORC_HEADER + 8ull * nchunks) != total) return ORC_ERR_FORMAT;
+
+  uint64_t total_changed = 0, total_esc = 0;
+  for (uint64_t c = 0; c < nchunks; c++) {
+    const uint64_t start = c * ORC_CHUNK;
+    const uint64_t nc = (n - start < ORC_CHUNK) ? n - start : ORC_CHUNK;
+    const uint64_t begin = get_u64(in + ORC_HEADER + 8ull * c);
+    const uint64_t end = get_u64(in + ORC_HEADER + 8ull * (c + 1));
+    if (begin > end || end > total) return ORC_ERR_FORMAT;
+
+    uint64_t pos = begin;
+    const uint64_t sm_pos = pos;
+    pos += pad128(nc);
+    uint64_t bitmap_pos = 0, nb = 0, nch = 0;
+    if (ciera) {
+      nb = ceil_div(nc, B);
+      bitmap_pos = pos;
+      pos += pad128(ceil_div(nb, 8));
+      if (pos > end) return ORC_ERR_FORMAT;
+      for (uint64_t j = 0; j < nb; j++) nch += (in[bitmap_pos + j / 8] >> (j % 8)) & 1u;
+    }
+    const uint64_t plane_bytes = ciera ? nch * B / 8 : ceil_div(nc, 8);
+    const uint64_t plane_pos[3] = {pos, pos + pad128(plane_bytes), pos + 2 * pad128(plane_bytes)};
+    const uint64_t esc_pos = pos + 3 * pad128(plane_bytes);
+    if (esc_pos > end) return ORC_ERR_FORMAT;
+
+    uint64_t nesc = 0;
+    if (!ciera) {
+      for (uint64_t t = 0; t < nc; t++) {
+        unsigned code = 0, e;
+        for (int b = 0; b < 3; b++) code |= ((in[plane_pos[b] + t / 8] >> (t % 8)) & 1u) << b;
+        if (code != 0) {
+          e = e0 + code - 1u;
+        } else {
+          if (esc_pos + nesc >= end) return ORC_ERR_FORMAT;
+          e = in[esc_pos + nesc++];
+        }
+        y[start + t] = join_fields(in[sm_pos + t], e);
+      }
+    } else {
+      uint64_t rank = 0; /* changed blocks of this chunk seen so far */
+      for (uint64_t j = 0; j < nb; j++) {
+        const int is_changed = (in[bitmap_pos + j / 8] >> (j % 8)) & 1u;
+        for (uint64_t s = 0; s < B && j * B + s < nc; s++) {
+          const uint64_t t = j * B + s;
+          unsigned e;
+          if (!is_changed) {
+            e = cache[start + t];
+          } else {
+            const uint64_t slot = rank * B + s;
+            unsigned code = 0;
+            for (int b = 0; b < 3; b++)
+              code |= ((in[plane_pos[b] + slot / 8] >> (slot % 8)) & 1u) << b;
+            if (code != 0) {
+              e = e0 + code - 1u;
+            } else {
+              if (esc_pos + nesc >= end) return ORC_ERR_FORMAT;
+              e = in[esc_pos + nesc++];
+            }
+            cache[start + t] = (uint8_t)e;
+          }
+          y[start + t] = join_fields(in[sm_pos + t], e);
+        }
+        if (is_changed) rank++;
+      }
+    }
+    if (esc_pos + pad128(nesc) != end) return ORC_ERR_FORMAT;
+    total_changed += nch;
+    total_esc += nesc;
+  }
+  if (get_u64(in + 40) != total_changed || get_u64(in + 48) != total_esc) return ORC_ERR_FORMAT;
+  return ORC_OK;
+}
