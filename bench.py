@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Codec benchmark: GB/s of BF16 input through encode + decode on one MI355X.
+
+A step is one pass of the whole codec over one synthetic tensor already
+resident in HBM: encode (variance/change pass, window plan, pack) and decode.
+Default workload: the 64 Mi-value gradient-like tensor (N(0, 1e-3) with 0.1 %
+Student-t(3) outliers, 3-bit code only).  Other workloads (1, 3, 4, 5) use
+exponent reuse; their steps alternate between two consecutive iterations so
+the caches always hold the previous iteration.
+
+Prints one JSON line.  ``value`` = 2 n K / (wall time of K steps), in GB/s of
+BF16 input (1 GB = 1e9 bytes).  ``roofline`` describes the dominant kernel,
+timed with HIP events on the stream it runs on; ``cpu_baseline`` times the
+plain CPU oracle (single thread) on the same tensor.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+WORKLOAD_NAMES = {
+    1: "shard 1,048,576 BF16 ~N(0,0.02), iter t = iter t-1 + N(0,1e-4); exponent reuse B=256 + 3-bit code",
+    2: "gradient 67,108,864 BF16 ~N(0,1e-3) + 0.1% Student-t(3); 3-bit code only, 128-B chunks",
+    3: "OLMoE-like layer shard W=4, 104,891,392 BF16 ~N(0,0.02), ~0.3% exponent flips; exponent reuse B={B}",
+    4: "DeepSeek-MoE-like layer shard W=8, 71,368,704 BF16 ~N(0,0.015), 0.5% flips in 20% of blocks; B=128",
+    5: "stress 1e9 BF16 mixed N/t/constant + specials, 1% flips; exponent reuse B=512",
+}
+
+
+def source_hash() -> str:
+    with open(os.path.join(ROOT, "lossless_bf16_tensor_exp_amd", "csrc", "ciera.hip"), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: int, B: int):
+    """Counter-derived HBM bytes per launch from profiles/traffic.json, if
+    they were taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("kernels", {}).get(f"{kernel}/w{workload}/B{B}")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--block", type=int, default=None, help="block size B for the reuse workloads")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--verify", action="store_true", help="check the last step's round trip on the host")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
+              "(the codec runs on one rank's shard; see the sharding note in DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import lossless_bf16_tensor_exp_amd as ciera
+    from lossless_bf16_tensor_exp_amd import workloads as wl
+
+    if not os.path.exists(ciera.library_path()):
+        from lossless_bf16_tensor_exp_amd import build as hip_build
+        hip_build.build()
+    ciera.load_library()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+
+    t0 = time.time()
+    gen = wl.WORKLOADS[args.workload]
+    d = gen()
+    iters = d["iters"]
+    mode = d["mode"]
+    B = 0 if mode == "zip3" else (args.block or d["B"][0])
+    n = iters[0].size
+    print(f"[bench] workload {args.workload} n={n} B={B} generated in {time.time() - t0:.1f}s", file=sys.stderr,
+          flush=True)
+
+    # the two tensors a step alternates between (zip3: one tensor)
+    pair = [iters[-2], iters[-1]] if len(iters) >= 2 else [iters[0], iters[0]]
+    xs = [torch.from_numpy(a.view(np.int16)).to(dev) for a in pair]
+    y = torch.empty(n, dtype=torch.int16, device=dev)
+    if mode == "zip3":
+        cap, wsz = ciera.zip3_max_encoded_size(n), ciera.zip3_workspace_size(n)
+    else:
+        cap, wsz = ciera.ciera_max_encoded_size(n, B), ciera.ciera_workspace_size(n, B)
+    out = torch.empty(cap, dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    size = torch.zeros(1, dtype=torch.int64, device=dev)
+    send = recv = None
+    if mode != "zip3":
+        e_prev = torch.from_numpy(((pair[0] >> 7) & 0xFF).astype(np.uint8)).to(dev)
+        send, recv = e_prev.clone(), e_prev.clone()
+    stream = torch.cuda.current_stream()
+
+    def encode(x):
+        if mode == "zip3":
+            ciera.zip3_encode(x, out, ws_e, size, -1, stream)
+        else:
+            ciera.ciera_encode(x, B, send, out, ws_e, size, -1, stream)
+
+    def decode(in_size):
+        if mode == "zip3":
+            ciera.zip3_decode(out, in_size, y, ws_d, stream)
+        else:
+            ciera.ciera_decode(out, in_size, y, B, recv, ws_d, stream)
+
+    # Stream sizes per input are fixed, so decode can take the size learned
+    # in warm-up without a host sync inside the timed loop.
+    sizes = {}
+    for i in range(2):
+        k = (i + 1) % 2 if mode != "zip3" else 0
+        encode(xs[k])
+        torch.cuda.synchronize()
+        sizes[k] = int(size.item())
+        decode(sizes[k])
+        torch.cuda.synchronize()
+        assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
+    # after these two steps the caches hold pair[0]'s exponents again
+    for w in range(args.warmup):
+        k = (w + 1) % 2 if mode != "zip3" else 0
+        encode(xs[k])
+        decode(sizes[k])
+        if mode != "zip3":
+            k2 = 1 - k
+            encode(xs[k2])
+            decode(sizes[k2])
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for s in range(K):
+        k = (s + 1) % 2 if mode != "zip3" else 0
+        ev[s][0].record(stream)
+        encode(xs[k])
+        ev[s][1].record(stream)
+        decode(sizes[k])
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    enc_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]
+    dec_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]
+    assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
+    if args.verify:
+        klast = K % 2 if mode != "zip3" else 0
+        assert torch.equal(y, xs[klast]), "round trip failed"
+
+    in_bytes = 2 * n
+    value = in_bytes * K / wall / 1e9
+    enc_avg = sum(enc_ms) / K
+    dec_avg = sum(dec_ms) / K
+    stream_bytes = sizes[1 if mode != "zip3" else 0]
+    ratio = in_bytes / stream_bytes
+
+    # Dominant kernel: the decode kernel is one launch per decode call, so
+    # the events around the call time exactly that kernel.  Its algorithmic
+    # bytes: the whole stream read once + the BF16 output written (+ for
+    # exponent reuse the receiver cache: read for unchanged blocks, written
+    # for changed ones, n bytes in total).
+    dec_bytes = stream_bytes + in_bytes + (n if mode != "zip3" else 0)
+    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
+    roofline = {"kernel": "k_decode", "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic("k_decode", args.workload, B),
+                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": round(dec_avg, 5)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        x_host = pair[1] if mode != "zip3" else pair[0]
+        t = time.perf_counter()
+        if mode == "zip3":
+            s_o, _ = oracle.zip3_encode(x_host)
+        else:
+            c = ((pair[0] >> 7) & 0xFF).astype(np.uint8)
+            s_o, _ = oracle.ciera_encode(x_host, B, c)
+        t_enc = time.perf_counter() - t
+        t = time.perf_counter()
+        if mode == "zip3":
+            oracle.zip3_decode(s_o, n)
+        else:
+            oracle.ciera_decode(s_o, n, B, ((pair[0] >> 7) & 0xFF).astype(np.uint8))
+        t_dec = time.perf_counter() - t
+        cpu = {"value": round(in_bytes / (t_enc + t_dec) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+               "sample": f"the full {n}-value tensor, one encode + one decode (scalar C oracle, 1 thread)",
+               "encode_GBps": round(in_bytes / t_enc / 1e9, 4), "decode_GBps": round(in_bytes / t_dec / 1e9, 4),
+               "host_cpus": os.cpu_count()}
+
+    line = {
+        "metric": "codec encode/decode GB/s of BF16 input (% HBM roofline) + compression ratio",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload].format(B=B), "n": n, "B": B, "mode": mode},
+        "encode_GBps": round(in_bytes / (enc_avg * 1e-3) / 1e9, 2),
+        "decode_GBps": round(in_bytes / (dec_avg * 1e-3) / 1e9, 2),
+        "encode_ms": round(enc_avg, 5),
+        "decode_ms": round(dec_avg, 5),
+        "compression_ratio": round(ratio, 4),
+        "stream_bytes": stream_bytes,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "source_hash": source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

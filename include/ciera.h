@@ -1,0 +1,154 @@
+/*
+ * ciera.h -- C ABI of the lossless BF16 codec for MI355X (gfx950).
+ *
+ * The codec turns a BF16 tensor into a byte stream and back, bit for bit:
+ *
+ *  - every value is split into a sign+mantissa byte and its 8-bit exponent
+ *    (ZipCCL research digest, section 3.1; CIERA page, section 3.1);
+ *  - exponents are coded in 3 bits against a 7-binade window whose base E0 is
+ *    chosen from the tensor's standard deviation, with code 0 plus the raw
+ *    exponent (an "escape") for values outside it (ZipCCL digest, section
+ *    3.1, the P_win and x_opt equations and Figure 2);
+ *  - in ciera mode, blocks of B values whose exponents all equal the previous
+ *    iteration's are flagged unchanged in a bitmap and send no exponents; the
+ *    receiver takes them from its own cache (CIERA page, sections 3.1-3.2);
+ *  - the stream is cut into chunks of 65,536 input values, each written as a
+ *    self-contained segment whose sections (sign+mantissa, bitmap, three code
+ *    bit-planes, escapes) start on 128-byte boundaries (ZipCCL digest,
+ *    section 3.1 last paragraph and Figure 1).
+ *
+ * Stream layout (little-endian; all padding and unnamed bytes are zero):
+ *   header (128 B): "ZIP3"|"CIER", u16 version=1, u8 mode (0 zip3, 1 ciera),
+ *     u8 E0, u64 n, u32 B (0 in zip3), u32 C=65536, u64 nchunks,
+ *     u64 total_bytes, u64 n_changed_blocks, u64 n_escapes;
+ *   chunk table at byte 128: nchunks+1 u64 absolute offsets, padded to 128;
+ *   per chunk: sm[n_c] | bitmap[ceil(nb_c/8)] (ciera) | plane0..2[P_c] |
+ *     escapes[n_esc_c], each padded to 128.  Plane b holds bit b of the code
+ *     of slot t in bit (t&7) of byte (t>>3).  zip3: slot t = value t of the
+ *     chunk.  ciera: the r-th changed block owns slots rB..rB+B-1.
+ *
+ * Conventions for every entry point:
+ *  - d_* arguments are device pointers on the current HIP device, 16-byte
+ *    aligned, owned and allocated by the caller.  The library never
+ *    allocates, frees or synchronises (except ciera_read_error).  Buffers
+ *    must not alias.
+ *  - BF16 data is passed as its 16-bit patterns (n values = 2n bytes).
+ *  - Calls are asynchronous on `stream`: they return once the kernels are
+ *    enqueued.  Argument errors are reported synchronously, before any
+ *    launch, and nothing is enqueued then.  Errors found on the device (a
+ *    malformed stream in decode) are written to the workspace; read them
+ *    with ciera_read_error.
+ *  - The workspace is caller-owned scratch of at least the size the
+ *    *_workspace_size query returns.  Its contents need no initialisation
+ *    and are meaningless between calls, except for the error words that
+ *    ciera_read_error reads.  Calls that share a workspace must be ordered
+ *    (same stream, or synchronised); distinct workspaces may be used
+ *    concurrently on different streams.
+ *  - n <= 2^40.  n = 0 is valid.  B is a power of two, 64 <= B <= 65536.
+ */
+#ifndef CIERA_H
+#define CIERA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int ciera_status;
+#define CIERA_OK 0
+#define CIERA_ERR_ARG 1       /* null or misaligned pointer, n too large, bad B or E0 override */
+#define CIERA_ERR_CAPACITY 2  /* out_capacity below the *_max_encoded_size bound */
+#define CIERA_ERR_WORKSPACE 3 /* ws_bytes below the *_workspace_size bound */
+#define CIERA_ERR_HIP 4       /* a HIP launch or runtime call failed */
+#define CIERA_ERR_FORMAT 5    /* decode: the stream is malformed or does not match n / B / mode */
+#define CIERA_ERR_INTERNAL 6  /* encode: a chunk-offset wait gave up (should not happen) */
+
+#define CIERA_CHUNK 65536u
+
+/* Largest stream zip3_encode can write for n values (every value an escape):
+ * about 2.375 n bytes plus headers.  Pass at least this as out_capacity. */
+uint64_t zip3_max_encoded_size(uint64_t n);
+/* Same for ciera_encode with block size B (every block changed).  Returns 0
+ * for an invalid B. */
+uint64_t ciera_max_encoded_size(uint64_t n, uint32_t B);
+/* Workspace bytes needed by zip3_encode and zip3_decode for n values. */
+uint64_t zip3_workspace_size(uint64_t n);
+/* Workspace bytes needed by ciera_encode and ciera_decode for n values and
+ * block size B (0 for an invalid B). */
+uint64_t ciera_workspace_size(uint64_t n, uint32_t B);
+
+/* zip3_encode: code every exponent of x (ZipCCL digest, section 3.1).
+ *   d_x        in   n BF16 patterns (u16), 16-byte aligned
+ *   d_out      out  the stream; out_capacity >= zip3_max_encoded_size(n)
+ *   d_ws       tmp  ws_bytes >= zip3_workspace_size(n)
+ *   d_out_size out  one u64 on the device: the stream's length in bytes
+ *                   (also in header bytes 32..39).  Read it after syncing.
+ * Errors: CIERA_ERR_ARG, _CAPACITY, _WORKSPACE, _HIP (synchronous). */
+ciera_status zip3_encode(const void* d_x, uint64_t n, void* d_out, uint64_t out_capacity,
+                         void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                         hipStream_t stream);
+
+/* zip3_decode: inverse of zip3_encode.
+ *   d_in   in   the stream, in_size bytes (at least its total_bytes)
+ *   d_y    out  n BF16 patterns, bit-identical to the encoded input
+ *   d_ws   tmp  ws_bytes >= zip3_workspace_size(n)
+ * A stream whose header, table or section sizes do not match n and the
+ * layout is rejected on the device: the kernels read nothing outside
+ * [d_in, d_in + in_size), leave d_y unspecified, and ciera_read_error then
+ * returns CIERA_ERR_FORMAT. */
+ciera_status zip3_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_t n,
+                         void* d_ws, uint64_t ws_bytes, hipStream_t stream);
+
+/* ciera_encode: exponent reuse across iterations plus the 3-bit code for the
+ * changed blocks (CIERA page, sections 3.1-3.2; ZipCCL digest, section 3.1).
+ *   d_x         in      n BF16 patterns of this iteration
+ *   B           in      block size
+ *   d_prev_exp  in/out  sender exponent cache, n bytes: the exponent fields
+ *                       of the previous iteration's tensor (all zero before
+ *                       the first).  On return it holds x's exponents.
+ *   d_out, out_capacity >= ciera_max_encoded_size(n, B), d_ws, ws_bytes >=
+ *   ciera_workspace_size(n, B), d_out_size: as for zip3_encode.
+ * The window E0 comes from the standard deviation of all finite values of
+ * x, not only of the changed blocks. */
+ciera_status ciera_encode(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp,
+                          void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes,
+                          uint64_t* d_out_size, hipStream_t stream);
+
+/* ciera_decode: rebuild x from the stream and the receiver's cache.
+ *   d_prev_exp  in/out  receiver exponent cache, n bytes, holding the
+ *                       previous iteration's exponents (all zero before the
+ *                       first); blocks the bitmap marks unchanged take their
+ *                       exponents from it.  On return it holds x's exponents.
+ * Other arguments and error behaviour as zip3_decode; B must equal the
+ * stream's B. */
+ciera_status ciera_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, uint32_t B,
+                          uint8_t* d_prev_exp, void* d_ws, uint64_t ws_bytes, hipStream_t stream);
+
+/* Synchronise `stream` and return the device-side status of the last call
+ * that used d_ws: CIERA_OK, CIERA_ERR_FORMAT (decode saw a malformed
+ * stream), CIERA_ERR_INTERNAL, or CIERA_ERR_HIP if the copy fails. */
+ciera_status ciera_read_error(const void* d_ws, hipStream_t stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* ciera_status_string(ciera_status status);
+
+/* Same as zip3_encode / ciera_encode with the window base forced to
+ * e0_override (0..249); -1 derives it from the standard deviation as the
+ * plain entry points do.  For tests that pin the layout at a given window
+ * and for callers that reuse the previous iteration's window. */
+ciera_status zip3_encode_ex(const void* d_x, uint64_t n, void* d_out, uint64_t out_capacity,
+                            void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, int e0_override,
+                            hipStream_t stream);
+ciera_status ciera_encode_ex(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp,
+                             void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes,
+                             uint64_t* d_out_size, int e0_override, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CIERA_H */

@@ -1,0 +1,195 @@
+"""Lossless BF16 codec for MI355X: exponent reuse across iterations (CIERA)
+plus the sigma-windowed 3-bit exponent code (ZipCCL), in hand-written HIP.
+
+This package is a thin binding over the C ABI in ``include/ciera.h``
+(``libciera.so``, built in-tree by ``build.py``).  Every step of the codec
+runs in the HIP kernels; the binding only checks tensor types and passes
+device pointers, sizes and the current HIP stream.  PyTorch supplies device
+memory and streams and nothing else.  If the library is not built, every
+entry point raises: there is no fallback.
+
+Same names as the C ABI::
+
+    zip3_max_encoded_size(n)              ciera_max_encoded_size(n, B)
+    zip3_workspace_size(n)                ciera_workspace_size(n, B)
+    zip3_encode(x, out, ws, out_size, e0_override=-1, stream=None)
+    zip3_decode(inp, in_size, y, ws, stream=None)
+    ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None)
+    ciera_decode(inp, in_size, y, B, prev_exp, ws, stream=None)
+    ciera_read_error(ws, stream=None)
+
+``x``/``y`` are CUDA(HIP) tensors of dtype bfloat16, int16 or uint16 holding
+the BF16 patterns; ``out``/``inp``/``ws``/``prev_exp`` are uint8 tensors and
+``out_size`` a one-element int64/uint64 tensor, all on the same device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "CieraError", "library_path", "load_library",
+    "zip3_max_encoded_size", "ciera_max_encoded_size", "zip3_workspace_size", "ciera_workspace_size",
+    "zip3_encode", "zip3_decode", "ciera_encode", "ciera_decode", "ciera_read_error", "ciera_status_string",
+    "CHUNK",
+]
+
+CHUNK = 65536
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libciera.so")
+_lib = None
+
+STATUS_NAMES = {0: "CIERA_OK", 1: "CIERA_ERR_ARG", 2: "CIERA_ERR_CAPACITY", 3: "CIERA_ERR_WORKSPACE",
+                4: "CIERA_ERR_HIP", 5: "CIERA_ERR_FORMAT", 6: "CIERA_ERR_INTERNAL"}
+
+
+class CieraError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {STATUS_NAMES.get(status, status)}")
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load ``libciera.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build() "
+                          "or python -m lossless_bf16_tensor_exp_amd.build")
+    lib = ctypes.CDLL(_LIB_PATH)
+    u64, u32, vp, i32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
+    for name, args in [("zip3_max_encoded_size", [u64]), ("ciera_max_encoded_size", [u64, u32]),
+                       ("zip3_workspace_size", [u64]), ("ciera_workspace_size", [u64, u32])]:
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, u64
+    sigs = {
+        "zip3_encode": [vp, u64, vp, u64, vp, u64, vp, vp],
+        "zip3_encode_ex": [vp, u64, vp, u64, vp, u64, vp, i32, vp],
+        "zip3_decode": [vp, u64, vp, u64, vp, u64, vp],
+        "ciera_encode": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
+        "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, vp],
+        "ciera_decode": [vp, u64, vp, u64, u32, vp, vp, u64, vp],
+        "ciera_read_error": [vp, vp],
+    }
+    for name, args in sigs.items():
+        f = getattr(lib, name)
+        f.argtypes, f.restype = args, i32
+    lib.ciera_status_string.argtypes, lib.ciera_status_string.restype = [i32], ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None and t.numel() else None
+
+
+def _check_values(x, name):
+    torch = _torch()
+    if x.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold BF16 patterns (bfloat16/int16/uint16), got {x.dtype}")
+    if not x.is_cuda or not x.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous device tensor")
+
+
+def _check_bytes(t, name, min_len=0):
+    torch = _torch()
+    if t.dtype != torch.uint8 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous uint8 device tensor")
+    if t.numel() < min_len:
+        raise ValueError(f"{name} holds {t.numel()} bytes, needs {min_len}")
+
+
+def _check_size_slot(t):
+    torch = _torch()
+    if t.dtype not in (torch.int64, torch.uint64) or t.numel() < 1 or not t.is_cuda:
+        raise ValueError("out_size must be a one-element int64/uint64 device tensor")
+
+
+def _raise(st, what):
+    if st != 0:
+        raise CieraError(st, what)
+
+
+def zip3_max_encoded_size(n: int) -> int:
+    return load_library().zip3_max_encoded_size(n)
+
+
+def ciera_max_encoded_size(n: int, B: int) -> int:
+    return load_library().ciera_max_encoded_size(n, B)
+
+
+def zip3_workspace_size(n: int) -> int:
+    return load_library().zip3_workspace_size(n)
+
+
+def ciera_workspace_size(n: int, B: int) -> int:
+    return load_library().ciera_workspace_size(n, B)
+
+
+def ciera_status_string(status: int) -> str:
+    return load_library().ciera_status_string(status).decode()
+
+
+def zip3_encode(x, out, ws, out_size, e0_override: int = -1, stream=None) -> None:
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.zip3_encode_ex(_ptr(x), x.numel(), _ptr(out), out.numel(), _ptr(ws), ws.numel(),
+                            ctypes.c_void_p(out_size.data_ptr()), e0_override, _stream(stream))
+    _raise(st, "zip3_encode")
+
+
+def zip3_decode(inp, in_size: int, y, ws, stream=None) -> None:
+    lib = load_library()
+    _check_bytes(inp, "inp", in_size)
+    _check_values(y, "y")
+    _check_bytes(ws, "ws")
+    st = lib.zip3_decode(_ptr(inp), in_size, _ptr(y), y.numel(), _ptr(ws), ws.numel(), _stream(stream))
+    _raise(st, "zip3_decode")
+
+
+def ciera_encode(x, B: int, prev_exp, out, ws, out_size, e0_override: int = -1, stream=None) -> None:
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(prev_exp, "prev_exp", x.numel())
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.ciera_encode_ex(_ptr(x), x.numel(), B, _ptr(prev_exp), _ptr(out), out.numel(), _ptr(ws),
+                             ws.numel(), ctypes.c_void_p(out_size.data_ptr()), e0_override, _stream(stream))
+    _raise(st, "ciera_encode")
+
+
+def ciera_decode(inp, in_size: int, y, B: int, prev_exp, ws, stream=None) -> None:
+    lib = load_library()
+    _check_bytes(inp, "inp", in_size)
+    _check_values(y, "y")
+    _check_bytes(prev_exp, "prev_exp", y.numel())
+    _check_bytes(ws, "ws")
+    st = lib.ciera_decode(_ptr(inp), in_size, _ptr(y), y.numel(), B, _ptr(prev_exp), _ptr(ws), ws.numel(),
+                          _stream(stream))
+    _raise(st, "ciera_decode")
+
+
+def ciera_read_error(ws, stream=None) -> int:
+    """Synchronise the stream and return the device-side status word."""
+    _check_bytes(ws, "ws")
+    return load_library().ciera_read_error(_ptr(ws), _stream(stream))

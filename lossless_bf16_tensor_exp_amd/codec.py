@@ -1,0 +1,61 @@
+"""Buffer owners for the C ABI: allocate the stream, workspace, size slot and
+exponent caches once with torch, then call the library on them.
+
+Allocation happens only in the constructors; ``encode``/``decode`` only pass
+pointers.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import (ciera_decode, ciera_encode, ciera_max_encoded_size, ciera_read_error, ciera_workspace_size,
+               zip3_decode, zip3_encode, zip3_max_encoded_size, zip3_workspace_size)
+
+
+class Zip3Codec:
+    """3-bit exponent code only (no cross-iteration state)."""
+
+    def __init__(self, n: int, device="cuda"):
+        self.n = n
+        self.capacity = zip3_max_encoded_size(n)
+        self.out = torch.empty(self.capacity, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(zip3_workspace_size(n), dtype=torch.uint8, device=device)
+        self.size = torch.zeros(1, dtype=torch.int64, device=device)
+
+    def encode(self, x, e0_override: int = -1, stream=None):
+        zip3_encode(x, self.out, self.ws, self.size, e0_override, stream)
+
+    def decode(self, stream_bytes, in_size: int, y, stream=None):
+        zip3_decode(stream_bytes, in_size, y, self.ws, stream)
+
+    def nbytes(self) -> int:
+        return int(self.size.item())
+
+    def error(self, stream=None) -> int:
+        return ciera_read_error(self.ws, stream)
+
+
+class CieraCodec:
+    """Exponent reuse with block size B plus the 3-bit code; keeps a sender
+    and a receiver exponent cache (both start at zero)."""
+
+    def __init__(self, n: int, B: int, device="cuda"):
+        self.n, self.B = n, B
+        self.capacity = ciera_max_encoded_size(n, B)
+        if self.capacity == 0:
+            raise ValueError(f"invalid block size {B}")
+        self.out = torch.empty(self.capacity, dtype=torch.uint8, device=device)
+        self.ws = torch.empty(ciera_workspace_size(n, B), dtype=torch.uint8, device=device)
+        self.ws_dec = torch.empty(ciera_workspace_size(n, B), dtype=torch.uint8, device=device)
+        self.size = torch.zeros(1, dtype=torch.int64, device=device)
+        self.send_cache = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+        self.recv_cache = torch.zeros(max(n, 1), dtype=torch.uint8, device=device)
+
+    def encode(self, x, e0_override: int = -1, stream=None):
+        ciera_encode(x, self.B, self.send_cache, self.out, self.ws, self.size, e0_override, stream)
+
+    def decode(self, stream_bytes, in_size: int, y, stream=None):
+        ciera_decode(stream_bytes, in_size, y, self.B, self.recv_cache, self.ws_dec, stream)
+
+    def nbytes(self) -> int:
+        return int(self.size.item())

@@ -221,3 +221,35 @@ WORKLOADS = {1: workload1, 2: workload2, 3: workload3, 4: workload4, 5: workload
 
 def all_bf16_patterns() -> np.ndarray:
     return np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+SPECIALS = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC1, 0xFF81, 0x7F81, 0xFFFF],
+                    dtype=np.uint16)
+
+
+def mixed_small(rng: np.random.Generator, n: int) -> np.ndarray:
+    """Small edge-case tensor: Gaussian at a random scale, Student-t, or raw
+    random bit patterns, with a few specials (+-0, subnormals, +-Inf, NaN
+    payloads) planted at random positions."""
+    kind = int(rng.integers(0, 3))
+    if kind == 0:
+        x = f32_to_bf16(rng.standard_normal(n, dtype=np.float32) * np.float32(10.0 ** rng.uniform(-6, 2)))
+    elif kind == 1:
+        x = f32_to_bf16((rng.standard_t(3, n) * 0.01).astype(np.float32))
+    else:
+        x = rng.integers(0, 65536, size=n, dtype=np.uint32).astype(np.uint16)
+    if n:
+        sp = rng.choice(n, size=min(n, int(rng.integers(0, 6))), replace=False)
+        x[sp] = rng.choice(SPECIALS, size=sp.size)
+    return x
+
+
+def perturbed_cache(rng: np.random.Generator, x: np.ndarray, frac: float) -> np.ndarray:
+    """Exponent bytes of x with about frac of them replaced, as a previous
+    iteration's cache would differ."""
+    cache = ((x >> 7) & 0xFF).astype(np.uint8)
+    n = x.size
+    if n:
+        k = max(1, int(n * frac))
+        cache[rng.choice(n, size=min(n, k), replace=False)] ^= np.uint8(rng.integers(1, 256))
+    return cache

@@ -1,0 +1,142 @@
+"""Helpers for the GPU parity tests: run the HIP library through its C ABI on
+canary-filled buffers and compare with the CPU oracle byte for byte."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+
+torch = pytest.importorskip("torch")
+import lossless_bf16_tensor_exp_amd as ciera  # noqa: E402
+
+GUARD = 256           # guard bytes on each side of every output buffer
+CANARY = 0xA5
+K0 = float.fromhex("0x1.a610ca4a234eep+9")
+
+
+def say(*args):
+    print(*args, file=sys.stderr, flush=True)
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    ciera.load_library()  # raises if the HIP library is not built
+
+
+def _guarded_bytes(n, fill=CANARY):
+    buf = torch.full((n + 2 * GUARD,), fill, dtype=torch.uint8, device="cuda")
+    return buf, buf[GUARD:GUARD + n]
+
+
+def _check_guards(host, n, what):
+    assert (host[:GUARD] == CANARY).all(), f"{what}: write before the buffer"
+    assert (host[GUARD + n:] == CANARY).all(), f"{what}: write after the buffer"
+
+
+def exps(x):
+    return ((x >> 7) & 0xFF).astype(np.uint8)
+
+
+def gpu_encode(x, B=0, cache=None, e0=-1, stream=None):
+    """Encode uint16 array x on the GPU.  Returns (stream bytes, cache after)."""
+    n = x.size
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    cap = ciera.ciera_max_encoded_size(n, B) if B else ciera.zip3_max_encoded_size(n)
+    ws_n = ciera.ciera_workspace_size(n, B) if B else ciera.zip3_workspace_size(n)
+    buf, out = _guarded_bytes(cap)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    size = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    cd = None
+    if B:
+        cbuf, cd = _guarded_bytes(n)
+        cd.copy_(torch.from_numpy(cache))
+        ciera.ciera_encode(xd, B, cd, out, ws, size, e0, stream)
+    else:
+        ciera.zip3_encode(xd, out, ws, size, e0, stream)
+    torch.cuda.synchronize()
+    assert ciera.ciera_read_error(ws) == 0
+    sz = int(size.item())
+    assert 0 < sz <= cap
+    host = buf.cpu().numpy()
+    _check_guards(host, cap, "stream")
+    assert (host[GUARD + sz:GUARD + cap] == CANARY).all(), "write past the stream's end"
+    new_cache = None
+    if B:
+        ch = cbuf.cpu().numpy()
+        _check_guards(ch, n, "sender cache")
+        new_cache = ch[GUARD:GUARD + n].copy()
+    return host[GUARD:GUARD + sz].copy(), new_cache
+
+
+def gpu_decode(stream_bytes, n, B=0, cache=None, in_size=None):
+    """Decode on the GPU.  Returns (values uint16, cache after, device status)."""
+    inp = torch.from_numpy(np.ascontiguousarray(stream_bytes)).cuda()
+    in_size = stream_bytes.size if in_size is None else in_size
+    ybuf, y = _guarded_bytes(2 * n)
+    ws_n = ciera.ciera_workspace_size(n, B) if B else ciera.zip3_workspace_size(n)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    yv = y.view(torch.int16)
+    cd = None
+    if B:
+        cbuf, cd = _guarded_bytes(n)
+        cd.copy_(torch.from_numpy(cache))
+        ciera.ciera_decode(inp, in_size, yv, B, cd, ws)
+    else:
+        ciera.zip3_decode(inp, in_size, yv, ws)
+    torch.cuda.synchronize()
+    status = ciera.ciera_read_error(ws)
+    host = ybuf.cpu().numpy()
+    _check_guards(host, 2 * n, "y")
+    new_cache = None
+    if B:
+        ch = cbuf.cpu().numpy()
+        _check_guards(ch, n, "receiver cache")
+        new_cache = ch[GUARD:GUARD + n].copy()
+    return host[GUARD:GUARD + 2 * n].copy().view(np.uint16), new_cache, status
+
+
+def _first_diff(a, b):
+    m = min(a.size, b.size)
+    d = np.flatnonzero(a[:m] != b[:m])
+    return int(d[0]) if d.size else m
+
+
+def check_encode(x, B=0, cache=None, e0=-1, stream=None):
+    """GPU encode == oracle encode, byte for byte (and caches).  Where the
+    window base differs, both choices must straddle a threshold within the
+    FP64 summation error, and the rest must equal the oracle run at the GPU's
+    window base.  Returns (stream, oracle stats)."""
+    g_stream, g_cache = gpu_encode(x, B, cache, e0, stream)
+    o_cache = cache.copy() if B else None
+    o_stream, o_st = oracle.encode(x, B, o_cache, e0)
+    if g_stream.tobytes() != o_stream.tobytes() and e0 < 0 and int(g_stream[7]) != o_st["E0"]:
+        var, nf = oracle.variance(x)
+        k = max(int(g_stream[7]), o_st["E0"]) - 127
+        t = K0 * 4.0 ** k
+        assert abs(int(g_stream[7]) - o_st["E0"]) == 1 and abs(var - t) <= 1e-6 * t, \
+            f"window base differs away from a threshold: gpu {g_stream[7]} oracle {o_st['E0']} var {var}"
+        o_cache = cache.copy() if B else None
+        o_stream, o_st = oracle.encode(x, B, o_cache, int(g_stream[7]))
+    if g_stream.tobytes() != o_stream.tobytes():
+        i = _first_diff(g_stream, o_stream)
+        raise AssertionError(f"stream differs from the oracle at byte {i} of {o_stream.size} "
+                             f"(gpu size {g_stream.size}): gpu {g_stream[i:i + 16]} oracle {o_stream[i:i + 16]}")
+    if B:
+        assert np.array_equal(g_cache, o_cache), "sender cache differs from the oracle's"
+        assert np.array_equal(g_cache, exps(x))
+    return g_stream, o_st
+
+
+def check_roundtrip(stream_bytes, x, B=0, cache=None):
+    y, c, st = gpu_decode(stream_bytes, x.size, B, cache)
+    assert st == 0, f"decode reported status {st}"
+    if not np.array_equal(y, x):
+        i = int(np.flatnonzero(y != x)[0])
+        raise AssertionError(f"decode differs at value {i}: {y[i]:#06x} vs {x[i]:#06x}")
+    if B:
+        assert np.array_equal(c, exps(x)), "receiver cache is not the decoded exponents"
+    return c

@@ -1,0 +1,78 @@
+"""The C-ABI library loads, exports every symbol include/ciera.h declares, and
+its host-side logic (size queries, argument checks) behaves; no GPU needed."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import lossless_bf16_tensor_exp_amd as ciera
+    if not os.path.exists(ciera.library_path()):
+        from lossless_bf16_tensor_exp_amd import build
+        build.build()
+    return ciera.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "ciera.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([a-z_][a-z0-9_]*)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for f in ("zip3_encode", "zip3_decode", "ciera_encode", "ciera_decode"):
+        assert f in names
+    assert len(names) >= 12
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+@pytest.mark.parametrize("B", [0, 64, 128, 512, 65536])
+def test_size_queries_match_the_oracle(lib, B):
+    for n in [0, 1, 7, 8, 100, 65535, 65536, 65537, 10 ** 6, 3 * 65536 + 5, 104891392, 10 ** 9]:
+        want = oracle.max_encoded_size(n, B)
+        got = lib.zip3_max_encoded_size(n) if B == 0 else lib.ciera_max_encoded_size(n, B)
+        assert got == want, (n, B)
+        ws = lib.zip3_workspace_size(n) if B == 0 else lib.ciera_workspace_size(n, B)
+        assert ws >= 256 and ws % 256 == 0
+
+
+def test_invalid_sizes_and_blocks(lib):
+    assert lib.ciera_max_encoded_size(1000, 100) == 0
+    assert lib.ciera_max_encoded_size(1000, 32) == 0
+    assert lib.ciera_max_encoded_size(1000, 131072) == 0
+    assert lib.zip3_max_encoded_size((1 << 40) + 1) == 0
+    assert lib.ciera_workspace_size(1000, 48) == 0
+
+
+def test_argument_errors_return_before_any_launch(lib):
+    # every case fails a host-side check, so no HIP call is made
+    big = (1 << 40) + 1
+    p = ctypes.c_void_p(16 * 1024)  # never dereferenced
+    assert lib.zip3_encode(p, big, p, 1 << 50, p, 1 << 30, p, None) == 1
+    assert lib.zip3_encode(None, 10, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.zip3_encode(p, 10, p, 10, p, 1 << 20, p, None) == 2
+    assert lib.zip3_encode(p, 10, p, 1 << 20, p, 10, p, None) == 3
+    assert lib.ciera_encode(p, 10, 100, p, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode(p, 10, 0, p, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.zip3_encode_ex(p, 10, p, 1 << 20, p, 1 << 20, p, 250, None) == 1
+    assert lib.ciera_decode(p, 1 << 20, p, 10, 96, p, p, 1 << 20, None) == 1
+    assert lib.zip3_decode(ctypes.c_void_p(16 * 1024 + 8), 1 << 20, p, 10, p, 1 << 20, None) == 1
+    assert lib.ciera_read_error(None, None) == 1
+
+
+def test_status_strings(lib):
+    assert lib.ciera_status_string(0) == b"ok"
+    assert lib.ciera_status_string(5) == b"malformed stream"
+    assert lib.ciera_status_string(99) == b"unknown status"
