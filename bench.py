@@ -110,58 +110,66 @@ def main() -> int:
         send, recv = e_prev.clone(), e_prev.clone()
     stream = torch.cuda.current_stream()
 
-    def encode(x):
-        if mode == "zip3":
-            ciera.zip3_encode(x, out, ws_e, size, -1, stream)
-        else:
-            ciera.ciera_encode(x, B, send, out, ws_e, size, -1, stream)
+    # Pre-bound C calls (argument marshalling done once, outside the timing).
+    if mode == "zip3":
+        enc = [ciera.bind("zip3_encode_ex", xs[k], n, out, cap, ws_e, wsz, size, -1, stream=stream) for k in (0, 1)]
+    else:
+        enc = [ciera.bind("ciera_encode_ex", xs[k], n, B, send, out, cap, ws_e, wsz, size, -1, stream=stream)
+               for k in (0, 1)]
 
-    def decode(in_size):
+    def dec_for(in_size):
         if mode == "zip3":
-            ciera.zip3_decode(out, in_size, y, ws_d, stream)
-        else:
-            ciera.ciera_decode(out, in_size, y, B, recv, ws_d, stream)
+            return ciera.bind("zip3_decode", out, in_size, y, n, ws_d, wsz, stream=stream)
+        return ciera.bind("ciera_decode", out, in_size, y, n, B, recv, ws_d, wsz, stream=stream)
 
-    # Stream sizes per input are fixed, so decode can take the size learned
-    # in warm-up without a host sync inside the timed loop.
-    sizes = {}
-    for i in range(2):
-        k = (i + 1) % 2 if mode != "zip3" else 0
-        encode(xs[k])
+    # Stream sizes per input are fixed, so decode takes the size learned in
+    # the first steps without a host sync inside the timed loops.  Step s
+    # encodes input (s+1) % 2 against caches holding the other input.
+    sizes, dec = {}, {}
+    order = [1, 0] if mode != "zip3" else [0, 0]
+    for k in order:
+        enc[k]()
         torch.cuda.synchronize()
         sizes[k] = int(size.item())
-        decode(sizes[k])
+        dec[k] = dec_for(sizes[k])
+        dec[k]()
         torch.cuda.synchronize()
         assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
-    # after these two steps the caches hold pair[0]'s exponents again
-    for w in range(args.warmup):
-        k = (w + 1) % 2 if mode != "zip3" else 0
-        encode(xs[k])
-        decode(sizes[k])
-        if mode != "zip3":
-            k2 = 1 - k
-            encode(xs[k2])
-            decode(sizes[k2])
+
+    def step(s):
+        k = (s + 1) % 2 if mode != "zip3" else 0
+        enc[k]()
+        dec[k]()
+
+    for w in range(2 * args.warmup):
+        step(w)
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # Pass 1, the headline number: K steps back to back, nothing between them.
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(K):
-        k = (s + 1) % 2 if mode != "zip3" else 0
-        ev[s][0].record(stream)
-        encode(xs[k])
-        ev[s][1].record(stream)
-        decode(sizes[k])
-        ev[s][2].record(stream)
+        step(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
+    # Pass 2, per-call durations: HIP events around every encode and decode
+    # call on the stream the kernels run on (the event markers add small gaps,
+    # so this pass is not the headline).
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    for s in range(K):
+        k = (K + s + 1) % 2 if mode != "zip3" else 0  # continues the alternation of pass 1
+        ev[s][0].record(stream)
+        enc[k]()
+        ev[s][1].record(stream)
+        dec[k]()
+        ev[s][2].record(stream)
+    torch.cuda.synchronize()
     enc_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]
     dec_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
     if args.verify:
-        klast = K % 2 if mode != "zip3" else 0
+        klast = (2 * K) % 2 if mode != "zip3" else 0  # input of the last step, index 2K-1
         assert torch.equal(y, xs[klast]), "round trip failed"
 
     in_bytes = 2 * n

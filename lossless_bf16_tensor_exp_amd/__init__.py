@@ -31,6 +31,7 @@ __all__ = [
     "CieraError", "library_path", "load_library",
     "zip3_max_encoded_size", "ciera_max_encoded_size", "zip3_workspace_size", "ciera_workspace_size",
     "zip3_encode", "zip3_decode", "ciera_encode", "ciera_decode", "ciera_read_error", "ciera_status_string",
+    "bind",
     "CHUNK",
 ]
 
@@ -187,6 +188,28 @@ def ciera_decode(inp, in_size: int, y, B: int, prev_exp, ws, stream=None) -> Non
     st = lib.ciera_decode(_ptr(inp), in_size, _ptr(y), y.numel(), B, _ptr(prev_exp), _ptr(ws), ws.numel(),
                           _stream(stream))
     _raise(st, "ciera_decode")
+
+
+def bind(name: str, *args, stream=None):
+    """Pre-marshal one entry point's arguments and return a zero-argument
+    callable that only makes the C call (for tight launch loops and
+    benchmarks).  ``args`` are the tensors and integers in the C order,
+    without the stream; tensors become device pointers, integers stay."""
+    lib = load_library()
+    fn = getattr(lib, name)
+    cargs = []
+    for a in args:
+        if hasattr(a, "data_ptr"):
+            cargs.append(ctypes.c_void_p(a.data_ptr()) if a.numel() else None)
+        else:
+            cargs.append(a)
+    cargs.append(_stream(stream))
+
+    def call():
+        st = fn(*cargs)
+        if st != 0:
+            raise CieraError(st, name)
+    return call
 
 
 def ciera_read_error(ws, stream=None) -> int:

@@ -116,8 +116,16 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
 // ------------------------------------------------------------------ device helpers
 __device__ inline uint32_t lane_id() { return threadIdx.x & 63u; }
 
-// Eight BF16 patterns of unit u (first value index `first`), `cnt` of them
-// real; the rest read as zero.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// v_perm_b32: byte i of the result is byte sel_i of {b (0..3), a (4..7)};
+// selector 0x0C yields a zero byte.
+__device__ inline uint32_t perm(uint32_t a, uint32_t b, uint32_t sel) { return __builtin_amdgcn_perm(a, b, sel); }
+// bits of a where mask is set, bits of b elsewhere (v_bfi_b32)
+__device__ inline uint32_t bfi(uint32_t mask, uint32_t a, uint32_t b) { return (mask & a) | (~mask & b); }
+
+// Eight BF16 patterns (a "unit"): w[i] holds value 2i in its low and value
+// 2i+1 in its high half.  Values past the data read as zero.
 struct Unit {
   uint32_t w[4];
 };
@@ -145,50 +153,116 @@ __device__ inline void store_unit(uint16_t* __restrict__ y, uint64_t first, uint
   }
 }
 
-__device__ inline uint64_t load_bytes8(const uint8_t* __restrict__ p, uint32_t cnt) {
-  if (cnt == 8u) return *reinterpret_cast<const uint64_t*>(p);
-  uint64_t v = 0;
-  for (uint32_t k = 0; k < cnt; k++) v |= uint64_t(p[k]) << (8u * k);
+__device__ inline uint2 load_bytes8(const uint8_t* __restrict__ p, uint32_t cnt) {
+  if (cnt == 8u) return *reinterpret_cast<const uint2*>(p);
+  uint2 v = make_uint2(0u, 0u);
+  for (uint32_t k = 0; k < cnt; k++) {
+    if (k < 4u)
+      v.x |= uint32_t(p[k]) << (8u * k);
+    else
+      v.y |= uint32_t(p[k]) << (8u * (k - 4u));
+  }
   return v;
 }
 
-__device__ inline void store_bytes8(uint8_t* __restrict__ p, uint32_t cnt, uint64_t v) {
+__device__ inline void store_bytes8(uint8_t* __restrict__ p, uint32_t cnt, uint2 v) {
   if (cnt == 8u) {
-    *reinterpret_cast<uint64_t*>(p) = v;
+    *reinterpret_cast<uint2*>(p) = v;
   } else {
-    for (uint32_t k = 0; k < cnt; k++) p[k] = uint8_t(v >> (8u * k));
+    for (uint32_t k = 0; k < cnt; k++) p[k] = uint8_t((k < 4u ? v.x : v.y) >> (8u * (k & 3u)));
   }
 }
 
-__device__ inline uint32_t value_bits(const Unit& u, uint32_t k) {
-  return (u.w[k >> 1] >> (16u * (k & 1u))) & 0xFFFFu;
+// Exponent fields as 16-bit lanes: bits 0..7 = exponent of the low value,
+// bits 16..23 = exponent of the high value.
+__device__ inline uint32_t exp_pair(uint32_t w) { return (w >> 7) & 0x00FF00FFu; }
+
+// Exponent bytes of the unit: byte k of {lo, hi} = exponent of value k.
+__device__ inline uint2 unit_exponents(const Unit& u) {
+  return make_uint2(perm(exp_pair(u.w[1]), exp_pair(u.w[0]), 0x06040200u),
+                    perm(exp_pair(u.w[3]), exp_pair(u.w[2]), 0x06040200u));
 }
 
-// Exponent fields of the unit's 8 values, byte k = exponent of value k.
-__device__ inline uint64_t unit_exponents(const Unit& u) {
-  uint64_t e = 0;
+// Sign+mantissa bytes: byte k = (sign << 7) | mantissa of value k.
+__device__ inline uint2 unit_sm(const Unit& u) {
+  uint32_t s[4];
 #pragma unroll
-  for (uint32_t k = 0; k < 8u; k++) e |= uint64_t((value_bits(u, k) >> 7) & 0xFFu) << (8u * k);
-  return e;
+  for (int i = 0; i < 4; i++) s[i] = bfi(0x00800080u, u.w[i] >> 8, u.w[i]);
+  return make_uint2(perm(s[1], s[0], 0x06040200u), perm(s[3], s[2], 0x06040200u));
 }
 
-// Sign+mantissa bytes, byte k = (sign << 7) | mantissa of value k.
-__device__ inline uint64_t unit_sm(const Unit& u) {
-  uint64_t s = 0;
+// 3-bit codes of an exponent pair as 16-bit lanes: min(E - E0 + 1, 8) with
+// 16-bit wrap-around, i.e. 1..7 inside the window, 0 or 8 outside.  Bits
+// 0..2 of each lane are the code (8 has code bits 000).
+__device__ inline uint32_t code_pair(uint32_t e, uint32_t bias /* (1 - E0) in both lanes */) {
+  const u16x2 s = __builtin_bit_cast(u16x2, e) + __builtin_bit_cast(u16x2, bias);
+  const u16x2 eight = {8, 8};
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_min(s, eight));
+}
+
+// The three code planes of a unit, byte b = plane b (bit k = bit b of the
+// code of value k), from the four code pairs.
+__device__ inline uint32_t unit_planes(const uint32_t (&c)[4]) {
+  // nibble i = code of value 2i, nibble 4+i = code of value 2i+1
+  const uint32_t q = c[0] | (c[1] << 4) | (c[2] << 8) | (c[3] << 12);
+  uint32_t planes = 0;
 #pragma unroll
-  for (uint32_t k = 0; k < 8u; k++) {
-    const uint32_t v = value_bits(u, k);
-    s |= uint64_t(((v >> 8) & 0x80u) | (v & 0x7Fu)) << (8u * k);
+  for (uint32_t b = 0; b < 3u; b++) {
+    uint32_t t = (q >> b) & 0x11111111u;  // even values at 4i, odd values at 16+4i
+    t = (t | (t >> 15)) & 0x3333u;       // (even, odd) pairs at 4i, 4i+1
+    t = (t | (t >> 2)) & 0x0F0Fu;
+    t = (t | (t >> 4)) & 0x00FFu;
+    planes |= t << (8u * b);
   }
-  return s;
+  return planes;
 }
 
-// Exact FP64 value of a finite BF16 pattern, built from its integer fields.
-__device__ inline double bf16_value(uint32_t v) {
-  const uint32_t e = (v >> 7) & 0xFFu;
-  const uint32_t m = v & 0x7Fu;
-  const double mag = e ? ldexp(double(128u + m), int(e) - 134) : ldexp(double(m), -133);
-  return (v & 0x8000u) ? -mag : mag;
+// Inverse of unit_planes for one half: bits k (k < 4) of the 4-bit value x
+// spread to bit 0 of byte k (the multiply's cross terms never land on a
+// multiple of 8).
+__device__ inline uint32_t spread4(uint32_t x) { return (x * 0x00204081u) & 0x01010101u; }
+
+// Code bytes (0..7) of a unit from its three plane bytes: lo = values 0..3,
+// hi = values 4..7.
+__device__ inline uint2 codes_from_planes(uint32_t p0, uint32_t p1, uint32_t p2) {
+  const uint32_t lo = spread4(p0 & 15u) | (spread4(p1 & 15u) << 1) | (spread4(p2 & 15u) << 2);
+  const uint32_t hi = spread4(p0 >> 4) | (spread4(p1 >> 4) << 1) | (spread4(p2 >> 4) << 2);
+  return make_uint2(lo, hi);
+}
+
+// Exponent bytes E0 + code - 1 for code bytes 1..7; code-0 bytes give junk
+// that the escape pass replaces.  No carry or borrow crosses a byte: with
+// E0 >= 1 every byte sum is at most 7 + 248; with E0 = 0 each byte is first
+// lifted by 0x80 so the subtraction cannot borrow.
+__device__ inline uint32_t exps_from_codes(uint32_t codes, uint32_t e0) {
+  return e0 ? codes + (e0 - 1u) * 0x01010101u : ((codes | 0x80808080u) - 0x01010101u) & 0x7F7F7F7Fu;
+}
+
+// Two output values from byte pairs: h = sm_a | E_a << 8 | sm_b << 16 | E_b << 24.
+__device__ inline uint32_t join_pair(uint32_t h) {
+  // bits 0..6 mantissa from sm, 7..14 exponent, 15 sign (sm bit 7)
+  return bfi(0x007F007Fu, h, bfi(0x80008000u, h << 8, h >> 1));
+}
+
+__device__ inline Unit unit_join(uint2 sm, uint2 e) {
+  Unit o;
+  o.w[0] = join_pair(perm(e.x, sm.x, 0x05010400u));
+  o.w[1] = join_pair(perm(e.x, sm.x, 0x07030602u));
+  o.w[2] = join_pair(perm(e.y, sm.y, 0x05010400u));
+  o.w[3] = join_pair(perm(e.y, sm.y, 0x07030602u));
+  return o;
+}
+
+__device__ inline uint32_t byte_of(uint2 v, uint32_t k) { return ((k < 4u ? v.x : v.y) >> (8u * (k & 3u))) & 0xFFu; }
+
+__device__ inline uint2 set_byte(uint2 v, uint32_t k, uint32_t b) {
+  const uint32_t sh = 8u * (k & 3u);
+  const uint32_t m = ~(0xFFu << sh);
+  if (k < 4u)
+    v.x = (v.x & m) | (b << sh);
+  else
+    v.y = (v.y & m) | (b << sh);
+  return v;
 }
 
 __device__ inline uint32_t wave_incl_scan(uint32_t v) {
@@ -207,6 +281,12 @@ __device__ inline double wave_sum(double v) {
   return v;
 }
 
+__device__ inline uint64_t wave_sum_u64(uint64_t v) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+  return v;
+}
+
 __device__ inline uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
@@ -216,7 +296,7 @@ __device__ inline uint32_t wave_sum_u32(uint32_t v) {
 // Escape positions: each thread holds kUnitsPerThread counts (one per unit,
 // 0..8), units ordered (j, wave, lane).  On return base[j] is the number of
 // escapes in all earlier units of the chunk and the function returns the
-// chunk total.  Needs a barrier-safe call by every thread of the workgroup.
+// chunk total.  Every thread of the workgroup must call it.
 __device__ inline uint32_t chunk_escape_scan(const uint32_t (&cnt)[kUnitsPerThread],
                                              uint32_t (&base)[kUnitsPerThread],
                                              uint32_t* s_tot /* kUnitsPerThread*kWaves + 1 */) {
@@ -253,6 +333,23 @@ __device__ inline uint32_t chunk_escape_scan(const uint32_t (&cnt)[kUnitsPerThre
 }
 
 // ------------------------------------------------------------------ k_stats
+// FP64 value of a BF16 pattern held in the top half of a float: BF16 -> FP32
+// is exact (denormals are kept), FP32 -> FP64 is exact.
+__device__ inline double widen_hi(uint32_t hi_bits) { return double(__uint_as_float(hi_bits)); }
+
+// Partial sums of one unit's finite values (the checked path).
+__device__ inline void stats_checked(const Unit& v, uint32_t cnt, double shift, double& s1, double& s2,
+                                     uint32_t& nf) {
+  for (uint32_t k = 0; k < cnt; k++) {
+    const uint32_t b = (v.w[k >> 1] >> (16u * (k & 1u))) & 0xFFFFu;
+    if (((b >> 7) & 0xFFu) == 0xFFu) continue;
+    const double d = widen_hi(b << 16) - shift;
+    s1 += d;
+    s2 = fma(d, d, s2);
+    nf++;
+  }
+}
+
 template <bool kCiera>
 __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
                                                     uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
@@ -266,37 +363,57 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
   const uint32_t nunits = (nc + 7u) / 8u;
   if (kCiera && tid < kBitmapWords) s_bits[tid] = 0u;
   const uint32_t first = x[0];
-  const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? bf16_value(first) : 0.0;
+  const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
   __syncthreads();
 
+  // Fast path: no finite test per value.  A non-finite input makes the
+  // thread's sums non-finite (squares of finite BF16 values cannot
+  // overflow FP64), and the thread then redoes its units on the checked path.
   double s1 = 0.0, s2 = 0.0;
   uint32_t nf = 0;
 #pragma unroll
   for (uint32_t j = 0; j < kUnitsPerThread; j++) {
     const uint32_t u = j * kThreads + tid;
-    if (u >= nunits) break;
-    const uint32_t cnt = min(8u, nc - 8u * u);
-    const uint64_t at = start + 8ull * u;
-    const Unit v = load_unit(x, at, cnt);
+    if (u < nunits) {
+      const uint32_t cnt = min(8u, nc - 8u * u);
+      const uint64_t at = start + 8ull * u;
+      const Unit v = load_unit(x, at, cnt);
+      if (cnt == 8u) {
 #pragma unroll
-    for (uint32_t k = 0; k < 8u; k++) {
-      const uint32_t b = value_bits(v, k);
-      if (k < cnt && ((b >> 7) & 0xFFu) != 0xFFu) {
-        const double d = bf16_value(b) - shift;
-        s1 += d;
-        s2 = fma(d, d, s2);
-        nf++;
+        for (int i = 0; i < 4; i++) {
+          const double lo = widen_hi(v.w[i] << 16) - shift;
+          const double hi = widen_hi(v.w[i] & 0xFFFF0000u) - shift;
+          s1 += lo;
+          s2 = fma(lo, lo, s2);
+          s1 += hi;
+          s2 = fma(hi, hi, s2);
+        }
+        nf += 8u;
+      } else {
+        stats_checked(v, cnt, shift, s1, s2, nf);
+      }
+      if (kCiera) {
+        const uint2 e = unit_exponents(v);
+        const uint2 old = load_bytes8(cache + at, cnt);
+        const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
+        const uint64_t diff = ((uint64_t(e.y ^ old.y) << 32) | (e.x ^ old.x)) & keep;
+        if (diff) {
+          store_bytes8(cache + at, cnt, e);
+          const uint32_t blk = (8u * u) >> log2B;
+          atomicOr(&s_bits[blk >> 5], 1u << (blk & 31u));
+        }
       }
     }
-    if (kCiera) {
-      const uint64_t e = unit_exponents(v);
-      const uint64_t old = load_bytes8(cache + at, cnt);
-      const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
-      if ((e ^ old) & keep) {
-        store_bytes8(cache + at, cnt, e);
-        const uint32_t blk = (8u * u) >> log2B;
-        atomicOr(&s_bits[blk >> 5], 1u << (blk & 31u));
-      }
+  }
+  if (!(__builtin_isfinite(s1) && __builtin_isfinite(s2))) {
+    s1 = 0.0;
+    s2 = 0.0;
+    nf = 0;
+    for (uint32_t j = 0; j < kUnitsPerThread; j++) {
+      const uint32_t u = j * kThreads + tid;
+      if (u >= nunits) break;
+      const uint32_t cnt = min(8u, nc - 8u * u);
+      stats_checked(load_unit(x, start + 8ull * u, cnt), cnt, shift, s1, s2, nf);
     }
   }
   s1 = wave_sum(s1);
@@ -332,19 +449,26 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
 }
 
 // ------------------------------------------------------------------ k_plan
+// Window base: E0 = 127 + k for the largest k with var >= K0 * 4^k, clamped
+// to [0, 249]; 0 without a finite spread.  The comparisons are exact: each
+// threshold is a power of two times K0.
 __device__ inline uint32_t window_base(double var, uint64_t nf) {
   if (nf < 2u || !(var > 0.0)) return 0u;
-  uint32_t e0 = 0u;
-  for (int k = -127; k <= 122; k++)
-    if (var >= ldexp(kK0, 2 * k)) e0 = uint32_t(127 + k);
-  return e0;
+  // K0 lies in [2^9, 2^10), so var >= K0 * 4^k holds for k = floor((t-11)/2)
+  // with t = ilogb(var), and fails for k > (t-8)/2: start low, step up.
+  const int t = ilogb(var);
+  int k = (t - 11 >= 0) ? (t - 11) / 2 : -((12 - t) / 2);
+  if (k < -128) k = -128;
+  if (k > 122) k = 122;  // var >= K0 * 4^122 already
+  while (k < 122 && var >= ldexp(kK0, 2 * (k + 1))) k++;
+  return k < -127 ? 0u : uint32_t(127 + k);
 }
 
 __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks, uint32_t B, int e0_override,
                                                    uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
                                                    Ws ws) {
-  __shared__ double s_s1[kThreads], s_s2[kThreads];
-  __shared__ uint64_t s_nf[kThreads], s_nch[kThreads];
+  __shared__ double s_s1[kWaves], s_s2[kWaves];
+  __shared__ uint64_t s_nf[kWaves], s_nch[kWaves];
   const uint32_t tid = threadIdx.x;
   double a = 0.0, b = 0.0;
   uint64_t m = 0, q = 0;
@@ -355,29 +479,33 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
     m += p.nf;
     q += p.nch;
   }
-  s_s1[tid] = a;
-  s_s2[tid] = b;
-  s_nf[tid] = m;
-  s_nch[tid] = q;
-  __syncthreads();
-  for (uint32_t h = kThreads / 2u; h >= 1u; h >>= 1) {
-    if (tid < h) {
-      s_s1[tid] += s_s1[tid + h];
-      s_s2[tid] += s_s2[tid + h];
-      s_nf[tid] += s_nf[tid + h];
-      s_nch[tid] += s_nch[tid + h];
-    }
-    __syncthreads();
+  a = wave_sum(a);
+  b = wave_sum(b);
+  m = wave_sum_u64(m);
+  q = wave_sum_u64(q);
+  if (lane_id() == 0u) {
+    s_s1[tid >> 6] = a;
+    s_s2[tid >> 6] = b;
+    s_nf[tid >> 6] = m;
+    s_nch[tid >> 6] = q;
   }
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
   const uint64_t base = table_end(nchunks);
   // zero the table's padding words (entries past nchunks)
   for (uint64_t i = nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
+  __syncthreads();
   if (tid == 0) {
-    const uint64_t nf = s_nf[0];
+    double s1 = 0.0, s2 = 0.0;
+    uint64_t nf = 0, nch = 0;
+    for (uint32_t w = 0; w < kWaves; w++) {
+      s1 += s_s1[w];
+      s2 += s_s2[w];
+      nf += s_nf[w];
+      nch += s_nch[w];
+    }
     double var = 0.0;
     if (nf >= 2u) {
-      var = (s_s2[0] - s_s1[0] * s_s1[0] / double(nf)) / double(nf - 1u);
+      var = (s2 - s1 * s1 / double(nf)) / double(nf - 1u);
       if (!(var > 0.0)) var = 0.0;
     }
     const uint32_t e0 = (e0_override >= 0) ? uint32_t(e0_override) : window_base(var, nf);
@@ -391,7 +519,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
     h[1] = n;
     h[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
     h[3] = nchunks;
-    h[5] = s_nch[0];
+    h[5] = nch;
     for (int i = 7; i < 16; i++) h[i] = 0u;
     if (nchunks == 0u) {
       h[4] = base;
@@ -425,6 +553,52 @@ __device__ inline void zero_fill(uint8_t* __restrict__ p, uint64_t from, uint64_
   for (uint64_t i = from + threadIdx.x; i < to; i += kThreads) p[i] = 0u;
 }
 
+// Decoupled look-back, run by one whole wave: publish this chunk's size as an
+// aggregate, then sum predecessors' published sizes 64 at a time until one
+// holds an inclusive prefix; publish the inclusive prefix.  Predecessors
+// always hold earlier tickets, so their workgroups are already running and
+// publish their aggregates without waiting on anything.  Returns the byte
+// offset of this chunk relative to the first chunk; sets *err if a wait
+// exceeds kSpinLimit polls.
+__device__ inline uint64_t look_back(uint64_t* __restrict__ status, uint32_t c, uint64_t size, uint32_t* err) {
+  const uint32_t lane = lane_id();
+  if (c == 0u) {
+    if (lane == 0u)
+      __hip_atomic_store(&status[0], kFlagInclusive | size, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+    return 0u;
+  }
+  if (lane == 0u)
+    __hip_atomic_store(&status[c], kFlagAggregate | size, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  uint64_t prefix = 0;
+  int64_t top = int64_t(c) - 1;  // closest predecessor not yet summed
+  uint32_t spins = 0;
+  while (true) {
+    const int64_t k = top - int64_t(lane);
+    const uint64_t s = (k >= 0) ? __hip_atomic_load(&status[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
+                                : kFlagInclusive;  // before chunk 0: an empty inclusive prefix
+    const uint64_t flag = s & ~kValueMask;
+    if (__ballot(flag == 0u) != 0u) {
+      if (++spins > kSpinLimit) {
+        *err = CIERA_ERR_INTERNAL;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    const uint64_t incl = __ballot(flag == kFlagInclusive);
+    if (incl != 0u) {
+      const uint32_t first = uint32_t(__builtin_ctzll(incl));  // closest inclusive predecessor
+      prefix += wave_sum_u64(lane <= first ? (s & kValueMask) : 0u);
+      break;
+    }
+    prefix += wave_sum_u64(s & kValueMask);
+    top -= 64;
+  }
+  if (lane == 0u)
+    __hip_atomic_store(&status[c], kFlagInclusive | (prefix + size), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  return prefix;
+}
+
 template <bool kCiera>
 __global__ __launch_bounds__(kThreads) void k_write(const uint16_t* __restrict__ x, uint64_t n, uint64_t nchunks,
                                                     uint32_t log2B, uint8_t* __restrict__ out,
@@ -444,6 +618,7 @@ __global__ __launch_bounds__(kThreads) void k_write(const uint16_t* __restrict__
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
   const uint32_t e0 = ws.ctrl->e0;
+  const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
 
   uint32_t nch = 0;
   if (kCiera) {
@@ -460,92 +635,68 @@ __global__ __launch_bounds__(kThreads) void k_write(const uint16_t* __restrict__
     nch = s_rank[kBitmapWords - 1] + __popc(s_bits[kBitmapWords - 1]);
   }
 
-  // Load the chunk and derive per-unit fields.
+  // Load the chunk; per unit: the three plane bytes and the escape mask.
   Unit v[kUnitsPerThread];
   uint32_t cnt[kUnitsPerThread], base[kUnitsPerThread];
-  uint32_t planes[kUnitsPerThread];  // p0 | p1 << 8 | p2 << 16, escape mask << 24
+  uint32_t planes[kUnitsPerThread];  // p0 | p1 << 8 | p2 << 16 | escape mask << 24
 #pragma unroll
   for (uint32_t j = 0; j < kUnitsPerThread; j++) {
     const uint32_t u = j * kThreads + tid;
     cnt[j] = 0u;
     planes[j] = 0u;
+    v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
     if (u < nunits) {
       const uint32_t valid = min(8u, nc - 8u * u);
       v[j] = load_unit(x, start + 8ull * u, valid);
+    }
+  }
+#pragma unroll
+  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
+    const uint32_t u = j * kThreads + tid;
+    if (u < nunits) {
       bool coded = true;
       if (kCiera) {
         const uint32_t blk = (8u * u) >> log2B;
         coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
       }
       if (coded) {
+        const uint32_t valid = min(8u, nc - 8u * u);
         const uint32_t vmask = (valid == 8u) ? 0xFFu : ((1u << valid) - 1u);
-        uint32_t p0 = 0, p1 = 0, p2 = 0, em = 0;
+        uint32_t cp[4];
 #pragma unroll
-        for (uint32_t k = 0; k < 8u; k++) {
-          const uint32_t e = (value_bits(v[j], k) >> 7) & 0xFFu;
-          const uint32_t d = e - e0;
-          const uint32_t code = (d <= 6u) ? d + 1u : 0u;
-          p0 |= (code & 1u) << k;
-          p1 |= ((code >> 1) & 1u) << k;
-          p2 |= ((code >> 2) & 1u) << k;
-          em |= uint32_t(code == 0u) << k;
-        }
-        p0 &= vmask;
-        p1 &= vmask;
-        p2 &= vmask;
-        em &= vmask;
-        planes[j] = p0 | (p1 << 8) | (p2 << 16) | (em << 24) | 0u;
+        for (int i = 0; i < 4; i++) cp[i] = code_pair(exp_pair(v[j].w[i]), bias);
+        uint32_t p = unit_planes(cp) & (vmask * 0x010101u);
+        const uint32_t em = ~(p | (p >> 8) | (p >> 16)) & vmask;
+        planes[j] = p | (em << 24);
         cnt[j] = __popc(em);
       }
-    } else {
-      v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
     }
   }
   const uint32_t nesc = chunk_escape_scan(cnt, base, s_tot);
 
-  // Chunk size and offset (decoupled look-back over earlier chunks).
+  // Chunk size, then its offset by look-back over earlier chunks (wave 0).
   const uint64_t size = pad128(nc) + (kCiera ? 128u : 0u) +
                         3u * pad128(kCiera ? uint64_t(nch) * B / 8u : cdiv(nc, 8u)) + pad128(nesc);
-  if (tid == 0) {
+  if (tid < 64u) {
+    if (tid == 0)
+      atomicAdd(reinterpret_cast<unsigned long long*>(&ws.ctrl->esc_total), (unsigned long long)nesc);
     uint32_t err = 0u;
-    atomicAdd(reinterpret_cast<unsigned long long*>(&ws.ctrl->esc_total), (unsigned long long)nesc);
-    uint64_t prefix = 0;
-    if (c == 0u) {
-      __hip_atomic_store(&ws.status[c], kFlagInclusive | size, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      __hip_atomic_store(&ws.status[c], kFlagAggregate | size, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      int64_t k = int64_t(c) - 1;
-      uint32_t spins = 0;
-      while (k >= 0) {
-        const uint64_t s = __hip_atomic_load(&ws.status[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-        if ((s & ~kValueMask) == 0u) {
-          if (++spins > kSpinLimit) {
-            err = CIERA_ERR_INTERNAL;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-          continue;
-        }
-        prefix += s & kValueMask;
-        if ((s & ~kValueMask) == kFlagInclusive) break;
-        k--;
+    const uint64_t prefix = look_back(ws.status, c, size, &err);
+    if (tid == 0) {
+      const uint64_t begin = table_end(nchunks) + prefix;
+      s_begin = begin;
+      s_err = err;
+      ws.err[c] = err;
+      uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
+      table[c] = begin;
+      if (uint64_t(c) + 1u == nchunks) {
+        const uint64_t total = begin + size;
+        table[nchunks] = total;
+        uint64_t* h = reinterpret_cast<uint64_t*>(out);
+        h[4] = total;
+        h[6] = __hip_atomic_load(&ws.ctrl->esc_total, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+        *out_size = total;
       }
-      __hip_atomic_store(&ws.status[c], kFlagInclusive | (prefix + size), __ATOMIC_RELEASE,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-    const uint64_t begin = table_end(nchunks) + prefix;
-    s_begin = begin;
-    s_err = err;
-    ws.err[c] = err;
-    uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
-    table[c] = begin;
-    if (uint64_t(c) + 1u == nchunks) {
-      const uint64_t total = begin + size;
-      table[nchunks] = total;
-      uint64_t* h = reinterpret_cast<uint64_t*>(out);
-      h[4] = total;
-      h[6] = __hip_atomic_load(&ws.ctrl->esc_total, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      *out_size = total;
     }
   }
   __syncthreads();
@@ -557,7 +708,7 @@ __global__ __launch_bounds__(kThreads) void k_write(const uint16_t* __restrict__
   for (uint32_t j = 0; j < kUnitsPerThread; j++) {
     const uint32_t u = j * kThreads + tid;
     if (u >= nunits) continue;
-    *reinterpret_cast<uint64_t*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
+    *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
     bool coded = true;
     uint64_t pbyte = u;
     if (kCiera) {
@@ -574,12 +725,12 @@ __global__ __launch_bounds__(kThreads) void k_write(const uint16_t* __restrict__
       out[g.plane + 2u * g.plane_bytes + pbyte] = uint8_t(p >> 16);
       uint32_t em = p >> 24;
       if (em) {
-        const uint64_t e = unit_exponents(v[j]);
+        const uint2 e = unit_exponents(v[j]);
         uint64_t at = g.esc + base[j];
         while (em) {
           const uint32_t k = __builtin_ctz(em);
           em &= em - 1u;
-          out[at++] = uint8_t(e >> (8u * k));
+          out[at++] = uint8_t(byte_of(e, k));
         }
       }
     }
@@ -702,15 +853,15 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__
     return;
   }
 
-  uint64_t smv[kUnitsPerThread], ev[kUnitsPerThread];
+  uint2 smv[kUnitsPerThread], ev[kUnitsPerThread];
   uint32_t cnt[kUnitsPerThread], base[kUnitsPerThread], emask[kUnitsPerThread];
 #pragma unroll
   for (uint32_t j = 0; j < kUnitsPerThread; j++) {
     const uint32_t u = j * kThreads + tid;
     cnt[j] = 0u;
     emask[j] = 0u;
-    smv[j] = 0u;
-    ev[j] = 0u;
+    smv[j] = make_uint2(0u, 0u);
+    ev[j] = make_uint2(0u, 0u);
     if (u >= nunits) continue;
     const uint32_t valid = min(8u, nc - 8u * u);
     smv[j] = load_bytes8(in + g.sm + 8ull * u, valid);
@@ -728,13 +879,8 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__
       const uint32_t p1 = in[g.plane + g.plane_bytes + pbyte];
       const uint32_t p2 = in[g.plane + 2u * g.plane_bytes + pbyte];
       const uint32_t vmask = (valid == 8u) ? 0xFFu : ((1u << valid) - 1u);
-      uint64_t e = 0;
-#pragma unroll
-      for (uint32_t k = 0; k < 8u; k++) {
-        const uint32_t code = ((p0 >> k) & 1u) | (((p1 >> k) & 1u) << 1) | (((p2 >> k) & 1u) << 2);
-        e |= uint64_t(code ? e0 + code - 1u : 0u) << (8u * k);
-      }
-      ev[j] = e;
+      const uint2 codes = codes_from_planes(p0, p1, p2);
+      ev[j] = make_uint2(exps_from_codes(codes.x, e0), exps_from_codes(codes.y, e0));
       emask[j] = ~(p0 | p1 | p2) & vmask;
       cnt[j] = __popc(emask[j]);
     } else {
@@ -751,28 +897,15 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__
     const uint32_t u = j * kThreads + tid;
     if (u >= nunits) continue;
     const uint32_t valid = min(8u, nc - 8u * u);
-    uint64_t e = ev[j];
+    uint2 e = ev[j];
     uint32_t em = emask[j];
     uint64_t at = g.esc + base[j];
     while (em) {
       const uint32_t k = __builtin_ctz(em);
       em &= em - 1u;
-      e |= uint64_t(in[at++]) << (8u * k);
+      e = set_byte(e, k, in[at++]);
     }
-    Unit o;
-#pragma unroll
-    for (uint32_t k2 = 0; k2 < 4u; k2++) {
-      uint32_t w = 0;
-#pragma unroll
-      for (uint32_t h = 0; h < 2u; h++) {
-        const uint32_t k = 2u * k2 + h;
-        const uint32_t sm = uint32_t(smv[j] >> (8u * k)) & 0xFFu;
-        const uint32_t ex = uint32_t(e >> (8u * k)) & 0xFFu;
-        w |= (((sm & 0x80u) << 8) | (ex << 7) | (sm & 0x7Fu)) << (16u * h);
-      }
-      o.w[k2] = w;
-    }
-    store_unit(y, start + 8ull * u, valid, o);
+    store_unit(y, start + 8ull * u, valid, unit_join(smv[j], e));
     if (kCiera) {
       const uint32_t blk = (8u * u) >> log2B;
       if ((s_bits[blk >> 5] >> (blk & 31u)) & 1u) store_bytes8(cache + start + 8ull * u, valid, e);

@@ -88,6 +88,20 @@ def test_constant_and_nonfinite_tensors():
         check_roundtrip(s, x)
 
 
+def test_extreme_magnitudes():
+    # variance near the top of the BF16 range clamps the window base at 249;
+    # tiny tensors (subnormals, smallest normals) clamp it at 0
+    rng = np.random.default_rng(12)
+    big = np.where(rng.random(100000) < 0.5, 0x7F7F, 0xFF7F).astype(np.uint16)
+    s, st = check_encode(big)
+    assert st["E0"] == 249
+    check_roundtrip(s, big)
+    tiny = rng.integers(0, 0x0100, size=100000).astype(np.uint16) | (rng.integers(0, 2, 100000).astype(np.uint16) << 15)
+    s, st = check_encode(tiny)
+    assert st["E0"] == 0
+    check_roundtrip(s, tiny)
+
+
 def test_deterministic_and_stream_independent():
     rng = np.random.default_rng(77)
     x = wl.f32_to_bf16(rng.standard_normal(5_000_000, dtype=np.float32) * np.float32(0.02))

@@ -77,6 +77,9 @@ def test_window_base_degenerate_cases():
     assert oracle.window_base(1.0, 0) == 0
     assert oracle.window_base(float.fromhex("0x1p-1000"), 5) == 0
     assert oracle.window_base(1e300, 5) == 249
+    # the largest BF16 variance (values of +-max) lies above K0 * 4^122
+    mx = oracle.bf16_value(0x7F7F)
+    assert mx * mx > brute.K0 * 4.0 ** 122 and oracle.window_base(mx * mx, 2) == 249
 
 
 def test_window_thresholds_exactly():
