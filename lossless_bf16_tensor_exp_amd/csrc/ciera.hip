@@ -1,29 +1,39 @@
 // ciera.hip -- HIP kernels and C ABI of the lossless BF16 codec, gfx950.
 //
-// Encode is three kernels on the caller's stream:
-//   k_stats  one workgroup per 65,536-value chunk: FP64 partial sums for the
-//            tensor's variance (ZipCCL research digest, section 3.1: sigma
-//            from one standard-deviation pass) and, in ciera mode, the
-//            changed-block bitmap against the sender's exponent cache plus the
-//            cache update (CIERA page, section 3.1).
-//   k_plan   one workgroup: reduces the partials in a fixed order, picks the
-//            window base E0 (integer nearest x_opt = log2 sigma + 0.5 log2(14
-//            ln2 / 16383), section 3.1 of the digest, as var >= K0 4^k), and
-//            writes the header's size-independent fields.
-//   k_write  one workgroup per chunk: splits values into sign+mantissa bytes
-//            and 3-bit codes, compacts escapes with wave scans, finds its
-//            chunk's stream offset with a decoupled look-back over the
-//            preceding chunks' sizes, and writes the 128-byte-aligned
-//            sections (digest, section 3.1 last paragraph, and Figure 1).
-// Decode is one kernel, k_decode, one workgroup per chunk; chunks are
-// independent because the chunk table holds every offset.
+// Encode is four kernels on the caller's stream:
+//   k_stats   one workgroup per 65,536-value chunk, one pass over the input:
+//             FP64 partial sums for the tensor's variance (ZipCCL research
+//             digest, section 3.1: sigma from one standard-deviation pass);
+//             in ciera mode the changed-block bitmap against the sender's
+//             exponent cache and the cache update (CIERA page, section 3.1);
+//             and an exponent histogram of the values to be coded, per
+//             quarter chunk ("part").
+//   k_plan    one workgroup: reduces the partial sums in a fixed order and
+//             picks the window base E0 (integer nearest x_opt = log2 sigma +
+//             0.5 log2(14 ln2 / 16383), digest section 3.1, evaluated as
+//             var >= K0 4^k); writes the header's size-independent fields.
+//   k_layout  one thread per chunk: the escape count of each part is the
+//             number of coded values outside [E0, E0+6], read off the
+//             histogram; chunk sizes follow exactly, and a decoupled
+//             look-back over groups of chunks turns them into the chunk
+//             table (the size exchange of the digest's Figure 1, done on one
+//             GPU).
+//   k_write   one workgroup per part, no synchronisation with any other:
+//             splits values into sign+mantissa bytes and 3-bit codes and
+//             writes the 128-byte-aligned sections at offsets k_layout fixed
+//             (digest, section 3.1 last paragraph).
+// Decode is one kernel, k_decode, one workgroup per part; parts are
+// independent because the chunk table holds every chunk offset and a part
+// finds its first escape by counting code-0 slots in the planes before it.
 //
 // Work mapping: a "unit" is 8 consecutive values (one 16-byte load).  A chunk
-// has 8192 units; thread t of the 1024-thread workgroup handles units
-// j*1024 + t, j = 0..7, so each wave instruction touches 1 KiB of contiguous
-// input.  Blocks (B >= 64) never split a unit, and chunks never split a block.
-// All data movement is integer: sign, NaN payloads, subnormals and -0 never
-// pass through floating-point registers.
+// has 8192 units.  In k_stats thread t of the 1024-thread workgroup handles
+// units j*1024 + t; in k_write and k_decode part h covers units [2048h,
+// 2048h + 2048) and thread t of its 256 handles unit 2048h + 256j + t
+// (j = 0..7).  Either way each wave instruction moves 1 KiB of contiguous
+// input.  Blocks (B >= 64) never split a unit, and chunks never split a
+// block.  All data movement is integer: sign, NaN payloads, subnormals and -0
+// never pass through floating-point registers.
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -34,10 +44,10 @@
 namespace {
 
 constexpr uint32_t kChunk = 65536u;
-constexpr uint32_t kThreads = 1024u;
+constexpr uint32_t kThreads = 1024u;  // k_stats and k_plan
 constexpr uint32_t kWaves = kThreads / 64u;
 constexpr uint32_t kUnitsPerChunk = kChunk / 8u;
-constexpr uint32_t kUnitsPerThread = kUnitsPerChunk / kThreads;  // 8
+constexpr uint32_t kUnitsPerThread = kUnitsPerChunk / kThreads;  // 8, k_stats
 constexpr uint32_t kBitmapWords = 32u;  // 1024 blocks per chunk at B = 64
 constexpr uint64_t kMaxN = 1ull << 40;
 constexpr uint64_t kHeader = 128u;
@@ -45,11 +55,28 @@ constexpr uint32_t kMaxE0 = 249u;
 // 16383 / (28 ln 2) as a double: the variance threshold of window base k is
 // kK0 * 4^k.
 constexpr double kK0 = 0x1.a610ca4a234eep+9;
-// Look-back status words: two flag bits over a 62-bit byte count.
+// Look-back status words: two flag bits over a 62-bit value.
 constexpr uint64_t kFlagAggregate = 1ull << 62;
 constexpr uint64_t kFlagInclusive = 2ull << 62;
 constexpr uint64_t kValueMask = (1ull << 62) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 26;
+
+// Parts: k_write and k_decode run kParts workgroups of kPartThreads threads
+// per chunk, kUPT units per thread.
+constexpr uint32_t kParts = 4u;
+constexpr uint32_t kPartThreads = 256u;
+constexpr uint32_t kPartWaves = kPartThreads / 64u;
+constexpr uint32_t kUPT = 8u;
+constexpr uint32_t kPartUnits = kPartThreads * kUPT;  // 2048 units = 16384 values
+static_assert(kPartUnits * kParts == kUnitsPerChunk, "parts tile a chunk");
+static_assert(kUPT * kPartWaves <= 64u, "one scan entry per lane");
+static_assert(kUnitsPerThread == 2u * kParts, "k_stats row pairs map to parts");
+constexpr uint32_t kStage = kPartUnits + 16u;  // LDS bytes per staged plane
+constexpr uint32_t kPartEscStage = 4096u;      // escape bytes staged in LDS per part
+constexpr uint32_t kBins = 256u;               // exponent histogram bins
+constexpr uint32_t kHistCopies = 8u;           // interleaved LDS copies (by lane) to spread atomics
+constexpr uint32_t kLayoutThreads = 256u;      // chunks per k_layout workgroup
+static_assert(kThreads == kParts * kBins, "k_stats stores one (part, bin) per thread");
 
 __host__ __device__ inline uint64_t pad128(uint64_t v) { return (v + 127u) & ~uint64_t(127); }
 __host__ __device__ inline uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1u) / b; }
@@ -57,14 +84,14 @@ __host__ __device__ inline uint64_t table_end(uint64_t nchunks) {
   return kHeader + pad128(8u * (nchunks + 1u));
 }
 
-// Workspace: a control block, one error word per chunk, per-chunk partial
-// sums, per-chunk bitmap words (ciera) and per-chunk look-back words.
+// Workspace: control block, error words, per-chunk partial sums, bitmap
+// words, per-part histograms (u16 bins) and coded-value counts, per-part
+// escape offsets, per-chunk escape totals, and look-back words of k_layout.
 struct Ctrl {
   uint32_t e0;
   uint32_t ticket;
-  uint64_t esc_total;
   uint64_t n_err_slots;
-  uint64_t reserved[29];
+  uint64_t reserved[30];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -77,7 +104,7 @@ struct Partial {
 };
 
 struct WsLayout {
-  uint64_t err, partial, bitmap, status, total;
+  uint64_t err, partial, bitmap, hist, coded, partesc, chunkesc, gstatus, gesc_agg, gesc_incl, total;
 };
 
 __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255); }
@@ -85,20 +112,33 @@ __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~
 __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   WsLayout l;
   const uint64_t slots = nchunks ? nchunks : 1u;
+  const uint64_t groups = cdiv(slots, kLayoutThreads);
   l.err = sizeof(Ctrl);
-  l.partial = align256(l.err + 4u * slots);
+  l.partial = align256(l.err + 4u * kParts * slots);
   l.bitmap = align256(l.partial + sizeof(Partial) * slots);
-  l.status = align256(l.bitmap + 4u * kBitmapWords * slots);
-  l.total = align256(l.status + 8u * slots);
+  l.hist = align256(l.bitmap + 4u * kBitmapWords * slots);
+  l.coded = align256(l.hist + 2u * kBins * kParts * slots);
+  l.partesc = align256(l.coded + 4u * kParts * slots);
+  l.chunkesc = align256(l.partesc + 4u * kParts * slots);
+  l.gstatus = align256(l.chunkesc + 4u * slots);
+  l.gesc_agg = align256(l.gstatus + 8u * groups);
+  l.gesc_incl = align256(l.gesc_agg + 8u * groups);
+  l.total = align256(l.gesc_incl + 8u * groups);
   return l;
 }
 
 struct Ws {
   Ctrl* ctrl;
-  uint32_t* err;
-  Partial* partial;
-  uint32_t* bitmap;
-  uint64_t* status;
+  uint32_t* err;        // one word per workgroup of k_write / k_decode
+  Partial* partial;     // per chunk
+  uint32_t* bitmap;     // kBitmapWords per chunk
+  uint16_t* hist;       // kParts x kBins per chunk
+  uint32_t* coded;      // values to code, per part
+  uint32_t* partesc;    // escapes before each part within its chunk
+  uint32_t* chunkesc;   // escapes per chunk
+  uint64_t* gstatus;    // k_layout look-back: flag | bytes, per group of chunks
+  uint64_t* gesc_agg;   // escapes of the group
+  uint64_t* gesc_incl;  // escapes of all groups up to this one
 };
 
 __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
@@ -109,7 +149,13 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.err = reinterpret_cast<uint32_t*>(b + l.err);
   w.partial = reinterpret_cast<Partial*>(b + l.partial);
   w.bitmap = reinterpret_cast<uint32_t*>(b + l.bitmap);
-  w.status = reinterpret_cast<uint64_t*>(b + l.status);
+  w.hist = reinterpret_cast<uint16_t*>(b + l.hist);
+  w.coded = reinterpret_cast<uint32_t*>(b + l.coded);
+  w.partesc = reinterpret_cast<uint32_t*>(b + l.partesc);
+  w.chunkesc = reinterpret_cast<uint32_t*>(b + l.chunkesc);
+  w.gstatus = reinterpret_cast<uint64_t*>(b + l.gstatus);
+  w.gesc_agg = reinterpret_cast<uint64_t*>(b + l.gesc_agg);
+  w.gesc_incl = reinterpret_cast<uint64_t*>(b + l.gesc_incl);
   return w;
 }
 
@@ -139,8 +185,13 @@ __device__ inline Unit load_unit(const uint16_t* __restrict__ x, uint64_t first,
     u.w[2] = v.z;
     u.w[3] = v.w;
   } else {
-    for (int i = 0; i < 4; i++) u.w[i] = 0u;
-    for (uint32_t k = 0; k < cnt; k++) u.w[k >> 1] |= uint32_t(x[first + k]) << (16u * (k & 1u));
+    // unrolled so that every index into w is a constant (no private array)
+#pragma unroll
+    for (uint32_t i = 0; i < 4u; i++) {
+      const uint32_t lo = (2u * i < cnt) ? uint32_t(x[first + 2u * i]) : 0u;
+      const uint32_t hi = (2u * i + 1u < cnt) ? uint32_t(x[first + 2u * i + 1u]) : 0u;
+      u.w[i] = lo | (hi << 16);
+    }
   }
   return u;
 }
@@ -149,18 +200,25 @@ __device__ inline void store_unit(uint16_t* __restrict__ y, uint64_t first, uint
   if (cnt == 8u) {
     *reinterpret_cast<uint4*>(y + first) = make_uint4(u.w[0], u.w[1], u.w[2], u.w[3]);
   } else {
-    for (uint32_t k = 0; k < cnt; k++) y[first + k] = uint16_t(u.w[k >> 1] >> (16u * (k & 1u)));
+#pragma unroll
+    for (uint32_t i = 0; i < 4u; i++) {
+      if (2u * i < cnt) y[first + 2u * i] = uint16_t(u.w[i]);
+      if (2u * i + 1u < cnt) y[first + 2u * i + 1u] = uint16_t(u.w[i] >> 16);
+    }
   }
 }
 
 __device__ inline uint2 load_bytes8(const uint8_t* __restrict__ p, uint32_t cnt) {
   if (cnt == 8u) return *reinterpret_cast<const uint2*>(p);
   uint2 v = make_uint2(0u, 0u);
-  for (uint32_t k = 0; k < cnt; k++) {
-    if (k < 4u)
-      v.x |= uint32_t(p[k]) << (8u * k);
-    else
-      v.y |= uint32_t(p[k]) << (8u * (k - 4u));
+#pragma unroll
+  for (uint32_t k = 0; k < 8u; k++) {
+    if (k < cnt) {
+      if (k < 4u)
+        v.x |= uint32_t(p[k]) << (8u * k);
+      else
+        v.y |= uint32_t(p[k]) << (8u * (k - 4u));
+    }
   }
   return v;
 }
@@ -169,7 +227,9 @@ __device__ inline void store_bytes8(uint8_t* __restrict__ p, uint32_t cnt, uint2
   if (cnt == 8u) {
     *reinterpret_cast<uint2*>(p) = v;
   } else {
-    for (uint32_t k = 0; k < cnt; k++) p[k] = uint8_t((k < 4u ? v.x : v.y) >> (8u * (k & 3u)));
+#pragma unroll
+    for (uint32_t k = 0; k < 8u; k++)
+      if (k < cnt) p[k] = uint8_t((k < 4u ? v.x : v.y) >> (8u * (k & 3u)));
   }
 }
 
@@ -275,6 +335,16 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+__device__ inline uint64_t wave_incl_scan_u64(uint64_t v) {
+  const uint32_t lane = lane_id();
+#pragma unroll
+  for (uint32_t d = 1; d < 64u; d <<= 1) {
+    const uint64_t t = __shfl_up(v, d, 64);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
 __device__ inline double wave_sum(double v) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
@@ -293,45 +363,6 @@ __device__ inline uint32_t wave_sum_u32(uint32_t v) {
   return v;
 }
 
-// Escape positions: each thread holds kUnitsPerThread counts (one per unit,
-// 0..8), units ordered (j, wave, lane).  On return base[j] is the number of
-// escapes in all earlier units of the chunk and the function returns the
-// chunk total.  Every thread of the workgroup must call it.
-__device__ inline uint32_t chunk_escape_scan(const uint32_t (&cnt)[kUnitsPerThread],
-                                             uint32_t (&base)[kUnitsPerThread],
-                                             uint32_t* s_tot /* kUnitsPerThread*kWaves + 1 */) {
-  const uint32_t lane = lane_id();
-  const uint32_t wave = threadIdx.x >> 6;
-  // two counts per 32-bit word (16-bit fields; a wave's sum is at most 512)
-#pragma unroll
-  for (uint32_t p = 0; p < kUnitsPerThread / 2u; p++) {
-    const uint32_t packed = cnt[2 * p] | (cnt[2 * p + 1] << 16);
-    const uint32_t incl = wave_incl_scan(packed);
-    const uint32_t excl = incl - packed;
-    base[2 * p] = excl & 0xFFFFu;
-    base[2 * p + 1] = excl >> 16;
-    if (lane == 63u) {
-      s_tot[(2 * p) * kWaves + wave] = incl & 0xFFFFu;
-      s_tot[(2 * p + 1) * kWaves + wave] = incl >> 16;
-    }
-  }
-  __syncthreads();
-  // exclusive scan of the kUnitsPerThread*kWaves totals in (j, wave) order,
-  // by wave 0: lane l owns entries 2l and 2l+1
-  if (wave == 0) {
-    const uint32_t a = s_tot[2 * lane], b = s_tot[2 * lane + 1];
-    const uint32_t incl = wave_incl_scan(a + b);
-    const uint32_t excl = incl - (a + b);
-    s_tot[2 * lane] = excl;
-    s_tot[2 * lane + 1] = excl + a;
-    if (lane == 63u) s_tot[kUnitsPerThread * kWaves] = incl;
-  }
-  __syncthreads();
-#pragma unroll
-  for (uint32_t j = 0; j < kUnitsPerThread; j++) base[j] += s_tot[j * kWaves + wave];
-  return s_tot[kUnitsPerThread * kWaves];
-}
-
 // ------------------------------------------------------------------ k_stats
 // FP64 value of a BF16 pattern held in the top half of a float: BF16 -> FP32
 // is exact (denormals are kept), FP32 -> FP64 is exact.
@@ -340,20 +371,24 @@ __device__ inline double widen_hi(uint32_t hi_bits) { return double(__uint_as_fl
 // Partial sums of one unit's finite values (the checked path).
 __device__ inline void stats_checked(const Unit& v, uint32_t cnt, double shift, double& s1, double& s2,
                                      uint32_t& nf) {
-  for (uint32_t k = 0; k < cnt; k++) {
+#pragma unroll
+  for (uint32_t k = 0; k < 8u; k++) {
     const uint32_t b = (v.w[k >> 1] >> (16u * (k & 1u))) & 0xFFFFu;
-    if (((b >> 7) & 0xFFu) == 0xFFu) continue;
-    const double d = widen_hi(b << 16) - shift;
-    s1 += d;
-    s2 = fma(d, d, s2);
-    nf++;
+    if (k < cnt && ((b >> 7) & 0xFFu) != 0xFFu) {
+      const double d = widen_hi(b << 16) - shift;
+      s1 += d;
+      s2 = fma(d, d, s2);
+      nf++;
+    }
   }
 }
 
 template <bool kCiera>
 __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
                                                     uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
+  __shared__ uint32_t s_hist[kParts * kHistCopies * kBins];
   __shared__ uint32_t s_bits[kBitmapWords];
+  __shared__ uint32_t s_coded[kParts];
   __shared__ double s_s1[kWaves], s_s2[kWaves];
   __shared__ uint32_t s_nf[kWaves];
   const uint32_t tid = threadIdx.x;
@@ -361,14 +396,40 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
   const uint64_t start = uint64_t(c) * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
-  if (kCiera && tid < kBitmapWords) s_bits[tid] = 0u;
+  for (uint32_t i = tid; i < kParts * kHistCopies * kBins; i += kThreads) s_hist[i] = 0u;
+  if (tid < kBitmapWords) s_bits[tid] = 0u;
+  if (tid < kParts) s_coded[tid] = 0u;
   const uint32_t first = x[0];
   const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
-  __syncthreads();
 
-  // Fast path: no finite test per value.  A non-finite input makes the
-  // thread's sums non-finite (squares of finite BF16 values cannot
-  // overflow FP64), and the thread then redoes its units on the checked path.
+  // Load: a full chunk issues all of a thread's 16-byte loads before using any.
+  Unit v[kUnitsPerThread];
+  if (nc == kChunk) {
+#pragma unroll
+    for (uint32_t j = 0; j < kUnitsPerThread; j++) v[j] = load_unit(x, start + 8ull * (j * kThreads + tid), 8u);
+  } else {
+#pragma unroll
+    for (uint32_t j = 0; j < kUnitsPerThread; j++) {
+      const uint32_t u = j * kThreads + tid;
+      v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
+      if (u < nunits) v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+    }
+  }
+  uint2 old[kUnitsPerThread];
+  if (kCiera) {
+#pragma unroll
+    for (uint32_t j = 0; j < kUnitsPerThread; j++) {
+      const uint32_t u = j * kThreads + tid;
+      old[j] = (u < nunits) ? load_bytes8(cache + start + 8ull * u, min(8u, nc - 8u * u)) : make_uint2(0u, 0u);
+    }
+  }
+  __syncthreads();  // LDS cleared
+
+  // Variance sums with no finite test per value: a non-finite input makes the
+  // thread's sums non-finite (squares of finite BF16 values cannot overflow
+  // FP64), and the thread then redoes its units on the checked path.  Ciera:
+  // compare exponents with the cache, rewrite the bytes that differ, mark the
+  // block changed.
   double s1 = 0.0, s2 = 0.0;
   uint32_t nf = 0;
 #pragma unroll
@@ -376,13 +437,11 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
     const uint32_t u = j * kThreads + tid;
     if (u < nunits) {
       const uint32_t cnt = min(8u, nc - 8u * u);
-      const uint64_t at = start + 8ull * u;
-      const Unit v = load_unit(x, at, cnt);
       if (cnt == 8u) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
-          const double lo = widen_hi(v.w[i] << 16) - shift;
-          const double hi = widen_hi(v.w[i] & 0xFFFF0000u) - shift;
+          const double lo = widen_hi(v[j].w[i] << 16) - shift;
+          const double hi = widen_hi(v[j].w[i] & 0xFFFF0000u) - shift;
           s1 += lo;
           s2 = fma(lo, lo, s2);
           s1 += hi;
@@ -390,15 +449,14 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
         }
         nf += 8u;
       } else {
-        stats_checked(v, cnt, shift, s1, s2, nf);
+        stats_checked(v[j], cnt, shift, s1, s2, nf);
       }
       if (kCiera) {
-        const uint2 e = unit_exponents(v);
-        const uint2 old = load_bytes8(cache + at, cnt);
+        const uint2 e = unit_exponents(v[j]);
         const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
-        const uint64_t diff = ((uint64_t(e.y ^ old.y) << 32) | (e.x ^ old.x)) & keep;
+        const uint64_t diff = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
         if (diff) {
-          store_bytes8(cache + at, cnt, e);
+          store_bytes8(cache + start + 8ull * u, cnt, e);
           const uint32_t blk = (8u * u) >> log2B;
           atomicOr(&s_bits[blk >> 5], 1u << (blk & 31u));
         }
@@ -409,22 +467,60 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
     s1 = 0.0;
     s2 = 0.0;
     nf = 0;
+#pragma unroll
     for (uint32_t j = 0; j < kUnitsPerThread; j++) {
       const uint32_t u = j * kThreads + tid;
-      if (u >= nunits) break;
-      const uint32_t cnt = min(8u, nc - 8u * u);
-      stats_checked(load_unit(x, start + 8ull * u, cnt), cnt, shift, s1, s2, nf);
+      if (u < nunits) stats_checked(v[j], min(8u, nc - 8u * u), shift, s1, s2, nf);
     }
+  }
+  if (kCiera) __syncthreads();  // bitmap complete
+
+  // Exponent histogram of the values to code, per part (units j*1024 + t with
+  // j in {2h, 2h+1} belong to part h).  Word (part * kBins + bin) *
+  // kHistCopies + copy, copy chosen by lane: equal exponents within a wave
+  // spread over kHistCopies consecutive words, i.e. over as many LDS banks.
+  const uint32_t copy = tid & (kHistCopies - 1u);
+  uint32_t coded[kParts] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
+    const uint32_t u = j * kThreads + tid;
+    if (u >= nunits) continue;
+    if (kCiera) {
+      const uint32_t blk = (8u * u) >> log2B;
+      if (!((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) continue;
+    }
+    const uint32_t cnt = min(8u, nc - 8u * u);
+    const uint2 e = unit_exponents(v[j]);
+    uint32_t* hist = s_hist + (j / 2u) * (kHistCopies * kBins) + copy;
+#pragma unroll
+    for (uint32_t k = 0; k < 8u; k++)
+      if (k < cnt) atomicAdd(&hist[byte_of(e, k) * kHistCopies], 1u);
+    coded[j / 2u] += cnt;
   }
   s1 = wave_sum(s1);
   s2 = wave_sum(s2);
   nf = wave_sum_u32(nf);
+#pragma unroll
+  for (uint32_t h = 0; h < kParts; h++) {
+    const uint32_t t = wave_sum_u32(coded[h]);
+    if (lane_id() == 0u && t) atomicAdd(&s_coded[h], t);
+  }
   if (lane_id() == 0u) {
     s_s1[tid >> 6] = s1;
     s_s2[tid >> 6] = s2;
     s_nf[tid >> 6] = nf;
   }
   __syncthreads();
+  // one (part, bin) per thread: sum the copies, store as u16 (a part holds at
+  // most 16384 values)
+  {
+    const uint32_t h = tid / kBins, bin = tid % kBins;
+    uint32_t s = 0;
+#pragma unroll
+    for (uint32_t q = 0; q < kHistCopies; q++) s += s_hist[(h * kBins + bin) * kHistCopies + q];
+    ws.hist[(uint64_t(c) * kParts + h) * kBins + bin] = uint16_t(s);
+  }
+  if (tid < kParts) ws.coded[uint64_t(c) * kParts + tid] = s_coded[tid];
   if (tid == 0) {
     double a = 0.0, b = 0.0;
     uint32_t m = 0;
@@ -443,7 +539,6 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
     p.nch = nch;
     p.pad[0] = p.pad[1] = 0u;
     ws.partial[c] = p;
-    ws.status[c] = 0u;
   }
   if (kCiera && tid < kBitmapWords) ws.bitmap[uint64_t(c) * kBitmapWords + tid] = s_bits[tid];
 }
@@ -491,8 +586,11 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
   }
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
   const uint64_t base = table_end(nchunks);
-  // zero the table's padding words (entries past nchunks)
+  // zero the table's padding words (entries past nchunks) and k_layout's
+  // look-back words
   for (uint64_t i = nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
+  const uint64_t groups = cdiv(nchunks, kLayoutThreads);
+  for (uint64_t i = tid; i < groups; i += kThreads) ws.gstatus[i] = 0u;
   __syncthreads();
   if (tid == 0) {
     double s1 = 0.0, s2 = 0.0;
@@ -511,8 +609,7 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
     const uint32_t e0 = (e0_override >= 0) ? uint32_t(e0_override) : window_base(var, nf);
     ws.ctrl->e0 = e0;
     ws.ctrl->ticket = 0u;
-    ws.ctrl->esc_total = 0u;
-    ws.ctrl->n_err_slots = nchunks;
+    ws.ctrl->n_err_slots = nchunks * kParts;
     const uint32_t magic = B ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
     uint64_t* h = reinterpret_cast<uint64_t*>(out);
     h[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(B ? 1u : 0u) << 48) | (uint64_t(e0) << 56);
@@ -530,8 +627,9 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
   }
 }
 
-// ------------------------------------------------------------------ k_write
-// Per-chunk static geometry shared by encode and decode.
+// ------------------------------------------------------------------ k_layout
+// Chunk geometry shared by encode and decode: section offsets from the
+// chunk's start, its value count and (ciera) changed-block count.
 struct ChunkGeom {
   uint64_t sm, bitmap, plane, esc;  // absolute section offsets
   uint64_t plane_bytes;             // padded size of one plane
@@ -549,115 +647,286 @@ __device__ inline ChunkGeom chunk_geom(uint64_t begin, uint32_t nc, bool ciera, 
   return g;
 }
 
-__device__ inline void zero_fill(uint8_t* __restrict__ p, uint64_t from, uint64_t to) {
-  for (uint64_t i = from + threadIdx.x; i < to; i += kThreads) p[i] = 0u;
-}
-
-// Decoupled look-back, run by one whole wave: publish this chunk's size as an
-// aggregate, then sum predecessors' published sizes 64 at a time until one
-// holds an inclusive prefix; publish the inclusive prefix.  Predecessors
-// always hold earlier tickets, so their workgroups are already running and
-// publish their aggregates without waiting on anything.  Returns the byte
-// offset of this chunk relative to the first chunk; sets *err if a wait
-// exceeds kSpinLimit polls.
-__device__ inline uint64_t look_back(uint64_t* __restrict__ status, uint32_t c, uint64_t size, uint32_t* err) {
-  const uint32_t lane = lane_id();
-  if (c == 0u) {
-    if (lane == 0u)
-      __hip_atomic_store(&status[0], kFlagInclusive | size, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    return 0u;
+// One thread per chunk.  Each part's escapes = its coded values minus those
+// whose exponent falls in the window (7 histogram bins); the chunk size then
+// follows from the layout, and a decoupled look-back over workgroups (groups
+// of kLayoutThreads chunks) turns sizes into offsets.  The group's ticket is
+// taken in launch order, so a group only ever waits on groups already running.
+// Group status: flag | bytes in gstatus; the escape counts sit in gesc_agg /
+// gesc_incl, written before the release of the flag that announces them.
+__global__ __launch_bounds__(kLayoutThreads) void k_layout(uint64_t n, uint64_t nchunks, uint32_t log2B,
+                                                           uint8_t* __restrict__ out,
+                                                           uint64_t* __restrict__ out_size, Ws ws) {
+  __shared__ uint32_t s_ticket;
+  __shared__ uint64_t s_wb[kLayoutThreads / 64u], s_we[kLayoutThreads / 64u];
+  __shared__ uint64_t s_pb, s_pe;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = lane_id(), wave = tid >> 6;
+  if (tid == 0) s_ticket = atomicAdd(&ws.ctrl->ticket, 1u);
+  __syncthreads();
+  const uint32_t g = s_ticket;
+  const uint64_t c = uint64_t(g) * kLayoutThreads + tid;
+  const uint32_t e0 = ws.ctrl->e0;
+  const uint32_t B = log2B ? (1u << log2B) : 0u;
+  uint64_t size = 0, esc = 0;
+  if (c < nchunks) {
+    const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
+    uint32_t pe[kParts];
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      const uint16_t* hb = ws.hist + (c * kParts + h) * kBins + e0;
+      uint32_t inwin = 0;
+#pragma unroll
+      for (uint32_t k = 0; k < 7u; k++) inwin += hb[k];
+      pe[h] = ws.coded[c * kParts + h] - inwin;
+    }
+    uint32_t acc = 0;
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      ws.partesc[c * kParts + h] = acc;
+      acc += pe[h];
+    }
+    ws.chunkesc[c] = acc;
+    esc = acc;
+    const uint64_t p = B ? uint64_t(ws.partial[c].nch) * B / 8u : cdiv(nc, 8u);
+    size = pad128(nc) + (B ? 128u : 0u) + 3u * pad128(p) + pad128(acc);
   }
-  if (lane == 0u)
-    __hip_atomic_store(&status[c], kFlagAggregate | size, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  uint64_t prefix = 0;
-  int64_t top = int64_t(c) - 1;  // closest predecessor not yet summed
-  uint32_t spins = 0;
-  while (true) {
-    const int64_t k = top - int64_t(lane);
-    const uint64_t s = (k >= 0) ? __hip_atomic_load(&status[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
-                                : kFlagInclusive;  // before chunk 0: an empty inclusive prefix
-    const uint64_t flag = s & ~kValueMask;
-    if (__ballot(flag == 0u) != 0u) {
-      if (++spins > kSpinLimit) {
-        *err = CIERA_ERR_INTERNAL;
-        break;
+  // workgroup scans of sizes and escapes
+  const uint64_t ib = wave_incl_scan_u64(size);
+  const uint64_t ie = wave_incl_scan_u64(esc);
+  if (lane == 63u) {
+    s_wb[wave] = ib;
+    s_we[wave] = ie;
+  }
+  __syncthreads();
+  uint64_t xb = ib - size, xe = ie - esc;  // exclusive within the workgroup
+  uint64_t tb = 0, te = 0;                 // workgroup totals
+  for (uint32_t w = 0; w < kLayoutThreads / 64u; w++) {
+    if (w < wave) {
+      xb += s_wb[w];
+      xe += s_we[w];
+    }
+    tb += s_wb[w];
+    te += s_we[w];
+  }
+  if (wave == 0) {
+    // publish this group's aggregate, then sum predecessors 64 at a time
+    uint32_t err = 0u;
+    if (lane == 0u) {
+      if (g == 0u) {
+        ws.gesc_incl[0] = te;
+        __hip_atomic_store(&ws.gstatus[0], kFlagInclusive | tb, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        ws.gesc_agg[g] = te;
+        __hip_atomic_store(&ws.gstatus[g], kFlagAggregate | tb, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
       }
-      __builtin_amdgcn_s_sleep(1);
-      continue;
     }
-    const uint64_t incl = __ballot(flag == kFlagInclusive);
-    if (incl != 0u) {
-      const uint32_t first = uint32_t(__builtin_ctzll(incl));  // closest inclusive predecessor
-      prefix += wave_sum_u64(lane <= first ? (s & kValueMask) : 0u);
-      break;
+    uint64_t pb = 0, pe = 0;
+    if (g > 0u) {
+      int64_t top = int64_t(g) - 1;
+      uint32_t spins = 0;
+      while (true) {
+        const int64_t k = top - int64_t(lane);
+        const uint64_t s = (k >= 0) ? __hip_atomic_load(&ws.gstatus[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
+                                    : kFlagInclusive;
+        const uint64_t flag = s & ~kValueMask;
+        if (__ballot(flag == 0u) != 0u) {
+          if (++spins > kSpinLimit) {
+            err = CIERA_ERR_INTERNAL;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          continue;
+        }
+        const uint64_t ev = (k < 0) ? 0u : (flag == kFlagInclusive ? ws.gesc_incl[k] : ws.gesc_agg[k]);
+        const uint64_t incl = __ballot(flag == kFlagInclusive);
+        if (incl != 0u) {
+          const uint32_t first = uint32_t(__builtin_ctzll(incl));
+          pb += wave_sum_u64(lane <= first ? (s & kValueMask) : 0u);
+          pe += wave_sum_u64(lane <= first ? ev : 0u);
+          break;
+        }
+        pb += wave_sum_u64(s & kValueMask);
+        pe += wave_sum_u64(ev);
+        top -= 64;
+      }
+      if (lane == 0u) {
+        // published even after a failed wait, so later groups never wait forever
+        ws.gesc_incl[g] = pe + te;
+        __hip_atomic_store(&ws.gstatus[g], kFlagInclusive | (pb + tb), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
-    prefix += wave_sum_u64(s & kValueMask);
-    top -= 64;
+    if (lane == 0u) {
+      s_pb = pb;
+      s_pe = pe;
+      // a failed wait makes every chunk of the group report the error
+      if (err) {
+        const uint64_t c0 = uint64_t(g) * kLayoutThreads;
+        for (uint64_t cc = c0; cc < c0 + kLayoutThreads && cc < nchunks; cc++) ws.partesc[cc * kParts] = ~0u;
+      }
+    }
   }
-  if (lane == 0u)
-    __hip_atomic_store(&status[c], kFlagInclusive | (prefix + size), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-  return prefix;
+  __syncthreads();
+  const uint64_t base = table_end(nchunks);
+  uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
+  if (c < nchunks) {
+    const uint64_t begin = base + s_pb + xb;
+    table[c] = begin;
+    if (c + 1u == nchunks) {
+      const uint64_t total = begin + size;
+      table[nchunks] = total;
+      uint64_t* hd = reinterpret_cast<uint64_t*>(out);
+      hd[4] = total;
+      hd[6] = s_pe + xe + esc;
+      *out_size = total;
+    }
+  }
 }
 
+// ------------------------------------------------------------------ k_write
+__device__ inline void zero_fill(uint8_t* __restrict__ p, uint64_t from, uint64_t to, uint32_t nthreads) {
+  for (uint64_t i = from + threadIdx.x; i < to; i += nthreads) p[i] = 0u;
+}
+
+// Escape positions within a part: cnt[j] (0..8) per unit, units ordered
+// (j, wave, lane).  base[j] receives the escapes in earlier units of the part;
+// returns the part's total.  Every thread of the workgroup must call it.
+__device__ inline uint32_t part_escape_scan(const uint32_t (&cnt)[kUPT], uint32_t (&base)[kUPT],
+                                            uint32_t* s_tot /* kUPT * kPartWaves + 1 */) {
+  const uint32_t lane = lane_id();
+  const uint32_t wave = threadIdx.x >> 6;
+  // two counts per 32-bit word (16-bit fields; a wave's sum is at most 512)
+#pragma unroll
+  for (uint32_t p = 0; p < kUPT / 2u; p++) {
+    const uint32_t packed = cnt[2 * p] | (cnt[2 * p + 1] << 16);
+    const uint32_t incl = wave_incl_scan(packed);
+    const uint32_t excl = incl - packed;
+    base[2 * p] = excl & 0xFFFFu;
+    base[2 * p + 1] = excl >> 16;
+    if (lane == 63u) {
+      s_tot[(2 * p) * kPartWaves + wave] = incl & 0xFFFFu;
+      s_tot[(2 * p + 1) * kPartWaves + wave] = incl >> 16;
+    }
+  }
+  __syncthreads();
+  constexpr uint32_t kEntries = kUPT * kPartWaves;
+  if (wave == 0) {
+    const uint32_t a = (lane < kEntries) ? s_tot[lane] : 0u;
+    const uint32_t incl = wave_incl_scan(a);
+    if (lane < kEntries) s_tot[lane] = incl - a;
+    if (lane == 63u) s_tot[kEntries] = incl;
+  }
+  __syncthreads();
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) base[j] += s_tot[j * kPartWaves + wave];
+  return s_tot[kEntries];
+}
+
+// Plane bytes (one per coded unit slot) before unit u of a ciera chunk: the
+// slots of all changed blocks before u's block, plus u's offset in its block
+// if that block is changed.  Units past the chunk's last block see all slots.
+__device__ inline uint32_t coded_before(uint32_t u, const uint32_t* s_bits, const uint32_t* s_rank, uint32_t log2B,
+                                        uint32_t nb, uint32_t nch) {
+  const uint32_t upb_log = log2B - 3u;  // units per block = B / 8
+  const uint32_t blk = u >> upb_log;
+  if (blk >= nb) return nch << upb_log;
+  const uint32_t word = s_bits[blk >> 5];
+  const uint32_t rank = s_rank[blk >> 5] + __popc(word & ((1u << (blk & 31u)) - 1u));
+  const bool changed = (word >> (blk & 31u)) & 1u;
+  return (rank << upb_log) + (changed ? (u & ((1u << upb_log) - 1u)) : 0u);
+}
+
+// Bitmap words into LDS with the changed-block counts before each word;
+// wave 0 only.
+__device__ inline void stage_bitmap(uint32_t w, uint32_t* s_bits, uint32_t* s_rank) {
+  const uint32_t tid = threadIdx.x;
+  const uint32_t pc = __popc(w);
+  const uint32_t incl = wave_incl_scan(pc);
+  if (tid < kBitmapWords) {
+    s_bits[tid] = w;
+    s_rank[tid] = incl - pc;
+  }
+}
+
+// One part of a chunk.  Its stream offset, the escapes before it in its chunk
+// and the chunk's escape total all come from k_layout, so the part waits on
+// nothing: load, code, write.
 template <bool kCiera>
-__global__ __launch_bounds__(kThreads) void k_write(const uint16_t* __restrict__ x, uint64_t n, uint64_t nchunks,
-                                                    uint32_t log2B, uint8_t* __restrict__ out,
-                                                    uint64_t* __restrict__ out_size, Ws ws) {
-  __shared__ uint32_t s_chunk;
+__global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restrict__ x, uint64_t n,
+                                                        uint32_t log2B, uint8_t* __restrict__ out, Ws ws) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_esc[kPartEscStage];
   __shared__ uint32_t s_bits[kBitmapWords];
   __shared__ uint32_t s_rank[kBitmapWords];
-  __shared__ uint32_t s_tot[kUnitsPerThread * kWaves + 1];
-  __shared__ uint64_t s_begin;
-  __shared__ uint32_t s_err;
+  __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
   const uint32_t tid = threadIdx.x;
+  const uint32_t wg = blockIdx.x;
+  const uint32_t c = wg / kParts;
+  const uint32_t h = wg % kParts;
+  const bool last_part = h + 1u == kParts;
   const uint32_t B = 1u << log2B;
-  if (tid == 0) s_chunk = atomicAdd(&ws.ctrl->ticket, 1u);
-  __syncthreads();
-  const uint32_t c = s_chunk;
   const uint64_t start = uint64_t(c) * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
+  const uint32_t pu0 = h * kPartUnits;
+
+  // Load the part first: all of a thread's 16-byte loads go out before any is used.
+  Unit v[kUPT];
+  if (8u * (pu0 + kPartUnits) <= nc) {
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) v[j] = load_unit(x, start + 8ull * (pu0 + j * kPartThreads + tid), 8u);
+  } else {
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
+      v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
+      if (u < nunits) v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+    }
+  }
+  const uint64_t begin = reinterpret_cast<const uint64_t*>(out + kHeader)[c];
+  const uint32_t esc_before = ws.partesc[c * kParts + h];
+  const uint32_t esc_chunk = ws.chunkesc[c];
+  const uint32_t esc_part = (last_part ? esc_chunk : ws.partesc[c * kParts + h + 1u]) - esc_before;
   const uint32_t e0 = ws.ctrl->e0;
   const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
+  for (uint32_t i = tid; i < 3u * kStage / 16u; i += kPartThreads)
+    reinterpret_cast<uint4*>(s_planes)[i] = make_uint4(0u, 0u, 0u, 0u);
 
-  uint32_t nch = 0;
+  uint32_t nch = 0, nb = 0;
   if (kCiera) {
-    if (tid < 64u) {
-      const uint32_t w = (tid < kBitmapWords) ? ws.bitmap[uint64_t(c) * kBitmapWords + tid] : 0u;
-      const uint32_t pc = __popc(w);
-      const uint32_t incl = wave_incl_scan(pc);
-      if (tid < kBitmapWords) {
-        s_bits[tid] = w;
-        s_rank[tid] = incl - pc;
-      }
-    }
-    __syncthreads();
-    nch = s_rank[kBitmapWords - 1] + __popc(s_bits[kBitmapWords - 1]);
+    if (tid < 64u)
+      stage_bitmap((tid < kBitmapWords) ? ws.bitmap[uint64_t(c) * kBitmapWords + tid] : 0u, s_bits, s_rank);
+    nb = (nc + B - 1u) >> log2B;
   }
+  __syncthreads();  // staging cleared, bitmap staged
+  if (kCiera) nch = s_rank[kBitmapWords - 1] + __popc(s_bits[kBitmapWords - 1]);
+  const ChunkGeom g = chunk_geom(begin, nc, kCiera, nch, B);
+  const uint32_t pb = uint32_t(g.plane_bytes);
+  // Plane bytes this part stages and writes.  zip3: one byte per unit, so the
+  // part owns bytes [pu0, pu0 + kPartUnits) of each plane (padding included).
+  // ciera: the slots of the part's units in changed blocks, [S_h, S_next);
+  // the last part also owns the padding after the chunk's last slot.  Every
+  // bound is a multiple of 8.
+  const uint32_t s_h = kCiera ? coded_before(pu0, s_bits, s_rank, log2B, nb, nch) : pu0;
+  const uint32_t s_next = kCiera ? (!last_part ? coded_before(pu0 + kPartUnits, s_bits, s_rank, log2B, nb, nch)
+                                               : nch * (B / 8u))
+                                 : pu0 + kPartUnits;
 
-  // Load the chunk; per unit: the three plane bytes and the escape mask.
-  Unit v[kUnitsPerThread];
-  uint32_t cnt[kUnitsPerThread], base[kUnitsPerThread];
-  uint32_t planes[kUnitsPerThread];  // p0 | p1 << 8 | p2 << 16 | escape mask << 24
+  // Code every unit: sign+mantissa bytes straight to HBM, plane bytes into LDS.
+  uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
 #pragma unroll
-  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-    const uint32_t u = j * kThreads + tid;
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
     cnt[j] = 0u;
-    planes[j] = 0u;
-    v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
+    emask[j] = 0u;
     if (u < nunits) {
-      const uint32_t valid = min(8u, nc - 8u * u);
-      v[j] = load_unit(x, start + 8ull * u, valid);
-    }
-  }
-#pragma unroll
-  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-    const uint32_t u = j * kThreads + tid;
-    if (u < nunits) {
+      *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
       bool coded = true;
+      uint32_t pbyte = u;
       if (kCiera) {
         const uint32_t blk = (8u * u) >> log2B;
         coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
+        pbyte = coded_before(u, s_bits, s_rank, log2B, nb, nch);
       }
       if (coded) {
         const uint32_t valid = min(8u, nc - 8u * u);
@@ -665,68 +934,57 @@ __global__ __launch_bounds__(kThreads) void k_write(const uint16_t* __restrict__
         uint32_t cp[4];
 #pragma unroll
         for (int i = 0; i < 4; i++) cp[i] = code_pair(exp_pair(v[j].w[i]), bias);
-        uint32_t p = unit_planes(cp) & (vmask * 0x010101u);
-        const uint32_t em = ~(p | (p >> 8) | (p >> 16)) & vmask;
-        planes[j] = p | (em << 24);
-        cnt[j] = __popc(em);
+        const uint32_t p = unit_planes(cp) & (vmask * 0x010101u);
+        const uint32_t at = pbyte - s_h;
+        s_planes[at] = uint8_t(p);
+        s_planes[kStage + at] = uint8_t(p >> 8);
+        s_planes[2u * kStage + at] = uint8_t(p >> 16);
+        emask[j] = ~(p | (p >> 8) | (p >> 16)) & vmask;
+        cnt[j] = __popc(emask[j]);
       }
     }
   }
-  const uint32_t nesc = chunk_escape_scan(cnt, base, s_tot);
-
-  // Chunk size, then its offset by look-back over earlier chunks (wave 0).
-  const uint64_t size = pad128(nc) + (kCiera ? 128u : 0u) +
-                        3u * pad128(kCiera ? uint64_t(nch) * B / 8u : cdiv(nc, 8u)) + pad128(nesc);
-  if (tid < 64u) {
-    if (tid == 0)
-      atomicAdd(reinterpret_cast<unsigned long long*>(&ws.ctrl->esc_total), (unsigned long long)nesc);
-    uint32_t err = 0u;
-    const uint64_t prefix = look_back(ws.status, c, size, &err);
-    if (tid == 0) {
-      const uint64_t begin = table_end(nchunks) + prefix;
-      s_begin = begin;
-      s_err = err;
-      ws.err[c] = err;
-      uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
-      table[c] = begin;
-      if (uint64_t(c) + 1u == nchunks) {
-        const uint64_t total = begin + size;
-        table[nchunks] = total;
-        uint64_t* h = reinterpret_cast<uint64_t*>(out);
-        h[4] = total;
-        h[6] = __hip_atomic_load(&ws.ctrl->esc_total, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-        *out_size = total;
-      }
-    }
+  const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
+  // The count must match what k_layout read off the histogram; a mismatch
+  // would overrun the escape section, so no escapes are written and the error
+  // word reports it.
+  const bool esc_ok = pesc == esc_part;
+  if (tid == 0) ws.err[wg] = esc_ok ? 0u : uint32_t(CIERA_ERR_INTERNAL);
+  // planes: LDS -> HBM in 8-byte pieces over the owned range, clipped to the
+  // padded plane length
+  const uint32_t own_hi = min(s_next, pb);
+  const uint32_t own = own_hi > s_h ? own_hi - s_h : 0u;
+  for (uint32_t i = tid; i < 3u * (own / 8u); i += kPartThreads) {
+    const uint32_t b = i / (own / 8u);
+    const uint32_t off = 8u * (i - b * (own / 8u));
+    const uint2 val = *reinterpret_cast<const uint2*>(s_planes + b * kStage + off);
+    *reinterpret_cast<uint2*>(out + g.plane + b * pb + s_h + off) = val;
   }
-  __syncthreads();
-  if (s_err) return;  // uniform; the error word tells the caller
-  const ChunkGeom g = chunk_geom(s_begin, nc, kCiera, nch, B);
-
-  // Write sections.
+  // escapes of this part: [esc_before, esc_before + pesc) of the chunk's section
+  const uint64_t esc_at = g.esc + esc_before;
+  if (esc_ok && pesc <= kPartEscStage) {
 #pragma unroll
-  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-    const uint32_t u = j * kThreads + tid;
-    if (u >= nunits) continue;
-    *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
-    bool coded = true;
-    uint64_t pbyte = u;
-    if (kCiera) {
-      const uint32_t blk = (8u * u) >> log2B;
-      const uint32_t word = s_bits[blk >> 5];
-      coded = (word >> (blk & 31u)) & 1u;
-      const uint32_t rank = s_rank[blk >> 5] + __popc(word & ((1u << (blk & 31u)) - 1u));
-      pbyte = uint64_t(rank) * (B / 8u) + (u & (B / 8u - 1u));
-    }
-    if (coded) {
-      const uint32_t p = planes[j];
-      out[g.plane + pbyte] = uint8_t(p);
-      out[g.plane + g.plane_bytes + pbyte] = uint8_t(p >> 8);
-      out[g.plane + 2u * g.plane_bytes + pbyte] = uint8_t(p >> 16);
-      uint32_t em = p >> 24;
+    for (uint32_t j = 0; j < kUPT; j++) {
+      uint32_t em = emask[j];
       if (em) {
         const uint2 e = unit_exponents(v[j]);
-        uint64_t at = g.esc + base[j];
+        uint32_t at = base[j];
+        while (em) {
+          const uint32_t k = __builtin_ctz(em);
+          em &= em - 1u;
+          s_esc[at++] = uint8_t(byte_of(e, k));
+        }
+      }
+    }
+    __syncthreads();
+    for (uint32_t i = tid; i < pesc; i += kPartThreads) out[esc_at + i] = s_esc[i];
+  } else if (esc_ok) {
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) {
+      uint32_t em = emask[j];
+      if (em) {
+        const uint2 e = unit_exponents(v[j]);
+        uint64_t at = esc_at + base[j];
         while (em) {
           const uint32_t k = __builtin_ctz(em);
           em &= em - 1u;
@@ -735,63 +993,61 @@ __global__ __launch_bounds__(kThreads) void k_write(const uint16_t* __restrict__
       }
     }
   }
-  if (kCiera && tid < kBitmapWords) *reinterpret_cast<uint32_t*>(out + g.bitmap + 4u * tid) = s_bits[tid];
-  // Zero padding after each section's data.
-  zero_fill(out, g.sm + 8ull * nunits, g.bitmap);
-  uint64_t plane_data;
-  if (!kCiera) {
-    plane_data = nunits;
-  } else {
-    const uint32_t last = (nc - 1u) >> log2B;  // last block of the chunk
-    const bool last_changed = (s_bits[last >> 5] >> (last & 31u)) & 1u;
-    const uint32_t last_rank = s_rank[last >> 5] + __popc(s_bits[last >> 5] & ((1u << (last & 31u)) - 1u));
-    plane_data = last_changed ? uint64_t(last_rank) * (B / 8u) + (nunits - last * (B / 8u))
-                              : uint64_t(nch) * (B / 8u);
+  if (last_part) {
+    // zero padding after each section's data, and the bitmap
+    zero_fill(out, g.sm + 8ull * nunits, g.bitmap, kPartThreads);
+    if (kCiera && tid < kBitmapWords) *reinterpret_cast<uint32_t*>(out + g.bitmap + 4u * tid) = s_bits[tid];
+    if (kCiera)
+      for (uint32_t b = 0; b < 3u; b++) zero_fill(out, g.plane + b * pb + s_next, g.plane + (b + 1u) * pb, kPartThreads);
+    if (esc_chunk <= kChunk) zero_fill(out, g.esc + esc_chunk, g.esc + pad128(esc_chunk), kPartThreads);
   }
-  for (uint32_t b = 0; b < 3u; b++)
-    zero_fill(out, g.plane + b * g.plane_bytes + plane_data, g.plane + (b + 1u) * g.plane_bytes);
-  zero_fill(out, g.esc + nesc, g.esc + pad128(nesc));
 }
 
 // ------------------------------------------------------------------ k_decode
+// One part of a chunk; parts never wait on each other.  A part's first escape
+// is found by counting the code-0 slots of the plane bytes before its own.
 template <bool kCiera>
-__global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__ in, uint64_t in_size,
-                                                     uint16_t* __restrict__ y, uint64_t n, uint64_t nchunks,
-                                                     uint32_t log2B, uint8_t* __restrict__ cache,
-                                                     uint64_t* __restrict__ n_err_slots,
-                                                     uint32_t* __restrict__ err_slots) {
+__global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restrict__ in, uint64_t in_size,
+                                                         uint16_t* __restrict__ y, uint64_t n, uint64_t nchunks,
+                                                         uint32_t log2B, uint8_t* __restrict__ cache,
+                                                         uint64_t* __restrict__ n_err_slots,
+                                                         uint32_t* __restrict__ err_slots) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
   __shared__ uint32_t s_ok;    // header and table entries are consistent
   __shared__ uint32_t s_fits;  // the chunk's fixed-size sections lie inside it
   __shared__ uint32_t s_e0;
   __shared__ uint64_t s_begin, s_end;
   __shared__ uint32_t s_bits[kBitmapWords];
   __shared__ uint32_t s_rank[kBitmapWords];
-  __shared__ uint32_t s_tot[kUnitsPerThread * kWaves + 1];
+  __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
+  __shared__ uint32_t s_red[kPartWaves];
   const uint32_t tid = threadIdx.x;
-  const uint32_t c = blockIdx.x;
+  const uint32_t wg = blockIdx.x;
+  const uint32_t c = wg / kParts;
+  const uint32_t h = wg % kParts;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint64_t base_off = table_end(nchunks);
   if (tid == 0) {
     uint32_t ok = 1u;
-    const uint64_t* h = reinterpret_cast<const uint64_t*>(in);
+    const uint64_t* hd = reinterpret_cast<const uint64_t*>(in);
     const uint32_t magic = kCiera ? 0x52454943u : 0x3350495Au;
     uint64_t begin = 0, end = 0;
     uint32_t e0 = 0;
     if (in_size < base_off) {
       ok = 0u;
     } else {
-      const uint64_t h0 = h[0];
+      const uint64_t h0 = hd[0];
       e0 = uint32_t(h0 >> 56);
       ok &= uint32_t(h0 & 0xFFFFFFFFu) == magic;
       ok &= ((h0 >> 32) & 0xFFFFu) == 1u;
       ok &= ((h0 >> 48) & 0xFFu) == (kCiera ? 1u : 0u);
       ok &= e0 <= kMaxE0;
-      ok &= h[1] == n;
-      ok &= h[2] == (uint64_t(B) | (uint64_t(kChunk) << 32));
-      ok &= h[3] == nchunks;
-      const uint64_t total = h[4];
+      ok &= hd[1] == n;
+      ok &= hd[2] == (uint64_t(B) | (uint64_t(kChunk) << 32));
+      ok &= hd[3] == nchunks;
+      const uint64_t total = hd[4];
       ok &= total <= in_size;
-      for (int i = 7; i < 16; i++) ok &= h[i] == 0u;
+      for (int i = 7; i < 16; i++) ok &= hd[i] == 0u;
       const uint64_t* table = reinterpret_cast<const uint64_t*>(in + kHeader);
       ok &= table[0] == base_off;
       ok &= table[nchunks] == total;
@@ -806,11 +1062,11 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__
     s_e0 = e0;
     s_begin = begin;
     s_end = end;
-    if (c == 0u) *n_err_slots = gridDim.x;
+    if (wg == 0u) *n_err_slots = gridDim.x;
   }
   __syncthreads();
   if (!s_ok || nchunks == 0u) {
-    if (tid == 0) err_slots[c] = s_ok ? 0u : uint32_t(CIERA_ERR_FORMAT);
+    if (tid == 0) err_slots[wg] = s_ok ? 0u : uint32_t(CIERA_ERR_FORMAT);
     return;
   }
   const uint32_t e0 = s_e0;
@@ -818,26 +1074,22 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__
   const uint64_t start = uint64_t(c) * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
+  const uint32_t pu0 = h * kPartUnits;
 
-  uint32_t nch = 0;
+  uint32_t nch = 0, nb = 0;
   if (kCiera) {
     // the bitmap section must lie inside the chunk before it is read
     const uint64_t bm = begin + pad128(nc);
     const bool fits = bm + 128u <= end;
+    nb = (nc + B - 1u) >> log2B;
     if (tid < 64u) {
-      const uint32_t nb = (nc + B - 1u) >> log2B;
       uint32_t w = 0;
       if (fits && tid < kBitmapWords) {
         w = *reinterpret_cast<const uint32_t*>(in + bm + 4u * tid);
         const uint32_t lo = 32u * tid;
         w = (lo >= nb) ? 0u : (nb - lo >= 32u ? w : (w & ((1u << (nb - lo)) - 1u)));
       }
-      const uint32_t pc = __popc(w);
-      const uint32_t incl = wave_incl_scan(pc);
-      if (tid < kBitmapWords) {
-        s_bits[tid] = w;
-        s_rank[tid] = incl - pc;
-      }
+      stage_bitmap(w, s_bits, s_rank);
     }
     if (tid == 0) s_fits = fits ? 1u : 0u;
     __syncthreads();
@@ -849,57 +1101,107 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__
   const uint32_t bitmap_fits = s_fits;
   const ChunkGeom g = chunk_geom(begin, nc, kCiera, nch, B);
   if (!bitmap_fits || g.esc > end) {
-    if (tid == 0) err_slots[c] = uint32_t(CIERA_ERR_FORMAT);
+    if (tid == 0) err_slots[wg] = uint32_t(CIERA_ERR_FORMAT);
     return;
   }
+  if (pu0 >= nunits) {  // a part past the chunk's data
+    if (tid == 0) err_slots[wg] = 0u;
+    return;
+  }
+  const uint32_t pb = uint32_t(g.plane_bytes);
+  const uint32_t esc_len = uint32_t(end - g.esc);
+  const uint32_t s_h = kCiera ? coded_before(pu0, s_bits, s_rank, log2B, nb, nch) : pu0;
+  const bool last_with_data = pu0 + kPartUnits >= nunits;
+  // slots of the part's own units (a block may span several parts)
+  const uint32_t s_next = kCiera ? coded_before(pu0 + kPartUnits, s_bits, s_rank, log2B, nb, nch)
+                                 : min(pu0 + kPartUnits, nunits);
+  const uint32_t sbase = s_h;  // a multiple of 8 for a part holding values
+  const uint32_t stage_len = (s_next + 7u) / 8u * 8u - sbase;  // <= kPartUnits + 8
 
-  uint2 smv[kUnitsPerThread], ev[kUnitsPerThread];
-  uint32_t cnt[kUnitsPerThread], base[kUnitsPerThread], emask[kUnitsPerThread];
+  // Issue every load before using any: sign+mantissa and, for unchanged
+  // blocks, the receiver cache into registers; the part's plane bytes into
+  // LDS; the planes before the part for its escape offset.
+  uint2 smv[kUPT], ev[kUPT];
+  const bool full = 8u * (pu0 + kPartUnits) <= nc;
 #pragma unroll
-  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-    const uint32_t u = j * kThreads + tid;
-    cnt[j] = 0u;
-    emask[j] = 0u;
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
     smv[j] = make_uint2(0u, 0u);
     ev[j] = make_uint2(0u, 0u);
+    if (full || u < nunits) {
+      const uint32_t valid = full ? 8u : min(8u, nc - 8u * u);
+      smv[j] = load_bytes8(in + g.sm + 8ull * u, valid);
+      if (kCiera) {
+        const uint32_t blk = (8u * u) >> log2B;
+        if (!((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) ev[j] = load_bytes8(cache + start + 8ull * u, valid);
+      }
+    }
+  }
+  // code-0 slots before this part: every such slot is a real value
+  uint32_t zeros = 0;
+  for (uint32_t i = tid; i < sbase / 8u; i += kPartThreads) {
+    const uint2 a = *reinterpret_cast<const uint2*>(in + g.plane + 8u * i);
+    const uint2 b = *reinterpret_cast<const uint2*>(in + g.plane + pb + 8u * i);
+    const uint2 d = *reinterpret_cast<const uint2*>(in + g.plane + 2u * pb + 8u * i);
+    zeros += __popc(~(a.x | b.x | d.x)) + __popc(~(a.y | b.y | d.y));
+  }
+  for (uint32_t i = tid; i < 3u * (stage_len / 8u); i += kPartThreads) {
+    const uint32_t b = i / (stage_len / 8u);
+    const uint32_t off = 8u * (i - b * (stage_len / 8u));
+    *reinterpret_cast<uint2*>(s_planes + b * kStage + off) =
+        *reinterpret_cast<const uint2*>(in + g.plane + b * pb + sbase + off);
+  }
+  zeros = wave_sum_u32(zeros);
+  if (lane_id() == 0u) s_red[tid >> 6] = zeros;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPartWaves; w++) before += s_red[w];
+
+  uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
+    cnt[j] = 0u;
+    emask[j] = 0u;
     if (u >= nunits) continue;
-    const uint32_t valid = min(8u, nc - 8u * u);
-    smv[j] = load_bytes8(in + g.sm + 8ull * u, valid);
     bool coded = true;
-    uint64_t pbyte = u;
+    uint32_t pbyte = u;
     if (kCiera) {
       const uint32_t blk = (8u * u) >> log2B;
-      const uint32_t word = s_bits[blk >> 5];
-      coded = (word >> (blk & 31u)) & 1u;
-      const uint32_t rank = s_rank[blk >> 5] + __popc(word & ((1u << (blk & 31u)) - 1u));
-      pbyte = uint64_t(rank) * (B / 8u) + (u & (B / 8u - 1u));
+      coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
+      pbyte = coded_before(u, s_bits, s_rank, log2B, nb, nch);
     }
     if (coded) {
-      const uint32_t p0 = in[g.plane + pbyte];
-      const uint32_t p1 = in[g.plane + g.plane_bytes + pbyte];
-      const uint32_t p2 = in[g.plane + 2u * g.plane_bytes + pbyte];
+      const uint32_t at = pbyte - sbase;
+      const uint32_t p0 = s_planes[at];
+      const uint32_t p1 = s_planes[kStage + at];
+      const uint32_t p2 = s_planes[2u * kStage + at];
+      const uint32_t valid = min(8u, nc - 8u * u);
       const uint32_t vmask = (valid == 8u) ? 0xFFu : ((1u << valid) - 1u);
       const uint2 codes = codes_from_planes(p0, p1, p2);
       ev[j] = make_uint2(exps_from_codes(codes.x, e0), exps_from_codes(codes.y, e0));
       emask[j] = ~(p0 | p1 | p2) & vmask;
       cnt[j] = __popc(emask[j]);
-    } else {
-      ev[j] = load_bytes8(cache + start + 8ull * u, valid);
     }
   }
-  const uint32_t nesc = chunk_escape_scan(cnt, base, s_tot);
-  if (g.esc + pad128(nesc) != end) {
-    if (tid == 0) err_slots[c] = uint32_t(CIERA_ERR_FORMAT);
-    return;  // uniform: every thread sees the same nesc
+  const uint32_t pesc = part_escape_scan(cnt, base, s_tot);
+  // every escape read stays inside the chunk's escape section; the part that
+  // holds the chunk's last values also checks the section's padded length
+  const bool bad = (uint64_t(before) + pesc > esc_len) ||
+                   (last_with_data && g.esc + pad128(uint64_t(before) + pesc) != end);
+  if (bad) {
+    if (tid == 0) err_slots[wg] = uint32_t(CIERA_ERR_FORMAT);
+    return;  // uniform
   }
 #pragma unroll
-  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-    const uint32_t u = j * kThreads + tid;
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
     if (u >= nunits) continue;
     const uint32_t valid = min(8u, nc - 8u * u);
     uint2 e = ev[j];
     uint32_t em = emask[j];
-    uint64_t at = g.esc + base[j];
+    uint64_t at = g.esc + before + base[j];
     while (em) {
       const uint32_t k = __builtin_ctz(em);
       em &= em - 1u;
@@ -911,7 +1213,7 @@ __global__ __launch_bounds__(kThreads) void k_decode(const uint8_t* __restrict__
       if ((s_bits[blk >> 5] >> (blk & 31u)) & 1u) store_bytes8(cache + start + 8ull * u, valid, e);
     }
   }
-  if (tid == 0) err_slots[c] = 0u;
+  if (tid == 0) err_slots[wg] = 0u;
 }
 
 // ------------------------------------------------------------------ host side
@@ -973,12 +1275,14 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   }
   hipLaunchKernelGGL(k_plan, dim3(1), dim3(kThreads), 0, stream, n, nchunks, B, e0_override, out, d_out_size, ws);
   if (nchunks) {
+    hipLaunchKernelGGL(k_layout, dim3(uint32_t(cdiv(nchunks, kLayoutThreads))), dim3(kLayoutThreads), 0, stream, n,
+                       nchunks, lb, out, d_out_size, ws);
     if (ciera)
-      hipLaunchKernelGGL(k_write<true>, dim3(uint32_t(nchunks)), dim3(kThreads), 0, stream, x, n, nchunks, lb, out,
-                         d_out_size, ws);
+      hipLaunchKernelGGL(k_write<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), 0, stream, x, n, lb,
+                         out, ws);
     else
-      hipLaunchKernelGGL(k_write<false>, dim3(uint32_t(nchunks)), dim3(kThreads), 0, stream, x, n, nchunks, 0u,
-                         out, d_out_size, ws);
+      hipLaunchKernelGGL(k_write<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), 0, stream, x, n, 0u,
+                         out, ws);
   }
   return launch_status();
 }
@@ -994,15 +1298,15 @@ ciera_status decode_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t
   const uint64_t nchunks = cdiv(n, kChunk);
   if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
   const Ws ws = ws_bind(d_ws, nchunks);
-  const uint32_t grid = uint32_t(nchunks ? nchunks : 1u);
+  const uint32_t grid = uint32_t(nchunks ? nchunks * kParts : 1u);
   const uint8_t* in = static_cast<const uint8_t*>(d_in);
   uint16_t* y = static_cast<uint16_t*>(d_y);
   (void)hipGetLastError();
   if (ciera)
-    hipLaunchKernelGGL(k_decode<true>, dim3(grid), dim3(kThreads), 0, stream, in, in_size, y, n, nchunks, log2u(B),
+    hipLaunchKernelGGL(k_decode<true>, dim3(grid), dim3(kPartThreads), 0, stream, in, in_size, y, n, nchunks, log2u(B),
                        d_cache, &ws.ctrl->n_err_slots, ws.err);
   else
-    hipLaunchKernelGGL(k_decode<false>, dim3(grid), dim3(kThreads), 0, stream, in, in_size, y, n, nchunks, 0u,
+    hipLaunchKernelGGL(k_decode<false>, dim3(grid), dim3(kPartThreads), 0, stream, in, in_size, y, n, nchunks, 0u,
                        nullptr, &ws.ctrl->n_err_slots, ws.err);
   return launch_status();
 }
@@ -1067,7 +1371,7 @@ ciera_status ciera_read_error(const void* d_ws, hipStream_t stream) {
       hipStreamSynchronize(stream) != hipSuccess)
     return CIERA_ERR_HIP;
   if (slots == 0u) return CIERA_OK;
-  if (slots > cdiv(kMaxN, kChunk)) return CIERA_ERR_INTERNAL;
+  if (slots > kParts * cdiv(kMaxN, kChunk)) return CIERA_ERR_INTERNAL;
   const uint32_t* err = reinterpret_cast<const uint32_t*>(static_cast<const uint8_t*>(d_ws) + sizeof(Ctrl));
   uint32_t worst = 0;
   uint32_t buf[4096];
