@@ -1004,6 +1004,160 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
 }
 
 // ------------------------------------------------------------------ k_decode
+// Escape bytes a decoding part stages in LDS.  A chunk's escape section of at
+// most kEscWhole bytes is loaded whole, together with the part's other loads;
+// a longer one is staged as a window starting at the part's first escape,
+// which holds all of the part's escapes (a part has kPartUnits * 8 values).
+constexpr uint32_t kEscStage = kPartUnits * 8u;
+constexpr uint32_t kEscWhole = 16u * kPartThreads;
+constexpr uint32_t kPlaneRounds = (3u * (kStage / 8u) + kPartThreads - 1u) / kPartThreads;
+
+struct DecodePart {
+  const uint8_t* in;
+  uint16_t* y;
+  uint8_t* cache;
+  ChunkGeom g;
+  uint64_t start;
+  uint32_t nc, nunits, pu0, e0, pb, esc_len, sbase, stage_len;
+  bool last_with_data;
+  uint32_t log2B, nb, nch;
+};
+
+// Decode one part.  kFull: every unit of the part holds 8 values, so no
+// per-unit tail handling.  Returns the part's status word.
+template <bool kCiera, bool kFull>
+__device__ __attribute__((always_inline)) inline uint32_t decode_part(const DecodePart& p, const uint32_t* s_bits,
+                                                                      const uint32_t* s_rank, uint8_t* s_planes,
+                                                                      uint8_t* s_esc, uint32_t* s_tot,
+                                                                      uint32_t* s_red) {
+  const uint32_t tid = threadIdx.x;
+  const uint8_t* __restrict__ in = p.in;
+  const ChunkGeom& g = p.g;
+  // Issue every load before using any: sign+mantissa and, for unchanged
+  // blocks, the receiver cache into registers; the part's plane bytes, a
+  // small escape section, and the planes before the part (for its escape
+  // offset).
+  uint2 smv[kUPT], ev[kUPT];
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = p.pu0 + j * kPartThreads + tid;
+    smv[j] = make_uint2(0u, 0u);
+    ev[j] = make_uint2(0u, 0u);
+    if (kFull || u < p.nunits) {
+      const uint32_t valid = kFull ? 8u : min(8u, p.nc - 8u * u);
+      smv[j] = load_bytes8(in + g.sm + 8ull * u, valid);
+      if (kCiera) {
+        const uint32_t blk = (8u * u) >> p.log2B;
+        if (!((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) ev[j] = load_bytes8(p.cache + p.start + 8ull * u, valid);
+      }
+    }
+  }
+  const bool esc_whole = p.esc_len <= kEscWhole;
+  const uint32_t np = p.stage_len / 8u;  // 8-byte pieces per plane, <= kStage / 8
+  uint2 st[kPlaneRounds];
+#pragma unroll
+  for (uint32_t r = 0; r < kPlaneRounds; r++) {
+    const uint32_t i = tid + r * kPartThreads;
+    if (i < 3u * np) {
+      const uint32_t b = i / np;
+      st[r] = *reinterpret_cast<const uint2*>(in + g.plane + b * p.pb + p.sbase + 8u * (i - b * np));
+    }
+  }
+  uint4 se = make_uint4(0u, 0u, 0u, 0u);
+  if (esc_whole && tid < p.esc_len / 16u) se = *reinterpret_cast<const uint4*>(in + g.esc + 16u * tid);
+  // code-0 slots before this part: every such slot is a real value
+  uint32_t zeros = 0;
+  for (uint32_t i = tid; i < p.sbase / 8u; i += kPartThreads) {
+    const uint2 a = *reinterpret_cast<const uint2*>(in + g.plane + 8u * i);
+    const uint2 b = *reinterpret_cast<const uint2*>(in + g.plane + p.pb + 8u * i);
+    const uint2 d = *reinterpret_cast<const uint2*>(in + g.plane + 2u * p.pb + 8u * i);
+    zeros += __popc(~(a.x | b.x | d.x)) + __popc(~(a.y | b.y | d.y));
+  }
+#pragma unroll
+  for (uint32_t r = 0; r < kPlaneRounds; r++) {
+    const uint32_t i = tid + r * kPartThreads;
+    if (i < 3u * np) {
+      const uint32_t b = i / np;
+      *reinterpret_cast<uint2*>(s_planes + b * kStage + 8u * (i - b * np)) = st[r];
+    }
+  }
+  if (esc_whole && tid < p.esc_len / 16u) reinterpret_cast<uint4*>(s_esc)[tid] = se;
+  zeros = wave_sum_u32(zeros);
+  if (lane_id() == 0u) s_red[tid >> 6] = zeros;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPartWaves; w++) before += s_red[w];
+  // staged byte range [esc_lo, esc_hi) of the escape section; a long section
+  // is staged from the 16-byte boundary at or below the part's first escape
+  uint32_t esc_lo = 0, esc_hi = p.esc_len;
+  if (!esc_whole) {  // uniform
+    esc_lo = min(before, p.esc_len) & ~15u;
+    esc_hi = min(esc_lo + kEscStage, p.esc_len);
+    const uint32_t pieces = (esc_hi - esc_lo) / 16u;  // the section length is a multiple of 128
+#pragma unroll 4
+    for (uint32_t i = tid; i < pieces; i += kPartThreads)
+      reinterpret_cast<uint4*>(s_esc)[i] = *reinterpret_cast<const uint4*>(in + g.esc + esc_lo + 16u * i);
+    __syncthreads();
+  }
+
+  uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = p.pu0 + j * kPartThreads + tid;
+    cnt[j] = 0u;
+    emask[j] = 0u;
+    if (!kFull && u >= p.nunits) continue;
+    bool coded = true;
+    uint32_t pbyte = u;
+    if (kCiera) {
+      const uint32_t blk = (8u * u) >> p.log2B;
+      coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
+      pbyte = coded_before(u, s_bits, s_rank, p.log2B, p.nb, p.nch);
+    }
+    if (coded) {
+      const uint32_t at = pbyte - p.sbase;
+      const uint32_t p0 = s_planes[at];
+      const uint32_t p1 = s_planes[kStage + at];
+      const uint32_t p2 = s_planes[2u * kStage + at];
+      const uint32_t vmask = kFull ? 0xFFu : ((min(8u, p.nc - 8u * u) == 8u) ? 0xFFu
+                                                                           : ((1u << (p.nc - 8u * u)) - 1u));
+      const uint2 codes = codes_from_planes(p0, p1, p2);
+      ev[j] = make_uint2(exps_from_codes(codes.x, p.e0), exps_from_codes(codes.y, p.e0));
+      emask[j] = ~(p0 | p1 | p2) & vmask;
+      cnt[j] = __popc(emask[j]);
+    }
+  }
+  const uint32_t pesc = part_escape_scan(cnt, base, s_tot);
+  // every escape read stays inside the chunk's escape section; the part that
+  // holds the chunk's last values also checks the section's padded length
+  const bool bad = (uint64_t(before) + pesc > p.esc_len) ||
+                   (p.last_with_data && g.esc + pad128(uint64_t(before) + pesc) != g.esc + p.esc_len);
+  if (bad) return uint32_t(CIERA_ERR_FORMAT);  // uniform
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = p.pu0 + j * kPartThreads + tid;
+    if (!kFull && u >= p.nunits) continue;
+    const uint32_t valid = kFull ? 8u : min(8u, p.nc - 8u * u);
+    uint2 e = ev[j];
+    uint32_t em = emask[j];
+    uint32_t at = before + base[j];
+    while (em) {
+      const uint32_t k = __builtin_ctz(em);
+      em &= em - 1u;
+      const uint32_t b = (at >= esc_lo && at < esc_hi) ? uint32_t(s_esc[at - esc_lo]) : uint32_t(in[g.esc + at]);
+      e = set_byte(e, k, b);
+      at++;
+    }
+    store_unit(p.y, p.start + 8ull * u, valid, unit_join(smv[j], e));
+    if (kCiera) {
+      const uint32_t blk = (8u * u) >> p.log2B;
+      if ((s_bits[blk >> 5] >> (blk & 31u)) & 1u) store_bytes8(p.cache + p.start + 8ull * u, valid, e);
+    }
+  }
+  return 0u;
+}
+
 // One part of a chunk; parts never wait on each other.  A part's first escape
 // is found by counting the code-0 slots of the plane bytes before its own.
 template <bool kCiera>
@@ -1013,6 +1167,7 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
                                                          uint64_t* __restrict__ n_err_slots,
                                                          uint32_t* __restrict__ err_slots) {
   __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_esc[kEscStage];
   __shared__ uint32_t s_ok;    // header and table entries are consistent
   __shared__ uint32_t s_fits;  // the chunk's fixed-size sections lie inside it
   __shared__ uint32_t s_e0;
@@ -1115,105 +1270,30 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   // slots of the part's own units (a block may span several parts)
   const uint32_t s_next = kCiera ? coded_before(pu0 + kPartUnits, s_bits, s_rank, log2B, nb, nch)
                                  : min(pu0 + kPartUnits, nunits);
-  const uint32_t sbase = s_h;  // a multiple of 8 for a part holding values
-  const uint32_t stage_len = (s_next + 7u) / 8u * 8u - sbase;  // <= kPartUnits + 8
-
-  // Issue every load before using any: sign+mantissa and, for unchanged
-  // blocks, the receiver cache into registers; the part's plane bytes into
-  // LDS; the planes before the part for its escape offset.
-  uint2 smv[kUPT], ev[kUPT];
-  const bool full = 8u * (pu0 + kPartUnits) <= nc;
-#pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
-    smv[j] = make_uint2(0u, 0u);
-    ev[j] = make_uint2(0u, 0u);
-    if (full || u < nunits) {
-      const uint32_t valid = full ? 8u : min(8u, nc - 8u * u);
-      smv[j] = load_bytes8(in + g.sm + 8ull * u, valid);
-      if (kCiera) {
-        const uint32_t blk = (8u * u) >> log2B;
-        if (!((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) ev[j] = load_bytes8(cache + start + 8ull * u, valid);
-      }
-    }
-  }
-  // code-0 slots before this part: every such slot is a real value
-  uint32_t zeros = 0;
-  for (uint32_t i = tid; i < sbase / 8u; i += kPartThreads) {
-    const uint2 a = *reinterpret_cast<const uint2*>(in + g.plane + 8u * i);
-    const uint2 b = *reinterpret_cast<const uint2*>(in + g.plane + pb + 8u * i);
-    const uint2 d = *reinterpret_cast<const uint2*>(in + g.plane + 2u * pb + 8u * i);
-    zeros += __popc(~(a.x | b.x | d.x)) + __popc(~(a.y | b.y | d.y));
-  }
-  for (uint32_t i = tid; i < 3u * (stage_len / 8u); i += kPartThreads) {
-    const uint32_t b = i / (stage_len / 8u);
-    const uint32_t off = 8u * (i - b * (stage_len / 8u));
-    *reinterpret_cast<uint2*>(s_planes + b * kStage + off) =
-        *reinterpret_cast<const uint2*>(in + g.plane + b * pb + sbase + off);
-  }
-  zeros = wave_sum_u32(zeros);
-  if (lane_id() == 0u) s_red[tid >> 6] = zeros;
-  __syncthreads();
-  uint32_t before = 0;
-#pragma unroll
-  for (uint32_t w = 0; w < kPartWaves; w++) before += s_red[w];
-
-  uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
-#pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
-    cnt[j] = 0u;
-    emask[j] = 0u;
-    if (u >= nunits) continue;
-    bool coded = true;
-    uint32_t pbyte = u;
-    if (kCiera) {
-      const uint32_t blk = (8u * u) >> log2B;
-      coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
-      pbyte = coded_before(u, s_bits, s_rank, log2B, nb, nch);
-    }
-    if (coded) {
-      const uint32_t at = pbyte - sbase;
-      const uint32_t p0 = s_planes[at];
-      const uint32_t p1 = s_planes[kStage + at];
-      const uint32_t p2 = s_planes[2u * kStage + at];
-      const uint32_t valid = min(8u, nc - 8u * u);
-      const uint32_t vmask = (valid == 8u) ? 0xFFu : ((1u << valid) - 1u);
-      const uint2 codes = codes_from_planes(p0, p1, p2);
-      ev[j] = make_uint2(exps_from_codes(codes.x, e0), exps_from_codes(codes.y, e0));
-      emask[j] = ~(p0 | p1 | p2) & vmask;
-      cnt[j] = __popc(emask[j]);
-    }
-  }
-  const uint32_t pesc = part_escape_scan(cnt, base, s_tot);
-  // every escape read stays inside the chunk's escape section; the part that
-  // holds the chunk's last values also checks the section's padded length
-  const bool bad = (uint64_t(before) + pesc > esc_len) ||
-                   (last_with_data && g.esc + pad128(uint64_t(before) + pesc) != end);
-  if (bad) {
-    if (tid == 0) err_slots[wg] = uint32_t(CIERA_ERR_FORMAT);
-    return;  // uniform
-  }
-#pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
-    if (u >= nunits) continue;
-    const uint32_t valid = min(8u, nc - 8u * u);
-    uint2 e = ev[j];
-    uint32_t em = emask[j];
-    uint64_t at = g.esc + before + base[j];
-    while (em) {
-      const uint32_t k = __builtin_ctz(em);
-      em &= em - 1u;
-      e = set_byte(e, k, in[at++]);
-    }
-    store_unit(y, start + 8ull * u, valid, unit_join(smv[j], e));
-    if (kCiera) {
-      const uint32_t blk = (8u * u) >> log2B;
-      if ((s_bits[blk >> 5] >> (blk & 31u)) & 1u) store_bytes8(cache + start + 8ull * u, valid, e);
-    }
-  }
-  if (tid == 0) err_slots[wg] = 0u;
+  DecodePart p;
+  p.in = in;
+  p.y = y;
+  p.cache = cache;
+  p.g = g;
+  p.start = start;
+  p.nc = nc;
+  p.nunits = nunits;
+  p.pu0 = pu0;
+  p.e0 = e0;
+  p.pb = pb;
+  p.esc_len = esc_len;
+  p.sbase = s_h;  // a multiple of 8 for a part holding values
+  p.stage_len = (s_next + 7u) / 8u * 8u - s_h;  // <= kPartUnits + 8
+  p.last_with_data = last_with_data;
+  p.log2B = log2B;
+  p.nb = nb;
+  p.nch = nch;
+  uint32_t err;
+  if (8u * (pu0 + kPartUnits) <= nc)
+    err = decode_part<kCiera, true>(p, s_bits, s_rank, s_planes, s_esc, s_tot, s_red);
+  else
+    err = decode_part<kCiera, false>(p, s_bits, s_rank, s_planes, s_esc, s_tot, s_red);
+  if (tid == 0) err_slots[wg] = err;
 }
 
 // ------------------------------------------------------------------ host side
