@@ -9,9 +9,10 @@ exponent reuse; their steps alternate between two consecutive iterations so
 the caches always hold the previous iteration.
 
 Prints one JSON line.  ``value`` = 2 n K / (wall time of K steps), in GB/s of
-BF16 input (1 GB = 1e9 bytes).  ``roofline`` describes the dominant kernel,
-timed with HIP events on the stream it runs on; ``cpu_baseline`` times the
-plain CPU oracle (single thread) on the same tensor.
+BF16 input (1 GB = 1e9 bytes).  A second pass of the same K steps times every
+kernel with HIP events recorded at the kernel's own start and end;
+``roofline`` describes the kernel with the longest average duration.
+``cpu_baseline`` times the plain CPU oracle (single thread) on the same tensor.
 """
 from __future__ import annotations
 
@@ -40,17 +41,66 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+KERNELS = ["k_stats", "k_plan", "k_layout", "k_write", "k_decode"]
+
+
+def measured_bandwidth(torch, dev, nbytes=2 << 30, reps=5):
+    """Practical HBM bandwidth in the same run: a streaming copy-like kernel
+    (reads and writes nbytes) and a read-only reduction (reads nbytes), each
+    the best of reps, in GB/s of bytes moved."""
+    a = torch.full((nbytes // 4,), 1, dtype=torch.int32, device=dev)
+    b = torch.empty_like(a)
+    af = torch.ones((nbytes // 4,), dtype=torch.float32, device=dev)
+    r = torch.empty((), dtype=torch.float32, device=dev)
+
+    def best(fn):
+        t = []
+        for _ in range(reps + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return min(t[1:]) * 1e-3
+
+    copy = 2 * nbytes / best(lambda: torch.bitwise_not(a, out=b)) / 1e9
+    read = nbytes / best(lambda: torch.sum(af, dim=0, out=r)) / 1e9
+    del a, b, af
+    return copy, read
+
+
+def changed_values(prev, cur, B):
+    """Values in blocks whose exponents changed between two iterations."""
+    import numpy as np
+    n = prev.size
+    nb = -(-n // B)
+    diff = ((prev ^ cur) & 0x7F80) != 0
+    pad = np.zeros(nb * B, dtype=bool)
+    pad[:n] = diff
+    blk = pad.reshape(nb, B).any(axis=1)
+    sizes = np.full(nb, B, dtype=np.int64)
+    sizes[-1] = n - (nb - 1) * B
+    return int(sizes[blk].sum())
+
+
 def load_traffic(kernel: str, workload: int, B: int):
-    """Counter-derived HBM bytes per launch from profiles/traffic.json, if
-    they were taken on the current kernel source."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    with open(path) as f:
-        rec = json.load(f)
-    if rec.get("source_hash") != source_hash():
-        return None
-    return rec.get("kernels", {}).get(f"{kernel}/w{workload}/B{B}")
+    """Counter-derived HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled
+    by a copy kernel of known size) from the ```json blocks of the traffic
+    summaries in profiles/, if they were taken on the current kernel source."""
+    import glob
+    import re
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
+        with open(path) as f:
+            text = f.read()
+        for block in re.findall(r"```json\n(.*?)```", text, flags=re.S):
+            rec = json.loads(block)
+            if rec.get("source_hash") != source_hash():
+                continue
+            hit = rec.get("kernels", {}).get(f"{kernel}/w{workload}/B{B}")
+            if hit is not None:
+                return hit
+    return None
 
 
 def main() -> int:
@@ -62,6 +112,9 @@ def main() -> int:
     ap.add_argument("--block", type=int, default=None, help="block size B for the reuse workloads")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--verify", action="store_true", help="check the last step's round trip on the host")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="after timing, run a plain elementwise kernel that reads and writes MIB MiB each "
+                         "(reference dispatch for calibrating hardware byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -153,24 +206,38 @@ def main() -> int:
         step(s)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    # Pass 2, per-call durations: HIP events around every encode and decode
-    # call on the stream the kernels run on (the event markers add small gaps,
-    # so this pass is not the headline).
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    # Pass 2, the same K steps with every kernel timed by HIP events that the
+    # runtime records at the kernel's own start and end (hipExtLaunchKernel);
+    # a step launches encode's four kernels, then decode's one.
+    names = KERNELS
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
+          for _ in range(K)]
+    ciera.ciera_time_kernels([pair for row in ev for pair in row], stream=stream)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
     for s in range(K):
         k = (K + s + 1) % 2 if mode != "zip3" else 0  # continues the alternation of pass 1
-        ev[s][0].record(stream)
         enc[k]()
-        ev[s][1].record(stream)
         dec[k]()
-        ev[s][2].record(stream)
     torch.cuda.synchronize()
-    enc_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in range(K)]
-    dec_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in range(K)]
+    wall2 = time.perf_counter() - t2
+    ciera.ciera_time_kernels([])
+    kern_ms = {nm: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(K)) / K for i, nm in enumerate(names)}
+    enc_ms = [ev[s][0][0].elapsed_time(ev[s][3][1]) for s in range(K)]  # k_stats start .. k_write end
+    dec_ms = [ev[s][4][0].elapsed_time(ev[s][4][1]) for s in range(K)]
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
     if args.verify:
         klast = (2 * K) % 2 if mode != "zip3" else 0  # input of the last step, index 2K-1
         assert torch.equal(y, xs[klast]), "round trip failed"
+
+    if args.copy_probe:
+        a = torch.full((args.copy_probe << 19,), 3, dtype=torch.int16, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.bitwise_not(a, out=b)
+        torch.cuda.synchronize()
+        del a, b
+    bw_copy, bw_read = measured_bandwidth(torch, dev)
 
     in_bytes = 2 * n
     value = in_bytes * K / wall / 1e9
@@ -179,17 +246,30 @@ def main() -> int:
     stream_bytes = sizes[1 if mode != "zip3" else 0]
     ratio = in_bytes / stream_bytes
 
-    # Dominant kernel: the decode kernel is one launch per decode call, so
-    # the events around the call time exactly that kernel.  Its algorithmic
-    # bytes: the whole stream read once + the BF16 output written (+ for
-    # exponent reuse the receiver cache: read for unchanged blocks, written
-    # for changed ones, n bytes in total).
-    dec_bytes = stream_bytes + in_bytes + (n if mode != "zip3" else 0)
-    dec_gbps = dec_bytes / (dec_avg * 1e-3) / 1e9
-    roofline = {"kernel": "k_decode", "bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                "traffic": load_traffic("k_decode", args.workload, B),
-                "algorithmic_bytes_per_launch": dec_bytes, "avg_launch_ms": round(dec_avg, 5)}
+    # Algorithmic bytes per launch of each streaming kernel: what the method
+    # must move.  k_stats reads x (+ the sender cache, and rewrites the
+    # exponents of changed blocks); k_write reads x and writes the stream;
+    # k_decode reads the stream and writes y (+ the receiver cache: read for
+    # unchanged blocks, written for changed ones, n bytes in total).
+    changed_vals = 0
+    if mode != "zip3":
+        changed_vals = changed_values(pair[0], pair[1], B)
+    alg = {
+        "k_stats": in_bytes + (n + changed_vals if mode != "zip3" else 0),
+        "k_write": in_bytes + stream_bytes,
+        "k_decode": stream_bytes + in_bytes + (n if mode != "zip3" else 0),
+    }
+    dom = max(alg, key=lambda nm: kern_ms[nm])
+    dom_gbps = alg[dom] / (kern_ms[dom] * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+                "traffic": load_traffic(dom, args.workload, B),
+                "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": round(kern_ms[dom], 5),
+                "frac_of_measured_copy": round(dom_gbps / bw_copy, 4)}
+    kernels = {nm: {"avg_ms": round(kern_ms[nm], 5)} for nm in names}
+    for nm, by in alg.items():
+        kernels[nm]["algorithmic_bytes"] = by
+        kernels[nm]["GBps"] = round(by / (kern_ms[nm] * 1e-3) / 1e9, 1)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -233,6 +313,9 @@ def main() -> int:
         "decode_ms": round(dec_avg, 5),
         "compression_ratio": round(ratio, 4),
         "stream_bytes": stream_bytes,
+        "pass2_ms_per_step": round(wall2 * 1e3 / K, 4),
+        "kernels": kernels,
+        "bw_measured_GBps": {"copy": round(bw_copy, 1), "read": round(bw_read, 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "source_hash": source_hash(),

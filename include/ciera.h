@@ -133,6 +133,17 @@ ciera_status ciera_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_
  * stream), CIERA_ERR_INTERNAL, or CIERA_ERR_HIP if the copy fails. */
 ciera_status ciera_read_error(const void* d_ws, hipStream_t stream);
 
+/* Kernel timing, a profiling aid (not part of the codec).  events holds
+ * n_pairs (start, stop) pairs of hipEvent_t handles, created with timing
+ * enabled and owned by the caller.  The next n_pairs kernel launches made by
+ * the calling host thread through this library (any entry point: encode
+ * launches four kernels, decode one) each take the next pair, which the HIP
+ * runtime records at that kernel's start and end (hipExtLaunchKernel);
+ * hipEventElapsedTime then gives the kernel's own duration.  The handles are
+ * copied; a later call replaces the queue, n_pairs = 0 clears it.  Returns
+ * CIERA_ERR_ARG for a null array or handle. */
+ciera_status ciera_time_kernels(void* const* events, uint32_t n_pairs);
+
 /* Human-readable name of a status code (static storage). */
 const char* ciera_status_string(ciera_status status);
 

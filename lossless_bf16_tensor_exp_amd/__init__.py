@@ -17,6 +17,7 @@ Same names as the C ABI::
     ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None)
     ciera_decode(inp, in_size, y, B, prev_exp, ws, stream=None)
     ciera_read_error(ws, stream=None)
+    ciera_time_kernels(pairs)             (profiling: per-kernel start/stop events)
 
 ``x``/``y`` are CUDA(HIP) tensors of dtype bfloat16, int16 or uint16 holding
 the BF16 patterns; ``out``/``inp``/``ws``/``prev_exp`` are uint8 tensors and
@@ -31,7 +32,7 @@ __all__ = [
     "CieraError", "library_path", "load_library",
     "zip3_max_encoded_size", "ciera_max_encoded_size", "zip3_workspace_size", "ciera_workspace_size",
     "zip3_encode", "zip3_decode", "ciera_encode", "ciera_decode", "ciera_read_error", "ciera_status_string",
-    "bind",
+    "bind", "ciera_time_kernels",
     "CHUNK",
 ]
 
@@ -76,6 +77,7 @@ def load_library():
         "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, vp],
         "ciera_decode": [vp, u64, vp, u64, u32, vp, vp, u64, vp],
         "ciera_read_error": [vp, vp],
+        "ciera_time_kernels": [ctypes.POINTER(vp), u32],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -216,3 +218,20 @@ def ciera_read_error(ws, stream=None) -> int:
     """Synchronise the stream and return the device-side status word."""
     _check_bytes(ws, "ws")
     return load_library().ciera_read_error(_ptr(ws), _stream(stream))
+
+
+def ciera_time_kernels(pairs, stream=None) -> None:
+    """Queue (start, stop) ``torch.cuda.Event(enable_timing=True)`` pairs: the
+    next ``len(pairs)`` kernel launches of this thread each record one pair at
+    the kernel's own start and end.  Events not yet backed by a HIP event are
+    recorded once on ``stream`` first so that their handles exist."""
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    handles = []
+    for a, b in pairs:
+        for e in (a, b):
+            if not e.cuda_event:
+                e.record(s)
+            handles.append(e.cuda_event)
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    _raise(load_library().ciera_time_kernels(arr, len(pairs)), "ciera_time_kernels")

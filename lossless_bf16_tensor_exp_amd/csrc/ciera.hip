@@ -34,10 +34,13 @@
 // input.  Blocks (B >= 64) never split a unit, and chunks never split a
 // block.  All data movement is integer: sign, NaN payloads, subnormals and -0
 // never pass through floating-point registers.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
 #include <string.h>
+
+#include <vector>
 
 #include "ciera.h"
 
@@ -1158,6 +1161,19 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   return 0u;
 }
 
+// Workgroups are dispatched round-robin over the chip's 8 XCDs, each with its
+// own L2.  Decode maps workgroup b to (chunk, part) so that the kParts parts of
+// a chunk share one XCD: a part reads the plane bytes of the parts before it,
+// which then come from that L2 instead of HBM.  Chunks past the last full
+// group of 8 keep the plain mapping.
+constexpr uint32_t kXcds = 8u;
+__device__ inline uint2 decode_part_of(uint32_t b, uint64_t nchunks) {
+  const uint64_t grouped = nchunks / kXcds * kXcds * kParts;
+  if (b >= grouped) return make_uint2(b / kParts, b % kParts);
+  const uint32_t x = b % kXcds, slot = b / kXcds;
+  return make_uint2((slot / kParts) * kXcds + x, slot % kParts);
+}
+
 // One part of a chunk; parts never wait on each other.  A part's first escape
 // is found by counting the code-0 slots of the plane bytes before its own.
 template <bool kCiera>
@@ -1178,8 +1194,9 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   __shared__ uint32_t s_red[kPartWaves];
   const uint32_t tid = threadIdx.x;
   const uint32_t wg = blockIdx.x;
-  const uint32_t c = wg / kParts;
-  const uint32_t h = wg % kParts;
+  const uint2 ch = decode_part_of(wg, nchunks);
+  const uint32_t c = ch.x;
+  const uint32_t h = ch.y;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint64_t base_off = table_end(nchunks);
   if (tid == 0) {
@@ -1328,6 +1345,23 @@ ciera_status launch_status() {
   return hipGetLastError() == hipSuccess ? CIERA_OK : CIERA_ERR_HIP;
 }
 
+// Kernel timing on request: each launch takes the next (start, stop) pair of
+// the calling thread's queue, if any, and has the runtime record the pair at
+// the kernel's own start and end.
+thread_local std::vector<hipEvent_t> t_events;
+thread_local size_t t_next_event = 0;
+
+template <typename... P, typename... A>
+void launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A... args) {
+  if (t_next_event + 2u <= t_events.size()) {
+    hipEvent_t start = t_events[t_next_event], stop = t_events[t_next_event + 1u];
+    t_next_event += 2u;
+    hipExtLaunchKernelGGL(kernel, grid, block, 0u, stream, start, stop, 0u, static_cast<P>(args)...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, 0, stream, static_cast<P>(args)...);
+  }
+}
+
 ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cache, void* d_out,
                          uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
                          int e0_override, hipStream_t stream) {
@@ -1349,20 +1383,18 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   (void)hipGetLastError();
   if (nchunks) {
     if (ciera)
-      hipLaunchKernelGGL(k_stats<true>, dim3(uint32_t(nchunks)), dim3(kThreads), 0, stream, x, n, d_cache, lb, ws);
+      launch(k_stats<true>, dim3(uint32_t(nchunks)), dim3(kThreads), stream, x, n, d_cache, lb, ws);
     else
-      hipLaunchKernelGGL(k_stats<false>, dim3(uint32_t(nchunks)), dim3(kThreads), 0, stream, x, n, nullptr, 0u, ws);
+      launch(k_stats<false>, dim3(uint32_t(nchunks)), dim3(kThreads), stream, x, n, nullptr, 0u, ws);
   }
-  hipLaunchKernelGGL(k_plan, dim3(1), dim3(kThreads), 0, stream, n, nchunks, B, e0_override, out, d_out_size, ws);
+  launch(k_plan, dim3(1), dim3(kThreads), stream, n, nchunks, B, e0_override, out, d_out_size, ws);
   if (nchunks) {
-    hipLaunchKernelGGL(k_layout, dim3(uint32_t(cdiv(nchunks, kLayoutThreads))), dim3(kLayoutThreads), 0, stream, n,
-                       nchunks, lb, out, d_out_size, ws);
+    launch(k_layout, dim3(uint32_t(cdiv(nchunks, kLayoutThreads))), dim3(kLayoutThreads), stream, n, nchunks, lb, out,
+           d_out_size, ws);
     if (ciera)
-      hipLaunchKernelGGL(k_write<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), 0, stream, x, n, lb,
-                         out, ws);
+      launch(k_write<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, lb, out, ws);
     else
-      hipLaunchKernelGGL(k_write<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), 0, stream, x, n, 0u,
-                         out, ws);
+      launch(k_write<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, 0u, out, ws);
   }
   return launch_status();
 }
@@ -1383,11 +1415,11 @@ ciera_status decode_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t
   uint16_t* y = static_cast<uint16_t*>(d_y);
   (void)hipGetLastError();
   if (ciera)
-    hipLaunchKernelGGL(k_decode<true>, dim3(grid), dim3(kPartThreads), 0, stream, in, in_size, y, n, nchunks, log2u(B),
-                       d_cache, &ws.ctrl->n_err_slots, ws.err);
+    launch(k_decode<true>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, log2u(B), d_cache,
+           &ws.ctrl->n_err_slots, ws.err);
   else
-    hipLaunchKernelGGL(k_decode<false>, dim3(grid), dim3(kPartThreads), 0, stream, in, in_size, y, n, nchunks, 0u,
-                       nullptr, &ws.ctrl->n_err_slots, ws.err);
+    launch(k_decode<false>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, 0u, nullptr,
+           &ws.ctrl->n_err_slots, ws.err);
   return launch_status();
 }
 
@@ -1464,6 +1496,16 @@ ciera_status ciera_read_error(const void* d_ws, hipStream_t stream) {
       if (buf[i] > worst) worst = buf[i];
   }
   return ciera_status(worst);
+}
+
+ciera_status ciera_time_kernels(void* const* events, uint32_t n_pairs) {
+  if (n_pairs && !events) return CIERA_ERR_ARG;
+  for (uint32_t i = 0; i < 2u * n_pairs; i++)
+    if (!events[i]) return CIERA_ERR_ARG;
+  const hipEvent_t* ev = reinterpret_cast<const hipEvent_t*>(events);
+  t_events.assign(ev, ev + 2u * n_pairs);
+  t_next_event = 0;
+  return CIERA_OK;
 }
 
 const char* ciera_status_string(ciera_status status) {
