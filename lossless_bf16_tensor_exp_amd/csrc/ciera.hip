@@ -1,13 +1,13 @@
 // ciera.hip -- HIP kernels and C ABI of the lossless BF16 codec, gfx950.
 //
 // Encode is four kernels on the caller's stream:
-//   k_stats   one workgroup per 65,536-value chunk, one pass over the input:
-//             FP64 partial sums for the tensor's variance (ZipCCL research
-//             digest, section 3.1: sigma from one standard-deviation pass);
-//             in ciera mode the changed-block bitmap against the sender's
-//             exponent cache and the cache update (CIERA page, section 3.1);
-//             and an exponent histogram of the values to be coded, per
-//             quarter chunk ("part").
+//   k_stats   one workgroup per quarter chunk ("part", 16,384 values), one
+//             pass over the input: FP64 partial sums for the tensor's
+//             variance (ZipCCL research digest, section 3.1: sigma from one
+//             standard-deviation pass); in ciera mode the changed-block bits
+//             against the sender's exponent cache and the cache update (CIERA
+//             page, section 3.1); and an exponent histogram of the values to
+//             be coded.
 //   k_plan    one workgroup: reduces the partial sums in a fixed order and
 //             picks the window base E0 (integer nearest x_opt = log2 sigma +
 //             0.5 log2(14 ln2 / 16383), digest section 3.1, evaluated as
@@ -27,11 +27,9 @@
 // finds its first escape by counting code-0 slots in the planes before it.
 //
 // Work mapping: a "unit" is 8 consecutive values (one 16-byte load).  A chunk
-// has 8192 units.  In k_stats thread t of the 1024-thread workgroup handles
-// units j*1024 + t; in k_write and k_decode part h covers units [2048h,
-// 2048h + 2048) and thread t of its 256 handles unit 2048h + 256j + t
-// (j = 0..7).  Either way each wave instruction moves 1 KiB of contiguous
-// input.  Blocks (B >= 64) never split a unit, and chunks never split a
+// has 8192 units.  In k_stats, k_write and k_decode part h covers units
+// [2048h, 2048h + 2048) and thread t of its 256 handles unit 2048h + 256j + t
+// (j = 0..7), so each wave instruction moves 1 KiB of contiguous input.  Blocks (B >= 64) never split a unit, and chunks never split a
 // block.  All data movement is integer: sign, NaN payloads, subnormals and -0
 // never pass through floating-point registers.
 #include <hip/hip_ext.h>
@@ -47,10 +45,9 @@
 namespace {
 
 constexpr uint32_t kChunk = 65536u;
-constexpr uint32_t kThreads = 1024u;  // k_stats and k_plan
+constexpr uint32_t kThreads = 1024u;  // k_plan
 constexpr uint32_t kWaves = kThreads / 64u;
 constexpr uint32_t kUnitsPerChunk = kChunk / 8u;
-constexpr uint32_t kUnitsPerThread = kUnitsPerChunk / kThreads;  // 8, k_stats
 constexpr uint32_t kBitmapWords = 32u;  // 1024 blocks per chunk at B = 64
 constexpr uint64_t kMaxN = 1ull << 40;
 constexpr uint64_t kHeader = 128u;
@@ -73,13 +70,15 @@ constexpr uint32_t kUPT = 8u;
 constexpr uint32_t kPartUnits = kPartThreads * kUPT;  // 2048 units = 16384 values
 static_assert(kPartUnits * kParts == kUnitsPerChunk, "parts tile a chunk");
 static_assert(kUPT * kPartWaves <= 64u, "one scan entry per lane");
-static_assert(kUnitsPerThread == 2u * kParts, "k_stats row pairs map to parts");
 constexpr uint32_t kStage = kPartUnits + 16u;  // LDS bytes per staged plane
 constexpr uint32_t kPartEscStage = 4096u;      // escape bytes staged in LDS per part
 constexpr uint32_t kBins = 256u;               // exponent histogram bins
-constexpr uint32_t kHistCopies = 8u;           // interleaved LDS copies (by lane) to spread atomics
+constexpr uint32_t kHistCopies = 16u;          // interleaved LDS copies (by lane) to spread atomics
 constexpr uint32_t kLayoutThreads = 256u;      // chunks per k_layout workgroup
-static_assert(kThreads == kParts * kBins, "k_stats stores one (part, bin) per thread");
+static_assert(kPartThreads == kBins, "k_stats stores one bin per thread");
+constexpr uint32_t kPartValues = kPartUnits * 8u;                 // 16384
+constexpr uint32_t kPartBitmapWords = kBitmapWords / kParts;      // 8: one bit per block at B = 64
+static_assert(kPartBitmapWords * 32u * 64u == kPartValues, "a part's blocks fit its bitmap words");
 
 __host__ __device__ inline uint64_t pad128(uint64_t v) { return (v + 127u) & ~uint64_t(127); }
 __host__ __device__ inline uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1u) / b; }
@@ -118,7 +117,7 @@ __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   const uint64_t groups = cdiv(slots, kLayoutThreads);
   l.err = sizeof(Ctrl);
   l.partial = align256(l.err + 4u * kParts * slots);
-  l.bitmap = align256(l.partial + sizeof(Partial) * slots);
+  l.bitmap = align256(l.partial + sizeof(Partial) * kParts * slots);
   l.hist = align256(l.bitmap + 4u * kBitmapWords * slots);
   l.coded = align256(l.hist + 2u * kBins * kParts * slots);
   l.partesc = align256(l.coded + 4u * kParts * slots);
@@ -386,44 +385,93 @@ __device__ inline void stats_checked(const Unit& v, uint32_t cnt, double shift, 
   }
 }
 
+// Changed blocks of a chunk from its parts' partials.  A part holds whole
+// blocks when B <= 16384 and counts them; a larger block spans B / 16384
+// parts, each of which records whether its own share changed.
+__device__ inline uint32_t chunk_changed_blocks(const Partial* part, uint32_t B) {
+  if (B <= kPartValues) return part[0].nch + part[1].nch + part[2].nch + part[3].nch;
+  const uint32_t ppb = B / kPartValues;
+  uint32_t nch = 0;
+  for (uint32_t first = 0; first < kParts; first += ppb) {
+    uint32_t any = 0;
+    for (uint32_t h = first; h < first + ppb; h++) any |= part[h].nch;
+    nch += any ? 1u : 0u;
+  }
+  return nch;
+}
+
+// Word t of a chunk's bitmap (bit j set = block j changed) from the words its
+// parts wrote (pw: kPartBitmapWords per part): part h keeps its own blocks'
+// bits from bit 0 of its first word, or, when a block spans several parts,
+// bit 0 = the part's share changed.
+__device__ inline uint32_t chunk_bitmap_word(const uint32_t* pw, uint32_t t, uint32_t B) {
+  if (32u * t >= kChunk / B) return 0u;  // past the chunk's last possible block
+  if (B * 32u <= kPartValues) {  // 32 or more blocks per part
+    const uint32_t nbp = kPartValues / B;
+    return pw[kPartBitmapWords * ((32u * t) / nbp) + ((32u * t) % nbp) / 32u];
+  }
+  uint32_t w = 0;
+  if (B <= kPartValues) {  // 1..16 blocks per part: chunk bits 0..63
+    const uint32_t nbp = kPartValues / B;
+    for (uint32_t h = 0; h < kParts; h++) {
+      const uint32_t first = h * nbp;
+      if (first / 32u == t) w |= (pw[kPartBitmapWords * h] & ((1u << nbp) - 1u)) << (first % 32u);
+    }
+  } else if (t == 0u) {
+    const uint32_t ppb = B / kPartValues;
+    for (uint32_t h = 0; h < kParts; h++) w |= (pw[kPartBitmapWords * h] & 1u) << (h / ppb);
+  }
+  return w;
+}
+
+// One 256-thread workgroup per part (quarter chunk), units pu0 + 256 j + t.
+// Per part: FP64 variance partials; ciera: changed-block bits against the
+// sender cache and the cache update; an exponent histogram of the values to
+// code; the coded-value count.
 template <bool kCiera>
-__global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
-                                                    uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
-  __shared__ uint32_t s_hist[kParts * kHistCopies * kBins];
-  __shared__ uint32_t s_bits[kBitmapWords];
-  __shared__ uint32_t s_coded[kParts];
-  __shared__ double s_s1[kWaves], s_s2[kWaves];
-  __shared__ uint32_t s_nf[kWaves];
+__global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
+                                                        uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
+  __shared__ uint32_t s_hist[kHistCopies * kBins];
+  __shared__ uint32_t s_bits[kPartBitmapWords];
+  __shared__ double s_s1[kPartWaves], s_s2[kPartWaves];
+  __shared__ uint32_t s_nf[kPartWaves], s_coded[kPartWaves];
   const uint32_t tid = threadIdx.x;
-  const uint32_t c = blockIdx.x;
-  const uint64_t start = uint64_t(c) * kChunk;
+  const uint32_t wg = blockIdx.x;
+  const uint64_t c = wg / kParts;
+  const uint32_t h = wg % kParts;
+  const uint64_t start = c * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
-  for (uint32_t i = tid; i < kParts * kHistCopies * kBins; i += kThreads) s_hist[i] = 0u;
-  if (tid < kBitmapWords) s_bits[tid] = 0u;
-  if (tid < kParts) s_coded[tid] = 0u;
+  const uint32_t pu0 = h * kPartUnits;
+  const bool full = 8u * (pu0 + kPartUnits) <= nc;
+  const uint32_t B = kCiera ? (1u << log2B) : 0u;
+  const uint32_t blk0 = kCiera ? ((8u * pu0) >> log2B) : 0u;  // first block of the part
+  for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
+  if (tid < kPartBitmapWords) s_bits[tid] = 0u;
   const uint32_t first = x[0];
   const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
 
-  // Load: a full chunk issues all of a thread's 16-byte loads before using any.
-  Unit v[kUnitsPerThread];
-  if (nc == kChunk) {
+  // Load: all of a thread's 16-byte loads (and 8-byte cache loads) before use.
+  Unit v[kUPT];
+  uint2 old[kUPT];
+  if (full) {
 #pragma unroll
-    for (uint32_t j = 0; j < kUnitsPerThread; j++) v[j] = load_unit(x, start + 8ull * (j * kThreads + tid), 8u);
+    for (uint32_t j = 0; j < kUPT; j++) v[j] = load_unit(x, start + 8ull * (pu0 + j * kPartThreads + tid), 8u);
+    if (kCiera) {
+#pragma unroll
+      for (uint32_t j = 0; j < kUPT; j++)
+        old[j] = *reinterpret_cast<const uint2*>(cache + start + 8ull * (pu0 + j * kPartThreads + tid));
+    }
   } else {
 #pragma unroll
-    for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-      const uint32_t u = j * kThreads + tid;
+    for (uint32_t j = 0; j < kUPT; j++) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
       v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
-      if (u < nunits) v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
-    }
-  }
-  uint2 old[kUnitsPerThread];
-  if (kCiera) {
-#pragma unroll
-    for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-      const uint32_t u = j * kThreads + tid;
-      old[j] = (u < nunits) ? load_bytes8(cache + start + 8ull * u, min(8u, nc - 8u * u)) : make_uint2(0u, 0u);
+      old[j] = make_uint2(0u, 0u);
+      if (u < nunits) {
+        v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+        if (kCiera) old[j] = load_bytes8(cache + start + 8ull * u, min(8u, nc - 8u * u));
+      }
     }
   }
   __syncthreads();  // LDS cleared
@@ -436,10 +484,10 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
   double s1 = 0.0, s2 = 0.0;
   uint32_t nf = 0;
 #pragma unroll
-  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-    const uint32_t u = j * kThreads + tid;
-    if (u < nunits) {
-      const uint32_t cnt = min(8u, nc - 8u * u);
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
+    if (full || u < nunits) {
+      const uint32_t cnt = full ? 8u : min(8u, nc - 8u * u);
       if (cnt == 8u) {
 #pragma unroll
         for (int i = 0; i < 4; i++) {
@@ -460,8 +508,8 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
         const uint64_t diff = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
         if (diff) {
           store_bytes8(cache + start + 8ull * u, cnt, e);
-          const uint32_t blk = (8u * u) >> log2B;
-          atomicOr(&s_bits[blk >> 5], 1u << (blk & 31u));
+          const uint32_t lb = ((8u * u) >> log2B) - blk0;
+          atomicOr(&s_bits[lb >> 5], 1u << (lb & 31u));
         }
       }
     }
@@ -471,79 +519,102 @@ __global__ __launch_bounds__(kThreads) void k_stats(const uint16_t* __restrict__
     s2 = 0.0;
     nf = 0;
 #pragma unroll
-    for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-      const uint32_t u = j * kThreads + tid;
+    for (uint32_t j = 0; j < kUPT; j++) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
       if (u < nunits) stats_checked(v[j], min(8u, nc - 8u * u), shift, s1, s2, nf);
     }
   }
-  if (kCiera) __syncthreads();  // bitmap complete
+  if (kCiera) __syncthreads();  // the part's block bits are complete
 
-  // Exponent histogram of the values to code, per part (units j*1024 + t with
-  // j in {2h, 2h+1} belong to part h).  Word (part * kBins + bin) *
-  // kHistCopies + copy, copy chosen by lane: equal exponents within a wave
-  // spread over kHistCopies consecutive words, i.e. over as many LDS banks.
-  const uint32_t copy = tid & (kHistCopies - 1u);
-  uint32_t coded[kParts] = {0u, 0u, 0u, 0u};
+  // Exponent histogram of the values to code: all values (zip3); ciera, those
+  // of the part's changed blocks, or all of the part's values when its block
+  // spans several parts (k_layout drops them if the block is unchanged).
+  // Word bin * kHistCopies + copy, copy chosen by lane: equal exponents
+  // within a wave spread over kHistCopies consecutive words (LDS banks).
+  const uint32_t copy4 = 4u * (tid & (kHistCopies - 1u));
+  uint32_t coded = 0;
+  if (!kCiera && full) {
+    // the bin's byte offset straight from the exponent bits of each half
+    constexpr uint32_t kBinShift = 6u;  // log2(kHistCopies * 4)
+    static_assert((1u << kBinShift) == kHistCopies * 4u, "kBinShift");
+    constexpr uint32_t kBinMask = 0xFFu << kBinShift;
+    uint8_t* hb = reinterpret_cast<uint8_t*>(s_hist);
 #pragma unroll
-  for (uint32_t j = 0; j < kUnitsPerThread; j++) {
-    const uint32_t u = j * kThreads + tid;
-    if (u >= nunits) continue;
-    if (kCiera) {
-      const uint32_t blk = (8u * u) >> log2B;
-      if (!((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) continue;
+    for (uint32_t j = 0; j < kUPT; j++) {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        const uint32_t w = v[j].w[i];
+        atomicAdd(reinterpret_cast<uint32_t*>(hb + (((w >> (7u - kBinShift)) & kBinMask) | copy4)), 1u);
+        atomicAdd(reinterpret_cast<uint32_t*>(hb + (((w >> (23u - kBinShift)) & kBinMask) | copy4)), 1u);
+      }
     }
-    const uint32_t cnt = min(8u, nc - 8u * u);
-    const uint2 e = unit_exponents(v[j]);
-    uint32_t* hist = s_hist + (j / 2u) * (kHistCopies * kBins) + copy;
+    coded = kUPT * 8u;
+  } else {
 #pragma unroll
-    for (uint32_t k = 0; k < 8u; k++)
-      if (k < cnt) atomicAdd(&hist[byte_of(e, k) * kHistCopies], 1u);
-    coded[j / 2u] += cnt;
+    for (uint32_t j = 0; j < kUPT; j++) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
+      if (u >= nunits) continue;
+      if (kCiera && B <= kPartValues) {
+        const uint32_t lb = ((8u * u) >> log2B) - blk0;
+        if (!((s_bits[lb >> 5] >> (lb & 31u)) & 1u)) continue;
+      }
+      const uint32_t cnt = min(8u, nc - 8u * u);
+      const uint2 e = unit_exponents(v[j]);
+      uint32_t* hist = s_hist + copy4 / 4u;
+#pragma unroll
+      for (uint32_t k = 0; k < 8u; k++)
+        if (k < cnt) atomicAdd(&hist[byte_of(e, k) * kHistCopies], 1u);
+      coded += cnt;
+    }
   }
   s1 = wave_sum(s1);
   s2 = wave_sum(s2);
   nf = wave_sum_u32(nf);
-#pragma unroll
-  for (uint32_t h = 0; h < kParts; h++) {
-    const uint32_t t = wave_sum_u32(coded[h]);
-    if (lane_id() == 0u && t) atomicAdd(&s_coded[h], t);
-  }
+  coded = wave_sum_u32(coded);
   if (lane_id() == 0u) {
     s_s1[tid >> 6] = s1;
     s_s2[tid >> 6] = s2;
     s_nf[tid >> 6] = nf;
+    s_coded[tid >> 6] = coded;
   }
   __syncthreads();
-  // one (part, bin) per thread: sum the copies, store as u16 (a part holds at
-  // most 16384 values)
+  // one bin per thread: sum the copies, store as u16 (a part holds at most
+  // 16384 values)
   {
-    const uint32_t h = tid / kBins, bin = tid % kBins;
-    uint32_t s = 0;
+    uint32_t sum = 0;
 #pragma unroll
-    for (uint32_t q = 0; q < kHistCopies; q++) s += s_hist[(h * kBins + bin) * kHistCopies + q];
-    ws.hist[(uint64_t(c) * kParts + h) * kBins + bin] = uint16_t(s);
+    for (uint32_t q = 0; q < kHistCopies; q++) sum += s_hist[tid * kHistCopies + q];
+    ws.hist[(c * kParts + h) * kBins + tid] = uint16_t(sum);
   }
-  if (tid < kParts) ws.coded[uint64_t(c) * kParts + tid] = s_coded[tid];
+  if (kCiera && tid < kPartBitmapWords) ws.bitmap[(c * kParts + h) * kPartBitmapWords + tid] = s_bits[tid];
   if (tid == 0) {
     double a = 0.0, b = 0.0;
-    uint32_t m = 0;
-    for (uint32_t w = 0; w < kWaves; w++) {
+    uint32_t m = 0, q = 0;
+#pragma unroll
+    for (uint32_t w = 0; w < kPartWaves; w++) {
       a += s_s1[w];
       b += s_s2[w];
       m += s_nf[w];
+      q += s_coded[w];
     }
     uint32_t nch = 0;
-    if (kCiera)
-      for (uint32_t w = 0; w < kBitmapWords; w++) nch += __popc(s_bits[w]);
+    if (kCiera) {
+      if (B <= kPartValues) {
+#pragma unroll
+        for (uint32_t w = 0; w < kPartBitmapWords; w++) nch += __popc(s_bits[w]);
+      } else {
+        nch = s_bits[0] & 1u;
+      }
+    }
     Partial p;
     p.s1 = a;
     p.s2 = b;
     p.nf = m;
     p.nch = nch;
     p.pad[0] = p.pad[1] = 0u;
-    ws.partial[c] = p;
+    ws.partial[c * kParts + h] = p;
+    ws.coded[c * kParts + h] = q;
   }
-  if (kCiera && tid < kBitmapWords) ws.bitmap[uint64_t(c) * kBitmapWords + tid] = s_bits[tid];
 }
 
 // ------------------------------------------------------------------ k_plan
@@ -571,11 +642,14 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
   double a = 0.0, b = 0.0;
   uint64_t m = 0, q = 0;
   for (uint64_t c = tid; c < nchunks; c += kThreads) {
-    const Partial p = ws.partial[c];
-    a += p.s1;
-    b += p.s2;
-    m += p.nf;
-    q += p.nch;
+    const Partial* pp = ws.partial + c * kParts;
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      a += pp[h].s1;
+      b += pp[h].s2;
+      m += pp[h].nf;
+    }
+    if (B) q += chunk_changed_blocks(pp, B);
   }
   a = wave_sum(a);
   b = wave_sum(b);
@@ -674,14 +748,24 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(uint64_t n, uint64_t 
   uint64_t size = 0, esc = 0;
   if (c < nchunks) {
     const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
+    const Partial* pp = ws.partial + c * kParts;
     uint32_t pe[kParts];
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) {
+      // a part inside a block that spans several parts codes its values only
+      // if some part of the block saw a change
+      bool coded = true;
+      if (B > kPartValues) {
+        const uint32_t ppb = B / kPartValues, first = h / ppb * ppb;
+        uint32_t any = 0;
+        for (uint32_t k = first; k < first + ppb; k++) any |= pp[k].nch;
+        coded = any != 0u;
+      }
       const uint16_t* hb = ws.hist + (c * kParts + h) * kBins + e0;
       uint32_t inwin = 0;
 #pragma unroll
       for (uint32_t k = 0; k < 7u; k++) inwin += hb[k];
-      pe[h] = ws.coded[c * kParts + h] - inwin;
+      pe[h] = coded ? ws.coded[c * kParts + h] - inwin : 0u;
     }
     uint32_t acc = 0;
 #pragma unroll
@@ -691,7 +775,7 @@ __global__ __launch_bounds__(kLayoutThreads) void k_layout(uint64_t n, uint64_t 
     }
     ws.chunkesc[c] = acc;
     esc = acc;
-    const uint64_t p = B ? uint64_t(ws.partial[c].nch) * B / 8u : cdiv(nc, 8u);
+    const uint64_t p = B ? uint64_t(chunk_changed_blocks(pp, B)) * B / 8u : cdiv(nc, 8u);
     size = pad128(nc) + (B ? 128u : 0u) + 3u * pad128(p) + pad128(acc);
   }
   // workgroup scans of sizes and escapes
@@ -898,7 +982,8 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   uint32_t nch = 0, nb = 0;
   if (kCiera) {
     if (tid < 64u)
-      stage_bitmap((tid < kBitmapWords) ? ws.bitmap[uint64_t(c) * kBitmapWords + tid] : 0u, s_bits, s_rank);
+      stage_bitmap((tid < kBitmapWords) ? chunk_bitmap_word(ws.bitmap + uint64_t(c) * kBitmapWords, tid, B) : 0u,
+                   s_bits, s_rank);
     nb = (nc + B - 1u) >> log2B;
   }
   __syncthreads();  // staging cleared, bitmap staged
@@ -1383,9 +1468,9 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   (void)hipGetLastError();
   if (nchunks) {
     if (ciera)
-      launch(k_stats<true>, dim3(uint32_t(nchunks)), dim3(kThreads), stream, x, n, d_cache, lb, ws);
+      launch(k_stats<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
     else
-      launch(k_stats<false>, dim3(uint32_t(nchunks)), dim3(kThreads), stream, x, n, nullptr, 0u, ws);
+      launch(k_stats<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
   }
   launch(k_plan, dim3(1), dim3(kThreads), stream, n, nchunks, B, e0_override, out, d_out_size, ws);
   if (nchunks) {
