@@ -300,18 +300,20 @@ __device__ inline uint32_t exps_from_codes(uint32_t codes, uint32_t e0) {
   return e0 ? codes + (e0 - 1u) * 0x01010101u : ((codes | 0x80808080u) - 0x01010101u) & 0x7F7F7F7Fu;
 }
 
-// Two output values from byte pairs: h = sm_a | E_a << 8 | sm_b << 16 | E_b << 24.
-__device__ inline uint32_t join_pair(uint32_t h) {
-  // bits 0..6 mantissa from sm, 7..14 exponent, 15 sign (sm bit 7)
-  return bfi(0x007F007Fu, h, bfi(0x80008000u, h << 8, h >> 1));
+// Output values 2i and 2i+1 of a unit from its sign+mantissa bytes (sm) and
+// exponent bytes (e), i = 0..3: [s, s', t, t'] with s = sm byte 2i keeps
+// mantissa bits 0..6 and, from its copy, the sign at bit 15; the exponent
+// bytes placed at bits 0..7 and 16..23 and shifted up by 7 fill bits 7..14.
+__device__ inline uint32_t join_word(uint32_t sm, uint32_t e, uint32_t dup_sel, uint32_t exp_sel) {
+  return (perm(0u, sm, dup_sel) & 0x807F807Fu) | (perm(0u, e, exp_sel) << 7);
 }
 
 __device__ inline Unit unit_join(uint2 sm, uint2 e) {
   Unit o;
-  o.w[0] = join_pair(perm(e.x, sm.x, 0x05010400u));
-  o.w[1] = join_pair(perm(e.x, sm.x, 0x07030602u));
-  o.w[2] = join_pair(perm(e.y, sm.y, 0x05010400u));
-  o.w[3] = join_pair(perm(e.y, sm.y, 0x07030602u));
+  o.w[0] = join_word(sm.x, e.x, 0x01010000u, 0x0C010C00u);
+  o.w[1] = join_word(sm.x, e.x, 0x03030202u, 0x0C030C02u);
+  o.w[2] = join_word(sm.y, e.y, 0x01010000u, 0x0C010C00u);
+  o.w[3] = join_word(sm.y, e.y, 0x03030202u, 0x0C030C02u);
   return o;
 }
 
@@ -327,13 +329,16 @@ __device__ inline uint2 set_byte(uint2 v, uint32_t k, uint32_t b) {
   return v;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
+// 4 and 8 within each 16-lane row, then row 0's total into row 1 and row 2's
+// into row 3, then lane 31's running total into rows 2 and 3.
 __device__ inline uint32_t wave_incl_scan(uint32_t v) {
-  const uint32_t lane = lane_id();
-#pragma unroll
-  for (uint32_t d = 1; d < 64u; d <<= 1) {
-    const uint32_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x111, 0xF, 0xF, true);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x112, 0xF, 0xF, true);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x114, 0xF, 0xF, true);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x118, 0xF, 0xF, true);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0u, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
 }
 
@@ -1094,10 +1099,33 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
 // ------------------------------------------------------------------ k_decode
 // Escape bytes a decoding part stages in LDS.  A chunk's escape section of at
 // most kEscWhole bytes is loaded whole, together with the part's other loads;
-// a longer one is staged as a window starting at the part's first escape,
-// which holds all of the part's escapes (a part has kPartUnits * 8 values).
-constexpr uint32_t kEscStage = kPartUnits * 8u;
+// a longer one is staged as a window from the 16-byte boundary at or below
+// the part's first escape, which holds all of the part's escapes (at most
+// kPartUnits * 8 bytes, after at most 15 bytes of earlier parts').  The LDS
+// array has 16 spare bytes for the 12-byte reads of merge_escapes.
+constexpr uint32_t kEscStage = kPartUnits * 8u + 16u;
 constexpr uint32_t kEscWhole = 16u * kPartThreads;
+static_assert(kEscStage % 16u == 0u && kEscWhole <= kEscStage, "escape staging");
+
+// Put a unit's escape bytes into e: the k-th set bit of emask (a code-0
+// byte) takes the k-th byte from byte a of the staged escapes.  Byte
+// selectors for v_perm from the escape ranks (a byte-wise prefix count of
+// emask's bits), no loop.
+__device__ inline uint2 merge_escapes(uint2 e, uint32_t emask, const uint8_t* s_esc, uint32_t a) {
+  const uint32_t* w = reinterpret_cast<const uint32_t*>(s_esc + (a & ~3u));
+  const uint32_t sh = a & 3u;
+  const uint32_t w0 = w[0], w1 = w[1], w2 = w[2];
+  const uint32_t x03 = __builtin_amdgcn_alignbyte(w1, w0, sh);  // the unit's escape bytes 0..3
+  const uint32_t x47 = __builtin_amdgcn_alignbyte(w2, w1, sh);  // 4..7
+  const uint32_t mlo = spread4(emask & 15u), mhi = spread4(emask >> 4);
+  const uint32_t r4 = __popc(emask & 15u);  // escapes among values 0..3
+  const uint32_t src_hi = (r4 == 4u) ? x47 : __builtin_amdgcn_alignbyte(x47, x03, r4);
+  // selector byte k: the escape's rank (0..3) in the source word, or 4 + k to
+  // keep e's byte k
+  const uint32_t sel_lo = bfi(mlo * 0xFFu, mlo * 0x01010100u, 0x07060504u);
+  const uint32_t sel_hi = bfi(mhi * 0xFFu, mhi * 0x01010100u, 0x07060504u);
+  return make_uint2(perm(e.x, x03, sel_lo), perm(e.y, src_hi, sel_hi));
+}
 constexpr uint32_t kPlaneRounds = (3u * (kStage / 8u) + kPartThreads - 1u) / kPartThreads;
 
 struct DecodePart {
@@ -1227,16 +1255,8 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
     const uint32_t u = p.pu0 + j * kPartThreads + tid;
     if (!kFull && u >= p.nunits) continue;
     const uint32_t valid = kFull ? 8u : min(8u, p.nc - 8u * u);
-    uint2 e = ev[j];
-    uint32_t em = emask[j];
-    uint32_t at = before + base[j];
-    while (em) {
-      const uint32_t k = __builtin_ctz(em);
-      em &= em - 1u;
-      const uint32_t b = (at >= esc_lo && at < esc_hi) ? uint32_t(s_esc[at - esc_lo]) : uint32_t(in[g.esc + at]);
-      e = set_byte(e, k, b);
-      at++;
-    }
+    // the unit's escapes are staged bytes [before + base - esc_lo, + cnt)
+    const uint2 e = merge_escapes(ev[j], emask[j], s_esc, before + base[j] - esc_lo);
     store_unit(p.y, p.start + 8ull * u, valid, unit_join(smv[j], e));
     if (kCiera) {
       const uint32_t blk = (8u * u) >> p.log2B;
@@ -1268,7 +1288,7 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
                                                          uint64_t* __restrict__ n_err_slots,
                                                          uint32_t* __restrict__ err_slots) {
   __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
-  __shared__ __attribute__((aligned(16))) uint8_t s_esc[kEscStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_esc[kEscStage + 16u];
   __shared__ uint32_t s_ok;    // header and table entries are consistent
   __shared__ uint32_t s_fits;  // the chunk's fixed-size sections lie inside it
   __shared__ uint32_t s_e0;
