@@ -41,7 +41,7 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-KERNELS = ["k_stats", "k_plan", "k_layout", "k_write", "k_decode"]
+KERNELS = ["k_stats", "k_plan", "k_write", "k_decode"]
 
 
 def measured_bandwidth(torch, dev, nbytes=2 << 30, reps=5):
@@ -208,7 +208,7 @@ def main() -> int:
     wall = time.perf_counter() - t_start
     # Pass 2, the same K steps with every kernel timed by HIP events that the
     # runtime records at the kernel's own start and end (hipExtLaunchKernel);
-    # a step launches encode's four kernels, then decode's one.
+    # a step launches encode's three kernels, then decode's one.
     names = KERNELS
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
           for _ in range(K)]
@@ -223,8 +223,8 @@ def main() -> int:
     wall2 = time.perf_counter() - t2
     ciera.ciera_time_kernels([])
     kern_ms = {nm: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(K)) / K for i, nm in enumerate(names)}
-    enc_ms = [ev[s][0][0].elapsed_time(ev[s][3][1]) for s in range(K)]  # k_stats start .. k_write end
-    dec_ms = [ev[s][4][0].elapsed_time(ev[s][4][1]) for s in range(K)]
+    enc_ms = [ev[s][0][0].elapsed_time(ev[s][2][1]) for s in range(K)]  # k_stats start .. k_write end
+    dec_ms = [ev[s][3][0].elapsed_time(ev[s][3][1]) for s in range(K)]
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
     if args.verify:
         klast = (2 * K) % 2 if mode != "zip3" else 0  # input of the last step, index 2K-1

@@ -137,7 +137,7 @@ ciera_status ciera_read_error(const void* d_ws, hipStream_t stream);
  * n_pairs (start, stop) pairs of hipEvent_t handles, created with timing
  * enabled and owned by the caller.  The next n_pairs kernel launches made by
  * the calling host thread through this library (any entry point: encode
- * launches four kernels, decode one) each take the next pair, which the HIP
+ * launches three kernels, decode one) each take the next pair, which the HIP
  * runtime records at that kernel's start and end (hipExtLaunchKernel);
  * hipEventElapsedTime then gives the kernel's own duration.  The handles are
  * copied; a later call replaces the queue, n_pairs = 0 clears it.  Returns

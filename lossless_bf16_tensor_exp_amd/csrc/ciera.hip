@@ -1,6 +1,6 @@
 // ciera.hip -- HIP kernels and C ABI of the lossless BF16 codec, gfx950.
 //
-// Encode is four kernels on the caller's stream:
+// Encode is three kernels on the caller's stream:
 //   k_stats   one workgroup per quarter chunk ("part", 16,384 values), one
 //             pass over the input: FP64 partial sums for the tensor's
 //             variance (ZipCCL research digest, section 3.1: sigma from one
@@ -11,16 +11,13 @@
 //   k_plan    one workgroup: reduces the partial sums in a fixed order and
 //             picks the window base E0 (integer nearest x_opt = log2 sigma +
 //             0.5 log2(14 ln2 / 16383), digest section 3.1, evaluated as
-//             var >= K0 4^k); writes the header's size-independent fields.
-//   k_layout  one thread per chunk: the escape count of each part is the
-//             number of coded values outside [E0, E0+6], read off the
-//             histogram; chunk sizes follow exactly, and a decoupled
-//             look-back over groups of chunks turns them into the chunk
-//             table (the size exchange of the digest's Figure 1, done on one
-//             GPU).
+//             var >= K0 4^k); each part's escape count is its number of coded
+//             values outside [E0, E0+6], read off the histogram, so chunk
+//             sizes follow exactly and a scan turns them into the chunk table
+//             (the size exchange of the digest's Figure 1, done on one GPU).
 //   k_write   one workgroup per part, no synchronisation with any other:
 //             splits values into sign+mantissa bytes and 3-bit codes and
-//             writes the 128-byte-aligned sections at offsets k_layout fixed
+//             writes the 128-byte-aligned sections at offsets k_plan fixed
 //             (digest, section 3.1 last paragraph).
 // Decode is one kernel, k_decode, one workgroup per part; parts are
 // independent because the chunk table holds every chunk offset and a part
@@ -29,9 +26,10 @@
 // Work mapping: a "unit" is 8 consecutive values (one 16-byte load).  A chunk
 // has 8192 units.  In k_stats, k_write and k_decode part h covers units
 // [2048h, 2048h + 2048) and thread t of its 256 handles unit 2048h + 256j + t
-// (j = 0..7), so each wave instruction moves 1 KiB of contiguous input.  Blocks (B >= 64) never split a unit, and chunks never split a
-// block.  All data movement is integer: sign, NaN payloads, subnormals and -0
-// never pass through floating-point registers.
+// (j = 0..7), so each wave instruction moves 1 KiB of contiguous input.
+// Blocks (B >= 64) never split a unit, and chunks never split a block.  All
+// data movement is integer: sign, NaN payloads, subnormals and -0 never pass
+// through floating-point registers.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -55,11 +53,6 @@ constexpr uint32_t kMaxE0 = 249u;
 // 16383 / (28 ln 2) as a double: the variance threshold of window base k is
 // kK0 * 4^k.
 constexpr double kK0 = 0x1.a610ca4a234eep+9;
-// Look-back status words: two flag bits over a 62-bit value.
-constexpr uint64_t kFlagAggregate = 1ull << 62;
-constexpr uint64_t kFlagInclusive = 2ull << 62;
-constexpr uint64_t kValueMask = (1ull << 62) - 1u;
-constexpr uint32_t kSpinLimit = 1u << 26;
 
 // Parts: k_write and k_decode run kParts workgroups of kPartThreads threads
 // per chunk, kUPT units per thread.
@@ -74,7 +67,6 @@ constexpr uint32_t kStage = kPartUnits + 16u;  // LDS bytes per staged plane
 constexpr uint32_t kPartEscStage = 4096u;      // escape bytes staged in LDS per part
 constexpr uint32_t kBins = 256u;               // exponent histogram bins
 constexpr uint32_t kHistCopies = 16u;          // interleaved LDS copies (by lane) to spread atomics
-constexpr uint32_t kLayoutThreads = 256u;      // chunks per k_layout workgroup
 static_assert(kPartThreads == kBins, "k_stats stores one bin per thread");
 constexpr uint32_t kPartValues = kPartUnits * 8u;                 // 16384
 constexpr uint32_t kPartBitmapWords = kBitmapWords / kParts;      // 8: one bit per block at B = 64
@@ -86,12 +78,12 @@ __host__ __device__ inline uint64_t table_end(uint64_t nchunks) {
   return kHeader + pad128(8u * (nchunks + 1u));
 }
 
-// Workspace: control block, error words, per-chunk partial sums, bitmap
-// words, per-part histograms (u16 bins) and coded-value counts, per-part
-// escape offsets, per-chunk escape totals, and look-back words of k_layout.
+// Workspace: control block, error words, per-part partial sums and bitmap
+// words, cumulative exponent histograms of the parts, per-part escape offsets
+// and per-chunk escape totals.
 struct Ctrl {
   uint32_t e0;
-  uint32_t ticket;
+  uint32_t reserved0;
   uint64_t n_err_slots;
   uint64_t reserved[30];
 };
@@ -106,41 +98,38 @@ struct Partial {
 };
 
 struct WsLayout {
-  uint64_t err, partial, bitmap, hist, coded, partesc, chunkesc, gstatus, gesc_agg, gesc_incl, total;
+  uint64_t err, partial, bitmap, cum, partesc, chunkesc, total;
 };
+
+// Cumulative exponent histogram rows: row r (0..256) holds, for every part,
+// the number of its coded values with exponent below r, as u16; row 256 is
+// the part's coded-value count.  Stored row-major (row r: parts 0..P-1), so
+// that the rows k_plan reads for one window base are contiguous over parts.
+constexpr uint32_t kCumRows = kBins + 1u;
 
 __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255); }
 
 __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   WsLayout l;
   const uint64_t slots = nchunks ? nchunks : 1u;
-  const uint64_t groups = cdiv(slots, kLayoutThreads);
   l.err = sizeof(Ctrl);
   l.partial = align256(l.err + 4u * kParts * slots);
   l.bitmap = align256(l.partial + sizeof(Partial) * kParts * slots);
-  l.hist = align256(l.bitmap + 4u * kBitmapWords * slots);
-  l.coded = align256(l.hist + 2u * kBins * kParts * slots);
-  l.partesc = align256(l.coded + 4u * kParts * slots);
+  l.cum = align256(l.bitmap + 4u * kBitmapWords * slots);
+  l.partesc = align256(l.cum + 2u * kCumRows * kParts * slots);
   l.chunkesc = align256(l.partesc + 4u * kParts * slots);
-  l.gstatus = align256(l.chunkesc + 4u * slots);
-  l.gesc_agg = align256(l.gstatus + 8u * groups);
-  l.gesc_incl = align256(l.gesc_agg + 8u * groups);
-  l.total = align256(l.gesc_incl + 8u * groups);
+  l.total = align256(l.chunkesc + 4u * slots);
   return l;
 }
 
 struct Ws {
   Ctrl* ctrl;
   uint32_t* err;        // one word per workgroup of k_write / k_decode
-  Partial* partial;     // per chunk
-  uint32_t* bitmap;     // kBitmapWords per chunk
-  uint16_t* hist;       // kParts x kBins per chunk
-  uint32_t* coded;      // values to code, per part
+  Partial* partial;     // per part
+  uint32_t* bitmap;     // kPartBitmapWords per part
+  uint16_t* cum;        // kCumRows rows of (kParts * nchunks) u16
   uint32_t* partesc;    // escapes before each part within its chunk
   uint32_t* chunkesc;   // escapes per chunk
-  uint64_t* gstatus;    // k_layout look-back: flag | bytes, per group of chunks
-  uint64_t* gesc_agg;   // escapes of the group
-  uint64_t* gesc_incl;  // escapes of all groups up to this one
 };
 
 __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
@@ -151,13 +140,9 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.err = reinterpret_cast<uint32_t*>(b + l.err);
   w.partial = reinterpret_cast<Partial*>(b + l.partial);
   w.bitmap = reinterpret_cast<uint32_t*>(b + l.bitmap);
-  w.hist = reinterpret_cast<uint16_t*>(b + l.hist);
-  w.coded = reinterpret_cast<uint32_t*>(b + l.coded);
+  w.cum = reinterpret_cast<uint16_t*>(b + l.cum);
   w.partesc = reinterpret_cast<uint32_t*>(b + l.partesc);
   w.chunkesc = reinterpret_cast<uint32_t*>(b + l.chunkesc);
-  w.gstatus = reinterpret_cast<uint64_t*>(b + l.gstatus);
-  w.gesc_agg = reinterpret_cast<uint64_t*>(b + l.gesc_agg);
-  w.gesc_incl = reinterpret_cast<uint64_t*>(b + l.gesc_incl);
   return w;
 }
 
@@ -319,16 +304,6 @@ __device__ inline Unit unit_join(uint2 sm, uint2 e) {
 
 __device__ inline uint32_t byte_of(uint2 v, uint32_t k) { return ((k < 4u ? v.x : v.y) >> (8u * (k & 3u))) & 0xFFu; }
 
-__device__ inline uint2 set_byte(uint2 v, uint32_t k, uint32_t b) {
-  const uint32_t sh = 8u * (k & 3u);
-  const uint32_t m = ~(0xFFu << sh);
-  if (k < 4u)
-    v.x = (v.x & m) | (b << sh);
-  else
-    v.y = (v.y & m) | (b << sh);
-  return v;
-}
-
 // Inclusive prefix sum over the 64 lanes of a wave with DPP: shifts by 1, 2,
 // 4 and 8 within each 16-lane row, then row 0's total into row 1 and row 2's
 // into row 3, then lane 31's running total into rows 2 and 3.
@@ -342,32 +317,49 @@ __device__ inline uint32_t wave_incl_scan(uint32_t v) {
   return v;
 }
 
+// A 64-bit value from the lane a DPP control selects (0 where it selects none
+// or the row is masked off), moved as two 32-bit halves.
+template <int kCtrl, int kRowMask, bool kBound>
+__device__ inline uint64_t dpp64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0u, uint32_t(v), kCtrl, kRowMask, 0xF, kBound);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0u, uint32_t(v >> 32), kCtrl, kRowMask, 0xF, kBound);
+  return (uint64_t(hi) << 32) | lo;
+}
+
 __device__ inline uint64_t wave_incl_scan_u64(uint64_t v) {
-  const uint32_t lane = lane_id();
-#pragma unroll
-  for (uint32_t d = 1; d < 64u; d <<= 1) {
-    const uint64_t t = __shfl_up(v, d, 64);
-    if (lane >= d) v += t;
-  }
+  v += dpp64<0x111, 0xF, true>(v);
+  v += dpp64<0x112, 0xF, true>(v);
+  v += dpp64<0x114, 0xF, true>(v);
+  v += dpp64<0x118, 0xF, true>(v);
+  v += dpp64<0x142, 0xA, false>(v);
+  v += dpp64<0x143, 0xC, false>(v);
   return v;
 }
 
+__device__ inline uint64_t lane63_u64(uint64_t v) {
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 63));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63));
+  return (uint64_t(hi) << 32) | lo;
+}
+
+// Wave totals, the same in every lane.  The FP64 one adds in the fixed order
+// of the scan above, so equal inputs give equal sums.
 __device__ inline double wave_sum(double v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
+  auto step = [](double x, uint64_t moved) { return x + __longlong_as_double(int64_t(moved)); };
+  const auto bits = [](double x) { return uint64_t(__double_as_longlong(x)); };
+  v = step(v, dpp64<0x111, 0xF, true>(bits(v)));
+  v = step(v, dpp64<0x112, 0xF, true>(bits(v)));
+  v = step(v, dpp64<0x114, 0xF, true>(bits(v)));
+  v = step(v, dpp64<0x118, 0xF, true>(bits(v)));
+  v = step(v, dpp64<0x142, 0xA, false>(bits(v)));
+  v = step(v, dpp64<0x143, 0xC, false>(bits(v)));
+  return __longlong_as_double(int64_t(lane63_u64(bits(v))));
 }
 
-__device__ inline uint64_t wave_sum_u64(uint64_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
-}
+__device__ inline uint64_t wave_sum_u64(uint64_t v) { return lane63_u64(wave_incl_scan_u64(v)); }
 
 __device__ inline uint32_t wave_sum_u32(uint32_t v) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-  return v;
+  return uint32_t(__builtin_amdgcn_readlane(int(wave_incl_scan(v)), 63));
 }
 
 // ------------------------------------------------------------------ k_stats
@@ -439,7 +431,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   __shared__ uint32_t s_hist[kHistCopies * kBins];
   __shared__ uint32_t s_bits[kPartBitmapWords];
   __shared__ double s_s1[kPartWaves], s_s2[kPartWaves];
-  __shared__ uint32_t s_nf[kPartWaves], s_coded[kPartWaves];
+  __shared__ uint32_t s_nf[kPartWaves], s_wtot[kPartWaves];
   const uint32_t tid = threadIdx.x;
   const uint32_t wg = blockIdx.x;
   const uint64_t c = wg / kParts;
@@ -533,11 +525,10 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
 
   // Exponent histogram of the values to code: all values (zip3); ciera, those
   // of the part's changed blocks, or all of the part's values when its block
-  // spans several parts (k_layout drops them if the block is unchanged).
+  // spans several parts (k_plan drops them if the block is unchanged).
   // Word bin * kHistCopies + copy, copy chosen by lane: equal exponents
   // within a wave spread over kHistCopies consecutive words (LDS banks).
   const uint32_t copy4 = 4u * (tid & (kHistCopies - 1u));
-  uint32_t coded = 0;
   if (!kCiera && full) {
     // the bin's byte offset straight from the exponent bits of each half
     constexpr uint32_t kBinShift = 6u;  // log2(kHistCopies * 4)
@@ -553,7 +544,6 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
         atomicAdd(reinterpret_cast<uint32_t*>(hb + (((w >> (23u - kBinShift)) & kBinMask) | copy4)), 1u);
       }
     }
-    coded = kUPT * 8u;
   } else {
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) {
@@ -569,38 +559,43 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
 #pragma unroll
       for (uint32_t k = 0; k < 8u; k++)
         if (k < cnt) atomicAdd(&hist[byte_of(e, k) * kHistCopies], 1u);
-      coded += cnt;
     }
   }
   s1 = wave_sum(s1);
   s2 = wave_sum(s2);
   nf = wave_sum_u32(nf);
-  coded = wave_sum_u32(coded);
   if (lane_id() == 0u) {
     s_s1[tid >> 6] = s1;
     s_s2[tid >> 6] = s2;
     s_nf[tid >> 6] = nf;
-    s_coded[tid >> 6] = coded;
   }
   __syncthreads();
-  // one bin per thread: sum the copies, store as u16 (a part holds at most
-  // 16384 values)
+  // One bin per thread: sum the copies; the part's column of the cumulative
+  // rows gets the count below each bin and, in row 256, its coded-value total
+  // (u16: a part holds at most 16384 values).
   {
     uint32_t sum = 0;
 #pragma unroll
     for (uint32_t q = 0; q < kHistCopies; q++) sum += s_hist[tid * kHistCopies + q];
-    ws.hist[(c * kParts + h) * kBins + tid] = uint16_t(sum);
+    const uint32_t incl = wave_incl_scan(sum);
+    if (lane_id() == 63u) s_wtot[tid >> 6] = incl;
+    __syncthreads();
+    uint32_t below = incl - sum;
+#pragma unroll
+    for (uint32_t w = 0; w < kPartWaves; w++) below += (w < (tid >> 6)) ? s_wtot[w] : 0u;
+    const uint64_t P = cdiv(n, kChunk) * kParts;
+    ws.cum[uint64_t(tid) * P + wg] = uint16_t(below);
+    if (tid == kBins - 1u) ws.cum[uint64_t(kBins) * P + wg] = uint16_t(below + sum);
   }
   if (kCiera && tid < kPartBitmapWords) ws.bitmap[(c * kParts + h) * kPartBitmapWords + tid] = s_bits[tid];
   if (tid == 0) {
     double a = 0.0, b = 0.0;
-    uint32_t m = 0, q = 0;
+    uint32_t m = 0;
 #pragma unroll
     for (uint32_t w = 0; w < kPartWaves; w++) {
       a += s_s1[w];
       b += s_s2[w];
       m += s_nf[w];
-      q += s_coded[w];
     }
     uint32_t nch = 0;
     if (kCiera) {
@@ -618,7 +613,6 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     p.nch = nch;
     p.pad[0] = p.pad[1] = 0u;
     ws.partial[c * kParts + h] = p;
-    ws.coded[c * kParts + h] = q;
   }
 }
 
@@ -638,78 +632,6 @@ __device__ inline uint32_t window_base(double var, uint64_t nf) {
   return k < -127 ? 0u : uint32_t(127 + k);
 }
 
-__global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks, uint32_t B, int e0_override,
-                                                   uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
-                                                   Ws ws) {
-  __shared__ double s_s1[kWaves], s_s2[kWaves];
-  __shared__ uint64_t s_nf[kWaves], s_nch[kWaves];
-  const uint32_t tid = threadIdx.x;
-  double a = 0.0, b = 0.0;
-  uint64_t m = 0, q = 0;
-  for (uint64_t c = tid; c < nchunks; c += kThreads) {
-    const Partial* pp = ws.partial + c * kParts;
-#pragma unroll
-    for (uint32_t h = 0; h < kParts; h++) {
-      a += pp[h].s1;
-      b += pp[h].s2;
-      m += pp[h].nf;
-    }
-    if (B) q += chunk_changed_blocks(pp, B);
-  }
-  a = wave_sum(a);
-  b = wave_sum(b);
-  m = wave_sum_u64(m);
-  q = wave_sum_u64(q);
-  if (lane_id() == 0u) {
-    s_s1[tid >> 6] = a;
-    s_s2[tid >> 6] = b;
-    s_nf[tid >> 6] = m;
-    s_nch[tid >> 6] = q;
-  }
-  uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
-  const uint64_t base = table_end(nchunks);
-  // zero the table's padding words (entries past nchunks) and k_layout's
-  // look-back words
-  for (uint64_t i = nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
-  const uint64_t groups = cdiv(nchunks, kLayoutThreads);
-  for (uint64_t i = tid; i < groups; i += kThreads) ws.gstatus[i] = 0u;
-  __syncthreads();
-  if (tid == 0) {
-    double s1 = 0.0, s2 = 0.0;
-    uint64_t nf = 0, nch = 0;
-    for (uint32_t w = 0; w < kWaves; w++) {
-      s1 += s_s1[w];
-      s2 += s_s2[w];
-      nf += s_nf[w];
-      nch += s_nch[w];
-    }
-    double var = 0.0;
-    if (nf >= 2u) {
-      var = (s2 - s1 * s1 / double(nf)) / double(nf - 1u);
-      if (!(var > 0.0)) var = 0.0;
-    }
-    const uint32_t e0 = (e0_override >= 0) ? uint32_t(e0_override) : window_base(var, nf);
-    ws.ctrl->e0 = e0;
-    ws.ctrl->ticket = 0u;
-    ws.ctrl->n_err_slots = nchunks * kParts;
-    const uint32_t magic = B ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
-    uint64_t* h = reinterpret_cast<uint64_t*>(out);
-    h[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(B ? 1u : 0u) << 48) | (uint64_t(e0) << 56);
-    h[1] = n;
-    h[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
-    h[3] = nchunks;
-    h[5] = nch;
-    for (int i = 7; i < 16; i++) h[i] = 0u;
-    if (nchunks == 0u) {
-      h[4] = base;
-      h[6] = 0u;
-      table[0] = base;
-      *out_size = base;
-    }
-  }
-}
-
-// ------------------------------------------------------------------ k_layout
 // Chunk geometry shared by encode and decode: section offsets from the
 // chunk's start, its value count and (ciera) changed-block count.
 struct ChunkGeom {
@@ -729,149 +651,194 @@ __device__ inline ChunkGeom chunk_geom(uint64_t begin, uint32_t nc, bool ciera, 
   return g;
 }
 
-// One thread per chunk.  Each part's escapes = its coded values minus those
-// whose exponent falls in the window (7 histogram bins); the chunk size then
-// follows from the layout, and a decoupled look-back over workgroups (groups
-// of kLayoutThreads chunks) turns sizes into offsets.  The group's ticket is
-// taken in launch order, so a group only ever waits on groups already running.
-// Group status: flag | bytes in gstatus; the escape counts sit in gesc_agg /
-// gesc_incl, written before the release of the flag that announces them.
-__global__ __launch_bounds__(kLayoutThreads) void k_layout(uint64_t n, uint64_t nchunks, uint32_t log2B,
-                                                           uint8_t* __restrict__ out,
-                                                           uint64_t* __restrict__ out_size, Ws ws) {
-  __shared__ uint32_t s_ticket;
-  __shared__ uint64_t s_wb[kLayoutThreads / 64u], s_we[kLayoutThreads / 64u];
-  __shared__ uint64_t s_pb, s_pe;
+// Chunk sizes a thread of k_plan keeps in registers (longer runs go through
+// the chunk table).
+constexpr uint32_t kRunRegs = 8u;
+
+// One workgroup plans the stream.  Thread t owns a contiguous run of chunks.
+// (1) The parts' partial sums are reduced in a fixed order (thread runs, then
+// waves in order) and the variance picks E0.  (2) Each chunk's escapes and
+// size follow exactly from the histograms; a workgroup scan over the runs
+// turns sizes into the chunk table (the size exchange of the digest's Figure
+// 1, done on one GPU).  Writes the header, the table, the per-part escape
+// offsets and *out_size.
+__global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks, uint32_t B, int e0_override,
+                                                   uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
+                                                   Ws ws) {
+  __shared__ double s_s1[kWaves], s_s2[kWaves];
+  __shared__ uint64_t s_nf[kWaves], s_nch[kWaves], s_bytes[kWaves], s_esc[kWaves];
+  __shared__ uint32_t s_e0;
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = lane_id(), wave = tid >> 6;
-  if (tid == 0) s_ticket = atomicAdd(&ws.ctrl->ticket, 1u);
-  __syncthreads();
-  const uint32_t g = s_ticket;
-  const uint64_t c = uint64_t(g) * kLayoutThreads + tid;
-  const uint32_t e0 = ws.ctrl->e0;
-  const uint32_t B = log2B ? (1u << log2B) : 0u;
-  uint64_t size = 0, esc = 0;
-  if (c < nchunks) {
-    const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
-    const Partial* pp = ws.partial + c * kParts;
-    uint32_t pe[kParts];
-#pragma unroll
-    for (uint32_t h = 0; h < kParts; h++) {
-      // a part inside a block that spans several parts codes its values only
-      // if some part of the block saw a change
-      bool coded = true;
-      if (B > kPartValues) {
-        const uint32_t ppb = B / kPartValues, first = h / ppb * ppb;
-        uint32_t any = 0;
-        for (uint32_t k = first; k < first + ppb; k++) any |= pp[k].nch;
-        coded = any != 0u;
-      }
-      const uint16_t* hb = ws.hist + (c * kParts + h) * kBins + e0;
-      uint32_t inwin = 0;
-#pragma unroll
-      for (uint32_t k = 0; k < 7u; k++) inwin += hb[k];
-      pe[h] = coded ? ws.coded[c * kParts + h] - inwin : 0u;
-    }
-    uint32_t acc = 0;
-#pragma unroll
-    for (uint32_t h = 0; h < kParts; h++) {
-      ws.partesc[c * kParts + h] = acc;
-      acc += pe[h];
-    }
-    ws.chunkesc[c] = acc;
-    esc = acc;
-    const uint64_t p = B ? uint64_t(chunk_changed_blocks(pp, B)) * B / 8u : cdiv(nc, 8u);
-    size = pad128(nc) + (B ? 128u : 0u) + 3u * pad128(p) + pad128(acc);
-  }
-  // workgroup scans of sizes and escapes
-  const uint64_t ib = wave_incl_scan_u64(size);
-  const uint64_t ie = wave_incl_scan_u64(esc);
-  if (lane == 63u) {
-    s_wb[wave] = ib;
-    s_we[wave] = ie;
-  }
-  __syncthreads();
-  uint64_t xb = ib - size, xe = ie - esc;  // exclusive within the workgroup
-  uint64_t tb = 0, te = 0;                 // workgroup totals
-  for (uint32_t w = 0; w < kLayoutThreads / 64u; w++) {
-    if (w < wave) {
-      xb += s_wb[w];
-      xe += s_we[w];
-    }
-    tb += s_wb[w];
-    te += s_we[w];
-  }
-  if (wave == 0) {
-    // publish this group's aggregate, then sum predecessors 64 at a time
-    uint32_t err = 0u;
-    if (lane == 0u) {
-      if (g == 0u) {
-        ws.gesc_incl[0] = te;
-        __hip_atomic_store(&ws.gstatus[0], kFlagInclusive | tb, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      } else {
-        ws.gesc_agg[g] = te;
-        __hip_atomic_store(&ws.gstatus[g], kFlagAggregate | tb, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    uint64_t pb = 0, pe = 0;
-    if (g > 0u) {
-      int64_t top = int64_t(g) - 1;
-      uint32_t spins = 0;
-      while (true) {
-        const int64_t k = top - int64_t(lane);
-        const uint64_t s = (k >= 0) ? __hip_atomic_load(&ws.gstatus[k], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)
-                                    : kFlagInclusive;
-        const uint64_t flag = s & ~kValueMask;
-        if (__ballot(flag == 0u) != 0u) {
-          if (++spins > kSpinLimit) {
-            err = CIERA_ERR_INTERNAL;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(2);
-          continue;
-        }
-        const uint64_t ev = (k < 0) ? 0u : (flag == kFlagInclusive ? ws.gesc_incl[k] : ws.gesc_agg[k]);
-        const uint64_t incl = __ballot(flag == kFlagInclusive);
-        if (incl != 0u) {
-          const uint32_t first = uint32_t(__builtin_ctzll(incl));
-          pb += wave_sum_u64(lane <= first ? (s & kValueMask) : 0u);
-          pe += wave_sum_u64(lane <= first ? ev : 0u);
-          break;
-        }
-        pb += wave_sum_u64(s & kValueMask);
-        pe += wave_sum_u64(ev);
-        top -= 64;
-      }
-      if (lane == 0u) {
-        // published even after a failed wait, so later groups never wait forever
-        ws.gesc_incl[g] = pe + te;
-        __hip_atomic_store(&ws.gstatus[g], kFlagInclusive | (pb + tb), __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-    if (lane == 0u) {
-      s_pb = pb;
-      s_pe = pe;
-      // a failed wait makes every chunk of the group report the error
-      if (err) {
-        const uint64_t c0 = uint64_t(g) * kLayoutThreads;
-        for (uint64_t cc = c0; cc < c0 + kLayoutThreads && cc < nchunks; cc++) ws.partesc[cc * kParts] = ~0u;
-      }
-    }
-  }
-  __syncthreads();
-  const uint64_t base = table_end(nchunks);
+  const uint64_t per = cdiv(nchunks, kThreads);
+  const uint64_t c0 = min(nchunks, per * tid), c1 = min(nchunks, c0 + per);
+  uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
-  if (c < nchunks) {
-    const uint64_t begin = base + s_pb + xb;
-    table[c] = begin;
-    if (c + 1u == nchunks) {
-      const uint64_t total = begin + size;
-      table[nchunks] = total;
-      uint64_t* hd = reinterpret_cast<uint64_t*>(out);
-      hd[4] = total;
-      hd[6] = s_pe + xe + esc;
-      *out_size = total;
+  const uint64_t base = table_end(nchunks);
+
+  // (1) partial sums over the run; the chunks' changed-block counts are kept
+  // for (2), in registers for short runs
+  double a = 0.0, b = 0.0;
+  uint64_t m = 0, q = 0;
+  uint32_t nchs[kRunRegs];
+#pragma unroll
+  for (uint32_t i = 0; i < kRunRegs; i++) nchs[i] = 0u;
+  for (uint64_t c = c0; c < c1; c++) {
+    const Partial* pp = ws.partial + c * kParts;
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      a += pp[h].s1;
+      b += pp[h].s2;
+      m += pp[h].nf;
     }
+    if (B) {
+      const uint32_t nch = chunk_changed_blocks(pp, B);
+      q += nch;
+#pragma unroll
+      for (uint32_t i = 0; i < kRunRegs; i++)
+        if (i == c - c0) nchs[i] = nch;
+    }
+  }
+  a = wave_sum(a);
+  b = wave_sum(b);
+  m = wave_sum_u64(m);
+  q = wave_sum_u64(q);
+  if (lane == 0u) {
+    s_s1[wave] = a;
+    s_s2[wave] = b;
+    s_nf[wave] = m;
+    s_nch[wave] = q;
+  }
+  // zero the table's padding words (entries past nchunks)
+  for (uint64_t i = nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    double s1 = 0.0, s2 = 0.0;
+    uint64_t nf = 0, nch = 0;
+    for (uint32_t w = 0; w < kWaves; w++) {
+      s1 += s_s1[w];
+      s2 += s_s2[w];
+      nf += s_nf[w];
+      nch += s_nch[w];
+    }
+    double var = 0.0;
+    if (nf >= 2u) {
+      var = (s2 - s1 * s1 / double(nf)) / double(nf - 1u);
+      if (!(var > 0.0)) var = 0.0;
+    }
+    const uint32_t e0 = (e0_override >= 0) ? uint32_t(e0_override) : window_base(var, nf);
+    s_e0 = e0;
+    ws.ctrl->e0 = e0;
+    ws.ctrl->n_err_slots = nchunks * kParts;
+    const uint32_t magic = B ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
+    hd[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(B ? 1u : 0u) << 48) | (uint64_t(e0) << 56);
+    hd[1] = n;
+    hd[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
+    hd[3] = nchunks;
+    hd[5] = nch;
+    for (int i = 7; i < 16; i++) hd[i] = 0u;
+  }
+  __syncthreads();
+  const uint32_t e0 = s_e0;
+
+  // (2) Sizes of the run's chunks.  A part's escapes are its coded values
+  // minus those whose exponent lies in the window [E0, E0 + 6]: three
+  // cumulative rows, read for the chunk's four parts at once.  A part inside a
+  // block that spans several parts codes its values only if some part of the
+  // block saw a change.
+  const uint64_t P = nchunks * kParts;
+  const uint16_t* row_lo = ws.cum + uint64_t(e0) * P;
+  const uint16_t* row_hi = ws.cum + uint64_t(e0 + 7u) * P;
+  const uint16_t* row_all = ws.cum + uint64_t(kBins) * P;
+  const uint32_t ppb = B > kPartValues ? B / kPartValues : 1u;  // parts per block when blocks span parts
+  uint64_t run_bytes = 0, run_esc = 0;
+  uint64_t sizes[kRunRegs];
+#pragma unroll
+  for (uint32_t i = 0; i < kRunRegs; i++) sizes[i] = 0u;
+  for (uint64_t c = c0; c < c1; c++) {
+    const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
+    const uint2 lo = *reinterpret_cast<const uint2*>(row_lo + c * kParts);
+    const uint2 hi = *reinterpret_cast<const uint2*>(row_hi + c * kParts);
+    const uint2 all = *reinterpret_cast<const uint2*>(row_all + c * kParts);
+    uint32_t nchp[kParts] = {1u, 1u, 1u, 1u};
+    if (B > kPartValues) {
+      const Partial* pp = ws.partial + c * kParts;
+#pragma unroll
+      for (uint32_t h = 0; h < kParts; h++) nchp[h] = pp[h].nch;
+    }
+    uint32_t nch = 0;
+    if (B) {
+      if (per <= kRunRegs) {
+#pragma unroll
+        for (uint32_t i = 0; i < kRunRegs; i++)
+          if (i == c - c0) nch = nchs[i];
+      } else {
+        nch = chunk_changed_blocks(ws.partial + c * kParts, B);
+      }
+    }
+    uint32_t esc[kParts], acc = 0;
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      const uint32_t sh = 16u * (h & 1u);
+      const uint32_t l = (((h < 2u) ? lo.x : lo.y) >> sh) & 0xFFFFu;
+      const uint32_t u = (((h < 2u) ? hi.x : hi.y) >> sh) & 0xFFFFu;
+      const uint32_t t = (((h < 2u) ? all.x : all.y) >> sh) & 0xFFFFu;
+      bool codes = true;
+      if (B > kPartValues) {
+        uint32_t any = 0;
+#pragma unroll
+        for (uint32_t k = 0; k < kParts; k++) any |= (k / ppb == h / ppb) ? nchp[k] : 0u;
+        codes = any != 0u;
+      }
+      esc[h] = acc;
+      acc += codes ? t - (u - l) : 0u;
+    }
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) ws.partesc[c * kParts + h] = esc[h];
+    ws.chunkesc[c] = acc;
+    const uint64_t planes = B ? uint64_t(nch) * B / 8u : cdiv(nc, 8u);
+    const uint64_t size = pad128(nc) + (B ? 128u : 0u) + 3u * pad128(planes) + pad128(acc);
+    if (per <= kRunRegs) {
+#pragma unroll
+      for (uint32_t i = 0; i < kRunRegs; i++)
+        if (i == c - c0) sizes[i] = size;
+    } else {
+      table[c] = size;
+    }
+    run_bytes += size;
+    run_esc += acc;
+  }
+  const uint64_t ib = wave_incl_scan_u64(run_bytes), ie = wave_incl_scan_u64(run_esc);
+  if (lane == 63u) {
+    s_bytes[wave] = ib;
+    s_esc[wave] = ie;
+  }
+  __syncthreads();
+  uint64_t before = ib - run_bytes, total_bytes = 0, total_esc = 0;
+  for (uint32_t w = 0; w < kWaves; w++) {
+    if (w < wave) before += s_bytes[w];
+    total_bytes += s_bytes[w];
+    total_esc += s_esc[w];
+  }
+  uint64_t at = base + before;
+  for (uint64_t c = c0; c < c1; c++) {
+    uint64_t size = 0;
+    if (per <= kRunRegs) {
+#pragma unroll
+      for (uint32_t i = 0; i < kRunRegs; i++)
+        if (i == c - c0) size = sizes[i];
+    } else {
+      size = table[c];
+    }
+    table[c] = at;
+    at += size;
+  }
+  if (tid == 0) {
+    const uint64_t total = base + total_bytes;
+    table[nchunks] = total;
+    hd[4] = total;
+    hd[6] = total_esc;
+    *out_size = total;
   }
 }
 
@@ -941,7 +908,7 @@ __device__ inline void stage_bitmap(uint32_t w, uint32_t* s_bits, uint32_t* s_ra
 }
 
 // One part of a chunk.  Its stream offset, the escapes before it in its chunk
-// and the chunk's escape total all come from k_layout, so the part waits on
+// and the chunk's escape total all come from k_plan, so the part waits on
 // nothing: load, code, write.
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restrict__ x, uint64_t n,
@@ -1038,7 +1005,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     }
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
-  // The count must match what k_layout read off the histogram; a mismatch
+  // The count must match what k_plan read off the histogram; a mismatch
   // would overrun the escape section, so no escapes are written and the error
   // word reports it.
   const bool esc_ok = pesc == esc_part;
@@ -1494,8 +1461,6 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   }
   launch(k_plan, dim3(1), dim3(kThreads), stream, n, nchunks, B, e0_override, out, d_out_size, ws);
   if (nchunks) {
-    launch(k_layout, dim3(uint32_t(cdiv(nchunks, kLayoutThreads))), dim3(kLayoutThreads), stream, n, nchunks, lb, out,
-           d_out_size, ws);
     if (ciera)
       launch(k_write<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, lb, out, ws);
     else
