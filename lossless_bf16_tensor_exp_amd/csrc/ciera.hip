@@ -1148,14 +1148,25 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   }
   uint4 se = make_uint4(0u, 0u, 0u, 0u);
   if (esc_whole && tid < p.esc_len / 16u) se = *reinterpret_cast<const uint4*>(in + g.esc + 16u * tid);
-  // code-0 slots before this part: every such slot is a real value
-  uint32_t zeros = 0;
-  for (uint32_t i = tid; i < p.sbase / 8u; i += kPartThreads) {
-    const uint2 a = *reinterpret_cast<const uint2*>(in + g.plane + 8u * i);
-    const uint2 b = *reinterpret_cast<const uint2*>(in + g.plane + p.pb + 8u * i);
-    const uint2 d = *reinterpret_cast<const uint2*>(in + g.plane + 2u * p.pb + 8u * i);
-    zeros += __popc(~(a.x | b.x | d.x)) + __popc(~(a.y | b.y | d.y));
+  // Code-0 slots before this part (every such slot is a real value): at most
+  // 3 * kPartUnits slots, i.e. kZeroRounds 8-byte pieces per thread, all
+  // loads issued before any is used.
+  constexpr uint32_t kZeroRounds = (3u * kPartUnits / 8u + kPartThreads - 1u) / kPartThreads;
+  uint2 za[kZeroRounds], zb[kZeroRounds], zd[kZeroRounds];
+#pragma unroll
+  for (uint32_t r = 0; r < kZeroRounds; r++) {
+    const uint32_t i = tid + r * kPartThreads;
+    za[r] = zb[r] = zd[r] = make_uint2(~0u, ~0u);
+    if (i < p.sbase / 8u) {
+      za[r] = *reinterpret_cast<const uint2*>(in + g.plane + 8u * i);
+      zb[r] = *reinterpret_cast<const uint2*>(in + g.plane + p.pb + 8u * i);
+      zd[r] = *reinterpret_cast<const uint2*>(in + g.plane + 2u * p.pb + 8u * i);
+    }
   }
+  uint32_t zeros = 0;
+#pragma unroll
+  for (uint32_t r = 0; r < kZeroRounds; r++)
+    zeros += __popc(~(za[r].x | zb[r].x | zd[r].x)) + __popc(~(za[r].y | zb[r].y | zd[r].y));
 #pragma unroll
   for (uint32_t r = 0; r < kPlaneRounds; r++) {
     const uint32_t i = tid + r * kPartThreads;
