@@ -74,9 +74,15 @@ static_assert(kPartBitmapWords * 32u * 64u == kPartValues, "a part's blocks fit 
 
 __host__ __device__ inline uint64_t pad128(uint64_t v) { return (v + 127u) & ~uint64_t(127); }
 __host__ __device__ inline uint64_t cdiv(uint64_t a, uint64_t b) { return (a + b - 1u) / b; }
+// After the header: the chunk table (nchunks + 1 absolute u64 offsets), then
+// the escape index (per chunk one u64 of four u16: the escapes among the
+// chunk's values before value 0, 16384, 32768 and 49152 of the chunk, i.e.
+// before each part), zero-padded to 128 bytes.  The index lets every part
+// of a chunk find its first escape without reading the parts before it.
 __host__ __device__ inline uint64_t table_end(uint64_t nchunks) {
-  return kHeader + pad128(8u * (nchunks + 1u));
+  return kHeader + pad128(8u * (nchunks + 1u) + 8u * nchunks);
 }
+static_assert(kParts == 4u, "one u64 of four u16 escape counts per chunk");
 
 // Workspace: control block, error words, per-part partial sums and bitmap
 // words, cumulative exponent histograms of the parts, per-part escape offsets
@@ -709,8 +715,8 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
     s_nf[wave] = m;
     s_nch[wave] = q;
   }
-  // zero the table's padding words (entries past nchunks)
-  for (uint64_t i = nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
+  // zero the padding words after the chunk table and the escape index
+  for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
   __syncthreads();
   if (tid == 0) {
     double s1 = 0.0, s2 = 0.0;
@@ -796,6 +802,8 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) ws.partesc[c * kParts + h] = esc[h];
     ws.chunkesc[c] = acc;
+    table[nchunks + 1u + c] = uint64_t(esc[0]) | (uint64_t(esc[1]) << 16) | (uint64_t(esc[2]) << 32) |
+                              (uint64_t(esc[3]) << 48);
     const uint64_t planes = B ? uint64_t(nch) * B / 8u : cdiv(nc, 8u);
     const uint64_t size = pad128(nc) + (B ? 128u : 0u) + 3u * pad128(planes) + pad128(acc);
     if (per <= kRunRegs) {
@@ -1064,15 +1072,12 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
 }
 
 // ------------------------------------------------------------------ k_decode
-// Escape bytes a decoding part stages in LDS.  A chunk's escape section of at
-// most kEscWhole bytes is loaded whole, together with the part's other loads;
-// a longer one is staged as a window from the 16-byte boundary at or below
-// the part's first escape, which holds all of the part's escapes (at most
-// kPartUnits * 8 bytes, after at most 15 bytes of earlier parts').  The LDS
-// array has 16 spare bytes for the 12-byte reads of merge_escapes.
+// Escape bytes a decoding part stages in LDS: from the 16-byte boundary at or
+// below its first escape, all of its escapes (at most kPartUnits * 8, after at
+// most 15 bytes of earlier parts').  The LDS array has 16 spare bytes for the
+// 12-byte reads of merge_escapes.
 constexpr uint32_t kEscStage = kPartUnits * 8u + 16u;
-constexpr uint32_t kEscWhole = 16u * kPartThreads;
-static_assert(kEscStage % 16u == 0u && kEscWhole <= kEscStage, "escape staging");
+static_assert(kEscStage % 16u == 0u, "escape staging");
 
 // Put a unit's escape bytes into e: the k-th set bit of emask (a code-0
 // byte) takes the k-th byte from byte a of the staged escapes.  Byte
@@ -1104,6 +1109,9 @@ struct DecodePart {
   uint32_t nc, nunits, pu0, e0, pb, esc_len, sbase, stage_len;
   bool last_with_data;
   uint32_t log2B, nb, nch;
+  uint32_t part;    // h: the part's quarter of the chunk
+  uint64_t index;   // the chunk's escape index word (four u16)
+  uint32_t before;  // escapes of the chunk before the part, from the index
 };
 
 // Decode one part.  kFull: every unit of the part holds 8 values, so no
@@ -1111,15 +1119,13 @@ struct DecodePart {
 template <bool kCiera, bool kFull>
 __device__ __attribute__((always_inline)) inline uint32_t decode_part(const DecodePart& p, const uint32_t* s_bits,
                                                                       const uint32_t* s_rank, uint8_t* s_planes,
-                                                                      uint8_t* s_esc, uint32_t* s_tot,
-                                                                      uint32_t* s_red) {
+                                                                      uint8_t* s_esc, uint32_t* s_tot) {
   const uint32_t tid = threadIdx.x;
   const uint8_t* __restrict__ in = p.in;
   const ChunkGeom& g = p.g;
   // Issue every load before using any: sign+mantissa and, for unchanged
-  // blocks, the receiver cache into registers; the part's plane bytes, a
-  // small escape section, and the planes before the part (for its escape
-  // offset).
+  // blocks, the receiver cache into registers; the part's plane bytes and
+  // escapes, staged in LDS.
   uint2 smv[kUPT], ev[kUPT];
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
@@ -1135,7 +1141,6 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
       }
     }
   }
-  const bool esc_whole = p.esc_len <= kEscWhole;
   const uint32_t np = p.stage_len / 8u;  // 8-byte pieces per plane, <= kStage / 8
   uint2 st[kPlaneRounds];
 #pragma unroll
@@ -1146,27 +1151,23 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
       st[r] = *reinterpret_cast<const uint2*>(in + g.plane + b * p.pb + p.sbase + 8u * (i - b * np));
     }
   }
-  uint4 se = make_uint4(0u, 0u, 0u, 0u);
-  if (esc_whole && tid < p.esc_len / 16u) se = *reinterpret_cast<const uint4*>(in + g.esc + 16u * tid);
-  // Code-0 slots before this part (every such slot is a real value): at most
-  // 3 * kPartUnits slots, i.e. kZeroRounds 8-byte pieces per thread, all
-  // loads issued before any is used.
-  constexpr uint32_t kZeroRounds = (3u * kPartUnits / 8u + kPartThreads - 1u) / kPartThreads;
-  uint2 za[kZeroRounds], zb[kZeroRounds], zd[kZeroRounds];
+  // Escapes: staged from the 16-byte boundary at or below the part's first
+  // escape, as many as the index gives the part (the count is checked against
+  // the planes below, before any escape is used).  The section length is a
+  // multiple of 128.
+  const uint32_t first = min(p.before, p.esc_len);
+  const uint32_t esc_lo = first & ~15u;
+  const uint32_t next = (p.part + 1u < kParts) ? uint32_t(p.index >> (16u * (p.part + 1u))) & 0xFFFFu : p.esc_len;
+  const uint32_t own = min(next > first ? next - first : 0u, kPartUnits * 8u);
+  const uint32_t pieces = min((p.esc_len - esc_lo) / 16u, (first - esc_lo + own + 15u) / 16u);
+  constexpr uint32_t kEscRounds = 2u;  // pieces loaded before any is used; more are rare
+  uint4 se[kEscRounds];
 #pragma unroll
-  for (uint32_t r = 0; r < kZeroRounds; r++) {
+  for (uint32_t r = 0; r < kEscRounds; r++) {
     const uint32_t i = tid + r * kPartThreads;
-    za[r] = zb[r] = zd[r] = make_uint2(~0u, ~0u);
-    if (i < p.sbase / 8u) {
-      za[r] = *reinterpret_cast<const uint2*>(in + g.plane + 8u * i);
-      zb[r] = *reinterpret_cast<const uint2*>(in + g.plane + p.pb + 8u * i);
-      zd[r] = *reinterpret_cast<const uint2*>(in + g.plane + 2u * p.pb + 8u * i);
-    }
+    se[r] = make_uint4(0u, 0u, 0u, 0u);
+    if (i < pieces) se[r] = *reinterpret_cast<const uint4*>(in + g.esc + esc_lo + 16u * i);
   }
-  uint32_t zeros = 0;
-#pragma unroll
-  for (uint32_t r = 0; r < kZeroRounds; r++)
-    zeros += __popc(~(za[r].x | zb[r].x | zd[r].x)) + __popc(~(za[r].y | zb[r].y | zd[r].y));
 #pragma unroll
   for (uint32_t r = 0; r < kPlaneRounds; r++) {
     const uint32_t i = tid + r * kPartThreads;
@@ -1175,25 +1176,15 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
       *reinterpret_cast<uint2*>(s_planes + b * kStage + 8u * (i - b * np)) = st[r];
     }
   }
-  if (esc_whole && tid < p.esc_len / 16u) reinterpret_cast<uint4*>(s_esc)[tid] = se;
-  zeros = wave_sum_u32(zeros);
-  if (lane_id() == 0u) s_red[tid >> 6] = zeros;
-  __syncthreads();
-  uint32_t before = 0;
 #pragma unroll
-  for (uint32_t w = 0; w < kPartWaves; w++) before += s_red[w];
-  // staged byte range [esc_lo, esc_hi) of the escape section; a long section
-  // is staged from the 16-byte boundary at or below the part's first escape
-  uint32_t esc_lo = 0, esc_hi = p.esc_len;
-  if (!esc_whole) {  // uniform
-    esc_lo = min(before, p.esc_len) & ~15u;
-    esc_hi = min(esc_lo + kEscStage, p.esc_len);
-    const uint32_t pieces = (esc_hi - esc_lo) / 16u;  // the section length is a multiple of 128
-#pragma unroll 4
-    for (uint32_t i = tid; i < pieces; i += kPartThreads)
-      reinterpret_cast<uint4*>(s_esc)[i] = *reinterpret_cast<const uint4*>(in + g.esc + esc_lo + 16u * i);
-    __syncthreads();
+  for (uint32_t r = 0; r < kEscRounds; r++) {
+    const uint32_t i = tid + r * kPartThreads;
+    if (i < pieces) reinterpret_cast<uint4*>(s_esc)[i] = se[r];
   }
+  for (uint32_t i = tid + kEscRounds * kPartThreads; i < pieces; i += kPartThreads)
+    reinterpret_cast<uint4*>(s_esc)[i] = *reinterpret_cast<const uint4*>(in + g.esc + esc_lo + 16u * i);
+  __syncthreads();
+  const uint32_t before = p.before;
 
   uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
 #pragma unroll
@@ -1223,10 +1214,16 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
     }
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);
-  // every escape read stays inside the chunk's escape section; the part that
-  // holds the chunk's last values also checks the section's padded length
-  const bool bad = (uint64_t(before) + pesc > p.esc_len) ||
-                   (p.last_with_data && g.esc + pad128(uint64_t(before) + pesc) != g.esc + p.esc_len);
+  // Every escape read stays inside the chunk's escape section and the staged
+  // bytes: the index entry after the part must equal before + pesc, and the
+  // part that holds the chunk's last values checks the section's padded
+  // length and the index entries of the quarters past the data.
+  const uint32_t after = before + pesc;
+  bool bad = after > p.esc_len || (p.part + 1u < kParts && next != after);
+  if (p.last_with_data) {
+    bad |= pad128(after) != p.esc_len;
+    for (uint32_t q = p.part + 1u; q < kParts; q++) bad |= (uint32_t(p.index >> (16u * q)) & 0xFFFFu) != after;
+  }
   if (bad) return uint32_t(CIERA_ERR_FORMAT);  // uniform
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
@@ -1244,21 +1241,8 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   return 0u;
 }
 
-// Workgroups are dispatched round-robin over the chip's 8 XCDs, each with its
-// own L2.  Decode maps workgroup b to (chunk, part) so that the kParts parts of
-// a chunk share one XCD: a part reads the plane bytes of the parts before it,
-// which then come from that L2 instead of HBM.  Chunks past the last full
-// group of 8 keep the plain mapping.
-constexpr uint32_t kXcds = 8u;
-__device__ inline uint2 decode_part_of(uint32_t b, uint64_t nchunks) {
-  const uint64_t grouped = nchunks / kXcds * kXcds * kParts;
-  if (b >= grouped) return make_uint2(b / kParts, b % kParts);
-  const uint32_t x = b % kXcds, slot = b / kXcds;
-  return make_uint2((slot / kParts) * kXcds + x, slot % kParts);
-}
-
-// One part of a chunk; parts never wait on each other.  A part's first escape
-// is found by counting the code-0 slots of the plane bytes before its own.
+// One part of a chunk; parts never wait on each other: the escape index gives
+// each part its first escape.
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restrict__ in, uint64_t in_size,
                                                          uint16_t* __restrict__ y, uint64_t n, uint64_t nchunks,
@@ -1270,23 +1254,21 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   __shared__ uint32_t s_ok;    // header and table entries are consistent
   __shared__ uint32_t s_fits;  // the chunk's fixed-size sections lie inside it
   __shared__ uint32_t s_e0;
-  __shared__ uint64_t s_begin, s_end;
+  __shared__ uint64_t s_begin, s_end, s_index;
   __shared__ uint32_t s_bits[kBitmapWords];
   __shared__ uint32_t s_rank[kBitmapWords];
   __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
-  __shared__ uint32_t s_red[kPartWaves];
   const uint32_t tid = threadIdx.x;
   const uint32_t wg = blockIdx.x;
-  const uint2 ch = decode_part_of(wg, nchunks);
-  const uint32_t c = ch.x;
-  const uint32_t h = ch.y;
+  const uint32_t c = wg / kParts;
+  const uint32_t h = wg % kParts;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint64_t base_off = table_end(nchunks);
   if (tid == 0) {
     uint32_t ok = 1u;
     const uint64_t* hd = reinterpret_cast<const uint64_t*>(in);
     const uint32_t magic = kCiera ? 0x52454943u : 0x3350495Au;
-    uint64_t begin = 0, end = 0;
+    uint64_t begin = 0, end = 0, index = 0;
     uint32_t e0 = 0;
     if (in_size < base_off) {
       ok = 0u;
@@ -1306,17 +1288,22 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
       const uint64_t* table = reinterpret_cast<const uint64_t*>(in + kHeader);
       ok &= table[0] == base_off;
       ok &= table[nchunks] == total;
+      if (wg == 0u)  // the padding after the escape index is zero
+        for (uint64_t i = 2u * nchunks + 1u; i < (base_off - kHeader) / 8u; i++) ok &= table[i] == 0u;
       if (ok && nchunks) {
         begin = table[c];
         end = table[c + 1u];
+        index = table[nchunks + 1u + c];
         ok &= begin >= base_off && begin <= end && end <= total;
         ok &= ((begin | end) & 127u) == 0u;
+        ok &= (index & 0xFFFFu) == 0u;  // no escapes before the chunk's first value
       }
     }
     s_ok = ok;
     s_e0 = e0;
     s_begin = begin;
     s_end = end;
+    s_index = index;
     if (wg == 0u) *n_err_slots = gridDim.x;
   }
   __syncthreads();
@@ -1365,6 +1352,7 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   }
   const uint32_t pb = uint32_t(g.plane_bytes);
   const uint32_t esc_len = uint32_t(end - g.esc);
+  const uint64_t index = s_index;
   const uint32_t s_h = kCiera ? coded_before(pu0, s_bits, s_rank, log2B, nb, nch) : pu0;
   const bool last_with_data = pu0 + kPartUnits >= nunits;
   // slots of the part's own units (a block may span several parts)
@@ -1388,11 +1376,14 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   p.log2B = log2B;
   p.nb = nb;
   p.nch = nch;
+  p.part = h;
+  p.index = index;
+  p.before = uint32_t(index >> (16u * h)) & 0xFFFFu;
   uint32_t err;
   if (8u * (pu0 + kPartUnits) <= nc)
-    err = decode_part<kCiera, true>(p, s_bits, s_rank, s_planes, s_esc, s_tot, s_red);
+    err = decode_part<kCiera, true>(p, s_bits, s_rank, s_planes, s_esc, s_tot);
   else
-    err = decode_part<kCiera, false>(p, s_bits, s_rank, s_planes, s_esc, s_tot, s_red);
+    err = decode_part<kCiera, false>(p, s_bits, s_rank, s_planes, s_esc, s_tot);
   if (tid == 0) err_slots[wg] = err;
 }
 

@@ -60,7 +60,11 @@
  *     40 u64 n_changed_blocks (ciera; in zip3 mode 0)
  *     48 u64 n_escapes
  *   chunk table at byte 128: nchunks+1 u64 absolute offsets (the last one is
- *     total_bytes), zero-padded to a 128-byte multiple.
+ *     total_bytes);
+ *   escape index right after it: for each chunk, four u16 giving the number of
+ *     escapes among the chunk's values before value 0, 16384, 32768 and
+ *     49152 of the chunk (a seek index: a decoder can start at any quarter of
+ *     a chunk); table and index together zero-padded to a 128-byte multiple.
  *   chunk c (values [cC, min(cC+C, n)), n_c of them), each section padded to
  *   a multiple of 128 bytes with zeros:
  *     1. sm:     n_c bytes, sm = (sign << 7) | mantissa
@@ -95,6 +99,7 @@ enum {
 };
 
 #define ORC_CHUNK 65536ull
+#define ORC_QUARTER 16384ull /* escape index granularity */
 #define ORC_HEADER 128ull
 #define ORC_MAX_N (1ull << 40)
 
@@ -103,6 +108,10 @@ static const double ORC_K0 = 0x1.a610ca4a234eep+9;
 
 static uint64_t pad128(uint64_t x) { return (x + 127ull) / 128ull * 128ull; }
 static uint64_t ceil_div(uint64_t a, uint64_t b) { return (a + b - 1) / b; }
+
+/* Byte offset of the escape index and of the first chunk. */
+static uint64_t index_pos(uint64_t nchunks) { return ORC_HEADER + 8ull * (nchunks + 1ull); }
+static uint64_t payload_pos(uint64_t nchunks) { return ORC_HEADER + pad128(8ull * (nchunks + 1ull) + 8ull * nchunks); }
 
 static unsigned exp_field(uint16_t v) { return (v >> 7) & 0xFFu; }
 static unsigned sm_field(uint16_t v) { return ((unsigned)(v >> 15) << 7) | (v & 0x7Fu); }
@@ -198,7 +207,7 @@ static int valid_block_size(uint32_t B) {
  * value an escape).  B = 0 selects zip3 mode. */
 uint64_t orc_max_encoded_size(uint64_t n, uint32_t B) {
   uint64_t nchunks = ceil_div(n, ORC_CHUNK);
-  uint64_t size = ORC_HEADER + pad128(8ull * (nchunks + 1ull));
+  uint64_t size = payload_pos(nchunks);
   for (uint64_t c = 0; c < nchunks; c++) {
     uint64_t nc = (n - c * ORC_CHUNK < ORC_CHUNK) ? n - c * ORC_CHUNK : ORC_CHUNK;
     size += pad128(nc);
@@ -249,12 +258,15 @@ int orc_encode(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, int e0
     }
   }
 
-  uint64_t pos = ORC_HEADER + pad128(8ull * (nchunks + 1ull));
+  uint64_t pos = payload_pos(nchunks);
   uint64_t total_changed = 0, total_esc = 0;
   for (uint64_t c = 0; c < nchunks; c++) {
     const uint64_t start = c * ORC_CHUNK;
     const uint64_t nc = (n - start < ORC_CHUNK) ? n - start : ORC_CHUNK;
     put_u64(out + ORC_HEADER + 8ull * c, pos);
+    /* escape index: escapes among the chunk's values before quarter q */
+    uint64_t quarter_esc[4] = {0, 0, 0, 0};
+    unsigned next_q = 1;
 
     /* 1. sign+mantissa bytes of every value */
     for (uint64_t t = 0; t < nc; t++) out[pos + t] = (uint8_t)sm_field(x[start + t]);
@@ -281,6 +293,7 @@ int orc_encode(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, int e0
     uint64_t slot = 0;
     if (!ciera) {
       for (uint64_t t = 0; t < nc; t++, slot++) {
+        while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
         unsigned e = exp_field(x[start + t]);
         unsigned code = code_of(e, e0);
         for (int b = 0; b < 3; b++)
@@ -293,6 +306,7 @@ int orc_encode(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, int e0
         for (uint64_t s = 0; s < B; s++, slot++) {
           uint64_t t = j * B + s;
           if (t >= nc) continue; /* slot past the end of the data: stays 0 */
+          while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
           unsigned e = exp_field(x[start + t]);
           unsigned code = code_of(e, e0);
           for (int b = 0; b < 3; b++)
@@ -301,6 +315,9 @@ int orc_encode(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, int e0
         }
       }
     }
+    while (next_q < 4u) quarter_esc[next_q++] = nesc;
+    for (unsigned q = 0; q < 4u; q++)
+      put_u16(out + index_pos(nchunks) + 8ull * c + 2ull * q, (unsigned)quarter_esc[q]);
     pos = esc_pos + pad128(nesc);
     total_changed += nch;
     total_esc += nesc;
@@ -345,7 +362,7 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
   if (in == NULL || in_size < ORC_HEADER) return ORC_ERR_FORMAT;
 
   const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
-  const uint64_t base = ORC_HEADER + pad128(8ull * (nchunks + 1ull));
+  const uint64_t base = payload_pos(nchunks);
   if (memcmp(in, ciera ? "CIER" : "ZIP3", 4) != 0) return ORC_ERR_FORMAT;
   if (get_u16(in + 4) != 1u) return ORC_ERR_FORMAT;
   if (in[6] != (ciera ? 1 : 0)) return ORC_ERR_FORMAT;
@@ -361,6 +378,8 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
     if (in[i] != 0) return ORC_ERR_FORMAT;
   if (get_u64(in + ORC_HEADER) != base) return ORC_ERR_FORMAT;
   if (get_u64(in + ORC_HEADER + 8ull * nchunks) != total) return ORC_ERR_FORMAT;
+  for (uint64_t i = index_pos(nchunks) + 8ull * nchunks; i < base; i++)
+    if (in[i] != 0) return ORC_ERR_FORMAT;
 
   uint64_t total_changed = 0, total_esc = 0;
   for (uint64_t c = 0; c < nchunks; c++) {
@@ -387,8 +406,11 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
     if (esc_pos > end) return ORC_ERR_FORMAT;
 
     uint64_t nesc = 0;
+    uint64_t quarter_esc[4] = {0, 0, 0, 0};
+    unsigned next_q = 1;
     if (!ciera) {
       for (uint64_t t = 0; t < nc; t++) {
+        while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
         unsigned code = 0, e;
         for (int b = 0; b < 3; b++) code |= ((in[plane_pos[b] + t / 8] >> (t % 8)) & 1u) << b;
         if (code != 0) {
@@ -405,6 +427,7 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
         const int is_changed = (in[bitmap_pos + j / 8] >> (j % 8)) & 1u;
         for (uint64_t s = 0; s < B && j * B + s < nc; s++) {
           const uint64_t t = j * B + s;
+          while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
           unsigned e;
           if (!is_changed) {
             e = cache[start + t];
@@ -427,6 +450,9 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
       }
     }
     if (esc_pos + pad128(nesc) != end) return ORC_ERR_FORMAT;
+    while (next_q < 4u) quarter_esc[next_q++] = nesc;
+    for (unsigned q = 0; q < 4u; q++)
+      if (get_u16(in + index_pos(nchunks) + 8ull * c + 2ull * q) != quarter_esc[q]) return ORC_ERR_FORMAT;
     total_changed += nch;
     total_esc += nesc;
   }

@@ -6,7 +6,8 @@ two implementations agreeing, not by one.  It also computes the variance
 with exact rationals, which pins the oracle's FP64 statistic.
 
 Layout (the same reading the oracle implements): header of 128 bytes, chunk
-table, then per 65,536-value chunk the sections sign+mantissa, [bitmap],
+table, escape index (per chunk four u16: escapes before each 16,384-value
+quarter), then per 65,536-value chunk the sections sign+mantissa, [bitmap],
 three code planes and escapes, each padded to 128 bytes (ZipCCL research
 digest, section 3.1; CIERA page, section 3.1).
 """
@@ -79,10 +80,11 @@ def encode(xs, B: int = 0, cache=None, e0: int | None = None) -> bytes:
         return e - e0 + 1 if e0 <= e <= e0 + 6 else 0
 
     nchunks = -(-n // CHUNK)
-    table_len = 8 * (nchunks + 1)
+    table_len = 8 * (nchunks + 1) + 8 * nchunks  # chunk offsets, then the escape index
     base = 128 + table_len + ((-table_len) % 128)
     body = bytearray()
     offsets = []
+    index = []  # per chunk: escapes among its values before each quarter
     total_changed = total_esc = 0
     for c in range(nchunks):
         offsets.append(base + len(body))
@@ -104,7 +106,9 @@ def encode(xs, B: int = 0, cache=None, e0: int | None = None) -> bytes:
         codes = [code(exps[i]) if i is not None else 0 for i in slots]
         for b in range(3):
             seg += _pad(_bits_to_bytes([(cd >> b) & 1 for cd in codes]))
-        esc = bytearray(exps[i] for i, cd in zip(slots, codes) if i is not None and cd == 0)
+        esc_at = [i for i, cd in zip(slots, codes) if i is not None and cd == 0]
+        esc = bytearray(exps[i] for i in esc_at)
+        index.append([sum(1 for i in esc_at if i < lo + q * (CHUNK // 4)) for q in range(4)])
         total_esc += len(esc)
         seg += _pad(esc)
         body += seg
@@ -115,6 +119,8 @@ def encode(xs, B: int = 0, cache=None, e0: int | None = None) -> bytes:
                         total_changed, total_esc)
     head += b"\0" * (128 - len(head))
     table = bytearray(struct.pack(f"<{nchunks + 1}Q", *offsets))
+    for q4 in index:
+        table += struct.pack("<4H", *q4)
     _pad(table)
     return bytes(head + table + body)
 
@@ -128,12 +134,12 @@ def decode_fields(stream: bytes) -> dict:
 
 
 def closed_form_size(n: int, B: int, chunk_changed: list[int], chunk_escapes: list[int]) -> int:
-    """Stream size from per-chunk counts: 128 + pad(8 (nc+1)) + sum over chunks
-    of pad(n_c) + [ciera] pad(ceil(nb_c/8)) + 3 pad(P_c) + pad(esc_c)."""
+    """Stream size from per-chunk counts: 128 + pad(8 (nc+1) + 8 nc) + sum over
+    chunks of pad(n_c) + [ciera] pad(ceil(nb_c/8)) + 3 pad(P_c) + pad(esc_c)."""
     def pad(v):
         return (v + 127) // 128 * 128
     nchunks = -(-n // CHUNK)
-    size = 128 + pad(8 * (nchunks + 1))
+    size = 128 + pad(8 * (nchunks + 1) + 8 * nchunks)
     for c in range(nchunks):
         nc = min(CHUNK, n - c * CHUNK)
         size += pad(nc)

@@ -120,8 +120,10 @@ def test_decode_rejects_malformed_streams():
     good, _ = gpu_encode(x)
     y, _, st = gpu_decode(good, n)
     assert st == 0 and np.array_equal(y, x)
+    idx = 128 + 8 * 5  # four chunks: five table entries, then the escape index
     for off, val in [(0, 0x41), (4, 2), (6, 1), (7, 250), (8, 0x71), (22, 0), (24, 9), (33, 0xEE), (60, 1),
-                     (128, 0x80), (136, 1), (144, 0x11)]:
+                     (128, 0x80), (136, 1), (144, 0x11), (idx, 1), (idx + 4, 0x7F), (idx + 10, 0xFF),
+                     (idx + 30, 0x3F), (idx + 32, 1)]:
         bad = good.copy()
         assert bad[off] != val
         bad[off] = val

@@ -343,9 +343,12 @@ def test_decode_rejects_corrupted_streams():
     good, _ = oracle.zip3_encode(x)
     assert np.array_equal(oracle.zip3_decode(good, n), x)
     # (byte offset, new value): magic, version, mode, E0 > 249, n, C, nchunks,
-    # total_bytes, reserved header byte, first table entry, second table entry
+    # total_bytes, reserved header byte, first table entry, second table entry,
+    # escape index of chunk 0 (quarters 0 and 2) and of chunk 1 (quarter 1),
+    # padding after the index
+    idx = 128 + 8 * 3  # two chunks: three table entries, then the index
     for off, val in [(0, 0x41), (4, 2), (6, 1), (7, 250), (8, 0x71), (22, 0), (24, 9), (33, 0xEE), (60, 1),
-                     (128, 0x80), (136, 1)]:
+                     (128, 0x80), (136, 1), (idx, 1), (idx + 4, 0x7F), (idx + 10, 0xFF), (idx + 16, 1)]:
         bad = good.copy()
         assert bad[off] != val
         bad[off] = np.uint8(val)
