@@ -21,7 +21,11 @@
  *   header (128 B): "ZIP3"|"CIER", u16 version=1, u8 mode (0 zip3, 1 ciera),
  *     u8 E0, u64 n, u32 B (0 in zip3), u32 C=65536, u64 nchunks,
  *     u64 total_bytes, u64 n_changed_blocks, u64 n_escapes;
- *   chunk table at byte 128: nchunks+1 u64 absolute offsets, padded to 128;
+ *   chunk table at byte 128: nchunks+1 u64 absolute offsets;
+ *   escape index right after it: per chunk four u16, the number of escapes
+ *     among the chunk's values before value 0, 16384, 32768 and 49152 of
+ *     the chunk (a seek index: each quarter decodes on its own); table and
+ *     index padded together to 128;
  *   per chunk: sm[n_c] | bitmap[ceil(nb_c/8)] (ciera) | plane0..2[P_c] |
  *     escapes[n_esc_c], each padded to 128.  Plane b holds bit b of the code
  *     of slot t in bit (t&7) of byte (t>>3).  zip3: slot t = value t of the
