@@ -427,6 +427,18 @@ __device__ inline uint32_t chunk_bitmap_word(const uint32_t* pw, uint32_t t, uin
   return w;
 }
 
+// Workgroups are dealt round-robin over the chip's 8 XCDs, each with its own
+// L2.  k_stats gives XCD x a contiguous range of parts, so that the 64 parts
+// whose u16 entries share a 128-byte line of a cumulative-histogram row are
+// written from one L2 (else every XCD writes the line back).  The last
+// (parts mod 8) workgroups keep their own index.
+constexpr uint32_t kXcds = 8u;
+__device__ inline uint32_t stats_part_of(uint32_t b, uint32_t parts) {
+  const uint32_t per = parts / kXcds;
+  if (b >= per * kXcds) return b;
+  return (b % kXcds) * per + b / kXcds;
+}
+
 // One 256-thread workgroup per part (quarter chunk), units pu0 + 256 j + t.
 // Per part: FP64 variance partials; ciera: changed-block bits against the
 // sender cache and the cache update; an exponent histogram of the values to
@@ -439,7 +451,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   __shared__ double s_s1[kPartWaves], s_s2[kPartWaves];
   __shared__ uint32_t s_nf[kPartWaves], s_wtot[kPartWaves];
   const uint32_t tid = threadIdx.x;
-  const uint32_t wg = blockIdx.x;
+  const uint32_t wg = stats_part_of(blockIdx.x, gridDim.x);  // the part this workgroup takes
   const uint64_t c = wg / kParts;
   const uint32_t h = wg % kParts;
   const uint64_t start = c * kChunk;
