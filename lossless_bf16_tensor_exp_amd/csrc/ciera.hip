@@ -547,14 +547,20 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   // Word bin * kHistCopies + copy, copy chosen by lane: equal exponents
   // within a wave spread over kHistCopies consecutive words (LDS banks).
   const uint32_t copy4 = 4u * (tid & (kHistCopies - 1u));
-  if (!kCiera && full) {
-    // the bin's byte offset straight from the exponent bits of each half
+  if (full) {
+    // every unit holds 8 values: the bin's byte offset comes straight from
+    // the exponent bits of each half; ciera skips units of unchanged blocks
+    // (a part inside a larger block counts all of its values)
     constexpr uint32_t kBinShift = 6u;  // log2(kHistCopies * 4)
     static_assert((1u << kBinShift) == kHistCopies * 4u, "kBinShift");
     constexpr uint32_t kBinMask = 0xFFu << kBinShift;
     uint8_t* hb = reinterpret_cast<uint8_t*>(s_hist);
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) {
+      if (kCiera && B <= kPartValues) {
+        const uint32_t lb = ((8u * (pu0 + j * kPartThreads + tid)) >> log2B) - blk0;
+        if (!((s_bits[lb >> 5] >> (lb & 31u)) & 1u)) continue;
+      }
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const uint32_t w = v[j].w[i];
