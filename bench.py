@@ -44,6 +44,19 @@ def source_hash() -> str:
 KERNELS = ["k_stats", "k_plan", "k_write", "k_decode"]
 
 
+class _Offset:
+    """A device pointer into a tensor at a byte offset, for ciera.bind."""
+
+    def __init__(self, t, off):
+        self.t, self.off = t, off
+
+    def data_ptr(self):
+        return self.t.data_ptr() + self.off
+
+    def numel(self):
+        return self.t.numel() - self.off
+
+
 def measured_bandwidth(torch, dev, nbytes=2 << 30, reps=5):
     """Practical HBM bandwidth in the same run: a streaming copy-like kernel
     (reads and writes nbytes) and a read-only reduction (reads nbytes), each
@@ -230,6 +243,40 @@ def main() -> int:
         klast = (2 * K) % 2 if mode != "zip3" else 0  # input of the last step, index 2K-1
         assert torch.equal(y, xs[klast]), "round trip failed"
 
+    # Single-read encode (zip3 only): the window base comes from byte 7 of the
+    # stream the full encode just wrote, read on the device; K calls, each
+    # kernel timed by HIP events as above.
+    single = None
+    if mode == "zip3":
+        out1 = torch.empty(cap, dtype=torch.uint8, device=dev)
+        size1 = torch.zeros(1, dtype=torch.int64, device=dev)
+        ws1 = torch.empty(wsz, dtype=torch.uint8, device=dev)
+        enc1 = ciera.bind("zip3_encode_e0", xs[0], n, _Offset(out, 7), out1, cap, ws1, wsz, size1, stream=stream)
+        for _ in range(args.warmup):
+            enc1()
+        torch.cuda.synchronize()
+        ev1 = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+               for _ in range(K)]
+        ciera.ciera_time_kernels([pair for row in ev1 for pair in row], stream=stream)
+        t1 = time.perf_counter()
+        for _ in range(K):
+            enc1()
+        torch.cuda.synchronize()
+        wall1 = time.perf_counter() - t1
+        ciera.ciera_time_kernels([])
+        assert ciera.ciera_read_error(ws1) == 0
+        sz1 = int(size1.item())
+        same = sz1 == sizes[0] and bool(torch.equal(out1[:sz1], out[:sz1]))
+        prep_ms = sum(ev1[s][0][0].elapsed_time(ev1[s][0][1]) for s in range(K)) / K
+        write_ms = sum(ev1[s][1][0].elapsed_time(ev1[s][1][1]) for s in range(K)) / K
+        call_ms = sum(ev1[s][0][0].elapsed_time(ev1[s][1][1]) for s in range(K)) / K
+        by1 = 2 * n + sz1
+        single = {"encode_GBps": round(2 * n / (call_ms * 1e-3) / 1e9, 2), "encode_ms": round(call_ms, 5),
+                  "wall_ms_per_call": round(wall1 * 1e3 / K, 4), "stream_equal_to_full_encode": same,
+                  "kernels": {"k_prep1": {"avg_ms": round(prep_ms, 5)},
+                              "k_write1": {"avg_ms": round(write_ms, 5), "algorithmic_bytes": by1,
+                                           "GBps": round(by1 / (write_ms * 1e-3) / 1e9, 1)}}}
+
     if args.copy_probe:
         a = torch.full((args.copy_probe << 19,), 3, dtype=torch.int16, device=dev)
         b = torch.empty_like(a)
@@ -315,6 +362,7 @@ def main() -> int:
         "stream_bytes": stream_bytes,
         "pass2_ms_per_step": round(wall2 * 1e3 / K, 4),
         "kernels": kernels,
+        "single_read_encode": single,
         "bw_measured_GBps": {"copy": round(bw_copy, 1), "read": round(bw_read, 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -137,6 +137,24 @@ ciera_status ciera_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_
  * stream), CIERA_ERR_INTERNAL, or CIERA_ERR_HIP if the copy fails. */
 ciera_status ciera_read_error(const void* d_ws, hipStream_t stream);
 
+/* zip3_encode_e0: zip3 encode with the window base read from device memory
+ * instead of derived from the standard deviation, so that x is read once
+ * (no variance pass).  The digest's window rule (section 3.1) sets E0 from
+ * the tensor's sigma; a caller that takes E0 from an earlier tensor, e.g.
+ * byte 7 of the previous iteration's stream header, trades a possibly less
+ * central window for one read of x instead of two.
+ *   d_e0  in  device pointer to one byte, the window base (0..249); read on
+ *             the device when the encode runs, so it may be produced by
+ *             earlier work on `stream`.  A value above 249 makes the call
+ *             write nothing and ciera_read_error report CIERA_ERR_ARG.
+ * Other arguments, sizes and the workspace as zip3_encode, except that n is
+ * limited to 2^39 (CIERA_ERR_ARG above); the stream equals zip3_encode_ex's
+ * with e0_override = *d_e0.  Within the call, workgroups
+ * wait on each other through the workspace (bounded waits; a wait that does
+ * not end is reported as CIERA_ERR_INTERNAL by ciera_read_error). */
+ciera_status zip3_encode_e0(const void* d_x, uint64_t n, const uint8_t* d_e0, void* d_out, uint64_t out_capacity,
+                            void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream);
+
 /* Kernel timing, a profiling aid (not part of the codec).  events holds
  * n_pairs (start, stop) pairs of hipEvent_t handles, created with timing
  * enabled and owned by the caller.  The next n_pairs kernel launches made by

@@ -14,6 +14,7 @@ Same names as the C ABI::
     zip3_workspace_size(n)                ciera_workspace_size(n, B)
     zip3_encode(x, out, ws, out_size, e0_override=-1, stream=None)
     zip3_decode(inp, in_size, y, ws, stream=None)
+    zip3_encode_e0(x, e0_src, out, ws, out_size, e0_offset=0, stream=None)
     ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None)
     ciera_decode(inp, in_size, y, B, prev_exp, ws, stream=None)
     ciera_read_error(ws, stream=None)
@@ -32,6 +33,7 @@ __all__ = [
     "CieraError", "library_path", "load_library",
     "zip3_max_encoded_size", "ciera_max_encoded_size", "zip3_workspace_size", "ciera_workspace_size",
     "zip3_encode", "zip3_decode", "ciera_encode", "ciera_decode", "ciera_read_error", "ciera_status_string",
+    "zip3_encode_e0",
     "bind", "ciera_time_kernels",
     "CHUNK",
 ]
@@ -72,6 +74,7 @@ def load_library():
     sigs = {
         "zip3_encode": [vp, u64, vp, u64, vp, u64, vp, vp],
         "zip3_encode_ex": [vp, u64, vp, u64, vp, u64, vp, i32, vp],
+        "zip3_encode_e0": [vp, u64, vp, vp, u64, vp, u64, vp, vp],
         "zip3_decode": [vp, u64, vp, u64, vp, u64, vp],
         "ciera_encode": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
         "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, vp],
@@ -158,6 +161,21 @@ def zip3_encode(x, out, ws, out_size, e0_override: int = -1, stream=None) -> Non
     st = lib.zip3_encode_ex(_ptr(x), x.numel(), _ptr(out), out.numel(), _ptr(ws), ws.numel(),
                             ctypes.c_void_p(out_size.data_ptr()), e0_override, _stream(stream))
     _raise(st, "zip3_encode")
+
+
+def zip3_encode_e0(x, e0_src, out, ws, out_size, e0_offset: int = 0, stream=None) -> None:
+    """zip3 encode reading x once, with the window base taken from byte
+    ``e0_offset`` of the uint8 device tensor ``e0_src`` (for instance byte 7,
+    the window base, of the previous iteration's stream)."""
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(e0_src, "e0_src", e0_offset + 1)
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.zip3_encode_e0(_ptr(x), x.numel(), ctypes.c_void_p(e0_src.data_ptr() + e0_offset), _ptr(out),
+                            out.numel(), _ptr(ws), ws.numel(), ctypes.c_void_p(out_size.data_ptr()), _stream(stream))
+    _raise(st, "zip3_encode_e0")
 
 
 def zip3_decode(inp, in_size: int, y, ws, stream=None) -> None:

@@ -86,12 +86,14 @@ static_assert(kParts == 4u, "one u64 of four u16 escape counts per chunk");
 
 // Workspace: control block, error words, per-part partial sums and bitmap
 // words, cumulative exponent histograms of the parts, per-part escape offsets
-// and per-chunk escape totals.
+// and per-chunk escape totals, and the look-back words of the single-read
+// encode.
 struct Ctrl {
   uint32_t e0;
   uint32_t reserved0;
   uint64_t n_err_slots;
-  uint64_t reserved[30];
+  uint64_t done_esc;  // single-read encode: chunks finished << 40 | their escapes
+  uint64_t reserved[29];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -104,7 +106,7 @@ struct Partial {
 };
 
 struct WsLayout {
-  uint64_t err, partial, bitmap, cum, partesc, chunkesc, total;
+  uint64_t err, partial, bitmap, cum, partesc, chunkesc, pcount, cstat, total;
 };
 
 // Cumulative exponent histogram rows: row r (0..256) holds, for every part,
@@ -124,7 +126,9 @@ __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   l.cum = align256(l.bitmap + 4u * kBitmapWords * slots);
   l.partesc = align256(l.cum + 2u * kCumRows * kParts * slots);
   l.chunkesc = align256(l.partesc + 4u * kParts * slots);
-  l.total = align256(l.chunkesc + 4u * slots);
+  l.pcount = align256(l.chunkesc + 4u * slots);
+  l.cstat = align256(l.pcount + 4u * kParts * slots);
+  l.total = align256(l.cstat + 8u * slots);
   return l;
 }
 
@@ -136,6 +140,9 @@ struct Ws {
   uint16_t* cum;        // kCumRows rows of (kParts * nchunks) u16
   uint32_t* partesc;    // escapes before each part within its chunk
   uint32_t* chunkesc;   // escapes per chunk
+  // single-read encode: look-back words
+  uint32_t* pcount;     // per part: kPartReady | escapes of the part
+  uint64_t* cstat;      // per chunk: flag | stream bytes (aggregate or inclusive prefix)
 };
 
 __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
@@ -149,6 +156,8 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.cum = reinterpret_cast<uint16_t*>(b + l.cum);
   w.partesc = reinterpret_cast<uint32_t*>(b + l.partesc);
   w.chunkesc = reinterpret_cast<uint32_t*>(b + l.chunkesc);
+  w.pcount = reinterpret_cast<uint32_t*>(b + l.pcount);
+  w.cstat = reinterpret_cast<uint64_t*>(b + l.cstat);
   return w;
 }
 
@@ -1089,6 +1098,311 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   }
 }
 
+// ------------------------------------------------------------------ single-read encode
+// With the window base known in advance (a byte in device memory, e.g. byte
+// 7 of the previous iteration's stream), encode needs no variance pass and
+// reads x once.  The window rule of the ZipCCL digest (section 3.1) sets E0
+// from the tensor's sigma; which tensor's sigma is the caller's choice here.
+// k_prep1 writes the header and clears the look-back words.  k_write1 codes
+// one part, publishes its escape count and reads those of its chunk's other
+// parts, so that every part knows the chunk's size.  The chunk's last part
+// publishes that size, and every part looks back over the earlier chunks
+// (decoupled look-back) for the chunk's offset; the last part then publishes
+// the chunk's inclusive prefix.
+// Every value passed between workgroups sits in the one word that carries its
+// ready flag, so relaxed device-scope atomics suffice (no cache-wide
+// acquire/release).  A part waits only on its own chunk's parts and on
+// earlier chunks: the lowest unfinished chunk always has all of its parts
+// dispatched, so every wait ends; each is bounded as well and ends in
+// CIERA_ERR_INTERNAL.
+constexpr uint32_t kPartReady = 1u << 31;
+constexpr uint64_t kFlagAgg = 1ull << 62;
+constexpr uint64_t kFlagIncl = 2ull << 62;
+constexpr uint64_t kValMask = (1ull << 62) - 1u;
+constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint32_t kBadE0 = ~0u;
+constexpr uint32_t kDoneShift = 40u;           // ctrl->done_esc: chunks << 40 | escapes
+constexpr uint64_t kMaxSingleReadN = 1ull << 39;  // keeps both fields of done_esc in range
+
+__device__ inline uint64_t load_relaxed(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t load_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_relaxed(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks, uint32_t B,
+                                                    const uint8_t* __restrict__ d_e0, uint8_t* __restrict__ out,
+                                                    uint64_t* __restrict__ out_size, Ws ws) {
+  const uint32_t tid = threadIdx.x;
+  uint64_t* hd = reinterpret_cast<uint64_t*>(out);
+  uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
+  const uint64_t base = table_end(nchunks);
+  for (uint64_t i = tid; i < nchunks * kParts; i += kThreads) ws.pcount[i] = 0u;
+  for (uint64_t i = tid; i < nchunks; i += kThreads) ws.cstat[i] = 0u;
+  if (tid == 0) ws.ctrl->done_esc = 0u;
+  // the padding words after the chunk table and the escape index
+  for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
+  if (tid == 0) {
+    const uint32_t e0 = d_e0[0];
+    const bool ok = e0 <= kMaxE0;
+    ws.ctrl->e0 = ok ? e0 : kBadE0;
+    ws.ctrl->n_err_slots = nchunks ? nchunks * kParts : 1u;
+    if (nchunks == 0u) ws.err[0] = ok ? 0u : uint32_t(CIERA_ERR_ARG);
+    const uint32_t magic = B ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
+    hd[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(B ? 1u : 0u) << 48) | (uint64_t(ok ? e0 : 0u) << 56);
+    hd[1] = n;
+    hd[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
+    hd[3] = nchunks;
+    hd[5] = 0u;
+    for (int i = 7; i < 16; i++) hd[i] = 0u;
+    if (nchunks == 0u) {
+      hd[4] = base;
+      hd[6] = 0u;
+      table[0] = base;
+      *out_size = base;
+    }
+  }
+}
+
+// Stream bytes of the chunks before c (wave 0, 64 predecessors at a time):
+// aggregates are added and the first inclusive prefix ends the search.
+// Returns false if a wait did not end.
+__device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint64_t& pb) {
+  const uint32_t lane = lane_id();
+  pb = 0;
+  int64_t top = int64_t(c) - 1;
+  uint32_t spins = 0;
+  while (top >= 0) {
+    const int64_t k = top - int64_t(lane);
+    const uint64_t st = (k >= 0) ? load_relaxed(&ws.cstat[k]) : kFlagIncl;
+    const uint64_t flag = st & ~kValMask;
+    if (__ballot(flag == 0u) != 0u) {
+      if (++spins > kSpinLimit) return false;
+      __builtin_amdgcn_s_sleep(2);
+      continue;
+    }
+    const uint64_t incl = __ballot(flag == kFlagIncl);
+    if (incl != 0u) {
+      const uint32_t first = uint32_t(__builtin_ctzll(incl));
+      pb += wave_sum_u64(lane <= first ? (st & kValMask) : 0u);
+      return true;
+    }
+    pb += wave_sum_u64(st & kValMask);
+    top -= 64;
+  }
+  return true;
+}
+
+// Part index of workgroup b: XCD x = b mod 8 takes chunks x, x + 8, x + 16,
+// ... with their parts in order; the chunks past the last full group of 8
+// keep the plain mapping.
+__device__ inline uint32_t single_part_of(uint32_t b, uint32_t nchunks) {
+  const uint32_t grouped = nchunks / kXcds * kXcds * kParts;
+  if (b >= grouped) return b;
+  const uint32_t x = b % kXcds, slot = b / kXcds;
+  return ((slot / kParts) * kXcds + x) * kParts + slot % kParts;
+}
+
+// One part of a chunk, zip3 mode.
+__global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restrict__ x, uint64_t n, uint64_t nchunks,
+                                                         uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
+                                                         Ws ws) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_esc[kPartEscStage];
+  __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
+  __shared__ uint64_t s_begin;
+  __shared__ uint32_t s_before, s_err;
+  const uint32_t tid = threadIdx.x;
+  const uint32_t lane = lane_id();
+  // Workgroups are dealt round-robin over the chip's 8 XCDs; the four parts of
+  // a chunk go to one XCD, one after the other, so that they are dispatched
+  // together and wait on each other only briefly.
+  const uint32_t wg = single_part_of(blockIdx.x, uint32_t(nchunks));
+  const uint64_t c = wg / kParts;
+  const uint32_t h = wg % kParts;
+  const bool last_part = h + 1u == kParts;
+  const uint64_t start = c * kChunk;
+  const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
+  const uint32_t nunits = (nc + 7u) / 8u;
+  const uint32_t pu0 = h * kPartUnits;
+  const uint32_t e0 = ws.ctrl->e0;
+  if (e0 == kBadE0) {  // the same for every workgroup: none waits on another
+    if (tid == 0) ws.err[wg] = uint32_t(CIERA_ERR_ARG);
+    return;
+  }
+
+  // Load the part first: all of a thread's 16-byte loads go out before any is used.
+  Unit v[kUPT];
+  if (8u * (pu0 + kPartUnits) <= nc) {
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) v[j] = load_unit(x, start + 8ull * (pu0 + j * kPartThreads + tid), 8u);
+  } else {
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
+      v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
+      if (u < nunits) v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+    }
+  }
+  const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
+  for (uint32_t i = tid; i < 3u * kStage / 16u; i += kPartThreads)
+    reinterpret_cast<uint4*>(s_planes)[i] = make_uint4(0u, 0u, 0u, 0u);
+  __syncthreads();  // staging cleared
+
+  // Code every unit: plane bytes into LDS (slot = unit), escape masks.
+  uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
+    cnt[j] = 0u;
+    emask[j] = 0u;
+    if (u < nunits) {
+      const uint32_t valid = min(8u, nc - 8u * u);
+      const uint32_t vmask = (valid == 8u) ? 0xFFu : ((1u << valid) - 1u);
+      uint32_t cp[4];
+#pragma unroll
+      for (int i = 0; i < 4; i++) cp[i] = code_pair(exp_pair(v[j].w[i]), bias);
+      const uint32_t p = unit_planes(cp) & (vmask * 0x010101u);
+      const uint32_t at = u - pu0;
+      s_planes[at] = uint8_t(p);
+      s_planes[kStage + at] = uint8_t(p >> 8);
+      s_planes[2u * kStage + at] = uint8_t(p >> 16);
+      emask[j] = ~(p | (p >> 8) | (p >> 16)) & vmask;
+      cnt[j] = __popc(emask[j]);
+    }
+  }
+  const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
+  if (tid == 0) store_relaxed(&ws.pcount[wg], kPartReady | pesc);
+
+  // Stream position (wave 0).
+  if (tid < 64u) {
+    uint32_t err = 0u;
+    // escape counts of the chunk's four parts: lane l < 4 reads part l
+    uint32_t cnt_l = 0u;
+    for (uint32_t spins = 0;; spins++) {
+      const uint32_t w = (lane < kParts) ? load_relaxed(&ws.pcount[c * kParts + lane]) : kPartReady;
+      if (__ballot(!(w & kPartReady)) == 0u) {
+        cnt_l = w & ~kPartReady;
+        break;
+      }
+      if (spins > kSpinLimit) {
+        err = CIERA_ERR_INTERNAL;
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    const uint32_t incl = wave_incl_scan(cnt_l);  // lane l: escapes of parts 0..l
+    const uint32_t before = (h == 0u) ? 0u : uint32_t(__builtin_amdgcn_readlane(int(incl), int(h) - 1));
+    const uint32_t e1 = uint32_t(__builtin_amdgcn_readlane(int(incl), 0));
+    const uint32_t e2 = uint32_t(__builtin_amdgcn_readlane(int(incl), 1));
+    const uint32_t e3 = uint32_t(__builtin_amdgcn_readlane(int(incl), 2));
+    const uint32_t esc_chunk = uint32_t(__builtin_amdgcn_readlane(int(incl), 3));
+    const uint64_t size = pad128(nc) + 3u * pad128(cdiv(nc, 8u)) + pad128(esc_chunk);
+    const uint64_t tbl = table_end(nchunks);
+    uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
+    uint64_t pb = 0;
+    if (last_part && lane == 0u && c > 0u) store_relaxed(&ws.cstat[c], kFlagAgg | size);
+    // every part looks back for the chunk's offset; the last part publishes it
+    if (!err && !chunk_lookback(ws, c, pb)) err = CIERA_ERR_INTERNAL;
+    if (last_part) {
+      if (lane == 0u) {
+        // published even after a failed wait, so that no later wait lasts forever
+        store_relaxed(&ws.cstat[c], kFlagIncl | (pb + size));
+        table[c] = tbl + pb;
+        table[nchunks + 1u + c] = (uint64_t(e1) << 16) | (uint64_t(e2) << 32) | (uint64_t(e3) << 48);
+        if (c + 1u == nchunks) {
+          uint64_t* hd = reinterpret_cast<uint64_t*>(out);
+          table[nchunks] = tbl + pb + size;
+          hd[4] = tbl + pb + size;
+          *out_size = tbl + pb + size;
+        }
+        // the chunk that finishes last writes the escape total
+        const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long*>(&ws.ctrl->done_esc),
+                                       (1ull << kDoneShift) | esc_chunk);
+        if ((old >> kDoneShift) + 1u == nchunks)
+          reinterpret_cast<uint64_t*>(out)[6] = (old & ((1ull << kDoneShift) - 1u)) + esc_chunk;
+      }
+    }
+    if (lane == 0u) {
+      s_begin = tbl + pb;
+      s_before = before;
+      s_err = err;
+    }
+  }
+  __syncthreads();
+  if (s_err) {
+    if (tid == 0) ws.err[wg] = s_err;
+    return;
+  }
+  const uint64_t begin = s_begin;
+  const uint32_t esc_before = s_before;
+  const ChunkGeom g = chunk_geom(begin, nc, false, 0u, 0u);
+  const uint32_t pb = uint32_t(g.plane_bytes);
+  // sign+mantissa bytes
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
+    if (u < nunits) *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
+  }
+  // planes: the part owns bytes [pu0, pu0 + kPartUnits) of each plane, clipped
+  // to the padded plane length
+  const uint32_t own_hi = min(pu0 + kPartUnits, pb);
+  const uint32_t own = own_hi > pu0 ? own_hi - pu0 : 0u;
+  for (uint32_t i = tid; i < 3u * (own / 8u); i += kPartThreads) {
+    const uint32_t b = i / (own / 8u);
+    const uint32_t off = 8u * (i - b * (own / 8u));
+    const uint2 val = *reinterpret_cast<const uint2*>(s_planes + b * kStage + off);
+    *reinterpret_cast<uint2*>(out + g.plane + b * pb + pu0 + off) = val;
+  }
+  // escapes of this part: [esc_before, esc_before + pesc) of the chunk's section
+  const uint64_t esc_at = g.esc + esc_before;
+  if (pesc <= kPartEscStage) {
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) {
+      uint32_t em = emask[j];
+      if (em) {
+        const uint2 e = unit_exponents(v[j]);
+        uint32_t at = base[j];
+        while (em) {
+          const uint32_t k = __builtin_ctz(em);
+          em &= em - 1u;
+          s_esc[at++] = uint8_t(byte_of(e, k));
+        }
+      }
+    }
+    __syncthreads();
+    for (uint32_t i = tid; i < pesc; i += kPartThreads) out[esc_at + i] = s_esc[i];
+  } else {
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) {
+      uint32_t em = emask[j];
+      if (em) {
+        const uint2 e = unit_exponents(v[j]);
+        uint64_t at = esc_at + base[j];
+        while (em) {
+          const uint32_t k = __builtin_ctz(em);
+          em &= em - 1u;
+          out[at++] = uint8_t(byte_of(e, k));
+        }
+      }
+    }
+  }
+  if (last_part) {
+    // zero padding after the sm section's data and after the chunk's escapes
+    const uint32_t esc_chunk = esc_before + pesc;
+    zero_fill(out, g.sm + 8ull * nunits, g.plane, kPartThreads);
+    if (esc_chunk <= kChunk) zero_fill(out, g.esc + esc_chunk, g.esc + pad128(esc_chunk), kPartThreads);
+  }
+  if (tid == 0) ws.err[wg] = 0u;
+}
+
 // ------------------------------------------------------------------ k_decode
 // Escape bytes a decoding part stages in LDS: from the 16-byte boundary at or
 // below its first escape, all of its escapes (at most kPartUnits * 8, after at
@@ -1489,6 +1803,26 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   return launch_status();
 }
 
+ciera_status encode_known_e0_impl(const void* d_x, uint64_t n, const uint8_t* d_e0, void* d_out,
+                                  uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                                  hipStream_t stream) {
+  if (n > kMaxSingleReadN) return CIERA_ERR_ARG;
+  if (!d_e0 || !d_out || !d_ws || !d_out_size || !aligned16(d_out) || !aligned16(d_ws)) return CIERA_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_out_size) & 7u) != 0u) return CIERA_ERR_ARG;
+  if (n > 0 && (!d_x || !aligned16(d_x))) return CIERA_ERR_ARG;
+  if (out_capacity < max_size(n, 0u)) return CIERA_ERR_CAPACITY;
+  const uint64_t nchunks = cdiv(n, kChunk);
+  if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
+  const Ws ws = ws_bind(d_ws, nchunks);
+  const uint16_t* x = static_cast<const uint16_t*>(d_x);
+  uint8_t* out = static_cast<uint8_t*>(d_out);
+  (void)hipGetLastError();
+  launch(k_prep1, dim3(1), dim3(kThreads), stream, n, nchunks, 0u, d_e0, out, d_out_size, ws);
+  if (nchunks) launch(k_write1, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nchunks, out,
+                      d_out_size, ws);
+  return launch_status();
+}
+
 ciera_status decode_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, uint32_t B,
                          uint8_t* d_cache, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
   const bool ciera = B != 0u;
@@ -1563,6 +1897,11 @@ ciera_status ciera_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_
                           uint8_t* d_prev_exp, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
   if (B == 0u) return CIERA_ERR_ARG;
   return decode_impl(d_in, in_size, d_y, n, B, d_prev_exp, d_ws, ws_bytes, stream);
+}
+
+ciera_status zip3_encode_e0(const void* d_x, uint64_t n, const uint8_t* d_e0, void* d_out, uint64_t out_capacity,
+                           void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream) {
+  return encode_known_e0_impl(d_x, n, d_e0, d_out, out_capacity, d_ws, ws_bytes, d_out_size, stream);
 }
 
 ciera_status ciera_read_error(const void* d_ws, hipStream_t stream) {

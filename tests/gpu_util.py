@@ -140,3 +140,39 @@ def check_roundtrip(stream_bytes, x, B=0, cache=None):
     if B:
         assert np.array_equal(c, exps(x)), "receiver cache is not the decoded exponents"
     return c
+
+
+def gpu_encode_e0(x, e0_src, e0_offset=0):
+    """Single-read zip3 encode with the window base read from byte
+    ``e0_offset`` of the uint8 device tensor ``e0_src``.  Returns (stream bytes
+    or None, device status)."""
+    n = x.size
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    cap = ciera.zip3_max_encoded_size(n)
+    buf, out = _guarded_bytes(cap)
+    ws = torch.empty(ciera.zip3_workspace_size(n), dtype=torch.uint8, device="cuda")
+    size = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    ciera.zip3_encode_e0(xd, e0_src, out, ws, size, e0_offset)
+    torch.cuda.synchronize()
+    status = ciera.ciera_read_error(ws)
+    host = buf.cpu().numpy()
+    _check_guards(host, cap, "stream")
+    if status:
+        return None, status
+    sz = int(size.item())
+    assert 0 < sz <= cap
+    assert (host[GUARD + sz:GUARD + cap] == CANARY).all(), "write past the stream's end"
+    return host[GUARD:GUARD + sz].copy(), 0
+
+
+def check_encode_e0(x, e0):
+    """Single-read encode at window base e0 == oracle encode at e0, byte for byte."""
+    src = torch.tensor([e0], dtype=torch.uint8, device="cuda")
+    g, st = gpu_encode_e0(x, src)
+    assert st == 0, f"single-read encode reported status {st}"
+    o, _ = oracle.encode(x, 0, None, e0)
+    if g.tobytes() != o.tobytes():
+        i = _first_diff(g, o)
+        raise AssertionError(f"single-read stream differs from the oracle at byte {i} of {o.size} "
+                             f"(gpu size {g.size}): gpu {g[i:i + 16]} oracle {o[i:i + 16]}")
+    return g

@@ -1,0 +1,81 @@
+"""GPU parity of the single-read encode (window base given in device memory,
+no variance pass): its stream must equal the oracle's at that window base,
+byte for byte, and decode back to the input."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import (check_encode_e0, check_roundtrip, gpu_encode, gpu_encode_e0, require_gpu, say, torch)
+from lossless_bf16_tensor_exp_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+SMALL_N = [0, 1, 7, 8, 9, 63, 64, 65, 1000, 65535, 65536, 65537, 3 * 65536 + 12345, 16384, 16385, 49152 + 3]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("n", SMALL_N)
+def test_single_read_small(n):
+    say(f"single-read n={n}")
+    rng = np.random.default_rng(3000 + n)
+    x = wl.mixed_small(rng, n)
+    for e0 in (oracle.choose_e0(x), 0, 120, 249):
+        s = check_encode_e0(x, e0)
+        check_roundtrip(s, x)
+
+
+def test_single_read_many_chunks():
+    # 300 chunks: the look-back spans several rounds of 64 predecessors
+    rng = np.random.default_rng(31)
+    n = 300 * 65536 - 999
+    x = wl.f32_to_bf16(rng.standard_normal(n, dtype=np.float32) * np.float32(0.01))
+    for e0 in (oracle.choose_e0(x), 110):
+        s = check_encode_e0(x, e0)
+    check_roundtrip(s, x)
+
+
+def test_single_read_window_from_previous_stream():
+    # the window base of iteration t is byte 7 of iteration t-1's stream,
+    # read on the device
+    rng = np.random.default_rng(32)
+    n = 5 * 65536 + 77
+    x0 = wl.f32_to_bf16(rng.standard_normal(n, dtype=np.float32) * np.float32(0.02))
+    x1 = x0.copy()
+    wl.flip(x1, rng.choice(n, size=4000, replace=False))
+    s0, _ = gpu_encode(x0)
+    prev = torch.from_numpy(s0).cuda()
+    g, st = gpu_encode_e0(x1, prev, 7)
+    assert st == 0
+    o, ost = oracle.encode(x1, 0, None, int(s0[7]))
+    assert g.tobytes() == o.tobytes()
+    assert ost["E0"] == int(s0[7])
+    check_roundtrip(g, x1)
+
+
+def test_single_read_rejects_bad_window_base():
+    x = np.arange(70000, dtype=np.uint16)
+    for bad in (250, 255):
+        g, st = gpu_encode_e0(x, torch.tensor([bad], dtype=torch.uint8, device="cuda"))
+        assert g is None and st == 1
+    g, st = gpu_encode_e0(np.zeros(0, np.uint16), torch.tensor([250], dtype=torch.uint8, device="cuda"))
+    assert g is None and st == 1
+
+
+def test_single_read_deterministic():
+    rng = np.random.default_rng(33)
+    x = wl.f32_to_bf16(rng.standard_normal(3_000_000, dtype=np.float32))
+    src = torch.tensor([oracle.choose_e0(x)], dtype=torch.uint8, device="cuda")
+    a, _ = gpu_encode_e0(x, src)
+    b, _ = gpu_encode_e0(x, src)
+    assert a.tobytes() == b.tobytes()
+
+
+def test_single_read_workload2():
+    (g,) = wl.workload2()["iters"]
+    say(f"single-read workload2 n={g.size}")
+    s = check_encode_e0(g, 112)
+    check_roundtrip(s, g)
