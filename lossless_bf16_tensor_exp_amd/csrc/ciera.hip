@@ -1105,10 +1105,10 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
 // from the tensor's sigma; which tensor's sigma is the caller's choice here.
 // k_prep1 writes the header and clears the look-back words.  k_write1 codes
 // one part, publishes its escape count and reads those of its chunk's other
-// parts, so that every part knows the chunk's size.  The chunk's last part
-// publishes that size, and every part looks back over the earlier chunks
-// (decoupled look-back) for the chunk's offset; the last part then publishes
-// the chunk's inclusive prefix.
+// parts, so that every part knows the chunk's size.  Every part then looks
+// back over the earlier chunks (decoupled look-back: a chunk's size follows
+// from its parts' published counts) for the chunk's offset, and the chunk's
+// last part publishes the chunk's inclusive prefix.
 // Every value passed between workgroups sits in the one word that carries its
 // ready flag, so relaxed device-scope atomics suffice (no cache-wide
 // acquire/release).  A part waits only on its own chunk's parts and on
@@ -1116,7 +1116,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
 // dispatched, so every wait ends; each is bounded as well and ends in
 // CIERA_ERR_INTERNAL.
 constexpr uint32_t kPartReady = 1u << 31;
-constexpr uint64_t kFlagAgg = 1ull << 62;
+constexpr uint64_t kFlagSize = 1ull << 62;  // look-back only: a predecessor's size, not a prefix
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kValMask = (1ull << 62) - 1u;
 constexpr uint32_t kSpinLimit = 1u << 22;
@@ -1171,9 +1171,13 @@ __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks
   }
 }
 
-// Stream bytes of the chunks before c (wave 0, 64 predecessors at a time):
-// aggregates are added and the first inclusive prefix ends the search.
+// Stream bytes of the chunks before c (wave 0, 64 predecessors at a time).
+// A predecessor contributes its inclusive prefix if its last part has
+// published one (and the search ends there), else its size, known as soon as
+// its four parts have published their escape counts: every chunk before the
+// last holds 65,536 values, so its fixed sections take kFullFixed bytes.
 // Returns false if a wait did not end.
+constexpr uint64_t kFullFixed = uint64_t(kChunk) + 3u * (kChunk / 8u);
 __device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint64_t& pb) {
   const uint32_t lane = lane_id();
   pb = 0;
@@ -1181,11 +1185,21 @@ __device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint64_t& pb) {
   uint32_t spins = 0;
   while (top >= 0) {
     const int64_t k = top - int64_t(lane);
-    const uint64_t st = (k >= 0) ? load_relaxed(&ws.cstat[k]) : kFlagIncl;
+    uint64_t st = (k >= 0) ? load_relaxed(&ws.cstat[k]) : kFlagIncl;
+    if (k >= 0 && (st & ~kValMask) != kFlagIncl) {
+      uint32_t esc = 0, ready = 1u;
+#pragma unroll
+      for (uint32_t q = 0; q < kParts; q++) {
+        const uint32_t w = load_relaxed(&ws.pcount[uint64_t(k) * kParts + q]);
+        ready &= w >> 31;
+        esc += w & ~kPartReady;
+      }
+      st = ready ? (kFlagSize | (kFullFixed + pad128(esc))) : 0u;
+    }
     const uint64_t flag = st & ~kValMask;
     if (__ballot(flag == 0u) != 0u) {
       if (++spins > kSpinLimit) return false;
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
       continue;
     }
     const uint64_t incl = __ballot(flag == kFlagIncl);
@@ -1308,7 +1322,6 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     const uint64_t tbl = table_end(nchunks);
     uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
     uint64_t pb = 0;
-    if (last_part && lane == 0u && c > 0u) store_relaxed(&ws.cstat[c], kFlagAgg | size);
     // every part looks back for the chunk's offset; the last part publishes it
     if (!err && !chunk_lookback(ws, c, pb)) err = CIERA_ERR_INTERNAL;
     if (last_part) {
