@@ -178,9 +178,9 @@ def main() -> int:
 
     # Pre-bound C calls (argument marshalling done once, outside the timing).
     if mode == "zip3":
-        enc = [ciera.bind("zip3_encode_ex", xs[k], n, out, cap, ws_e, wsz, size, -1, stream=stream) for k in (0, 1)]
+        enc = [ciera.bind("zip3_encode", xs[k], n, out, cap, ws_e, wsz, size, stream=stream) for k in (0, 1)]
     else:
-        enc = [ciera.bind("ciera_encode_ex", xs[k], n, B, send, out, cap, ws_e, wsz, size, -1, stream=stream)
+        enc = [ciera.bind("ciera_encode", xs[k], n, B, send, out, cap, ws_e, wsz, size, stream=stream)
                for k in (0, 1)]
 
     def dec_for(in_size):

@@ -172,13 +172,21 @@ const char* ciera_status_string(ciera_status status);
 /* Same as zip3_encode / ciera_encode with the window base forced to
  * e0_override (0..249); -1 derives it from the standard deviation as the
  * plain entry points do.  For tests that pin the layout at a given window
- * and for callers that reuse the previous iteration's window. */
+ * and for callers that reuse the previous iteration's window.
+ *   plan_groups  0 for the default; otherwise the planning step (which
+ *                reduces the variance sums and lays out the chunk table)
+ *                runs on at most this many workgroups, each taking more
+ *                chunks.  The stream does not depend on it; tests use it to
+ *                reach the long-range paths of the planner with small inputs.
+ *                The window base may differ only where the variance lies
+ *                within rounding of a threshold (the sums' order changes). */
 ciera_status zip3_encode_ex(const void* d_x, uint64_t n, void* d_out, uint64_t out_capacity,
                             void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, int e0_override,
-                            hipStream_t stream);
+                            uint32_t plan_groups, hipStream_t stream);
 ciera_status ciera_encode_ex(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp,
                              void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes,
-                             uint64_t* d_out_size, int e0_override, hipStream_t stream);
+                             uint64_t* d_out_size, int e0_override, uint32_t plan_groups,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

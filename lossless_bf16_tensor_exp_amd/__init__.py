@@ -12,10 +12,10 @@ Same names as the C ABI::
 
     zip3_max_encoded_size(n)              ciera_max_encoded_size(n, B)
     zip3_workspace_size(n)                ciera_workspace_size(n, B)
-    zip3_encode(x, out, ws, out_size, e0_override=-1, stream=None)
+    zip3_encode(x, out, ws, out_size, e0_override=-1, stream=None, plan_groups=0)
     zip3_decode(inp, in_size, y, ws, stream=None)
     zip3_encode_e0(x, e0_src, out, ws, out_size, e0_offset=0, stream=None)
-    ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None)
+    ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None, plan_groups=0)
     ciera_decode(inp, in_size, y, B, prev_exp, ws, stream=None)
     ciera_read_error(ws, stream=None)
     ciera_time_kernels(pairs)             (profiling: per-kernel start/stop events)
@@ -73,11 +73,11 @@ def load_library():
         f.argtypes, f.restype = args, u64
     sigs = {
         "zip3_encode": [vp, u64, vp, u64, vp, u64, vp, vp],
-        "zip3_encode_ex": [vp, u64, vp, u64, vp, u64, vp, i32, vp],
+        "zip3_encode_ex": [vp, u64, vp, u64, vp, u64, vp, i32, u32, vp],
         "zip3_encode_e0": [vp, u64, vp, vp, u64, vp, u64, vp, vp],
         "zip3_decode": [vp, u64, vp, u64, vp, u64, vp],
         "ciera_encode": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
-        "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, vp],
+        "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, u32, vp],
         "ciera_decode": [vp, u64, vp, u64, u32, vp, vp, u64, vp],
         "ciera_read_error": [vp, vp],
         "ciera_time_kernels": [ctypes.POINTER(vp), u32],
@@ -152,14 +152,14 @@ def ciera_status_string(status: int) -> str:
     return load_library().ciera_status_string(status).decode()
 
 
-def zip3_encode(x, out, ws, out_size, e0_override: int = -1, stream=None) -> None:
+def zip3_encode(x, out, ws, out_size, e0_override: int = -1, stream=None, plan_groups: int = 0) -> None:
     lib = load_library()
     _check_values(x, "x")
     _check_bytes(out, "out")
     _check_bytes(ws, "ws")
     _check_size_slot(out_size)
     st = lib.zip3_encode_ex(_ptr(x), x.numel(), _ptr(out), out.numel(), _ptr(ws), ws.numel(),
-                            ctypes.c_void_p(out_size.data_ptr()), e0_override, _stream(stream))
+                            ctypes.c_void_p(out_size.data_ptr()), e0_override, plan_groups, _stream(stream))
     _raise(st, "zip3_encode")
 
 
@@ -187,7 +187,8 @@ def zip3_decode(inp, in_size: int, y, ws, stream=None) -> None:
     _raise(st, "zip3_decode")
 
 
-def ciera_encode(x, B: int, prev_exp, out, ws, out_size, e0_override: int = -1, stream=None) -> None:
+def ciera_encode(x, B: int, prev_exp, out, ws, out_size, e0_override: int = -1, stream=None,
+                 plan_groups: int = 0) -> None:
     lib = load_library()
     _check_values(x, "x")
     _check_bytes(prev_exp, "prev_exp", x.numel())
@@ -195,7 +196,8 @@ def ciera_encode(x, B: int, prev_exp, out, ws, out_size, e0_override: int = -1, 
     _check_bytes(ws, "ws")
     _check_size_slot(out_size)
     st = lib.ciera_encode_ex(_ptr(x), x.numel(), B, _ptr(prev_exp), _ptr(out), out.numel(), _ptr(ws),
-                             ws.numel(), ctypes.c_void_p(out_size.data_ptr()), e0_override, _stream(stream))
+                             ws.numel(), ctypes.c_void_p(out_size.data_ptr()), e0_override, plan_groups,
+                             _stream(stream))
     _raise(st, "ciera_encode")
 
 

@@ -43,8 +43,7 @@
 namespace {
 
 constexpr uint32_t kChunk = 65536u;
-constexpr uint32_t kThreads = 1024u;  // k_plan
-constexpr uint32_t kWaves = kThreads / 64u;
+constexpr uint32_t kThreads = 1024u;  // k_prep1
 constexpr uint32_t kUnitsPerChunk = kChunk / 8u;
 constexpr uint32_t kBitmapWords = 32u;  // 1024 blocks per chunk at B = 64
 constexpr uint64_t kMaxN = 1ull << 40;
@@ -83,6 +82,18 @@ __host__ __device__ inline uint64_t table_end(uint64_t nchunks) {
   return kHeader + pad128(8u * (nchunks + 1u) + 8u * nchunks);
 }
 static_assert(kParts == 4u, "one u64 of four u16 escape counts per chunk");
+// Largest stream bytes of a chunk of nc values (B = 0: zip3): every value
+// escapes and, in ciera mode, every block changed.
+__host__ __device__ inline uint64_t chunk_max_bytes(uint64_t nc, uint32_t B) {
+  uint64_t s = 2u * pad128(nc);  // sign+mantissa and escapes
+  if (B) {
+    const uint64_t nb = cdiv(nc, B);
+    s += pad128(cdiv(nb, 8u)) + 3u * pad128(nb * B / 8u);
+  } else {
+    s += 3u * pad128(cdiv(nc, 8u));
+  }
+  return s;
+}
 
 // Workspace: control block, error words, per-part partial sums and bitmap
 // words, cumulative exponent histograms of the parts, per-part escape offsets
@@ -90,7 +101,7 @@ static_assert(kParts == 4u, "one u64 of four u16 escape counts per chunk");
 // encode.
 struct Ctrl {
   uint32_t e0;
-  uint32_t reserved0;
+  uint32_t plan_fail;  // set by a k_plan workgroup whose wait did not end
   uint64_t n_err_slots;
   uint64_t done_esc;  // single-read encode: chunks finished << 40 | their escapes
   uint64_t reserved[29];
@@ -105,8 +116,27 @@ struct Partial {
   uint32_t pad[2];
 };
 
+// k_plan runs as up to kPlanMaxGroups workgroups, each over a contiguous
+// range of chunks.  A group publishes its variance sums, then (once every
+// group's sums are in) its stream bytes, escapes and changed blocks, each in
+// a word of its slot that k_stats cleared to kSlotEmpty.
+constexpr uint32_t kPlanThreads = 256u;
+constexpr uint32_t kPlanWaves = kPlanThreads / 64u;
+constexpr uint32_t kPlanMaxGroups = kPlanThreads;  // one slot per thread in the waits
+constexpr uint32_t kPlanMinChunks = 16u;           // chunks per group, unless that needs too many groups
+constexpr uint64_t kSlotEmpty = ~0ull;             // a NaN: never the sum of finite values
+constexpr uint64_t kSlotReady = 1ull << 63;        // set in the count words
+
+struct PlanSlot {
+  uint64_t s1, s2;            // FP64 bit patterns of the group's variance sums
+  uint64_t nf;                // kSlotReady | finite values
+  uint64_t bytes, esc, nch;   // kSlotReady | the group's stream bytes, escapes, changed blocks
+  uint64_t pad[2];
+};
+static_assert(sizeof(PlanSlot) == 64, "plan slot is 64 bytes");
+
 struct WsLayout {
-  uint64_t err, partial, bitmap, cum, partesc, chunkesc, pcount, cstat, total;
+  uint64_t err, partial, bitmap, cum, partesc, chunkesc, pcount, cstat, plan, total;
 };
 
 // Cumulative exponent histogram rows: row r (0..256) holds, for every part,
@@ -128,7 +158,8 @@ __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   l.chunkesc = align256(l.partesc + 4u * kParts * slots);
   l.pcount = align256(l.chunkesc + 4u * slots);
   l.cstat = align256(l.pcount + 4u * kParts * slots);
-  l.total = align256(l.cstat + 8u * slots);
+  l.plan = align256(l.cstat + 8u * slots);
+  l.total = align256(l.plan + sizeof(PlanSlot) * kPlanMaxGroups);
   return l;
 }
 
@@ -143,6 +174,7 @@ struct Ws {
   // single-read encode: look-back words
   uint32_t* pcount;     // per part: kPartReady | escapes of the part
   uint64_t* cstat;      // per chunk: flag | stream bytes (aggregate or inclusive prefix)
+  PlanSlot* plan;       // per k_plan workgroup
 };
 
 __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
@@ -158,6 +190,7 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.chunkesc = reinterpret_cast<uint32_t*>(b + l.chunkesc);
   w.pcount = reinterpret_cast<uint32_t*>(b + l.pcount);
   w.cstat = reinterpret_cast<uint64_t*>(b + l.cstat);
+  w.plan = reinterpret_cast<PlanSlot*>(b + l.plan);
   return w;
 }
 
@@ -472,6 +505,12 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   const uint32_t blk0 = kCiera ? ((8u * pu0) >> log2B) : 0u;  // first block of the part
   for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
   if (tid < kPartBitmapWords) s_bits[tid] = 0u;
+  if (blockIdx.x == 0u) {
+    // k_plan's slots: the FP64 words empty, the count words not ready
+    uint64_t* sw = reinterpret_cast<uint64_t*>(ws.plan);
+    for (uint32_t i = tid; i < kPlanMaxGroups * 8u; i += kPartThreads) sw[i] = ((i & 7u) < 2u) ? kSlotEmpty : 0u;
+    if (tid == 0) ws.ctrl->plan_fail = 0u;
+  }
   const uint32_t first = x[0];
   const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
 
@@ -684,76 +723,138 @@ __device__ inline ChunkGeom chunk_geom(uint64_t begin, uint32_t nc, bool ciera, 
   return g;
 }
 
-// Chunk sizes a thread of k_plan keeps in registers (longer runs go through
-// the chunk table).
+// Values passed between workgroups (k_plan's groups, the parts of the
+// single-read encode) each sit in one word that also says whether it is
+// there yet, so relaxed device-scope atomics suffice: no cache-wide
+// acquire/release.  Every wait is bounded.
+constexpr uint32_t kSpinLimit = 1u << 22;
+__device__ inline uint64_t load_relaxed(const uint64_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline uint32_t load_relaxed(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_relaxed(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ inline void store_relaxed(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Waits until ready() holds in every thread of the workgroup; false if the
+// bound ran out first.
+template <typename F>
+__device__ inline bool wait_all(F ready) {
+  for (uint32_t spins = 0;; spins++) {
+    if (__syncthreads_and(ready())) return true;
+    if (spins >= kSpinLimit) return false;
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
+
+__device__ inline uint64_t as_bits(double v) { return uint64_t(__double_as_longlong(v)); }
+__device__ inline double from_bits(uint64_t v) { return __longlong_as_double((long long)v); }
+
+// Sums of the workgroup's u64 values (all threads get the total; the order
+// is fixed, which the FP64 variant below needs to give every group the same
+// bits).
+__device__ inline uint64_t plan_sum_u64(uint64_t v, uint64_t* s_w) {
+  v = wave_sum_u64(v);
+  __syncthreads();
+  if (lane_id() == 0u) s_w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint64_t t = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPlanWaves; w++) t += s_w[w];
+  return t;
+}
+__device__ inline double plan_sum_f64(double v, double* s_w) {
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane_id() == 0u) s_w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = 0.0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPlanWaves; w++) t += s_w[w];
+  return t;
+}
+
+// k_plan thread's chunk sizes over its rounds, kept in registers for ranges
+// up to kRunRegs rounds (longer ones park them in the chunk table).
 constexpr uint32_t kRunRegs = 8u;
 
-// One workgroup plans the stream.  Thread t owns a contiguous run of chunks.
-// (1) The parts' partial sums are reduced in a fixed order (thread runs, then
-// waves in order) and the variance picks E0.  (2) Each chunk's escapes and
-// size follow exactly from the histograms; a workgroup scan over the runs
-// turns sizes into the chunk table (the size exchange of the digest's Figure
-// 1, done on one GPU).  Writes the header, the table, the per-part escape
-// offsets and *out_size.
-__global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks, uint32_t B, int e0_override,
-                                                   uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
-                                                   Ws ws) {
-  __shared__ double s_s1[kWaves], s_s2[kWaves];
-  __shared__ uint64_t s_nf[kWaves], s_nch[kWaves], s_bytes[kWaves], s_esc[kWaves];
+// Up to kPlanMaxGroups workgroups plan the stream; group g takes chunks
+// [g per, (g + 1) per).  (1) Each group sums its parts' variance partials and
+// publishes them; once every group's sums are in, every group reduces them
+// in the same fixed order, so all pick the same E0.  (2) Each group sizes its
+// chunks: a part's escapes are its coded values minus those with exponent in
+// [E0, E0 + 6], read off three cumulative histogram rows, so each chunk's size
+// is exact (the size exchange of the digest's Figure 1, done on one GPU).  A
+// group publishes its bytes, escapes and changed blocks and adds up those of
+// the groups before it for its base offset; the last group also has the
+// totals.  Group 0 writes the header's fixed fields, the last group the
+// totals and *out_size.  Every group is resident at once (at most
+// kPlanMaxGroups small workgroups), so the waits end; if one does not end in
+// its bound, the group sets ctrl->plan_fail and k_write writes nothing.
+__global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchunks, uint64_t per, uint32_t B,
+                                                       int e0_override, uint8_t* __restrict__ out,
+                                                       uint64_t* __restrict__ out_size, Ws ws) {
+  __shared__ double s_f[kPlanWaves];
+  __shared__ uint64_t s_u[kPlanWaves];
   __shared__ uint32_t s_e0;
   const uint32_t tid = threadIdx.x;
-  const uint32_t lane = lane_id(), wave = tid >> 6;
-  const uint64_t per = cdiv(nchunks, kThreads);
-  const uint64_t c0 = min(nchunks, per * tid), c1 = min(nchunks, c0 + per);
+  const uint32_t g = blockIdx.x, G = gridDim.x;
+  const uint64_t c0 = min(nchunks, per * g), c1 = min(nchunks, c0 + per);
   uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
   const uint64_t base = table_end(nchunks);
+  PlanSlot* slot = ws.plan;
+  if (g == 0u) {
+    if (tid == 0) ws.ctrl->n_err_slots = nchunks * kParts;
+    // the padding words after the chunk table and the escape index
+    for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kPlanThreads) table[i] = 0u;
+  }
 
-  // (1) partial sums over the run; the chunks' changed-block counts are kept
-  // for (2), in registers for short runs
+  // (1) the group's variance partials, parts strided over the threads
   double a = 0.0, b = 0.0;
-  uint64_t m = 0, q = 0;
-  uint32_t nchs[kRunRegs];
-#pragma unroll
-  for (uint32_t i = 0; i < kRunRegs; i++) nchs[i] = 0u;
-  for (uint64_t c = c0; c < c1; c++) {
-    const Partial* pp = ws.partial + c * kParts;
-#pragma unroll
-    for (uint32_t h = 0; h < kParts; h++) {
-      a += pp[h].s1;
-      b += pp[h].s2;
-      m += pp[h].nf;
-    }
-    if (B) {
-      const uint32_t nch = chunk_changed_blocks(pp, B);
-      q += nch;
-#pragma unroll
-      for (uint32_t i = 0; i < kRunRegs; i++)
-        if (i == c - c0) nchs[i] = nch;
-    }
+  uint64_t m = 0;
+  for (uint64_t i = kParts * c0 + tid; i < kParts * c1; i += kPlanThreads) {
+    const Partial& p = ws.partial[i];
+    a += p.s1;
+    b += p.s2;
+    m += p.nf;
   }
-  a = wave_sum(a);
-  b = wave_sum(b);
-  m = wave_sum_u64(m);
-  q = wave_sum_u64(q);
-  if (lane == 0u) {
-    s_s1[wave] = a;
-    s_s2[wave] = b;
-    s_nf[wave] = m;
-    s_nch[wave] = q;
-  }
-  // zero the padding words after the chunk table and the escape index
-  for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
-  __syncthreads();
+  a = plan_sum_f64(a, s_f);
+  b = plan_sum_f64(b, s_f);
+  m = plan_sum_u64(m, s_u);
   if (tid == 0) {
-    double s1 = 0.0, s2 = 0.0;
-    uint64_t nf = 0, nch = 0;
-    for (uint32_t w = 0; w < kWaves; w++) {
-      s1 += s_s1[w];
-      s2 += s_s2[w];
-      nf += s_nf[w];
-      nch += s_nch[w];
-    }
+    store_relaxed(&slot[g].s1, as_bits(a));
+    store_relaxed(&slot[g].s2, as_bits(b));
+    store_relaxed(&slot[g].nf, kSlotReady | m);
+  }
+  double ga = 0.0, gb = 0.0;
+  uint64_t gm = 0;
+  const bool sums_in = wait_all([&] {
+    if (tid >= G) return true;
+    const uint64_t w1 = load_relaxed(&slot[tid].s1), w2 = load_relaxed(&slot[tid].s2);
+    const uint64_t w3 = load_relaxed(&slot[tid].nf);
+    ga = from_bits(w1);
+    gb = from_bits(w2);
+    gm = w3 & ~kSlotReady;
+    return w1 != kSlotEmpty && w2 != kSlotEmpty && (w3 & kSlotReady) != 0u;
+  });
+  if (!sums_in) {
+    if (tid == 0) store_relaxed(&ws.ctrl->plan_fail, 1u);
+    return;
+  }
+  if (tid >= G) {
+    ga = gb = 0.0;
+    gm = 0u;
+  }
+  const double s1 = plan_sum_f64(ga, s_f);
+  const double s2 = plan_sum_f64(gb, s_f);
+  const uint64_t nf = plan_sum_u64(gm, s_u);
+  if (tid == 0) {
     double var = 0.0;
     if (nf >= 2u) {
       var = (s2 - s1 * s1 / double(nf)) / double(nf - 1u);
@@ -761,54 +862,39 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
     }
     const uint32_t e0 = (e0_override >= 0) ? uint32_t(e0_override) : window_base(var, nf);
     s_e0 = e0;
-    ws.ctrl->e0 = e0;
-    ws.ctrl->n_err_slots = nchunks * kParts;
-    const uint32_t magic = B ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
-    hd[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(B ? 1u : 0u) << 48) | (uint64_t(e0) << 56);
-    hd[1] = n;
-    hd[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
-    hd[3] = nchunks;
-    hd[5] = nch;
-    for (int i = 7; i < 16; i++) hd[i] = 0u;
+    if (g == 0u) {
+      ws.ctrl->e0 = e0;
+      const uint32_t magic = B ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
+      hd[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(B ? 1u : 0u) << 48) | (uint64_t(e0) << 56);
+      hd[1] = n;
+      hd[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
+      hd[3] = nchunks;
+      for (int i = 7; i < 16; i++) hd[i] = 0u;
+    }
   }
   __syncthreads();
   const uint32_t e0 = s_e0;
 
-  // (2) Sizes of the run's chunks.  A part's escapes are its coded values
-  // minus those whose exponent lies in the window [E0, E0 + 6]: three
-  // cumulative rows, read for the chunk's four parts at once.  A part inside a
-  // block that spans several parts codes its values only if some part of the
-  // block saw a change.
+  // (2) sizes of the group's chunks, one per thread per round of 256.  A part
+  // inside a block that spans several parts codes its values only if some
+  // part of the block saw a change.
   const uint64_t P = nchunks * kParts;
   const uint16_t* row_lo = ws.cum + uint64_t(e0) * P;
   const uint16_t* row_hi = ws.cum + uint64_t(e0 + 7u) * P;
   const uint16_t* row_all = ws.cum + uint64_t(kBins) * P;
   const uint32_t ppb = B > kPartValues ? B / kPartValues : 1u;  // parts per block when blocks span parts
-  uint64_t run_bytes = 0, run_esc = 0;
-  uint64_t sizes[kRunRegs];
-#pragma unroll
-  for (uint32_t i = 0; i < kRunRegs; i++) sizes[i] = 0u;
-  for (uint64_t c = c0; c < c1; c++) {
+  auto chunk_size = [&](uint64_t c, uint64_t& esc_out, uint64_t& nch_out) -> uint64_t {
     const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
     const uint2 lo = *reinterpret_cast<const uint2*>(row_lo + c * kParts);
     const uint2 hi = *reinterpret_cast<const uint2*>(row_hi + c * kParts);
     const uint2 all = *reinterpret_cast<const uint2*>(row_all + c * kParts);
+    const Partial* pp = ws.partial + c * kParts;
     uint32_t nchp[kParts] = {1u, 1u, 1u, 1u};
     if (B > kPartValues) {
-      const Partial* pp = ws.partial + c * kParts;
 #pragma unroll
       for (uint32_t h = 0; h < kParts; h++) nchp[h] = pp[h].nch;
     }
-    uint32_t nch = 0;
-    if (B) {
-      if (per <= kRunRegs) {
-#pragma unroll
-        for (uint32_t i = 0; i < kRunRegs; i++)
-          if (i == c - c0) nch = nchs[i];
-      } else {
-        nch = chunk_changed_blocks(ws.partial + c * kParts, B);
-      }
-    }
+    const uint32_t nch = B ? chunk_changed_blocks(pp, B) : 0u;
     uint32_t esc[kParts], acc = 0;
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) {
@@ -831,48 +917,84 @@ __global__ __launch_bounds__(kThreads) void k_plan(uint64_t n, uint64_t nchunks,
     ws.chunkesc[c] = acc;
     table[nchunks + 1u + c] = uint64_t(esc[0]) | (uint64_t(esc[1]) << 16) | (uint64_t(esc[2]) << 32) |
                               (uint64_t(esc[3]) << 48);
+    esc_out += acc;
+    nch_out += nch;
     const uint64_t planes = B ? uint64_t(nch) * B / 8u : cdiv(nc, 8u);
-    const uint64_t size = pad128(nc) + (B ? 128u : 0u) + 3u * pad128(planes) + pad128(acc);
-    if (per <= kRunRegs) {
+    return pad128(nc) + (B ? 128u : 0u) + 3u * pad128(planes) + pad128(acc);
+  };
+  // one round: the chunk's offset from the group's start; carry = the
+  // group's bytes so far
+  uint64_t carry = 0, g_esc = 0, g_nch = 0;
+  auto round = [&](uint64_t r) -> uint64_t {
+    const uint64_t c = c0 + r * kPlanThreads + tid;
+    const uint64_t size = (c < c1) ? chunk_size(c, g_esc, g_nch) : 0u;
+    const uint64_t incl = wave_incl_scan_u64(size);
+    __syncthreads();
+    if (lane_id() == 63u) s_u[tid >> 6] = incl;
+    __syncthreads();
+    uint64_t before = carry + incl - size, total = 0;
 #pragma unroll
-      for (uint32_t i = 0; i < kRunRegs; i++)
-        if (i == c - c0) sizes[i] = size;
-    } else {
-      table[c] = size;
+    for (uint32_t w = 0; w < kPlanWaves; w++) {
+      before += (w < (tid >> 6)) ? s_u[w] : 0u;
+      total += s_u[w];
     }
-    run_bytes += size;
-    run_esc += acc;
-  }
-  const uint64_t ib = wave_incl_scan_u64(run_bytes), ie = wave_incl_scan_u64(run_esc);
-  if (lane == 63u) {
-    s_bytes[wave] = ib;
-    s_esc[wave] = ie;
-  }
-  __syncthreads();
-  uint64_t before = ib - run_bytes, total_bytes = 0, total_esc = 0;
-  for (uint32_t w = 0; w < kWaves; w++) {
-    if (w < wave) before += s_bytes[w];
-    total_bytes += s_bytes[w];
-    total_esc += s_esc[w];
-  }
-  uint64_t at = base + before;
-  for (uint64_t c = c0; c < c1; c++) {
-    uint64_t size = 0;
-    if (per <= kRunRegs) {
+    carry += total;
+    return before;
+  };
+  const uint64_t rounds = cdiv(c1 - c0, kPlanThreads);
+  uint64_t local[kRunRegs];
+  if (rounds <= kRunRegs) {
 #pragma unroll
-      for (uint32_t i = 0; i < kRunRegs; i++)
-        if (i == c - c0) size = sizes[i];
-    } else {
-      size = table[c];
+    for (uint32_t r = 0; r < kRunRegs; r++) local[r] = (r < rounds) ? round(r) : 0u;
+  } else {
+    for (uint64_t r = 0; r < rounds; r++) {
+      const uint64_t before = round(r);
+      const uint64_t c = c0 + r * kPlanThreads + tid;
+      if (c < c1) table[c] = before;
     }
-    table[c] = at;
-    at += size;
   }
+  const uint64_t own_bytes = carry;
+  const uint64_t own_esc = plan_sum_u64(g_esc, s_u);
+  const uint64_t own_nch = plan_sum_u64(g_nch, s_u);
   if (tid == 0) {
-    const uint64_t total = base + total_bytes;
+    store_relaxed(&slot[g].bytes, kSlotReady | own_bytes);
+    store_relaxed(&slot[g].esc, kSlotReady | own_esc);
+    store_relaxed(&slot[g].nch, kSlotReady | own_nch);
+  }
+  // the groups before this one
+  uint64_t pb = 0, pe = 0, pn = 0;
+  const bool preds_in = wait_all([&] {
+    if (tid >= g) return true;
+    const uint64_t w1 = load_relaxed(&slot[tid].bytes), w2 = load_relaxed(&slot[tid].esc);
+    const uint64_t w3 = load_relaxed(&slot[tid].nch);
+    pb = w1 & ~kSlotReady;
+    pe = w2 & ~kSlotReady;
+    pn = w3 & ~kSlotReady;
+    return (w1 & w2 & w3 & kSlotReady) != 0u;
+  });
+  if (!preds_in) {
+    if (tid == 0) store_relaxed(&ws.ctrl->plan_fail, 1u);
+    return;
+  }
+  if (tid >= g) pb = pe = pn = 0u;
+  const uint64_t at = base + plan_sum_u64(pb, s_u);
+  const uint64_t esc_before = plan_sum_u64(pe, s_u);
+  const uint64_t nch_before = plan_sum_u64(pn, s_u);
+  if (rounds <= kRunRegs) {
+#pragma unroll
+    for (uint32_t r = 0; r < kRunRegs; r++) {
+      const uint64_t c = c0 + uint64_t(r) * kPlanThreads + tid;
+      if (r < rounds && c < c1) table[c] = at + local[r];
+    }
+  } else {
+    for (uint64_t c = c0 + tid; c < c1; c += kPlanThreads) table[c] += at;
+  }
+  if (g + 1u == G && tid == 0) {
+    const uint64_t total = at + own_bytes;
     table[nchunks] = total;
     hd[4] = total;
-    hd[6] = total_esc;
+    hd[5] = nch_before + own_nch;
+    hd[6] = esc_before + own_esc;
     *out_size = total;
   }
 }
@@ -947,7 +1069,8 @@ __device__ inline void stage_bitmap(uint32_t w, uint32_t* s_bits, uint32_t* s_ra
 // nothing: load, code, write.
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restrict__ x, uint64_t n,
-                                                        uint32_t log2B, uint8_t* __restrict__ out, Ws ws) {
+                                                        uint32_t log2B, uint8_t* __restrict__ out,
+                                                        uint64_t capacity, Ws ws) {
   __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_esc[kPartEscStage];
   __shared__ uint32_t s_bits[kBitmapWords];
@@ -982,6 +1105,15 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   const uint32_t esc_chunk = ws.chunkesc[c];
   const uint32_t esc_part = (last_part ? esc_chunk : ws.partesc[c * kParts + h + 1u]) - esc_before;
   const uint32_t e0 = ws.ctrl->e0;
+  // Nothing is written unless the plan is complete and puts the chunk inside
+  // the output buffer.
+  const uint64_t nchunks = cdiv(n, kChunk);
+  if (ws.ctrl->plan_fail != 0u || begin < table_end(nchunks) || (begin & 127u) != 0u ||
+      begin > capacity || capacity - begin < chunk_max_bytes(nc, kCiera ? B : 0u) || esc_chunk > nc ||
+      esc_before > esc_chunk || esc_part > esc_chunk - esc_before) {
+    if (tid == 0) ws.err[wg] = uint32_t(CIERA_ERR_INTERNAL);
+    return;
+  }
   const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
   for (uint32_t i = tid; i < 3u * kStage / 16u; i += kPartThreads)
     reinterpret_cast<uint4*>(s_planes)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -1119,23 +1251,10 @@ constexpr uint32_t kPartReady = 1u << 31;
 constexpr uint64_t kFlagSize = 1ull << 62;  // look-back only: a predecessor's size, not a prefix
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kValMask = (1ull << 62) - 1u;
-constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr uint32_t kBadE0 = ~0u;
 constexpr uint32_t kDoneShift = 40u;           // ctrl->done_esc: chunks << 40 | escapes
 constexpr uint64_t kMaxSingleReadN = 1ull << 39;  // keeps both fields of done_esc in range
 
-__device__ inline uint64_t load_relaxed(const uint64_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline uint32_t load_relaxed(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void store_relaxed(uint64_t* p, uint64_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ inline void store_relaxed(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 
 __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks, uint32_t B,
                                                     const uint8_t* __restrict__ d_e0, uint8_t* __restrict__ out,
@@ -1747,17 +1866,19 @@ uint64_t max_size(uint64_t n, uint32_t B) {
   const uint64_t nchunks = cdiv(n, kChunk);
   const uint64_t full = n / kChunk;
   const uint64_t rem = n % kChunk;
-  auto chunk_max = [B](uint64_t nc) -> uint64_t {
-    uint64_t s = 2u * pad128(nc);  // sign+mantissa and worst-case escapes
-    if (B) {
-      const uint64_t nb = cdiv(nc, B);
-      s += pad128(cdiv(nb, 8u)) + 3u * pad128(nb * B / 8u);
-    } else {
-      s += 3u * pad128(cdiv(nc, 8u));
-    }
-    return s;
-  };
-  return table_end(nchunks) + full * chunk_max(kChunk) + (rem ? chunk_max(rem) : 0u);
+  return table_end(nchunks) + full * chunk_max_bytes(kChunk, B) + (rem ? chunk_max_bytes(rem, B) : 0u);
+}
+
+// k_plan's shape: at least kPlanMinChunks chunks per group unless that takes
+// more than kPlanMaxGroups (or max_groups, if nonzero) groups; no group is
+// empty.
+void plan_shape(uint64_t nchunks, uint32_t max_groups, uint64_t& per, uint32_t& groups) {
+  const uint32_t cap = (max_groups && max_groups < kPlanMaxGroups) ? max_groups : kPlanMaxGroups;
+  uint64_t g = cdiv(nchunks, kPlanMinChunks);
+  if (g < 1u) g = 1u;
+  if (g > cap) g = cap;
+  per = nchunks ? cdiv(nchunks, g) : 1u;
+  groups = nchunks ? uint32_t(cdiv(nchunks, per)) : 1u;
 }
 
 ciera_status launch_status() {
@@ -1783,7 +1904,7 @@ void launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A..
 
 ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cache, void* d_out,
                          uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
-                         int e0_override, hipStream_t stream) {
+                         int e0_override, uint32_t plan_groups, hipStream_t stream) {
   const bool ciera = B != 0u;
   if (n > kMaxN) return CIERA_ERR_ARG;
   if (ciera && !valid_block(B)) return CIERA_ERR_ARG;
@@ -1806,12 +1927,17 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
     else
       launch(k_stats<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
   }
-  launch(k_plan, dim3(1), dim3(kThreads), stream, n, nchunks, B, e0_override, out, d_out_size, ws);
+  uint64_t per = 0;
+  uint32_t groups = 0;
+  plan_shape(nchunks, plan_groups, per, groups);
+  launch(k_plan, dim3(groups), dim3(kPlanThreads), stream, n, nchunks, per, B, e0_override, out, d_out_size, ws);
   if (nchunks) {
     if (ciera)
-      launch(k_write<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, lb, out, ws);
+      launch(k_write<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, lb, out,
+             out_capacity, ws);
     else
-      launch(k_write<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, 0u, out, ws);
+      launch(k_write<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, 0u, out,
+             out_capacity, ws);
   }
   return launch_status();
 }
@@ -1878,12 +2004,14 @@ uint64_t ciera_workspace_size(uint64_t n, uint32_t B) {
 
 ciera_status zip3_encode(const void* d_x, uint64_t n, void* d_out, uint64_t out_capacity, void* d_ws,
                          uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream) {
-  return encode_impl(d_x, n, 0u, nullptr, d_out, out_capacity, d_ws, ws_bytes, d_out_size, -1, stream);
+  return encode_impl(d_x, n, 0u, nullptr, d_out, out_capacity, d_ws, ws_bytes, d_out_size, -1, 0u, stream);
 }
 
 ciera_status zip3_encode_ex(const void* d_x, uint64_t n, void* d_out, uint64_t out_capacity, void* d_ws,
-                            uint64_t ws_bytes, uint64_t* d_out_size, int e0_override, hipStream_t stream) {
-  return encode_impl(d_x, n, 0u, nullptr, d_out, out_capacity, d_ws, ws_bytes, d_out_size, e0_override, stream);
+                            uint64_t ws_bytes, uint64_t* d_out_size, int e0_override, uint32_t plan_groups,
+                            hipStream_t stream) {
+  return encode_impl(d_x, n, 0u, nullptr, d_out, out_capacity, d_ws, ws_bytes, d_out_size, e0_override,
+                     plan_groups, stream);
 }
 
 ciera_status zip3_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, void* d_ws,
@@ -1895,15 +2023,15 @@ ciera_status ciera_encode(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_pr
                           uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
                           hipStream_t stream) {
   if (B == 0u) return CIERA_ERR_ARG;
-  return encode_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, d_ws, ws_bytes, d_out_size, -1, stream);
+  return encode_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, d_ws, ws_bytes, d_out_size, -1, 0u, stream);
 }
 
 ciera_status ciera_encode_ex(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, void* d_out,
                              uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
-                             int e0_override, hipStream_t stream) {
+                             int e0_override, uint32_t plan_groups, hipStream_t stream) {
   if (B == 0u) return CIERA_ERR_ARG;
   return encode_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, d_ws, ws_bytes, d_out_size, e0_override,
-                     stream);
+                     plan_groups, stream);
 }
 
 ciera_status ciera_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, uint32_t B,

@@ -41,7 +41,7 @@ def exps(x):
     return ((x >> 7) & 0xFF).astype(np.uint8)
 
 
-def gpu_encode(x, B=0, cache=None, e0=-1, stream=None):
+def gpu_encode(x, B=0, cache=None, e0=-1, stream=None, plan_groups=0):
     """Encode uint16 array x on the GPU.  Returns (stream bytes, cache after)."""
     n = x.size
     xd = torch.from_numpy(x.view(np.int16)).cuda()
@@ -54,9 +54,9 @@ def gpu_encode(x, B=0, cache=None, e0=-1, stream=None):
     if B:
         cbuf, cd = _guarded_bytes(n)
         cd.copy_(torch.from_numpy(cache))
-        ciera.ciera_encode(xd, B, cd, out, ws, size, e0, stream)
+        ciera.ciera_encode(xd, B, cd, out, ws, size, e0, stream, plan_groups)
     else:
-        ciera.zip3_encode(xd, out, ws, size, e0, stream)
+        ciera.zip3_encode(xd, out, ws, size, e0, stream, plan_groups)
     torch.cuda.synchronize()
     assert ciera.ciera_read_error(ws) == 0
     sz = int(size.item())
@@ -105,12 +105,12 @@ def _first_diff(a, b):
     return int(d[0]) if d.size else m
 
 
-def check_encode(x, B=0, cache=None, e0=-1, stream=None):
+def check_encode(x, B=0, cache=None, e0=-1, stream=None, plan_groups=0):
     """GPU encode == oracle encode, byte for byte (and caches).  Where the
     window base differs, both choices must straddle a threshold within the
     FP64 summation error, and the rest must equal the oracle run at the GPU's
     window base.  Returns (stream, oracle stats)."""
-    g_stream, g_cache = gpu_encode(x, B, cache, e0, stream)
+    g_stream, g_cache = gpu_encode(x, B, cache, e0, stream, plan_groups)
     o_cache = cache.copy() if B else None
     o_stream, o_st = oracle.encode(x, B, o_cache, e0)
     if g_stream.tobytes() != o_stream.tobytes() and e0 < 0 and int(g_stream[7]) != o_st["E0"]:

@@ -66,7 +66,7 @@ def test_argument_errors_return_before_any_launch(lib):
     assert lib.zip3_encode(p, 10, p, 1 << 20, p, 10, p, None) == 3
     assert lib.ciera_encode(p, 10, 100, p, p, 1 << 20, p, 1 << 20, p, None) == 1
     assert lib.ciera_encode(p, 10, 0, p, p, 1 << 20, p, 1 << 20, p, None) == 1
-    assert lib.zip3_encode_ex(p, 10, p, 1 << 20, p, 1 << 20, p, 250, None) == 1
+    assert lib.zip3_encode_ex(p, 10, p, 1 << 20, p, 1 << 20, p, 250, 0, None) == 1
     assert lib.ciera_decode(p, 1 << 20, p, 10, 96, p, p, 1 << 20, None) == 1
     assert lib.zip3_decode(ctypes.c_void_p(16 * 1024 + 8), 1 << 20, p, 10, p, 1 << 20, None) == 1
     assert lib.ciera_read_error(None, None) == 1
