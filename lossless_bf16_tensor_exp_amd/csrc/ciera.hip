@@ -8,13 +8,14 @@
 //             against the sender's exponent cache and the cache update (CIERA
 //             page, section 3.1); and an exponent histogram of the values to
 //             be coded.
-//   k_plan    one workgroup: reduces the partial sums in a fixed order and
-//             picks the window base E0 (integer nearest x_opt = log2 sigma +
-//             0.5 log2(14 ln2 / 16383), digest section 3.1, evaluated as
-//             var >= K0 4^k); each part's escape count is its number of coded
-//             values outside [E0, E0+6], read off the histogram, so chunk
-//             sizes follow exactly and a scan turns them into the chunk table
-//             (the size exchange of the digest's Figure 1, done on one GPU).
+//   k_plan    up to 256 workgroups over ranges of chunks: reduce the partial
+//             sums in a fixed order and pick the window base E0 (integer
+//             nearest x_opt = log2 sigma + 0.5 log2(14 ln2 / 16383), digest
+//             section 3.1, evaluated as var >= K0 4^k); each part's escape
+//             count is its number of coded values outside [E0, E0+6], read
+//             off the histogram, so chunk sizes follow exactly and a scan
+//             turns them into the chunk table (the size exchange of the
+//             digest's Figure 1, done on one GPU).
 //   k_write   one workgroup per part, no synchronisation with any other:
 //             splits values into sign+mantissa bytes and 3-bit codes and
 //             writes the 128-byte-aligned sections at offsets k_plan fixed
@@ -96,7 +97,7 @@ __host__ __device__ inline uint64_t chunk_max_bytes(uint64_t nc, uint32_t B) {
 }
 
 // Workspace: control block, error words, per-part partial sums and bitmap
-// words, cumulative exponent histograms of the parts, per-part escape offsets
+// words, exponent histograms of the parts, per-part escape offsets
 // and per-chunk escape totals, and the look-back words of the single-read
 // encode.
 struct Ctrl {
@@ -113,7 +114,8 @@ struct Partial {
   double s2;
   uint32_t nf;
   uint32_t nch;
-  uint32_t pad[2];
+  uint32_t coded;  // values the part codes (all of them in zip3 mode)
+  uint32_t pad;
 };
 
 // k_plan runs as up to kPlanMaxGroups workgroups, each over a contiguous
@@ -136,14 +138,12 @@ struct PlanSlot {
 static_assert(sizeof(PlanSlot) == 64, "plan slot is 64 bytes");
 
 struct WsLayout {
-  uint64_t err, partial, bitmap, cum, partesc, chunkesc, pcount, cstat, plan, total;
+  uint64_t err, partial, bitmap, hist, partesc, chunkesc, pcount, cstat, plan, total;
 };
 
-// Cumulative exponent histogram rows: row r (0..256) holds, for every part,
-// the number of its coded values with exponent below r, as u16; row 256 is
-// the part's coded-value count.  Stored row-major (row r: parts 0..P-1), so
-// that the rows k_plan reads for one window base are contiguous over parts.
-constexpr uint32_t kCumRows = kBins + 1u;
+// Exponent histograms: per part one row of kBins u16 counts (a part holds at
+// most 16384 values) of its coded values by exponent field, rows in part
+// order, so that each part writes whole 128-byte lines.
 
 __host__ __device__ inline uint64_t align256(uint64_t v) { return (v + 255u) & ~uint64_t(255); }
 
@@ -153,8 +153,8 @@ __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   l.err = sizeof(Ctrl);
   l.partial = align256(l.err + 4u * kParts * slots);
   l.bitmap = align256(l.partial + sizeof(Partial) * kParts * slots);
-  l.cum = align256(l.bitmap + 4u * kBitmapWords * slots);
-  l.partesc = align256(l.cum + 2u * kCumRows * kParts * slots);
+  l.hist = align256(l.bitmap + 4u * kBitmapWords * slots);
+  l.partesc = align256(l.hist + 2u * kBins * kParts * slots);
   l.chunkesc = align256(l.partesc + 4u * kParts * slots);
   l.pcount = align256(l.chunkesc + 4u * slots);
   l.cstat = align256(l.pcount + 4u * kParts * slots);
@@ -168,7 +168,7 @@ struct Ws {
   uint32_t* err;        // one word per workgroup of k_write / k_decode
   Partial* partial;     // per part
   uint32_t* bitmap;     // kPartBitmapWords per part
-  uint16_t* cum;        // kCumRows rows of (kParts * nchunks) u16
+  uint16_t* hist;       // kBins u16 per part
   uint32_t* partesc;    // escapes before each part within its chunk
   uint32_t* chunkesc;   // escapes per chunk
   // single-read encode: look-back words
@@ -185,7 +185,7 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.err = reinterpret_cast<uint32_t*>(b + l.err);
   w.partial = reinterpret_cast<Partial*>(b + l.partial);
   w.bitmap = reinterpret_cast<uint32_t*>(b + l.bitmap);
-  w.cum = reinterpret_cast<uint16_t*>(b + l.cum);
+  w.hist = reinterpret_cast<uint16_t*>(b + l.hist);
   w.partesc = reinterpret_cast<uint32_t*>(b + l.partesc);
   w.chunkesc = reinterpret_cast<uint32_t*>(b + l.chunkesc);
   w.pcount = reinterpret_cast<uint32_t*>(b + l.pcount);
@@ -470,10 +470,10 @@ __device__ inline uint32_t chunk_bitmap_word(const uint32_t* pw, uint32_t t, uin
 }
 
 // Workgroups are dealt round-robin over the chip's 8 XCDs, each with its own
-// L2.  k_stats gives XCD x a contiguous range of parts, so that the 64 parts
-// whose u16 entries share a 128-byte line of a cumulative-histogram row are
-// written from one L2 (else every XCD writes the line back).  The last
-// (parts mod 8) workgroups keep their own index.
+// L2.  k_stats gives XCD x a contiguous range of parts, so that the small
+// per-part records (partial sums, bitmap words) that share a 128-byte line
+// are written from one L2.  The last (parts mod 8) workgroups keep their own
+// index.
 constexpr uint32_t kXcds = 8u;
 __device__ inline uint32_t stats_part_of(uint32_t b, uint32_t parts) {
   const uint32_t per = parts / kXcds;
@@ -484,7 +484,7 @@ __device__ inline uint32_t stats_part_of(uint32_t b, uint32_t parts) {
 // One 256-thread workgroup per part (quarter chunk), units pu0 + 256 j + t.
 // Per part: FP64 variance partials; ciera: changed-block bits against the
 // sender cache and the cache update; an exponent histogram of the values to
-// code; the coded-value count.
+// code, and their count.
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
                                                         uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
@@ -493,6 +493,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   __shared__ double s_s1[kPartWaves], s_s2[kPartWaves];
   __shared__ uint32_t s_nf[kPartWaves], s_wtot[kPartWaves];
   const uint32_t tid = threadIdx.x;
+  const uint32_t lane = lane_id(), wave = tid >> 6;
   const uint32_t wg = stats_part_of(blockIdx.x, gridDim.x);  // the part this workgroup takes
   const uint64_t c = wg / kParts;
   const uint32_t h = wg % kParts;
@@ -542,13 +543,20 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   // Variance sums with no finite test per value: a non-finite input makes the
   // thread's sums non-finite (squares of finite BF16 values cannot overflow
   // FP64), and the thread then redoes its units on the checked path.  Ciera:
-  // compare exponents with the cache, rewrite the bytes that differ, mark the
-  // block changed.
+  // compare exponents with the cache and rewrite the bytes that differ; a
+  // wave ballot gives the changed blocks among the wave's 64 units (lanes
+  // [kL, kL + L) hold block k for L = B / 8 up to 64; from B = 512 on the 64
+  // units lie in one block), set in s_bits by one atomic per wave.  Bit j of
+  // `coded` says unit j's values are coded.
   double s1 = 0.0, s2 = 0.0;
   uint32_t nf = 0;
+  uint32_t coded = kCiera ? 0u : 0xFFu;
+  const uint32_t L = (B >= 512u) ? 64u : B / 8u;
+  const uint64_t gmask = (L >= 64u) ? ~0ull : ((1ull << L) - 1u);
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
     const uint32_t u = pu0 + j * kPartThreads + tid;
+    bool diff = false;
     if (full || u < nunits) {
       const uint32_t cnt = full ? 8u : min(8u, nc - 8u * u);
       if (cnt == 8u) {
@@ -568,12 +576,22 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       if (kCiera) {
         const uint2 e = unit_exponents(v[j]);
         const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
-        const uint64_t diff = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
-        if (diff) {
+        const uint64_t d = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
+        if (d) {
           store_bytes8(cache + start + 8ull * u, cnt, e);
-          const uint32_t lb = ((8u * u) >> log2B) - blk0;
-          atomicOr(&s_bits[lb >> 5], 1u << (lb & 31u));
+          diff = true;
         }
+      }
+    }
+    if (kCiera) {
+      const uint64_t m = __ballot(diff);
+      if (m != 0u) {
+        // first block of the wave's units, relative to the part
+        const uint32_t lbw = ((8u * (pu0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
+        uint32_t bits = 0;
+        for (uint32_t k = 0; k < 64u / L; k++) bits |= ((m >> (k * L)) & gmask) ? (1u << k) : 0u;
+        if (lane == 0u) atomicOr(&s_bits[lbw >> 5], bits << (lbw & 31u));
+        if (B <= 512u) coded |= ((m >> (lane & ~(L - 1u))) & gmask) ? (1u << j) : 0u;
       }
     }
   }
@@ -587,28 +605,37 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       if (u < nunits) stats_checked(v[j], min(8u, nc - 8u * u), shift, s1, s2, nf);
     }
   }
-  if (kCiera) __syncthreads();  // the part's block bits are complete
+  if (kCiera && B > 512u) {
+    // a block spans several waves: its bit is complete after the barrier.  A
+    // part inside a block that spans several parts counts all of its values
+    // (k_plan drops them if the block is unchanged).
+    __syncthreads();
+    if (B > kPartValues) {
+      coded = 0xFFu;
+    } else {
+      const uint32_t w0 = s_bits[0];  // at most 16 blocks per part
+#pragma unroll
+      for (uint32_t j = 0; j < kUPT; j++) {
+        const uint32_t lb = ((8u * (pu0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
+        coded |= ((w0 >> lb) & 1u) << j;
+      }
+    }
+  }
 
-  // Exponent histogram of the values to code: all values (zip3); ciera, those
-  // of the part's changed blocks, or all of the part's values when its block
-  // spans several parts (k_plan drops them if the block is unchanged).
-  // Word bin * kHistCopies + copy, copy chosen by lane: equal exponents
-  // within a wave spread over kHistCopies consecutive words (LDS banks).
+  // Exponent histogram of the coded values.  Word bin * kHistCopies + copy,
+  // copy chosen by lane: equal exponents within a wave spread over
+  // kHistCopies consecutive words (LDS banks).
   const uint32_t copy4 = 4u * (tid & (kHistCopies - 1u));
   if (full) {
     // every unit holds 8 values: the bin's byte offset comes straight from
-    // the exponent bits of each half; ciera skips units of unchanged blocks
-    // (a part inside a larger block counts all of its values)
+    // the exponent bits of each half
     constexpr uint32_t kBinShift = 6u;  // log2(kHistCopies * 4)
     static_assert((1u << kBinShift) == kHistCopies * 4u, "kBinShift");
     constexpr uint32_t kBinMask = 0xFFu << kBinShift;
     uint8_t* hb = reinterpret_cast<uint8_t*>(s_hist);
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) {
-      if (kCiera && B <= kPartValues) {
-        const uint32_t lb = ((8u * (pu0 + j * kPartThreads + tid)) >> log2B) - blk0;
-        if (!((s_bits[lb >> 5] >> (lb & 31u)) & 1u)) continue;
-      }
+      if (!((coded >> j) & 1u)) continue;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
         const uint32_t w = v[j].w[i];
@@ -620,11 +647,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) {
       const uint32_t u = pu0 + j * kPartThreads + tid;
-      if (u >= nunits) continue;
-      if (kCiera && B <= kPartValues) {
-        const uint32_t lb = ((8u * u) >> log2B) - blk0;
-        if (!((s_bits[lb >> 5] >> (lb & 31u)) & 1u)) continue;
-      }
+      if (u >= nunits || !((coded >> j) & 1u)) continue;
       const uint32_t cnt = min(8u, nc - 8u * u);
       const uint2 e = unit_exponents(v[j]);
       uint32_t* hist = s_hist + copy4 / 4u;
@@ -636,38 +659,33 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   s1 = wave_sum(s1);
   s2 = wave_sum(s2);
   nf = wave_sum_u32(nf);
-  if (lane_id() == 0u) {
-    s_s1[tid >> 6] = s1;
-    s_s2[tid >> 6] = s2;
-    s_nf[tid >> 6] = nf;
+  if (lane == 0u) {
+    s_s1[wave] = s1;
+    s_s2[wave] = s2;
+    s_nf[wave] = nf;
   }
   __syncthreads();
-  // One bin per thread: sum the copies; the part's column of the cumulative
-  // rows gets the count below each bin and, in row 256, its coded-value total
-  // (u16: a part holds at most 16384 values).
+  // One bin per thread: sum the copies and store the part's row (u16: a
+  // part holds at most 16384 values); the bins add up to the coded count.
   {
     uint32_t sum = 0;
 #pragma unroll
-    for (uint32_t q = 0; q < kHistCopies; q++) sum += s_hist[tid * kHistCopies + q];
-    const uint32_t incl = wave_incl_scan(sum);
-    if (lane_id() == 63u) s_wtot[tid >> 6] = incl;
-    __syncthreads();
-    uint32_t below = incl - sum;
-#pragma unroll
-    for (uint32_t w = 0; w < kPartWaves; w++) below += (w < (tid >> 6)) ? s_wtot[w] : 0u;
-    const uint64_t P = cdiv(n, kChunk) * kParts;
-    ws.cum[uint64_t(tid) * P + wg] = uint16_t(below);
-    if (tid == kBins - 1u) ws.cum[uint64_t(kBins) * P + wg] = uint16_t(below + sum);
+    for (uint32_t q = 0; q < kHistCopies; q++) sum += s_hist[tid * kHistCopies + ((q + tid) & (kHistCopies - 1u))];
+    ws.hist[uint64_t(wg) * kBins + tid] = uint16_t(sum);
+    sum = wave_sum_u32(sum);
+    if (lane == 0u) s_wtot[wave] = sum;
   }
   if (kCiera && tid < kPartBitmapWords) ws.bitmap[(c * kParts + h) * kPartBitmapWords + tid] = s_bits[tid];
+  __syncthreads();
   if (tid == 0) {
     double a = 0.0, b = 0.0;
-    uint32_t m = 0;
+    uint32_t m = 0, t = 0;
 #pragma unroll
     for (uint32_t w = 0; w < kPartWaves; w++) {
       a += s_s1[w];
       b += s_s2[w];
       m += s_nf[w];
+      t += s_wtot[w];
     }
     uint32_t nch = 0;
     if (kCiera) {
@@ -683,7 +701,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     p.s2 = b;
     p.nf = m;
     p.nch = nch;
-    p.pad[0] = p.pad[1] = 0u;
+    p.coded = t;
+    p.pad = 0u;
     ws.partial[c * kParts + h] = p;
   }
 }
@@ -788,7 +807,7 @@ constexpr uint32_t kRunRegs = 8u;
 // publishes them; once every group's sums are in, every group reduces them
 // in the same fixed order, so all pick the same E0.  (2) Each group sizes its
 // chunks: a part's escapes are its coded values minus those with exponent in
-// [E0, E0 + 6], read off three cumulative histogram rows, so each chunk's size
+// [E0, E0 + 6], read off its histogram row, so each chunk's size
 // is exact (the size exchange of the digest's Figure 1, done on one GPU).  A
 // group publishes its bytes, escapes and changed blocks and adds up those of
 // the groups before it for its base offset; the last group also has the
@@ -878,17 +897,19 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
   // (2) sizes of the group's chunks, one per thread per round of 256.  A part
   // inside a block that spans several parts codes its values only if some
   // part of the block saw a change.
-  const uint64_t P = nchunks * kParts;
-  const uint16_t* row_lo = ws.cum + uint64_t(e0) * P;
-  const uint16_t* row_hi = ws.cum + uint64_t(e0 + 7u) * P;
-  const uint16_t* row_all = ws.cum + uint64_t(kBins) * P;
   const uint32_t ppb = B > kPartValues ? B / kPartValues : 1u;  // parts per block when blocks span parts
   auto chunk_size = [&](uint64_t c, uint64_t& esc_out, uint64_t& nch_out) -> uint64_t {
     const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
-    const uint2 lo = *reinterpret_cast<const uint2*>(row_lo + c * kParts);
-    const uint2 hi = *reinterpret_cast<const uint2*>(row_hi + c * kParts);
-    const uint2 all = *reinterpret_cast<const uint2*>(row_all + c * kParts);
     const Partial* pp = ws.partial + c * kParts;
+    uint32_t inwin[kParts];  // coded values with exponent in [E0, E0 + 6], per part
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      const uint16_t* row = ws.hist + (c * kParts + h) * kBins + e0;  // e0 + 6 <= 255
+      uint32_t w = 0;
+#pragma unroll
+      for (uint32_t k = 0; k < 7u; k++) w += row[k];
+      inwin[h] = w;
+    }
     uint32_t nchp[kParts] = {1u, 1u, 1u, 1u};
     if (B > kPartValues) {
 #pragma unroll
@@ -898,10 +919,6 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
     uint32_t esc[kParts], acc = 0;
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) {
-      const uint32_t sh = 16u * (h & 1u);
-      const uint32_t l = (((h < 2u) ? lo.x : lo.y) >> sh) & 0xFFFFu;
-      const uint32_t u = (((h < 2u) ? hi.x : hi.y) >> sh) & 0xFFFFu;
-      const uint32_t t = (((h < 2u) ? all.x : all.y) >> sh) & 0xFFFFu;
       bool codes = true;
       if (B > kPartValues) {
         uint32_t any = 0;
@@ -910,7 +927,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
         codes = any != 0u;
       }
       esc[h] = acc;
-      acc += codes ? t - (u - l) : 0u;
+      acc += codes ? pp[h].coded - inwin[h] : 0u;
     }
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) ws.partesc[c * kParts + h] = esc[h];
