@@ -898,17 +898,26 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
   // inside a block that spans several parts codes its values only if some
   // part of the block saw a change.
   const uint32_t ppb = B > kPartValues ? B / kPartValues : 1u;  // parts per block when blocks span parts
+  const uint32_t r0 = e0 & 7u;
   auto chunk_size = [&](uint64_t c, uint64_t& esc_out, uint64_t& nch_out) -> uint64_t {
     const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
     const Partial* pp = ws.partial + c * kParts;
-    uint32_t inwin[kParts];  // coded values with exponent in [E0, E0 + 6], per part
+    // Coded values with exponent in [E0, E0 + 6], per part: bins E0..E0+6
+    // lie in the two 16-byte words q = E0 / 8 and q + 1 of the part's row
+    // (q + 1 <= 31 since E0 <= 249), at u16 positions r .. r + 6, r = E0 mod 8.
+    uint32_t inwin[kParts];
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) {
-      const uint16_t* row = ws.hist + (c * kParts + h) * kBins + e0;  // e0 + 6 <= 255
-      uint32_t w = 0;
+      const uint4* row = reinterpret_cast<const uint4*>(ws.hist + (c * kParts + h) * kBins) + (e0 >> 3);
+      const uint4 a = row[0], b = row[1];
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      uint32_t sum = 0;
 #pragma unroll
-      for (uint32_t k = 0; k < 7u; k++) w += row[k];
-      inwin[h] = w;
+      for (uint32_t i = 0; i < 16u; i++) {
+        const uint32_t cnt = (w[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
+        sum += (i - r0 < 7u) ? cnt : 0u;  // r0 <= i <= r0 + 6
+      }
+      inwin[h] = sum;
     }
     uint32_t nchp[kParts] = {1u, 1u, 1u, 1u};
     if (B > kPartValues) {
