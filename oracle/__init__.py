@@ -11,7 +11,8 @@ Parity pins (see the tests under ``tests/``): exhaustive round trips over all
 97.5 % window share, the optimum u = 0.0172 and x_opt = log2(sigma) - 5.36
 (ZipCCL research digest, section 3.1), the block reuse law (1-c)^B (CIERA
 page, section 2), the closed-form stream size, exact-rational variance on
-small inputs, and a second, independent pure-Python encoder.  The byte layout
+small inputs, a second, independent pure-Python encoder, and, for the block
+hash of the hash sender, SplitMix64's published output sequence.  The byte layout
 itself is a reading of the pages (they print no encoded bytes); it is pinned
 by the size identity and by that second implementation only.
 """
@@ -72,6 +73,10 @@ def _load():
     lib.orc_encode.restype = i32
     lib.orc_decode.argtypes = [vp, u64, vp, u64, u32, vp]
     lib.orc_decode.restype = i32
+    lib.orc_splitmix64_next.argtypes = [ctypes.POINTER(u64)]
+    lib.orc_splitmix64_next.restype = u64
+    lib.orc_block_hashes.argtypes = [vp, u64, u32, vp]
+    lib.orc_block_hashes.restype = None
     _lib = lib
     return lib
 
@@ -146,6 +151,22 @@ def decode(stream, n: int, B: int = 0, cache: np.ndarray | None = None) -> np.nd
     if st != OK:
         raise OracleError(st, "decode")
     return y
+
+
+def splitmix64(seed: int, count: int) -> list[int]:
+    """The first ``count`` outputs of a SplitMix64 generator seeded with ``seed``."""
+    st = ctypes.c_uint64(seed)
+    return [int(_load().orc_splitmix64_next(ctypes.byref(st))) for _ in range(count)]
+
+
+def block_hashes(x, B: int) -> np.ndarray:
+    """The two 64-bit hashes of every block of B values of ``x``'s exponent
+    fields: a uint64 array of shape (ceil(len(x) / B), 2)."""
+    x = _u16(x)
+    nb = -(-x.size // B)
+    out = np.zeros((nb, 2), dtype=np.uint64)
+    _load().orc_block_hashes(_ptr(x), x.size, B, _ptr(out))
+    return out
 
 
 def zip3_encode(x, e0_override: int = -1):

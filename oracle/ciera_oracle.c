@@ -38,6 +38,20 @@
  *    (payload S_{s+m} + S_bm + q S_e).  The cache here holds the exponents
  *    themselves, compared exactly, in place of the page's per-block hash.
  *
+ *  - Block hash (the page's sender state, section 3.1: a 128-bit hash per
+ *    block made of two independent 64-bit SplitMix64 hashes; a block counts
+ *    as unchanged only when its hash equals the stored one).  The page does
+ *    not say how a block's bytes enter SplitMix64.  Here: the block's
+ *    exponent fields, 8 at a time, form little-endian 64-bit words w_k (the
+ *    last word of a short block filled with zeros); hash h is the sum mod
+ *    2^64, over the words that are not zero, of mix(w_k + s_h + (k+1) g_h),
+ *    where mix is SplitMix64's output function, i.e. the (k+1)-th output of
+ *    a SplitMix64 generator with seed w_k + s_h and increment g_h.  Hash 0
+ *    uses seed 0 and SplitMix64's own increment; hash 1 its own seed and odd
+ *    increment.  An all-zero block hashes to (0, 0), so an all-zero hash
+ *    cache stands for all-zero previous exponents, as an all-zero exponent
+ *    cache does.
+ *
  *  - Packing.  The stream is cut into chunks of 65,536 input values; each
  *    chunk is written as a self-contained segment whose sections start on
  *    128-byte boundaries, and the three code bits go to three 1-bit arrays.
@@ -193,6 +207,46 @@ int orc_choose_e0(const uint16_t* x, uint64_t n) {
   uint64_t nf;
   orc_variance(x, n, &var, &nf);
   return orc_window_base(var, nf);
+}
+
+/* SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+ * generators", OOPSLA 2014): the state advances by an odd increment and each
+ * output is the new state through a fixed mixing function (two xor-shift
+ * multiply rounds and a final xor-shift). */
+#define ORC_SM64_GAMMA 0x9E3779B97F4A7C15ull
+
+static uint64_t sm64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+uint64_t orc_splitmix64_next(uint64_t* state) {
+  *state += ORC_SM64_GAMMA;
+  return sm64_mix(*state);
+}
+
+/* The block hashes (two u64 per block, block b at out[2b], out[2b+1]) of
+ * x's exponent fields: see "Block hash" at the top of this file. */
+static const uint64_t ORC_HASH_SEED[2] = {0ull, 0x243F6A8885A308D3ull};
+static const uint64_t ORC_HASH_GAMMA[2] = {ORC_SM64_GAMMA, 0xD1B54A32D192ED03ull};
+
+void orc_block_hashes(const uint16_t* x, uint64_t n, uint32_t B, uint64_t* out) {
+  uint64_t nb = ceil_div(n, B);
+  for (uint64_t b = 0; b < nb; b++) {
+    uint64_t begin = b * B;
+    uint64_t end = (begin + B < n) ? begin + B : n;
+    uint64_t h[2] = {0ull, 0ull};
+    for (uint64_t k = 0; begin + 8ull * k < end; k++) {
+      uint64_t w = 0;
+      for (unsigned i = 0; i < 8u && begin + 8ull * k + i < end; i++)
+        w |= (uint64_t)exp_field(x[begin + 8ull * k + i]) << (8u * i);
+      if (w == 0) continue;
+      for (int j = 0; j < 2; j++) h[j] += sm64_mix(w + ORC_HASH_SEED[j] + (k + 1ull) * ORC_HASH_GAMMA[j]);
+    }
+    out[2 * b] = h[0];
+    out[2 * b + 1] = h[1];
+  }
 }
 
 static unsigned code_of(unsigned e, unsigned e0) {

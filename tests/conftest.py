@@ -16,6 +16,18 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: full-size workload (minutes of host work)")
 
 
+def read_golden_ints(name):
+    """Like read_golden, with integer values kept exact."""
+    rows = {}
+    with open(os.path.join(TESTS, "golden", name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split()
+                rows[k] = int(v)
+    return rows
+
+
 def read_golden(name):
     """Parse a tests/golden fixture: '#' comments, then 'key value' lines."""
     rows = {}

@@ -13,7 +13,7 @@ import pytest
 
 import brute
 import oracle
-from conftest import read_golden
+from conftest import read_golden, read_golden_ints
 from lossless_bf16_tensor_exp_amd import workloads as wl
 
 C_OPT = 0.5 * math.log2(14.0 * math.log(2.0) / 16383.0)
@@ -361,3 +361,107 @@ def test_decode_rejects_corrupted_streams():
         oracle.zip3_decode(good, n + 1)
     with pytest.raises(oracle.OracleError):
         oracle.decode(good, n, 64, np.zeros(n, np.uint8))  # zip3 stream read as ciera
+
+
+# ---------------------------------------------------------------- block hash
+# CIERA page, section 3.1: the sender keeps a 128-bit hash per block built
+# from two independent 64-bit SplitMix64 hashes.  The oracle's construction
+# (a reading: the page does not say how a block's bytes enter SplitMix64) is
+# pinned to SplitMix64's published output sequence through hash 0, whose
+# term for a lone word w at position k is the (k+1)-th output of the
+# generator seeded with w.
+
+def _block_with_words(words, B):
+    """BF16 patterns whose exponent fields spell the given little-endian
+    u64 words (8 exponents each); sign and mantissa bits random."""
+    rng = np.random.default_rng(len(words) + B)
+    e = np.zeros(B, dtype=np.uint16)
+    for k, w in enumerate(words):
+        for i in range(8):
+            e[8 * k + i] = (w >> (8 * i)) & 0xFF
+    return ((rng.integers(0, 2, B, dtype=np.uint16) << 15) | (e << 7) |
+            rng.integers(0, 128, B, dtype=np.uint16)).astype(np.uint16)
+
+
+def test_splitmix64_published_sequence():
+    g = read_golden_ints("splitmix64_seed1234567.txt")
+    assert oracle.splitmix64(g["seed"], 5) == [g[f"out{i}"] for i in range(1, 6)]
+
+
+@pytest.mark.parametrize("k", range(5))
+def test_block_hash_lone_word_is_a_splitmix64_output(k):
+    g = read_golden_ints("splitmix64_seed1234567.txt")
+    for B in (64, 256):
+        words = [0] * (B // 8)
+        words[k] = g["seed"]
+        h = oracle.block_hashes(_block_with_words(words, B), B)
+        assert int(h[0, 0]) == g[f"out{k + 1}"]
+        assert int(h[0, 1]) not in (0, int(h[0, 0]))
+
+
+def test_block_hash_of_zero_exponents_is_zero():
+    rng = np.random.default_rng(5)
+    for n, B in [(64, 64), (1000, 128), (65536 + 77, 512), (100, 65536)]:
+        # zeros, subnormals: exponent field 0 everywhere, the last block short
+        x = (rng.integers(0, 2, n, dtype=np.uint16) << 15) | rng.integers(0, 128, n, dtype=np.uint16)
+        assert not oracle.block_hashes(x.astype(np.uint16), B).any()
+
+
+def test_block_hash_is_a_sum_over_words():
+    rng = np.random.default_rng(6)
+    B = 128
+    words = [int(v) for v in rng.integers(0, 1 << 63, B // 8, dtype=np.uint64)]
+    words[3] = 0
+    total = oracle.block_hashes(_block_with_words(words, B), B)[0].astype(object)
+    parts = np.zeros(2, dtype=object)
+    for k, w in enumerate(words):
+        lone = [0] * (B // 8)
+        lone[k] = w
+        parts += oracle.block_hashes(_block_with_words(lone, B), B)[0].astype(object)
+    assert [int(v) % (1 << 64) for v in parts] == [int(v) for v in total]
+
+
+@pytest.mark.parametrize("B", [64, 512])
+def test_block_hash_sees_every_single_exponent_change(B):
+    """Changing any one exponent field of a block, to any other value tried,
+    changes both 64-bit hashes (brute force over positions)."""
+    rng = np.random.default_rng(B)
+    x = wl.normal_bf16(rng, B, 0.02)
+    h = oracle.block_hashes(x, B)[0]
+    for i in range(B):
+        for new in rng.choice(256, size=6, replace=False):
+            e = (int(x[i]) >> 7) & 0xFF
+            if new == e:
+                continue
+            y = x.copy()
+            y[i] = (int(x[i]) & 0x807F) | (int(new) << 7)
+            g = oracle.block_hashes(y, B)[0]
+            assert g[0] != h[0] and g[1] != h[1], (i, e, new)
+
+
+def test_block_hash_sees_word_order():
+    rng = np.random.default_rng(8)
+    B = 64
+    words = [int(v) for v in rng.integers(1, 1 << 63, B // 8, dtype=np.uint64)]
+    h = oracle.block_hashes(_block_with_words(words, B), B)[0]
+    for a in range(8):
+        for b in range(a + 1, 8):
+            sw = list(words)
+            sw[a], sw[b] = sw[b], sw[a]
+            g = oracle.block_hashes(_block_with_words(sw, B), B)[0]
+            assert g[0] != h[0] and g[1] != h[1]
+
+
+def test_block_hash_no_collisions_among_random_blocks():
+    """2^17 blocks of Gaussian-like exponents (few distinct values per
+    position, so similar blocks are common): no two share either 64-bit hash
+    unless their exponents are equal."""
+    rng = np.random.default_rng(9)
+    B, nb = 64, 1 << 17
+    x = wl.normal_bf16(rng, B * nb, 0.02)
+    e = ((x >> 7) & 0xFF).astype(np.uint8).reshape(nb, B)
+    h = oracle.block_hashes(x, B)
+    _, first = np.unique(e, axis=0, return_index=True)
+    distinct = np.sort(first)
+    for j in range(2):
+        assert np.unique(h[distinct, j]).size == distinct.size
