@@ -122,6 +122,38 @@ ciera_status ciera_encode(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_pr
                           void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes,
                           uint64_t* d_out_size, hipStream_t stream);
 
+/* ciera_encode_hashed: ciera_encode with the sender state of the CIERA page
+ * (section 3.1): per block a 128-bit hash of its exponents made of two
+ * independent 64-bit SplitMix64 hashes, in place of the n-byte exponent
+ * cache, so encode reads 16 bytes per block instead of one byte per value.
+ * A block counts as unchanged only when both hashes equal the stored ones.
+ * The stream is the one ciera_encode writes from an exponent cache holding
+ * the previous exponents, unless a changed block's two hashes both collide
+ * with the stored ones (about 2^-128 per comparison); the receiver side is
+ * ciera_decode with its exponent cache, unchanged.
+ *   d_hash_cache  in/out  ciera_hash_cache_size(n, B) bytes, 16-byte aligned:
+ *                 per block two u64, the hashes of the exponents last sent.
+ *                 Zero-filled before the first iteration: (0, 0) is the hash
+ *                 of all-zero exponents, so the first stream equals
+ *                 ciera_encode's from a zeroed exponent cache.  Changed
+ *                 blocks get their new hashes.
+ * Block hash: block b's exponent fields, 8 at a time, form little-endian u64
+ * words w_k (the last word of a short block zero-filled); hash j is the sum
+ * mod 2^64, over the words that are not zero, of SplitMix64's output function
+ * at w_k + s_j + (k + 1) g_j, i.e. the (k+1)-th output of a SplitMix64
+ * generator with seed w_k + s_j and increment g_j; (s_0, g_0) =
+ * (0, 0x9E3779B97F4A7C15), (s_1, g_1) = (0x243F6A8885A308D3,
+ * 0xD1B54A32D192ED03).
+ * Other arguments, the workspace and errors as ciera_encode; CIERA_ERR_ARG
+ * also for a misaligned d_hash_cache, or a null one with n > 0. */
+ciera_status ciera_encode_hashed(const void* d_x, uint64_t n, uint32_t B, void* d_hash_cache, void* d_out,
+                                 uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                                 hipStream_t stream);
+
+/* Bytes of the hash sender's cache: 16 per block of B values (0 for an
+ * invalid B or n above 2^40). */
+uint64_t ciera_hash_cache_size(uint64_t n, uint32_t B);
+
 /* ciera_decode: rebuild x from the stream and the receiver's cache.
  *   d_prev_exp  in/out  receiver exponent cache, n bytes, holding the
  *                       previous iteration's exponents (all zero before the

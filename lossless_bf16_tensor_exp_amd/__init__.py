@@ -16,6 +16,8 @@ Same names as the C ABI::
     zip3_decode(inp, in_size, y, ws, stream=None)
     zip3_encode_e0(x, e0_src, out, ws, out_size, e0_offset=0, stream=None)
     ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None, plan_groups=0)
+    ciera_encode_hashed(x, B, hash_cache, out, ws, out_size, stream=None)
+    ciera_hash_cache_size(n, B)
     ciera_decode(inp, in_size, y, B, prev_exp, ws, stream=None)
     ciera_read_error(ws, stream=None)
     ciera_time_kernels(pairs)             (profiling: per-kernel start/stop events)
@@ -33,7 +35,7 @@ __all__ = [
     "CieraError", "library_path", "load_library",
     "zip3_max_encoded_size", "ciera_max_encoded_size", "zip3_workspace_size", "ciera_workspace_size",
     "zip3_encode", "zip3_decode", "ciera_encode", "ciera_decode", "ciera_read_error", "ciera_status_string",
-    "zip3_encode_e0",
+    "zip3_encode_e0", "ciera_encode_hashed", "ciera_hash_cache_size",
     "bind", "ciera_time_kernels",
     "CHUNK",
 ]
@@ -68,7 +70,8 @@ def load_library():
     lib = ctypes.CDLL(_LIB_PATH)
     u64, u32, vp, i32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
     for name, args in [("zip3_max_encoded_size", [u64]), ("ciera_max_encoded_size", [u64, u32]),
-                       ("zip3_workspace_size", [u64]), ("ciera_workspace_size", [u64, u32])]:
+                       ("zip3_workspace_size", [u64]), ("ciera_workspace_size", [u64, u32]),
+                       ("ciera_hash_cache_size", [u64, u32])]:
         f = getattr(lib, name)
         f.argtypes, f.restype = args, u64
     sigs = {
@@ -79,6 +82,7 @@ def load_library():
         "ciera_encode": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
         "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, u32, vp],
         "ciera_decode": [vp, u64, vp, u64, u32, vp, vp, u64, vp],
+        "ciera_encode_hashed": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
         "ciera_read_error": [vp, vp],
         "ciera_time_kernels": [ctypes.POINTER(vp), u32],
     }
@@ -199,6 +203,24 @@ def ciera_encode(x, B: int, prev_exp, out, ws, out_size, e0_override: int = -1, 
                              ws.numel(), ctypes.c_void_p(out_size.data_ptr()), e0_override, plan_groups,
                              _stream(stream))
     _raise(st, "ciera_encode")
+
+
+def ciera_hash_cache_size(n: int, B: int) -> int:
+    return load_library().ciera_hash_cache_size(n, B)
+
+
+def ciera_encode_hashed(x, B: int, hash_cache, out, ws, out_size, stream=None) -> None:
+    """ciera encode with the block-hash sender state (uint8 tensor of
+    ciera_hash_cache_size(n, B) bytes, zeroed before the first iteration)."""
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(hash_cache, "hash_cache", ciera_hash_cache_size(x.numel(), B))
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.ciera_encode_hashed(_ptr(x), x.numel(), B, _ptr(hash_cache), _ptr(out), out.numel(), _ptr(ws),
+                                 ws.numel(), ctypes.c_void_p(out_size.data_ptr()), _stream(stream))
+    _raise(st, "ciera_encode_hashed")
 
 
 def ciera_decode(inp, in_size: int, y, B: int, prev_exp, ws, stream=None) -> None:

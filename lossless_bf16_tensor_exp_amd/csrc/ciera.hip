@@ -138,7 +138,7 @@ struct PlanSlot {
 static_assert(sizeof(PlanSlot) == 64, "plan slot is 64 bytes");
 
 struct WsLayout {
-  uint64_t err, partial, bitmap, hist, partesc, chunkesc, pcount, cstat, plan, total;
+  uint64_t err, partial, bitmap, hist, partesc, chunkesc, pcount, cstat, plan, phash, total;
 };
 
 // Exponent histograms: per part one row of kBins u16 counts (a part holds at
@@ -159,7 +159,8 @@ __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   l.pcount = align256(l.chunkesc + 4u * slots);
   l.cstat = align256(l.pcount + 4u * kParts * slots);
   l.plan = align256(l.cstat + 8u * slots);
-  l.total = align256(l.plan + sizeof(PlanSlot) * kPlanMaxGroups);
+  l.phash = align256(l.plan + sizeof(PlanSlot) * kPlanMaxGroups);
+  l.total = align256(l.phash + 16u * kParts * slots);
   return l;
 }
 
@@ -175,6 +176,7 @@ struct Ws {
   uint32_t* pcount;     // per part: kPartReady | escapes of the part
   uint64_t* cstat;      // per chunk: flag | stream bytes (aggregate or inclusive prefix)
   PlanSlot* plan;       // per k_plan workgroup
+  uint64_t* phash;      // hash sender, blocks larger than a part: the part's two partial hashes
 };
 
 __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
@@ -191,6 +193,7 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.pcount = reinterpret_cast<uint32_t*>(b + l.pcount);
   w.cstat = reinterpret_cast<uint64_t*>(b + l.cstat);
   w.plan = reinterpret_cast<PlanSlot*>(b + l.plan);
+  w.phash = reinterpret_cast<uint64_t*>(b + l.phash);
   return w;
 }
 
@@ -410,6 +413,33 @@ __device__ inline uint32_t wave_sum_u32(uint32_t v) {
   return uint32_t(__builtin_amdgcn_readlane(int(wave_incl_scan(v)), 63));
 }
 
+// ------------------------------------------------------------------ block hash
+// Hash sender (CIERA page, section 3.1: per block a 128-bit hash of its
+// exponents made of two independent 64-bit SplitMix64 hashes; a block is
+// unchanged only when its hash equals the stored one).  A block's exponent
+// fields, 8 at a time, form little-endian 64-bit words w_k; hash h is the sum
+// mod 2^64, over the words that are not zero, of the SplitMix64 output
+// function applied to w_k + s_h + (k + 1) g_h: the (k+1)-th output of a
+// SplitMix64 generator (Steele, Lea and Flood, OOPSLA 2014) with seed
+// w_k + s_h and increment g_h.  An all-zero block hashes to (0, 0), so a
+// zeroed hash cache means all-zero previous exponents, as a zeroed exponent
+// cache does, and the stream equals the exact-cache stream unless two
+// different blocks' hashes collide.
+constexpr uint64_t kHashSeed0 = 0ull, kHashGamma0 = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kHashSeed1 = 0x243F6A8885A308D3ull, kHashGamma1 = 0xD1B54A32D192ED03ull;
+
+__device__ inline uint64_t splitmix64_out(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__device__ inline uint64_t shfl_u64(uint64_t v, uint32_t src) {
+  const uint32_t lo = uint32_t(__shfl(int(uint32_t(v)), int(src)));
+  const uint32_t hi = uint32_t(__shfl(int(uint32_t(v >> 32)), int(src)));
+  return (uint64_t(hi) << 32) | lo;
+}
+
 // ------------------------------------------------------------------ k_stats
 // FP64 value of a BF16 pattern held in the top half of a float: BF16 -> FP32
 // is exact (denormals are kept), FP32 -> FP64 is exact.
@@ -484,14 +514,18 @@ __device__ inline uint32_t stats_part_of(uint32_t b, uint32_t parts) {
 // One 256-thread workgroup per part (quarter chunk), units pu0 + 256 j + t.
 // Per part: FP64 variance partials; ciera: changed-block bits against the
 // sender cache and the cache update; an exponent histogram of the values to
-// code, and their count.
-template <bool kCiera>
+// code, and their count.  kHash: the sender cache is the block-hash cache
+// (two u64 per block) instead of the exponents.
+template <bool kCiera, bool kHash>
 __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
                                                         uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
-  __shared__ uint32_t s_hist[kHistCopies * kBins];
+  static_assert(kCiera || !kHash, "the hash sender is a ciera mode");
+  // hash sender: first the part's exponent words (2048 u64), then the histogram
+  __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistCopies * kBins];
   __shared__ uint32_t s_bits[kPartBitmapWords];
   __shared__ double s_s1[kPartWaves], s_s2[kPartWaves];
   __shared__ uint32_t s_nf[kPartWaves], s_wtot[kPartWaves];
+  __shared__ uint64_t s_wh[2][kPartWaves];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = lane_id(), wave = tid >> 6;
   const uint32_t wg = stats_part_of(blockIdx.x, gridDim.x);  // the part this workgroup takes
@@ -504,7 +538,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   const bool full = 8u * (pu0 + kPartUnits) <= nc;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint32_t blk0 = kCiera ? ((8u * pu0) >> log2B) : 0u;  // first block of the part
-  for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
+  if (!kHash)
+    for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
   if (tid < kPartBitmapWords) s_bits[tid] = 0u;
   if (blockIdx.x == 0u) {
     // k_plan's slots: the FP64 words empty, the count words not ready
@@ -515,13 +550,27 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   const uint32_t first = x[0];
   const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
 
+  // Hash sender, blocks within the part: the hash phase gives each block
+  // hb_threads consecutive threads (8 units each); the last of them decides
+  // and fetches the block's stored hashes now.
+  uint64_t* hcache = reinterpret_cast<uint64_t*>(cache);
+  const uint32_t hb_threads = (kHash && B <= kPartValues) ? B / 64u : kPartThreads;
+  const uint64_t hblk = kHash ? c * (kChunk >> log2B) + blk0 + tid / hb_threads : 0u;  // global block
+  const bool decider = kHash && B <= kPartValues && tid % hb_threads == hb_threads - 1u && (hblk << log2B) < n;
+  uint64_t hc0 = 0, hc1 = 0;
+  if (decider) {
+    const uint4 e = *reinterpret_cast<const uint4*>(hcache + 2u * hblk);
+    hc0 = (uint64_t(e.y) << 32) | e.x;
+    hc1 = (uint64_t(e.w) << 32) | e.z;
+  }
+
   // Load: all of a thread's 16-byte loads (and 8-byte cache loads) before use.
   Unit v[kUPT];
   uint2 old[kUPT];
   if (full) {
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) v[j] = load_unit(x, start + 8ull * (pu0 + j * kPartThreads + tid), 8u);
-    if (kCiera) {
+    if (kCiera && !kHash) {
 #pragma unroll
       for (uint32_t j = 0; j < kUPT; j++)
         old[j] = *reinterpret_cast<const uint2*>(cache + start + 8ull * (pu0 + j * kPartThreads + tid));
@@ -534,7 +583,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       old[j] = make_uint2(0u, 0u);
       if (u < nunits) {
         v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
-        if (kCiera) old[j] = load_bytes8(cache + start + 8ull * u, min(8u, nc - 8u * u));
+        if (kCiera && !kHash) old[j] = load_bytes8(cache + start + 8ull * u, min(8u, nc - 8u * u));
       }
     }
   }
@@ -576,14 +625,20 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       if (kCiera) {
         const uint2 e = unit_exponents(v[j]);
         const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
-        const uint64_t d = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
-        if (d) {
-          store_bytes8(cache + start + 8ull * u, cnt, e);
-          diff = true;
+        if (kHash) {
+          reinterpret_cast<uint64_t*>(s_hist)[j * kPartThreads + tid] = ((uint64_t(e.y) << 32) | e.x) & keep;
+        } else {
+          const uint64_t d = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
+          if (d) {
+            store_bytes8(cache + start + 8ull * u, cnt, e);
+            diff = true;
+          }
         }
       }
+    } else if (kHash) {
+      reinterpret_cast<uint64_t*>(s_hist)[j * kPartThreads + tid] = 0u;  // past the data
     }
-    if (kCiera) {
+    if (kCiera && !kHash) {
       const uint64_t m = __ballot(diff);
       if (m != 0u) {
         // first block of the wave's units, relative to the part
@@ -605,7 +660,95 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       if (u < nunits) stats_checked(v[j], min(8u, nc - 8u * u), shift, s1, s2, nf);
     }
   }
-  if (kCiera && B > 512u) {
+  if (kHash) {
+    // The part's exponent words are in LDS; thread t hashes units 8t .. 8t+7
+    // of the part (64 values), word k of its block being unit k of it.
+    __syncthreads();
+    const uint4* se = reinterpret_cast<const uint4*>(s_hist) + 4u * tid;
+    uint64_t w[8];
+#pragma unroll
+    for (uint32_t i = 0; i < 4u; i++) {
+      const uint4 q = se[i];
+      w[2u * i] = (uint64_t(q.y) << 32) | q.x;
+      w[2u * i + 1u] = (uint64_t(q.w) << 32) | q.z;
+    }
+    const uint64_t k1 = uint64_t(((pu0 + 8u * tid) & ((B >> 3) - 1u)) + 1u);  // k + 1 of the first word
+    uint64_t key0 = kHashSeed0 + k1 * kHashGamma0, key1 = kHashSeed1 + k1 * kHashGamma1;
+    uint64_t p0 = 0, p1 = 0;
+#pragma unroll
+    for (uint32_t i = 0; i < 8u; i++) {
+      if (w[i]) {
+        p0 += splitmix64_out(w[i] + key0);
+        p1 += splitmix64_out(w[i] + key1);
+      }
+      key0 += kHashGamma0;
+      key1 += kHashGamma1;
+    }
+    // The block's sum (mod 2^64) over its threads, in its last thread: a wave
+    // scan minus the scan before the block's first lane, or, for blocks (or
+    // a part's share of a block) wider than a wave, the waves' totals.
+    uint64_t s0 = p0, s1 = p1;
+    if (hb_threads > 1u) {
+      const uint64_t i0 = wave_incl_scan_u64(p0), i1 = wave_incl_scan_u64(p1);
+      if (hb_threads <= 64u) {
+        const uint32_t first = lane & ~(hb_threads - 1u);
+        s0 = i0 - shfl_u64(i0 - p0, first);
+        s1 = i1 - shfl_u64(i1 - p1, first);
+      } else {
+        if (lane == 63u) {
+          s_wh[0][wave] = i0;
+          s_wh[1][wave] = i1;
+        }
+        __syncthreads();
+        const uint32_t wpb = hb_threads / 64u, wfirst = (wave / wpb) * wpb;
+        s0 = s1 = 0u;
+        for (uint32_t q = 0; q < wpb; q++) {
+          s0 += s_wh[0][wfirst + q];
+          s1 += s_wh[1][wfirst + q];
+        }
+      }
+    }
+    if (B <= kPartValues) {
+      // decide: a changed block's new hashes go to the cache and its bit to s_bits
+      bool changed = false;
+      if (decider) {
+        changed = s0 != hc0 || s1 != hc1;
+        if (changed)
+          *reinterpret_cast<uint4*>(hcache + 2u * hblk) =
+              make_uint4(uint32_t(s0), uint32_t(s0 >> 32), uint32_t(s1), uint32_t(s1 >> 32));
+      }
+      if (hb_threads <= 64u) {
+        const uint64_t m = __ballot(changed);  // set only at the blocks' last lanes
+        if (m != 0u && lane == 0u) {
+          const uint32_t per = 64u / hb_threads;  // blocks of this wave
+          uint64_t bits = 0;
+          for (uint32_t i = 0; i < per; i++) bits |= ((m >> (i * hb_threads + hb_threads - 1u)) & 1u) << i;
+          const uint32_t b0 = wave * per;
+          atomicOr(&s_bits[b0 >> 5], uint32_t(bits) << (b0 & 31u));
+          if (per > 32u) atomicOr(&s_bits[(b0 >> 5) + 1u], uint32_t(bits >> 32));
+        }
+      } else if (changed) {
+        const uint32_t b = tid / hb_threads;
+        atomicOr(&s_bits[b >> 5], 1u << (b & 31u));
+      }
+    } else if (tid == kPartThreads - 1u) {
+      // a block spans several parts: k_plan adds the parts' shares and decides
+      ws.phash[2u * wg] = s0;
+      ws.phash[2u * wg + 1u] = s1;
+    }
+    __syncthreads();  // the exponent words are no longer read; s_bits complete
+    for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
+    if (B > kPartValues) {
+      coded = 0xFFu;
+    } else {
+#pragma unroll
+      for (uint32_t j = 0; j < kUPT; j++) {
+        const uint32_t lb = ((8u * (pu0 + j * kPartThreads + tid)) >> log2B) - blk0;
+        coded |= ((s_bits[lb >> 5] >> (lb & 31u)) & 1u) << j;
+      }
+    }
+    __syncthreads();  // histogram cleared
+  } else if (kCiera && B > 512u) {
     // a block spans several waves: its bit is complete after the barrier.  A
     // part inside a block that spans several parts counts all of its values
     // (k_plan drops them if the block is unchanged).
@@ -815,9 +958,13 @@ constexpr uint32_t kRunRegs = 8u;
 // totals and *out_size.  Every group is resident at once (at most
 // kPlanMaxGroups small workgroups), so the waits end; if one does not end in
 // its bound, the group sets ctrl->plan_fail and k_write writes nothing.
+// kHashBlocks: hash sender with blocks larger than a part, whose change
+// decision k_stats leaves to this kernel (hcache is then the hash cache).
+template <bool kHashBlocks>
 __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchunks, uint64_t per, uint32_t B,
                                                        int e0_override, uint8_t* __restrict__ out,
-                                                       uint64_t* __restrict__ out_size, Ws ws) {
+                                                       uint64_t* __restrict__ out_size, uint64_t* __restrict__ hcache,
+                                                       Ws ws) {
   __shared__ double s_f[kPlanWaves];
   __shared__ uint64_t s_u[kPlanWaves];
   __shared__ uint32_t s_e0;
@@ -920,11 +1067,39 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
       inwin[h] = sum;
     }
     uint32_t nchp[kParts] = {1u, 1u, 1u, 1u};
-    if (B > kPartValues) {
+    uint32_t nch = 0;
+    if (kHashBlocks) {
+      // hash sender, blocks spanning ppb parts: the block's hashes are the
+      // sums of its parts' shares; a changed block's go to the cache, and
+      // each of its parts gets the block's flag (bit 0 of its bitmap word)
+      for (uint32_t q = 0; q < kChunk / B; q++) {
+        const uint64_t blk = c * (kChunk / B) + q;
+        bool changed = false;
+        if (blk * B < n) {
+          uint64_t s0 = 0, s1 = 0;
+          for (uint32_t h = q * ppb; h < (q + 1u) * ppb; h++) {
+            s0 += ws.phash[2u * (c * kParts + h)];
+            s1 += ws.phash[2u * (c * kParts + h) + 1u];
+          }
+          const uint4 old = *reinterpret_cast<const uint4*>(hcache + 2u * blk);
+          changed = s0 != ((uint64_t(old.y) << 32) | old.x) || s1 != ((uint64_t(old.w) << 32) | old.z);
+          if (changed)
+            *reinterpret_cast<uint4*>(hcache + 2u * blk) =
+                make_uint4(uint32_t(s0), uint32_t(s0 >> 32), uint32_t(s1), uint32_t(s1 >> 32));
+        }
+        for (uint32_t h = q * ppb; h < (q + 1u) * ppb; h++) {
+          nchp[h] = changed ? 1u : 0u;
+          ws.bitmap[(c * kParts + h) * kPartBitmapWords] = changed ? 1u : 0u;
+        }
+        nch += changed ? 1u : 0u;
+      }
+    } else {
+      if (B > kPartValues) {
 #pragma unroll
-      for (uint32_t h = 0; h < kParts; h++) nchp[h] = pp[h].nch;
+        for (uint32_t h = 0; h < kParts; h++) nchp[h] = pp[h].nch;
+      }
+      nch = B ? chunk_changed_blocks(pp, B) : 0u;
     }
-    const uint32_t nch = B ? chunk_changed_blocks(pp, B) : 0u;
     uint32_t esc[kParts], acc = 0;
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) {
@@ -1928,35 +2103,50 @@ void launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A..
   }
 }
 
+// d_hash non-null: ciera mode with the block-hash sender state instead of the
+// exponent cache (d_cache unused).
 ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cache, void* d_out,
                          uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
-                         int e0_override, uint32_t plan_groups, hipStream_t stream) {
+                         int e0_override, uint32_t plan_groups, hipStream_t stream, void* d_hash = nullptr) {
   const bool ciera = B != 0u;
+  const bool hashed = d_hash != nullptr;
   if (n > kMaxN) return CIERA_ERR_ARG;
   if (ciera && !valid_block(B)) return CIERA_ERR_ARG;
   if (e0_override < -1 || e0_override > int(kMaxE0)) return CIERA_ERR_ARG;
   if (!d_out || !d_ws || !d_out_size || !aligned16(d_out) || !aligned16(d_ws)) return CIERA_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_out_size) & 7u) != 0u) return CIERA_ERR_ARG;
   if (n > 0 && (!d_x || !aligned16(d_x))) return CIERA_ERR_ARG;
-  if (ciera && n > 0 && (!d_cache || !aligned16(d_cache))) return CIERA_ERR_ARG;
+  if (ciera && !hashed && n > 0 && (!d_cache || !aligned16(d_cache))) return CIERA_ERR_ARG;
+  if (hashed && (!ciera || !aligned16(d_hash))) return CIERA_ERR_ARG;
   if (out_capacity < max_size(n, B)) return CIERA_ERR_CAPACITY;
   const uint64_t nchunks = cdiv(n, kChunk);
   if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
   const Ws ws = ws_bind(d_ws, nchunks);
   const uint32_t lb = ciera ? log2u(B) : 0u;
+  uint64_t* hcache = static_cast<uint64_t*>(d_hash);
   const uint16_t* x = static_cast<const uint16_t*>(d_x);
   uint8_t* out = static_cast<uint8_t*>(d_out);
   (void)hipGetLastError();
   if (nchunks) {
-    if (ciera)
-      launch(k_stats<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
+    if (hashed)
+      launch(k_stats<true, true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n,
+             static_cast<uint8_t*>(d_hash), lb, ws);
+    else if (ciera)
+      launch(k_stats<true, false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, d_cache, lb,
+             ws);
     else
-      launch(k_stats<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
+      launch(k_stats<false, false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nullptr, 0u,
+             ws);
   }
   uint64_t per = 0;
   uint32_t groups = 0;
   plan_shape(nchunks, plan_groups, per, groups);
-  launch(k_plan, dim3(groups), dim3(kPlanThreads), stream, n, nchunks, per, B, e0_override, out, d_out_size, ws);
+  if (hashed && B > kPartValues)
+    launch(k_plan<true>, dim3(groups), dim3(kPlanThreads), stream, n, nchunks, per, B, e0_override, out, d_out_size,
+           hcache, ws);
+  else
+    launch(k_plan<false>, dim3(groups), dim3(kPlanThreads), stream, n, nchunks, per, B, e0_override, out, d_out_size,
+           nullptr, ws);
   if (nchunks) {
     if (ciera)
       launch(k_write<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, lb, out,
@@ -2058,6 +2248,18 @@ ciera_status ciera_encode_ex(const void* d_x, uint64_t n, uint32_t B, uint8_t* d
   if (B == 0u) return CIERA_ERR_ARG;
   return encode_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, d_ws, ws_bytes, d_out_size, e0_override,
                      plan_groups, stream);
+}
+
+uint64_t ciera_hash_cache_size(uint64_t n, uint32_t B) {
+  return (n > kMaxN || !valid_block(B)) ? 0u : 16u * cdiv(n, B);
+}
+
+ciera_status ciera_encode_hashed(const void* d_x, uint64_t n, uint32_t B, void* d_hash_cache, void* d_out,
+                                 uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                                 hipStream_t stream) {
+  if (B == 0u || (!d_hash_cache && n > 0)) return CIERA_ERR_ARG;
+  return encode_impl(d_x, n, B, nullptr, d_out, out_capacity, d_ws, ws_bytes, d_out_size, -1, 0u, stream,
+                     d_hash_cache);
 }
 
 ciera_status ciera_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, uint32_t B,

@@ -176,3 +176,57 @@ def check_encode_e0(x, e0):
         raise AssertionError(f"single-read stream differs from the oracle at byte {i} of {o.size} "
                              f"(gpu size {g.size}): gpu {g[i:i + 16]} oracle {o[i:i + 16]}")
     return g
+
+
+def exps_as_bf16(e):
+    """BF16 patterns whose exponent fields are the bytes e (sign and mantissa
+    zero): a tensor whose block hashes stand for the exponent cache e."""
+    return (np.asarray(e, dtype=np.uint16) << 7).astype(np.uint16)
+
+
+def gpu_encode_hashed(x, B, hash_cache):
+    """Hash-sender encode on the GPU.  Returns (stream bytes, hash cache after
+    as a (blocks, 2) uint64 array)."""
+    n = x.size
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    cap = ciera.ciera_max_encoded_size(n, B)
+    buf, out = _guarded_bytes(cap)
+    ws = torch.empty(ciera.ciera_workspace_size(n, B), dtype=torch.uint8, device="cuda")
+    size = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    hb = ciera.ciera_hash_cache_size(n, B)
+    hbuf, hd = _guarded_bytes(hb)
+    hd.copy_(torch.from_numpy(np.ascontiguousarray(hash_cache).view(np.uint8).reshape(-1)))
+    ciera.ciera_encode_hashed(xd, B, hd, out, ws, size)
+    torch.cuda.synchronize()
+    assert ciera.ciera_read_error(ws) == 0
+    sz = int(size.item())
+    assert 0 < sz <= cap
+    host = buf.cpu().numpy()
+    _check_guards(host, cap, "stream")
+    assert (host[GUARD + sz:GUARD + cap] == CANARY).all(), "write past the stream's end"
+    hh = hbuf.cpu().numpy()
+    _check_guards(hh, hb, "hash cache")
+    return host[GUARD:GUARD + sz].copy(), hh[GUARD:GUARD + hb].copy().view(np.uint64).reshape(-1, 2)
+
+
+def check_encode_hashed(x, B, prev_exps):
+    """Hash-sender encode against a hash cache holding the hashes of
+    prev_exps == the oracle's exact-cache encode from prev_exps, byte for
+    byte, and the cache afterwards holds x's block hashes."""
+    hc = oracle.block_hashes(exps_as_bf16(prev_exps), B)
+    g, hc_after = gpu_encode_hashed(x, B, hc)
+    o_cache = np.ascontiguousarray(prev_exps, dtype=np.uint8).copy()
+    o, st = oracle.encode(x, B, o_cache, -1)
+    if g.tobytes() != o.tobytes() and int(g[7]) != st["E0"]:
+        var, nf = oracle.variance(x)
+        k = max(int(g[7]), st["E0"]) - 127
+        t = K0 * 4.0 ** k
+        assert abs(int(g[7]) - st["E0"]) == 1 and abs(var - t) <= 1e-6 * t
+        o_cache = np.ascontiguousarray(prev_exps, dtype=np.uint8).copy()
+        o, st = oracle.encode(x, B, o_cache, int(g[7]))
+    if g.tobytes() != o.tobytes():
+        i = _first_diff(g, o)
+        raise AssertionError(f"hash-sender stream differs from the oracle at byte {i} of {o.size} "
+                             f"(gpu size {g.size}): gpu {g[i:i + 16]} oracle {o[i:i + 16]}")
+    assert np.array_equal(hc_after, oracle.block_hashes(x, B)), "hash cache after encode"
+    return g, st

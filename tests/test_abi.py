@@ -72,6 +72,12 @@ def test_argument_errors_return_before_any_launch(lib):
     assert lib.ciera_read_error(None, None) == 1
     assert lib.zip3_encode_e0(p, 10, None, p, 1 << 20, p, 1 << 20, p, None) == 1
     assert lib.zip3_encode_e0(p, 10, p, p, 10, p, 1 << 20, p, None) == 2
+    assert lib.ciera_encode_hashed(p, 10, 64, None, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode_hashed(p, 10, 0, p, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode_hashed(p, 10, 64, ctypes.c_void_p(16 * 1024 + 8), p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode_hashed(p, 10, 64, p, p, 10, p, 1 << 20, p, None) == 2
+    assert lib.ciera_hash_cache_size(1000, 64) == 16 * 16
+    assert lib.ciera_hash_cache_size(1000, 48) == 0
     assert lib.ciera_time_kernels(None, 1) == 1
     assert lib.ciera_time_kernels(None, 0) == 0
 
