@@ -77,6 +77,14 @@ def _load():
     lib.orc_splitmix64_next.restype = u64
     lib.orc_block_hashes.argtypes = [vp, u64, u32, vp]
     lib.orc_block_hashes.restype = None
+    lib.orc_rans_freqs.argtypes = [vp, vp]
+    lib.orc_rans_freqs.restype = None
+    lib.orc_rans_max_encoded_size.argtypes = [u64, u32]
+    lib.orc_rans_max_encoded_size.restype = u64
+    lib.orc_encode_rans.argtypes = [vp, u64, u32, vp, vp, u64, ctypes.POINTER(u64), vp]
+    lib.orc_encode_rans.restype = i32
+    lib.orc_decode_rans.argtypes = [vp, u64, vp, u64, u32, vp]
+    lib.orc_decode_rans.restype = i32
     _lib = lib
     return lib
 
@@ -167,6 +175,50 @@ def block_hashes(x, B: int) -> np.ndarray:
     out = np.zeros((nb, 2), dtype=np.uint64)
     _load().orc_block_hashes(_ptr(x), x.size, B, _ptr(out))
     return out
+
+
+def rans_freqs(hist) -> np.ndarray:
+    """The normalised rANS frequencies (sum 4096) of a 256-bin histogram."""
+    h = np.ascontiguousarray(hist, dtype=np.uint32).reshape(-1)
+    assert h.size == 256
+    f = np.zeros(256, dtype=np.uint16)
+    _load().orc_rans_freqs(_ptr(h), _ptr(f))
+    return f
+
+
+def rans_max_encoded_size(n: int, B: int = 0) -> int:
+    return _load().orc_rans_max_encoded_size(n, B)
+
+
+def encode_rans(x, B: int = 0, cache: np.ndarray | None = None):
+    """rANS-mode encode (B = 0: zip3 + rANS; else ciera + rANS, ``cache``
+    updated in place).  Returns (stream, {"changed_blocks", "coded"})."""
+    x = _u16(x)
+    n = x.size
+    if B:
+        if cache is None or cache.dtype != np.uint8 or cache.size != n or not cache.flags.c_contiguous:
+            raise ValueError("ciera mode needs a contiguous uint8 cache of len(x)")
+    cap = rans_max_encoded_size(n, B)
+    out = np.zeros(cap, dtype=np.uint8)
+    size = ctypes.c_uint64()
+    stats = np.zeros(2, dtype=np.uint64)
+    st = _load().orc_encode_rans(_ptr(x), n, B, _ptr(cache) if B else None, _ptr(out), cap, ctypes.byref(size),
+                                 _ptr(stats))
+    if st != OK:
+        raise OracleError(st, "encode_rans")
+    return out[: size.value].copy(), {"changed_blocks": int(stats[0]), "coded": int(stats[1])}
+
+
+def decode_rans(stream, n: int, B: int = 0, cache: np.ndarray | None = None) -> np.ndarray:
+    stream = np.ascontiguousarray(stream, dtype=np.uint8).reshape(-1)
+    y = np.zeros(n, dtype=np.uint16)
+    if B:
+        if cache is None or cache.dtype != np.uint8 or cache.size != n or not cache.flags.c_contiguous:
+            raise ValueError("ciera mode needs a contiguous uint8 cache of n bytes")
+    st = _load().orc_decode_rans(_ptr(stream), stream.size, _ptr(y), n, B, _ptr(cache) if B else None)
+    if st != OK:
+        raise OracleError(st, "decode_rans")
+    return y
 
 
 def zip3_encode(x, e0_override: int = -1):

@@ -513,3 +513,369 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
   if (get_u64(in + 40) != total_changed || get_u64(in + 48) != total_esc) return ORC_ERR_FORMAT;
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------
+ * rANS variant (modes 2 = zip3 + rANS, 3 = ciera + rANS).  The coded
+ * exponents (all of them in zip3 mode, those of changed blocks in ciera mode)
+ * are entropy coded with range ANS instead of the 3-bit window code, in
+ * place of the ANS coder the CIERA page uses for changed exponents (section
+ * 3.1: the sender ANS-encodes the changed exponents, the receiver
+ * ANS-decodes them).  The page names no ANS parameters; this format is ours.
+ *
+ *  - Symbols: per part (a quarter chunk, values [16384 h, 16384 (h+1)) of
+ *    the chunk), the exponent fields of its coded values in value order,
+ *    s_0 .. s_{m-1}.
+ *  - Frequencies: the part's histogram h over those symbols, normalised to
+ *    M = 4096: with d distinct symbols, f_s = max(1, floor(h_s (M - d) / m))
+ *    for every symbol present (0 otherwise), and the rest, M - sum f, is
+ *    added to the most frequent symbol (the lowest one on ties).  c_s is
+ *    the sum of f over the symbols below s.
+ *  - Coding: 64 interleaved rANS states; symbol i goes to state i mod 64
+ *    (step i div 64).  A state is a 32-bit x in [2^16, 2^32), starting at
+ *    2^16.  Encoding runs over the steps from last to first; a state about
+ *    to code symbol s first emits its low 16 bits and shifts right by 16
+ *    when x >= f_s 2^20, then becomes (x div f_s) 2^12 + (x mod f_s) + c_s.
+ *    Decoding runs forward: slot = x mod 2^12, s is the symbol whose range
+ *    [c_s, c_s + f_s) holds slot, x becomes f_s (x div 2^12) + slot - c_s,
+ *    and a state below 2^16 reads one 16-bit word: x = x 2^16 + word.
+ *  - Part payload (little-endian): u8 lo, u8 hi (the first and last symbol
+ *    with f > 0), u16 0, u32 nwords, then f_lo .. f_hi as u16, then nwords
+ *    16-bit words: the 64 final encoder states (low half, high half, state
+ *    0 first), then, step by step from the first, the words the encoder
+ *    emitted at that step, in ascending state order.  A part without coded
+ *    symbols has an empty payload.
+ *  - Stream: the 128-byte header (mode 2 or 3, E0 = 0, bytes 48..55 the
+ *    number of coded symbols); at byte 128 a part table of 4 nchunks + 1 u64
+ *    absolute payload offsets (the last is total_bytes), zero-padded to 128;
+ *    then the sign+mantissa bytes of all n values, zero-padded to 128; in
+ *    ciera mode the chunks' bitmaps, 128 bytes each (bit j & 7 of byte
+ *    j >> 3 for block j of the chunk); then the part payloads, each
+ *    zero-padded to 128.
+ * A decoder checks that every word is used and that every state ends at
+ * 2^16, the encoder's start.
+ * ------------------------------------------------------------------------ */
+#define ORC_RANS_M 4096u
+#define ORC_RANS_L 65536u
+#define ORC_RANS_LANES 64u
+#define ORC_PART 16384ull
+
+void orc_rans_freqs(const uint32_t hist[256], uint16_t freq[256]) {
+  uint64_t m = 0;
+  unsigned d = 0, top = 0;
+  for (unsigned s = 0; s < 256; s++) {
+    m += hist[s];
+    if (hist[s]) d++;
+    if (hist[s] > hist[top]) top = s;
+  }
+  if (m == 0) {
+    memset(freq, 0, 256 * sizeof(uint16_t));
+    return;
+  }
+  unsigned sum = 0;
+  for (unsigned s = 0; s < 256; s++) {
+    unsigned f = 0;
+    if (hist[s]) {
+      f = (unsigned)((uint64_t)hist[s] * (ORC_RANS_M - d) / m);
+      if (f == 0) f = 1;
+    }
+    freq[s] = (uint16_t)f;
+    sum += f;
+  }
+  freq[top] = (uint16_t)(freq[top] + (ORC_RANS_M - sum));
+}
+
+static uint64_t rans_part_max(uint64_t m) { return m ? 8ull + 512ull + 256ull + 2ull * m : 0ull; }
+
+uint64_t orc_rans_max_encoded_size(uint64_t n, uint32_t B) {
+  uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+  uint64_t size = ORC_HEADER + pad128(8ull * (4ull * nchunks + 1ull)) + pad128(n);
+  if (B) size += 128ull * nchunks;
+  for (uint64_t v = 0; v < n; v += ORC_PART) {
+    uint64_t m = (n - v < ORC_PART) ? n - v : ORC_PART;
+    size += pad128(rans_part_max(m));
+  }
+  return size;
+}
+
+/* Payload of one part's m symbols; returns its length in bytes (0 for m = 0). */
+static uint64_t rans_encode_part(const uint8_t* sym, uint64_t m, uint8_t* out) {
+  if (m == 0) return 0;
+  uint32_t hist[256] = {0};
+  for (uint64_t i = 0; i < m; i++) hist[sym[i]]++;
+  uint16_t f[256];
+  orc_rans_freqs(hist, f);
+  uint32_t cum[256];
+  unsigned lo = 256, hi = 0, c = 0;
+  for (unsigned s = 0; s < 256; s++) {
+    cum[s] = c;
+    c += f[s];
+    if (f[s]) {
+      if (lo == 256) lo = s;
+      hi = s;
+    }
+  }
+  const uint64_t steps = ceil_div(m, ORC_RANS_LANES);
+  uint32_t x[ORC_RANS_LANES];
+  for (unsigned l = 0; l < ORC_RANS_LANES; l++) x[l] = ORC_RANS_L;
+  /* emitted words in encode order (last step first) and each step's count */
+  uint16_t* emit = (uint16_t*)malloc(m * sizeof(uint16_t));
+  uint64_t* count = (uint64_t*)calloc(steps, sizeof(uint64_t));
+  uint64_t ne = 0;
+  for (uint64_t t = steps; t-- > 0;) {
+    for (unsigned l = 0; l < ORC_RANS_LANES; l++) {
+      uint64_t i = t * ORC_RANS_LANES + l;
+      if (i >= m) break;
+      unsigned s = sym[i];
+      uint64_t xmax = (uint64_t)f[s] << 20;
+      if (x[l] >= xmax) {
+        emit[ne++] = (uint16_t)(x[l] & 0xFFFFu);
+        count[t]++;
+        x[l] >>= 16;
+      }
+      x[l] = (x[l] / f[s]) * ORC_RANS_M + (x[l] % f[s]) + cum[s];
+    }
+  }
+  const uint64_t nwords = 2ull * ORC_RANS_LANES + ne;
+  out[0] = (uint8_t)lo;
+  out[1] = (uint8_t)hi;
+  out[2] = out[3] = 0;
+  put_u32(out + 4, (uint32_t)nwords);
+  uint8_t* p = out + 8;
+  for (unsigned s = lo; s <= hi; s++, p += 2) put_u16(p, f[s]);
+  for (unsigned l = 0; l < ORC_RANS_LANES; l++, p += 4) {
+    put_u16(p, x[l] & 0xFFFFu);
+    put_u16(p + 2, x[l] >> 16);
+  }
+  /* step t's words sit in emit[] after those of the steps above t */
+  uint64_t above = 0;
+  for (uint64_t t = steps; t-- > 0;) {
+    uint64_t tmp = count[t];
+    count[t] = above; /* now: index in emit[] of step t's first word */
+    above += tmp;
+  }
+  for (uint64_t t = 0; t < steps; t++) {
+    uint64_t first = count[t];
+    uint64_t end = (t == 0) ? ne : count[t - 1];
+    for (uint64_t k = first; k < end; k++, p += 2) put_u16(p, emit[k]);
+  }
+  free(emit);
+  free(count);
+  return (uint64_t)(p - out);
+}
+
+/* Decode one part's payload (len bytes, the padding excluded) into m symbols. */
+static int rans_decode_part(const uint8_t* in, uint64_t len, uint64_t m, uint8_t* sym) {
+  if (len < 8) return ORC_ERR_FORMAT;
+  unsigned lo = in[0], hi = in[1];
+  uint64_t nwords = get_u32(in + 4);
+  if (hi < lo || in[2] || in[3]) return ORC_ERR_FORMAT;
+  const uint64_t fbytes = 2ull * (hi - lo + 1u);
+  if (len != 8 + fbytes + 2 * nwords || nwords < 2ull * ORC_RANS_LANES) return ORC_ERR_FORMAT;
+  uint32_t f[256] = {0}, cum[256];
+  unsigned total = 0;
+  for (unsigned s = lo; s <= hi; s++) {
+    f[s] = get_u16(in + 8 + 2 * (s - lo));
+    total += f[s];
+  }
+  if (total != ORC_RANS_M) return ORC_ERR_FORMAT;
+  uint8_t sym_of[ORC_RANS_M];
+  unsigned c = 0;
+  for (unsigned s = 0; s < 256; s++) {
+    cum[s] = c;
+    for (unsigned k = 0; k < f[s]; k++) sym_of[c + k] = (uint8_t)s;
+    c += f[s];
+  }
+  const uint8_t* w = in + 8 + fbytes;
+  uint32_t x[ORC_RANS_LANES];
+  for (unsigned l = 0; l < ORC_RANS_LANES; l++) {
+    x[l] = (uint32_t)get_u16(w + 4 * l) | ((uint32_t)get_u16(w + 4 * l + 2) << 16);
+    if (x[l] < ORC_RANS_L) return ORC_ERR_FORMAT;
+  }
+  uint64_t q = 2ull * ORC_RANS_LANES;
+  const uint64_t steps = ceil_div(m, ORC_RANS_LANES);
+  for (uint64_t t = 0; t < steps; t++) {
+    for (unsigned l = 0; l < ORC_RANS_LANES; l++) {
+      uint64_t i = t * ORC_RANS_LANES + l;
+      if (i >= m) break;
+      unsigned slot = x[l] & (ORC_RANS_M - 1u);
+      unsigned s = sym_of[slot];
+      x[l] = f[s] * (x[l] >> 12) + slot - cum[s];
+      if (x[l] < ORC_RANS_L) {
+        if (q >= nwords) return ORC_ERR_FORMAT;
+        x[l] = (x[l] << 16) | get_u16(w + 2 * q);
+        q++;
+      }
+      sym[i] = (uint8_t)s;
+    }
+  }
+  if (q != nwords) return ORC_ERR_FORMAT;
+  for (unsigned l = 0; l < ORC_RANS_LANES; l++)
+    if (x[l] != ORC_RANS_L) return ORC_ERR_FORMAT;
+  return ORC_OK;
+}
+
+static uint64_t rans_sm_pos(uint64_t nchunks) { return ORC_HEADER + pad128(8ull * (4ull * nchunks + 1ull)); }
+
+/* Is value i coded?  zip3: always; ciera: when its block changed. */
+static int rans_coded(const uint8_t* changed, uint32_t B, uint64_t i) { return B == 0 || changed[i / B]; }
+
+/* Encode in an rANS mode (B = 0: zip3 + rANS; else ciera + rANS with the
+ * sender cache as in orc_encode).  stats (may be NULL): {changed blocks,
+ * coded symbols}. */
+int orc_encode_rans(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, uint8_t* out, uint64_t capacity,
+                    uint64_t* out_size, uint64_t* stats) {
+  const int ciera = (B != 0);
+  if (n > ORC_MAX_N) return ORC_ERR_ARG;
+  if (ciera && !valid_block_size(B)) return ORC_ERR_ARG;
+  if (ciera && n > 0 && cache == NULL) return ORC_ERR_ARG;
+  if (n > 0 && x == NULL) return ORC_ERR_ARG;
+  const uint64_t need = orc_rans_max_encoded_size(n, B);
+  if (out == NULL || capacity < need) return ORC_ERR_CAPACITY;
+  memset(out, 0, need);
+  const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+  const uint64_t nparts = 4ull * nchunks;
+  const uint64_t nblocks = ciera ? ceil_div(n, B) : 0;
+  uint8_t* changed = NULL;
+  uint64_t n_changed = 0;
+  if (ciera) {
+    changed = (uint8_t*)calloc(nblocks ? nblocks : 1, 1);
+    if (!changed) return ORC_ERR_NOMEM;
+    for (uint64_t i = 0; i < n; i++)
+      if (exp_field(x[i]) != cache[i]) changed[i / B] = 1;
+    for (uint64_t b = 0; b < nblocks; b++) n_changed += changed[b];
+  }
+  const uint64_t sm_pos = rans_sm_pos(nchunks);
+  const uint64_t bm_pos = sm_pos + pad128(n);
+  uint64_t pos = bm_pos + (ciera ? 128ull * nchunks : 0);
+  for (uint64_t i = 0; i < n; i++) out[sm_pos + i] = (uint8_t)sm_field(x[i]);
+  if (ciera) {
+    for (uint64_t c = 0; c < nchunks; c++)
+      for (uint64_t j = 0; j < ORC_CHUNK / B && c * ORC_CHUNK + j * B < n; j++)
+        if (changed[c * (ORC_CHUNK / B) + j]) out[bm_pos + 128 * c + (j >> 3)] |= (uint8_t)(1u << (j & 7));
+  }
+  uint8_t* sym = (uint8_t*)malloc(ORC_PART);
+  uint64_t n_coded = 0;
+  for (uint64_t p = 0; p < nparts; p++) {
+    put_u64(out + ORC_HEADER + 8 * p, pos);
+    uint64_t begin = p * ORC_PART, end = begin + ORC_PART < n ? begin + ORC_PART : n;
+    uint64_t m = 0;
+    for (uint64_t i = begin; i < end; i++)
+      if (rans_coded(changed, B, i)) sym[m++] = (uint8_t)exp_field(x[i]);
+    n_coded += m;
+    pos += pad128(rans_encode_part(sym, m, out + pos));
+  }
+  free(sym);
+  put_u64(out + ORC_HEADER + 8 * nparts, pos);
+  memcpy(out, ciera ? "CIER" : "ZIP3", 4);
+  put_u16(out + 4, 1);
+  out[6] = ciera ? 3 : 2;
+  out[7] = 0;
+  put_u64(out + 8, n);
+  put_u32(out + 16, B);
+  put_u32(out + 20, (uint32_t)ORC_CHUNK);
+  put_u64(out + 24, nchunks);
+  put_u64(out + 32, pos);
+  put_u64(out + 40, n_changed);
+  put_u64(out + 48, n_coded);
+  if (ciera)
+    for (uint64_t i = 0; i < n; i++) cache[i] = (uint8_t)exp_field(x[i]);
+  free(changed);
+  *out_size = pos;
+  if (stats) {
+    stats[0] = n_changed;
+    stats[1] = n_coded;
+  }
+  return ORC_OK;
+}
+
+int orc_decode_rans(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uint32_t B, uint8_t* cache) {
+  const int ciera = (B != 0);
+  if (in == NULL || (n > 0 && y == NULL) || (ciera && n > 0 && cache == NULL)) return ORC_ERR_ARG;
+  if (n > ORC_MAX_N || (ciera && !valid_block_size(B))) return ORC_ERR_ARG;
+  const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+  const uint64_t nparts = 4ull * nchunks;
+  const uint64_t sm_pos = rans_sm_pos(nchunks);
+  const uint64_t bm_pos = sm_pos + pad128(n);
+  const uint64_t pay_pos = bm_pos + (ciera ? 128ull * nchunks : 0);
+  if (in_size < pay_pos) return ORC_ERR_FORMAT;
+  if (memcmp(in, ciera ? "CIER" : "ZIP3", 4) != 0 || get_u16(in + 4) != 1 || in[6] != (ciera ? 3 : 2) ||
+      in[7] != 0 || get_u64(in + 8) != n || get_u32(in + 16) != B || get_u32(in + 20) != ORC_CHUNK ||
+      get_u64(in + 24) != nchunks || get_u64(in + 32) != in_size)
+    return ORC_ERR_FORMAT;
+  for (unsigned k = 56; k < ORC_HEADER; k++)
+    if (in[k]) return ORC_ERR_FORMAT;
+  if (get_u64(in + ORC_HEADER) != pay_pos || get_u64(in + ORC_HEADER + 8 * nparts) != in_size) return ORC_ERR_FORMAT;
+  uint8_t* sym = (uint8_t*)malloc(ORC_PART);
+  uint64_t n_changed = 0, n_coded = 0;
+  int st = ORC_OK;
+  for (uint64_t p = 0; p < nparts && st == ORC_OK; p++) {
+    uint64_t a = get_u64(in + ORC_HEADER + 8 * p), b = get_u64(in + ORC_HEADER + 8 * (p + 1));
+    if (b < a || b > in_size || (a & 127u) || (b & 127u)) {
+      st = ORC_ERR_FORMAT;
+      break;
+    }
+    uint64_t begin = p * ORC_PART, end = begin + ORC_PART < n ? begin + ORC_PART : n;
+    uint64_t m = 0;
+    for (uint64_t i = begin; i < end; i++) {
+      int coded = 1;
+      if (ciera) {
+        uint64_t c = i / ORC_CHUNK, j = (i % ORC_CHUNK) / B;
+        coded = (in[bm_pos + 128 * c + (j >> 3)] >> (j & 7)) & 1;
+      }
+      m += coded ? 1 : 0;
+    }
+    n_coded += m;
+    if (m == 0) {
+      if (b != a) st = ORC_ERR_FORMAT;
+      continue;
+    }
+    if (b - a < 8) {
+      st = ORC_ERR_FORMAT;
+      break;
+    }
+    uint64_t len = 8 + 2ull * (in[a + 1] >= in[a] ? in[a + 1] - in[a] + 1u : 0) + 2ull * get_u32(in + a + 4);
+    if (pad128(len) != b - a) {
+      st = ORC_ERR_FORMAT;
+      break;
+    }
+    for (uint64_t k = a + len; k < b; k++)
+      if (in[k]) st = ORC_ERR_FORMAT;
+    if (st == ORC_OK) st = rans_decode_part(in + a, len, m, sym);
+    if (st != ORC_OK) break;
+    uint64_t k = 0;
+    for (uint64_t i = begin; i < end; i++) {
+      int coded = 1;
+      if (ciera) {
+        uint64_t c = i / ORC_CHUNK, j = (i % ORC_CHUNK) / B;
+        coded = (in[bm_pos + 128 * c + (j >> 3)] >> (j & 7)) & 1;
+      }
+      if (coded) {
+        y[i] = join_fields(in[sm_pos + i], sym[k++]);
+        if (ciera) cache[i] = (uint8_t)exp_field(y[i]);
+      }
+    }
+  }
+  free(sym);
+  if (st != ORC_OK) return st;
+  /* values of unchanged blocks (and parts without coded symbols) */
+  for (uint64_t i = 0; i < n; i++) {
+    int coded = 1;
+    if (ciera) {
+      uint64_t c = i / ORC_CHUNK, j = (i % ORC_CHUNK) / B;
+      coded = (in[bm_pos + 128 * c + (j >> 3)] >> (j & 7)) & 1;
+    }
+    if (!coded) y[i] = join_fields(in[sm_pos + i], cache[i]);
+  }
+  if (ciera) {
+    for (uint64_t c = 0; c < nchunks; c++) {
+      uint64_t nb_c = ceil_div((n - c * ORC_CHUNK < ORC_CHUNK) ? n - c * ORC_CHUNK : ORC_CHUNK, B);
+      for (uint64_t j = 0; j < 1024; j++) {
+        int bit = (in[bm_pos + 128 * c + (j >> 3)] >> (j & 7)) & 1;
+        if (bit && j >= nb_c) return ORC_ERR_FORMAT;
+        n_changed += bit;
+      }
+    }
+  }
+  if (get_u64(in + 40) != n_changed || get_u64(in + 48) != n_coded) return ORC_ERR_FORMAT;
+  return ORC_OK;
+}
