@@ -18,6 +18,8 @@ Same names as the C ABI::
     ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None, plan_groups=0)
     ciera_encode_hashed(x, B, hash_cache, out, ws, out_size, stream=None)
     ciera_hash_cache_size(n, B)
+    zip3_encode_rans / zip3_decode_rans / ciera_encode_rans / ciera_decode_rans   (rANS-coded exponents)
+    rans_max_encoded_size(n, B), rans_workspace_size(n, B)
     ciera_decode(inp, in_size, y, B, prev_exp, ws, stream=None)
     ciera_read_error(ws, stream=None)
     ciera_time_kernels(pairs)             (profiling: per-kernel start/stop events)
@@ -36,6 +38,8 @@ __all__ = [
     "zip3_max_encoded_size", "ciera_max_encoded_size", "zip3_workspace_size", "ciera_workspace_size",
     "zip3_encode", "zip3_decode", "ciera_encode", "ciera_decode", "ciera_read_error", "ciera_status_string",
     "zip3_encode_e0", "ciera_encode_hashed", "ciera_hash_cache_size",
+    "rans_max_encoded_size", "rans_workspace_size", "zip3_encode_rans", "zip3_decode_rans", "ciera_encode_rans",
+    "ciera_decode_rans",
     "bind", "ciera_time_kernels",
     "CHUNK",
 ]
@@ -71,7 +75,8 @@ def load_library():
     u64, u32, vp, i32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
     for name, args in [("zip3_max_encoded_size", [u64]), ("ciera_max_encoded_size", [u64, u32]),
                        ("zip3_workspace_size", [u64]), ("ciera_workspace_size", [u64, u32]),
-                       ("ciera_hash_cache_size", [u64, u32])]:
+                       ("ciera_hash_cache_size", [u64, u32]), ("rans_max_encoded_size", [u64, u32]),
+                       ("rans_workspace_size", [u64, u32])]:
         f = getattr(lib, name)
         f.argtypes, f.restype = args, u64
     sigs = {
@@ -83,6 +88,10 @@ def load_library():
         "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, u32, vp],
         "ciera_decode": [vp, u64, vp, u64, u32, vp, vp, u64, vp],
         "ciera_encode_hashed": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
+        "zip3_encode_rans": [vp, u64, vp, u64, vp, u64, vp, vp],
+        "zip3_decode_rans": [vp, u64, vp, u64, vp, u64, vp],
+        "ciera_encode_rans": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
+        "ciera_decode_rans": [vp, u64, vp, u64, u32, vp, vp, u64, vp],
         "ciera_read_error": [vp, vp],
         "ciera_time_kernels": [ctypes.POINTER(vp), u32],
     }
@@ -221,6 +230,57 @@ def ciera_encode_hashed(x, B: int, hash_cache, out, ws, out_size, stream=None) -
     st = lib.ciera_encode_hashed(_ptr(x), x.numel(), B, _ptr(hash_cache), _ptr(out), out.numel(), _ptr(ws),
                                  ws.numel(), ctypes.c_void_p(out_size.data_ptr()), _stream(stream))
     _raise(st, "ciera_encode_hashed")
+
+
+def rans_max_encoded_size(n: int, B: int = 0) -> int:
+    return load_library().rans_max_encoded_size(n, B)
+
+
+def rans_workspace_size(n: int, B: int = 0) -> int:
+    return load_library().rans_workspace_size(n, B)
+
+
+def zip3_encode_rans(x, out, ws, out_size, stream=None) -> None:
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.zip3_encode_rans(_ptr(x), x.numel(), _ptr(out), out.numel(), _ptr(ws), ws.numel(),
+                              ctypes.c_void_p(out_size.data_ptr()), _stream(stream))
+    _raise(st, "zip3_encode_rans")
+
+
+def zip3_decode_rans(inp, in_size: int, y, ws, stream=None) -> None:
+    lib = load_library()
+    _check_bytes(inp, "inp", in_size)
+    _check_values(y, "y")
+    _check_bytes(ws, "ws")
+    st = lib.zip3_decode_rans(_ptr(inp), in_size, _ptr(y), y.numel(), _ptr(ws), ws.numel(), _stream(stream))
+    _raise(st, "zip3_decode_rans")
+
+
+def ciera_encode_rans(x, B: int, prev_exp, out, ws, out_size, stream=None) -> None:
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(prev_exp, "prev_exp", x.numel())
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.ciera_encode_rans(_ptr(x), x.numel(), B, _ptr(prev_exp), _ptr(out), out.numel(), _ptr(ws), ws.numel(),
+                               ctypes.c_void_p(out_size.data_ptr()), _stream(stream))
+    _raise(st, "ciera_encode_rans")
+
+
+def ciera_decode_rans(inp, in_size: int, y, B: int, prev_exp, ws, stream=None) -> None:
+    lib = load_library()
+    _check_bytes(inp, "inp", in_size)
+    _check_values(y, "y")
+    _check_bytes(prev_exp, "prev_exp", y.numel())
+    _check_bytes(ws, "ws")
+    st = lib.ciera_decode_rans(_ptr(inp), in_size, _ptr(y), y.numel(), B, _ptr(prev_exp), _ptr(ws), ws.numel(),
+                               _stream(stream))
+    _raise(st, "ciera_decode_rans")
 
 
 def ciera_decode(inp, in_size: int, y, B: int, prev_exp, ws, stream=None) -> None:

@@ -177,6 +177,11 @@ struct Ws {
   uint64_t* cstat;      // per chunk: flag | stream bytes (aggregate or inclusive prefix)
   PlanSlot* plan;       // per k_plan workgroup
   uint64_t* phash;      // hash sender, blocks larger than a part: the part's two partial hashes
+  // rANS modes only (null otherwise): per part a look-back word, its coded
+  // count and changed blocks, and a scratch slot for its payload
+  uint64_t* rstat;
+  uint64_t* rinfo;
+  uint8_t* rslot;
 };
 
 __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
@@ -194,6 +199,9 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.cstat = reinterpret_cast<uint64_t*>(b + l.cstat);
   w.plan = reinterpret_cast<PlanSlot*>(b + l.plan);
   w.phash = reinterpret_cast<uint64_t*>(b + l.phash);
+  w.rstat = nullptr;
+  w.rinfo = nullptr;
+  w.rslot = nullptr;
   return w;
 }
 
@@ -541,6 +549,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   if (!kHash)
     for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
   if (tid < kPartBitmapWords) s_bits[tid] = 0u;
+  if (ws.rstat && tid == 0) ws.rstat[wg] = 0u;  // rANS encode: the part's look-back word, not ready
   if (blockIdx.x == 0u) {
     // k_plan's slots: the FP64 words empty, the count words not ready
     uint64_t* sw = reinterpret_cast<uint64_t*>(ws.plan);
@@ -2052,6 +2061,567 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   if (tid == 0) err_slots[wg] = err;
 }
 
+// ------------------------------------------------------------------ rANS modes
+// The coded exponents (all of them in zip3 mode, those of changed blocks in
+// ciera mode) entropy coded with range ANS in place of the 3-bit code, as the
+// CIERA page ANS-codes changed exponents (section 3.1); the page names no ANS
+// parameters, so the coder is our own:
+//  - per part (16384 values), the symbols are the coded exponents in value
+//    order; frequencies: the part's histogram normalised to M = 4096 (with d
+//    distinct symbols among m, f = max(1, floor(h (M - d) / m)) for each
+//    present symbol, the rest to the most frequent one, the lowest on ties);
+//  - 64 interleaved 32-bit states (symbol i to state i mod 64) in
+//    [2^16, 2^32), starting at 2^16; encode: if x >= f 2^20 emit its low 16
+//    bits and shift, then x = (x div f) M + x mod f + c; decode: slot =
+//    x mod M, x = f (x div M) + slot - c, then one 16-bit word if x < 2^16;
+//  - payload: u8 lo, u8 hi, u16 0, u32 nwords, u16 f_lo .. f_hi, then the
+//    64 final states (low, high half) and the words each step emitted, steps
+//    in decode order, states ascending within a step;
+//  - stream: header (mode 2 zip3 + rANS, 3 ciera + rANS; bytes 48..55 the
+//    coded symbols), a table of 4 nchunks + 1 u64 part payload offsets,
+//    every value's sign+mantissa byte, in ciera mode 128 bitmap bytes per
+//    chunk, then the part payloads, each padded to 128 bytes.
+// One wave per part runs the 64 states; the part's other waves load, write
+// the sign+mantissa bytes and stage the symbols.  Encode: k_stats (the
+// part's histogram of coded exponents), k_rans_enc (code into a scratch
+// slot, find the offset by look-back over the parts before, copy into the
+// stream), k_rans_finish (header totals).  Decode: k_rans_dec.
+constexpr uint32_t kRansM = 4096u;
+constexpr uint32_t kRansL = 1u << 16;
+constexpr uint32_t kRansStates = 64u;
+constexpr uint32_t kRansSlot = 33664u;       // pad128(8 + 512 + 256 + 2 * 16384): a part's largest payload
+constexpr uint32_t kRansStage = 20480u;      // payload bytes k_rans_dec stages in LDS (the rest read from HBM)
+
+__host__ __device__ inline uint64_t rans_sm_pos(uint64_t nchunks) {
+  return kHeader + pad128(8u * (kParts * nchunks + 1u));
+}
+__host__ __device__ inline uint64_t rans_pay_pos(uint64_t n, uint64_t nchunks, bool ciera) {
+  return rans_sm_pos(nchunks) + pad128(n) + (ciera ? 128u * nchunks : 0u);
+}
+
+// The block's ready flag and inclusive prefix or own size, as in the
+// single-read encode: kFlagSize | padded payload bytes, then kFlagIncl |
+// payload bytes of the parts up to and including it.
+__device__ inline bool part_lookback(const uint64_t* rstat, uint64_t p, uint64_t& before) {
+  const uint32_t lane = lane_id();
+  before = 0;
+  int64_t top = int64_t(p) - 1;
+  uint32_t spins = 0;
+  while (top >= 0) {
+    const int64_t k = top - int64_t(lane);
+    const uint64_t st = (k >= 0) ? load_relaxed(&rstat[k]) : kFlagIncl;
+    const uint64_t flag = st & ~kValMask;
+    if (__ballot(flag == 0u) != 0u) {
+      if (++spins > kSpinLimit) return false;
+      __builtin_amdgcn_s_sleep(1);
+      continue;
+    }
+    const uint64_t incl = __ballot(flag == kFlagIncl);
+    if (incl != 0u) {
+      const uint32_t first = uint32_t(__builtin_ctzll(incl));
+      before += wave_sum_u64(lane <= first ? (st & kValMask) : 0u);
+      return true;
+    }
+    before += wave_sum_u64(st & kValMask);
+    top -= 64;
+  }
+  return true;
+}
+
+// Block-wide (256 threads) sum and inclusive scan of u32 values.
+__device__ inline uint32_t part_sum_u32(uint32_t v, uint32_t* s_w) {
+  v = wave_sum_u32(v);
+  __syncthreads();
+  if (lane_id() == 0u) s_w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPartWaves; w++) t += s_w[w];
+  return t;
+}
+__device__ inline uint32_t part_incl_scan_u32(uint32_t v, uint32_t* s_w) {
+  const uint32_t incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane_id() == 63u) s_w[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPartWaves; w++) before += (w < (threadIdx.x >> 6)) ? s_w[w] : 0u;
+  return before + incl;
+}
+
+// x div f and x mod f for x < 2^32, 1 <= f <= 4096, by the FP64 reciprocal:
+// x * rcp is within 2^-20 of x / f, and x / f is at least 1/f from the next
+// integer above it, so the floor is the quotient or one less.
+__device__ inline uint32_t div_by_freq(uint32_t x, uint32_t f, double rcp, uint32_t& rem) {
+  uint32_t q = uint32_t(double(x) * rcp);
+  uint32_t r = x - q * f;
+  if (r >= f) {
+    q++;
+    r -= f;
+  }
+  rem = r;
+  return q;
+}
+
+template <bool kCiera>
+__global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __restrict__ x, uint64_t n,
+                                                           uint32_t log2B, uint8_t* __restrict__ out, Ws ws) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_sym[kPartValues];
+  __shared__ uint32_t s_f[kBins], s_cum[kBins];
+  __shared__ double s_rcp[kBins];
+  __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
+  __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
+  __shared__ uint32_t s_w[kPartWaves];
+  __shared__ uint32_t s_lohi, s_ok;
+  __shared__ uint64_t s_start, s_bytes;
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t p = blockIdx.x;
+  const uint64_t c = p / kParts;
+  const uint32_t h = p % kParts;
+  const uint64_t nchunks = cdiv(n, kChunk);
+  const uint32_t B = kCiera ? (1u << log2B) : 0u;
+  const uint64_t start = c * kChunk;
+  const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
+  const uint32_t nunits = (nc + 7u) / 8u;
+  const uint32_t pu0 = h * kPartUnits;
+  const uint64_t sm_pos = rans_sm_pos(nchunks);
+
+  Unit v[kUPT];
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
+    v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
+    if (u < nunits) v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+  }
+  if (kCiera && tid < 64u)
+    stage_bitmap((tid < kBitmapWords) ? chunk_bitmap_word(ws.bitmap + c * kBitmapWords, tid, B) : 0u, s_bits,
+                 s_rank);
+  __syncthreads();
+
+  // sign+mantissa bytes to their fixed place; coded values per unit
+  uint32_t cnt[kUPT], base[kUPT];
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
+    cnt[j] = 0u;
+    if (u < nunits) {
+      store_bytes8(out + sm_pos + start + 8ull * u, min(8u, nc - 8u * u), unit_sm(v[j]));
+      bool coded = true;
+      if (kCiera) {
+        const uint32_t blk = (8u * u) >> log2B;
+        coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
+      }
+      cnt[j] = coded ? min(8u, nc - 8u * u) : 0u;
+    }
+  }
+  const uint32_t m = part_escape_scan(cnt, base, s_tot);
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    if (cnt[j]) {
+      const uint2 e = unit_exponents(v[j]);
+      for (uint32_t k = 0; k < cnt[j]; k++) s_sym[base[j] + k] = uint8_t(byte_of(e, k));
+    }
+  }
+
+  // frequencies from the part's histogram row (one symbol per thread)
+  const uint32_t hs = (m != 0u) ? ws.hist[uint64_t(p) * kBins + tid] : 0u;
+  const uint32_t hsum = part_sum_u32(hs, s_w);
+  const uint32_t d = part_sum_u32(hs ? 1u : 0u, s_w);
+  // most frequent symbol, the lowest on ties: max of (h << 8) | (255 - s)
+  uint32_t key = (hs << 8) | (255u - tid);
+  for (uint32_t o = 32; o >= 1; o >>= 1) key = max(key, uint32_t(__shfl_xor(int(key), int(o))));
+  __syncthreads();
+  if (lane == 0u) s_w[wave] = key;
+  __syncthreads();
+  key = max(max(s_w[0], s_w[1]), max(s_w[2], s_w[3]));
+  const uint32_t top = 255u - (key & 0xFFu);
+  uint32_t f = 0;
+  if (hs) {
+    f = uint32_t(uint64_t(hs) * (kRansM - d) / max(hsum, 1u));
+    if (f == 0u) f = 1u;
+  }
+  const uint32_t fsum = part_sum_u32(f, s_w);
+  if (tid == top) f += kRansM - fsum;
+  const uint32_t cum_incl = part_incl_scan_u32(f, s_w);
+  s_f[tid] = f;
+  s_cum[tid] = cum_incl - f;
+  s_rcp[tid] = f ? 1.0 / double(f) : 0.0;
+  // first and last symbol with f > 0
+  const uint32_t lo_key = f ? tid : 255u, hi_key = f ? tid : 0u;
+  uint32_t lo = lo_key, hi = hi_key;
+  for (uint32_t o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, uint32_t(__shfl_xor(int(lo), int(o))));
+    hi = max(hi, uint32_t(__shfl_xor(int(hi), int(o))));
+  }
+  __syncthreads();
+  if (lane == 0u) s_w[wave] = lo | (hi << 16);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t l = 255u, u = 0u;
+    for (uint32_t w = 0; w < kPartWaves; w++) {
+      l = min(l, s_w[w] & 0xFFFFu);
+      u = max(u, s_w[w] >> 16);
+    }
+    s_lohi = l | (u << 8);
+    s_ok = (hsum == m) ? 1u : 0u;  // the histogram counted exactly the coded values
+  }
+  __syncthreads();
+  const bool ok = s_ok != 0u;
+
+  // wave 0 codes the m symbols with 64 states, last step first, into the
+  // part's scratch slot from its end
+  uint8_t* slot = ws.rslot + uint64_t(p) * kRansSlot;
+  uint16_t* slot16 = reinterpret_cast<uint16_t*>(slot);
+  if (wave == 0 && m && ok) {
+    uint32_t xs = kRansL;
+    uint32_t wpos = kRansSlot / 2u;
+    const uint64_t below = (1ull << lane) - 1u;
+    for (int64_t t = int64_t(cdiv(m, kRansStates)) - 1; t >= 0; t--) {
+      const uint32_t i = uint32_t(t) * kRansStates + lane;
+      const bool act = i < m;
+      const uint32_t sym = act ? s_sym[i] : 0u;
+      const uint32_t fs = s_f[sym], cs = s_cum[sym];
+      const double rs = s_rcp[sym];
+      const bool emit = act && uint64_t(xs) >= (uint64_t(fs) << 20);
+      const uint64_t mk = __ballot(emit);
+      const uint32_t ne = uint32_t(__popcll(mk));
+      if (emit) {
+        slot16[wpos - ne + uint32_t(__popcll(mk & below))] = uint16_t(xs & 0xFFFFu);
+        xs >>= 16;
+      }
+      wpos -= ne;
+      if (act) {
+        uint32_t r;
+        const uint32_t q = div_by_freq(xs, fs, rs, r);
+        xs = q * kRansM + r + cs;
+      }
+    }
+    wpos -= 2u * kRansStates;
+    slot16[wpos + 2u * lane] = uint16_t(xs & 0xFFFFu);
+    slot16[wpos + 2u * lane + 1u] = uint16_t(xs >> 16);
+    const uint32_t lo_s = s_lohi & 0xFFu, hi_s = s_lohi >> 8;
+    const uint32_t span = hi_s - lo_s + 1u;
+    const uint32_t nwords = kRansSlot / 2u - wpos;
+    const uint32_t beg = 2u * wpos - 8u - 2u * span;  // payload start in the slot (even)
+    for (uint32_t k = lane; k < span; k += 64u) slot16[beg / 2u + 4u + k] = uint16_t(s_f[lo_s + k]);
+    if (lane == 0) {
+      slot16[beg / 2u] = uint16_t(lo_s | (hi_s << 8));
+      slot16[beg / 2u + 1u] = 0u;
+      slot16[beg / 2u + 2u] = uint16_t(nwords & 0xFFFFu);
+      slot16[beg / 2u + 3u] = uint16_t(nwords >> 16);
+      s_start = beg;
+      s_bytes = 8u + 2u * span + 2u * nwords;
+    }
+  }
+  if (tid == 0 && !(m && ok)) {
+    s_start = 0;
+    s_bytes = 0;
+  }
+  __syncthreads();
+  const uint64_t bytes = s_bytes, padded = pad128(bytes);
+
+  // offset: publish the padded size, look back over the parts before
+  if (tid == 0) store_relaxed(&ws.rstat[p], kFlagSize | padded);
+  __shared__ uint64_t s_before;
+  __shared__ uint32_t s_found;
+  if (wave == 0) {
+    uint64_t before = 0;
+    const bool found = part_lookback(ws.rstat, p, before);
+    if (lane == 0) {
+      s_before = before;
+      s_found = found ? 1u : 0u;
+      if (found) store_relaxed(&ws.rstat[p], kFlagIncl | (before + padded));
+    }
+  }
+  __syncthreads();
+  const uint32_t err = (!ok) ? uint32_t(CIERA_ERR_INTERNAL) : (s_found ? 0u : uint32_t(CIERA_ERR_INTERNAL));
+  if (tid == 0) ws.err[p] = err;
+  if (err) return;
+  const uint64_t pay_pos = rans_pay_pos(n, nchunks, kCiera);
+  const uint64_t at = pay_pos + s_before;
+  uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
+  if (tid == 0) {
+    table[p] = at;
+    ws.rinfo[p] = uint64_t(m) | (uint64_t((h == kParts - 1u && kCiera) ? s_rank[kBitmapWords - 1] +
+                                                                            __popc(s_bits[kBitmapWords - 1])
+                                                                      : 0u)
+                                 << 32);
+    if (p + 1u == gridDim.x) table[p + 1u] = at + padded;
+  }
+  // copy the payload (2-byte aligned in the slot) and zero the padding
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(slot + s_start);
+  uint16_t* dst = reinterpret_cast<uint16_t*>(out + at);
+  for (uint32_t k = tid; k < bytes / 2u; k += kPartThreads) dst[k] = src[k];
+  for (uint64_t k = bytes + tid; k < padded; k += kPartThreads) out[at + k] = 0u;
+  // the chunk's bitmap (its last part)
+  if (kCiera && h == kParts - 1u && tid < kBitmapWords)
+    *reinterpret_cast<uint32_t*>(out + sm_pos + pad128(n) + 128u * c + 4u * tid) = s_bits[tid];
+}
+
+// Header and the part table's padding; the totals of coded symbols and
+// changed blocks from the parts' records.  One workgroup.
+__global__ __launch_bounds__(kThreads) void k_rans_finish(uint64_t n, uint64_t nchunks, uint32_t B,
+                                                          uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
+                                                          Ws ws) {
+  __shared__ uint64_t s_m[kThreads / 64u], s_c[kThreads / 64u];
+  const uint32_t tid = threadIdx.x;
+  const uint64_t P = kParts * nchunks;
+  uint64_t* hd = reinterpret_cast<uint64_t*>(out);
+  uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
+  if (tid == 0) ws.ctrl->n_err_slots = P;
+  uint64_t m = 0, ch = 0;
+  for (uint64_t i = tid; i < P; i += kThreads) {
+    const uint64_t r = ws.rinfo[i];
+    m += r & 0xFFFFFFFFu;
+    ch += r >> 32;
+  }
+  m = wave_sum_u64(m);
+  ch = wave_sum_u64(ch);
+  if (lane_id() == 0u) {
+    s_m[tid >> 6] = m;
+    s_c[tid >> 6] = ch;
+  }
+  const uint64_t sm_pos = rans_sm_pos(nchunks);
+  for (uint64_t i = P + 1u + tid; i < (sm_pos - kHeader) / 8u; i += kThreads) table[i] = 0u;
+  __syncthreads();
+  if (tid == 0) {
+    uint64_t tm = 0, tc = 0;
+    for (uint32_t w = 0; w < kThreads / 64u; w++) {
+      tm += s_m[w];
+      tc += s_c[w];
+    }
+    const bool ciera = B != 0u;
+    if (P == 0u) table[0] = rans_pay_pos(n, nchunks, ciera);
+    const uint64_t total = table[P];
+    const uint32_t magic = ciera ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
+    hd[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(ciera ? 3u : 2u) << 48);
+    hd[1] = n;
+    hd[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
+    hd[3] = nchunks;
+    hd[4] = total;
+    hd[5] = tc;
+    hd[6] = tm;
+    for (int i = 7; i < 16; i++) hd[i] = 0u;
+    *out_size = total;
+    // zero padding after the sign+mantissa bytes
+    for (uint64_t i = sm_pos + n; i < sm_pos + pad128(n); i++) out[i] = 0u;
+  }
+}
+
+template <bool kCiera>
+__global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __restrict__ in, uint64_t in_size,
+                                                           uint16_t* __restrict__ y, uint64_t n, uint64_t nchunks,
+                                                           uint32_t log2B, uint8_t* __restrict__ cache,
+                                                           uint64_t* __restrict__ n_err_slots,
+                                                           uint32_t* __restrict__ err_slots) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kRansStage];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sym[kPartValues];
+  __shared__ uint8_t s_map[kRansM];
+  __shared__ uint32_t s_f[kBins], s_cum[kBins];
+  __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
+  __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
+  __shared__ uint32_t s_w[kPartWaves];
+  __shared__ uint32_t s_ok;
+  __shared__ uint64_t s_a, s_b;
+  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t p = blockIdx.x;
+  const uint64_t c = p / kParts;
+  const uint32_t h = p % kParts;
+  const uint32_t B = kCiera ? (1u << log2B) : 0u;
+  const uint64_t P = kParts * nchunks;
+  const uint64_t sm_pos = rans_sm_pos(nchunks);
+  const uint64_t bm_pos = sm_pos + pad128(n);
+  const uint64_t pay_pos = rans_pay_pos(n, nchunks, kCiera);
+  if (tid == 0) {
+    uint32_t ok = 1u;
+    uint64_t a = 0, b = 0;
+    const uint64_t* hd = reinterpret_cast<const uint64_t*>(in);
+    if (in_size < pay_pos) {
+      ok = 0u;
+    } else {
+      const uint32_t magic = kCiera ? 0x52454943u : 0x3350495Au;
+      ok &= hd[0] == (uint64_t(magic) | (1ull << 32) | (uint64_t(kCiera ? 3u : 2u) << 48));
+      ok &= hd[1] == n;
+      ok &= hd[2] == (uint64_t(B) | (uint64_t(kChunk) << 32));
+      ok &= hd[3] == nchunks;
+      ok &= hd[4] == in_size;
+      for (int i = 7; i < 16; i++) ok &= hd[i] == 0u;
+      const uint64_t* table = reinterpret_cast<const uint64_t*>(in + kHeader);
+      ok &= table[0] == pay_pos && table[P] == in_size;
+      if (ok && P > 0u) {
+        a = table[p];
+        b = table[p + 1u];
+        ok &= a >= pay_pos && a <= b && b <= in_size && ((a | b) & 127u) == 0u;
+      }
+    }
+    s_ok = ok;
+    s_a = a;
+    s_b = b;
+    if (p == 0u) *n_err_slots = gridDim.x;
+  }
+  __syncthreads();
+  if (!s_ok || P == 0u) {  // an empty tensor: the header and table are all there is
+    if (tid == 0) err_slots[p] = s_ok ? 0u : uint32_t(CIERA_ERR_FORMAT);
+    return;
+  }
+  const uint64_t a = s_a, b = s_b;
+  const uint64_t start = c * kChunk;
+  const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
+  const uint32_t nunits = (nc + 7u) / 8u;
+  const uint32_t pu0 = h * kPartUnits;
+  bool bad = false;
+  if (kCiera && tid < 64u) {
+    const uint32_t w = (tid < kBitmapWords) ? *reinterpret_cast<const uint32_t*>(in + bm_pos + 128u * c + 4u * tid) : 0u;
+    // no bit past the chunk's last block
+    const uint32_t nb = (nc + B - 1u) >> log2B;
+    const uint32_t lo_bit = 32u * tid;
+    const uint32_t valid = (lo_bit >= nb) ? 0u : ((nb - lo_bit >= 32u) ? ~0u : ((1u << (nb - lo_bit)) - 1u));
+    if (w & ~valid) bad = true;
+    stage_bitmap(w, s_bits, s_rank);
+  }
+  // sign+mantissa bytes, and the receiver cache of unchanged units
+  uint2 sm[kUPT], old[kUPT];
+  uint32_t cnt[kUPT], base[kUPT];
+  __syncthreads();
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
+    cnt[j] = 0u;
+    sm[j] = old[j] = make_uint2(0u, 0u);
+    if (u < nunits) {
+      const uint32_t k = min(8u, nc - 8u * u);
+      sm[j] = load_bytes8(in + sm_pos + start + 8ull * u, k);
+      bool coded = true;
+      if (kCiera) {
+        const uint32_t blk = (8u * u) >> log2B;
+        coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
+        if (!coded) old[j] = load_bytes8(cache + start + 8ull * u, k);
+      }
+      cnt[j] = coded ? k : 0u;
+    }
+  }
+  const uint32_t m = part_escape_scan(cnt, base, s_tot);
+  const uint64_t len_pad = b - a;
+  uint32_t nwords = 0, lo = 0, hi = 0;
+  uint64_t len = 0;
+  if (m == 0u) {
+    bad |= len_pad != 0u;
+  } else if (len_pad < 8u) {
+    bad = true;
+  } else {
+    lo = in[a];
+    hi = in[a + 1];
+    nwords = uint32_t(in[a + 4]) | (uint32_t(in[a + 5]) << 8) | (uint32_t(in[a + 6]) << 16) |
+             (uint32_t(in[a + 7]) << 24);
+    len = 8u + 2u * uint64_t(hi >= lo ? hi - lo + 1u : 0u) + 2u * uint64_t(nwords);
+    bad |= hi < lo || in[a + 2] != 0u || in[a + 3] != 0u || nwords < 2u * kRansStates || pad128(len) != len_pad;
+  }
+  if (part_sum_u32(bad ? 1u : 0u, s_w) != 0u) {
+    if (tid == 0) err_slots[p] = uint32_t(CIERA_ERR_FORMAT);
+    return;
+  }
+  const uint32_t span = hi - lo + 1u;
+  const uint64_t wbyte = 8u + 2u * span;  // the words' offset in the payload
+  bool pad_bad = false;
+  if (m) {
+    // stage the payload's first kRansStage bytes (16-byte loads), check the padding
+    const uint64_t stage = min(len_pad, uint64_t(kRansStage));
+    for (uint64_t k = 16u * tid; k < stage; k += 16u * kPartThreads)
+      *reinterpret_cast<uint4*>(s_stage + k) = *reinterpret_cast<const uint4*>(in + a + k);
+    for (uint64_t k = len + tid; k < len_pad; k += kPartThreads) pad_bad |= in[a + k] != 0u;
+  }
+  __syncthreads();
+  // frequencies (one symbol per thread) and the slot -> symbol map
+  uint32_t f = 0;
+  if (m && tid >= lo && tid <= hi) {
+    const uint64_t o = 8u + 2u * (tid - lo);
+    f = (o + 1u < kRansStage) ? (uint32_t(s_stage[o]) | (uint32_t(s_stage[o + 1]) << 8))
+                              : (uint32_t(in[a + o]) | (uint32_t(in[a + o + 1]) << 8));
+  }
+  const uint32_t fsum = part_sum_u32(f, s_w);
+  const uint32_t cum_incl = part_incl_scan_u32(f, s_w);
+  s_f[tid] = f;
+  s_cum[tid] = cum_incl - f;
+  __syncthreads();
+  const bool table_ok = (m == 0u) || fsum == kRansM;
+  if (m && table_ok) {
+    for (uint32_t k = tid; k < kRansM; k += kPartThreads) {
+      // the symbol whose range [cum, cum + f) holds slot k: the first s with cum_s + f_s > k
+      uint32_t lo_s = 0, hi_s = 255u;
+      while (lo_s < hi_s) {
+        const uint32_t mid = (lo_s + hi_s) >> 1;
+        if (s_cum[mid] + s_f[mid] > k) hi_s = mid; else lo_s = mid + 1u;
+      }
+      s_map[k] = uint8_t(lo_s);
+    }
+  }
+  __syncthreads();
+  // wave 0 decodes the 64 states
+  __shared__ uint32_t s_dec_ok;
+  if (wave == 0) {
+    bool okd = table_ok;
+    if (m && okd) {
+      auto word = [&](uint64_t k) -> uint32_t {  // payload word k of the words region
+        const uint64_t o = wbyte + 2u * k;
+        return (o + 1u < kRansStage) ? (uint32_t(s_stage[o]) | (uint32_t(s_stage[o + 1]) << 8))
+                                     : (uint32_t(in[a + o]) | (uint32_t(in[a + o + 1]) << 8));
+      };
+      uint32_t xs = word(2u * lane) | (word(2u * lane + 1u) << 16);
+      okd = xs >= kRansL;
+      uint64_t q = 2u * kRansStates;
+      const uint64_t below = (1ull << lane) - 1u;
+      const uint32_t steps = uint32_t(cdiv(m, kRansStates));
+      for (uint32_t t = 0; t < steps; t++) {
+        const uint32_t i = t * kRansStates + lane;
+        const bool act = i < m;
+        uint32_t sym = 0;
+        if (act) {
+          const uint32_t slotv = xs & (kRansM - 1u);
+          sym = s_map[slotv];
+          xs = s_f[sym] * (xs >> 12) + slotv - s_cum[sym];
+        }
+        const bool need = act && xs < kRansL;
+        const uint64_t mk = __ballot(need);
+        if (need) {
+          const uint64_t k = q + uint64_t(__popcll(mk & below));
+          if (k < nwords) xs = (xs << 16) | word(k); else okd = false;
+        }
+        q += uint64_t(__popcll(mk));
+        if (act) s_sym[i] = uint8_t(sym);
+      }
+      okd = okd && q == nwords && xs == kRansL;
+    }
+    const bool all_ok = __ballot(!okd) == 0u;
+    if (lane == 0) s_dec_ok = all_ok ? 1u : 0u;
+  }
+  __syncthreads();
+  const bool dec_ok = s_dec_ok != 0u && part_sum_u32(pad_bad ? 1u : 0u, s_w) == 0u;
+  if (!dec_ok) {
+    if (tid == 0) err_slots[p] = uint32_t(CIERA_ERR_FORMAT);
+    return;
+  }
+  // merge: exponents from the decoded symbols (coded units) or the cache
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    const uint32_t u = pu0 + j * kPartThreads + tid;
+    if (u >= nunits) continue;
+    const uint32_t k = min(8u, nc - 8u * u);
+    uint2 e = old[j];
+    if (cnt[j]) {
+      uint32_t lo4 = 0, hi4 = 0;
+      for (uint32_t q = 0; q < k; q++) {
+        const uint32_t sb = s_sym[base[j] + q];
+        if (q < 4u) lo4 |= sb << (8u * q); else hi4 |= sb << (8u * (q - 4u));
+      }
+      e = make_uint2(lo4, hi4);
+      if (kCiera) store_bytes8(cache + start + 8ull * u, k, e);
+    }
+    store_unit(y, start + 8ull * u, k, unit_join(sm[j], e));
+  }
+  if (tid == 0) err_slots[p] = 0u;
+}
+
 // ------------------------------------------------------------------ host side
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0u; }
 
@@ -2178,6 +2748,88 @@ ciera_status encode_known_e0_impl(const void* d_x, uint64_t n, const uint8_t* d_
   return launch_status();
 }
 
+// rANS modes: the workspace of the 3-bit path followed by, per part, the
+// look-back word, the coded-count record and a payload scratch slot.
+uint64_t rans_ws_size(uint64_t n) {
+  const uint64_t nchunks = cdiv(n, kChunk), P = kParts * nchunks;
+  return ws_layout(nchunks).total + 2u * align256(8u * P) + P * uint64_t(kRansSlot);
+}
+
+Ws rans_ws_bind(void* base, uint64_t n) {
+  const uint64_t nchunks = cdiv(n, kChunk), P = kParts * nchunks;
+  Ws w = ws_bind(base, nchunks);
+  uint8_t* b = static_cast<uint8_t*>(base) + ws_layout(nchunks).total;
+  w.rstat = reinterpret_cast<uint64_t*>(b);
+  w.rinfo = reinterpret_cast<uint64_t*>(b + align256(8u * P));
+  w.rslot = b + 2u * align256(8u * P);
+  return w;
+}
+
+uint64_t rans_max_size(uint64_t n, uint32_t B) {
+  const uint64_t nchunks = cdiv(n, kChunk);
+  uint64_t size = rans_pay_pos(n, nchunks, B != 0u);
+  const uint64_t full = n / kPartValues, rem = n % kPartValues;
+  size += full * uint64_t(kRansSlot);
+  if (rem) size += pad128(8u + 512u + 256u + 2u * rem);
+  return size;
+}
+
+ciera_status encode_rans_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cache, void* d_out,
+                              uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                              hipStream_t stream) {
+  const bool ciera = B != 0u;
+  if (n > kMaxN) return CIERA_ERR_ARG;
+  if (ciera && !valid_block(B)) return CIERA_ERR_ARG;
+  if (!d_out || !d_ws || !d_out_size || !aligned16(d_out) || !aligned16(d_ws)) return CIERA_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_out_size) & 7u) != 0u) return CIERA_ERR_ARG;
+  if (n > 0 && (!d_x || !aligned16(d_x))) return CIERA_ERR_ARG;
+  if (ciera && n > 0 && (!d_cache || !aligned16(d_cache))) return CIERA_ERR_ARG;
+  if (out_capacity < rans_max_size(n, B)) return CIERA_ERR_CAPACITY;
+  if (ws_bytes < rans_ws_size(n)) return CIERA_ERR_WORKSPACE;
+  const uint64_t nchunks = cdiv(n, kChunk);
+  const Ws ws = rans_ws_bind(d_ws, n);
+  const uint32_t lb = ciera ? log2u(B) : 0u;
+  const uint16_t* x = static_cast<const uint16_t*>(d_x);
+  uint8_t* out = static_cast<uint8_t*>(d_out);
+  const uint32_t parts = uint32_t(nchunks * kParts);
+  (void)hipGetLastError();
+  if (nchunks) {
+    if (ciera) {
+      launch(k_stats<true, false>, dim3(parts), dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
+      launch(k_rans_enc<true>, dim3(parts), dim3(kPartThreads), stream, x, n, lb, out, ws);
+    } else {
+      launch(k_stats<false, false>, dim3(parts), dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
+      launch(k_rans_enc<false>, dim3(parts), dim3(kPartThreads), stream, x, n, 0u, out, ws);
+    }
+  }
+  launch(k_rans_finish, dim3(1), dim3(kThreads), stream, n, nchunks, B, out, d_out_size, ws);
+  return launch_status();
+}
+
+ciera_status decode_rans_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, uint32_t B,
+                              uint8_t* d_cache, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
+  const bool ciera = B != 0u;
+  if (n > kMaxN) return CIERA_ERR_ARG;
+  if (ciera && !valid_block(B)) return CIERA_ERR_ARG;
+  if (!d_in || !d_ws || !aligned16(d_in) || !aligned16(d_ws)) return CIERA_ERR_ARG;
+  if (n > 0 && (!d_y || !aligned16(d_y))) return CIERA_ERR_ARG;
+  if (ciera && n > 0 && (!d_cache || !aligned16(d_cache))) return CIERA_ERR_ARG;
+  const uint64_t nchunks = cdiv(n, kChunk);
+  if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
+  const Ws ws = ws_bind(d_ws, nchunks);
+  const uint32_t grid = uint32_t(nchunks ? nchunks * kParts : 1u);
+  const uint8_t* in = static_cast<const uint8_t*>(d_in);
+  uint16_t* y = static_cast<uint16_t*>(d_y);
+  (void)hipGetLastError();
+  if (ciera)
+    launch(k_rans_dec<true>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, log2u(B), d_cache,
+           &ws.ctrl->n_err_slots, ws.err);
+  else
+    launch(k_rans_dec<false>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, 0u, nullptr,
+           &ws.ctrl->n_err_slots, ws.err);
+  return launch_status();
+}
+
 ciera_status decode_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, uint32_t B,
                          uint8_t* d_cache, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
   const bool ciera = B != 0u;
@@ -2248,6 +2900,37 @@ ciera_status ciera_encode_ex(const void* d_x, uint64_t n, uint32_t B, uint8_t* d
   if (B == 0u) return CIERA_ERR_ARG;
   return encode_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, d_ws, ws_bytes, d_out_size, e0_override,
                      plan_groups, stream);
+}
+
+uint64_t rans_max_encoded_size(uint64_t n, uint32_t B) {
+  return (n > kMaxN || (B && !valid_block(B))) ? 0u : rans_max_size(n, B);
+}
+
+uint64_t rans_workspace_size(uint64_t n, uint32_t B) {
+  return (n > kMaxN || (B && !valid_block(B))) ? 0u : rans_ws_size(n);
+}
+
+ciera_status zip3_encode_rans(const void* d_x, uint64_t n, void* d_out, uint64_t out_capacity, void* d_ws,
+                              uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream) {
+  return encode_rans_impl(d_x, n, 0u, nullptr, d_out, out_capacity, d_ws, ws_bytes, d_out_size, stream);
+}
+
+ciera_status zip3_decode_rans(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, void* d_ws,
+                              uint64_t ws_bytes, hipStream_t stream) {
+  return decode_rans_impl(d_in, in_size, d_y, n, 0u, nullptr, d_ws, ws_bytes, stream);
+}
+
+ciera_status ciera_encode_rans(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, void* d_out,
+                               uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                               hipStream_t stream) {
+  if (B == 0u) return CIERA_ERR_ARG;
+  return encode_rans_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, d_ws, ws_bytes, d_out_size, stream);
+}
+
+ciera_status ciera_decode_rans(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, uint32_t B,
+                               uint8_t* d_prev_exp, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
+  if (B == 0u) return CIERA_ERR_ARG;
+  return decode_rans_impl(d_in, in_size, d_y, n, B, d_prev_exp, d_ws, ws_bytes, stream);
 }
 
 uint64_t ciera_hash_cache_size(uint64_t n, uint32_t B) {

@@ -230,3 +230,82 @@ def check_encode_hashed(x, B, prev_exps):
                              f"(gpu size {g.size}): gpu {g[i:i + 16]} oracle {o[i:i + 16]}")
     assert np.array_equal(hc_after, oracle.block_hashes(x, B)), "hash cache after encode"
     return g, st
+
+
+def gpu_encode_rans(x, B=0, cache=None):
+    """rANS-mode encode on the GPU.  Returns (stream bytes, cache after)."""
+    n = x.size
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    cap = ciera.rans_max_encoded_size(n, B)
+    buf, out = _guarded_bytes(cap)
+    ws = torch.empty(ciera.rans_workspace_size(n, B), dtype=torch.uint8, device="cuda")
+    size = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    cd = None
+    if B:
+        cbuf, cd = _guarded_bytes(n)
+        cd.copy_(torch.from_numpy(cache))
+        ciera.ciera_encode_rans(xd, B, cd, out, ws, size)
+    else:
+        ciera.zip3_encode_rans(xd, out, ws, size)
+    torch.cuda.synchronize()
+    assert ciera.ciera_read_error(ws) == 0
+    sz = int(size.item())
+    assert 0 < sz <= cap
+    host = buf.cpu().numpy()
+    _check_guards(host, cap, "stream")
+    assert (host[GUARD + sz:GUARD + cap] == CANARY).all(), "write past the stream's end"
+    new_cache = None
+    if B:
+        ch = cbuf.cpu().numpy()
+        _check_guards(ch, n, "sender cache")
+        new_cache = ch[GUARD:GUARD + n].copy()
+    return host[GUARD:GUARD + sz].copy(), new_cache
+
+
+def gpu_decode_rans(stream_bytes, n, B=0, cache=None):
+    """rANS-mode decode on the GPU.  Returns (values, cache after, status)."""
+    inp = torch.from_numpy(np.ascontiguousarray(stream_bytes)).cuda()
+    ybuf, y = _guarded_bytes(2 * n)
+    ws_n = ciera.ciera_workspace_size(n, B) if B else ciera.zip3_workspace_size(n)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device="cuda")
+    yv = y.view(torch.int16)
+    cd = None
+    if B:
+        cbuf, cd = _guarded_bytes(n)
+        cd.copy_(torch.from_numpy(cache))
+        ciera.ciera_decode_rans(inp, stream_bytes.size, yv, B, cd, ws)
+    else:
+        ciera.zip3_decode_rans(inp, stream_bytes.size, yv, ws)
+    torch.cuda.synchronize()
+    status = ciera.ciera_read_error(ws)
+    host = ybuf.cpu().numpy()
+    _check_guards(host, 2 * n, "y")
+    new_cache = None
+    if B:
+        ch = cbuf.cpu().numpy()
+        _check_guards(ch, n, "receiver cache")
+        new_cache = ch[GUARD:GUARD + n].copy()
+    return host[GUARD:GUARD + 2 * n].copy().view(np.uint16), new_cache, status
+
+
+def check_rans(x, B=0, cache=None):
+    """GPU rANS encode == oracle rANS encode byte for byte (and the sender
+    caches), and GPU decode returns x (and the receiver cache).  Returns the
+    stream."""
+    g, gc = gpu_encode_rans(x, B, cache)
+    oc = cache.copy() if B else None
+    o, _ = oracle.encode_rans(x, B, oc)
+    if g.tobytes() != o.tobytes():
+        i = _first_diff(g, o)
+        raise AssertionError(f"rANS stream differs from the oracle at byte {i} of {o.size} "
+                             f"(gpu size {g.size}): gpu {g[i:i + 16]} oracle {o[i:i + 16]}")
+    if B:
+        assert np.array_equal(gc, oc), "sender cache differs from the oracle's"
+    y, rc, st = gpu_decode_rans(g, x.size, B, cache.copy() if B else None)
+    assert st == 0, f"rANS decode reported status {st}"
+    if not np.array_equal(y, x):
+        i = int(np.flatnonzero(y != x)[0])
+        raise AssertionError(f"rANS decode differs at value {i}: {y[i]:#06x} vs {x[i]:#06x}")
+    if B:
+        assert np.array_equal(rc, exps(x)), "receiver cache is not the decoded exponents"
+    return g

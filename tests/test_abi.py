@@ -78,6 +78,13 @@ def test_argument_errors_return_before_any_launch(lib):
     assert lib.ciera_encode_hashed(p, 10, 64, p, p, 10, p, 1 << 20, p, None) == 2
     assert lib.ciera_hash_cache_size(1000, 64) == 16 * 16
     assert lib.ciera_hash_cache_size(1000, 48) == 0
+    assert lib.zip3_encode_rans(p, 10, p, 10, p, 1 << 30, p, None) == 2
+    assert lib.zip3_encode_rans(p, 10, p, 1 << 20, p, 10, p, None) == 3
+    assert lib.ciera_encode_rans(p, 10, 0, p, p, 1 << 20, p, 1 << 30, p, None) == 1
+    assert lib.ciera_encode_rans(p, 10, 96, p, p, 1 << 20, p, 1 << 30, p, None) == 1
+    assert lib.ciera_decode_rans(p, 1 << 20, p, 10, 0, p, p, 1 << 20, None) == 1
+    assert lib.zip3_decode_rans(ctypes.c_void_p(16 * 1024 + 8), 1 << 20, p, 10, p, 1 << 20, None) == 1
+    assert lib.rans_max_encoded_size(1000, 48) == 0 and lib.rans_max_encoded_size(0, 0) == 256
     assert lib.ciera_time_kernels(None, 1) == 1
     assert lib.ciera_time_kernels(None, 0) == 0
 

@@ -1,0 +1,100 @@
+"""GPU parity of the rANS modes (zip3 + rANS, ciera + rANS): streams byte for
+byte equal to the oracle's, decode returns the input bit for bit, caches
+match, canary guards intact; malformed streams are rejected."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check_rans, exps, gpu_decode_rans, gpu_encode_rans, require_gpu, say
+from lossless_bf16_tensor_exp_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+SMALL_N = [0, 1, 7, 8, 9, 63, 64, 65, 1000, 16383, 16384, 16385, 65535, 65536, 65537, 3 * 65536 + 12345]
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+@pytest.mark.parametrize("n", SMALL_N)
+def test_zip3_rans_small(n):
+    say(f"zip3 rans n={n}")
+    rng = np.random.default_rng(3000 + n)
+    for _ in range(2):
+        check_rans(wl.mixed_small(rng, n))
+
+
+@pytest.mark.parametrize("B", [64, 256, 4096, 32768, 65536])
+@pytest.mark.parametrize("n", SMALL_N)
+def test_ciera_rans_small(n, B):
+    say(f"ciera rans n={n} B={B}")
+    rng = np.random.default_rng(4000 + n + B)
+    x = wl.mixed_small(rng, n)
+    check_rans(x, B, wl.perturbed_cache(rng, x, 0.01))
+    x2 = x.copy()
+    if n:
+        wl.flip(x2, rng.choice(n, size=max(1, n // 300), replace=False))
+    check_rans(x2, B, exps(x))
+
+
+@pytest.mark.parametrize("order", ["sorted", "shuffled"])
+def test_rans_all_patterns(order):
+    x = wl.all_bf16_patterns()
+    if order == "shuffled":
+        x = x[np.random.default_rng(8).permutation(x.size)]
+    check_rans(x)
+    check_rans(x, 512, np.zeros(x.size, dtype=np.uint8))
+
+
+@pytest.mark.parametrize("sigma", [1e-3, 0.02, 1.0])
+def test_rans_gaussian_many_chunks(sigma):
+    rng = np.random.default_rng(int(sigma * 1000) + 5)
+    x = wl.normal_bf16(rng, 37 * 65536 - 999, sigma)
+    check_rans(x)
+
+
+def test_rans_gradient_64M():
+    d = wl.workload2()
+    x = d["iters"][0]
+    say(f"rans workload2 n={x.size}")
+    s = check_rans(x)
+    t, _ = oracle.encode(x)
+    say(f"  rANS ratio {2 * x.size / s.size:.4f}, 3-bit ratio {2 * x.size / t.size:.4f}")
+    assert s.size < t.size
+
+
+def test_rans_olmoe_shard_B64():
+    d = wl.workload3()
+    x0, x1 = d["iters"]
+    say(f"rans workload3 n={x0.size}")
+    s = check_rans(x1, 64, exps(x0))
+    say(f"  rANS ratio {2 * x1.size / s.size:.4f}")
+
+
+def test_rans_decode_rejects_corruption():
+    rng = np.random.default_rng(6)
+    x = wl.normal_bf16(rng, 65536, 0.02)
+    s, _ = gpu_encode_rans(x)
+    a = int(s[128:136].view(np.uint64)[0])
+    nw = int(s[a + 4:a + 8].view(np.uint32)[0])
+    lo, hi = int(s[a]), int(s[a + 1])
+    words = a + 8 + 2 * (hi - lo + 1)
+    cases = {
+        "mode byte": (6, 0),
+        "nwords": (a + 4, (nw + 1) & 0xFF),
+        "frequency": (a + 8, s[a + 8] ^ 1),
+        "renormalisation word": (words + 256 + 20, s[words + 256 + 20] ^ 0x10),
+        "final state": (words + 3, s[words + 3] ^ 0x80),
+        "part table": (136, s[136] ^ 0x40),
+    }
+    for name, (at, val) in cases.items():
+        t = s.copy()
+        t[at] = val
+        with pytest.raises(oracle.OracleError):
+            oracle.decode_rans(t, x.size)
+        _, _, st = gpu_decode_rans(t, x.size)
+        assert st == 5, f"{name}: status {st}"
+    y, _, st = gpu_decode_rans(s, x.size)
+    assert st == 0 and np.array_equal(y, x)
