@@ -354,6 +354,52 @@ def main() -> int:
                   "cache_bytes": hsz, "stream_equal_to_exact_sender": same,
                   "kernels": {"k_stats": round(hk[0], 5), "k_plan": round(hk[1], 5), "k_write": round(hk[2], 5)}}
         del h_pristine, h_cache, out_h
+    # rANS modes: the same input and caches, the coded exponents range-ANS
+    # coded instead of the 3-bit code; encode and decode timed like pass 3,
+    # each kernel once more with events; the round trip checked on the GPU.
+    rans = None
+    rcap, rwsz = ciera.rans_max_encoded_size(n, B), ciera.rans_workspace_size(n, B)
+    out_r = torch.empty(rcap, dtype=torch.uint8, device=dev)
+    ws_r = torch.empty(rwsz, dtype=torch.uint8, device=dev)
+    size_r = torch.zeros(1, dtype=torch.int64, device=dev)
+    y_r = torch.empty_like(y)
+    if mode == "zip3":
+        enc_r = ciera.bind("zip3_encode_rans", xs[k_iso], n, out_r, rcap, ws_r, rwsz, size_r, stream=stream)
+    else:
+        enc_r = ciera.bind("ciera_encode_rans", xs[k_iso], n, B, send, out_r, rcap, ws_r, rwsz, size_r, stream=stream)
+    if mode != "zip3":
+        send.copy_(e_prev)
+    enc_r()
+    torch.cuda.synchronize()
+    assert ciera.ciera_read_error(ws_r) == 0
+    szr = int(size_r.item())
+    if mode == "zip3":
+        dec_r = ciera.bind("zip3_decode_rans", out_r, szr, y_r, n, ws_d, wsz, stream=stream)
+    else:
+        dec_r = ciera.bind("ciera_decode_rans", out_r, szr, y_r, n, B, recv, ws_d, wsz, stream=stream)
+    r_enc, r_enc_min = isolated(enc_r, send)
+    r_dec, r_dec_min = isolated(dec_r, recv)
+    assert ciera.ciera_read_error(ws_r) == 0 and ciera.ciera_read_error(ws_d) == 0
+    r_ok = bool(torch.equal(y_r, xs[k_iso]))
+    evr = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
+           for _ in range(K)]
+    ciera.ciera_time_kernels([pr for row in evr for pr in row], stream=stream)
+    for i in range(K):
+        if mode != "zip3":
+            send.copy_(e_prev)
+            recv.copy_(e_prev)
+        torch.sum(sweep, dim=0, out=sweep_out)
+        enc_r()
+        dec_r()
+    torch.cuda.synchronize()
+    ciera.ciera_time_kernels([])
+    rk = [sum(evr[i][j][0].elapsed_time(evr[i][j][1]) for i in range(K)) / K for j in range(4)]
+    rans = {"encode_ms": round(r_enc, 5), "encode_min_ms": round(r_enc_min, 5),
+            "decode_ms": round(r_dec, 5), "decode_min_ms": round(r_dec_min, 5),
+            "stream_bytes": szr, "roundtrip_ok": r_ok,
+            "kernels": {"k_stats": round(rk[0], 5), "k_rans_enc": round(rk[1], 5), "k_rans_finish": round(rk[2], 5),
+                        "k_rans_dec": round(rk[3], 5)}}
+    del out_r, ws_r, y_r
     del sweep
 
     if args.copy_probe:
@@ -407,6 +453,9 @@ def main() -> int:
         hashed["encode_algorithmic_bytes"] = alg_h
         hashed["encode_frac_of_measured_copy"] = round(alg_h / (hashed["encode_ms"] * 1e-3) / 1e9 / bw_copy, 4)
         hashed["blocks"] = nb
+    rans["compression_ratio"] = round(in_bytes / rans["stream_bytes"], 4)
+    rans["encode_GBps"] = round(in_bytes / (rans["encode_ms"] * 1e-3) / 1e9, 2)
+    rans["decode_GBps"] = round(in_bytes / (rans["decode_ms"] * 1e-3) / 1e9, 2)
     iso = {"method": "each call alone, MALL swept by a 1 GiB read before it; median (min) of K calls",
            "encode_ms": round(enc_iso, 5), "encode_min_ms": round(enc_iso_min, 5),
            "encode_GBps": round(in_bytes / (enc_iso * 1e-3) / 1e9, 2),
@@ -463,6 +512,7 @@ def main() -> int:
         "kernels": kernels,
         "isolated": iso,
         "hash_sender": hashed,
+        "rans": rans,
         "single_read_encode": single,
         "bw_measured_GBps": {"copy": round(bw_copy, 1), "read": round(bw_read, 1)},
         "roofline": roofline,
