@@ -242,9 +242,14 @@ __device__ inline Unit load_unit(const uint16_t* __restrict__ x, uint64_t first,
   return u;
 }
 
+// Decoded values: full units go out as non-temporal 16-byte stores, so that
+// the decoder's output does not sit dirty in the MALL (256 MB) and get
+// written back while the next kernel streams its own input.
 __device__ inline void store_unit(uint16_t* __restrict__ y, uint64_t first, uint32_t cnt, const Unit& u) {
   if (cnt == 8u) {
-    *reinterpret_cast<uint4*>(y + first) = make_uint4(u.w[0], u.w[1], u.w[2], u.w[3]);
+    typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+    const v4u val = {u.w[0], u.w[1], u.w[2], u.w[3]};
+    __builtin_nontemporal_store(val, reinterpret_cast<v4u*>(y + first));
   } else {
 #pragma unroll
     for (uint32_t i = 0; i < 4u; i++) {
