@@ -2174,6 +2174,7 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
                                                            uint32_t log2B, uint8_t* __restrict__ out, Ws ws) {
   __shared__ __attribute__((aligned(16))) uint8_t s_sym[kPartValues];
   __shared__ uint32_t s_f[kBins], s_cum[kBins];
+  __shared__ uint32_t s_fc[kBins];  // f | cum << 16
   __shared__ double s_rcp[kBins];
   __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
   __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
@@ -2251,6 +2252,7 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
   const uint32_t cum_incl = part_incl_scan_u32(f, s_w);
   s_f[tid] = f;
   s_cum[tid] = cum_incl - f;
+  s_fc[tid] = f | ((cum_incl - f) << 16);
   s_rcp[tid] = f ? 1.0 / double(f) : 0.0;
   // first and last symbol with f > 0
   const uint32_t lo_key = f ? tid : 255u, hi_key = f ? tid : 0u;
@@ -2282,12 +2284,26 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
     uint32_t xs = kRansL;
     uint32_t wpos = kRansSlot / 2u;
     const uint64_t below = (1ull << lane) - 1u;
-    for (int64_t t = int64_t(cdiv(m, kRansStates)) - 1; t >= 0; t--) {
+    // The symbols and their table entries do not depend on the states: the
+    // entries of step t - 1 and the symbol of step t - 2 are loaded while
+    // step t computes.
+    const int64_t steps = int64_t(cdiv(m, kRansStates));
+    auto sym_at = [&](int64_t t) -> uint32_t {
+      const int64_t i = t * int64_t(kRansStates) + int64_t(lane);
+      return (t >= 0 && i < int64_t(m)) ? uint32_t(s_sym[i]) : 0u;
+    };
+    uint32_t sym_c = sym_at(steps - 1);
+    uint32_t fc_c = s_fc[sym_c];
+    double rs_c = s_rcp[sym_c];
+    uint32_t sym_n = sym_at(steps - 2);
+    for (int64_t t = steps - 1; t >= 0; t--) {
       const uint32_t i = uint32_t(t) * kRansStates + lane;
       const bool act = i < m;
-      const uint32_t sym = act ? s_sym[i] : 0u;
-      const uint32_t fs = s_f[sym], cs = s_cum[sym];
-      const double rs = s_rcp[sym];
+      const uint32_t fc_n = s_fc[sym_n];
+      const double rs_n = s_rcp[sym_n];
+      const uint32_t sym_nn = sym_at(t - 2);
+      const uint32_t fs = fc_c & 0xFFFFu, cs = fc_c >> 16;
+      const double rs = rs_c;
       const bool emit = act && uint64_t(xs) >= (uint64_t(fs) << 20);
       const uint64_t mk = __ballot(emit);
       const uint32_t ne = uint32_t(__popcll(mk));
@@ -2301,6 +2317,9 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
         const uint32_t q = div_by_freq(xs, fs, rs, r);
         xs = q * kRansM + r + cs;
       }
+      fc_c = fc_n;
+      rs_c = rs_n;
+      sym_n = sym_nn;
     }
     wpos -= 2u * kRansStates;
     slot16[wpos + 2u * lane] = uint16_t(xs & 0xFFFFu);
@@ -2421,9 +2440,12 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
                                                            uint64_t* __restrict__ n_err_slots,
                                                            uint32_t* __restrict__ err_slots) {
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[kRansStage];
+  // decoded symbols; before decoding its first 2 KB hold f and cum per symbol
   __shared__ __attribute__((aligned(16))) uint8_t s_sym[kPartValues];
-  __shared__ uint8_t s_map[kRansM];
-  __shared__ uint32_t s_f[kBins], s_cum[kBins];
+  // per slot: symbol | (f - 1) << 8 | (slot - cum) << 20
+  __shared__ uint32_t s_dtab[kRansM];
+  uint32_t* s_f = reinterpret_cast<uint32_t*>(s_sym);
+  uint32_t* s_cum = s_f + kBins;
   __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
   __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
   __shared__ uint32_t s_w[kPartWaves];
@@ -2558,7 +2580,7 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
         const uint32_t mid = (lo_s + hi_s) >> 1;
         if (s_cum[mid] + s_f[mid] > k) hi_s = mid; else lo_s = mid + 1u;
       }
-      s_map[k] = uint8_t(lo_s);
+      s_dtab[k] = lo_s | ((s_f[lo_s] - 1u) << 8) | ((k - s_cum[lo_s]) << 20);
     }
   }
   __syncthreads();
@@ -2582,9 +2604,9 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
         const bool act = i < m;
         uint32_t sym = 0;
         if (act) {
-          const uint32_t slotv = xs & (kRansM - 1u);
-          sym = s_map[slotv];
-          xs = s_f[sym] * (xs >> 12) + slotv - s_cum[sym];
+          const uint32_t e = s_dtab[xs & (kRansM - 1u)];
+          sym = e & 0xFFu;
+          xs = (((e >> 8) & 0xFFFu) + 1u) * (xs >> 12) + (e >> 20);
         }
         const bool need = act && xs < kRansL;
         const uint64_t mk = __ballot(need);
