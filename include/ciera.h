@@ -231,8 +231,10 @@ ciera_status zip3_encode_e0(const void* d_x, uint64_t n, const uint8_t* d_e0, vo
 /* Kernel timing, a profiling aid (not part of the codec).  events holds
  * n_pairs (start, stop) pairs of hipEvent_t handles, created with timing
  * enabled and owned by the caller.  The next n_pairs kernel launches made by
- * the calling host thread through this library (any entry point: encode
- * launches three kernels, decode one) each take the next pair, which the HIP
+ * the calling host thread through this library (any entry point: the
+ * 3-bit encode launches three kernels and its decode one; the single-read
+ * encode two; the rANS encode three and its decode one) each take the next
+ * pair, which the HIP
  * runtime records at that kernel's start and end (hipExtLaunchKernel);
  * hipEventElapsedTime then gives the kernel's own duration.  The handles are
  * copied; a later call replaces the queue, n_pairs = 0 clears it.  Returns
