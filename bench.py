@@ -498,6 +498,18 @@ def main() -> int:
            "decode_GBps": round(in_bytes / (dec_iso * 1e-3) / 1e9, 2),
            "decode_algorithmic_bytes": alg_dec,
            "decode_frac_of_measured_copy": round(alg_dec / (dec_iso * 1e-3) / 1e9 / bw_copy, 4)}
+    # The same fractions with the bytes the HBM counters saw (FETCH_SIZE +
+    # WRITE_SIZE per launch, from the traffic summaries taken on this kernel
+    # source), null where no such record exists.
+    cnt = {nm: load_traffic(nm, args.workload, B) for nm in ("k_stats", "k_plan", "k_write", "k_decode")}
+    if all(v is not None for v in cnt.values()):
+        c_enc = cnt["k_stats"] + cnt["k_plan"] + cnt["k_write"]
+        iso["encode_counted_bytes"] = c_enc
+        iso["encode_frac_counted"] = round(c_enc / (enc_iso * 1e-3) / 1e9 / bw_copy, 4)
+        iso["decode_counted_bytes"] = cnt["k_decode"]
+        iso["decode_frac_counted"] = round(cnt["k_decode"] / (dec_iso * 1e-3) / 1e9 / bw_copy, 4)
+    else:
+        iso["encode_frac_counted"] = iso["decode_frac_counted"] = None
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -137,6 +137,16 @@ struct PlanSlot {
 };
 static_assert(sizeof(PlanSlot) == 64, "plan slot is 64 bytes");
 
+// Single-read look-back: each chunk's status word and its four part counts
+// sit on a 128-byte line of their own (strides in words).  Neighbouring
+// chunks are written and polled by workgroups on different XCDs; when they
+// shared lines, the line moved between the L2s on every write and the
+// single-read encode of a 64M-value tensor took a quarter longer.
+constexpr uint32_t kCstatStride = 16u;   // u64 words
+constexpr uint32_t kPcountStride = 32u;  // u32 words
+// rANS encode: the look-back word of each part, likewise on a line of its own.
+constexpr uint32_t kRstatStride = 16u;   // u64 words
+
 struct WsLayout {
   uint64_t err, partial, bitmap, hist, partesc, chunkesc, pcount, cstat, plan, phash, total;
 };
@@ -157,8 +167,8 @@ __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   l.partesc = align256(l.hist + 2u * kBins * kParts * slots);
   l.chunkesc = align256(l.partesc + 4u * kParts * slots);
   l.pcount = align256(l.chunkesc + 4u * slots);
-  l.cstat = align256(l.pcount + 4u * kParts * slots);
-  l.plan = align256(l.cstat + 8u * slots);
+  l.cstat = align256(l.pcount + 4u * kPcountStride * slots);
+  l.plan = align256(l.cstat + 8u * kCstatStride * slots);
   l.phash = align256(l.plan + sizeof(PlanSlot) * kPlanMaxGroups);
   l.total = align256(l.phash + 16u * kParts * slots);
   return l;
@@ -173,8 +183,8 @@ struct Ws {
   uint32_t* partesc;    // escapes before each part within its chunk
   uint32_t* chunkesc;   // escapes per chunk
   // single-read encode: look-back words
-  uint32_t* pcount;     // per part: kPartReady | escapes of the part
-  uint64_t* cstat;      // per chunk: flag | stream bytes (aggregate or inclusive prefix)
+  uint32_t* pcount;     // per part, kPcountStride per chunk: kPartReady | escapes of the part
+  uint64_t* cstat;      // per chunk, kCstatStride apart: flag | stream bytes (inclusive prefix)
   PlanSlot* plan;       // per k_plan workgroup
   uint64_t* phash;      // hash sender, blocks larger than a part: the part's two partial hashes
   // rANS modes only (null otherwise): per part a look-back word, its coded
@@ -554,7 +564,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   if (!kHash)
     for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
   if (tid < kPartBitmapWords) s_bits[tid] = 0u;
-  if (ws.rstat && tid == 0) ws.rstat[wg] = 0u;  // rANS encode: the part's look-back word, not ready
+  if (ws.rstat && tid == 0) ws.rstat[uint64_t(wg) * kRstatStride] = 0u;  // rANS encode: the part's look-back word, not ready
   if (blockIdx.x == 0u) {
     // k_plan's slots: the FP64 words empty, the count words not ready
     uint64_t* sw = reinterpret_cast<uint64_t*>(ws.plan);
@@ -1478,8 +1488,9 @@ __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks
   uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
   const uint64_t base = table_end(nchunks);
-  for (uint64_t i = tid; i < nchunks * kParts; i += kThreads) ws.pcount[i] = 0u;
-  for (uint64_t i = tid; i < nchunks; i += kThreads) ws.cstat[i] = 0u;
+  for (uint64_t i = tid; i < nchunks * kParts; i += kThreads)
+    ws.pcount[(i / kParts) * kPcountStride + i % kParts] = 0u;
+  for (uint64_t i = tid; i < nchunks; i += kThreads) ws.cstat[i * kCstatStride] = 0u;
   if (tid == 0) ws.ctrl->done_esc = 0u;
   // the padding words after the chunk table and the escape index
   for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
@@ -1519,12 +1530,12 @@ __device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint64_t& pb) {
   uint32_t spins = 0;
   while (top >= 0) {
     const int64_t k = top - int64_t(lane);
-    uint64_t st = (k >= 0) ? load_relaxed(&ws.cstat[k]) : kFlagIncl;
+    uint64_t st = (k >= 0) ? load_relaxed(&ws.cstat[uint64_t(k) * kCstatStride]) : kFlagIncl;
     if (k >= 0 && (st & ~kValMask) != kFlagIncl) {
       uint32_t esc = 0, ready = 1u;
 #pragma unroll
       for (uint32_t q = 0; q < kParts; q++) {
-        const uint32_t w = load_relaxed(&ws.pcount[uint64_t(k) * kParts + q]);
+        const uint32_t w = load_relaxed(&ws.pcount[uint64_t(k) * kPcountStride + q]);
         ready &= w >> 31;
         esc += w & ~kPartReady;
       }
@@ -1627,7 +1638,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     }
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
-  if (tid == 0) store_relaxed(&ws.pcount[wg], kPartReady | pesc);
+  if (tid == 0) store_relaxed(&ws.pcount[c * kPcountStride + h], kPartReady | pesc);
 
   // Stream position (wave 0).
   if (tid < 64u) {
@@ -1635,7 +1646,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     // escape counts of the chunk's four parts: lane l < 4 reads part l
     uint32_t cnt_l = 0u;
     for (uint32_t spins = 0;; spins++) {
-      const uint32_t w = (lane < kParts) ? load_relaxed(&ws.pcount[c * kParts + lane]) : kPartReady;
+      const uint32_t w = (lane < kParts) ? load_relaxed(&ws.pcount[c * kPcountStride + lane]) : kPartReady;
       if (__ballot(!(w & kPartReady)) == 0u) {
         cnt_l = w & ~kPartReady;
         break;
@@ -1661,7 +1672,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     if (last_part) {
       if (lane == 0u) {
         // published even after a failed wait, so that no later wait lasts forever
-        store_relaxed(&ws.cstat[c], kFlagIncl | (pb + size));
+        store_relaxed(&ws.cstat[c * kCstatStride], kFlagIncl | (pb + size));
         table[c] = tbl + pb;
         table[nchunks + 1u + c] = (uint64_t(e1) << 16) | (uint64_t(e2) << 32) | (uint64_t(e3) << 48);
         if (c + 1u == nchunks) {
@@ -2114,7 +2125,7 @@ __device__ inline bool part_lookback(const uint64_t* rstat, uint64_t p, uint64_t
   uint32_t spins = 0;
   while (top >= 0) {
     const int64_t k = top - int64_t(lane);
-    const uint64_t st = (k >= 0) ? load_relaxed(&rstat[k]) : kFlagIncl;
+    const uint64_t st = (k >= 0) ? load_relaxed(&rstat[uint64_t(k) * kRstatStride]) : kFlagIncl;
     const uint64_t flag = st & ~kValMask;
     if (__ballot(flag == 0u) != 0u) {
       if (++spins > kSpinLimit) return false;
@@ -2346,7 +2357,7 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
   const uint64_t bytes = s_bytes, padded = pad128(bytes);
 
   // offset: publish the padded size, look back over the parts before
-  if (tid == 0) store_relaxed(&ws.rstat[p], kFlagSize | padded);
+  if (tid == 0) store_relaxed(&ws.rstat[uint64_t(p) * kRstatStride], kFlagSize | padded);
   __shared__ uint64_t s_before;
   __shared__ uint32_t s_found;
   if (wave == 0) {
@@ -2355,7 +2366,7 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
     if (lane == 0) {
       s_before = before;
       s_found = found ? 1u : 0u;
-      if (found) store_relaxed(&ws.rstat[p], kFlagIncl | (before + padded));
+      if (found) store_relaxed(&ws.rstat[uint64_t(p) * kRstatStride], kFlagIncl | (before + padded));
     }
   }
   __syncthreads();
@@ -2779,7 +2790,7 @@ ciera_status encode_known_e0_impl(const void* d_x, uint64_t n, const uint8_t* d_
 // look-back word, the coded-count record and a payload scratch slot.
 uint64_t rans_ws_size(uint64_t n) {
   const uint64_t nchunks = cdiv(n, kChunk), P = kParts * nchunks;
-  return ws_layout(nchunks).total + 2u * align256(8u * P) + P * uint64_t(kRansSlot);
+  return ws_layout(nchunks).total + align256(8u * kRstatStride * P) + align256(8u * P) + P * uint64_t(kRansSlot);
 }
 
 Ws rans_ws_bind(void* base, uint64_t n) {
@@ -2787,8 +2798,8 @@ Ws rans_ws_bind(void* base, uint64_t n) {
   Ws w = ws_bind(base, nchunks);
   uint8_t* b = static_cast<uint8_t*>(base) + ws_layout(nchunks).total;
   w.rstat = reinterpret_cast<uint64_t*>(b);
-  w.rinfo = reinterpret_cast<uint64_t*>(b + align256(8u * P));
-  w.rslot = b + 2u * align256(8u * P);
+  w.rinfo = reinterpret_cast<uint64_t*>(b + align256(8u * kRstatStride * P));
+  w.rslot = b + align256(8u * kRstatStride * P) + align256(8u * P);
   return w;
 }
 
