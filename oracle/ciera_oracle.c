@@ -522,15 +522,17 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
  * 3.1: the sender ANS-encodes the changed exponents, the receiver
  * ANS-decodes them).  The page names no ANS parameters; this format is ours.
  *
- *  - Symbols: per part (a quarter chunk, values [16384 h, 16384 (h+1)) of
- *    the chunk), the exponent fields of its coded values in value order,
- *    s_0 .. s_{m-1}.
- *  - Frequencies: the part's histogram h over those symbols, normalised to
- *    M = 4096: with d distinct symbols, f_s = max(1, floor(h_s (M - d) / m))
- *    for every symbol present (0 otherwise), and the rest, M - sum f, is
- *    added to the most frequent symbol (the lowest one on ties).  c_s is
- *    the sum of f over the symbols below s.
- *  - Coding: 64 interleaved rANS states; symbol i goes to state i mod 64
+ *  - Symbols: the exponent fields of a chunk's coded values.  Part h of the
+ *    chunk (values [16384 h, 16384 (h+1)) of it) holds the coded ones among
+ *    its values, in value order: s_0 .. s_{m_h - 1}.
+ *  - Frequencies: one table per chunk, from the histogram h over all of its
+ *    m = m_0 + m_1 + m_2 + m_3 symbols, normalised to M = 4096: with d
+ *    distinct symbols, f_s = max(1, floor(h_s (M - d) / m)) for every
+ *    symbol present (0 otherwise), and the rest, M - sum f, is added to the
+ *    most frequent symbol (the lowest one on ties).  c_s is the sum of f
+ *    over the symbols below s.
+ *  - Coding: each part codes its own symbols with the chunk's table and 64
+ *    interleaved rANS states; symbol i of the part goes to state i mod 64
  *    (step i div 64).  A state is a 32-bit x in [2^16, 2^32), starting at
  *    2^16.  Encoding runs over the steps from last to first; a state about
  *    to code symbol s first emits its low 16 bits and shifts right by 16
@@ -538,19 +540,21 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
  *    Decoding runs forward: slot = x mod 2^12, s is the symbol whose range
  *    [c_s, c_s + f_s) holds slot, x becomes f_s (x div 2^12) + slot - c_s,
  *    and a state below 2^16 reads one 16-bit word: x = x 2^16 + word.
- *  - Part payload (little-endian): u8 lo, u8 hi (the first and last symbol
- *    with f > 0), u16 0, u32 nwords, then f_lo .. f_hi as u16, then nwords
- *    16-bit words: the 64 final encoder states (low half, high half, state
- *    0 first), then, step by step from the first, the words the encoder
- *    emitted at that step, in ascending state order.  A part without coded
- *    symbols has an empty payload.
- *  - Stream: the 128-byte header (mode 2 or 3, E0 = 0, bytes 48..55 the
- *    number of coded symbols); at byte 128 a part table of 4 nchunks + 1 u64
- *    absolute payload offsets (the last is total_bytes), zero-padded to 128;
- *    then the sign+mantissa bytes of all n values, zero-padded to 128; in
- *    ciera mode the chunks' bitmaps, 128 bytes each (bit j & 7 of byte
- *    j >> 3 for block j of the chunk); then the part payloads, each
- *    zero-padded to 128.
+ *  - Chunk payload (little-endian): u8 lo, u8 hi (the first and last symbol
+ *    with f > 0), u16 0, u16 w_0 .. w_3 (the number of 16-bit words in each
+ *    part's stream), f_lo .. f_hi as u16, then the four part streams in
+ *    part order.  A part's stream: the 64 final encoder states (low half,
+ *    high half, state 0 first), then, step by step from the first, the
+ *    words the encoder emitted at that step, in ascending state order; a
+ *    part without coded symbols has an empty stream (w_h = 0).  A chunk
+ *    without coded symbols has an empty payload.
+ *  - Stream: the 128-byte header (version 2, mode 2 or 3, E0 = 0, bytes
+ *    48..55 the number of coded symbols); at byte 128 a chunk table of
+ *    nchunks + 1 u64 absolute payload offsets (the last is total_bytes),
+ *    zero-padded to 128; then the sign+mantissa bytes of all n values,
+ *    zero-padded to 128; in ciera mode the chunks' bitmaps, 128 bytes each
+ *    (bit j & 7 of byte j >> 3 for block j of the chunk); then the chunk
+ *    payloads, each zero-padded to 128.
  * A decoder checks that every word is used and that every state ends at
  * 2^16, the encoder's start.
  * ------------------------------------------------------------------------ */
@@ -558,6 +562,8 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
 #define ORC_RANS_L 65536u
 #define ORC_RANS_LANES 64u
 #define ORC_PART 16384ull
+#define ORC_RANS_HEAD 12ull
+#define ORC_RANS_VERSION 2u
 
 void orc_rans_freqs(const uint32_t hist[256], uint16_t freq[256]) {
   uint64_t m = 0;
@@ -584,36 +590,26 @@ void orc_rans_freqs(const uint32_t hist[256], uint16_t freq[256]) {
   freq[top] = (uint16_t)(freq[top] + (ORC_RANS_M - sum));
 }
 
-static uint64_t rans_part_max(uint64_t m) { return m ? 8ull + 512ull + 256ull + 2ull * m : 0ull; }
+/* Largest payload of a chunk of nc values: every value coded, and at most
+ * one word emitted per symbol. */
+static uint64_t rans_chunk_max(uint64_t nc) {
+  if (nc == 0) return 0;
+  return ORC_RANS_HEAD + 512ull + 2ull * (2ull * ORC_RANS_LANES * ceil_div(nc, ORC_PART) + nc);
+}
 
 uint64_t orc_rans_max_encoded_size(uint64_t n, uint32_t B) {
   uint64_t nchunks = ceil_div(n, ORC_CHUNK);
-  uint64_t size = ORC_HEADER + pad128(8ull * (4ull * nchunks + 1ull)) + pad128(n);
+  uint64_t size = ORC_HEADER + pad128(8ull * (nchunks + 1ull)) + pad128(n);
   if (B) size += 128ull * nchunks;
-  for (uint64_t v = 0; v < n; v += ORC_PART) {
-    uint64_t m = (n - v < ORC_PART) ? n - v : ORC_PART;
-    size += pad128(rans_part_max(m));
-  }
+  for (uint64_t v = 0; v < n; v += ORC_CHUNK) size += pad128(rans_chunk_max((n - v < ORC_CHUNK) ? n - v : ORC_CHUNK));
   return size;
 }
 
-/* Payload of one part's m symbols; returns its length in bytes (0 for m = 0). */
-static uint64_t rans_encode_part(const uint8_t* sym, uint64_t m, uint8_t* out) {
+/* One part's stream: its m symbols coded with the chunk's table (f, cum),
+ * written at out.  Returns its number of 16-bit words (0 for m = 0). */
+static uint64_t rans_encode_stream(const uint8_t* sym, uint64_t m, const uint16_t* f, const uint32_t* cum,
+                                   uint8_t* out) {
   if (m == 0) return 0;
-  uint32_t hist[256] = {0};
-  for (uint64_t i = 0; i < m; i++) hist[sym[i]]++;
-  uint16_t f[256];
-  orc_rans_freqs(hist, f);
-  uint32_t cum[256];
-  unsigned lo = 256, hi = 0, c = 0;
-  for (unsigned s = 0; s < 256; s++) {
-    cum[s] = c;
-    c += f[s];
-    if (f[s]) {
-      if (lo == 256) lo = s;
-      hi = s;
-    }
-  }
   const uint64_t steps = ceil_div(m, ORC_RANS_LANES);
   uint32_t x[ORC_RANS_LANES];
   for (unsigned l = 0; l < ORC_RANS_LANES; l++) x[l] = ORC_RANS_L;
@@ -635,13 +631,7 @@ static uint64_t rans_encode_part(const uint8_t* sym, uint64_t m, uint8_t* out) {
       x[l] = (x[l] / f[s]) * ORC_RANS_M + (x[l] % f[s]) + cum[s];
     }
   }
-  const uint64_t nwords = 2ull * ORC_RANS_LANES + ne;
-  out[0] = (uint8_t)lo;
-  out[1] = (uint8_t)hi;
-  out[2] = out[3] = 0;
-  put_u32(out + 4, (uint32_t)nwords);
-  uint8_t* p = out + 8;
-  for (unsigned s = lo; s <= hi; s++, p += 2) put_u16(p, f[s]);
+  uint8_t* p = out;
   for (unsigned l = 0; l < ORC_RANS_LANES; l++, p += 4) {
     put_u16(p, x[l] & 0xFFFFu);
     put_u16(p + 2, x[l] >> 16);
@@ -660,32 +650,49 @@ static uint64_t rans_encode_part(const uint8_t* sym, uint64_t m, uint8_t* out) {
   }
   free(emit);
   free(count);
+  return 2ull * ORC_RANS_LANES + ne;
+}
+
+/* Payload of one chunk; sym holds the parts' symbols back to back, m[h] of
+ * part h.  Returns its length in bytes (0 without symbols). */
+static uint64_t rans_encode_chunk(const uint8_t* sym, const uint64_t m[4], uint8_t* out) {
+  const uint64_t total = m[0] + m[1] + m[2] + m[3];
+  if (total == 0) return 0;
+  uint32_t hist[256] = {0};
+  for (uint64_t i = 0; i < total; i++) hist[sym[i]]++;
+  uint16_t f[256];
+  orc_rans_freqs(hist, f);
+  uint32_t cum[256];
+  unsigned lo = 256, hi = 0, c = 0;
+  for (unsigned s = 0; s < 256; s++) {
+    cum[s] = c;
+    c += f[s];
+    if (f[s]) {
+      if (lo == 256) lo = s;
+      hi = s;
+    }
+  }
+  out[0] = (uint8_t)lo;
+  out[1] = (uint8_t)hi;
+  out[2] = out[3] = 0;
+  uint8_t* p = out + ORC_RANS_HEAD;
+  for (unsigned s = lo; s <= hi; s++, p += 2) put_u16(p, f[s]);
+  const uint8_t* s = sym;
+  for (unsigned h = 0; h < 4; h++) {
+    uint64_t w = rans_encode_stream(s, m[h], f, cum, p);
+    put_u16(out + 4 + 2 * h, (unsigned)w);
+    p += 2 * w;
+    s += m[h];
+  }
   return (uint64_t)(p - out);
 }
 
-/* Decode one part's payload (len bytes, the padding excluded) into m symbols. */
-static int rans_decode_part(const uint8_t* in, uint64_t len, uint64_t m, uint8_t* sym) {
-  if (len < 8) return ORC_ERR_FORMAT;
-  unsigned lo = in[0], hi = in[1];
-  uint64_t nwords = get_u32(in + 4);
-  if (hi < lo || in[2] || in[3]) return ORC_ERR_FORMAT;
-  const uint64_t fbytes = 2ull * (hi - lo + 1u);
-  if (len != 8 + fbytes + 2 * nwords || nwords < 2ull * ORC_RANS_LANES) return ORC_ERR_FORMAT;
-  uint32_t f[256] = {0}, cum[256];
-  unsigned total = 0;
-  for (unsigned s = lo; s <= hi; s++) {
-    f[s] = get_u16(in + 8 + 2 * (s - lo));
-    total += f[s];
-  }
-  if (total != ORC_RANS_M) return ORC_ERR_FORMAT;
-  uint8_t sym_of[ORC_RANS_M];
-  unsigned c = 0;
-  for (unsigned s = 0; s < 256; s++) {
-    cum[s] = c;
-    for (unsigned k = 0; k < f[s]; k++) sym_of[c + k] = (uint8_t)s;
-    c += f[s];
-  }
-  const uint8_t* w = in + 8 + fbytes;
+/* Decode one part's stream (nwords words at w) into m symbols with the
+ * chunk's table. */
+static int rans_decode_stream(const uint8_t* w, uint64_t nwords, uint64_t m, const uint32_t* f, const uint32_t* cum,
+                              const uint8_t* sym_of, uint8_t* sym) {
+  if (m == 0) return nwords == 0 ? ORC_OK : ORC_ERR_FORMAT;
+  if (nwords < 2ull * ORC_RANS_LANES) return ORC_ERR_FORMAT;
   uint32_t x[ORC_RANS_LANES];
   for (unsigned l = 0; l < ORC_RANS_LANES; l++) {
     x[l] = (uint32_t)get_u16(w + 4 * l) | ((uint32_t)get_u16(w + 4 * l + 2) << 16);
@@ -714,10 +721,54 @@ static int rans_decode_part(const uint8_t* in, uint64_t len, uint64_t m, uint8_t
   return ORC_OK;
 }
 
-static uint64_t rans_sm_pos(uint64_t nchunks) { return ORC_HEADER + pad128(8ull * (4ull * nchunks + 1ull)); }
+/* Decode one chunk's payload (len bytes, the padding excluded) into the
+ * parts' symbols, back to back (m[h] of part h). */
+static int rans_decode_chunk(const uint8_t* in, uint64_t len, const uint64_t m[4], uint8_t* sym) {
+  if (len < ORC_RANS_HEAD) return ORC_ERR_FORMAT;
+  unsigned lo = in[0], hi = in[1];
+  if (hi < lo || in[2] || in[3]) return ORC_ERR_FORMAT;
+  uint64_t nw[4], words = 0;
+  for (unsigned h = 0; h < 4; h++) {
+    nw[h] = get_u16(in + 4 + 2 * h);
+    words += nw[h];
+  }
+  const uint64_t fbytes = 2ull * (hi - lo + 1u);
+  if (len != ORC_RANS_HEAD + fbytes + 2 * words) return ORC_ERR_FORMAT;
+  uint32_t f[256] = {0}, cum[256];
+  unsigned total = 0;
+  for (unsigned s = lo; s <= hi; s++) {
+    f[s] = get_u16(in + ORC_RANS_HEAD + 2 * (s - lo));
+    total += f[s];
+  }
+  if (total != ORC_RANS_M) return ORC_ERR_FORMAT;
+  uint8_t sym_of[ORC_RANS_M];
+  unsigned c = 0;
+  for (unsigned s = 0; s < 256; s++) {
+    cum[s] = c;
+    for (unsigned k = 0; k < f[s]; k++) sym_of[c + k] = (uint8_t)s;
+    c += f[s];
+  }
+  const uint8_t* p = in + ORC_RANS_HEAD + fbytes;
+  for (unsigned h = 0; h < 4; h++) {
+    int st = rans_decode_stream(p, nw[h], m[h], f, cum, sym_of, sym);
+    if (st != ORC_OK) return st;
+    p += 2 * nw[h];
+    sym += m[h];
+  }
+  return ORC_OK;
+}
+
+static uint64_t rans_sm_pos(uint64_t nchunks) { return ORC_HEADER + pad128(8ull * (nchunks + 1ull)); }
 
 /* Is value i coded?  zip3: always; ciera: when its block changed. */
 static int rans_coded(const uint8_t* changed, uint32_t B, uint64_t i) { return B == 0 || changed[i / B]; }
+
+/* Is value i coded, by the stream's bitmap (ciera; zip3: always)? */
+static int rans_bit(const uint8_t* in, uint64_t bm_pos, uint32_t B, uint64_t i) {
+  if (B == 0) return 1;
+  uint64_t c = i / ORC_CHUNK, j = (i % ORC_CHUNK) / B;
+  return (in[bm_pos + 128 * c + (j >> 3)] >> (j & 7)) & 1;
+}
 
 /* Encode in an rANS mode (B = 0: zip3 + rANS; else ciera + rANS with the
  * sender cache as in orc_encode).  stats (may be NULL): {changed blocks,
@@ -733,7 +784,6 @@ int orc_encode_rans(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, u
   if (out == NULL || capacity < need) return ORC_ERR_CAPACITY;
   memset(out, 0, need);
   const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
-  const uint64_t nparts = 4ull * nchunks;
   const uint64_t nblocks = ciera ? ceil_div(n, B) : 0;
   uint8_t* changed = NULL;
   uint64_t n_changed = 0;
@@ -753,21 +803,28 @@ int orc_encode_rans(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, u
       for (uint64_t j = 0; j < ORC_CHUNK / B && c * ORC_CHUNK + j * B < n; j++)
         if (changed[c * (ORC_CHUNK / B) + j]) out[bm_pos + 128 * c + (j >> 3)] |= (uint8_t)(1u << (j & 7));
   }
-  uint8_t* sym = (uint8_t*)malloc(ORC_PART);
+  uint8_t* sym = (uint8_t*)malloc(ORC_CHUNK);
   uint64_t n_coded = 0;
-  for (uint64_t p = 0; p < nparts; p++) {
-    put_u64(out + ORC_HEADER + 8 * p, pos);
-    uint64_t begin = p * ORC_PART, end = begin + ORC_PART < n ? begin + ORC_PART : n;
-    uint64_t m = 0;
-    for (uint64_t i = begin; i < end; i++)
-      if (rans_coded(changed, B, i)) sym[m++] = (uint8_t)exp_field(x[i]);
-    n_coded += m;
-    pos += pad128(rans_encode_part(sym, m, out + pos));
+  for (uint64_t c = 0; c < nchunks; c++) {
+    put_u64(out + ORC_HEADER + 8 * c, pos);
+    uint64_t m[4], k = 0;
+    for (unsigned h = 0; h < 4; h++) {
+      uint64_t begin = c * ORC_CHUNK + h * ORC_PART;
+      uint64_t end = begin + ORC_PART < n ? begin + ORC_PART : n;
+      m[h] = 0;
+      for (uint64_t i = begin; i < end; i++)
+        if (rans_coded(changed, B, i)) {
+          sym[k++] = (uint8_t)exp_field(x[i]);
+          m[h]++;
+        }
+    }
+    n_coded += k;
+    pos += pad128(rans_encode_chunk(sym, m, out + pos));
   }
   free(sym);
-  put_u64(out + ORC_HEADER + 8 * nparts, pos);
+  put_u64(out + ORC_HEADER + 8 * nchunks, pos);
   memcpy(out, ciera ? "CIER" : "ZIP3", 4);
-  put_u16(out + 4, 1);
+  put_u16(out + 4, ORC_RANS_VERSION);
   out[6] = ciera ? 3 : 2;
   out[7] = 0;
   put_u64(out + 8, n);
@@ -793,63 +850,58 @@ int orc_decode_rans(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n
   if (in == NULL || (n > 0 && y == NULL) || (ciera && n > 0 && cache == NULL)) return ORC_ERR_ARG;
   if (n > ORC_MAX_N || (ciera && !valid_block_size(B))) return ORC_ERR_ARG;
   const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
-  const uint64_t nparts = 4ull * nchunks;
   const uint64_t sm_pos = rans_sm_pos(nchunks);
   const uint64_t bm_pos = sm_pos + pad128(n);
   const uint64_t pay_pos = bm_pos + (ciera ? 128ull * nchunks : 0);
   if (in_size < pay_pos) return ORC_ERR_FORMAT;
-  if (memcmp(in, ciera ? "CIER" : "ZIP3", 4) != 0 || get_u16(in + 4) != 1 || in[6] != (ciera ? 3 : 2) ||
-      in[7] != 0 || get_u64(in + 8) != n || get_u32(in + 16) != B || get_u32(in + 20) != ORC_CHUNK ||
-      get_u64(in + 24) != nchunks || get_u64(in + 32) != in_size)
+  if (memcmp(in, ciera ? "CIER" : "ZIP3", 4) != 0 || get_u16(in + 4) != ORC_RANS_VERSION ||
+      in[6] != (ciera ? 3 : 2) || in[7] != 0 || get_u64(in + 8) != n || get_u32(in + 16) != B ||
+      get_u32(in + 20) != ORC_CHUNK || get_u64(in + 24) != nchunks || get_u64(in + 32) != in_size)
     return ORC_ERR_FORMAT;
   for (unsigned k = 56; k < ORC_HEADER; k++)
     if (in[k]) return ORC_ERR_FORMAT;
-  if (get_u64(in + ORC_HEADER) != pay_pos || get_u64(in + ORC_HEADER + 8 * nparts) != in_size) return ORC_ERR_FORMAT;
-  uint8_t* sym = (uint8_t*)malloc(ORC_PART);
+  if (get_u64(in + ORC_HEADER) != pay_pos || get_u64(in + ORC_HEADER + 8 * nchunks) != in_size)
+    return ORC_ERR_FORMAT;
+  uint8_t* sym = (uint8_t*)malloc(ORC_CHUNK);
   uint64_t n_changed = 0, n_coded = 0;
   int st = ORC_OK;
-  for (uint64_t p = 0; p < nparts && st == ORC_OK; p++) {
-    uint64_t a = get_u64(in + ORC_HEADER + 8 * p), b = get_u64(in + ORC_HEADER + 8 * (p + 1));
+  for (uint64_t c = 0; c < nchunks && st == ORC_OK; c++) {
+    uint64_t a = get_u64(in + ORC_HEADER + 8 * c), b = get_u64(in + ORC_HEADER + 8 * (c + 1));
     if (b < a || b > in_size || (a & 127u) || (b & 127u)) {
       st = ORC_ERR_FORMAT;
       break;
     }
-    uint64_t begin = p * ORC_PART, end = begin + ORC_PART < n ? begin + ORC_PART : n;
-    uint64_t m = 0;
-    for (uint64_t i = begin; i < end; i++) {
-      int coded = 1;
-      if (ciera) {
-        uint64_t c = i / ORC_CHUNK, j = (i % ORC_CHUNK) / B;
-        coded = (in[bm_pos + 128 * c + (j >> 3)] >> (j & 7)) & 1;
-      }
-      m += coded ? 1 : 0;
+    uint64_t m[4], total = 0;
+    for (unsigned h = 0; h < 4; h++) {
+      uint64_t begin = c * ORC_CHUNK + h * ORC_PART;
+      uint64_t end = begin + ORC_PART < n ? begin + ORC_PART : n;
+      m[h] = 0;
+      for (uint64_t i = begin; i < end; i++) m[h] += (uint64_t)rans_bit(in, bm_pos, B, i);
+      total += m[h];
     }
-    n_coded += m;
-    if (m == 0) {
+    n_coded += total;
+    if (total == 0) {
       if (b != a) st = ORC_ERR_FORMAT;
       continue;
     }
-    if (b - a < 8) {
+    if (b - a < ORC_RANS_HEAD) {
       st = ORC_ERR_FORMAT;
       break;
     }
-    uint64_t len = 8 + 2ull * (in[a + 1] >= in[a] ? in[a + 1] - in[a] + 1u : 0) + 2ull * get_u32(in + a + 4);
+    uint64_t words = 0;
+    for (unsigned h = 0; h < 4; h++) words += get_u16(in + a + 4 + 2 * h);
+    uint64_t len = ORC_RANS_HEAD + 2ull * (in[a + 1] >= in[a] ? in[a + 1] - in[a] + 1u : 0) + 2ull * words;
     if (pad128(len) != b - a) {
       st = ORC_ERR_FORMAT;
       break;
     }
     for (uint64_t k = a + len; k < b; k++)
       if (in[k]) st = ORC_ERR_FORMAT;
-    if (st == ORC_OK) st = rans_decode_part(in + a, len, m, sym);
+    if (st == ORC_OK) st = rans_decode_chunk(in + a, len, m, sym);
     if (st != ORC_OK) break;
     uint64_t k = 0;
-    for (uint64_t i = begin; i < end; i++) {
-      int coded = 1;
-      if (ciera) {
-        uint64_t c = i / ORC_CHUNK, j = (i % ORC_CHUNK) / B;
-        coded = (in[bm_pos + 128 * c + (j >> 3)] >> (j & 7)) & 1;
-      }
-      if (coded) {
+    for (uint64_t i = c * ORC_CHUNK; i < n && i < (c + 1) * ORC_CHUNK; i++) {
+      if (rans_bit(in, bm_pos, B, i)) {
         y[i] = join_fields(in[sm_pos + i], sym[k++]);
         if (ciera) cache[i] = (uint8_t)exp_field(y[i]);
       }
@@ -857,15 +909,9 @@ int orc_decode_rans(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n
   }
   free(sym);
   if (st != ORC_OK) return st;
-  /* values of unchanged blocks (and parts without coded symbols) */
-  for (uint64_t i = 0; i < n; i++) {
-    int coded = 1;
-    if (ciera) {
-      uint64_t c = i / ORC_CHUNK, j = (i % ORC_CHUNK) / B;
-      coded = (in[bm_pos + 128 * c + (j >> 3)] >> (j & 7)) & 1;
-    }
-    if (!coded) y[i] = join_fields(in[sm_pos + i], cache[i]);
-  }
+  /* values of unchanged blocks */
+  for (uint64_t i = 0; i < n; i++)
+    if (!rans_bit(in, bm_pos, B, i)) y[i] = join_fields(in[sm_pos + i], cache[i]);
   if (ciera) {
     for (uint64_t c = 0; c < nchunks; c++) {
       uint64_t nb_c = ceil_div((n - c * ORC_CHUNK < ORC_CHUNK) ? n - c * ORC_CHUNK : ORC_CHUNK, B);

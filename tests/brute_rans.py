@@ -1,9 +1,11 @@
 """A second, independent encoder for the rANS stream modes (zip3 + rANS and
 ciera + rANS), in plain Python, written from the format description and not
-from the oracle's C: per part (16384 values) the coded exponents, a
-frequency table normalised to 4096, 64 interleaved rANS states with 16-bit
-renormalisation, payload = header, table, flushed states, then the emitted
-words step by step.  Slow; for small inputs only."""
+from the oracle's C: per chunk (65536 values) one frequency table over its
+coded exponents, normalised to 4096; per part (16384 values) 64 interleaved
+rANS states with 16-bit renormalisation over the part's coded exponents;
+chunk payload = header with the parts' word counts, table, then each part's
+flushed states and emitted words step by step.  Slow; for small inputs
+only."""
 from __future__ import annotations
 
 import struct
@@ -31,16 +33,12 @@ def norm_freqs(hist):
     return f
 
 
-def part_payload(sym):
+def coded_stream(sym, f, cum):
+    """One part's 16-bit words: 64 interleaved states coding sym with the
+    table (f, cum), last step first; then the flushed states and the words
+    each step emitted, steps in decoding order."""
     if not sym:
-        return b""
-    hist = [0] * 256
-    for s in sym:
-        hist[s] += 1
-    f = norm_freqs(hist)
-    cum = [sum(f[:s]) for s in range(256)]
-    present = [s for s in range(256) if f[s]]
-    lo, hi = present[0], present[-1]
+        return []
     steps = -(-len(sym) // LANES)
     x = [L] * LANES
     groups = [[] for _ in range(steps)]
@@ -59,9 +57,27 @@ def part_payload(sym):
         words += [v & 0xFFFF, v >> 16]
     for g in groups:
         words += g
-    out = bytes([lo, hi, 0, 0]) + struct.pack("<I", len(words))
+    return words
+
+
+def chunk_payload(parts):
+    """Payload of one chunk from its four parts' symbol lists: one table
+    over all of them, then each part's stream."""
+    allsym = [s for part in parts for s in part]
+    if not allsym:
+        return b""
+    hist = [0] * 256
+    for s in allsym:
+        hist[s] += 1
+    f = norm_freqs(hist)
+    cum = [sum(f[:s]) for s in range(256)]
+    present = [s for s in range(256) if f[s]]
+    lo, hi = present[0], present[-1]
+    streams = [coded_stream(part, f, cum) for part in parts]
+    out = bytes([lo, hi, 0, 0]) + struct.pack("<4H", *[len(w) for w in streams])
     out += b"".join(struct.pack("<H", f[s]) for s in range(lo, hi + 1))
-    out += b"".join(struct.pack("<H", w) for w in words)
+    for w in streams:
+        out += b"".join(struct.pack("<H", v) for v in w)
     return out
 
 
@@ -71,12 +87,11 @@ def encode(x, B=0, cache=None):
     n = len(x)
     e = [(v >> 7) & 0xFF for v in x]
     nchunks = -(-n // CHUNK)
-    nparts = 4 * nchunks
     changed = []
     if B:
         nb = -(-n // B)
         changed = [any(e[i] != int(cache[i]) for i in range(b * B, min(n, (b + 1) * B))) for b in range(nb)]
-    sm_pos = 128 + pad128(8 * (nparts + 1))
+    sm_pos = 128 + pad128(8 * (nchunks + 1))
     bm_pos = sm_pos + pad128(n)
     pos = bm_pos + (128 * nchunks if B else 0)
     body = bytearray(pos)
@@ -89,17 +104,20 @@ def encode(x, B=0, cache=None):
                     body[bm_pos + 128 * c + (j >> 3)] |= 1 << (j & 7)
     table = []
     coded = 0
-    for p in range(nparts):
+    for c in range(nchunks):
         table.append(pos)
-        sym = [e[i] for i in range(p * PART, min(n, (p + 1) * PART)) if not B or changed[i // B]]
-        coded += len(sym)
-        pay = part_payload(sym)
+        parts = []
+        for h in range(4):
+            lo_v = c * CHUNK + h * PART
+            parts.append([e[i] for i in range(lo_v, min(n, lo_v + PART)) if not B or changed[i // B]])
+        coded += sum(len(q) for q in parts)
+        pay = chunk_payload(parts)
         body += pay + bytes(pad128(len(pay)) - len(pay))
         pos += pad128(len(pay))
     table.append(pos)
     for k, t in enumerate(table):
         body[128 + 8 * k:136 + 8 * k] = struct.pack("<Q", t)
-    hd = (b"CIER" if B else b"ZIP3") + struct.pack("<HBB", 1, 3 if B else 2, 0)
+    hd = (b"CIER" if B else b"ZIP3") + struct.pack("<HBB", 2, 3 if B else 2, 0)
     hd += struct.pack("<QIIQQQQ", n, B, CHUNK, nchunks, pos, sum(changed), coded)
     body[:len(hd)] = hd
     return np.frombuffer(bytes(body), dtype=np.uint8)

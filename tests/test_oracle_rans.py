@@ -41,22 +41,57 @@ def test_freqs_properties():
     assert f[200] == 4096 and f.sum() == 4096
 
 
-def _payloads(stream, nparts):
-    table = stream[128:128 + 8 * (nparts + 1)].view(np.uint64)
-    return [stream[int(table[p]):int(table[p + 1])] for p in range(nparts)]
+def _payloads(stream, nchunks):
+    table = stream[128:128 + 8 * (nchunks + 1)].view(np.uint64)
+    return [stream[int(table[c]):int(table[c + 1])] for c in range(nchunks)]
 
 
 def test_single_symbol_part_needs_no_words():
     x = np.full(1000, 0x3C00, dtype=np.uint16)  # one exponent everywhere
     s, st = oracle.encode_rans(x)
-    pay = _payloads(s, 4)
-    assert [p.size for p in pay] == [384, 0, 0, 0]  # pad128(8 + 2 + 256)
+    pay = _payloads(s, 1)
+    assert [p.size for p in pay] == [384]  # pad128(12 + 2 + 256)
     p = pay[0]
-    assert p[0] == p[1] == 0x78 and int(p[4:8].view(np.uint32)[0]) == 128
-    assert int(p[8:10].view(np.uint16)[0]) == 4096
-    states = p[10:10 + 256].view(np.uint16)
+    assert p[0] == p[1] == 0x78
+    assert list(p[4:12].view(np.uint16)) == [128, 0, 0, 0]  # words per part: the 64 states of part 0 only
+    assert int(p[12:14].view(np.uint16)[0]) == 4096
+    states = p[14:14 + 256].view(np.uint16)
     assert (states[0::2] == 0).all() and (states[1::2] == 1).all()  # every state 2^16
     assert np.array_equal(oracle.decode_rans(s, x.size), x)
+
+
+def test_one_table_per_chunk_one_stream_per_part():
+    """Four parts with different exponent mixes share the chunk's table,
+    normalised from the chunk's histogram; each part with coded values has
+    a stream of its own (ciera: a part whose blocks are all unchanged has
+    none)."""
+    rng = np.random.default_rng(12)
+    x = np.concatenate([np.full(16384, 0x3C00, np.uint16),            # exponent 120 only
+                        wl.normal_bf16(rng, 16384, 1.0),
+                        np.full(16384, 0x3F80, np.uint16),            # exponent 127 only
+                        wl.normal_bf16(rng, 9000, 1e-3)])
+    s, _ = oracle.encode_rans(x)
+    pay = _payloads(s, 1)[0]
+    e = (x >> 7) & 0xFF
+    f = oracle.rans_freqs(np.bincount(e, minlength=256).astype(np.uint32))
+    lo, hi = int(pay[0]), int(pay[1])
+    assert lo == int(np.flatnonzero(f)[0]) and hi == int(np.flatnonzero(f)[-1])
+    assert np.array_equal(pay[12:12 + 2 * (hi - lo + 1)].view(np.uint16), f[lo:hi + 1])
+    w = pay[4:12].view(np.uint16).astype(int)
+    assert (w >= 128).all()
+    assert pay.size == -(-(12 + 2 * (hi - lo + 1) + 2 * int(w.sum())) // 128) * 128
+    assert np.array_equal(oracle.decode_rans(s, x.size), x)
+    # ciera: only part 1's blocks changed
+    cache = e.astype(np.uint8).copy()
+    prev = cache.copy()
+    prev[16384 + 5] ^= 1
+    s, st = oracle.encode_rans(x, 512, prev.copy())
+    assert st == {"changed_blocks": 1, "coded": 512}
+    pay = _payloads(s, 1)[0]
+    w = pay[4:12].view(np.uint16).astype(int)
+    assert w[0] == 0 and w[1] >= 128 and w[2] == 0 and w[3] == 0
+    r = prev.copy()
+    assert np.array_equal(oracle.decode_rans(s, x.size, 512, r), x) and np.array_equal(r, cache)
 
 
 @pytest.mark.parametrize("sigma", [1.0, 0.02, 1e-3])
@@ -67,12 +102,13 @@ def test_coded_size_is_the_information_content(sigma):
     rng = np.random.default_rng(3)
     x = wl.normal_bf16(rng, 16384, sigma)
     s, _ = oracle.encode_rans(x)
-    pay = _payloads(s, 4)[0]
+    pay = _payloads(s, 1)[0]
     lo, hi = int(pay[0]), int(pay[1])
     f = np.zeros(256)
-    f[lo:hi + 1] = pay[8:8 + 2 * (hi - lo + 1)].view(np.uint16)
-    w = pay[8 + 2 * (hi - lo + 1):].view(np.uint16)
-    nwords = int(pay[4:8].view(np.uint32)[0])
+    f[lo:hi + 1] = pay[12:12 + 2 * (hi - lo + 1)].view(np.uint16)
+    w = pay[12 + 2 * (hi - lo + 1):].view(np.uint16)
+    nwords = int(pay[4:6].view(np.uint16)[0])
+    assert list(pay[6:12].view(np.uint16)) == [0, 0, 0]
     xs = w[0:128:2].astype(np.float64) + w[1:128:2].astype(np.float64) * 65536.0
     spent = 16 * (nwords - 128) + sum(math.log2(v) - 16 for v in xs)
     e = (x >> 7) & 0xFF
@@ -133,9 +169,9 @@ def test_decode_rejects_corruption():
     x = wl.normal_bf16(rng, C, 0.02)
     s, _ = oracle.encode_rans(x)
     a = int(s[128:136].view(np.uint64)[0])
-    nw = int(s[a + 4:a + 8].view(np.uint32)[0])
+    nw = int(s[a + 4:a + 6].view(np.uint16)[0])
     lo, hi = int(s[a]), int(s[a + 1])
-    words = a + 8 + 2 * (hi - lo + 1)
+    words = a + 12 + 2 * (hi - lo + 1)
 
     def bad(mutate):
         t = s.copy()
@@ -144,8 +180,9 @@ def test_decode_rejects_corruption():
             oracle.decode_rans(t, x.size)
 
     bad(lambda t: t.__setitem__(6, 0))                        # mode byte
-    bad(lambda t: t.__setitem__(slice(a + 4, a + 8), np.frombuffer(np.uint32(nw + 1).tobytes(), np.uint8)))
-    bad(lambda t: t.__setitem__(a + 8, t[a + 8] ^ 1))         # table no longer sums to 4096
+    bad(lambda t: t.__setitem__(slice(a + 4, a + 6), np.frombuffer(np.uint16(nw + 1).tobytes(), np.uint8)))
+    bad(lambda t: t.__setitem__(a + 12, t[a + 12] ^ 1))       # table no longer sums to 4096
     bad(lambda t: t.__setitem__(words + 256 + 20, t[words + 256 + 20] ^ 0x10))  # a renormalisation word
     bad(lambda t: t.__setitem__(words + 3, t[words + 3] ^ 0x80))                # a final state
-    bad(lambda t: t.__setitem__(136, t[136] ^ 0x40))          # part table entry
+    bad(lambda t: t.__setitem__(136, t[136] ^ 0x40))          # chunk table entry
+    bad(lambda t: t.__setitem__(4, 1))                        # version
