@@ -564,7 +564,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   if (!kHash)
     for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
   if (tid < kPartBitmapWords) s_bits[tid] = 0u;
-  if (ws.rstat && tid == 0) ws.rstat[uint64_t(wg) * kRstatStride] = 0u;  // rANS encode: the part's look-back word, not ready
+  if (ws.rstat && tid == 0 && h == 0u) ws.rstat[c * kRstatStride] = 0u;  // rANS encode: the chunk's look-back word, not ready
   if (blockIdx.x == 0u) {
     // k_plan's slots: the FP64 words empty, the count words not ready
     uint64_t* sw = reinterpret_cast<uint64_t*>(ws.plan);
@@ -2082,37 +2082,82 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
 // ciera mode) entropy coded with range ANS in place of the 3-bit code, as the
 // CIERA page ANS-codes changed exponents (section 3.1); the page names no ANS
 // parameters, so the coder is our own:
-//  - per part (16384 values), the symbols are the coded exponents in value
-//    order; frequencies: the part's histogram normalised to M = 4096 (with d
-//    distinct symbols among m, f = max(1, floor(h (M - d) / m)) for each
-//    present symbol, the rest to the most frequent one, the lowest on ties);
-//  - 64 interleaved 32-bit states (symbol i to state i mod 64) in
-//    [2^16, 2^32), starting at 2^16; encode: if x >= f 2^20 emit its low 16
-//    bits and shift, then x = (x div f) M + x mod f + c; decode: slot =
-//    x mod M, x = f (x div M) + slot - c, then one 16-bit word if x < 2^16;
-//  - payload: u8 lo, u8 hi, u16 0, u32 nwords, u16 f_lo .. f_hi, then the
-//    64 final states (low, high half) and the words each step emitted, steps
-//    in decode order, states ascending within a step;
-//  - stream: header (mode 2 zip3 + rANS, 3 ciera + rANS; bytes 48..55 the
-//    coded symbols), a table of 4 nchunks + 1 u64 part payload offsets,
-//    every value's sign+mantissa byte, in ciera mode 128 bitmap bytes per
-//    chunk, then the part payloads, each padded to 128 bytes.
-// One wave per part runs the 64 states; the part's other waves load, write
-// the sign+mantissa bytes and stage the symbols.  Encode: k_stats (the
-// part's histogram of coded exponents), k_rans_enc (code into a scratch
-// slot, find the offset by look-back over the parts before, copy into the
-// stream), k_rans_finish (header totals).  Decode: k_rans_dec.
+//  - symbols: a chunk's coded exponents; part h of the chunk (its values
+//    16384 h .. 16384 h + 16383) codes its own ones in value order;
+//  - one frequency table per chunk: the histogram of all its coded
+//    exponents normalised to M = 4096 (with d distinct symbols among m,
+//    f = max(1, floor(h (M - d) / m)) for each present symbol, the rest to
+//    the most frequent one, the lowest on ties);
+//  - per part, 64 interleaved 32-bit states (symbol i of the part to state
+//    i mod 64) in [2^16, 2^32), starting at 2^16; encode: if x >= f 2^20
+//    emit its low 16 bits and shift, then x = (x div f) M + x mod f + c;
+//    decode: slot = x mod M, x = f (x div M) + slot - c, then one 16-bit
+//    word if x < 2^16;
+//  - chunk payload: u8 lo, u8 hi, u16 0, u16 w_0 .. w_3 (the words of each
+//    part's stream, 0 without coded symbols), u16 f_lo .. f_hi, then the
+//    part streams in part order: the 64 final states (low, high half), then
+//    the words each step emitted, steps in decode order, states ascending
+//    within a step;
+//  - stream (version 2): header (mode 2 zip3 + rANS, 3 ciera + rANS; bytes
+//    48..55 the coded symbols), a table of nchunks + 1 u64 chunk payload
+//    offsets, every value's sign+mantissa byte, in ciera mode 128 bitmap
+//    bytes per chunk, then the chunk payloads, each padded to 128 bytes.
+// One workgroup per chunk; wave h codes part h against the chunk's table in
+// LDS, so the four serial coders of a chunk run at once.  Encode: k_stats
+// (per part, the histogram of its coded exponents), k_rans_enc (code the
+// parts into the chunk's scratch slot, find the offset by look-back over the
+// chunks before, copy into the stream), k_rans_finish (header totals).
+// Decode: k_rans_dec.
 constexpr uint32_t kRansM = 4096u;
 constexpr uint32_t kRansL = 1u << 16;
 constexpr uint32_t kRansStates = 64u;
-constexpr uint32_t kRansSlot = 33664u;       // pad128(8 + 512 + 256 + 2 * 16384): a part's largest payload
-constexpr uint32_t kRansStage = 20480u;      // payload bytes k_rans_dec stages in LDS (the rest read from HBM)
+constexpr uint32_t kRansVersion = 2u;
+constexpr uint32_t kRansHead = 12u;                                 // payload bytes before the table
+constexpr uint32_t kRansPartWords = 2u * kRansStates + kPartValues;  // a part stream's largest word count
+constexpr uint32_t kRansSlot = kParts * 2u * kRansPartWords;         // scratch per chunk: one region per part
+constexpr uint32_t kRansStage = 32768u;  // payload bytes k_rans_dec stages in LDS (the rest read from HBM)
+constexpr uint32_t kRansWin = 8u;        // steps whose inputs a coding wave loads ahead
+constexpr uint32_t kGranules = kPartValues / 64u;  // a part's largest granule count (B = 64)
 
-__host__ __device__ inline uint64_t rans_sm_pos(uint64_t nchunks) {
-  return kHeader + pad128(8u * (kParts * nchunks + 1u));
-}
+__host__ __device__ inline uint64_t rans_sm_pos(uint64_t nchunks) { return kHeader + pad128(8u * (nchunks + 1u)); }
 __host__ __device__ inline uint64_t rans_pay_pos(uint64_t n, uint64_t nchunks, bool ciera) {
   return rans_sm_pos(nchunks) + pad128(n) + (ciera ? 128u * nchunks : 0u);
+}
+// Largest payload of a chunk of nc values: every value coded, at most one
+// word per symbol.
+__host__ __device__ inline uint64_t rans_chunk_max(uint64_t nc) {
+  return nc ? kRansHead + 2u * kBins + 2u * (2u * kRansStates * cdiv(nc, kPartValues) + nc) : 0u;
+}
+
+// The coded values of part h (wave h).  Its values fall into granules of
+// G = min(B, 16384) values (zip3: one granule, always coded); granule j of
+// the chunk (j = h 16384 / G + g) is coded when its block changed and it
+// holds values.  Their chunk-relative indices go to gl in order, so that
+// symbol i of the part is value gl[i >> log2G] G + (i mod G) of the chunk.
+// Returns the part's coded values (every lane of the wave).
+__device__ inline uint32_t part_granules(uint32_t h, uint32_t nc, uint32_t log2B, uint32_t log2G, bool ciera,
+                                         const uint32_t* s_bits, uint16_t* gl) {
+  const uint32_t lane = lane_id();
+  const uint32_t G = 1u << log2G, ng = kPartValues >> log2G;
+  const uint64_t below = (1ull << lane) - 1u;
+  uint32_t nl = 0, m = 0;
+  for (uint32_t g0 = 0; g0 < ng; g0 += 64u) {
+    const uint32_t g = g0 + lane;
+    const uint32_t j = h * ng + g;
+    uint32_t cnt = 0;
+    if (g < ng && j * G < nc) {
+      cnt = min(G, nc - j * G);
+      if (ciera) {
+        const uint32_t blk = j >> (log2B - log2G);
+        if (!((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) cnt = 0;
+      }
+    }
+    const uint64_t mk = __ballot(cnt != 0u);
+    if (cnt) gl[nl + uint32_t(__popcll(mk & below))] = uint16_t(j);
+    nl += uint32_t(__popcll(mk));
+    m += cnt;
+  }
+  return wave_sum_u32(m);
 }
 
 // The block's ready flag and inclusive prefix or own size, as in the
@@ -2182,67 +2227,52 @@ __device__ inline uint32_t div_by_freq(uint32_t x, uint32_t f, double rcp, uint3
 
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __restrict__ x, uint64_t n,
-                                                           uint32_t log2B, uint8_t* __restrict__ out, Ws ws) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_sym[kPartValues];
-  __shared__ uint32_t s_f[kBins], s_cum[kBins];
-  __shared__ uint32_t s_fc[kBins];  // f | cum << 16
+                                                           uint64_t nchunks, uint32_t log2B,
+                                                           uint8_t* __restrict__ out, Ws ws) {
+  __shared__ uint32_t s_f[kBins], s_fc[kBins];  // f; f | cum << 16
   __shared__ double s_rcp[kBins];
+  __shared__ uint16_t s_gl[kParts][kGranules];
   __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
-  __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
   __shared__ uint32_t s_w[kPartWaves];
+  __shared__ uint32_t s_m[kParts], s_nw[kParts], s_wpos[kParts];
   __shared__ uint32_t s_lohi, s_ok;
-  __shared__ uint64_t s_start, s_bytes;
+  __shared__ uint64_t s_before;
+  __shared__ uint32_t s_found;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const uint32_t p = blockIdx.x;
-  const uint64_t c = p / kParts;
-  const uint32_t h = p % kParts;
-  const uint64_t nchunks = cdiv(n, kChunk);
+  const uint64_t c = blockIdx.x;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
+  const uint32_t log2G = kCiera ? min(log2B, 14u) : 14u;
   const uint64_t start = c * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
-  const uint32_t nunits = (nc + 7u) / 8u;
-  const uint32_t pu0 = h * kPartUnits;
   const uint64_t sm_pos = rans_sm_pos(nchunks);
 
-  Unit v[kUPT];
-#pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
-    v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
-    if (u < nunits) v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
-  }
   if (kCiera && tid < 64u)
     stage_bitmap((tid < kBitmapWords) ? chunk_bitmap_word(ws.bitmap + c * kBitmapWords, tid, B) : 0u, s_bits,
                  s_rank);
   __syncthreads();
-
-  // sign+mantissa bytes to their fixed place; coded values per unit
-  uint32_t cnt[kUPT], base[kUPT];
-#pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
-    cnt[j] = 0u;
-    if (u < nunits) {
-      store_bytes8(out + sm_pos + start + 8ull * u, min(8u, nc - 8u * u), unit_sm(v[j]));
-      bool coded = true;
-      if (kCiera) {
-        const uint32_t blk = (8u * u) >> log2B;
-        coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
-      }
-      cnt[j] = coded ? min(8u, nc - 8u * u) : 0u;
+  const uint32_t mh = part_granules(wave, nc, log2B, log2G, kCiera, s_bits, s_gl[wave]);
+  if (lane == 0u) s_m[wave] = mh;
+  if (kCiera) {
+    // sign+mantissa bytes of the values that are not coded (the coders write
+    // those of the coded ones)
+    const uint32_t nunits = (nc + 7u) / 8u;
+    for (uint32_t u = tid; u < nunits; u += kPartThreads) {
+      const uint32_t blk = (8u * u) >> log2B;
+      if ((s_bits[blk >> 5] >> (blk & 31u)) & 1u) continue;
+      const uint32_t k = min(8u, nc - 8u * u);
+      store_bytes8(out + sm_pos + start + 8ull * u, k, unit_sm(load_unit(x, start + 8ull * u, k)));
     }
   }
-  const uint32_t m = part_escape_scan(cnt, base, s_tot);
-#pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    if (cnt[j]) {
-      const uint2 e = unit_exponents(v[j]);
-      for (uint32_t k = 0; k < cnt[j]; k++) s_sym[base[j] + k] = uint8_t(byte_of(e, k));
-    }
-  }
+  __syncthreads();
+  const uint32_t m = s_m[0] + s_m[1] + s_m[2] + s_m[3];
 
-  // frequencies from the part's histogram row (one symbol per thread)
-  const uint32_t hs = (m != 0u) ? ws.hist[uint64_t(p) * kBins + tid] : 0u;
+  // frequencies from the parts' histogram rows (one symbol per thread); a
+  // part without coded values adds nothing (with B > 16384 its row counts
+  // all of its values, which its unchanged block leaves uncoded)
+  uint32_t hs = 0;
+#pragma unroll
+  for (uint32_t h = 0; h < kParts; h++)
+    if (s_m[h]) hs += ws.hist[(c * kParts + h) * kBins + tid];
   const uint32_t hsum = part_sum_u32(hs, s_w);
   const uint32_t d = part_sum_u32(hs ? 1u : 0u, s_w);
   // most frequent symbol, the lowest on ties: max of (h << 8) | (255 - s)
@@ -2262,12 +2292,10 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
   if (tid == top) f += kRansM - fsum;
   const uint32_t cum_incl = part_incl_scan_u32(f, s_w);
   s_f[tid] = f;
-  s_cum[tid] = cum_incl - f;
   s_fc[tid] = f | ((cum_incl - f) << 16);
   s_rcp[tid] = f ? 1.0 / double(f) : 0.0;
   // first and last symbol with f > 0
-  const uint32_t lo_key = f ? tid : 255u, hi_key = f ? tid : 0u;
-  uint32_t lo = lo_key, hi = hi_key;
+  uint32_t lo = f ? tid : 255u, hi = f ? tid : 0u;
   for (uint32_t o = 32; o >= 1; o >>= 1) {
     lo = min(lo, uint32_t(__shfl_xor(int(lo), int(o))));
     hi = max(hi, uint32_t(__shfl_xor(int(hi), int(o))));
@@ -2282,131 +2310,149 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
       u = max(u, s_w[w] >> 16);
     }
     s_lohi = l | (u << 8);
-    s_ok = (hsum == m) ? 1u : 0u;  // the histogram counted exactly the coded values
+    s_ok = (hsum == m) ? 1u : 0u;  // the histograms counted exactly the coded values
   }
   __syncthreads();
   const bool ok = s_ok != 0u;
 
-  // wave 0 codes the m symbols with 64 states, last step first, into the
-  // part's scratch slot from its end
-  uint8_t* slot = ws.rslot + uint64_t(p) * kRansSlot;
-  uint16_t* slot16 = reinterpret_cast<uint16_t*>(slot);
-  if (wave == 0 && m && ok) {
-    uint32_t xs = kRansL;
-    uint32_t wpos = kRansSlot / 2u;
+  // Wave h codes part h, last step first, into its region of the chunk's
+  // scratch slot from the region's end.  Its inputs (the values, through
+  // the granule list) are loaded kRansWin steps ahead; each coded value's
+  // sign+mantissa byte is written on the way.
+  uint16_t* reg = reinterpret_cast<uint16_t*>(ws.rslot + c * uint64_t(kRansSlot)) + wave * kRansPartWords;
+  uint32_t wpos = kRansPartWords;
+  if (mh && ok) {
+    const uint16_t* gl = s_gl[wave];
+    const uint32_t gmask = (1u << log2G) - 1u;
     const uint64_t below = (1ull << lane) - 1u;
-    // The symbols and their table entries do not depend on the states: the
-    // entries of step t - 1 and the symbol of step t - 2 are loaded while
-    // step t computes.
-    const int64_t steps = int64_t(cdiv(m, kRansStates));
-    auto sym_at = [&](int64_t t) -> uint32_t {
-      const int64_t i = t * int64_t(kRansStates) + int64_t(lane);
-      return (t >= 0 && i < int64_t(m)) ? uint32_t(s_sym[i]) : 0u;
+    auto fetch = [&](int32_t t, uint32_t& val, uint32_t& vi) {
+      val = 0u;
+      vi = 0u;
+      if (t >= 0) {
+        const uint32_t i = uint32_t(t) * kRansStates + lane;
+        if (i < mh) {
+          vi = kCiera ? ((uint32_t(gl[i >> log2G]) << log2G) | (i & gmask)) : (wave * kPartValues + i);
+          val = x[start + vi];
+        }
+      }
     };
-    uint32_t sym_c = sym_at(steps - 1);
-    uint32_t fc_c = s_fc[sym_c];
-    double rs_c = s_rcp[sym_c];
-    uint32_t sym_n = sym_at(steps - 2);
-    for (int64_t t = steps - 1; t >= 0; t--) {
-      const uint32_t i = uint32_t(t) * kRansStates + lane;
-      const bool act = i < m;
-      const uint32_t fc_n = s_fc[sym_n];
-      const double rs_n = s_rcp[sym_n];
-      const uint32_t sym_nn = sym_at(t - 2);
-      const uint32_t fs = fc_c & 0xFFFFu, cs = fc_c >> 16;
-      const double rs = rs_c;
-      const bool emit = act && uint64_t(xs) >= (uint64_t(fs) << 20);
-      const uint64_t mk = __ballot(emit);
-      const uint32_t ne = uint32_t(__popcll(mk));
-      if (emit) {
-        slot16[wpos - ne + uint32_t(__popcll(mk & below))] = uint16_t(xs & 0xFFFFu);
-        xs >>= 16;
+    uint32_t xs = kRansL;
+    int32_t t0 = int32_t(cdiv(mh, kRansStates)) - 1;  // the group's first (highest) step
+    uint32_t xv[kRansWin], vv[kRansWin];
+#pragma unroll
+    for (uint32_t k = 0; k < kRansWin; k++) fetch(t0 - int32_t(k), xv[k], vv[k]);
+    while (t0 >= 0) {
+      uint32_t xn[kRansWin], vn[kRansWin];
+#pragma unroll
+      for (uint32_t k = 0; k < kRansWin; k++) fetch(t0 - int32_t(kRansWin + k), xn[k], vn[k]);
+#pragma unroll
+      for (uint32_t k = 0; k < kRansWin; k++) {
+        const int32_t t = t0 - int32_t(k);
+        if (t >= 0) {
+          const bool act = uint32_t(t) * kRansStates + lane < mh;
+          const uint32_t e = (xv[k] >> 7) & 0xFFu;
+          const uint32_t fc = s_fc[e];
+          const double rs = s_rcp[e];
+          const uint32_t fs = fc & 0xFFFFu, cs = fc >> 16;
+          const bool emit = act && uint64_t(xs) >= (uint64_t(fs) << 20);
+          const uint64_t mk = __ballot(emit);
+          const uint32_t ne = uint32_t(__popcll(mk));
+          if (emit) {
+            reg[wpos - ne + uint32_t(__popcll(mk & below))] = uint16_t(xs & 0xFFFFu);
+            xs >>= 16;
+          }
+          wpos -= ne;
+          if (act) {
+            uint32_t r;
+            const uint32_t q = div_by_freq(xs, fs, rs, r);
+            xs = q * kRansM + r + cs;
+            out[sm_pos + start + vv[k]] = uint8_t(((xv[k] >> 8) & 0x80u) | (xv[k] & 0x7Fu));
+          }
+        }
       }
-      wpos -= ne;
-      if (act) {
-        uint32_t r;
-        const uint32_t q = div_by_freq(xs, fs, rs, r);
-        xs = q * kRansM + r + cs;
+#pragma unroll
+      for (uint32_t k = 0; k < kRansWin; k++) {
+        xv[k] = xn[k];
+        vv[k] = vn[k];
       }
-      fc_c = fc_n;
-      rs_c = rs_n;
-      sym_n = sym_nn;
+      t0 -= int32_t(kRansWin);
     }
     wpos -= 2u * kRansStates;
-    slot16[wpos + 2u * lane] = uint16_t(xs & 0xFFFFu);
-    slot16[wpos + 2u * lane + 1u] = uint16_t(xs >> 16);
-    const uint32_t lo_s = s_lohi & 0xFFu, hi_s = s_lohi >> 8;
-    const uint32_t span = hi_s - lo_s + 1u;
-    const uint32_t nwords = kRansSlot / 2u - wpos;
-    const uint32_t beg = 2u * wpos - 8u - 2u * span;  // payload start in the slot (even)
-    for (uint32_t k = lane; k < span; k += 64u) slot16[beg / 2u + 4u + k] = uint16_t(s_f[lo_s + k]);
-    if (lane == 0) {
-      slot16[beg / 2u] = uint16_t(lo_s | (hi_s << 8));
-      slot16[beg / 2u + 1u] = 0u;
-      slot16[beg / 2u + 2u] = uint16_t(nwords & 0xFFFFu);
-      slot16[beg / 2u + 3u] = uint16_t(nwords >> 16);
-      s_start = beg;
-      s_bytes = 8u + 2u * span + 2u * nwords;
-    }
+    reg[wpos + 2u * lane] = uint16_t(xs & 0xFFFFu);
+    reg[wpos + 2u * lane + 1u] = uint16_t(xs >> 16);
   }
-  if (tid == 0 && !(m && ok)) {
-    s_start = 0;
-    s_bytes = 0;
+  if (lane == 0u) {
+    s_nw[wave] = kRansPartWords - wpos;
+    s_wpos[wave] = wpos;
   }
   __syncthreads();
-  const uint64_t bytes = s_bytes, padded = pad128(bytes);
+  const uint32_t lo_s = s_lohi & 0xFFu, hi_s = s_lohi >> 8;
+  const uint32_t span = hi_s - lo_s + 1u;
+  const uint32_t w0 = s_nw[0], w1 = s_nw[1], w2 = s_nw[2], w3 = s_nw[3];
+  const uint32_t words = w0 + w1 + w2 + w3;
+  const uint64_t bytes = (m && ok) ? kRansHead + 2u * span + 2u * uint64_t(words) : 0u;
+  const uint64_t padded = pad128(bytes);
 
-  // offset: publish the padded size, look back over the parts before
-  if (tid == 0) store_relaxed(&ws.rstat[uint64_t(p) * kRstatStride], kFlagSize | padded);
-  __shared__ uint64_t s_before;
-  __shared__ uint32_t s_found;
+  // offset: publish the padded size, look back over the chunks before
+  if (tid == 0) store_relaxed(&ws.rstat[c * kRstatStride], kFlagSize | padded);
   if (wave == 0) {
     uint64_t before = 0;
-    const bool found = part_lookback(ws.rstat, p, before);
+    const bool found = part_lookback(ws.rstat, c, before);
     if (lane == 0) {
       s_before = before;
       s_found = found ? 1u : 0u;
-      if (found) store_relaxed(&ws.rstat[uint64_t(p) * kRstatStride], kFlagIncl | (before + padded));
+      if (found) store_relaxed(&ws.rstat[c * kRstatStride], kFlagIncl | (before + padded));
     }
   }
   __syncthreads();
-  const uint32_t err = (!ok) ? uint32_t(CIERA_ERR_INTERNAL) : (s_found ? 0u : uint32_t(CIERA_ERR_INTERNAL));
-  if (tid == 0) ws.err[p] = err;
+  const uint32_t err = (!ok || !s_found) ? uint32_t(CIERA_ERR_INTERNAL) : 0u;
+  if (tid == 0) ws.err[c] = err;
   if (err) return;
-  const uint64_t pay_pos = rans_pay_pos(n, nchunks, kCiera);
-  const uint64_t at = pay_pos + s_before;
+  const uint64_t at = rans_pay_pos(n, nchunks, kCiera) + s_before;
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
   if (tid == 0) {
-    table[p] = at;
-    ws.rinfo[p] = uint64_t(m) | (uint64_t((h == kParts - 1u && kCiera) ? s_rank[kBitmapWords - 1] +
-                                                                            __popc(s_bits[kBitmapWords - 1])
-                                                                      : 0u)
-                                 << 32);
-    if (p + 1u == gridDim.x) table[p + 1u] = at + padded;
+    table[c] = at;
+    ws.rinfo[c] = uint64_t(m) |
+                  (uint64_t(kCiera ? s_rank[kBitmapWords - 1] + __popc(s_bits[kBitmapWords - 1]) : 0u) << 32);
+    if (c + 1u == nchunks) table[nchunks] = at + padded;
   }
-  // copy the payload (2-byte aligned in the slot) and zero the padding
-  const uint16_t* src = reinterpret_cast<const uint16_t*>(slot + s_start);
-  uint16_t* dst = reinterpret_cast<uint16_t*>(out + at);
-  for (uint32_t k = tid; k < bytes / 2u; k += kPartThreads) dst[k] = src[k];
-  for (uint64_t k = bytes + tid; k < padded; k += kPartThreads) out[at + k] = 0u;
-  // the chunk's bitmap (its last part)
-  if (kCiera && h == kParts - 1u && tid < kBitmapWords)
+  if (bytes) {
+    // head, table, then the part streams (u16 aligned: the payload starts on
+    // 128 bytes and its head and table take an even number of bytes)
+    uint16_t* dst = reinterpret_cast<uint16_t*>(out + at);
+    if (tid < 6u) {
+      const uint32_t v = (tid == 0) ? (lo_s | (hi_s << 8)) : (tid == 1) ? 0u : s_nw[tid - 2u];
+      dst[tid] = uint16_t(v);
+    }
+    for (uint32_t k = tid; k < span; k += kPartThreads) dst[kRansHead / 2u + k] = uint16_t(s_f[lo_s + k]);
+    uint16_t* ds = dst + kRansHead / 2u + span;
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(ws.rslot + c * uint64_t(kRansSlot));
+    for (uint32_t k = tid; k < words; k += kPartThreads) {
+      uint32_t h = 0, off = k;
+      if (off >= w0) { off -= w0; h = 1u;
+        if (off >= w1) { off -= w1; h = 2u;
+          if (off >= w2) { off -= w2; h = 3u; } } }
+      ds[k] = src[h * kRansPartWords + s_wpos[h] + off];
+    }
+    for (uint64_t k = bytes + tid; k < padded; k += kPartThreads) out[at + k] = 0u;
+  }
+  // the chunk's bitmap
+  if (kCiera && tid < kBitmapWords)
     *reinterpret_cast<uint32_t*>(out + sm_pos + pad128(n) + 128u * c + 4u * tid) = s_bits[tid];
 }
 
-// Header and the part table's padding; the totals of coded symbols and
-// changed blocks from the parts' records.  One workgroup.
+// Header and the chunk table's padding; the totals of coded symbols and
+// changed blocks from the chunks' records.  One workgroup.
 __global__ __launch_bounds__(kThreads) void k_rans_finish(uint64_t n, uint64_t nchunks, uint32_t B,
                                                           uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
                                                           Ws ws) {
   __shared__ uint64_t s_m[kThreads / 64u], s_c[kThreads / 64u];
   const uint32_t tid = threadIdx.x;
-  const uint64_t P = kParts * nchunks;
   uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
-  if (tid == 0) ws.ctrl->n_err_slots = P;
+  if (tid == 0) ws.ctrl->n_err_slots = nchunks;
   uint64_t m = 0, ch = 0;
-  for (uint64_t i = tid; i < P; i += kThreads) {
+  for (uint64_t i = tid; i < nchunks; i += kThreads) {
     const uint64_t r = ws.rinfo[i];
     m += r & 0xFFFFFFFFu;
     ch += r >> 32;
@@ -2418,7 +2464,7 @@ __global__ __launch_bounds__(kThreads) void k_rans_finish(uint64_t n, uint64_t n
     s_c[tid >> 6] = ch;
   }
   const uint64_t sm_pos = rans_sm_pos(nchunks);
-  for (uint64_t i = P + 1u + tid; i < (sm_pos - kHeader) / 8u; i += kThreads) table[i] = 0u;
+  for (uint64_t i = nchunks + 1u + tid; i < (sm_pos - kHeader) / 8u; i += kThreads) table[i] = 0u;
   __syncthreads();
   if (tid == 0) {
     uint64_t tm = 0, tc = 0;
@@ -2427,10 +2473,10 @@ __global__ __launch_bounds__(kThreads) void k_rans_finish(uint64_t n, uint64_t n
       tc += s_c[w];
     }
     const bool ciera = B != 0u;
-    if (P == 0u) table[0] = rans_pay_pos(n, nchunks, ciera);
-    const uint64_t total = table[P];
+    if (nchunks == 0u) table[0] = rans_pay_pos(n, nchunks, ciera);
+    const uint64_t total = table[nchunks];
     const uint32_t magic = ciera ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
-    hd[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(ciera ? 3u : 2u) << 48);
+    hd[0] = uint64_t(magic) | (uint64_t(kRansVersion) << 32) | (uint64_t(ciera ? 3u : 2u) << 48);
     hd[1] = n;
     hd[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
     hd[3] = nchunks;
@@ -2451,23 +2497,19 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
                                                            uint64_t* __restrict__ n_err_slots,
                                                            uint32_t* __restrict__ err_slots) {
   __shared__ __attribute__((aligned(16))) uint8_t s_stage[kRansStage];
-  // decoded symbols; before decoding its first 2 KB hold f and cum per symbol
-  __shared__ __attribute__((aligned(16))) uint8_t s_sym[kPartValues];
   // per slot: symbol | (f - 1) << 8 | (slot - cum) << 20
   __shared__ uint32_t s_dtab[kRansM];
-  uint32_t* s_f = reinterpret_cast<uint32_t*>(s_sym);
-  uint32_t* s_cum = s_f + kBins;
+  __shared__ uint32_t s_f[kBins], s_cum[kBins];
+  __shared__ uint16_t s_gl[kParts][kGranules];
   __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
-  __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
   __shared__ uint32_t s_w[kPartWaves];
+  __shared__ uint32_t s_m[kParts], s_nw[kParts];
   __shared__ uint32_t s_ok;
   __shared__ uint64_t s_a, s_b;
   const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
-  const uint32_t p = blockIdx.x;
-  const uint64_t c = p / kParts;
-  const uint32_t h = p % kParts;
+  const uint64_t c = blockIdx.x;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
-  const uint64_t P = kParts * nchunks;
+  const uint32_t log2G = kCiera ? min(log2B, 14u) : 14u;
   const uint64_t sm_pos = rans_sm_pos(nchunks);
   const uint64_t bm_pos = sm_pos + pad128(n);
   const uint64_t pay_pos = rans_pay_pos(n, nchunks, kCiera);
@@ -2479,35 +2521,33 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
       ok = 0u;
     } else {
       const uint32_t magic = kCiera ? 0x52454943u : 0x3350495Au;
-      ok &= hd[0] == (uint64_t(magic) | (1ull << 32) | (uint64_t(kCiera ? 3u : 2u) << 48));
+      ok &= hd[0] == (uint64_t(magic) | (uint64_t(kRansVersion) << 32) | (uint64_t(kCiera ? 3u : 2u) << 48));
       ok &= hd[1] == n;
       ok &= hd[2] == (uint64_t(B) | (uint64_t(kChunk) << 32));
       ok &= hd[3] == nchunks;
       ok &= hd[4] == in_size;
       for (int i = 7; i < 16; i++) ok &= hd[i] == 0u;
       const uint64_t* table = reinterpret_cast<const uint64_t*>(in + kHeader);
-      ok &= table[0] == pay_pos && table[P] == in_size;
-      if (ok && P > 0u) {
-        a = table[p];
-        b = table[p + 1u];
+      ok &= table[0] == pay_pos && table[nchunks] == in_size;
+      if (ok && nchunks > 0u) {
+        a = table[c];
+        b = table[c + 1u];
         ok &= a >= pay_pos && a <= b && b <= in_size && ((a | b) & 127u) == 0u;
       }
     }
     s_ok = ok;
     s_a = a;
     s_b = b;
-    if (p == 0u) *n_err_slots = gridDim.x;
+    if (c == 0u) *n_err_slots = gridDim.x;
   }
   __syncthreads();
-  if (!s_ok || P == 0u) {  // an empty tensor: the header and table are all there is
-    if (tid == 0) err_slots[p] = s_ok ? 0u : uint32_t(CIERA_ERR_FORMAT);
+  if (!s_ok || nchunks == 0u) {  // an empty tensor: the header and table are all there is
+    if (tid == 0) err_slots[c] = s_ok ? 0u : uint32_t(CIERA_ERR_FORMAT);
     return;
   }
   const uint64_t a = s_a, b = s_b;
   const uint64_t start = c * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
-  const uint32_t nunits = (nc + 7u) / 8u;
-  const uint32_t pu0 = h * kPartUnits;
   bool bad = false;
   if (kCiera && tid < 64u) {
     const uint32_t w = (tid < kBitmapWords) ? *reinterpret_cast<const uint32_t*>(in + bm_pos + 128u * c + 4u * tid) : 0u;
@@ -2516,51 +2556,52 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
     const uint32_t lo_bit = 32u * tid;
     const uint32_t valid = (lo_bit >= nb) ? 0u : ((nb - lo_bit >= 32u) ? ~0u : ((1u << (nb - lo_bit)) - 1u));
     if (w & ~valid) bad = true;
-    stage_bitmap(w, s_bits, s_rank);
+    stage_bitmap(w & valid, s_bits, s_rank);
   }
-  // sign+mantissa bytes, and the receiver cache of unchanged units
-  uint2 sm[kUPT], old[kUPT];
-  uint32_t cnt[kUPT], base[kUPT];
   __syncthreads();
-#pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
-    cnt[j] = 0u;
-    sm[j] = old[j] = make_uint2(0u, 0u);
-    if (u < nunits) {
+  const uint32_t mh = part_granules(wave, nc, log2B, log2G, kCiera, s_bits, s_gl[wave]);
+  if (lane == 0u) s_m[wave] = mh;
+  if (kCiera) {
+    // values of unchanged blocks: sign+mantissa byte and the receiver cache
+    const uint32_t nunits = (nc + 7u) / 8u;
+    for (uint32_t u = tid; u < nunits; u += kPartThreads) {
+      const uint32_t blk = (8u * u) >> log2B;
+      if ((s_bits[blk >> 5] >> (blk & 31u)) & 1u) continue;
       const uint32_t k = min(8u, nc - 8u * u);
-      sm[j] = load_bytes8(in + sm_pos + start + 8ull * u, k);
-      bool coded = true;
-      if (kCiera) {
-        const uint32_t blk = (8u * u) >> log2B;
-        coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
-        if (!coded) old[j] = load_bytes8(cache + start + 8ull * u, k);
-      }
-      cnt[j] = coded ? k : 0u;
+      const uint2 sm = load_bytes8(in + sm_pos + start + 8ull * u, k);
+      const uint2 e = load_bytes8(cache + start + 8ull * u, k);
+      store_unit(y, start + 8ull * u, k, unit_join(sm, e));
     }
   }
-  const uint32_t m = part_escape_scan(cnt, base, s_tot);
+  __syncthreads();
+  const uint32_t m = s_m[0] + s_m[1] + s_m[2] + s_m[3];
   const uint64_t len_pad = b - a;
-  uint32_t nwords = 0, lo = 0, hi = 0;
+  uint32_t lo = 0, hi = 0, words = 0;
   uint64_t len = 0;
   if (m == 0u) {
     bad |= len_pad != 0u;
-  } else if (len_pad < 8u) {
+  } else if (len_pad < kRansHead) {
     bad = true;
   } else {
     lo = in[a];
     hi = in[a + 1];
-    nwords = uint32_t(in[a + 4]) | (uint32_t(in[a + 5]) << 8) | (uint32_t(in[a + 6]) << 16) |
-             (uint32_t(in[a + 7]) << 24);
-    len = 8u + 2u * uint64_t(hi >= lo ? hi - lo + 1u : 0u) + 2u * uint64_t(nwords);
-    bad |= hi < lo || in[a + 2] != 0u || in[a + 3] != 0u || nwords < 2u * kRansStates || pad128(len) != len_pad;
+    const uint16_t* hw = reinterpret_cast<const uint16_t*>(in + a);
+    bad |= hi < lo || hw[1] != 0u;
+    for (uint32_t h = 0; h < kParts; h++) {
+      const uint32_t w = hw[2u + h];
+      words += w;
+      // a part codes its values exactly when it has a stream, which holds at least the states
+      bad |= (s_m[h] == 0u) != (w == 0u) || (w != 0u && w < 2u * kRansStates);
+      if (tid == 0) s_nw[h] = w;
+    }
+    len = kRansHead + 2u * uint64_t(hi >= lo ? hi - lo + 1u : 0u) + 2u * uint64_t(words);
+    bad |= pad128(len) != len_pad;
   }
   if (part_sum_u32(bad ? 1u : 0u, s_w) != 0u) {
-    if (tid == 0) err_slots[p] = uint32_t(CIERA_ERR_FORMAT);
+    if (tid == 0) err_slots[c] = uint32_t(CIERA_ERR_FORMAT);
     return;
   }
   const uint32_t span = hi - lo + 1u;
-  const uint64_t wbyte = 8u + 2u * span;  // the words' offset in the payload
   bool pad_bad = false;
   if (m) {
     // stage the payload's first kRansStage bytes (16-byte loads), check the padding
@@ -2570,12 +2611,13 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
     for (uint64_t k = len + tid; k < len_pad; k += kPartThreads) pad_bad |= in[a + k] != 0u;
   }
   __syncthreads();
-  // frequencies (one symbol per thread) and the slot -> symbol map
+  // frequencies (one symbol per thread), then the slot table: thread t fills
+  // slots 16 t .. 16 t + 15, the first symbol by binary search over the
+  // cumulative counts, the rest by stepping
   uint32_t f = 0;
   if (m && tid >= lo && tid <= hi) {
-    const uint64_t o = 8u + 2u * (tid - lo);
-    f = (o + 1u < kRansStage) ? (uint32_t(s_stage[o]) | (uint32_t(s_stage[o + 1]) << 8))
-                              : (uint32_t(in[a + o]) | (uint32_t(in[a + o + 1]) << 8));
+    const uint32_t o = kRansHead + 2u * (tid - lo);  // within the first 524 bytes: always staged
+    f = uint32_t(s_stage[o]) | (uint32_t(s_stage[o + 1u]) << 8);
   }
   const uint32_t fsum = part_sum_u32(f, s_w);
   const uint32_t cum_incl = part_incl_scan_u32(f, s_w);
@@ -2584,80 +2626,94 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
   __syncthreads();
   const bool table_ok = (m == 0u) || fsum == kRansM;
   if (m && table_ok) {
-    for (uint32_t k = tid; k < kRansM; k += kPartThreads) {
-      // the symbol whose range [cum, cum + f) holds slot k: the first s with cum_s + f_s > k
-      uint32_t lo_s = 0, hi_s = 255u;
-      while (lo_s < hi_s) {
-        const uint32_t mid = (lo_s + hi_s) >> 1;
-        if (s_cum[mid] + s_f[mid] > k) hi_s = mid; else lo_s = mid + 1u;
+    const uint32_t k0 = 16u * tid;
+    uint32_t lo_s = 0, hi_s = 255u;
+    while (lo_s < hi_s) {  // the first s with cum_s + f_s > k0
+      const uint32_t mid = (lo_s + hi_s) >> 1;
+      if (s_cum[mid] + s_f[mid] > k0) hi_s = mid; else lo_s = mid + 1u;
+    }
+    uint32_t s = lo_s, cs = s_cum[s], fs = s_f[s];
+    for (uint32_t k = k0; k < k0 + 16u; k++) {
+      while (cs + fs <= k) {  // ends: the counts sum to 4096 > k
+        s++;
+        cs = s_cum[s];
+        fs = s_f[s];
       }
-      s_dtab[k] = lo_s | ((s_f[lo_s] - 1u) << 8) | ((k - s_cum[lo_s]) << 20);
+      s_dtab[k] = s | ((fs - 1u) << 8) | ((k - cs) << 20);
     }
   }
   __syncthreads();
-  // wave 0 decodes the 64 states
-  __shared__ uint32_t s_dec_ok;
-  if (wave == 0) {
-    bool okd = table_ok;
-    if (m && okd) {
-      auto word = [&](uint64_t k) -> uint32_t {  // payload word k of the words region
-        const uint64_t o = wbyte + 2u * k;
-        return (o + 1u < kRansStage) ? (uint32_t(s_stage[o]) | (uint32_t(s_stage[o + 1]) << 8))
-                                     : (uint32_t(in[a + o]) | (uint32_t(in[a + o + 1]) << 8));
-      };
-      uint32_t xs = word(2u * lane) | (word(2u * lane + 1u) << 16);
-      okd = xs >= kRansL;
-      uint64_t q = 2u * kRansStates;
-      const uint64_t below = (1ull << lane) - 1u;
-      const uint32_t steps = uint32_t(cdiv(m, kRansStates));
-      for (uint32_t t = 0; t < steps; t++) {
-        const uint32_t i = t * kRansStates + lane;
-        const bool act = i < m;
-        uint32_t sym = 0;
-        if (act) {
-          const uint32_t e = s_dtab[xs & (kRansM - 1u)];
-          sym = e & 0xFFu;
-          xs = (((e >> 8) & 0xFFFu) + 1u) * (xs >> 12) + (e >> 20);
-        }
-        const bool need = act && xs < kRansL;
-        const uint64_t mk = __ballot(need);
-        if (need) {
-          const uint64_t k = q + uint64_t(__popcll(mk & below));
-          if (k < nwords) xs = (xs << 16) | word(k); else okd = false;
-        }
-        q += uint64_t(__popcll(mk));
-        if (act) s_sym[i] = uint8_t(sym);
+  // Wave h decodes part h; each symbol goes straight to y (and, in ciera
+  // mode, to the receiver cache) with its sign+mantissa byte, loaded
+  // kRansWin steps ahead.
+  bool okd = table_ok;
+  if (mh && okd) {
+    uint32_t so = kRansHead + 2u * span;  // the part's stream in the payload (bytes)
+    for (uint32_t h = 0; h < wave; h++) so += 2u * s_nw[h];
+    const uint32_t nw = s_nw[wave];
+    const uint16_t* stage16 = reinterpret_cast<const uint16_t*>(s_stage);
+    const uint16_t* in16 = reinterpret_cast<const uint16_t*>(in + a);
+    auto word = [&](uint32_t k) -> uint32_t {  // word k of the part's stream
+      const uint32_t o = so + 2u * k;
+      return (o + 2u <= kRansStage) ? uint32_t(stage16[o / 2u]) : uint32_t(in16[o / 2u]);
+    };
+    const uint16_t* gl = s_gl[wave];
+    const uint32_t gmask = (1u << log2G) - 1u;
+    auto fetch = [&](uint32_t t, uint32_t& smb, uint32_t& vi) {
+      const uint32_t i = t * kRansStates + lane;
+      smb = 0u;
+      vi = 0u;
+      if (i < mh) {
+        vi = kCiera ? ((uint32_t(gl[i >> log2G]) << log2G) | (i & gmask)) : (wave * kPartValues + i);
+        smb = in[sm_pos + start + vi];
       }
-      okd = okd && q == nwords && xs == kRansL;
-    }
-    const bool all_ok = __ballot(!okd) == 0u;
-    if (lane == 0) s_dec_ok = all_ok ? 1u : 0u;
-  }
-  __syncthreads();
-  const bool dec_ok = s_dec_ok != 0u && part_sum_u32(pad_bad ? 1u : 0u, s_w) == 0u;
-  if (!dec_ok) {
-    if (tid == 0) err_slots[p] = uint32_t(CIERA_ERR_FORMAT);
-    return;
-  }
-  // merge: exponents from the decoded symbols (coded units) or the cache
+    };
+    uint32_t xs = word(2u * lane) | (word(2u * lane + 1u) << 16);
+    okd = xs >= kRansL;
+    uint32_t q = 2u * kRansStates;
+    const uint64_t below = (1ull << lane) - 1u;
+    const uint32_t steps = cdiv(mh, kRansStates);
+    uint32_t sv[kRansWin], vv[kRansWin];
 #pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
-    if (u >= nunits) continue;
-    const uint32_t k = min(8u, nc - 8u * u);
-    uint2 e = old[j];
-    if (cnt[j]) {
-      uint32_t lo4 = 0, hi4 = 0;
-      for (uint32_t q = 0; q < k; q++) {
-        const uint32_t sb = s_sym[base[j] + q];
-        if (q < 4u) lo4 |= sb << (8u * q); else hi4 |= sb << (8u * (q - 4u));
+    for (uint32_t k = 0; k < kRansWin; k++) fetch(k, sv[k], vv[k]);
+    for (uint32_t t0 = 0; t0 < steps; t0 += kRansWin) {
+      uint32_t sn[kRansWin], vn[kRansWin];
+#pragma unroll
+      for (uint32_t k = 0; k < kRansWin; k++) fetch(t0 + kRansWin + k, sn[k], vn[k]);
+#pragma unroll
+      for (uint32_t k = 0; k < kRansWin; k++) {
+        const uint32_t t = t0 + k;
+        if (t < steps) {
+          const bool act = t * kRansStates + lane < mh;
+          uint32_t sym = 0;
+          if (act) {
+            const uint32_t e = s_dtab[xs & (kRansM - 1u)];
+            sym = e & 0xFFu;
+            xs = (((e >> 8) & 0xFFFu) + 1u) * (xs >> 12) + (e >> 20);
+          }
+          const bool need = act && xs < kRansL;
+          const uint64_t mk = __ballot(need);
+          if (need) {
+            const uint32_t kk = q + uint32_t(__popcll(mk & below));
+            if (kk < nw) xs = (xs << 16) | word(kk); else okd = false;
+          }
+          q += uint32_t(__popcll(mk));
+          if (act) {
+            y[start + vv[k]] = uint16_t(((sv[k] & 0x80u) << 8) | (sym << 7) | (sv[k] & 0x7Fu));
+            if (kCiera) cache[start + vv[k]] = uint8_t(sym);
+          }
+        }
       }
-      e = make_uint2(lo4, hi4);
-      if (kCiera) store_bytes8(cache + start + 8ull * u, k, e);
+#pragma unroll
+      for (uint32_t k = 0; k < kRansWin; k++) {
+        sv[k] = sn[k];
+        vv[k] = vn[k];
+      }
     }
-    store_unit(y, start + 8ull * u, k, unit_join(sm[j], e));
+    okd = okd && q == nw && xs == kRansL;
   }
-  if (tid == 0) err_slots[p] = 0u;
+  const bool dec_ok = part_sum_u32((okd && !pad_bad) ? 0u : 1u, s_w) == 0u;
+  if (tid == 0) err_slots[c] = dec_ok ? 0u : uint32_t(CIERA_ERR_FORMAT);
 }
 
 // ------------------------------------------------------------------ host side
@@ -2786,29 +2842,30 @@ ciera_status encode_known_e0_impl(const void* d_x, uint64_t n, const uint8_t* d_
   return launch_status();
 }
 
-// rANS modes: the workspace of the 3-bit path followed by, per part, the
+// rANS modes: the workspace of the 3-bit path followed by, per chunk, the
 // look-back word, the coded-count record and a payload scratch slot.
 uint64_t rans_ws_size(uint64_t n) {
-  const uint64_t nchunks = cdiv(n, kChunk), P = kParts * nchunks;
-  return ws_layout(nchunks).total + align256(8u * kRstatStride * P) + align256(8u * P) + P * uint64_t(kRansSlot);
+  const uint64_t nchunks = cdiv(n, kChunk);
+  return ws_layout(nchunks).total + align256(8u * kRstatStride * nchunks) + align256(8u * nchunks) +
+         nchunks * uint64_t(kRansSlot);
 }
 
 Ws rans_ws_bind(void* base, uint64_t n) {
-  const uint64_t nchunks = cdiv(n, kChunk), P = kParts * nchunks;
+  const uint64_t nchunks = cdiv(n, kChunk);
   Ws w = ws_bind(base, nchunks);
   uint8_t* b = static_cast<uint8_t*>(base) + ws_layout(nchunks).total;
   w.rstat = reinterpret_cast<uint64_t*>(b);
-  w.rinfo = reinterpret_cast<uint64_t*>(b + align256(8u * kRstatStride * P));
-  w.rslot = b + align256(8u * kRstatStride * P) + align256(8u * P);
+  w.rinfo = reinterpret_cast<uint64_t*>(b + align256(8u * kRstatStride * nchunks));
+  w.rslot = b + align256(8u * kRstatStride * nchunks) + align256(8u * nchunks);
   return w;
 }
 
 uint64_t rans_max_size(uint64_t n, uint32_t B) {
   const uint64_t nchunks = cdiv(n, kChunk);
   uint64_t size = rans_pay_pos(n, nchunks, B != 0u);
-  const uint64_t full = n / kPartValues, rem = n % kPartValues;
-  size += full * uint64_t(kRansSlot);
-  if (rem) size += pad128(8u + 512u + 256u + 2u * rem);
+  const uint64_t full = n / kChunk, rem = n % kChunk;
+  size += full * pad128(rans_chunk_max(kChunk));
+  if (rem) size += pad128(rans_chunk_max(rem));
   return size;
 }
 
@@ -2834,10 +2891,10 @@ ciera_status encode_rans_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* 
   if (nchunks) {
     if (ciera) {
       launch(k_stats<true, false>, dim3(parts), dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
-      launch(k_rans_enc<true>, dim3(parts), dim3(kPartThreads), stream, x, n, lb, out, ws);
+      launch(k_rans_enc<true>, dim3(uint32_t(nchunks)), dim3(kPartThreads), stream, x, n, nchunks, lb, out, ws);
     } else {
       launch(k_stats<false, false>, dim3(parts), dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
-      launch(k_rans_enc<false>, dim3(parts), dim3(kPartThreads), stream, x, n, 0u, out, ws);
+      launch(k_rans_enc<false>, dim3(uint32_t(nchunks)), dim3(kPartThreads), stream, x, n, nchunks, 0u, out, ws);
     }
   }
   launch(k_rans_finish, dim3(1), dim3(kThreads), stream, n, nchunks, B, out, d_out_size, ws);
@@ -2855,7 +2912,7 @@ ciera_status decode_rans_impl(const void* d_in, uint64_t in_size, void* d_y, uin
   const uint64_t nchunks = cdiv(n, kChunk);
   if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
   const Ws ws = ws_bind(d_ws, nchunks);
-  const uint32_t grid = uint32_t(nchunks ? nchunks * kParts : 1u);
+  const uint32_t grid = uint32_t(nchunks ? nchunks : 1u);
   const uint8_t* in = static_cast<const uint8_t*>(d_in);
   uint16_t* y = static_cast<uint16_t*>(d_y);
   (void)hipGetLastError();

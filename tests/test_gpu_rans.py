@@ -1,6 +1,9 @@
 """GPU parity of the rANS modes (zip3 + rANS, ciera + rANS): streams byte for
 byte equal to the oracle's, decode returns the input bit for bit, caches
-match, canary guards intact; malformed streams are rejected."""
+match, canary guards intact; malformed streams are rejected.  A chunk's
+four parts are coded by four waves against the chunk's one table; payloads
+beyond the decoder's 32 KB LDS stage (all 65536 patterns, random bits) take
+the HBM word path."""
 import numpy as np
 import pytest
 
@@ -78,16 +81,20 @@ def test_rans_decode_rejects_corruption():
     x = wl.normal_bf16(rng, 65536, 0.02)
     s, _ = gpu_encode_rans(x)
     a = int(s[128:136].view(np.uint64)[0])
-    nw = int(s[a + 4:a + 8].view(np.uint32)[0])
+    nw = [int(v) for v in s[a + 4:a + 12].view(np.uint16)]
     lo, hi = int(s[a]), int(s[a + 1])
-    words = a + 8 + 2 * (hi - lo + 1)
+    words = a + 12 + 2 * (hi - lo + 1)        # part 0's stream
+    words3 = words + 2 * sum(nw[:3])          # part 3's stream
     cases = {
         "mode byte": (6, 0),
-        "nwords": (a + 4, (nw + 1) & 0xFF),
-        "frequency": (a + 8, s[a + 8] ^ 1),
+        "version": (4, 1),
+        "part 0 word count": (a + 4, (nw[0] + 1) & 0xFF),
+        "part 2 word count": (a + 8, (nw[2] - 1) & 0xFF),
+        "frequency": (a + 12, s[a + 12] ^ 1),
         "renormalisation word": (words + 256 + 20, s[words + 256 + 20] ^ 0x10),
         "final state": (words + 3, s[words + 3] ^ 0x80),
-        "part table": (136, s[136] ^ 0x40),
+        "part 3 final state": (words3 + 130, s[words3 + 130] ^ 0x80),
+        "chunk table": (136, s[136] ^ 0x40),
     }
     for name, (at, val) in cases.items():
         t = s.copy()
