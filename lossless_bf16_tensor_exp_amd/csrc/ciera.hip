@@ -624,7 +624,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   double s1 = 0.0, s2 = 0.0;
   uint32_t nf = 0;
   uint32_t coded = kCiera ? 0u : 0xFFu;
-  const uint32_t L = (B >= 512u) ? 64u : B / 8u;
+  const uint32_t L = (B >= 512u) ? 64u : max(B / 8u, 8u);  // B >= 64 in ciera mode
   const uint64_t gmask = (L >= 64u) ? ~0ull : ((1ull << L) - 1u);
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
@@ -2115,7 +2115,7 @@ constexpr uint32_t kRansVersion = 2u;
 constexpr uint32_t kRansHead = 12u;                                 // payload bytes before the table
 constexpr uint32_t kRansPartWords = 2u * kRansStates + kPartValues;  // a part stream's largest word count
 constexpr uint32_t kRansSlot = kParts * 2u * kRansPartWords;         // scratch per chunk: one region per part
-constexpr uint32_t kRansStage = 32768u;  // payload bytes k_rans_dec stages in LDS (the rest read from HBM)
+constexpr uint32_t kRansBlock = 1024u;   // payload bytes per block of a decoding wave's LDS ring
 constexpr uint32_t kRansWin = 8u;        // steps whose inputs a coding wave loads ahead
 constexpr uint32_t kGranules = kPartValues / 64u;  // a part's largest granule count (B = 64)
 
@@ -2211,18 +2211,22 @@ __device__ inline uint32_t part_incl_scan_u32(uint32_t v, uint32_t* s_w) {
   return before + incl;
 }
 
-// x div f and x mod f for x < 2^32, 1 <= f <= 4096, by the FP64 reciprocal:
-// x * rcp is within 2^-20 of x / f, and x / f is at least 1/f from the next
-// integer above it, so the floor is the quotient or one less.
-__device__ inline uint32_t div_by_freq(uint32_t x, uint32_t f, double rcp, uint32_t& rem) {
-  uint32_t q = uint32_t(double(x) * rcp);
-  uint32_t r = x - q * f;
-  if (r >= f) {
-    q++;
-    r -= f;
-  }
-  rem = r;
-  return q;
+// One encoder state update, x = (x div f) M + (x mod f) + c, for
+// x < f 2^20 (the state after its renormalisation), 1 <= f <= 4096, with
+// rf = 1 / f rounded to FP32.  The FP32 product x rf has a relative error
+// below 3 2^-24, so it is within 2^20 * 3 2^-24 < 0.2 of x / f < 2^20, and
+// its truncation is the quotient or one off either way; the remainder, exact
+// in 32-bit arithmetic, says which, and one step corrects it.
+__device__ inline uint32_t rans_push(uint32_t x, uint32_t f, uint32_t c, float rf) {
+  uint32_t q = uint32_t(float(x) * rf);                    // < 2^21: a 24-bit product suffices
+  int32_t r = int32_t(x - __umul24(q, f));  // exact: |r| < 2 f
+  const int32_t neg = r >> 31;                              // -1 when the quotient was one too large
+  q += uint32_t(neg);
+  r += neg & int32_t(f);
+  const uint32_t over = (r >= int32_t(f)) ? 1u : 0u;        // one too small
+  q += over;
+  r -= int32_t(over * f);
+  return (q << 12) + uint32_t(r) + c;
 }
 
 template <bool kCiera>
@@ -2230,8 +2234,9 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
                                                            uint64_t nchunks, uint32_t log2B,
                                                            uint8_t* __restrict__ out, Ws ws) {
   __shared__ uint32_t s_f[kBins], s_fc[kBins];  // f; f | cum << 16
-  __shared__ double s_rcp[kBins];
+  __shared__ float s_rcp[kBins];                 // 1 / f, rounded to FP32
   __shared__ uint16_t s_gl[kParts][kGranules];
+  __shared__ __attribute__((aligned(16))) uint8_t s_sym[kPartWaves][kRansWin * kRansStates];
   __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
   __shared__ uint32_t s_w[kPartWaves];
   __shared__ uint32_t s_m[kParts], s_nw[kParts], s_wpos[kParts];
@@ -2293,7 +2298,7 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
   const uint32_t cum_incl = part_incl_scan_u32(f, s_w);
   s_f[tid] = f;
   s_fc[tid] = f | ((cum_incl - f) << 16);
-  s_rcp[tid] = f ? 1.0 / double(f) : 0.0;
+  s_rcp[tid] = f ? float(1.0 / double(f)) : 0.0f;
   // first and last symbol with f > 0
   uint32_t lo = f ? tid : 255u, hi = f ? tid : 0u;
   for (uint32_t o = 32; o >= 1; o >>= 1) {
@@ -2316,66 +2321,92 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
   const bool ok = s_ok != 0u;
 
   // Wave h codes part h, last step first, into its region of the chunk's
-  // scratch slot from the region's end.  Its inputs (the values, through
-  // the granule list) are loaded kRansWin steps ahead; each coded value's
-  // sign+mantissa byte is written on the way.
+  // scratch slot from the region's end.  It takes its symbols in groups of
+  // kRansWin steps (512 symbols): lane l loads the 8 values of symbols
+  // 512 g + 8 l .. + 7 (one 16-byte load, contiguous through the granule
+  // list), writes their sign+mantissa bytes (one 8-byte store) and stages
+  // their exponents in the wave's LDS buffer, from which each step reads its
+  // symbol.  A group's loads are issued while the group above it codes (two
+  // buffers take turns); the top group, the only one that can be partial,
+  // goes first on its own.
   uint16_t* reg = reinterpret_cast<uint16_t*>(ws.rslot + c * uint64_t(kRansSlot)) + wave * kRansPartWords;
   uint32_t wpos = kRansPartWords;
   if (mh && ok) {
     const uint16_t* gl = s_gl[wave];
+    uint8_t* sym = s_sym[wave];
     const uint32_t gmask = (1u << log2G) - 1u;
     const uint64_t below = (1ull << lane) - 1u;
-    auto fetch = [&](int32_t t, uint32_t& val, uint32_t& vi) {
-      val = 0u;
-      vi = 0u;
-      if (t >= 0) {
-        const uint32_t i = uint32_t(t) * kRansStates + lane;
-        if (i < mh) {
-          vi = kCiera ? ((uint32_t(gl[i >> log2G]) << log2G) | (i & gmask)) : (wave * kPartValues + i);
-          val = x[start + vi];
-        }
-      }
+    constexpr uint32_t kGroup = kRansWin * kRansStates;
+    auto value_of = [&](uint32_t i) -> uint32_t {  // chunk-relative value of the part's symbol i
+      return kCiera ? ((uint32_t(gl[i >> log2G]) << log2G) | (i & gmask)) : (wave * kPartValues + i);
     };
     uint32_t xs = kRansL;
-    int32_t t0 = int32_t(cdiv(mh, kRansStates)) - 1;  // the group's first (highest) step
-    uint32_t xv[kRansWin], vv[kRansWin];
-#pragma unroll
-    for (uint32_t k = 0; k < kRansWin; k++) fetch(t0 - int32_t(k), xv[k], vv[k]);
-    while (t0 >= 0) {
-      uint32_t xn[kRansWin], vn[kRansWin];
-#pragma unroll
-      for (uint32_t k = 0; k < kRansWin; k++) fetch(t0 - int32_t(kRansWin + k), xn[k], vn[k]);
-#pragma unroll
-      for (uint32_t k = 0; k < kRansWin; k++) {
-        const int32_t t = t0 - int32_t(k);
-        if (t >= 0) {
-          const bool act = uint32_t(t) * kRansStates + lane < mh;
-          const uint32_t e = (xv[k] >> 7) & 0xFFu;
-          const uint32_t fc = s_fc[e];
-          const double rs = s_rcp[e];
-          const uint32_t fs = fc & 0xFFFFu, cs = fc >> 16;
-          const bool emit = act && uint64_t(xs) >= (uint64_t(fs) << 20);
-          const uint64_t mk = __ballot(emit);
-          const uint32_t ne = uint32_t(__popcll(mk));
-          if (emit) {
-            reg[wpos - ne + uint32_t(__popcll(mk & below))] = uint16_t(xs & 0xFFFFu);
-            xs >>= 16;
-          }
-          wpos -= ne;
-          if (act) {
-            uint32_t r;
-            const uint32_t q = div_by_freq(xs, fs, rs, r);
-            xs = q * kRansM + r + cs;
-            out[sm_pos + start + vv[k]] = uint8_t(((xv[k] >> 8) & 0x80u) | (xv[k] & 0x7Fu));
-          }
-        }
-      }
+    auto code = [&](uint32_t t, uint32_t fc, float rf, bool full) {
+      const bool act = full || t * kRansStates + lane < mh;
+      const uint32_t fs = fc & 0xFFFFu, cs = fc >> 16;
+      const bool emit = act && (xs >> 20) >= fs;  // x >= f 2^20
+      const uint64_t mk = __ballot(emit);
+      const uint32_t ne = uint32_t(__popcll(mk));
+      if (emit) reg[wpos - ne + uint32_t(__popcll(mk & below))] = uint16_t(xs & 0xFFFFu);
+      xs = emit ? (xs >> 16) : xs;
+      wpos -= ne;
+      const uint32_t xn = rans_push(xs, fs, cs, rf);
+      xs = act ? xn : xs;
+    };
+    // one group: the lane's sign+mantissa bytes out, its exponents staged,
+    // then the group's steps from the highest
+    auto group = [&](uint32_t g, const Unit& u, uint32_t vi, uint32_t cnt, bool full) {
+      store_bytes8(out + sm_pos + start + vi, cnt, unit_sm(u));
+      *reinterpret_cast<uint2*>(sym + 8u * lane) = unit_exponents(u);
+      __builtin_amdgcn_wave_barrier();
+      // the steps' table entries, read before the state chain needs them
+      uint32_t fcv[kRansWin];
+      float rfv[kRansWin];
 #pragma unroll
       for (uint32_t k = 0; k < kRansWin; k++) {
-        xv[k] = xn[k];
-        vv[k] = vn[k];
+        const uint32_t e = sym[k * kRansStates + lane];
+        fcv[k] = s_fc[e];
+        rfv[k] = s_rcp[e];
       }
-      t0 -= int32_t(kRansWin);
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int32_t k = int32_t(kRansWin) - 1; k >= 0; k--) {
+        const uint32_t t = g * kRansWin + uint32_t(k);
+        if (full || t * kRansStates < mh) code(t, fcv[k], rfv[k], full);
+      }
+    };
+    const uint32_t ng = cdiv(mh, kGroup);
+    {
+      const uint32_t i0 = (ng - 1u) * kGroup + 8u * lane;
+      const uint32_t cnt = (i0 < mh) ? min(8u, mh - i0) : 0u;
+      const uint32_t vi = value_of(cnt ? i0 : 0u);
+      Unit u;
+      u.w[0] = u.w[1] = u.w[2] = u.w[3] = 0u;
+      if (cnt) u = load_unit(x, start + vi, cnt);
+      group(ng - 1u, u, vi, cnt, false);
+    }
+    if (ng >= 2u) {
+      // full groups: every lane has 8 values, so every load is issued
+      auto fetch = [&](uint32_t g, Unit& u, uint32_t& vi) {
+        vi = value_of(g * kGroup + 8u * lane);
+        const uint4 v = *reinterpret_cast<const uint4*>(x + start + vi);
+        u.w[0] = v.x;
+        u.w[1] = v.y;
+        u.w[2] = v.z;
+        u.w[3] = v.w;
+      };
+      Unit ua, ub;
+      uint32_t va, vb;
+      uint32_t g = ng - 2u;
+      fetch(g, ua, va);
+      while (true) {
+        fetch(g ? g - 1u : 0u, ub, vb);
+        group(g, ua, va, 8u, true);
+        if (g-- == 0u) break;
+        fetch(g ? g - 1u : 0u, ua, va);
+        group(g, ub, vb, 8u, true);
+        if (g-- == 0u) break;
+      }
     }
     wpos -= 2u * kRansStates;
     reg[wpos + 2u * lane] = uint16_t(xs & 0xFFFFu);
@@ -2496,10 +2527,17 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
                                                            uint32_t log2B, uint8_t* __restrict__ cache,
                                                            uint64_t* __restrict__ n_err_slots,
                                                            uint32_t* __restrict__ err_slots) {
-  __shared__ __attribute__((aligned(16))) uint8_t s_stage[kRansStage];
+  // per wave, a ring of 4 payload blocks of 1 KB (block j in slot j mod 4)
+  __shared__ __attribute__((aligned(16))) uint8_t s_ring[kPartWaves][4u * kRansBlock];
   // per slot: symbol | (f - 1) << 8 | (slot - cum) << 20
   __shared__ uint32_t s_dtab[kRansM];
-  __shared__ uint32_t s_f[kBins], s_cum[kBins];
+  // f and cum per symbol while the slot table is built, then the waves'
+  // decoded-symbol buffers (kRansWin steps each)
+  __shared__ __attribute__((aligned(16))) uint32_t s_fcum[2u * kBins];
+  static_assert(2u * kBins * 4u >= kPartWaves * kRansWin * kRansStates, "symbol buffers fit");
+  uint32_t* s_f = s_fcum;
+  uint32_t* s_cum = s_fcum + kBins;
+  uint8_t* s_sym = reinterpret_cast<uint8_t*>(s_fcum);
   __shared__ uint16_t s_gl[kParts][kGranules];
   __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
   __shared__ uint32_t s_w[kPartWaves];
@@ -2603,21 +2641,15 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
   }
   const uint32_t span = hi - lo + 1u;
   bool pad_bad = false;
-  if (m) {
-    // stage the payload's first kRansStage bytes (16-byte loads), check the padding
-    const uint64_t stage = min(len_pad, uint64_t(kRansStage));
-    for (uint64_t k = 16u * tid; k < stage; k += 16u * kPartThreads)
-      *reinterpret_cast<uint4*>(s_stage + k) = *reinterpret_cast<const uint4*>(in + a + k);
+  if (m)
     for (uint64_t k = len + tid; k < len_pad; k += kPartThreads) pad_bad |= in[a + k] != 0u;
-  }
-  __syncthreads();
   // frequencies (one symbol per thread), then the slot table: thread t fills
   // slots 16 t .. 16 t + 15, the first symbol by binary search over the
   // cumulative counts, the rest by stepping
   uint32_t f = 0;
   if (m && tid >= lo && tid <= hi) {
-    const uint32_t o = kRansHead + 2u * (tid - lo);  // within the first 524 bytes: always staged
-    f = uint32_t(s_stage[o]) | (uint32_t(s_stage[o + 1u]) << 8);
+    const uint64_t o = a + kRansHead + 2u * (tid - lo);
+    f = uint32_t(in[o]) | (uint32_t(in[o + 1u]) << 8);
   }
   const uint32_t fsum = part_sum_u32(f, s_w);
   const uint32_t cum_incl = part_incl_scan_u32(f, s_w);
@@ -2651,64 +2683,118 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
     uint32_t so = kRansHead + 2u * span;  // the part's stream in the payload (bytes)
     for (uint32_t h = 0; h < wave; h++) so += 2u * s_nw[h];
     const uint32_t nw = s_nw[wave];
-    const uint16_t* stage16 = reinterpret_cast<const uint16_t*>(s_stage);
-    const uint16_t* in16 = reinterpret_cast<const uint16_t*>(in + a);
+    // The part's words come through the wave's ring: payload block j (bytes
+    // 1024 j .. 1024 j + 1023) sits in slot j mod 4.  Each group first stores
+    // the block loaded during the group before, then loads the block two
+    // past the one holding the next unread word (the last block at most).
+    // A group reads at most 512 words (one block), so every word it reads is
+    // in the ring: the unread word's block and the next were loaded earlier,
+    // and the four slots hold them until then.  Lanes whose part of a block
+    // lies past the payload read its last 16 bytes instead (never used).
+    uint8_t* ring = s_ring[wave];
+    const uint16_t* ring16 = reinterpret_cast<const uint16_t*>(ring);
+    const uint32_t jmax = uint32_t((len_pad - 1u) / kRansBlock);
+    const uint64_t gmax = a + len_pad - 16u;
+    auto block_load = [&](uint32_t j) -> uint4 {
+      const uint64_t ad = min(a + uint64_t(j) * kRansBlock + 16u * lane, gmax);
+      return *reinterpret_cast<const uint4*>(in + ad);
+    };
+    auto block_store = [&](uint32_t j, uint4 v) {
+      *reinterpret_cast<uint4*>(ring + (j & 3u) * kRansBlock + 16u * lane) = v;
+    };
     auto word = [&](uint32_t k) -> uint32_t {  // word k of the part's stream
       const uint32_t o = so + 2u * k;
-      return (o + 2u <= kRansStage) ? uint32_t(stage16[o / 2u]) : uint32_t(in16[o / 2u]);
+      return ring16[((o / kRansBlock) & 3u) * (kRansBlock / 2u) + (o % kRansBlock) / 2u];
     };
+    {
+      const uint32_t j0 = so / kRansBlock;
+      const uint4 b0 = block_load(min(j0, jmax)), b1 = block_load(min(j0 + 1u, jmax)),
+                  b2 = block_load(min(j0 + 2u, jmax));
+      block_store(min(j0, jmax), b0);
+      block_store(min(j0 + 1u, jmax), b1);
+      block_store(min(j0 + 2u, jmax), b2);
+      __builtin_amdgcn_wave_barrier();
+    }
     const uint16_t* gl = s_gl[wave];
+    uint8_t* sym = s_sym + wave * kRansWin * kRansStates;
     const uint32_t gmask = (1u << log2G) - 1u;
-    auto fetch = [&](uint32_t t, uint32_t& smb, uint32_t& vi) {
-      const uint32_t i = t * kRansStates + lane;
-      smb = 0u;
-      vi = 0u;
-      if (i < mh) {
-        vi = kCiera ? ((uint32_t(gl[i >> log2G]) << log2G) | (i & gmask)) : (wave * kPartValues + i);
-        smb = in[sm_pos + start + vi];
-      }
+    constexpr uint32_t kGroup = kRansWin * kRansStates;
+    auto value_of = [&](uint32_t i) -> uint32_t {  // chunk-relative value of the part's symbol i
+      return kCiera ? ((uint32_t(gl[i >> log2G]) << log2G) | (i & gmask)) : (wave * kPartValues + i);
     };
     uint32_t xs = word(2u * lane) | (word(2u * lane + 1u) << 16);
     okd = xs >= kRansL;
     uint32_t q = 2u * kRansStates;
     const uint64_t below = (1ull << lane) - 1u;
-    const uint32_t steps = cdiv(mh, kRansStates);
-    uint32_t sv[kRansWin], vv[kRansWin];
-#pragma unroll
-    for (uint32_t k = 0; k < kRansWin; k++) fetch(k, sv[k], vv[k]);
-    for (uint32_t t0 = 0; t0 < steps; t0 += kRansWin) {
-      uint32_t sn[kRansWin], vn[kRansWin];
-#pragma unroll
-      for (uint32_t k = 0; k < kRansWin; k++) fetch(t0 + kRansWin + k, sn[k], vn[k]);
+    auto want = [&]() -> uint32_t { return min((so + 2u * q) / kRansBlock + 2u, jmax); };
+    uint32_t jp = want();
+    uint4 pend = block_load(jp);
+    auto decode = [&](uint32_t t, bool full) -> uint32_t {
+      const bool act = full || t * kRansStates + lane < mh;
+      uint32_t s = 0;
+      if (act) {
+        const uint32_t e = s_dtab[xs & (kRansM - 1u)];
+        s = e & 0xFFu;
+        xs = (((e >> 8) & 0xFFFu) + 1u) * (xs >> 12) + (e >> 20);
+      }
+      const bool need = act && xs < kRansL;
+      const uint64_t mk = __ballot(need);
+      if (need) {
+        const uint32_t kk = q + uint32_t(__popcll(mk & below));
+        if (kk < nw) xs = (xs << 16) | word(kk); else okd = false;
+      }
+      q += uint32_t(__popcll(mk));
+      return s;
+    };
+    // One group of kRansWin steps (512 symbols): the steps' symbols go to the
+    // wave's LDS buffer; then lane l joins symbols 8 l .. 8 l + 7 of the
+    // group (8 contiguous values through the granule list) with their
+    // sign+mantissa bytes and writes them (and, in ciera mode, the receiver
+    // cache) with one wide store.  The sign+mantissa bytes of a group are
+    // loaded while the group before it decodes (two buffers take turns); the
+    // last group, the only one that can be partial, goes on its own.
+    auto group = [&](uint32_t g, uint2 smv, uint32_t vi, uint32_t cnt, bool full) {
+      block_store(jp, pend);
+      __builtin_amdgcn_wave_barrier();
+      jp = want();
+      pend = block_load(jp);
 #pragma unroll
       for (uint32_t k = 0; k < kRansWin; k++) {
-        const uint32_t t = t0 + k;
-        if (t < steps) {
-          const bool act = t * kRansStates + lane < mh;
-          uint32_t sym = 0;
-          if (act) {
-            const uint32_t e = s_dtab[xs & (kRansM - 1u)];
-            sym = e & 0xFFu;
-            xs = (((e >> 8) & 0xFFFu) + 1u) * (xs >> 12) + (e >> 20);
-          }
-          const bool need = act && xs < kRansL;
-          const uint64_t mk = __ballot(need);
-          if (need) {
-            const uint32_t kk = q + uint32_t(__popcll(mk & below));
-            if (kk < nw) xs = (xs << 16) | word(kk); else okd = false;
-          }
-          q += uint32_t(__popcll(mk));
-          if (act) {
-            y[start + vv[k]] = uint16_t(((sv[k] & 0x80u) << 8) | (sym << 7) | (sv[k] & 0x7Fu));
-            if (kCiera) cache[start + vv[k]] = uint8_t(sym);
-          }
-        }
+        const uint32_t t = g * kRansWin + k;
+        if (full || t * kRansStates < mh) sym[k * kRansStates + lane] = uint8_t(decode(t, full));
       }
-#pragma unroll
-      for (uint32_t k = 0; k < kRansWin; k++) {
-        sv[k] = sn[k];
-        vv[k] = vn[k];
+      __builtin_amdgcn_wave_barrier();
+      const uint2 e = *reinterpret_cast<const uint2*>(sym + 8u * lane);
+      __builtin_amdgcn_wave_barrier();
+      store_unit(y, start + vi, cnt, unit_join(smv, e));
+      if (kCiera) store_bytes8(cache + start + vi, cnt, e);
+    };
+    const uint32_t ng = cdiv(mh, kGroup);
+    if (ng >= 2u) {
+      // full groups: every lane has 8 values, so every load is issued
+      auto fetch = [&](uint32_t g, uint2& smv, uint32_t& vi) {
+        vi = value_of(g * kGroup + 8u * lane);
+        smv = *reinterpret_cast<const uint2*>(in + sm_pos + start + vi);
+      };
+      uint2 sa, sb;
+      uint32_t va, vb;
+      uint32_t g = 0;
+      fetch(0u, sa, va);
+      while (true) {
+        fetch(min(g + 1u, ng - 2u), sb, vb);
+        group(g, sa, va, 8u, true);
+        if (++g == ng - 1u) break;
+        fetch(min(g + 1u, ng - 2u), sa, va);
+        group(g, sb, vb, 8u, true);
+        if (++g == ng - 1u) break;
       }
+    }
+    {
+      const uint32_t i0 = (ng - 1u) * kGroup + 8u * lane;
+      const uint32_t cnt = (i0 < mh) ? min(8u, mh - i0) : 0u;
+      const uint32_t vi = value_of(cnt ? i0 : 0u);
+      const uint2 smv = cnt ? load_bytes8(in + sm_pos + start + vi, cnt) : make_uint2(0u, 0u);
+      group(ng - 1u, smv, vi, cnt, false);
     }
     okd = okd && q == nw && xs == kRansL;
   }
