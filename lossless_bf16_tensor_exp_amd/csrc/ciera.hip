@@ -2243,7 +2243,8 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
   __shared__ uint32_t s_lohi, s_ok;
   __shared__ uint64_t s_before;
   __shared__ uint32_t s_found;
-  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = lane_id();
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave addresses stay scalar
   const uint64_t c = blockIdx.x;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint32_t log2G = kCiera ? min(log2B, 14u) : 14u;
@@ -2544,7 +2545,8 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
   __shared__ uint32_t s_m[kParts], s_nw[kParts];
   __shared__ uint32_t s_ok;
   __shared__ uint64_t s_a, s_b;
-  const uint32_t tid = threadIdx.x, lane = lane_id(), wave = tid >> 6;
+  const uint32_t tid = threadIdx.x, lane = lane_id();
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: per-wave addresses stay scalar
   const uint64_t c = blockIdx.x;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint32_t log2G = kCiera ? min(log2B, 14u) : 14u;
