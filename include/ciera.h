@@ -159,30 +159,34 @@ uint64_t ciera_hash_cache_size(uint64_t n, uint32_t B);
  * are entropy coded with range ANS instead of the 3-bit window code, as the
  * CIERA page ANS-codes the changed exponents (section 3.1; the page names
  * no ANS parameters, so this coder and its format are ours):
- *   - per part (16384 values of a chunk) the symbols are the coded exponent
- *     fields in value order; frequencies are the part's histogram
- *     normalised to 4096: with d distinct symbols among m, f = max(1,
- *     floor(h (4096 - d) / m)) for each present symbol, the remainder to
- *     the most frequent one (the lowest on ties);
- *   - 64 interleaved rANS states, symbol i to state i mod 64, 32-bit states
- *     in [2^16, 2^32) starting at 2^16, 16-bit renormalisation words;
- *   - part payload: u8 lo, u8 hi, u16 0, u32 nwords, u16 frequencies of
- *     symbols lo..hi, then nwords 16-bit words: the 64 final states (low,
- *     high half), then the words each step emitted, steps in decode order,
- *     states ascending within a step;
- *   - stream: the 128-byte header (E0 byte 0; bytes 48..55 the number of
- *     coded symbols), a table of 4 nchunks + 1 u64 absolute payload offsets
- *     (the last equals total_bytes) zero-padded to 128, the sign+mantissa
- *     bytes of all n values zero-padded to 128, in ciera mode one 128-byte
- *     bitmap per chunk, then the part payloads, each zero-padded to 128.
+ *   - per chunk, one frequency table: the histogram of all the chunk's
+ *     coded exponent fields normalised to 4096: with d distinct symbols
+ *     among m, f = max(1, floor(h (4096 - d) / m)) for each present
+ *     symbol, the remainder to the most frequent one (the lowest on ties);
+ *   - per part (16384 values of a chunk) the symbols are its coded exponent
+ *     fields in value order, coded with the chunk's table by 64 interleaved
+ *     rANS states, symbol i to state i mod 64, 32-bit states in
+ *     [2^16, 2^32) starting at 2^16, 16-bit renormalisation words;
+ *   - chunk payload: u8 lo, u8 hi, u16 0, u16 w_0 .. w_3 (the 16-bit words
+ *     of each part's stream; 0 for a part without coded symbols), u16
+ *     frequencies of symbols lo..hi, then the part streams in part order: a
+ *     part's 64 final states (low, high half), then the words each step
+ *     emitted, steps in decode order, states ascending within a step;
+ *   - stream (version 2): the 128-byte header (E0 byte 0; bytes 48..55 the
+ *     number of coded symbols), a table of nchunks + 1 u64 absolute payload
+ *     offsets (the last equals total_bytes) zero-padded to 128, the
+ *     sign+mantissa bytes of all n values zero-padded to 128, in ciera mode
+ *     one 128-byte bitmap per chunk, then the chunk payloads, each
+ *     zero-padded to 128.
  * Arguments, caches, ownership and errors as the 3-bit entry points; the
  * workspace is rans_workspace_size(n, B) bytes for encode (it holds a
- * payload scratch slot per part) and *_workspace_size(n) for decode; the
+ * payload scratch slot per chunk) and *_workspace_size(n) for decode; the
  * output capacity rans_max_encoded_size(n, B).  Encode's workgroups wait on
  * earlier ones for their stream offsets (bounded waits, reported as
- * CIERA_ERR_INTERNAL).  Decode checks the header, the part table, every
- * payload's length and padding, that the frequencies sum to 4096, that
- * every word is used and every state ends at 2^16 (else CIERA_ERR_FORMAT). */
+ * CIERA_ERR_INTERNAL).  Decode checks the header, the chunk table, every
+ * payload's word counts, length and padding, that the frequencies sum to
+ * 4096, that every word is used and every state ends at 2^16 (else
+ * CIERA_ERR_FORMAT; the output and the receiver cache are then undefined). */
 uint64_t rans_max_encoded_size(uint64_t n, uint32_t B);
 uint64_t rans_workspace_size(uint64_t n, uint32_t B);
 ciera_status zip3_encode_rans(const void* d_x, uint64_t n, void* d_out, uint64_t out_capacity, void* d_ws,
