@@ -105,3 +105,33 @@ def test_rans_decode_rejects_corruption():
         assert st == 5, f"{name}: status {st}"
     y, _, st = gpu_decode_rans(s, x.size)
     assert st == 0 and np.array_equal(y, x)
+
+
+def test_rans_decode_rejects_moved_part_boundary():
+    """Word counts that keep the payload length but move a boundary between
+    two parts' streams (one part then runs into the next one's words), and a
+    corruption in a later chunk of several, are rejected without writes past
+    the outputs (the canary guards)."""
+    rng = np.random.default_rng(7)
+    x = wl.normal_bf16(rng, 3 * 65536 + 4321, 0.02)
+    s, _ = gpu_encode_rans(x)
+    table = s[128:128 + 8 * 5].view(np.uint64)
+    cases = {}
+    for c in (0, 2):
+        a = int(table[c])
+        nw = [int(v) for v in s[a + 4:a + 12].view(np.uint16)]
+        for h in range(3):
+            if nw[h + 1]:
+                t = s.copy()
+                t[a + 4:a + 12] = np.array(nw[:h] + [nw[h] + 1, nw[h + 1] - 1] + nw[h + 2:], np.uint16).view(np.uint8)
+                cases[f"chunk {c}: boundary between parts {h} and {h + 1}"] = t
+        t = s.copy()
+        t[a + 4:a + 6] = np.array([0xFFFF], np.uint16).view(np.uint8)
+        cases[f"chunk {c}: part 0 word count 65535"] = t
+    for name, t in cases.items():
+        with pytest.raises(oracle.OracleError):
+            oracle.decode_rans(t, x.size)
+        _, _, st = gpu_decode_rans(t, x.size)
+        assert st == 5, f"{name}: status {st}"
+    y, _, st = gpu_decode_rans(s, x.size)
+    assert st == 0 and np.array_equal(y, x)
