@@ -232,6 +232,24 @@ ciera_status ciera_read_error(const void* d_ws, hipStream_t stream);
 ciera_status zip3_encode_e0(const void* d_x, uint64_t n, const uint8_t* d_e0, void* d_out, uint64_t out_capacity,
                             void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream);
 
+/* ciera_encode_e0: ciera_encode with the window base read from device memory
+ * (d_e0, as in zip3_encode_e0), so that x and the sender cache are read
+ * once: each part compares its exponents with the cache, rewrites the
+ * bytes that differ and codes its changed blocks in the same pass.  The
+ * CIERA page keeps the exponents of unchanged blocks out of the message
+ * (section 3.1); the window rule of the ZipCCL digest (section 3.1) sets
+ * E0 from the tensor's sigma, here the caller's choice (e.g. byte 7 of the
+ * previous iteration's stream header).  Arguments, caches, sizes and the
+ * workspace as ciera_encode (workspace ciera_workspace_size(n, B)), except
+ * that n is limited to 2^39 (CIERA_ERR_ARG above); the stream and the cache
+ * equal ciera_encode_ex's with e0_override = *d_e0.  A *d_e0 above 249 makes
+ * the call write nothing, leave the cache as it was and ciera_read_error
+ * report CIERA_ERR_ARG.  Workgroups wait on each other through the
+ * workspace as in zip3_encode_e0. */
+ciera_status ciera_encode_e0(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, const uint8_t* d_e0,
+                             void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                             hipStream_t stream);
+
 /* Kernel timing, a profiling aid (not part of the codec).  events holds
  * n_pairs (start, stop) pairs of hipEvent_t handles, created with timing
  * enabled and owned by the caller.  The next n_pairs kernel launches made by

@@ -16,6 +16,7 @@ Same names as the C ABI::
     zip3_decode(inp, in_size, y, ws, stream=None)
     zip3_encode_e0(x, e0_src, out, ws, out_size, e0_offset=0, stream=None)
     ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None, plan_groups=0)
+    ciera_encode_e0(x, B, prev_exp, e0_src, out, ws, out_size, e0_offset=0, stream=None)
     ciera_encode_hashed(x, B, hash_cache, out, ws, out_size, stream=None)
     ciera_hash_cache_size(n, B)
     zip3_encode_rans / zip3_decode_rans / ciera_encode_rans / ciera_decode_rans   (rANS-coded exponents)
@@ -37,7 +38,7 @@ __all__ = [
     "CieraError", "library_path", "load_library",
     "zip3_max_encoded_size", "ciera_max_encoded_size", "zip3_workspace_size", "ciera_workspace_size",
     "zip3_encode", "zip3_decode", "ciera_encode", "ciera_decode", "ciera_read_error", "ciera_status_string",
-    "zip3_encode_e0", "ciera_encode_hashed", "ciera_hash_cache_size",
+    "zip3_encode_e0", "ciera_encode_e0", "ciera_encode_hashed", "ciera_hash_cache_size",
     "rans_max_encoded_size", "rans_workspace_size", "zip3_encode_rans", "zip3_decode_rans", "ciera_encode_rans",
     "ciera_decode_rans",
     "bind", "ciera_time_kernels",
@@ -83,6 +84,7 @@ def load_library():
         "zip3_encode": [vp, u64, vp, u64, vp, u64, vp, vp],
         "zip3_encode_ex": [vp, u64, vp, u64, vp, u64, vp, i32, u32, vp],
         "zip3_encode_e0": [vp, u64, vp, vp, u64, vp, u64, vp, vp],
+        "ciera_encode_e0": [vp, u64, u32, vp, vp, vp, u64, vp, u64, vp, vp],
         "zip3_decode": [vp, u64, vp, u64, vp, u64, vp],
         "ciera_encode": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
         "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, u32, vp],
@@ -212,6 +214,22 @@ def ciera_encode(x, B: int, prev_exp, out, ws, out_size, e0_override: int = -1, 
                              ws.numel(), ctypes.c_void_p(out_size.data_ptr()), e0_override, plan_groups,
                              _stream(stream))
     _raise(st, "ciera_encode")
+
+
+def ciera_encode_e0(x, B: int, prev_exp, e0_src, out, ws, out_size, e0_offset: int = 0, stream=None) -> None:
+    """ciera encode reading x and the sender cache once, with the window base
+    taken from byte ``e0_offset`` of the uint8 device tensor ``e0_src``."""
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(prev_exp, "prev_exp", x.numel())
+    _check_bytes(e0_src, "e0_src", e0_offset + 1)
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.ciera_encode_e0(_ptr(x), x.numel(), B, _ptr(prev_exp), ctypes.c_void_p(e0_src.data_ptr() + e0_offset),
+                             _ptr(out), out.numel(), _ptr(ws), ws.numel(), ctypes.c_void_p(out_size.data_ptr()),
+                             _stream(stream))
+    _raise(st, "ciera_encode_e0")
 
 
 def ciera_hash_cache_size(n: int, B: int) -> int:

@@ -105,7 +105,8 @@ struct Ctrl {
   uint32_t plan_fail;  // set by a k_plan workgroup whose wait did not end
   uint64_t n_err_slots;
   uint64_t done_esc;  // single-read encode: chunks finished << 40 | their escapes
-  uint64_t reserved[29];
+  uint64_t done_nch;  // single-read ciera encode: the finished chunks' changed blocks
+  uint64_t reserved[28];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -1472,7 +1473,6 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
 // earlier chunks: the lowest unfinished chunk always has all of its parts
 // dispatched, so every wait ends; each is bounded as well and ends in
 // CIERA_ERR_INTERNAL.
-constexpr uint32_t kPartReady = 1u << 31;
 constexpr uint64_t kFlagSize = 1ull << 62;  // look-back only: a predecessor's size, not a prefix
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kValMask = (1ull << 62) - 1u;
@@ -1480,6 +1480,67 @@ constexpr uint32_t kBadE0 = ~0u;
 constexpr uint32_t kDoneShift = 40u;           // ctrl->done_esc: chunks << 40 | escapes
 constexpr uint64_t kMaxSingleReadN = 1ull << 39;  // keeps both fields of done_esc in range
 
+// A part's published word: bit 31 ready, bits 15..30 a 16-bit field, bits
+// 0..14 the part's escapes (at most 16,384).  The field is 0 in zip3 mode;
+// in ciera mode, with B <= 512 the part's changed blocks (at most 256), with
+// 1024 <= B <= 16384 the part's block bits (at most 16), with B > 16384 bit
+// 0 = some value of the part changed (its share of the block).
+constexpr uint32_t kPartReady = 1u << 31;
+constexpr uint32_t kEscBits = 15u;
+__device__ inline uint32_t word_esc(uint32_t w) { return w & ((1u << kEscBits) - 1u); }
+__device__ inline uint32_t word_field(uint32_t w) { return (w >> kEscBits) & 0xFFFFu; }
+
+// A chunk's layout from its parts' words: its changed blocks and escapes,
+// per part the escapes and plane bytes before it in the chunk, and whether
+// it codes its values (a part inside a block that spans several parts codes
+// them only if some part of the block changed).
+struct ChunkCounts {
+  uint32_t nch, esc, coded;  // coded: bit h for part h
+  uint32_t esc_before[kParts], slot_before[kParts];
+};
+__device__ inline ChunkCounts chunk_counts(const uint32_t (&w)[kParts], bool ciera, uint32_t log2B) {
+  ChunkCounts k;
+  k.nch = k.esc = k.coded = 0u;
+  const uint32_t B = 1u << log2B;
+  if (!ciera || B <= kPartValues) {
+    uint32_t slots = 0;
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      k.esc_before[h] = k.esc;
+      k.slot_before[h] = slots;
+      k.esc += word_esc(w[h]);
+      const uint32_t f = word_field(w[h]);
+      const uint32_t nb = !ciera ? 0u : (B <= 512u ? f : uint32_t(__popc(f)));
+      k.nch += nb;
+      slots += nb * (B / 8u);
+      k.coded |= 1u << h;
+    }
+  } else {
+    const uint32_t ppb = B / kPartValues;  // parts per block: 2 or 4
+    uint32_t rank = 0;
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      const uint32_t first = h / ppb * ppb;
+      uint32_t any = 0;
+      for (uint32_t q = first; q < first + ppb; q++) any |= word_field(w[q]) & 1u;
+      if (h == first && any) rank++;  // this block's rank + 1 among the changed blocks
+      k.slot_before[h] = any ? (rank - 1u) * (B / 8u) + (h - first) * (kPartValues / 8u) : 0u;
+      k.esc_before[h] = k.esc;
+      if (any) {
+        k.coded |= 1u << h;
+        k.esc += word_esc(w[h]);
+      }
+    }
+    k.nch = rank;
+  }
+  return k;
+}
+
+// Stream bytes of a chunk of nc values.
+__device__ inline uint64_t chunk_bytes(uint32_t nc, bool ciera, uint32_t log2B, uint32_t nch, uint32_t esc) {
+  const uint64_t planes = ciera ? (uint64_t(nch) << log2B) / 8u : cdiv(nc, 8u);
+  return pad128(nc) + (ciera ? 128u : 0u) + 3u * pad128(planes) + pad128(esc);
+}
 
 __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks, uint32_t B,
                                                     const uint8_t* __restrict__ d_e0, uint8_t* __restrict__ out,
@@ -1491,7 +1552,10 @@ __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks
   for (uint64_t i = tid; i < nchunks * kParts; i += kThreads)
     ws.pcount[(i / kParts) * kPcountStride + i % kParts] = 0u;
   for (uint64_t i = tid; i < nchunks; i += kThreads) ws.cstat[i * kCstatStride] = 0u;
-  if (tid == 0) ws.ctrl->done_esc = 0u;
+  if (tid == 0) {
+    ws.ctrl->done_esc = 0u;
+    ws.ctrl->done_nch = 0u;
+  }
   // the padding words after the chunk table and the escape index
   for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
   if (tid == 0) {
@@ -1519,11 +1583,10 @@ __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks
 // Stream bytes of the chunks before c (wave 0, 64 predecessors at a time).
 // A predecessor contributes its inclusive prefix if its last part has
 // published one (and the search ends there), else its size, known as soon as
-// its four parts have published their escape counts: every chunk before the
-// last holds 65,536 values, so its fixed sections take kFullFixed bytes.
-// Returns false if a wait did not end.
-constexpr uint64_t kFullFixed = uint64_t(kChunk) + 3u * (kChunk / 8u);
-__device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint64_t& pb) {
+// its four parts have published their words (every chunk before the last
+// holds 65,536 values).  Returns false if a wait did not end.
+template <bool kCiera>
+__device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint32_t log2B, uint64_t& pb) {
   const uint32_t lane = lane_id();
   pb = 0;
   int64_t top = int64_t(c) - 1;
@@ -1532,14 +1595,14 @@ __device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint64_t& pb) {
     const int64_t k = top - int64_t(lane);
     uint64_t st = (k >= 0) ? load_relaxed(&ws.cstat[uint64_t(k) * kCstatStride]) : kFlagIncl;
     if (k >= 0 && (st & ~kValMask) != kFlagIncl) {
-      uint32_t esc = 0, ready = 1u;
+      uint32_t w[kParts], ready = 1u;
 #pragma unroll
       for (uint32_t q = 0; q < kParts; q++) {
-        const uint32_t w = load_relaxed(&ws.pcount[uint64_t(k) * kPcountStride + q]);
-        ready &= w >> 31;
-        esc += w & ~kPartReady;
+        w[q] = load_relaxed(&ws.pcount[uint64_t(k) * kPcountStride + q]);
+        ready &= w[q] >> 31;
       }
-      st = ready ? (kFlagSize | (kFullFixed + pad128(esc))) : 0u;
+      const ChunkCounts cc = chunk_counts(w, kCiera, log2B);
+      st = ready ? (kFlagSize | chunk_bytes(kChunk, kCiera, log2B, cc.nch, cc.esc)) : 0u;
     }
     const uint64_t flag = st & ~kValMask;
     if (__ballot(flag == 0u) != 0u) {
@@ -1569,17 +1632,23 @@ __device__ inline uint32_t single_part_of(uint32_t b, uint32_t nchunks) {
   return ((slot / kParts) * kXcds + x) * kParts + slot % kParts;
 }
 
-// One part of a chunk, zip3 mode.
+// One part of a chunk.  ciera mode: the part also compares its exponents with
+// the sender cache, rewrites the units that differ, and codes only the
+// values of its changed blocks (a block that spans several parts: once the
+// chunk's words show some part of it changed).
+template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restrict__ x, uint64_t n, uint64_t nchunks,
+                                                         uint32_t log2B, uint8_t* __restrict__ cache,
                                                          uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
                                                          Ws ws) {
   __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_esc[kPartEscStage];
   __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
+  __shared__ uint32_t s_pbits[kPartBitmapWords];  // ciera: the part's block bits (B > 16384: bit 0, its share)
   __shared__ uint64_t s_begin;
-  __shared__ uint32_t s_before, s_err;
+  __shared__ uint32_t s_before, s_slot0, s_nch, s_coded, s_err;
   const uint32_t tid = threadIdx.x;
-  const uint32_t lane = lane_id();
+  const uint32_t lane = lane_id(), wave = tid >> 6;
   // Workgroups are dealt round-robin over the chip's 8 XCDs; the four parts of
   // a chunk go to one XCD, one after the other, so that they are dispatched
   // together and wait on each other only briefly.
@@ -1591,45 +1660,114 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
   const uint32_t pu0 = h * kPartUnits;
+  const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint32_t e0 = ws.ctrl->e0;
   if (e0 == kBadE0) {  // the same for every workgroup: none waits on another
     if (tid == 0) ws.err[wg] = uint32_t(CIERA_ERR_ARG);
     return;
   }
 
-  // Load the part first: all of a thread's 16-byte loads go out before any is used.
+  // Load the part (and its cache bytes) first: all loads go out before any is used.
   Unit v[kUPT];
-  if (8u * (pu0 + kPartUnits) <= nc) {
+  uint2 old[kUPT];
+  const bool full = 8u * (pu0 + kPartUnits) <= nc;
+  if (full) {
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) v[j] = load_unit(x, start + 8ull * (pu0 + j * kPartThreads + tid), 8u);
+    if (kCiera) {
+#pragma unroll
+      for (uint32_t j = 0; j < kUPT; j++)
+        old[j] = *reinterpret_cast<const uint2*>(cache + start + 8ull * (pu0 + j * kPartThreads + tid));
+    }
   } else {
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) {
       const uint32_t u = pu0 + j * kPartThreads + tid;
       v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
-      if (u < nunits) v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+      old[j] = make_uint2(0u, 0u);
+      if (u < nunits) {
+        v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+        if (kCiera) old[j] = load_bytes8(cache + start + 8ull * u, min(8u, nc - 8u * u));
+      }
     }
   }
   const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
   for (uint32_t i = tid; i < 3u * kStage / 16u; i += kPartThreads)
     reinterpret_cast<uint4*>(s_planes)[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (kCiera && tid < kPartBitmapWords) s_pbits[tid] = 0u;
   __syncthreads();  // staging cleared
 
-  // Code every unit: plane bytes into LDS (slot = unit), escape masks.
+  // ciera: exponents against the cache; the units that differ are rewritten,
+  // and a wave ballot gives the changed blocks among the wave's 64 units
+  // (lanes [kL, kL + L) hold block k for L = B / 8 up to 64; from B = 512 on
+  // the 64 units lie in one block), set in s_pbits by one atomic per wave.
+  // Blocks count from the part's start; with B > 16384 the part is one share.
+  if (kCiera) {
+    const uint32_t L = (B >= 512u) ? 64u : B / 8u;
+    const uint64_t gmask = (L >= 64u) ? ~0ull : ((1ull << L) - 1u);
+    const uint32_t lb = min(log2B, 14u);  // the part's blocks are min(B, 16384) values long
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
+      bool diff = false;
+      if (u < nunits) {
+        const uint32_t cnt = min(8u, nc - 8u * u);
+        const uint2 e = unit_exponents(v[j]);
+        const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
+        const uint64_t d = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
+        if (d) {
+          store_bytes8(cache + start + 8ull * u, cnt, e);
+          diff = true;
+        }
+      }
+      const uint64_t m = __ballot(diff);
+      if (m != 0u) {
+        const uint32_t lbw = (8u * (j * kPartThreads + 64u * wave)) >> lb;  // the wave's first block in the part
+        uint32_t bits = 0;
+        for (uint32_t k = 0; k < 64u / L; k++) bits |= ((m >> (k * L)) & gmask) ? (1u << k) : 0u;
+        if (lane == 0u) atomicOr(&s_pbits[lbw >> 5], bits << (lbw & 31u));
+      }
+    }
+    __syncthreads();  // s_pbits complete
+  }
+  // the part's changed blocks, and those before each bitmap word
+  uint32_t pnch = 0, prank[kPartBitmapWords];
+  if (kCiera) {
+#pragma unroll
+    for (uint32_t k = 0; k < kPartBitmapWords; k++) {
+      prank[k] = pnch;
+      pnch += __popc(s_pbits[k]);
+    }
+  }
+
+  // Code every unit that is coded: plane bytes into LDS at the unit's plane
+  // byte within the part's slots (zip3: the unit's own byte), escape masks.
   uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
     const uint32_t u = pu0 + j * kPartThreads + tid;
+    const uint32_t ul = u - pu0;
     cnt[j] = 0u;
     emask[j] = 0u;
-    if (u < nunits) {
+    bool coded = true;
+    uint32_t at = ul;
+    if (kCiera && B <= kPartValues) {
+      const uint32_t upb_log = log2B - 3u;  // units per block
+      const uint32_t blk = ul >> upb_log;
+      const uint32_t word = s_pbits[blk >> 5];
+      uint32_t before = 0;  // changed blocks in the words before blk's (constant indices: no private array)
+#pragma unroll
+      for (uint32_t k = 0; k < kPartBitmapWords; k++) before = (k == (blk >> 5)) ? prank[k] : before;
+      coded = (word >> (blk & 31u)) & 1u;
+      at = ((before + __popc(word & ((1u << (blk & 31u)) - 1u))) << upb_log) + (ul & ((1u << upb_log) - 1u));
+    }
+    if (u < nunits && coded) {
       const uint32_t valid = min(8u, nc - 8u * u);
       const uint32_t vmask = (valid == 8u) ? 0xFFu : ((1u << valid) - 1u);
       uint32_t cp[4];
 #pragma unroll
       for (int i = 0; i < 4; i++) cp[i] = code_pair(exp_pair(v[j].w[i]), bias);
       const uint32_t p = unit_planes(cp) & (vmask * 0x010101u);
-      const uint32_t at = u - pu0;
       s_planes[at] = uint8_t(p);
       s_planes[kStage + at] = uint8_t(p >> 8);
       s_planes[2u * kStage + at] = uint8_t(p >> 16);
@@ -1638,59 +1776,74 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     }
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
-  if (tid == 0) store_relaxed(&ws.pcount[c * kPcountStride + h], kPartReady | pesc);
+  uint32_t field = 0u;
+  if (kCiera) field = (B <= 512u) ? pnch : (B <= kPartValues ? s_pbits[0] : (s_pbits[0] & 1u));
+  if (tid == 0) store_relaxed(&ws.pcount[c * kPcountStride + h], kPartReady | (field << kEscBits) | pesc);
 
   // Stream position (wave 0).
   if (tid < 64u) {
     uint32_t err = 0u;
-    // escape counts of the chunk's four parts: lane l < 4 reads part l
-    uint32_t cnt_l = 0u;
+    // the words of the chunk's four parts: lane l < 4 reads part l's
+    uint32_t w_l = 0u;
     for (uint32_t spins = 0;; spins++) {
-      const uint32_t w = (lane < kParts) ? load_relaxed(&ws.pcount[c * kPcountStride + lane]) : kPartReady;
-      if (__ballot(!(w & kPartReady)) == 0u) {
-        cnt_l = w & ~kPartReady;
-        break;
-      }
+      w_l = (lane < kParts) ? load_relaxed(&ws.pcount[c * kPcountStride + lane]) : kPartReady;
+      if (__ballot(!(w_l & kPartReady)) == 0u) break;
       if (spins > kSpinLimit) {
         err = CIERA_ERR_INTERNAL;
         break;
       }
       __builtin_amdgcn_s_sleep(2);
     }
-    const uint32_t incl = wave_incl_scan(cnt_l);  // lane l: escapes of parts 0..l
-    const uint32_t before = (h == 0u) ? 0u : uint32_t(__builtin_amdgcn_readlane(int(incl), int(h) - 1));
-    const uint32_t e1 = uint32_t(__builtin_amdgcn_readlane(int(incl), 0));
-    const uint32_t e2 = uint32_t(__builtin_amdgcn_readlane(int(incl), 1));
-    const uint32_t e3 = uint32_t(__builtin_amdgcn_readlane(int(incl), 2));
-    const uint32_t esc_chunk = uint32_t(__builtin_amdgcn_readlane(int(incl), 3));
-    const uint64_t size = pad128(nc) + 3u * pad128(cdiv(nc, 8u)) + pad128(esc_chunk);
+    uint32_t w[kParts];
+#pragma unroll
+    for (uint32_t q = 0; q < kParts; q++) w[q] = uint32_t(__builtin_amdgcn_readlane(int(w_l), int(q)));
+    const ChunkCounts cc = chunk_counts(w, kCiera, log2B);
+    const uint64_t size = chunk_bytes(nc, kCiera, log2B, cc.nch, cc.esc);
     const uint64_t tbl = table_end(nchunks);
     uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
     uint64_t pb = 0;
     // every part looks back for the chunk's offset; the last part publishes it
-    if (!err && !chunk_lookback(ws, c, pb)) err = CIERA_ERR_INTERNAL;
+    if (!err && !chunk_lookback<kCiera>(ws, c, log2B, pb)) err = CIERA_ERR_INTERNAL;
     if (last_part) {
       if (lane == 0u) {
         // published even after a failed wait, so that no later wait lasts forever
         store_relaxed(&ws.cstat[c * kCstatStride], kFlagIncl | (pb + size));
         table[c] = tbl + pb;
-        table[nchunks + 1u + c] = (uint64_t(e1) << 16) | (uint64_t(e2) << 32) | (uint64_t(e3) << 48);
+        table[nchunks + 1u + c] = (uint64_t(cc.esc_before[1]) << 16) | (uint64_t(cc.esc_before[2]) << 32) |
+                                  (uint64_t(cc.esc_before[3]) << 48);
         if (c + 1u == nchunks) {
           uint64_t* hd = reinterpret_cast<uint64_t*>(out);
           table[nchunks] = tbl + pb + size;
           hd[4] = tbl + pb + size;
           *out_size = tbl + pb + size;
         }
-        // the chunk that finishes last writes the escape total
-        const uint64_t old = atomicAdd(reinterpret_cast<unsigned long long*>(&ws.ctrl->done_esc),
-                                       (1ull << kDoneShift) | esc_chunk);
-        if ((old >> kDoneShift) + 1u == nchunks)
-          reinterpret_cast<uint64_t*>(out)[6] = (old & ((1ull << kDoneShift) - 1u)) + esc_chunk;
+        // The chunk that finishes last writes the totals.  Each chunk adds its
+        // changed blocks before it counts itself done: the second atomic
+        // takes an operand from the first's result, so it is issued only
+        // once the first is performed.
+        uint64_t dep = 0u;
+        if (kCiera) dep = atomicAdd(reinterpret_cast<unsigned long long*>(&ws.ctrl->done_nch), cc.nch) >> 63;
+        const uint64_t old_d = atomicAdd(reinterpret_cast<unsigned long long*>(&ws.ctrl->done_esc),
+                                         ((1ull << kDoneShift) | cc.esc) + dep);
+        if ((old_d >> kDoneShift) + 1u == nchunks) {
+          uint64_t* hd = reinterpret_cast<uint64_t*>(out);
+          hd[6] = (old_d & ((1ull << kDoneShift) - 1u)) + cc.esc;
+          if (kCiera) hd[5] = load_relaxed(&ws.ctrl->done_nch);
+        }
       }
     }
     if (lane == 0u) {
+      uint32_t eb = 0, sb = 0;  // part h's entries (constant indices: no private array)
+#pragma unroll
+      for (uint32_t q = 0; q < kParts; q++) {
+        eb = (q == h) ? cc.esc_before[q] : eb;
+        sb = (q == h) ? cc.slot_before[q] : sb;
+      }
       s_begin = tbl + pb;
-      s_before = before;
+      s_before = eb;
+      s_slot0 = sb;
+      s_nch = cc.nch;
+      s_coded = (cc.coded >> h) & 1u;
       s_err = err;
     }
   }
@@ -1701,7 +1854,9 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   }
   const uint64_t begin = s_begin;
   const uint32_t esc_before = s_before;
-  const ChunkGeom g = chunk_geom(begin, nc, false, 0u, 0u);
+  const uint32_t nch = s_nch;
+  const bool coded_part = s_coded != 0u;
+  const ChunkGeom g = chunk_geom(begin, nc, kCiera, nch, B);
   const uint32_t pb = uint32_t(g.plane_bytes);
   // sign+mantissa bytes
 #pragma unroll
@@ -1709,19 +1864,21 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     const uint32_t u = pu0 + j * kPartThreads + tid;
     if (u < nunits) *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
   }
-  // planes: the part owns bytes [pu0, pu0 + kPartUnits) of each plane, clipped
-  // to the padded plane length
-  const uint32_t own_hi = min(pu0 + kPartUnits, pb);
-  const uint32_t own = own_hi > pu0 ? own_hi - pu0 : 0u;
+  // planes: the part's plane bytes [slot0, slot0 + own) of each plane, clipped
+  // to the padded plane length (zip3: bytes [pu0, pu0 + kPartUnits))
+  const uint32_t slot0 = kCiera ? s_slot0 : pu0;
+  const uint32_t span = !kCiera ? kPartUnits : (!coded_part ? 0u : (B <= kPartValues ? pnch * (B / 8u) : kPartUnits));
+  const uint32_t own_hi = min(slot0 + span, pb);
+  const uint32_t own = own_hi > slot0 ? own_hi - slot0 : 0u;
   for (uint32_t i = tid; i < 3u * (own / 8u); i += kPartThreads) {
     const uint32_t b = i / (own / 8u);
     const uint32_t off = 8u * (i - b * (own / 8u));
     const uint2 val = *reinterpret_cast<const uint2*>(s_planes + b * kStage + off);
-    *reinterpret_cast<uint2*>(out + g.plane + b * pb + pu0 + off) = val;
+    *reinterpret_cast<uint2*>(out + g.plane + b * pb + slot0 + off) = val;
   }
   // escapes of this part: [esc_before, esc_before + pesc) of the chunk's section
   const uint64_t esc_at = g.esc + esc_before;
-  if (pesc <= kPartEscStage) {
+  if (coded_part && pesc <= kPartEscStage) {
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) {
       uint32_t em = emask[j];
@@ -1737,7 +1894,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     }
     __syncthreads();
     for (uint32_t i = tid; i < pesc; i += kPartThreads) out[esc_at + i] = s_esc[i];
-  } else {
+  } else if (coded_part) {
 #pragma unroll
     for (uint32_t j = 0; j < kUPT; j++) {
       uint32_t em = emask[j];
@@ -1752,10 +1909,40 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
       }
     }
   }
+  if (kCiera) {
+    // the chunk's bitmap: with B <= 512 each part writes its own words; else
+    // the last part assembles the (at most two) words, the others zero
+    const uint32_t bpp = kPartValues >> min(log2B, 14u);  // blocks per part (1 with B > 16384)
+    if (B <= 512u) {
+      if (tid < bpp / 32u)
+        *reinterpret_cast<uint32_t*>(out + g.bitmap + 4u * (h * (bpp / 32u) + tid)) = s_pbits[tid];
+    } else if (last_part && tid < 64u) {
+      uint32_t wl = 0u;
+      if (lane < kParts) wl = load_relaxed(&ws.pcount[c * kPcountStride + lane]);
+      uint64_t bits = 0;
+      if (B <= kPartValues) {
+#pragma unroll
+        for (uint32_t q = 0; q < kParts; q++)
+          bits |= uint64_t(word_field(uint32_t(__builtin_amdgcn_readlane(int(wl), int(q))))) << (q * bpp);
+      } else {
+        const uint32_t ppb = B / kPartValues;
+#pragma unroll
+        for (uint32_t q = 0; q < kParts; q++)
+          bits |= uint64_t(word_field(uint32_t(__builtin_amdgcn_readlane(int(wl), int(q)))) & 1u) << (q / ppb);
+      }
+      if (tid < 2u) *reinterpret_cast<uint32_t*>(out + g.bitmap + 4u * tid) = uint32_t(bits >> (32u * tid));
+    }
+  }
   if (last_part) {
-    // zero padding after the sm section's data and after the chunk's escapes
-    const uint32_t esc_chunk = esc_before + pesc;
-    zero_fill(out, g.sm + 8ull * nunits, g.plane, kPartThreads);
+    // zero padding after each section's data (and the bitmap's unused words)
+    const uint32_t esc_chunk = esc_before + (coded_part ? pesc : 0u);
+    zero_fill(out, g.sm + 8ull * nunits, g.bitmap, kPartThreads);
+    if (kCiera) {
+      const uint32_t used = (B <= 512u) ? (kChunk >> log2B) / 8u : 8u;  // bitmap bytes written above
+      zero_fill(out, g.bitmap + used, g.plane, kPartThreads);
+      const uint32_t slots = uint32_t((uint64_t(nch) << log2B) / 8u);
+      for (uint32_t b = 0; b < 3u; b++) zero_fill(out, g.plane + b * pb + slots, g.plane + (b + 1u) * pb, kPartThreads);
+    }
     if (esc_chunk <= kChunk) zero_fill(out, g.esc + esc_chunk, g.esc + pad128(esc_chunk), kPartThreads);
   }
   if (tid == 0) ws.err[wg] = 0u;
@@ -2910,23 +3097,32 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   return launch_status();
 }
 
-ciera_status encode_known_e0_impl(const void* d_x, uint64_t n, const uint8_t* d_e0, void* d_out,
-                                  uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
-                                  hipStream_t stream) {
+ciera_status encode_known_e0_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cache, const uint8_t* d_e0,
+                                  void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes,
+                                  uint64_t* d_out_size, hipStream_t stream) {
+  const bool ciera = B != 0u;
   if (n > kMaxSingleReadN) return CIERA_ERR_ARG;
+  if (ciera && !valid_block(B)) return CIERA_ERR_ARG;
   if (!d_e0 || !d_out || !d_ws || !d_out_size || !aligned16(d_out) || !aligned16(d_ws)) return CIERA_ERR_ARG;
   if ((reinterpret_cast<uintptr_t>(d_out_size) & 7u) != 0u) return CIERA_ERR_ARG;
   if (n > 0 && (!d_x || !aligned16(d_x))) return CIERA_ERR_ARG;
-  if (out_capacity < max_size(n, 0u)) return CIERA_ERR_CAPACITY;
+  if (ciera && n > 0 && (!d_cache || !aligned16(d_cache))) return CIERA_ERR_ARG;
+  if (out_capacity < max_size(n, B)) return CIERA_ERR_CAPACITY;
   const uint64_t nchunks = cdiv(n, kChunk);
   if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
   const Ws ws = ws_bind(d_ws, nchunks);
   const uint16_t* x = static_cast<const uint16_t*>(d_x);
   uint8_t* out = static_cast<uint8_t*>(d_out);
   (void)hipGetLastError();
-  launch(k_prep1, dim3(1), dim3(kThreads), stream, n, nchunks, 0u, d_e0, out, d_out_size, ws);
-  if (nchunks) launch(k_write1, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nchunks, out,
-                      d_out_size, ws);
+  launch(k_prep1, dim3(1), dim3(kThreads), stream, n, nchunks, B, d_e0, out, d_out_size, ws);
+  if (nchunks) {
+    if (ciera)
+      launch(k_write1<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nchunks, log2u(B),
+             d_cache, out, d_out_size, ws);
+    else
+      launch(k_write1<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nchunks, 0u,
+             nullptr, out, d_out_size, ws);
+  }
   return launch_status();
 }
 
@@ -3136,7 +3332,14 @@ ciera_status ciera_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_
 
 ciera_status zip3_encode_e0(const void* d_x, uint64_t n, const uint8_t* d_e0, void* d_out, uint64_t out_capacity,
                            void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream) {
-  return encode_known_e0_impl(d_x, n, d_e0, d_out, out_capacity, d_ws, ws_bytes, d_out_size, stream);
+  return encode_known_e0_impl(d_x, n, 0u, nullptr, d_e0, d_out, out_capacity, d_ws, ws_bytes, d_out_size, stream);
+}
+
+ciera_status ciera_encode_e0(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, const uint8_t* d_e0,
+                             void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                             hipStream_t stream) {
+  if (B == 0u) return CIERA_ERR_ARG;
+  return encode_known_e0_impl(d_x, n, B, d_prev_exp, d_e0, d_out, out_capacity, d_ws, ws_bytes, d_out_size, stream);
 }
 
 ciera_status ciera_read_error(const void* d_ws, hipStream_t stream) {

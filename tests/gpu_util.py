@@ -178,6 +178,51 @@ def check_encode_e0(x, e0):
     return g
 
 
+def gpu_encode_e0_ciera(x, B, cache, e0_src, e0_offset=0):
+    """Single-read ciera encode: the window base from byte ``e0_offset`` of
+    the uint8 device tensor ``e0_src``, the sender cache ``cache`` (n bytes,
+    updated on the GPU).  Returns (stream bytes or None, device status,
+    cache after)."""
+    n = x.size
+    xd = torch.from_numpy(x.view(np.int16)).cuda()
+    cap = ciera.ciera_max_encoded_size(n, B)
+    buf, out = _guarded_bytes(cap)
+    ws = torch.empty(ciera.ciera_workspace_size(n, B), dtype=torch.uint8, device="cuda")
+    size = torch.full((1,), -1, dtype=torch.int64, device="cuda")
+    cbuf, cd = _guarded_bytes(n)
+    cd.copy_(torch.from_numpy(cache))
+    ciera.ciera_encode_e0(xd, B, cd, e0_src, out, ws, size, e0_offset)
+    torch.cuda.synchronize()
+    status = ciera.ciera_read_error(ws)
+    host = buf.cpu().numpy()
+    _check_guards(host, cap, "stream")
+    ch = cbuf.cpu().numpy()
+    _check_guards(ch, n, "sender cache")
+    new_cache = ch[GUARD:GUARD + n].copy()
+    if status:
+        return None, status, new_cache
+    sz = int(size.item())
+    assert 0 < sz <= cap
+    assert (host[GUARD + sz:GUARD + cap] == CANARY).all(), "write past the stream's end"
+    return host[GUARD:GUARD + sz].copy(), 0, new_cache
+
+
+def check_encode_e0_ciera(x, B, cache, e0):
+    """Single-read ciera encode at window base e0 == oracle ciera encode at
+    e0, stream and sender cache, byte for byte."""
+    src = torch.tensor([e0], dtype=torch.uint8, device="cuda")
+    g, st, gc = gpu_encode_e0_ciera(x, B, cache.copy(), src)
+    assert st == 0, f"single-read ciera encode reported status {st}"
+    oc = cache.copy()
+    o, _ = oracle.encode(x, B, oc, e0)
+    if g.tobytes() != o.tobytes():
+        i = _first_diff(g, o)
+        raise AssertionError(f"single-read ciera stream differs from the oracle at byte {i} of {o.size} "
+                             f"(gpu size {g.size}): gpu {g[i:i + 16]} oracle {o[i:i + 16]}")
+    assert np.array_equal(gc, oc), "sender cache differs from the oracle's"
+    return g
+
+
 def exps_as_bf16(e):
     """BF16 patterns whose exponent fields are the bytes e (sign and mantissa
     zero): a tensor whose block hashes stand for the exponent cache e."""

@@ -79,3 +79,64 @@ def test_single_read_workload2():
     say(f"single-read workload2 n={g.size}")
     s = check_encode_e0(g, 112)
     check_roundtrip(s, g)
+
+
+# ---------------------------------------------------------------- ciera mode
+from gpu_util import check_encode_e0_ciera, exps, gpu_encode_e0_ciera  # noqa: E402
+
+CIERA_B = [64, 256, 512, 1024, 4096, 16384, 32768, 65536]
+
+
+@pytest.mark.parametrize("B", CIERA_B)
+@pytest.mark.parametrize("n", SMALL_N)
+def test_single_read_ciera_small(n, B):
+    say(f"single-read ciera n={n} B={B}")
+    rng = np.random.default_rng(5000 + n + B)
+    x = wl.mixed_small(rng, n)
+    cache = wl.perturbed_cache(rng, x, 0.01)
+    for e0 in (oracle.choose_e0(x), 120):
+        s = check_encode_e0_ciera(x, B, cache, e0)
+    recv = cache.copy()
+    check_roundtrip(s, x, B, recv)
+
+
+@pytest.mark.parametrize("B", [64, 1024, 32768])
+def test_single_read_ciera_unchanged_and_all_changed(B):
+    rng = np.random.default_rng(B + 1)
+    n = 2 * 65536 + 5000
+    x = wl.f32_to_bf16(rng.standard_normal(n, dtype=np.float32) * np.float32(0.02))
+    e0 = oracle.choose_e0(x)
+    s = check_encode_e0_ciera(x, B, exps(x), e0)          # nothing changed: no planes, no escapes
+    check_roundtrip(s, x, B, exps(x))
+    s = check_encode_e0_ciera(x, B, np.zeros(n, np.uint8), e0)  # every block changed
+    check_roundtrip(s, x, B, np.zeros(n, np.uint8))
+
+
+@pytest.mark.parametrize("B", [64, 4096])
+def test_single_read_ciera_many_chunks(B):
+    # 300 chunks: the look-back spans several rounds of 64 predecessors,
+    # each predecessor's size from its parts' words
+    rng = np.random.default_rng(41 + B)
+    n = 300 * 65536 - 999
+    x = wl.f32_to_bf16(rng.standard_normal(n, dtype=np.float32) * np.float32(0.01))
+    cache = wl.perturbed_cache(rng, x, 0.002)
+    s = check_encode_e0_ciera(x, B, cache, oracle.choose_e0(x))
+    check_roundtrip(s, x, B, cache.copy())
+
+
+def test_single_read_ciera_rejects_bad_window_base():
+    rng = np.random.default_rng(42)
+    x = wl.mixed_small(rng, 70000)
+    cache = wl.perturbed_cache(rng, x, 0.05)
+    for bad in (250, 255):
+        g, st, gc = gpu_encode_e0_ciera(x, 256, cache.copy(), torch.tensor([bad], dtype=torch.uint8, device="cuda"))
+        assert g is None and st == 1
+        assert np.array_equal(gc, cache), "the cache changed although nothing was encoded"
+
+
+def test_single_read_ciera_workload3():
+    d = wl.workload3()
+    x0, x1 = d["iters"]
+    say(f"single-read ciera workload3 n={x1.size}")
+    s = check_encode_e0_ciera(x1, 64, exps(x0), 116)
+    check_roundtrip(s, x1, 64, exps(x0))
