@@ -72,6 +72,15 @@ def test_argument_errors_return_before_any_launch(lib):
     assert lib.ciera_read_error(None, None) == 1
     assert lib.zip3_encode_e0(p, 10, None, p, 1 << 20, p, 1 << 20, p, None) == 1
     assert lib.zip3_encode_e0(p, 10, p, p, 10, p, 1 << 20, p, None) == 2
+    # ciera_encode_e0(x, n, B, cache, e0, out, cap, ws, ws_bytes, out_size, stream)
+    assert lib.ciera_encode_e0(p, 10, 0, p, p, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode_e0(p, 10, 96, p, p, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode_e0(p, 10, 64, p, None, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode_e0(p, 10, 64, None, p, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode_e0(p, 10, 64, ctypes.c_void_p(16 * 1024 + 8), p, p, 1 << 20, p, 1 << 20, p, None) == 1
+    assert lib.ciera_encode_e0(p, (1 << 39) + 1, 64, p, p, p, 1 << 50, p, 1 << 40, p, None) == 1
+    assert lib.ciera_encode_e0(p, 10, 64, p, p, p, 10, p, 1 << 20, p, None) == 2
+    assert lib.ciera_encode_e0(p, 10, 64, p, p, p, 1 << 20, p, 10, p, None) == 3
     assert lib.ciera_encode_hashed(p, 10, 64, None, p, 1 << 20, p, 1 << 20, p, None) == 1
     assert lib.ciera_encode_hashed(p, 10, 0, p, p, 1 << 20, p, 1 << 20, p, None) == 1
     assert lib.ciera_encode_hashed(p, 10, 64, ctypes.c_void_p(16 * 1024 + 8), p, 1 << 20, p, 1 << 20, p, None) == 1
