@@ -8,8 +8,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (ciera_decode, ciera_encode, ciera_max_encoded_size, ciera_read_error, ciera_workspace_size,
-               zip3_decode, zip3_encode, zip3_max_encoded_size, zip3_workspace_size)
+from . import (ciera_decode, ciera_encode, ciera_encode_e0, ciera_max_encoded_size, ciera_read_error,
+               ciera_workspace_size, zip3_decode, zip3_encode, zip3_encode_e0, zip3_max_encoded_size,
+               zip3_workspace_size)
 
 
 class Zip3Codec:
@@ -24,6 +25,12 @@ class Zip3Codec:
 
     def encode(self, x, e0_override: int = -1, stream=None):
         zip3_encode(x, self.out, self.ws, self.size, e0_override, stream)
+
+    def encode_e0(self, x, stream=None):
+        """Single-read encode with the window base of the previous stream in
+        ``out`` (its header byte 7, read on the device before it is
+        rewritten); the previous call must have been an encode."""
+        zip3_encode_e0(x, self.out, self.out, self.ws, self.size, 7, stream)
 
     def decode(self, stream_bytes, in_size: int, y, stream=None):
         zip3_decode(stream_bytes, in_size, y, self.ws, stream)
@@ -54,8 +61,23 @@ class CieraCodec:
     def encode(self, x, e0_override: int = -1, stream=None):
         ciera_encode(x, self.B, self.send_cache, self.out, self.ws, self.size, e0_override, stream)
 
+    def encode_e0(self, x, stream=None):
+        """Single-read encode (x and the sender cache read once) with the
+        window base of the previous stream in ``out`` (its header byte 7,
+        read on the device before it is rewritten); the previous call must
+        have been an encode."""
+        ciera_encode_e0(x, self.B, self.send_cache, self.out, self.out, self.ws, self.size, 7, stream)
+
     def decode(self, stream_bytes, in_size: int, y, stream=None):
         ciera_decode(stream_bytes, in_size, y, self.B, self.recv_cache, self.ws_dec, stream)
 
     def nbytes(self) -> int:
         return int(self.size.item())
+
+    def error(self, stream=None) -> int:
+        """Device status of the last encode."""
+        return ciera_read_error(self.ws, stream)
+
+    def decode_error(self, stream=None) -> int:
+        """Device status of the last decode."""
+        return ciera_read_error(self.ws_dec, stream)

@@ -140,3 +140,40 @@ def test_single_read_ciera_workload3():
     say(f"single-read ciera workload3 n={x1.size}")
     s = check_encode_e0_ciera(x1, 64, exps(x0), 116)
     check_roundtrip(s, x1, 64, exps(x0))
+
+
+def test_codec_encode_e0_takes_the_previous_window():
+    """Codec objects: after a full encode, encode_e0 takes the window base
+    from byte 7 of the previous stream in the same output buffer."""
+    from lossless_bf16_tensor_exp_amd.codec import CieraCodec, Zip3Codec
+    rng = np.random.default_rng(44)
+    n = 3 * 65536 + 999
+    xs = [wl.f32_to_bf16(rng.standard_normal(n, dtype=np.float32) * np.float32(0.02))]
+    for _ in range(2):
+        x = xs[-1].copy()
+        wl.flip(x, rng.choice(n, size=3000, replace=False))
+        xs.append(x)
+    dev = [torch.from_numpy(x.view(np.int16)).cuda() for x in xs]
+    z = Zip3Codec(n)
+    z.encode(dev[0])
+    torch.cuda.synchronize()
+    e0 = int(z.out[7].item())
+    for x, d in zip(xs[1:], dev[1:]):
+        z.encode_e0(d)
+        torch.cuda.synchronize()
+        assert z.error() == 0
+        o, st = oracle.encode(x, 0, None, e0)
+        assert z.out[:z.nbytes()].cpu().numpy().tobytes() == o.tobytes() and st["E0"] == e0
+    c = CieraCodec(n, 256)
+    cache = np.zeros(n, np.uint8)
+    c.encode(dev[0])
+    oracle.encode(xs[0], 256, cache)
+    torch.cuda.synchronize()
+    e0 = int(c.out[7].item())
+    for x, d in zip(xs[1:], dev[1:]):
+        c.encode_e0(d)
+        torch.cuda.synchronize()
+        assert c.error() == 0
+        o, _ = oracle.encode(x, 256, cache, e0)
+        assert c.out[:c.nbytes()].cpu().numpy().tobytes() == o.tobytes()
+        assert np.array_equal(c.send_cache[:n].cpu().numpy(), cache)
