@@ -136,7 +136,7 @@ def main() -> int:
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: --gpus {args.gpus} is not supported "
-              "(the codec runs on one rank's shard; see the sharding note in DESIGN.md)", file=sys.stderr)
+              "(the codec codes one rank's shard on its own GPU; there is no multi-GPU path)", file=sys.stderr)
         return 2
 
     import numpy as np
