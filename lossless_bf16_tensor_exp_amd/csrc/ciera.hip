@@ -2416,6 +2416,32 @@ __device__ inline uint32_t rans_push(uint32_t x, uint32_t f, uint32_t c, float r
   return (q << 12) + uint32_t(r) + c;
 }
 
+// Bytes sh .. sh + 15 of the 32 bytes p, q (p first), sh < 16.
+__device__ inline uint4 shift_bytes(const uint4& p, const uint4& q, uint32_t sh) {
+  const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+  const uint32_t r = sh & 3u;
+  uint32_t o[4];
+  switch (sh >> 2) {  // constant indices in each case (no private array)
+    case 0:
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r);
+      break;
+    case 1:
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 2], w[i + 1], r);
+      break;
+    case 2:
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 3], w[i + 2], r);
+      break;
+    default:
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 4], w[i + 3], r);
+      break;
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __restrict__ x, uint64_t n,
                                                            uint64_t nchunks, uint32_t log2B,
@@ -2644,14 +2670,40 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
       dst[tid] = uint16_t(v);
     }
     for (uint32_t k = tid; k < span; k += kPartThreads) dst[kRansHead / 2u + k] = uint16_t(s_f[lo_s + k]);
-    uint16_t* ds = dst + kRansHead / 2u + span;
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(ws.rslot + c * uint64_t(kRansSlot));
-    for (uint32_t k = tid; k < words; k += kPartThreads) {
-      uint32_t h = 0, off = k;
-      if (off >= w0) { off -= w0; h = 1u;
-        if (off >= w1) { off -= w1; h = 2u;
-          if (off >= w2) { off -= w2; h = 3u; } } }
-      ds[k] = src[h * kRansPartWords + s_wpos[h] + off];
+    // The part streams, from their regions of the scratch slot (16-byte
+    // aligned) to their place after the table (any even offset): a thread
+    // writes one 16-byte block of the payload from the two aligned source
+    // blocks that cover it; a part's first and last blocks, which it shares
+    // with what comes before and after, go byte by byte.
+    const uint8_t* slot = ws.rslot + c * uint64_t(kRansSlot);
+    uint8_t* pay = out + at;
+    uint32_t dpos = kRansHead + 2u * span;  // the part's first byte in the payload
+#pragma unroll 1
+    for (uint32_t h = 0; h < kParts; h++) {
+      const uint32_t len = 2u * s_nw[h];
+      if (len) {
+        const uint32_t region = h * 2u * kRansPartWords, region_end = region + 2u * kRansPartWords;
+        const int32_t delta = int32_t(region + 2u * s_wpos[h]) - int32_t(dpos);  // source byte = payload byte + delta
+        const uint32_t sh = uint32_t(delta) & 15u;  // the same for every block of the part
+        const uint32_t b_first = dpos / 16u, b_last = (dpos + len - 1u) / 16u;
+        for (uint32_t b = b_first + tid; b <= b_last; b += kPartThreads) {
+          const uint32_t d0 = 16u * b;
+          if (b == b_first || b == b_last) {
+            for (uint32_t i = 0; i < 16u; i++) {
+              const uint32_t d = d0 + i;
+              if (d >= dpos && d < dpos + len) pay[d] = slot[uint32_t(int32_t(d) + delta)];
+            }
+          } else {
+            const uint32_t a0 = uint32_t(int32_t(d0) + delta) & ~15u;
+            const uint4 p = *reinterpret_cast<const uint4*>(slot + a0);
+            // the next source block (inside the region whenever it is needed, sh > 0)
+            const uint4 q = (a0 + 16u < region_end) ? *reinterpret_cast<const uint4*>(slot + a0 + 16u)
+                                                    : make_uint4(0u, 0u, 0u, 0u);
+            *reinterpret_cast<uint4*>(pay + d0) = shift_bytes(p, q, sh);
+          }
+        }
+      }
+      dpos += len;
     }
     for (uint64_t k = bytes + tid; k < padded; k += kPartThreads) out[at + k] = 0u;
   }
