@@ -2671,39 +2671,52 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
     }
     for (uint32_t k = tid; k < span; k += kPartThreads) dst[kRansHead / 2u + k] = uint16_t(s_f[lo_s + k]);
     // The part streams, from their regions of the scratch slot (16-byte
-    // aligned) to their place after the table (any even offset): a thread
-    // writes one 16-byte block of the payload from the two aligned source
-    // blocks that cover it; a part's first and last blocks, which it shares
-    // with what comes before and after, go byte by byte.
-    const uint8_t* slot = ws.rslot + c * uint64_t(kRansSlot);
-    uint8_t* pay = out + at;
-    uint32_t dpos = kRansHead + 2u * span;  // the part's first byte in the payload
-#pragma unroll 1
+    // aligned) to their place after the table (any even offset), the blocks
+    // of all four parts dealt to the threads in one pass: a thread builds
+    // one 16-byte block of the payload from the two aligned source blocks
+    // that cover it (a source block outside the part's region holds no byte
+    // of the part and is not read) and stores it whole, or, for a part's
+    // first and last blocks, which it shares with what comes before and
+    // after, as the u16 units that belong to the part.
+    const uint8_t* __restrict__ slot = ws.rslot + c * uint64_t(kRansSlot);
+    uint8_t* __restrict__ pay = out + at;
+    uint32_t dp[kParts], ln[kParts], cum[kParts + 1];
+    int32_t dl[kParts];
+    cum[0] = 0u;
+    uint32_t dpos = kRansHead + 2u * span;  // a part's first byte in the payload
+#pragma unroll
     for (uint32_t h = 0; h < kParts; h++) {
-      const uint32_t len = 2u * s_nw[h];
-      if (len) {
-        const uint32_t region = h * 2u * kRansPartWords, region_end = region + 2u * kRansPartWords;
-        const int32_t delta = int32_t(region + 2u * s_wpos[h]) - int32_t(dpos);  // source byte = payload byte + delta
-        const uint32_t sh = uint32_t(delta) & 15u;  // the same for every block of the part
-        const uint32_t b_first = dpos / 16u, b_last = (dpos + len - 1u) / 16u;
-        for (uint32_t b = b_first + tid; b <= b_last; b += kPartThreads) {
-          const uint32_t d0 = 16u * b;
-          if (b == b_first || b == b_last) {
-            for (uint32_t i = 0; i < 16u; i++) {
-              const uint32_t d = d0 + i;
-              if (d >= dpos && d < dpos + len) pay[d] = slot[uint32_t(int32_t(d) + delta)];
-            }
-          } else {
-            const uint32_t a0 = uint32_t(int32_t(d0) + delta) & ~15u;
-            const uint4 p = *reinterpret_cast<const uint4*>(slot + a0);
-            // the next source block (inside the region whenever it is needed, sh > 0)
-            const uint4 q = (a0 + 16u < region_end) ? *reinterpret_cast<const uint4*>(slot + a0 + 16u)
-                                                    : make_uint4(0u, 0u, 0u, 0u);
-            *reinterpret_cast<uint4*>(pay + d0) = shift_bytes(p, q, sh);
-          }
+      dp[h] = dpos;
+      ln[h] = 2u * s_nw[h];
+      dl[h] = int32_t(h * 2u * kRansPartWords + 2u * s_wpos[h]) - int32_t(dpos);  // source byte = payload byte + dl
+      cum[h + 1] = cum[h] + (ln[h] ? (dpos + ln[h] - 1u) / 16u - dpos / 16u + 1u : 0u);
+      dpos += ln[h];
+    }
+    for (uint32_t k = tid; k < cum[kParts]; k += kPartThreads) {
+      uint32_t h = 0, d_lo = dp[0], d_len = ln[0], kb = cum[0];
+      int32_t delta = dl[0];
+#pragma unroll
+      for (uint32_t j = 1; j < kParts; j++)
+        if (k >= cum[j]) { h = j; d_lo = dp[j]; d_len = ln[j]; delta = dl[j]; kb = cum[j]; }
+      const int32_t region = int32_t(h * 2u * kRansPartWords), region_end = region + int32_t(2u * kRansPartWords);
+      const uint32_t b_first = d_lo / 16u, b_last = (d_lo + d_len - 1u) / 16u, b = b_first + (k - kb);
+      const uint32_t d0 = 16u * b;
+      const int32_t a0 = (int32_t(d0) + delta) & ~15;
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+      const uint4 p = (a0 >= region) ? *reinterpret_cast<const uint4*>(slot + a0) : zero;
+      const uint4 q = (a0 + 16 < region_end) ? *reinterpret_cast<const uint4*>(slot + a0 + 16) : zero;
+      const uint4 v = shift_bytes(p, q, uint32_t(delta) & 15u);
+      if (b != b_first && b != b_last) {
+        *reinterpret_cast<uint4*>(pay + d0) = v;
+      } else {
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (uint32_t i = 0; i < 8u; i++) {
+          const uint32_t d = d0 + 2u * i;
+          if (d >= d_lo && d < d_lo + d_len)
+            *reinterpret_cast<uint16_t*>(pay + d) = uint16_t(w[i / 2u] >> (16u * (i % 2u)));
         }
       }
-      dpos += len;
     }
     for (uint64_t k = bytes + tid; k < padded; k += kPartThreads) out[at + k] = 0u;
   }
