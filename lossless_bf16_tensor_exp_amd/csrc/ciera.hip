@@ -2304,6 +2304,7 @@ constexpr uint32_t kRansPartWords = 2u * kRansStates + kPartValues;  // a part s
 constexpr uint32_t kRansSlot = kParts * 2u * kRansPartWords;         // scratch per chunk: one region per part
 constexpr uint32_t kRansBlock = 1024u;   // payload bytes per block of a decoding wave's LDS ring
 constexpr uint32_t kRansWin = 8u;        // steps whose inputs a coding wave loads ahead
+constexpr uint32_t kSpanUnits = 8u;      // units of unchanged blocks a decoding thread moves at a time (ciera)
 constexpr uint32_t kGranules = kPartValues / 64u;  // a part's largest granule count (B = 64)
 
 __host__ __device__ inline uint64_t rans_sm_pos(uint64_t nchunks) { return kHeader + pad128(8u * (nchunks + 1u)); }
@@ -2398,22 +2399,39 @@ __device__ inline uint32_t part_incl_scan_u32(uint32_t v, uint32_t* s_w) {
   return before + incl;
 }
 
+// Encoder table entry of a symbol with frequency f >= 1 and cumulative
+// frequency c: x = thr is the largest state that needs no renormalisation
+// word (f 2^20 - 1), rfd a FP32 value a little below 1 / f, nf = -f, and
+// c | f << 16.
+struct RansEnt {
+  uint32_t thr;
+  float rfd;
+  int32_t nf;
+  uint32_t cf;
+};
+__device__ inline RansEnt rans_entry(uint32_t f, uint32_t c) {
+  RansEnt e;
+  e.thr = uint32_t((uint64_t(f) << 20) - 1u);
+  // rounded down from (1 - 2^-22) / f, so rfd (1 + 2^-24)^2 < 1 / f and
+  // rfd > (1 - 2^-21) / f
+  e.rfd = __double2float_rd((1.0 - 0x1p-22) / double(f));
+  e.nf = -int32_t(f);
+  e.cf = c | (f << 16);
+  return e;
+}
+
 // One encoder state update, x = (x div f) M + (x mod f) + c, for
-// x < f 2^20 (the state after its renormalisation), 1 <= f <= 4096, with
-// rf = 1 / f rounded to FP32.  The FP32 product x rf has a relative error
-// below 3 2^-24, so it is within 2^20 * 3 2^-24 < 0.2 of x / f < 2^20, and
-// its truncation is the quotient or one off either way; the remainder, exact
-// in 32-bit arithmetic, says which, and one step corrects it.
-__device__ inline uint32_t rans_push(uint32_t x, uint32_t f, uint32_t c, float rf) {
-  uint32_t q = uint32_t(float(x) * rf);                    // < 2^21: a 24-bit product suffices
-  int32_t r = int32_t(x - __umul24(q, f));  // exact: |r| < 2 f
-  const int32_t neg = r >> 31;                              // -1 when the quotient was one too large
-  q += uint32_t(neg);
-  r += neg & int32_t(f);
-  const uint32_t over = (r >= int32_t(f)) ? 1u : 0u;        // one too small
-  q += over;
-  r -= int32_t(over * f);
-  return (q << 12) + uint32_t(r) + c;
+// x < f 2^20 (the state after its renormalisation).  x and the product with
+// rfd are each rounded to FP32 (relative error 2^-24 each), so the product
+// p lies in ((1 - 2^-21) x / f, x / f]; as x / f < 2^20, p > x / f - 1/2.
+// Its truncation q0 is thus the quotient Q or Q - 1, and r0 = x - q0 f, exact
+// in 32 bits, is below 2 f: Q = q0 + (r0 >= f).  Then
+// x (div f) M + x mod f + c = x + c + Q (M - f) = (Q << 12) + x + c - Q f.
+__device__ inline uint32_t rans_push(uint32_t x, const RansEnt& e) {
+  const uint32_t q0 = uint32_t(float(x) * e.rfd);                     // < 2^20: 24-bit products suffice
+  const uint32_t r0 = uint32_t(__mul24(int32_t(q0), e.nf) + int32_t(x));  // exact: 0 <= r0 < 2 f
+  const uint32_t q = q0 + ((r0 >= (e.cf >> 16)) ? 1u : 0u);
+  return uint32_t(__mul24(int32_t(q), e.nf)) + ((q << 12) + x + (e.cf & 0xFFFFu));
 }
 
 // Bytes sh .. sh + 15 of the 32 bytes p, q (p first), sh < 16.
@@ -2446,8 +2464,8 @@ template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __restrict__ x, uint64_t n,
                                                            uint64_t nchunks, uint32_t log2B,
                                                            uint8_t* __restrict__ out, Ws ws) {
-  __shared__ uint32_t s_f[kBins], s_fc[kBins];  // f; f | cum << 16
-  __shared__ float s_rcp[kBins];                 // 1 / f, rounded to FP32
+  __shared__ uint32_t s_f[kBins];
+  __shared__ RansEnt s_ent[kBins];
   __shared__ uint16_t s_gl[kParts][kGranules];
   __shared__ __attribute__((aligned(16))) uint8_t s_sym[kPartWaves][kRansWin * kRansStates];
   __shared__ uint32_t s_bits[kBitmapWords], s_rank[kBitmapWords];
@@ -2511,8 +2529,7 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
   if (tid == top) f += kRansM - fsum;
   const uint32_t cum_incl = part_incl_scan_u32(f, s_w);
   s_f[tid] = f;
-  s_fc[tid] = f | ((cum_incl - f) << 16);
-  s_rcp[tid] = f ? float(1.0 / double(f)) : 0.0f;
+  s_ent[tid] = rans_entry(max(f, 1u), cum_incl - f);  // (symbols with f = 0 are never coded)
   // first and last symbol with f > 0
   uint32_t lo = f ? tid : 255u, hi = f ? tid : 0u;
   for (uint32_t o = 32; o >= 1; o >>= 1) {
@@ -2549,22 +2566,23 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
     const uint16_t* gl = s_gl[wave];
     uint8_t* sym = s_sym[wave];
     const uint32_t gmask = (1u << log2G) - 1u;
-    const uint64_t below = (1ull << lane) - 1u;
     constexpr uint32_t kGroup = kRansWin * kRansStates;
     auto value_of = [&](uint32_t i) -> uint32_t {  // chunk-relative value of the part's symbol i
       return kCiera ? ((uint32_t(gl[i >> log2G]) << log2G) | (i & gmask)) : (wave * kPartValues + i);
     };
     uint32_t xs = kRansL;
-    auto code = [&](uint32_t t, uint32_t fc, float rf, bool full) {
+    uint8_t* reg8 = reinterpret_cast<uint8_t*>(reg);
+    auto code = [&](uint32_t t, const RansEnt& e, bool full) {
       const bool act = full || t * kRansStates + lane < mh;
-      const uint32_t fs = fc & 0xFFFFu, cs = fc >> 16;
-      const bool emit = act && (xs >> 20) >= fs;  // x >= f 2^20
+      const bool emit = act && xs > e.thr;  // x >= f 2^20
       const uint64_t mk = __ballot(emit);
       const uint32_t ne = uint32_t(__popcll(mk));
-      if (emit) reg[wpos - ne + uint32_t(__popcll(mk & below))] = uint16_t(xs & 0xFFFFu);
-      xs = emit ? (xs >> 16) : xs;
-      wpos -= ne;
-      const uint32_t xn = rans_push(xs, fs, cs, rf);
+      const uint32_t rank = __builtin_amdgcn_mbcnt_hi(uint32_t(mk >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mk), 0u));
+      // (a 32-bit byte offset from the wave's base: one address operand)
+      wpos = __builtin_amdgcn_readfirstlane(wpos - ne);  // uniform: keep it scalar
+      if (emit) *reinterpret_cast<uint16_t*>(reg8 + 2u * (wpos + rank)) = uint16_t(xs & 0xFFFFu);
+      xs >>= emit ? 16u : 0u;
+      const uint32_t xn = rans_push(xs, e);
       xs = act ? xn : xs;
     };
     // one group: the lane's sign+mantissa bytes out, its exponents staged,
@@ -2574,19 +2592,14 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
       *reinterpret_cast<uint2*>(sym + 8u * lane) = unit_exponents(u);
       __builtin_amdgcn_wave_barrier();
       // the steps' table entries, read before the state chain needs them
-      uint32_t fcv[kRansWin];
-      float rfv[kRansWin];
+      RansEnt ev[kRansWin];
 #pragma unroll
-      for (uint32_t k = 0; k < kRansWin; k++) {
-        const uint32_t e = sym[k * kRansStates + lane];
-        fcv[k] = s_fc[e];
-        rfv[k] = s_rcp[e];
-      }
+      for (uint32_t k = 0; k < kRansWin; k++) ev[k] = s_ent[sym[k * kRansStates + lane]];
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int32_t k = int32_t(kRansWin) - 1; k >= 0; k--) {
         const uint32_t t = g * kRansWin + uint32_t(k);
-        if (full || t * kRansStates < mh) code(t, fcv[k], rfv[k], full);
+        if (full || t * kRansStates < mh) code(t, ev[k], full);
       }
     };
     const uint32_t ng = cdiv(mh, kGroup);
@@ -2854,15 +2867,30 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
   const uint32_t mh = part_granules(wave, nc, log2B, log2G, kCiera, s_bits, s_gl[wave]);
   if (lane == 0u) s_m[wave] = mh;
   if (kCiera) {
-    // values of unchanged blocks: sign+mantissa byte and the receiver cache
+    // values of unchanged blocks: sign+mantissa byte and the receiver cache,
+    // kSpanUnits units per thread at a time with all their loads issued
+    // before the first store
     const uint32_t nunits = (nc + 7u) / 8u;
-    for (uint32_t u = tid; u < nunits; u += kPartThreads) {
-      const uint32_t blk = (8u * u) >> log2B;
-      if ((s_bits[blk >> 5] >> (blk & 31u)) & 1u) continue;
-      const uint32_t k = min(8u, nc - 8u * u);
-      const uint2 sm = load_bytes8(in + sm_pos + start + 8ull * u, k);
-      const uint2 e = load_bytes8(cache + start + 8ull * u, k);
-      store_unit(y, start + 8ull * u, k, unit_join(sm, e));
+    for (uint32_t u0 = 0; u0 < nunits; u0 += kSpanUnits * kPartThreads) {
+      uint2 smv[kSpanUnits], ev[kSpanUnits];
+      uint32_t keep = 0;
+#pragma unroll
+      for (uint32_t j = 0; j < kSpanUnits; j++) {
+        const uint32_t u = u0 + j * kPartThreads + tid;
+        const uint32_t blk = (8u * u) >> log2B;
+        smv[j] = ev[j] = make_uint2(0u, 0u);
+        if (u < nunits && !((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) {
+          const uint32_t k = min(8u, nc - 8u * u);
+          smv[j] = load_bytes8(in + sm_pos + start + 8ull * u, k);
+          ev[j] = load_bytes8(cache + start + 8ull * u, k);
+          keep |= 1u << j;
+        }
+      }
+#pragma unroll
+      for (uint32_t j = 0; j < kSpanUnits; j++) {
+        const uint32_t u = u0 + j * kPartThreads + tid;
+        if ((keep >> j) & 1u) store_unit(y, start + 8ull * u, min(8u, nc - 8u * u), unit_join(smv[j], ev[j]));
+      }
     }
   }
   __syncthreads();
@@ -2979,7 +3007,6 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
     uint32_t xs = word(2u * lane) | (word(2u * lane + 1u) << 16);
     okd = xs >= kRansL;
     uint32_t q = 2u * kRansStates;
-    const uint64_t below = (1ull << lane) - 1u;
     auto want = [&]() -> uint32_t { return min((so + 2u * q) / kRansBlock + 2u, jmax); };
     uint32_t jp = want();
     uint4 pend = block_load(jp);
@@ -2993,11 +3020,11 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
       }
       const bool need = act && xs < kRansL;
       const uint64_t mk = __ballot(need);
-      if (need) {
-        const uint32_t kk = q + uint32_t(__popcll(mk & below));
-        if (kk < nw) xs = (xs << 16) | word(kk); else okd = false;
-      }
-      q += uint32_t(__popcll(mk));
+      // word q + (the lanes below that need one); a read past the part's
+      // words stays inside the ring and fails the count check at the end
+      const uint32_t kk = __builtin_amdgcn_mbcnt_hi(uint32_t(mk >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mk), q));
+      if (need) xs = (xs << 16) | word(kk);
+      q = __builtin_amdgcn_readfirstlane(q + uint32_t(__popcll(mk)));  // uniform: keep it scalar
       return s;
     };
     // One group of kRansWin steps (512 symbols): the steps' symbols go to the
