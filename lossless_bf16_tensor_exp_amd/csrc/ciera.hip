@@ -1076,12 +1076,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
     const Partial* pp = ws.partial + c * kParts;
     // Coded values with exponent in [E0, E0 + 6], per part: bins E0..E0+6
     // lie in the two 16-byte words q = E0 / 8 and q + 1 of the part's row
-    // (q + 1 <= 31 since E0 <= 249), at u16 positions r .. r + 6, r = E0 mod 8.
+    // (only in word q when E0 >= 248, and q + 1 is then past the row and not
+    // read), at u16 positions r .. r + 6, r = E0 mod 8.
     uint32_t inwin[kParts];
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) {
       const uint4* row = reinterpret_cast<const uint4*>(ws.hist + (c * kParts + h) * kBins) + (e0 >> 3);
-      const uint4 a = row[0], b = row[1];
+      const uint4 a = row[0], b = (e0 >> 3) < kBins / 8u - 1u ? row[1] : make_uint4(0u, 0u, 0u, 0u);
       const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
       uint32_t sum = 0;
 #pragma unroll
