@@ -31,6 +31,10 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+# VALU issue peak of MI355X: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz lane
+# instructions per second (a wave64 instruction occupies a 16-lane SIMD for 4
+# cycles): 614.4 G wave instructions/s.
+VALU_PEAK_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 WORKLOAD_NAMES = {
     1: "shard 1,048,576 BF16 ~N(0,0.02), iter t = iter t-1 + N(0,1e-4); exponent reuse B=256 + 3-bit code",
     2: "gradient 67,108,864 BF16 ~N(0,1e-3) + 0.1% Student-t(3); 3-bit code only, 128-B chunks",
@@ -99,6 +103,38 @@ def changed_values(prev, cur, B):
     sizes = np.full(nb, B, dtype=np.int64)
     sizes[-1] = n - (nb - 1) * B
     return int(sizes[blk].sum())
+
+
+def load_valu(kernel: str, workload: int, B: int):
+    """VALU wave instructions per launch (rocprofv3 SQ_INSTS_VALU, a device
+    total) from the ```json blocks of the instruction summaries in profiles/,
+    if they were taken on the current kernel source."""
+    import glob
+    import re
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*valu*.md"))):
+        with open(path) as f:
+            text = f.read()
+        for block in re.findall(r"```json\n(.*?)```", text, flags=re.S):
+            rec = json.loads(block)
+            if rec.get("source_hash") != source_hash():
+                continue
+            hit = rec.get("kernels", {}).get(f"{kernel}/w{workload}/B{B}")
+            if hit is not None:
+                return hit
+    return None
+
+
+def alu_roofline(kernel: str, key: str, workload: int, B: int, ms: float):
+    """The kernel against the VALU issue peak: its counted VALU instructions
+    per launch over its average duration (null without a counter record)."""
+    v = load_valu(key, workload, B)
+    if v is None:
+        return {"kernel": kernel, "bound": "alu", "achieved": None, "peak": VALU_PEAK_WAVE_INSTR_PER_S / 1e9,
+                "unit": "G VALU wave instr/s", "frac": None}
+    a = v / (ms * 1e-3)
+    return {"kernel": kernel, "bound": "alu", "achieved": round(a / 1e9, 1), "peak": VALU_PEAK_WAVE_INSTR_PER_S / 1e9,
+            "unit": "G VALU wave instr/s", "frac": round(a / VALU_PEAK_WAVE_INSTR_PER_S, 4),
+            "valu_instr_per_launch": v, "avg_launch_ms": round(ms, 5)}
 
 
 def load_traffic(kernel: str, workload: int, B: int):
@@ -404,7 +440,9 @@ def main() -> int:
         hk = [sum(evk[i][j][0].elapsed_time(evk[i][j][1]) for i in range(K)) / K for j in range(3)]
         hashed = {"encode_ms": round(ms[len(ms) // 2], 5), "encode_min_ms": round(ms[0], 5),
                   "cache_bytes": hsz, "stream_equal_to_exact_sender": same,
-                  "kernels": {"k_stats": round(hk[0], 5), "k_plan": round(hk[1], 5), "k_write": round(hk[2], 5)}}
+                  "kernels": {"k_stats": round(hk[0], 5), "k_plan": round(hk[1], 5), "k_write": round(hk[2], 5)},
+                  # its k_stats hashes every exponent word twice: VALU-bound
+                  "alu_roofline": alu_roofline("k_stats<true, true>", "k_stats_hash", args.workload, B, hk[0])}
         del h_pristine, h_cache, out_h
     # rANS modes: the same input and caches, the coded exponents range-ANS
     # coded instead of the 3-bit code; encode and decode timed like pass 3,
@@ -450,7 +488,11 @@ def main() -> int:
             "decode_ms": round(r_dec, 5), "decode_min_ms": round(r_dec_min, 5),
             "stream_bytes": szr, "roundtrip_ok": r_ok,
             "kernels": {"k_stats": round(rk[0], 5), "k_rans_enc": round(rk[1], 5), "k_rans_finish": round(rk[2], 5),
-                        "k_rans_dec": round(rk[3], 5)}}
+                        "k_rans_dec": round(rk[3], 5)},
+            # the coders are bound by their dependent steps, not by HBM:
+            # their VALU issue rate against the chip's
+            "alu_roofline": [alu_roofline("k_rans_enc", "k_rans_enc", args.workload, B, rk[1]),
+                             alu_roofline("k_rans_dec", "k_rans_dec", args.workload, B, rk[3])]}
     del out_r, ws_r, y_r
     del sweep
 
