@@ -59,6 +59,15 @@
  *    codes as three aligned 1-bit arrays) and Figure 1 (codec writes the
  *    collective's chunk layout; only a size exchange is added).
  *
+ * Parity unpinned by the pages: the byte layout below (the pages print no
+ * encoded bytes; the tests pin it only by the closed-form stream size and a
+ * second, independent encoder), the rANS variant's format and parameters
+ * further down (the CIERA page names an ANS coder and gives no parameters;
+ * pinned by a second encoder, a worked normalisation and the information
+ * content), and hash 1's seed and increment (chosen here; only their
+ * behaviour is checked).  Every value the pages do fix (fields, window,
+ * codes, reuse, SplitMix64) is pinned by the tests against the pages.
+ *
  * Byte layout (all integers little-endian, all unnamed bytes zero):
  *
  *   header, 128 bytes:
