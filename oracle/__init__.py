@@ -21,6 +21,7 @@ from __future__ import annotations
 import ctypes
 import os
 import subprocess
+from fractions import Fraction
 
 import numpy as np
 
@@ -45,7 +46,7 @@ def build(force: bool = True) -> str:
     if force or not os.path.exists(_LIB_PATH):
         tmp = _LIB_PATH + ".tmp"
         cmd = ["gcc", "-O2", "-std=c99", "-Wall", "-Wextra", "-fPIC", "-shared",
-               "-ffp-contract=off", "-o", tmp, _SRC, "-lm"]
+               "-ffp-contract=off", "-pthread", "-o", tmp, _SRC, "-lm"]
         subprocess.run(cmd, check=True)
         os.replace(tmp, _LIB_PATH)
     return _LIB_PATH
@@ -61,8 +62,10 @@ def _load():
     u64, u32, vp, i32 = ctypes.c_uint64, ctypes.c_uint32, ctypes.c_void_p, ctypes.c_int
     lib.orc_bf16_value.argtypes = [ctypes.c_uint16]
     lib.orc_bf16_value.restype = ctypes.c_double
-    lib.orc_variance.argtypes = [vp, u64, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(u64)]
-    lib.orc_variance.restype = None
+    lib.orc_exponent_sums.argtypes = [vp, u64, vp, vp, ctypes.POINTER(u64)]
+    lib.orc_exponent_sums.restype = None
+    lib.orc_window_base_exact.argtypes = [vp, vp, u64]
+    lib.orc_window_base_exact.restype = i32
     lib.orc_window_base.argtypes = [ctypes.c_double, u64]
     lib.orc_window_base.restype = i32
     lib.orc_choose_e0.argtypes = [vp, u64]
@@ -73,6 +76,10 @@ def _load():
     lib.orc_encode.restype = i32
     lib.orc_decode.argtypes = [vp, u64, vp, u64, u32, vp]
     lib.orc_decode.restype = i32
+    lib.orc_encode_mt.argtypes = [vp, u64, u32, vp, i32, vp, u64, ctypes.POINTER(u64), vp, i32]
+    lib.orc_encode_mt.restype = i32
+    lib.orc_decode_mt.argtypes = [vp, u64, vp, u64, u32, vp, i32]
+    lib.orc_decode_mt.restype = i32
     lib.orc_splitmix64_next.argtypes = [ctypes.POINTER(u64)]
     lib.orc_splitmix64_next.restype = u64
     lib.orc_block_hashes.argtypes = [vp, u64, u32, vp]
@@ -104,12 +111,34 @@ def bf16_value(bits: int) -> float:
     return _load().orc_bf16_value(bits)
 
 
-def variance(x) -> tuple[float, int]:
-    """(sample variance of the finite values, number of finite values)."""
+def exponent_sums(x) -> tuple[np.ndarray, np.ndarray, int]:
+    """Per exponent field E (256 entries): the sum of the signed integer
+    significands M and of M^2 over the finite values (a value is
+    M * 2^(max(E, 1) - 134)), and the number of finite values."""
     x = _u16(x)
-    var, nf = ctypes.c_double(), ctypes.c_uint64()
-    _load().orc_variance(_ptr(x), x.size, ctypes.byref(var), ctypes.byref(nf))
-    return var.value, nf.value
+    a = np.zeros(256, dtype=np.int64)
+    b = np.zeros(256, dtype=np.uint64)
+    nf = ctypes.c_uint64()
+    _load().orc_exponent_sums(_ptr(x), x.size, _ptr(a), _ptr(b), ctypes.byref(nf))
+    return a, b, nf.value
+
+
+def exact_moments(x) -> tuple[int, Fraction, Fraction]:
+    """(finite count, exact sum of the finite values, exact sum of their
+    squares), from the oracle's integer sums."""
+    a, b, nf = exponent_sums(x)
+    s1 = sum(int(a[e]) << (max(e, 1) - 1) for e in range(255))
+    s2 = sum(int(b[e]) << (2 * max(e, 1) - 2) for e in range(255))
+    return nf, Fraction(s1, 1 << 133), Fraction(s2, 1 << 266)
+
+
+def variance(x) -> tuple[Fraction, int]:
+    """(exact sample variance of the finite values, number of finite values);
+    0 when fewer than two values are finite."""
+    nf, s1, s2 = exact_moments(x)
+    if nf < 2:
+        return Fraction(0), nf
+    return (nf * s2 - s1 * s1) / (nf * (nf - 1)), nf
 
 
 def window_base(var: float, nfinite: int) -> int:
@@ -121,15 +150,24 @@ def choose_e0(x) -> int:
     return _load().orc_choose_e0(_ptr(x), x.size)
 
 
+def window_base_exact(a, b, nf: int) -> int:
+    """Window base from per-exponent significand sums (see exponent_sums)."""
+    a = np.ascontiguousarray(a, dtype=np.int64)
+    b = np.ascontiguousarray(b, dtype=np.uint64)
+    assert a.size == 256 and b.size == 256
+    return _load().orc_window_base_exact(_ptr(a), _ptr(b), nf)
+
+
 def max_encoded_size(n: int, B: int = 0) -> int:
     return _load().orc_max_encoded_size(n, B)
 
 
-def encode(x, B: int = 0, cache: np.ndarray | None = None, e0_override: int = -1):
+def encode(x, B: int = 0, cache: np.ndarray | None = None, e0_override: int = -1, threads: int = 0):
     """Encode ``x`` (uint16 BF16 patterns).  ``B = 0`` is zip3 mode; otherwise
     ciera mode with block size ``B`` and the sender cache ``cache`` (uint8,
-    len(x), updated in place).  Returns (stream bytes as uint8 array,
-    {"E0", "changed_blocks", "escapes"})."""
+    len(x), updated in place).  ``threads`` > 0 runs the chunk-parallel
+    driver on that many threads (same bytes).  Returns (stream bytes as uint8
+    array, {"E0", "changed_blocks", "escapes"})."""
     x = _u16(x)
     n = x.size
     if B:
@@ -139,23 +177,30 @@ def encode(x, B: int = 0, cache: np.ndarray | None = None, e0_override: int = -1
     out = np.zeros(cap, dtype=np.uint8)
     size = ctypes.c_uint64()
     stats = np.zeros(3, dtype=np.uint64)
-    st = _load().orc_encode(_ptr(x), n, B, _ptr(cache) if B else None, e0_override,
-                            _ptr(out), cap, ctypes.byref(size), _ptr(stats))
+    if threads > 0:
+        st = _load().orc_encode_mt(_ptr(x), n, B, _ptr(cache) if B else None, e0_override,
+                                   _ptr(out), cap, ctypes.byref(size), _ptr(stats), threads)
+    else:
+        st = _load().orc_encode(_ptr(x), n, B, _ptr(cache) if B else None, e0_override,
+                                _ptr(out), cap, ctypes.byref(size), _ptr(stats))
     if st != OK:
         raise OracleError(st, "encode")
     return out[: size.value].copy(), {"E0": int(stats[0]), "changed_blocks": int(stats[1]),
                                       "escapes": int(stats[2])}
 
 
-def decode(stream, n: int, B: int = 0, cache: np.ndarray | None = None) -> np.ndarray:
+def decode(stream, n: int, B: int = 0, cache: np.ndarray | None = None, threads: int = 0) -> np.ndarray:
     """Decode a stream back to n uint16 BF16 patterns (ciera mode updates
-    ``cache`` in place)."""
+    ``cache`` in place); ``threads`` > 0 decodes chunks on that many threads."""
     stream = np.ascontiguousarray(stream, dtype=np.uint8).reshape(-1)
     y = np.zeros(n, dtype=np.uint16)
     if B:
         if cache is None or cache.dtype != np.uint8 or cache.size != n or not cache.flags.c_contiguous:
             raise ValueError("ciera mode needs a contiguous uint8 cache of n bytes")
-    st = _load().orc_decode(_ptr(stream), stream.size, _ptr(y), n, B, _ptr(cache) if B else None)
+    if threads > 0:
+        st = _load().orc_decode_mt(_ptr(stream), stream.size, _ptr(y), n, B, _ptr(cache) if B else None, threads)
+    else:
+        st = _load().orc_decode(_ptr(stream), stream.size, _ptr(y), n, B, _ptr(cache) if B else None)
     if st != OK:
         raise OracleError(st, "decode")
     return y

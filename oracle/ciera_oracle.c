@@ -64,9 +64,13 @@
  * second, independent encoder), the rANS variant's format and parameters
  * further down (the CIERA page names an ANS coder and gives no parameters;
  * pinned by a second encoder, a worked normalisation and the information
- * content), and hash 1's seed and increment (chosen here; only their
- * behaviour is checked).  Every value the pages do fix (fields, window,
- * codes, reuse, SplitMix64) is pinned by the tests against the pages.
+ * content), and hash 1's seed and increment (chosen here: the pages give
+ * none; both hashes are pinned by value against an independent
+ * implementation of the construction below, hash 0 also against
+ * SplitMix64's published outputs).  Every value the pages do fix (fields,
+ * window, codes, reuse, SplitMix64) is pinned by the tests against the
+ * pages, and the largest-stream bound against the closed-form size at full
+ * counts and a stream that attains it.
  *
  * Byte layout (all integers little-endian, all unnamed bytes zero):
  *
@@ -103,11 +107,25 @@
  *     4. escapes: one byte (the raw exponent) per code-0 slot that holds a
  *                value, in slot order.
  *
- * Floating point: the variance is computed in FP64 (the precision the GPU
- * kernels use for the same statistic) with one-pass sums shifted by the
- * first value (0 if it is not finite), summed in element order.
+ * The statistic is exact.  Every finite BF16 value is an integer significand
+ * M (|M| <= 255, the hidden bit included) times 2^(E'-134), E' = max(E, 1).
+ * Per exponent field E the oracle sums M and M^2 in 64-bit integers, so the
+ * sums do not depend on the order of the values; the variance
+ * (n S2 - S1^2) / (n (n - 1)) is then formed and compared with the
+ * thresholds K0 * 4^k in fixed-size integer arithmetic (768-bit, enough for
+ * n <= 2^40), with K0 taken as the double nearest 16383 / (28 ln 2).
+ * No rounding happens anywhere, so a chunk-parallel run that adds the same
+ * integer sums gives the same window.
+ *
+ * orc_encode_mt / orc_decode_mt run the same per-chunk steps as orc_encode /
+ * orc_decode on several threads (chunks are self-contained segments; their
+ * offsets come from the closed-form size of each chunk, checked against what
+ * the chunk's writer returns).  They exist to time the oracle on all host
+ * cores and to check full-size tensors quickly; their output is byte-equal
+ * to the single-threaded functions', which the tests check.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -173,35 +191,168 @@ double orc_bf16_value(uint16_t v) {
   return (v & 0x8000u) ? -mag : mag;
 }
 
-/* Sample variance (correction 1) of the finite values of x; NaN and +-Inf
- * (exponent field 255) are left out.  ZipCCL digest, section 3.1: sigma from
- * one standard-deviation call. */
-void orc_variance(const uint16_t* x, uint64_t n, double* var_out, uint64_t* nfinite_out) {
-  double shift = 0.0;
-  if (n > 0 && exp_field(x[0]) != 255u) shift = orc_bf16_value(x[0]);
-  uint64_t nf = 0;
-  double s1 = 0.0, s2 = 0.0;
-  for (uint64_t i = 0; i < n; i++) {
-    if (exp_field(x[i]) == 255u) continue;
-    double d = orc_bf16_value(x[i]) - shift;
-    s1 += d;
-    s2 += d * d;
-    nf++;
-  }
-  double var = 0.0;
-  if (nf >= 2) {
-    var = (s2 - s1 * s1 / (double)nf) / (double)(nf - 1);
-    if (!(var > 0.0)) var = 0.0;
-  }
-  *var_out = var;
-  *nfinite_out = nf;
+/* ---- exact window statistic ---------------------------------------------
+ * ZipCCL digest, section 3.1: sigma comes from one standard-deviation call
+ * over the tensor (sample variance, correction 1); NaN and +-Inf (exponent
+ * field 255) are left out, since a plain std of them is NaN.
+ *
+ * A finite value is M 2^(E'-134) with M = +-(128 + m) for E >= 1, M = +-m
+ * for E = 0, and E' = max(E, 1).  a[E] = sum of M and b[E] = sum of M^2 over
+ * the finite values with exponent field E (|a| < 2^48, b < 2^56 for
+ * n <= 2^40).  Scaled by 2^133 and 2^266, the sums of the values and of their
+ * squares are the integers s1 = sum a[E] 2^(E'-1) (< 2^310 in magnitude)
+ * and s2 = sum b[E] 2^(2E'-2) (< 2^570), and
+ *     var = (nf s2 - s1^2) / (nf (nf - 1) 2^266).
+ * With K0 = K0m 2^-43 (K0m the 53-bit integer significand of the double),
+ *     var >= K0 4^k  <=>  nf s2 - s1^2 >= K0m nf (nf - 1) 2^(223 + 2k),
+ * both sides below 2^660 for every k in [-127, 122]. */
+#define BN_LIMBS 24 /* 768 bits */
+typedef struct {
+  uint32_t w[BN_LIMBS]; /* little-endian 32-bit limbs */
+} bn_t;
+
+static void bn_from_u64(bn_t* a, uint64_t v) {
+  memset(a, 0, sizeof(*a));
+  a->w[0] = (uint32_t)v;
+  a->w[1] = (uint32_t)(v >> 32);
 }
 
-/* Window base E0 from the variance.  x_opt = 0.5 log2(var) + 0.5 log2(14 ln2 /
- * 16383); the window's first unbiased exponent is k = floor(x_opt + 1/2),
- * i.e. the largest k with var >= K0 * 4^k.  E0 = 127 + k, clamped to
- * [0, 249] so that E0+6 stays a valid 8-bit field.  No finite spread
- * (fewer than two finite values, or zero variance) gives E0 = 0. */
+static void bn_shl(bn_t* a, unsigned sh) {
+  const unsigned limbs = sh / 32u, bits = sh % 32u;
+  for (int i = BN_LIMBS - 1; i >= 0; i--) {
+    uint64_t hi = (i - (int)limbs >= 0) ? a->w[i - limbs] : 0u;
+    uint64_t lo = (i - (int)limbs - 1 >= 0) ? a->w[i - limbs - 1] : 0u;
+    a->w[i] = (uint32_t)(((hi << 32 | lo) << bits) >> 32);
+  }
+}
+
+static void bn_add(bn_t* a, const bn_t* b) {
+  uint64_t carry = 0;
+  for (int i = 0; i < BN_LIMBS; i++) {
+    carry += (uint64_t)a->w[i] + b->w[i];
+    a->w[i] = (uint32_t)carry;
+    carry >>= 32;
+  }
+}
+
+/* a -= b; requires a >= b. */
+static void bn_sub(bn_t* a, const bn_t* b) {
+  int64_t borrow = 0;
+  for (int i = 0; i < BN_LIMBS; i++) {
+    int64_t d = (int64_t)a->w[i] - (int64_t)b->w[i] - borrow;
+    borrow = d < 0;
+    a->w[i] = (uint32_t)(d + (borrow << 32));
+  }
+}
+
+static int bn_cmp(const bn_t* a, const bn_t* b) {
+  for (int i = BN_LIMBS - 1; i >= 0; i--)
+    if (a->w[i] != b->w[i]) return a->w[i] < b->w[i] ? -1 : 1;
+  return 0;
+}
+
+/* r = a * b; the operands' sizes keep the product below 2^768. */
+static void bn_mul(bn_t* r, const bn_t* a, const bn_t* b) {
+  uint32_t acc[2 * BN_LIMBS];
+  memset(acc, 0, sizeof(acc));
+  for (int i = 0; i < BN_LIMBS; i++) {
+    uint64_t carry = 0;
+    for (int j = 0; j < BN_LIMBS; j++) {
+      carry += (uint64_t)a->w[i] * b->w[j] + acc[i + j];
+      acc[i + j] = (uint32_t)carry;
+      carry >>= 32;
+    }
+    acc[i + BN_LIMBS] = (uint32_t)carry;
+  }
+  memcpy(r->w, acc, sizeof(r->w));
+}
+
+static void bn_mul_u64(bn_t* a, uint64_t m) {
+  bn_t t;
+  bn_from_u64(&t, m);
+  bn_t r;
+  bn_mul(&r, a, &t);
+  *a = r;
+}
+
+/* Per exponent field: the sum of the signed significands and of their
+ * squares over the finite values, and the number of finite values.  a and b
+ * have 256 entries (entry 255 stays 0). */
+void orc_exponent_sums(const uint16_t* x, uint64_t n, int64_t* a, uint64_t* b, uint64_t* nfinite) {
+  memset(a, 0, 256 * sizeof(int64_t));
+  memset(b, 0, 256 * sizeof(uint64_t));
+  uint64_t nf = 0;
+  for (uint64_t i = 0; i < n; i++) {
+    const unsigned e = exp_field(x[i]);
+    if (e == 255u) continue;
+    const int64_t mag = (int64_t)((e == 0u ? 0u : 128u) + (x[i] & 0x7Fu));
+    a[e] += (x[i] & 0x8000u) ? -mag : mag;
+    b[e] += (uint64_t)(mag * mag);
+    nf++;
+  }
+  *nfinite = nf;
+}
+
+/* Window base from exact sums (see above): E0 = clamp(127 + k, 0, 249) for
+ * the largest k with var >= K0 4^k; E0 = 0 when nf < 2 or var = 0. */
+int orc_window_base_exact(const int64_t* a, const uint64_t* b, uint64_t nf) {
+  if (nf < 2) return 0;
+  bn_t pos, neg, s2, t;
+  bn_from_u64(&pos, 0);
+  bn_from_u64(&neg, 0);
+  bn_from_u64(&s2, 0);
+  for (unsigned e = 0; e < 255u; e++) {
+    const unsigned ep = e ? e : 1u;
+    if (a[e] != 0) {
+      bn_from_u64(&t, a[e] > 0 ? (uint64_t)a[e] : (uint64_t)(-a[e]));
+      bn_shl(&t, ep - 1u);
+      bn_add(a[e] > 0 ? &pos : &neg, &t);
+    }
+    bn_from_u64(&t, b[e]);
+    bn_shl(&t, 2u * ep - 2u);
+    bn_add(&s2, &t);
+  }
+  /* |s1| = |pos - neg| */
+  bn_t s1 = pos;
+  if (bn_cmp(&pos, &neg) >= 0) {
+    bn_sub(&s1, &neg);
+  } else {
+    s1 = neg;
+    bn_sub(&s1, &pos);
+  }
+  bn_t d, sq;
+  d = s2;
+  bn_mul_u64(&d, nf);
+  bn_mul(&sq, &s1, &s1);
+  bn_sub(&d, &sq); /* nf s2 - s1^2 >= 0 (Cauchy-Schwarz) */
+  bn_t zero;
+  bn_from_u64(&zero, 0);
+  if (bn_cmp(&d, &zero) == 0) return 0;
+
+  int exp2;
+  const double mant = frexp(ORC_K0, &exp2);          /* K0 = mant 2^exp2, mant in [1/2, 1) */
+  const uint64_t k0m = (uint64_t)ldexp(mant, 53);   /* exact: a 53-bit integer */
+  const int k0e = exp2 - 53;                         /* K0 = k0m 2^k0e (k0e = -43) */
+  int e0 = 0;
+  for (int k = -127; k <= 122; k++) {
+    /* var >= K0 4^k  <=>  d 2^266 ... rearranged: d >= k0m nf (nf-1) 2^(266 + k0e + 2k) */
+    const int sh = 266 + k0e + 2 * k;
+    bn_t lhs = d, rhs;
+    bn_from_u64(&rhs, k0m);
+    bn_mul_u64(&rhs, nf);
+    bn_mul_u64(&rhs, nf - 1u);
+    if (sh >= 0)
+      bn_shl(&rhs, (unsigned)sh);
+    else
+      bn_shl(&lhs, (unsigned)(-sh));
+    if (bn_cmp(&lhs, &rhs) >= 0) e0 = 127 + k;
+  }
+  return e0;
+}
+
+/* Window base for a given variance (a double, so K0 4^k and the comparison
+ * are exact): the largest k with var >= K0 4^k, E0 = clamp(127 + k, 0, 249);
+ * E0 = 0 for fewer than two finite values or var <= 0. */
 int orc_window_base(double var, uint64_t nfinite) {
   if (nfinite < 2 || !(var > 0.0)) return 0;
   int e0 = 0;
@@ -212,10 +363,10 @@ int orc_window_base(double var, uint64_t nfinite) {
 }
 
 int orc_choose_e0(const uint16_t* x, uint64_t n) {
-  double var;
-  uint64_t nf;
-  orc_variance(x, n, &var, &nf);
-  return orc_window_base(var, nf);
+  int64_t a[256];
+  uint64_t b[256], nf;
+  orc_exponent_sums(x, n, a, b, &nf);
+  return orc_window_base_exact(a, b, nf);
 }
 
 /* SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
@@ -288,6 +439,122 @@ uint64_t orc_max_encoded_size(uint64_t n, uint32_t B) {
   return size;
 }
 
+/* ---- 3-bit encode ------------------------------------------------------- */
+
+/* Values in chunk c. */
+static uint64_t chunk_len(uint64_t n, uint64_t c) {
+  const uint64_t start = c * ORC_CHUNK;
+  return (n - start < ORC_CHUNK) ? n - start : ORC_CHUNK;
+}
+
+/* What the writer of one chunk reads. */
+typedef struct {
+  const uint16_t* x;
+  uint64_t n;
+  uint32_t B;             /* 0: zip3 mode */
+  const uint8_t* changed; /* ciera mode: one flag per block */
+  unsigned e0;
+  uint64_t nchunks;
+  uint8_t* out;
+} orc_enc;
+
+/* Writes chunk c's table entry, its sections from stream offset pos and its
+ * escape-index entry; returns the offset after its last section.  *nch_out
+ * and *nesc_out receive its changed blocks and escapes. */
+static uint64_t encode_chunk(const orc_enc* e, uint64_t c, uint64_t pos, uint64_t* nch_out, uint64_t* nesc_out) {
+  const int ciera = (e->B != 0);
+  const uint32_t B = e->B;
+  const uint16_t* x = e->x;
+  uint8_t* out = e->out;
+  const uint64_t start = c * ORC_CHUNK;
+  const uint64_t nc = chunk_len(e->n, c);
+  put_u64(out + ORC_HEADER + 8ull * c, pos);
+  /* escape index: escapes among the chunk's values before quarter q */
+  uint64_t quarter_esc[4] = {0, 0, 0, 0};
+  unsigned next_q = 1;
+
+  /* 1. sign+mantissa bytes of every value */
+  for (uint64_t t = 0; t < nc; t++) out[pos + t] = (uint8_t)sm_field(x[start + t]);
+  pos += pad128(nc);
+
+  /* 2. bitmap of changed blocks */
+  uint64_t nch = 0, nb = 0;
+  if (ciera) {
+    nb = ceil_div(nc, B);
+    for (uint64_t j = 0; j < nb; j++) {
+      if (e->changed[start / B + j]) {
+        out[pos + j / 8] |= (uint8_t)(1u << (j % 8));
+        nch++;
+      }
+    }
+    pos += pad128(ceil_div(nb, 8));
+  }
+
+  /* 3./4. code planes and escapes, slot by slot */
+  const uint64_t plane_bytes = ciera ? nch * B / 8 : ceil_div(nc, 8);
+  const uint64_t plane_pos[3] = {pos, pos + pad128(plane_bytes), pos + 2 * pad128(plane_bytes)};
+  const uint64_t esc_pos = pos + 3 * pad128(plane_bytes);
+  uint64_t nesc = 0;
+  uint64_t slot = 0;
+  if (!ciera) {
+    for (uint64_t t = 0; t < nc; t++, slot++) {
+      while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
+      unsigned ex = exp_field(x[start + t]);
+      unsigned code = code_of(ex, e->e0);
+      for (int b = 0; b < 3; b++)
+        if ((code >> b) & 1u) out[plane_pos[b] + slot / 8] |= (uint8_t)(1u << (slot % 8));
+      if (code == 0) out[esc_pos + nesc++] = (uint8_t)ex;
+    }
+  } else {
+    for (uint64_t j = 0; j < nb; j++) {
+      if (!e->changed[start / B + j]) continue;
+      for (uint64_t s = 0; s < B; s++, slot++) {
+        uint64_t t = j * B + s;
+        if (t >= nc) continue; /* slot past the end of the data: stays 0 */
+        while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
+        unsigned ex = exp_field(x[start + t]);
+        unsigned code = code_of(ex, e->e0);
+        for (int b = 0; b < 3; b++)
+          if ((code >> b) & 1u) out[plane_pos[b] + slot / 8] |= (uint8_t)(1u << (slot % 8));
+        if (code == 0) out[esc_pos + nesc++] = (uint8_t)ex;
+      }
+    }
+  }
+  while (next_q < 4u) quarter_esc[next_q++] = nesc;
+  for (unsigned q = 0; q < 4u; q++)
+    put_u16(out + index_pos(e->nchunks) + 8ull * c + 2ull * q, (unsigned)quarter_esc[q]);
+  *nch_out = nch;
+  *nesc_out = nesc;
+  return esc_pos + pad128(nesc);
+}
+
+static void write_header(uint8_t* out, int ciera, unsigned e0, uint64_t n, uint32_t B, uint64_t nchunks,
+                         uint64_t total, uint64_t changed, uint64_t esc) {
+  put_u64(out + ORC_HEADER + 8ull * nchunks, total);
+  memcpy(out, ciera ? "CIER" : "ZIP3", 4);
+  put_u16(out + 4, 1);
+  out[6] = (uint8_t)(ciera ? 1 : 0);
+  out[7] = (uint8_t)e0;
+  put_u64(out + 8, n);
+  put_u32(out + 16, B);
+  put_u32(out + 20, (uint32_t)ORC_CHUNK);
+  put_u64(out + 24, nchunks);
+  put_u64(out + 32, total);
+  put_u64(out + 40, changed);
+  put_u64(out + 48, esc);
+}
+
+static int check_encode_args(const uint16_t* x, uint64_t n, uint32_t B, const uint8_t* cache, int e0_override,
+                             const uint8_t* out, uint64_t capacity) {
+  if (n > ORC_MAX_N) return ORC_ERR_ARG;
+  if (B != 0 && !valid_block_size(B)) return ORC_ERR_ARG;
+  if (B != 0 && n > 0 && cache == NULL) return ORC_ERR_ARG;
+  if (n > 0 && x == NULL) return ORC_ERR_ARG;
+  if (e0_override < -1 || e0_override > 249) return ORC_ERR_ARG;
+  if (out == NULL || capacity < orc_max_encoded_size(n, B)) return ORC_ERR_CAPACITY;
+  return ORC_OK;
+}
+
 /* Encode.  B = 0: zip3 mode (every value coded, cache unused and may be
  * NULL).  B != 0: ciera mode; cache holds n exponent bytes from the previous
  * iteration (all zero before the first) and is overwritten with x's
@@ -297,107 +564,33 @@ uint64_t orc_max_encoded_size(uint64_t n, uint32_t B) {
 int orc_encode(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, int e0_override,
                uint8_t* out, uint64_t capacity, uint64_t* out_size, uint64_t* stats) {
   const int ciera = (B != 0);
-  if (n > ORC_MAX_N) return ORC_ERR_ARG;
-  if (ciera && !valid_block_size(B)) return ORC_ERR_ARG;
-  if (ciera && n > 0 && cache == NULL) return ORC_ERR_ARG;
-  if (n > 0 && x == NULL) return ORC_ERR_ARG;
-  if (e0_override < -1 || e0_override > 249) return ORC_ERR_ARG;
-  const uint64_t need = orc_max_encoded_size(n, B);
-  if (out == NULL || capacity < need) return ORC_ERR_CAPACITY;
-  memset(out, 0, need);
+  int st = check_encode_args(x, n, B, cache, e0_override, out, capacity);
+  if (st != ORC_OK) return st;
+  memset(out, 0, orc_max_encoded_size(n, B));
 
   const unsigned e0 = (e0_override >= 0) ? (unsigned)e0_override : (unsigned)orc_choose_e0(x, n);
   const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
 
   /* Block change flags against the sender cache. */
   uint8_t* changed = NULL;
-  uint64_t nblocks = 0;
   if (ciera) {
-    nblocks = ceil_div(n, B);
-    changed = (uint8_t*)calloc(nblocks ? nblocks : 1, 1);
+    changed = (uint8_t*)calloc(ceil_div(n, B) + 1u, 1);
     if (!changed) return ORC_ERR_NOMEM;
     for (uint64_t i = 0; i < n; i++) {
       if (exp_field(x[i]) != cache[i]) changed[i / B] = 1;
     }
   }
 
+  const orc_enc e = {x, n, B, changed, e0, nchunks, out};
   uint64_t pos = payload_pos(nchunks);
   uint64_t total_changed = 0, total_esc = 0;
   for (uint64_t c = 0; c < nchunks; c++) {
-    const uint64_t start = c * ORC_CHUNK;
-    const uint64_t nc = (n - start < ORC_CHUNK) ? n - start : ORC_CHUNK;
-    put_u64(out + ORC_HEADER + 8ull * c, pos);
-    /* escape index: escapes among the chunk's values before quarter q */
-    uint64_t quarter_esc[4] = {0, 0, 0, 0};
-    unsigned next_q = 1;
-
-    /* 1. sign+mantissa bytes of every value */
-    for (uint64_t t = 0; t < nc; t++) out[pos + t] = (uint8_t)sm_field(x[start + t]);
-    pos += pad128(nc);
-
-    /* 2. bitmap of changed blocks */
-    uint64_t nch = 0, nb = 0;
-    if (ciera) {
-      nb = ceil_div(nc, B);
-      for (uint64_t j = 0; j < nb; j++) {
-        if (changed[start / B + j]) {
-          out[pos + j / 8] |= (uint8_t)(1u << (j % 8));
-          nch++;
-        }
-      }
-      pos += pad128(ceil_div(nb, 8));
-    }
-
-    /* 3./4. code planes and escapes, slot by slot */
-    const uint64_t plane_bytes = ciera ? nch * B / 8 : ceil_div(nc, 8);
-    const uint64_t plane_pos[3] = {pos, pos + pad128(plane_bytes), pos + 2 * pad128(plane_bytes)};
-    const uint64_t esc_pos = pos + 3 * pad128(plane_bytes);
-    uint64_t nesc = 0;
-    uint64_t slot = 0;
-    if (!ciera) {
-      for (uint64_t t = 0; t < nc; t++, slot++) {
-        while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
-        unsigned e = exp_field(x[start + t]);
-        unsigned code = code_of(e, e0);
-        for (int b = 0; b < 3; b++)
-          if ((code >> b) & 1u) out[plane_pos[b] + slot / 8] |= (uint8_t)(1u << (slot % 8));
-        if (code == 0) out[esc_pos + nesc++] = (uint8_t)e;
-      }
-    } else {
-      for (uint64_t j = 0; j < nb; j++) {
-        if (!changed[start / B + j]) continue;
-        for (uint64_t s = 0; s < B; s++, slot++) {
-          uint64_t t = j * B + s;
-          if (t >= nc) continue; /* slot past the end of the data: stays 0 */
-          while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
-          unsigned e = exp_field(x[start + t]);
-          unsigned code = code_of(e, e0);
-          for (int b = 0; b < 3; b++)
-            if ((code >> b) & 1u) out[plane_pos[b] + slot / 8] |= (uint8_t)(1u << (slot % 8));
-          if (code == 0) out[esc_pos + nesc++] = (uint8_t)e;
-        }
-      }
-    }
-    while (next_q < 4u) quarter_esc[next_q++] = nesc;
-    for (unsigned q = 0; q < 4u; q++)
-      put_u16(out + index_pos(nchunks) + 8ull * c + 2ull * q, (unsigned)quarter_esc[q]);
-    pos = esc_pos + pad128(nesc);
+    uint64_t nch, nesc;
+    pos = encode_chunk(&e, c, pos, &nch, &nesc);
     total_changed += nch;
     total_esc += nesc;
   }
-  put_u64(out + ORC_HEADER + 8ull * nchunks, pos);
-
-  memcpy(out, ciera ? "CIER" : "ZIP3", 4);
-  put_u16(out + 4, 1);
-  out[6] = (uint8_t)(ciera ? 1 : 0);
-  out[7] = (uint8_t)e0;
-  put_u64(out + 8, n);
-  put_u32(out + 16, B);
-  put_u32(out + 20, (uint32_t)ORC_CHUNK);
-  put_u64(out + 24, nchunks);
-  put_u64(out + 32, pos);
-  put_u64(out + 40, total_changed);
-  put_u64(out + 48, total_esc);
+  write_header(out, ciera, e0, n, B, nchunks, pos, total_changed, total_esc);
 
   if (ciera) {
     for (uint64_t i = 0; i < n; i++) cache[i] = (uint8_t)exp_field(x[i]);
@@ -412,18 +605,13 @@ int orc_encode(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, int e0
   return ORC_OK;
 }
 
-/* Decode.  B = 0 expects a zip3 stream; B != 0 a ciera stream with that B,
- * and cache holds the receiver's exponents of the previous iteration (updated
- * in place).  Every header field, table entry and section size is checked
- * against the layout above; any mismatch returns ORC_ERR_FORMAT. */
-int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uint32_t B,
-               uint8_t* cache) {
-  const int ciera = (B != 0);
-  if (n > ORC_MAX_N) return ORC_ERR_ARG;
-  if (ciera && !valid_block_size(B)) return ORC_ERR_ARG;
-  if (n > 0 && (y == NULL || (ciera && cache == NULL))) return ORC_ERR_ARG;
-  if (in == NULL || in_size < ORC_HEADER) return ORC_ERR_FORMAT;
+/* ---- 3-bit decode ------------------------------------------------------- */
 
+/* Checks the header and the table's first and last entries. */
+static int check_stream_header(const uint8_t* in, uint64_t in_size, uint64_t n, uint32_t B, unsigned* e0_out,
+                               uint64_t* total_out) {
+  const int ciera = (B != 0);
+  if (in == NULL || in_size < ORC_HEADER) return ORC_ERR_FORMAT;
   const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
   const uint64_t base = payload_pos(nchunks);
   if (memcmp(in, ciera ? "CIER" : "ZIP3", 4) != 0) return ORC_ERR_FORMAT;
@@ -443,84 +631,404 @@ int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uin
   if (get_u64(in + ORC_HEADER + 8ull * nchunks) != total) return ORC_ERR_FORMAT;
   for (uint64_t i = index_pos(nchunks) + 8ull * nchunks; i < base; i++)
     if (in[i] != 0) return ORC_ERR_FORMAT;
+  *e0_out = e0;
+  *total_out = total;
+  return ORC_OK;
+}
 
-  uint64_t total_changed = 0, total_esc = 0;
-  for (uint64_t c = 0; c < nchunks; c++) {
-    const uint64_t start = c * ORC_CHUNK;
-    const uint64_t nc = (n - start < ORC_CHUNK) ? n - start : ORC_CHUNK;
-    const uint64_t begin = get_u64(in + ORC_HEADER + 8ull * c);
-    const uint64_t end = get_u64(in + ORC_HEADER + 8ull * (c + 1));
-    if (begin > end || end > total) return ORC_ERR_FORMAT;
+/* Decodes chunk c of a stream whose header passed check_stream_header:
+ * writes its values to y (and, ciera, the changed blocks' exponents to
+ * cache) and returns ORC_OK with its changed blocks and escapes, or
+ * ORC_ERR_FORMAT when its sections or escape-index entry do not match. */
+static int decode_chunk(const uint8_t* in, uint64_t n, uint32_t B, unsigned e0, uint64_t total, uint64_t c,
+                        uint16_t* y, uint8_t* cache, uint64_t* nch_out, uint64_t* nesc_out) {
+  const int ciera = (B != 0);
+  const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+  const uint64_t start = c * ORC_CHUNK;
+  const uint64_t nc = chunk_len(n, c);
+  const uint64_t begin = get_u64(in + ORC_HEADER + 8ull * c);
+  const uint64_t end = get_u64(in + ORC_HEADER + 8ull * (c + 1));
+  if (begin > end || end > total) return ORC_ERR_FORMAT;
 
-    uint64_t pos = begin;
-    const uint64_t sm_pos = pos;
-    pos += pad128(nc);
-    uint64_t bitmap_pos = 0, nb = 0, nch = 0;
-    if (ciera) {
-      nb = ceil_div(nc, B);
-      bitmap_pos = pos;
-      pos += pad128(ceil_div(nb, 8));
-      if (pos > end) return ORC_ERR_FORMAT;
-      for (uint64_t j = 0; j < nb; j++) nch += (in[bitmap_pos + j / 8] >> (j % 8)) & 1u;
+  uint64_t pos = begin;
+  const uint64_t sm_pos = pos;
+  pos += pad128(nc);
+  uint64_t bitmap_pos = 0, nb = 0, nch = 0;
+  if (ciera) {
+    nb = ceil_div(nc, B);
+    bitmap_pos = pos;
+    pos += pad128(ceil_div(nb, 8));
+    if (pos > end) return ORC_ERR_FORMAT;
+    for (uint64_t j = 0; j < nb; j++) nch += (in[bitmap_pos + j / 8] >> (j % 8)) & 1u;
+  }
+  const uint64_t plane_bytes = ciera ? nch * B / 8 : ceil_div(nc, 8);
+  const uint64_t plane_pos[3] = {pos, pos + pad128(plane_bytes), pos + 2 * pad128(plane_bytes)};
+  const uint64_t esc_pos = pos + 3 * pad128(plane_bytes);
+  if (esc_pos > end) return ORC_ERR_FORMAT;
+
+  uint64_t nesc = 0;
+  uint64_t quarter_esc[4] = {0, 0, 0, 0};
+  unsigned next_q = 1;
+  if (!ciera) {
+    for (uint64_t t = 0; t < nc; t++) {
+      while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
+      unsigned code = 0, e;
+      for (int b = 0; b < 3; b++) code |= ((in[plane_pos[b] + t / 8] >> (t % 8)) & 1u) << b;
+      if (code != 0) {
+        e = e0 + code - 1u;
+      } else {
+        if (esc_pos + nesc >= end) return ORC_ERR_FORMAT;
+        e = in[esc_pos + nesc++];
+      }
+      y[start + t] = join_fields(in[sm_pos + t], e);
     }
-    const uint64_t plane_bytes = ciera ? nch * B / 8 : ceil_div(nc, 8);
-    const uint64_t plane_pos[3] = {pos, pos + pad128(plane_bytes), pos + 2 * pad128(plane_bytes)};
-    const uint64_t esc_pos = pos + 3 * pad128(plane_bytes);
-    if (esc_pos > end) return ORC_ERR_FORMAT;
-
-    uint64_t nesc = 0;
-    uint64_t quarter_esc[4] = {0, 0, 0, 0};
-    unsigned next_q = 1;
-    if (!ciera) {
-      for (uint64_t t = 0; t < nc; t++) {
+  } else {
+    uint64_t rank = 0; /* changed blocks of this chunk seen so far */
+    for (uint64_t j = 0; j < nb; j++) {
+      const int is_changed = (in[bitmap_pos + j / 8] >> (j % 8)) & 1u;
+      for (uint64_t s = 0; s < B && j * B + s < nc; s++) {
+        const uint64_t t = j * B + s;
         while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
-        unsigned code = 0, e;
-        for (int b = 0; b < 3; b++) code |= ((in[plane_pos[b] + t / 8] >> (t % 8)) & 1u) << b;
-        if (code != 0) {
-          e = e0 + code - 1u;
+        unsigned e;
+        if (!is_changed) {
+          e = cache[start + t];
         } else {
-          if (esc_pos + nesc >= end) return ORC_ERR_FORMAT;
-          e = in[esc_pos + nesc++];
+          const uint64_t slot = rank * B + s;
+          unsigned code = 0;
+          for (int b = 0; b < 3; b++)
+            code |= ((in[plane_pos[b] + slot / 8] >> (slot % 8)) & 1u) << b;
+          if (code != 0) {
+            e = e0 + code - 1u;
+          } else {
+            if (esc_pos + nesc >= end) return ORC_ERR_FORMAT;
+            e = in[esc_pos + nesc++];
+          }
+          cache[start + t] = (uint8_t)e;
         }
         y[start + t] = join_fields(in[sm_pos + t], e);
       }
-    } else {
-      uint64_t rank = 0; /* changed blocks of this chunk seen so far */
-      for (uint64_t j = 0; j < nb; j++) {
-        const int is_changed = (in[bitmap_pos + j / 8] >> (j % 8)) & 1u;
-        for (uint64_t s = 0; s < B && j * B + s < nc; s++) {
-          const uint64_t t = j * B + s;
-          while (next_q < 4u && t >= next_q * ORC_QUARTER) quarter_esc[next_q++] = nesc;
-          unsigned e;
-          if (!is_changed) {
-            e = cache[start + t];
-          } else {
-            const uint64_t slot = rank * B + s;
-            unsigned code = 0;
-            for (int b = 0; b < 3; b++)
-              code |= ((in[plane_pos[b] + slot / 8] >> (slot % 8)) & 1u) << b;
-            if (code != 0) {
-              e = e0 + code - 1u;
-            } else {
-              if (esc_pos + nesc >= end) return ORC_ERR_FORMAT;
-              e = in[esc_pos + nesc++];
-            }
-            cache[start + t] = (uint8_t)e;
-          }
-          y[start + t] = join_fields(in[sm_pos + t], e);
-        }
-        if (is_changed) rank++;
-      }
+      if (is_changed) rank++;
     }
-    if (esc_pos + pad128(nesc) != end) return ORC_ERR_FORMAT;
-    while (next_q < 4u) quarter_esc[next_q++] = nesc;
-    for (unsigned q = 0; q < 4u; q++)
-      if (get_u16(in + index_pos(nchunks) + 8ull * c + 2ull * q) != quarter_esc[q]) return ORC_ERR_FORMAT;
+  }
+  if (esc_pos + pad128(nesc) != end) return ORC_ERR_FORMAT;
+  while (next_q < 4u) quarter_esc[next_q++] = nesc;
+  for (unsigned q = 0; q < 4u; q++)
+    if (get_u16(in + index_pos(nchunks) + 8ull * c + 2ull * q) != quarter_esc[q]) return ORC_ERR_FORMAT;
+  *nch_out = nch;
+  *nesc_out = nesc;
+  return ORC_OK;
+}
+
+static int check_decode_args(uint64_t n, uint32_t B, const uint16_t* y, const uint8_t* cache) {
+  if (n > ORC_MAX_N) return ORC_ERR_ARG;
+  if (B != 0 && !valid_block_size(B)) return ORC_ERR_ARG;
+  if (n > 0 && (y == NULL || (B != 0 && cache == NULL))) return ORC_ERR_ARG;
+  return ORC_OK;
+}
+
+/* Decode.  B = 0 expects a zip3 stream; B != 0 a ciera stream with that B,
+ * and cache holds the receiver's exponents of the previous iteration (updated
+ * in place).  Every header field, table entry and section size is checked
+ * against the layout above; any mismatch returns ORC_ERR_FORMAT.  in_size
+ * may exceed the stream's total_bytes (the rest is not read). */
+int orc_decode(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uint32_t B,
+               uint8_t* cache) {
+  int st = check_decode_args(n, B, y, cache);
+  if (st != ORC_OK) return st;
+  unsigned e0;
+  uint64_t total;
+  st = check_stream_header(in, in_size, n, B, &e0, &total);
+  if (st != ORC_OK) return st;
+  const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+  uint64_t total_changed = 0, total_esc = 0;
+  for (uint64_t c = 0; c < nchunks; c++) {
+    uint64_t nch, nesc;
+    st = decode_chunk(in, n, B, e0, total, c, y, cache, &nch, &nesc);
+    if (st != ORC_OK) return st;
     total_changed += nch;
     total_esc += nesc;
   }
   if (get_u64(in + 40) != total_changed || get_u64(in + 48) != total_esc) return ORC_ERR_FORMAT;
   return ORC_OK;
+}
+
+/* ---- chunk-parallel drivers --------------------------------------------- */
+
+#define ORC_MAX_THREADS 256
+
+typedef void (*orc_range_fn)(void* arg, int job, uint64_t begin, uint64_t end);
+typedef struct {
+  orc_range_fn fn;
+  void* arg;
+  int job;
+  uint64_t begin, end;
+} orc_job;
+
+static void* job_main(void* p) {
+  orc_job* j = (orc_job*)p;
+  j->fn(j->arg, j->job, j->begin, j->end);
+  return NULL;
+}
+
+/* Runs fn over [0, count) split into `jobs` contiguous ranges, one thread
+ * each (a thread that cannot be created runs its range on the caller). */
+static void parallel_for(int jobs, uint64_t count, orc_range_fn fn, void* arg) {
+  pthread_t th[ORC_MAX_THREADS];
+  orc_job job[ORC_MAX_THREADS];
+  int started[ORC_MAX_THREADS];
+  for (int t = 0; t < jobs; t++) {
+    job[t].fn = fn;
+    job[t].arg = arg;
+    job[t].job = t;
+    job[t].begin = count * (uint64_t)t / (uint64_t)jobs;
+    job[t].end = count * (uint64_t)(t + 1) / (uint64_t)jobs;
+    started[t] = (t > 0) && pthread_create(&th[t], NULL, job_main, &job[t]) == 0;
+  }
+  for (int t = 0; t < jobs; t++)
+    if (!started[t]) job_main(&job[t]);
+  for (int t = 1; t < jobs; t++)
+    if (started[t]) pthread_join(th[t], NULL);
+}
+
+static int clamp_threads(int nthreads) {
+  if (nthreads < 1) return 1;
+  return nthreads > ORC_MAX_THREADS ? ORC_MAX_THREADS : nthreads;
+}
+
+typedef struct {
+  const uint16_t* x;
+  uint64_t n;
+  uint32_t B;
+  uint8_t* cache;
+  uint8_t* changed;
+  uint8_t* out;
+  orc_enc enc;
+  int64_t (*a)[256];
+  uint64_t (*b)[256];
+  uint64_t* nf;
+  uint64_t* nch;  /* per chunk */
+  uint64_t* nesc; /* per chunk */
+  uint64_t* off;  /* per chunk + 1 */
+  int bad;        /* a chunk's writer ended off its closed-form size */
+} orc_mt;
+
+static void mt_zero(void* p, int job, uint64_t begin, uint64_t end) {
+  (void)job;
+  memset(((orc_mt*)p)->out + begin, 0, end - begin);
+}
+
+static void mt_sums(void* p, int job, uint64_t begin, uint64_t end) {
+  orc_mt* m = (orc_mt*)p;
+  orc_exponent_sums(m->x + begin, end - begin, m->a[job], m->b[job], &m->nf[job]);
+}
+
+static void mt_changed(void* p, int job, uint64_t begin, uint64_t end) {
+  (void)job;
+  orc_mt* m = (orc_mt*)p;
+  for (uint64_t blk = begin; blk < end; blk++) {
+    const uint64_t i_end = (blk + 1) * m->B < m->n ? (blk + 1) * m->B : m->n;
+    for (uint64_t i = blk * m->B; i < i_end; i++)
+      if (exp_field(m->x[i]) != m->cache[i]) {
+        m->changed[blk] = 1;
+        break;
+      }
+  }
+}
+
+/* Changed blocks and escapes of each chunk, counted value by value. */
+static void mt_counts(void* p, int job, uint64_t begin, uint64_t end) {
+  (void)job;
+  orc_mt* m = (orc_mt*)p;
+  for (uint64_t c = begin; c < end; c++) {
+    const uint64_t start = c * ORC_CHUNK, nc = chunk_len(m->n, c);
+    uint64_t nch = 0, nesc = 0;
+    if (m->B)
+      for (uint64_t j = 0; j < ceil_div(nc, m->B); j++) nch += m->changed[start / m->B + j];
+    for (uint64_t t = 0; t < nc; t++) {
+      const int coded = (m->B == 0) || m->changed[(start + t) / m->B];
+      if (coded && code_of(exp_field(m->x[start + t]), m->enc.e0) == 0) nesc++;
+    }
+    m->nch[c] = nch;
+    m->nesc[c] = nesc;
+  }
+}
+
+static void mt_write(void* p, int job, uint64_t begin, uint64_t end) {
+  (void)job;
+  orc_mt* m = (orc_mt*)p;
+  for (uint64_t c = begin; c < end; c++) {
+    uint64_t nch, nesc;
+    const uint64_t after = encode_chunk(&m->enc, c, m->off[c], &nch, &nesc);
+    if (after != m->off[c + 1] || nch != m->nch[c] || nesc != m->nesc[c]) m->bad = 1;
+  }
+}
+
+static void mt_cache(void* p, int job, uint64_t begin, uint64_t end) {
+  (void)job;
+  orc_mt* m = (orc_mt*)p;
+  for (uint64_t i = begin; i < end; i++) m->cache[i] = (uint8_t)exp_field(m->x[i]);
+}
+
+/* Stream bytes of a chunk of nc values with nch changed blocks (ciera) and
+ * nesc escapes: the sections' padded sizes added up. */
+static uint64_t chunk_bytes(uint64_t nc, uint32_t B, uint64_t nch, uint64_t nesc) {
+  uint64_t s = pad128(nc), plane;
+  if (B != 0) {
+    s += pad128(ceil_div(ceil_div(nc, B), 8));
+    plane = nch * B / 8;
+  } else {
+    plane = ceil_div(nc, 8);
+  }
+  return s + 3ull * pad128(plane) + pad128(nesc);
+}
+
+/* orc_encode on nthreads threads: the same window (exact integer sums added
+ * across threads), change flags, per-chunk writer and header, so the stream
+ * and the cache are byte-equal to orc_encode's.  Chunk offsets come from the
+ * chunks' counts through chunk_bytes; a chunk whose writer ends elsewhere
+ * makes the call fail with ORC_ERR_INTERNAL. */
+#define ORC_ERR_INTERNAL 7
+int orc_encode_mt(const uint16_t* x, uint64_t n, uint32_t B, uint8_t* cache, int e0_override, uint8_t* out,
+                  uint64_t capacity, uint64_t* out_size, uint64_t* stats, int nthreads) {
+  const int ciera = (B != 0);
+  int st = check_encode_args(x, n, B, cache, e0_override, out, capacity);
+  if (st != ORC_OK) return st;
+  const int T = clamp_threads(nthreads);
+  const uint64_t nchunks = ceil_div(n, ORC_CHUNK);
+  orc_mt m;
+  memset(&m, 0, sizeof(m));
+  m.x = x;
+  m.n = n;
+  m.B = B;
+  m.cache = cache;
+  m.out = out;
+  m.a = (int64_t(*)[256])calloc((size_t)T, sizeof(*m.a));
+  m.b = (uint64_t(*)[256])calloc((size_t)T, sizeof(*m.b));
+  m.nf = (uint64_t*)calloc((size_t)T, sizeof(uint64_t));
+  m.nch = (uint64_t*)calloc(nchunks + 1u, sizeof(uint64_t));
+  m.nesc = (uint64_t*)calloc(nchunks + 1u, sizeof(uint64_t));
+  m.off = (uint64_t*)calloc(nchunks + 1u, sizeof(uint64_t));
+  m.changed = ciera ? (uint8_t*)calloc(ceil_div(n, B) + 1u, 1) : NULL;
+  if (!m.a || !m.b || !m.nf || !m.nch || !m.nesc || !m.off || (ciera && !m.changed)) {
+    st = ORC_ERR_NOMEM;
+    goto done;
+  }
+  parallel_for(T, orc_max_encoded_size(n, B), mt_zero, &m);
+
+  unsigned e0;
+  if (e0_override >= 0) {
+    e0 = (unsigned)e0_override;
+  } else {
+    parallel_for(T, n, mt_sums, &m);
+    int64_t a[256] = {0};
+    uint64_t b[256] = {0}, nf = 0;
+    for (int t = 0; t < T; t++) {
+      for (unsigned k = 0; k < 256u; k++) {
+        a[k] += m.a[t][k];
+        b[k] += m.b[t][k];
+      }
+      nf += m.nf[t];
+    }
+    e0 = (unsigned)orc_window_base_exact(a, b, nf);
+  }
+  if (ciera) parallel_for(T, ceil_div(n, B), mt_changed, &m);
+  const orc_enc e = {x, n, B, m.changed, e0, nchunks, out};
+  m.enc = e;
+  parallel_for(T, nchunks, mt_counts, &m);
+  uint64_t total_changed = 0, total_esc = 0;
+  m.off[0] = payload_pos(nchunks);
+  for (uint64_t c = 0; c < nchunks; c++) {
+    m.off[c + 1] = m.off[c] + chunk_bytes(chunk_len(n, c), B, m.nch[c], m.nesc[c]);
+    total_changed += m.nch[c];
+    total_esc += m.nesc[c];
+  }
+  parallel_for(T, nchunks, mt_write, &m);
+  if (m.bad) {
+    st = ORC_ERR_INTERNAL;
+    goto done;
+  }
+  write_header(out, ciera, e0, n, B, nchunks, m.off[nchunks], total_changed, total_esc);
+  if (ciera) parallel_for(T, n, mt_cache, &m);
+  *out_size = m.off[nchunks];
+  if (stats) {
+    stats[0] = e0;
+    stats[1] = total_changed;
+    stats[2] = total_esc;
+  }
+done:
+  free(m.a);
+  free(m.b);
+  free(m.nf);
+  free(m.nch);
+  free(m.nesc);
+  free(m.off);
+  free(m.changed);
+  return st;
+}
+
+typedef struct {
+  const uint8_t* in;
+  uint64_t n;
+  uint32_t B;
+  unsigned e0;
+  uint64_t total;
+  uint16_t* y;
+  uint8_t* cache;
+  int* status;    /* per job */
+  uint64_t* nch;  /* per job */
+  uint64_t* nesc; /* per job */
+} orc_mt_dec;
+
+static void mt_decode(void* p, int job, uint64_t begin, uint64_t end) {
+  orc_mt_dec* d = (orc_mt_dec*)p;
+  uint64_t nch_sum = 0, nesc_sum = 0;
+  int st = ORC_OK;
+  for (uint64_t c = begin; c < end && st == ORC_OK; c++) {
+    uint64_t nch, nesc;
+    st = decode_chunk(d->in, d->n, d->B, d->e0, d->total, c, d->y, d->cache, &nch, &nesc);
+    nch_sum += nch;
+    nesc_sum += nesc;
+  }
+  d->status[job] = st;
+  d->nch[job] = nch_sum;
+  d->nesc[job] = nesc_sum;
+}
+
+/* orc_decode on nthreads threads (chunks are decoded by the same per-chunk
+ * step; the same checks, the same result). */
+int orc_decode_mt(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n, uint32_t B, uint8_t* cache,
+                  int nthreads) {
+  int st = check_decode_args(n, B, y, cache);
+  if (st != ORC_OK) return st;
+  orc_mt_dec d;
+  memset(&d, 0, sizeof(d));
+  st = check_stream_header(in, in_size, n, B, &d.e0, &d.total);
+  if (st != ORC_OK) return st;
+  const int T = clamp_threads(nthreads);
+  d.in = in;
+  d.n = n;
+  d.B = B;
+  d.y = y;
+  d.cache = cache;
+  d.status = (int*)calloc((size_t)T, sizeof(int));
+  d.nch = (uint64_t*)calloc((size_t)T, sizeof(uint64_t));
+  d.nesc = (uint64_t*)calloc((size_t)T, sizeof(uint64_t));
+  if (!d.status || !d.nch || !d.nesc) {
+    st = ORC_ERR_NOMEM;
+  } else {
+    parallel_for(T, ceil_div(n, ORC_CHUNK), mt_decode, &d);
+    uint64_t total_changed = 0, total_esc = 0;
+    for (int t = 0; t < T; t++) {
+      if (d.status[t] != ORC_OK) st = d.status[t];
+      total_changed += d.nch[t];
+      total_esc += d.nesc[t];
+    }
+    if (st == ORC_OK && (get_u64(in + 40) != total_changed || get_u64(in + 48) != total_esc)) st = ORC_ERR_FORMAT;
+  }
+  free(d.status);
+  free(d.nch);
+  free(d.nesc);
+  return st;
 }
 
 /* ------------------------------------------------------------------------
@@ -865,18 +1373,19 @@ int orc_decode_rans(const uint8_t* in, uint64_t in_size, uint16_t* y, uint64_t n
   if (in_size < pay_pos) return ORC_ERR_FORMAT;
   if (memcmp(in, ciera ? "CIER" : "ZIP3", 4) != 0 || get_u16(in + 4) != ORC_RANS_VERSION ||
       in[6] != (ciera ? 3 : 2) || in[7] != 0 || get_u64(in + 8) != n || get_u32(in + 16) != B ||
-      get_u32(in + 20) != ORC_CHUNK || get_u64(in + 24) != nchunks || get_u64(in + 32) != in_size)
+      get_u32(in + 20) != ORC_CHUNK || get_u64(in + 24) != nchunks || get_u64(in + 32) > in_size)
     return ORC_ERR_FORMAT;
+  const uint64_t total = get_u64(in + 32); /* in_size may exceed it: the rest is not read */
   for (unsigned k = 56; k < ORC_HEADER; k++)
     if (in[k]) return ORC_ERR_FORMAT;
-  if (get_u64(in + ORC_HEADER) != pay_pos || get_u64(in + ORC_HEADER + 8 * nchunks) != in_size)
+  if (get_u64(in + ORC_HEADER) != pay_pos || get_u64(in + ORC_HEADER + 8 * nchunks) != total)
     return ORC_ERR_FORMAT;
   uint8_t* sym = (uint8_t*)malloc(ORC_CHUNK);
   uint64_t n_changed = 0, n_coded = 0;
   int st = ORC_OK;
   for (uint64_t c = 0; c < nchunks && st == ORC_OK; c++) {
     uint64_t a = get_u64(in + ORC_HEADER + 8 * c), b = get_u64(in + ORC_HEADER + 8 * (c + 1));
-    if (b < a || b > in_size || (a & 127u) || (b & 127u)) {
+    if (b < a || b > total || (a & 127u) || (b & 127u)) {
       st = ORC_ERR_FORMAT;
       break;
     }

@@ -152,6 +152,59 @@ def closed_form_size(n: int, B: int, chunk_changed: list[int], chunk_escapes: li
     return size
 
 
+MASK64 = (1 << 64) - 1
+SM64_GAMMA = 0x9E3779B97F4A7C15
+# The block hash's two (seed, increment) pairs, as documented with the hash
+# sender's entry point: hash 0 is SplitMix64 itself, hash 1 its own pair.
+HASH_SEEDS = (0, 0x243F6A8885A308D3)
+HASH_GAMMAS = (SM64_GAMMA, 0xD1B54A32D192ED03)
+
+
+def splitmix64_mix(z: int) -> int:
+    """SplitMix64's output function (Steele, Lea and Flood, OOPSLA 2014, with
+    the finaliser constants of the published generator)."""
+    z &= MASK64
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & MASK64
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & MASK64
+    return z ^ (z >> 31)
+
+
+class SplitMix64:
+    """The generator itself: the state steps by an odd increment, each output
+    is the new state through the output function."""
+
+    def __init__(self, seed: int, gamma: int = SM64_GAMMA):
+        self.state = seed & MASK64
+        self.gamma = gamma
+
+    def next(self) -> int:
+        self.state = (self.state + self.gamma) & MASK64
+        return splitmix64_mix(self.state)
+
+
+def block_hashes(xs, B: int) -> list[tuple[int, int]]:
+    """The hash sender's two 64-bit hashes of every block of B values (CIERA
+    page, section 3.1: a 128-bit block hash from two independent 64-bit
+    SplitMix64 hashes).  The block's exponent fields, 8 at a time, form
+    little-endian words w_k (the last zero-filled); hash j adds, over the
+    nonzero words, the (k+1)-th output of a SplitMix64 generator seeded with
+    w_k + s_j and stepping by g_j, i.e. mix(w_k + s_j + (k+1) g_j)."""
+    e = [(int(v) >> 7) & 0xFF for v in xs]
+    out = []
+    for lo in range(0, len(e), B):
+        blk = e[lo:lo + B]
+        blk += [0] * ((-len(blk)) % 8)
+        h = [0, 0]
+        for k in range(len(blk) // 8):
+            w = sum(blk[8 * k + i] << (8 * i) for i in range(8))
+            if w == 0:
+                continue
+            for j in range(2):
+                h[j] = (h[j] + splitmix64_mix(w + HASH_SEEDS[j] + (k + 1) * HASH_GAMMAS[j])) & MASK64
+        out.append((h[0], h[1]))
+    return out
+
+
 def window_share(x: float, sigma: float) -> float:
     """P_win(x) = erf(2^(x+7) / (sigma sqrt 2)) - erf(2^x / (sigma sqrt 2))
     (ZipCCL digest, section 3.1)."""

@@ -101,21 +101,20 @@ def test_variance_matches_exact_rationals(seed):
     pos = rng.choice(n, size=min(k, n - 1), replace=False)
     specials = np.array([0x0000, 0x8000, 0x0001, 0x807F, 0x7F80, 0xFF80, 0x7FC1, 0xFF81], dtype=np.uint16)
     x[pos] = rng.choice(specials, size=pos.size)
+    # the oracle's statistic is exact: its integer sums per exponent give the
+    # same rational as the mean-subtracted sum of exact values
     var, nf = oracle.variance(x)
     ev, enf = brute.exact_variance(x)
-    assert nf == enf
-    if ev == 0:
-        assert var == 0.0
-    else:
-        assert abs(Fraction(var) - ev) <= ev * Fraction(1, 10 ** 10)
+    assert nf == enf and var == ev
+    assert oracle.choose_e0(x) == brute.e0_from_exact(ev, enf)
 
 
 def test_variance_subnormal_only_tensor():
     x = np.array([0x0001, 0x0002, 0x8003, 0x007F, 0x0000], dtype=np.uint16)
     var, nf = oracle.variance(x)
     ev, _ = brute.exact_variance(x)
-    # the sums are exact (tiny dyadics); only the final divisions round
-    assert nf == 5 and abs(Fraction(var) - ev) <= ev * Fraction(1, 10 ** 15)
+    assert nf == 5 and var == ev
+    assert oracle.choose_e0(x) == brute.e0_from_exact(ev, 5)
 
 
 def test_constant_and_nonfinite_tensors_choose_zero():

@@ -186,3 +186,17 @@ def test_decode_rejects_corruption():
     bad(lambda t: t.__setitem__(words + 3, t[words + 3] ^ 0x80))                # a final state
     bad(lambda t: t.__setitem__(136, t[136] ^ 0x40))          # chunk table entry
     bad(lambda t: t.__setitem__(4, 1))                        # version
+
+
+def test_decode_reads_only_the_stream_in_a_larger_buffer():
+    """in_size is the buffer's size, as for the 3-bit streams: bytes after
+    total_bytes are not read; a buffer shorter than total_bytes is rejected."""
+    rng = np.random.default_rng(8)
+    x = wl.normal_bf16(rng, 2 * C + 999, 0.02)
+    for B in (0, 256):
+        cache = wl.perturbed_cache(rng, x, 0.05) if B else None
+        s, _ = oracle.encode_rans(x, B, cache.copy() if B else None)
+        longer = np.concatenate([s, rng.integers(0, 256, 4096, dtype=np.uint8)])
+        assert np.array_equal(oracle.decode_rans(longer, x.size, B, cache.copy() if B else None), x)
+        with pytest.raises(oracle.OracleError):
+            oracle.decode_rans(s[:-128], x.size, B, cache.copy() if B else None)
