@@ -49,6 +49,18 @@
  *    (same stream, or synchronised); distinct workspaces may be used
  *    concurrently on different streams.
  *  - n <= 2^40.  n = 0 is valid.  B is a power of two, 64 <= B <= 65536.
+ *  - Within an encode, workgroups wait on each other only through bounded
+ *    waits on lower-numbered workgroups (which the GPU dispatches first), so
+ *    an encode completes while other kernels share the GPU.  A wait that
+ *    runs out of its bound (seconds of polling) makes ciera_read_error
+ *    report CIERA_ERR_INTERNAL.  The stream is then not valid and must not
+ *    be sent; the 3-bit encodes with a derived window (zip3_encode,
+ *    ciera_encode, ciera_encode_hashed, *_encode_ex) also set *d_out_size
+ *    to 0 and clear the header's first 8 bytes.  The sender's cache (or
+ *    hash cache) may then hold the new exponents (hashes) of some blocks
+ *    and the previous ones of others, so the caches of sender and receivers
+ *    are out of step: zero the sender's cache and every receiver's cache
+ *    before the next iteration (a full resend).
  */
 #ifndef CIERA_H
 #define CIERA_H
@@ -69,7 +81,7 @@ typedef int ciera_status;
 #define CIERA_ERR_WORKSPACE 3 /* ws_bytes below the *_workspace_size bound */
 #define CIERA_ERR_HIP 4       /* a HIP launch or runtime call failed */
 #define CIERA_ERR_FORMAT 5    /* decode: the stream is malformed or does not match n / B / mode */
-#define CIERA_ERR_INTERNAL 6  /* encode: a chunk-offset wait gave up (should not happen) */
+#define CIERA_ERR_INTERNAL 6  /* encode: a wait on another workgroup gave up (see below) */
 
 #define CIERA_CHUNK 65536u
 
@@ -181,7 +193,9 @@ uint64_t ciera_hash_cache_size(uint64_t n, uint32_t B);
  * Arguments, caches, ownership and errors as the 3-bit entry points; the
  * workspace is rans_workspace_size(n, B) bytes for encode (it holds a
  * payload scratch slot per chunk) and *_workspace_size(n) for decode; the
- * output capacity rans_max_encoded_size(n, B).  Encode's workgroups wait on
+ * output capacity rans_max_encoded_size(n, B).  As for the 3-bit streams,
+ * a decoder's in_size is the buffer's size: at least the stream's
+ * total_bytes, whose bytes alone are read.  Encode's workgroups wait on
  * earlier ones for their stream offsets (bounded waits, reported as
  * CIERA_ERR_INTERNAL).  Decode checks the header, the chunk table, every
  * payload's word counts, length and padding, that the frequencies sum to
@@ -223,7 +237,11 @@ ciera_status ciera_read_error(const void* d_ws, hipStream_t stream);
  *   d_e0  in  device pointer to one byte, the window base (0..249); read on
  *             the device when the encode runs, so it may be produced by
  *             earlier work on `stream`.  A value above 249 makes the call
- *             write nothing and ciera_read_error report CIERA_ERR_ARG.
+ *             write only the stream's first 8 bytes, whose E0 byte (byte 7)
+ *             keeps that value, so that a decoder rejects the stream and a
+ *             next encode that takes its window base from byte 7 is refused
+ *             too; *d_out_size becomes 0 and ciera_read_error reports
+ *             CIERA_ERR_ARG.
  * Other arguments, sizes and the workspace as zip3_encode, except that n is
  * limited to 2^39 (CIERA_ERR_ARG above); the stream equals zip3_encode_ex's
  * with e0_override = *d_e0.  Within the call, workgroups
@@ -242,9 +260,9 @@ ciera_status zip3_encode_e0(const void* d_x, uint64_t n, const uint8_t* d_e0, vo
  * previous iteration's stream header).  Arguments, caches, sizes and the
  * workspace as ciera_encode (workspace ciera_workspace_size(n, B)), except
  * that n is limited to 2^39 (CIERA_ERR_ARG above); the stream and the cache
- * equal ciera_encode_ex's with e0_override = *d_e0.  A *d_e0 above 249 makes
- * the call write nothing, leave the cache as it was and ciera_read_error
- * report CIERA_ERR_ARG.  Workgroups wait on each other through the
+ * equal ciera_encode_ex's with e0_override = *d_e0.  A *d_e0 above 249 leaves
+ * the cache as it was and the stream and *d_out_size as zip3_encode_e0 does
+ * (CIERA_ERR_ARG).  Workgroups wait on each other through the
  * workspace as in zip3_encode_e0. */
 ciera_status ciera_encode_e0(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, const uint8_t* d_e0,
                              void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
@@ -262,6 +280,13 @@ ciera_status ciera_encode_e0(const void* d_x, uint64_t n, uint32_t B, uint8_t* d
  * copied; a later call replaces the queue, n_pairs = 0 clears it.  Returns
  * CIERA_ERR_ARG for a null array or handle. */
 ciera_status ciera_time_kernels(void* const* events, uint32_t n_pairs);
+
+/* Test hook: the number of polls after which the next calls' waits on
+ * other workgroups give up (CIERA_ERR_INTERNAL); 0 restores the default
+ * (2^22).  Returns the previous value.  Tests lower it to drive the failure
+ * path from the host with every kernel still ending normally.  Applies to
+ * calls made after it, from any thread. */
+uint32_t ciera_set_wait_limit(uint32_t polls);
 
 /* Human-readable name of a status code (static storage). */
 const char* ciera_status_string(ciera_status status);

@@ -24,6 +24,7 @@ Same names as the C ABI::
     ciera_decode(inp, in_size, y, B, prev_exp, ws, stream=None)
     ciera_read_error(ws, stream=None)
     ciera_time_kernels(pairs)             (profiling: per-kernel start/stop events)
+    ciera_set_wait_limit(polls)           (test hook: bound of the waits between workgroups)
 
 ``x``/``y`` are CUDA(HIP) tensors of dtype bfloat16, int16 or uint16 holding
 the BF16 patterns; ``out``/``inp``/``ws``/``prev_exp`` are uint8 tensors and
@@ -41,7 +42,7 @@ __all__ = [
     "zip3_encode_e0", "ciera_encode_e0", "ciera_encode_hashed", "ciera_hash_cache_size",
     "rans_max_encoded_size", "rans_workspace_size", "zip3_encode_rans", "zip3_decode_rans", "ciera_encode_rans",
     "ciera_decode_rans",
-    "bind", "ciera_time_kernels",
+    "bind", "ciera_time_kernels", "ciera_set_wait_limit",
     "CHUNK",
 ]
 
@@ -52,6 +53,7 @@ _lib = None
 
 STATUS_NAMES = {0: "CIERA_OK", 1: "CIERA_ERR_ARG", 2: "CIERA_ERR_CAPACITY", 3: "CIERA_ERR_WORKSPACE",
                 4: "CIERA_ERR_HIP", 5: "CIERA_ERR_FORMAT", 6: "CIERA_ERR_INTERNAL"}
+STATUS_CODES = {name: code for code, name in STATUS_NAMES.items()}
 
 
 class CieraError(RuntimeError):
@@ -101,6 +103,7 @@ def load_library():
         f = getattr(lib, name)
         f.argtypes, f.restype = args, i32
     lib.ciera_status_string.argtypes, lib.ciera_status_string.restype = [i32], ctypes.c_char_p
+    lib.ciera_set_wait_limit.argtypes, lib.ciera_set_wait_limit.restype = [u32], u32
     _lib = lib
     return lib
 
@@ -355,3 +358,9 @@ def ciera_time_kernels(pairs, stream=None) -> None:
             handles.append(e.cuda_event)
     arr = (ctypes.c_void_p * len(handles))(*handles)
     _raise(load_library().ciera_time_kernels(arr, len(pairs)), "ciera_time_kernels")
+
+
+def ciera_set_wait_limit(polls: int) -> int:
+    """Test hook: polls after which the next calls' waits on other workgroups
+    give up (0 restores the default).  Returns the previous bound."""
+    return int(load_library().ciera_set_wait_limit(polls))

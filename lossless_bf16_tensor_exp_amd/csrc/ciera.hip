@@ -37,6 +37,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <vector>
 
 #include "ciera.h"
@@ -96,6 +97,10 @@ __host__ __device__ inline uint64_t chunk_max_bytes(uint64_t nc, uint32_t B) {
   return s;
 }
 
+// Every wait of one workgroup on another is bounded: it gives up after this
+// many polls (seconds of GPU time; it ends only a wait that would not end).
+constexpr uint32_t kSpinLimit = 1u << 22;
+
 // Workspace: control block, error words, per-part partial sums and bitmap
 // words, exponent histograms of the parts, per-part escape offsets
 // and per-chunk escape totals, and the look-back words of the single-read
@@ -119,21 +124,20 @@ struct Partial {
   uint32_t pad;
 };
 
-// k_plan runs as up to kPlanMaxGroups workgroups, each over a contiguous
-// range of chunks.  A group publishes its variance sums, then (once every
-// group's sums are in) its stream bytes, escapes and changed blocks, each in
-// a word of its slot that k_stats cleared to kSlotEmpty.
+// k_sums and k_plan run as up to kPlanMaxGroups workgroups, each over a
+// contiguous range of chunks.  k_sums stores each group's variance sums in
+// its slot; k_plan publishes each group's stream bytes, escapes and changed
+// blocks there, each in a word that k_stats cleared (not ready).
 constexpr uint32_t kPlanThreads = 256u;
 constexpr uint32_t kPlanWaves = kPlanThreads / 64u;
 constexpr uint32_t kPlanMaxGroups = kPlanThreads;  // one slot per thread in the waits
 constexpr uint32_t kPlanMinChunks = 16u;           // chunks per group, unless that needs too many groups
-constexpr uint64_t kSlotEmpty = ~0ull;             // a NaN: never the sum of finite values
 constexpr uint64_t kSlotReady = 1ull << 63;        // set in the count words
 
 struct PlanSlot {
-  uint64_t s1, s2;            // FP64 bit patterns of the group's variance sums
-  uint64_t nf;                // kSlotReady | finite values
-  uint64_t bytes, esc, nch;   // kSlotReady | the group's stream bytes, escapes, changed blocks
+  uint64_t s1, s2;            // FP64 bit patterns of the group's variance sums (k_sums)
+  uint64_t nf;                // finite values (k_sums)
+  uint64_t bytes, esc, nch;   // kSlotReady | the group's stream bytes, escapes, changed blocks (k_plan)
   uint64_t pad[2];
 };
 static_assert(sizeof(PlanSlot) == 64, "plan slot is 64 bytes");
@@ -193,7 +197,11 @@ struct Ws {
   uint64_t* rstat;
   uint64_t* rinfo;
   uint8_t* rslot;
+  uint32_t spin_limit;  // polls before a wait gives up (kSpinLimit unless a test lowers it)
 };
+
+// The bound the next calls pass to their kernels (ciera_set_wait_limit).
+std::atomic<uint32_t> g_wait_limit{kSpinLimit};
 
 __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   const WsLayout l = ws_layout(nchunks);
@@ -213,6 +221,7 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.rstat = nullptr;
   w.rinfo = nullptr;
   w.rslot = nullptr;
+  w.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
   return w;
 }
 
@@ -567,9 +576,9 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   if (tid < kPartBitmapWords) s_bits[tid] = 0u;
   if (ws.rstat && tid == 0 && h == 0u) ws.rstat[c * kRstatStride] = 0u;  // rANS encode: the chunk's look-back word, not ready
   if (blockIdx.x == 0u) {
-    // k_plan's slots: the FP64 words empty, the count words not ready
+    // k_plan's slots: the count words not ready
     uint64_t* sw = reinterpret_cast<uint64_t*>(ws.plan);
-    for (uint32_t i = tid; i < kPlanMaxGroups * 8u; i += kPartThreads) sw[i] = ((i & 7u) < 2u) ? kSlotEmpty : 0u;
+    for (uint32_t i = tid; i < kPlanMaxGroups * 8u; i += kPartThreads) sw[i] = 0u;
     if (tid == 0) ws.ctrl->plan_fail = 0u;
   }
   const uint32_t first = x[0];
@@ -913,8 +922,7 @@ __device__ inline ChunkGeom chunk_geom(uint64_t begin, uint32_t nc, bool ciera, 
 // Values passed between workgroups (k_plan's groups, the parts of the
 // single-read encode) each sit in one word that also says whether it is
 // there yet, so relaxed device-scope atomics suffice: no cache-wide
-// acquire/release.  Every wait is bounded.
-constexpr uint32_t kSpinLimit = 1u << 22;
+// acquire/release.  Every wait is bounded by Ws::spin_limit polls.
 __device__ inline uint64_t load_relaxed(const uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -931,10 +939,10 @@ __device__ inline void store_relaxed(uint32_t* p, uint32_t v) {
 // Waits until ready() holds in every thread of the workgroup; false if the
 // bound ran out first.
 template <typename F>
-__device__ inline bool wait_all(F ready) {
+__device__ inline bool wait_all(F ready, uint32_t limit) {
   for (uint32_t spins = 0;; spins++) {
     if (__syncthreads_and(ready())) return true;
-    if (spins >= kSpinLimit) return false;
+    if (spins >= limit) return false;
     __builtin_amdgcn_s_sleep(1);
   }
 }
@@ -970,21 +978,47 @@ __device__ inline double plan_sum_f64(double v, double* s_w) {
 // up to kRunRegs rounds (longer ones park them in the chunk table).
 constexpr uint32_t kRunRegs = 8u;
 
-// Up to kPlanMaxGroups workgroups plan the stream; group g takes chunks
-// [g per, (g + 1) per).  (1) Each group sums its parts' variance partials and
-// publishes them; once every group's sums are in, every group reduces them
-// in the same fixed order, so all pick the same E0.  (2) Each group sizes its
-// chunks: a part's escapes are its coded values minus those with exponent in
-// [E0, E0 + 6], read off its histogram row, so each chunk's size
-// is exact (the size exchange of the digest's Figure 1, done on one GPU).  A
-// group publishes its bytes, escapes and changed blocks and adds up those of
-// the groups before it for its base offset; the last group also has the
-// totals.  Group 0 writes the header's fixed fields, the last group the
-// totals and *out_size.  Every group is resident at once (at most
-// kPlanMaxGroups small workgroups), so the waits end; if one does not end in
-// its bound, the group sets ctrl->plan_fail and k_write writes nothing.
-// kHashBlocks: hash sender with blocks larger than a part, whose change
-// decision k_stats leaves to this kernel (hcache is then the hash cache).
+// The planner's groups: group g of G takes chunks [g per, (g + 1) per).
+// k_sums: each group adds up its parts' variance partials in a fixed order
+// and stores them in its slot.  Nothing waits; k_plan, the next launch,
+// reads every slot.
+__global__ __launch_bounds__(kPlanThreads) void k_sums(uint64_t nchunks, uint64_t per, Ws ws) {
+  __shared__ double s_f[kPlanWaves];
+  __shared__ uint64_t s_u[kPlanWaves];
+  const uint32_t tid = threadIdx.x, g = blockIdx.x;
+  const uint64_t c0 = min(nchunks, per * g), c1 = min(nchunks, c0 + per);
+  double a = 0.0, b = 0.0;
+  uint64_t m = 0;
+  for (uint64_t i = kParts * c0 + tid; i < kParts * c1; i += kPlanThreads) {
+    const Partial& p = ws.partial[i];
+    a += p.s1;
+    b += p.s2;
+    m += p.nf;
+  }
+  a = plan_sum_f64(a, s_f);
+  b = plan_sum_f64(b, s_f);
+  m = plan_sum_u64(m, s_u);
+  if (tid == 0) {
+    ws.plan[g].s1 = as_bits(a);
+    ws.plan[g].s2 = as_bits(b);
+    ws.plan[g].nf = m;
+  }
+}
+
+// k_plan, the same groups: (1) every group adds the G groups' sums in group
+// order, so all pick the same E0.  (2) Each group sizes its chunks: a
+// part's escapes are its coded values minus those with exponent in
+// [E0, E0 + 6], read off its histogram row, so each chunk's size is exact
+// (the size exchange of the digest's Figure 1, done on one GPU).  A group
+// publishes its bytes, escapes and changed blocks and adds up those of the
+// groups before it for its base offset; the last group also has the totals.
+// Group 0 writes the header's fixed fields, the last group the totals and
+// *out_size.  A group waits only on lower-numbered groups, which the GPU
+// dispatches first, so the waits end whatever else runs on the GPU; if one
+// does not end in its bound, the group sets ctrl->plan_fail and k_write
+// writes nothing.  kHashBlocks: hash sender with blocks larger than a part,
+// whose change decision k_stats leaves to this kernel (hcache is then the
+// hash cache).
 template <bool kHashBlocks>
 __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchunks, uint64_t per, uint32_t B,
                                                        int e0_override, uint8_t* __restrict__ out,
@@ -1006,41 +1040,13 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
     for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kPlanThreads) table[i] = 0u;
   }
 
-  // (1) the group's variance partials, parts strided over the threads
-  double a = 0.0, b = 0.0;
-  uint64_t m = 0;
-  for (uint64_t i = kParts * c0 + tid; i < kParts * c1; i += kPlanThreads) {
-    const Partial& p = ws.partial[i];
-    a += p.s1;
-    b += p.s2;
-    m += p.nf;
-  }
-  a = plan_sum_f64(a, s_f);
-  b = plan_sum_f64(b, s_f);
-  m = plan_sum_u64(m, s_u);
-  if (tid == 0) {
-    store_relaxed(&slot[g].s1, as_bits(a));
-    store_relaxed(&slot[g].s2, as_bits(b));
-    store_relaxed(&slot[g].nf, kSlotReady | m);
-  }
+  // (1) the variance from every group's sums (k_sums wrote them)
   double ga = 0.0, gb = 0.0;
   uint64_t gm = 0;
-  const bool sums_in = wait_all([&] {
-    if (tid >= G) return true;
-    const uint64_t w1 = load_relaxed(&slot[tid].s1), w2 = load_relaxed(&slot[tid].s2);
-    const uint64_t w3 = load_relaxed(&slot[tid].nf);
-    ga = from_bits(w1);
-    gb = from_bits(w2);
-    gm = w3 & ~kSlotReady;
-    return w1 != kSlotEmpty && w2 != kSlotEmpty && (w3 & kSlotReady) != 0u;
-  });
-  if (!sums_in) {
-    if (tid == 0) store_relaxed(&ws.ctrl->plan_fail, 1u);
-    return;
-  }
-  if (tid >= G) {
-    ga = gb = 0.0;
-    gm = 0u;
+  if (tid < G) {
+    ga = from_bits(slot[tid].s1);
+    gb = from_bits(slot[tid].s2);
+    gm = slot[tid].nf;
   }
   const double s1 = plan_sum_f64(ga, s_f);
   const double s2 = plan_sum_f64(gb, s_f);
@@ -1190,15 +1196,17 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
   }
   // the groups before this one
   uint64_t pb = 0, pe = 0, pn = 0;
-  const bool preds_in = wait_all([&] {
-    if (tid >= g) return true;
-    const uint64_t w1 = load_relaxed(&slot[tid].bytes), w2 = load_relaxed(&slot[tid].esc);
-    const uint64_t w3 = load_relaxed(&slot[tid].nch);
-    pb = w1 & ~kSlotReady;
-    pe = w2 & ~kSlotReady;
-    pn = w3 & ~kSlotReady;
-    return (w1 & w2 & w3 & kSlotReady) != 0u;
-  });
+  const bool preds_in = wait_all(
+      [&] {
+        if (tid >= g) return true;
+        const uint64_t w1 = load_relaxed(&slot[tid].bytes), w2 = load_relaxed(&slot[tid].esc);
+        const uint64_t w3 = load_relaxed(&slot[tid].nch);
+        pb = w1 & ~kSlotReady;
+        pe = w2 & ~kSlotReady;
+        pn = w3 & ~kSlotReady;
+        return (w1 & w2 & w3 & kSlotReady) != 0u;
+      },
+      ws.spin_limit);
   if (!preds_in) {
     if (tid == 0) store_relaxed(&ws.ctrl->plan_fail, 1u);
     return;
@@ -1297,7 +1305,7 @@ __device__ inline void stage_bitmap(uint32_t w, uint32_t* s_bits, uint32_t* s_ra
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restrict__ x, uint64_t n,
                                                         uint32_t log2B, uint8_t* __restrict__ out,
-                                                        uint64_t capacity, Ws ws) {
+                                                        uint64_t capacity, uint64_t* __restrict__ out_size, Ws ws) {
   __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_esc[kPartEscStage];
   __shared__ uint32_t s_bits[kBitmapWords];
@@ -1335,10 +1343,18 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   // Nothing is written unless the plan is complete and puts the chunk inside
   // the output buffer.
   const uint64_t nchunks = cdiv(n, kChunk);
-  if (ws.ctrl->plan_fail != 0u || begin < table_end(nchunks) || (begin & 127u) != 0u ||
-      begin > capacity || capacity - begin < chunk_max_bytes(nc, kCiera ? B : 0u) || esc_chunk > nc ||
-      esc_before > esc_chunk || esc_part > esc_chunk - esc_before) {
-    if (tid == 0) ws.err[wg] = uint32_t(CIERA_ERR_INTERNAL);
+  const bool plan_failed = ws.ctrl->plan_fail != 0u;
+  if (plan_failed || begin < table_end(nchunks) || (begin & 127u) != 0u || begin > capacity ||
+      capacity - begin < chunk_max_bytes(nc, kCiera ? B : 0u) || esc_chunk > nc || esc_before > esc_chunk ||
+      esc_part > esc_chunk - esc_before) {
+    if (tid == 0) {
+      ws.err[wg] = uint32_t(CIERA_ERR_INTERNAL);
+      // after a failed plan the stream must not pass for one: no size, no magic
+      if (plan_failed && wg == 0u) {
+        *out_size = 0u;
+        *reinterpret_cast<uint64_t*>(out) = 0u;
+      }
+    }
     return;
   }
   const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
@@ -1550,23 +1566,33 @@ __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks
   uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
   const uint64_t base = table_end(nchunks);
+  const uint32_t e0 = d_e0[0];
+  const bool ok = e0 <= kMaxE0;
   for (uint64_t i = tid; i < nchunks * kParts; i += kThreads)
     ws.pcount[(i / kParts) * kPcountStride + i % kParts] = 0u;
   for (uint64_t i = tid; i < nchunks; i += kThreads) ws.cstat[i * kCstatStride] = 0u;
   if (tid == 0) {
     ws.ctrl->done_esc = 0u;
     ws.ctrl->done_nch = 0u;
+    ws.ctrl->e0 = ok ? e0 : kBadE0;
+    ws.ctrl->n_err_slots = nchunks ? nchunks * kParts : 1u;
+    if (nchunks == 0u) ws.err[0] = ok ? 0u : uint32_t(CIERA_ERR_ARG);
+  }
+  if (!ok) {
+    // An invalid window base: the stream gets only its first header word,
+    // whose E0 byte keeps the bad value, so that neither a decoder nor a
+    // next encode that takes its window base from byte 7 accepts it.
+    if (tid == 0) {
+      hd[0] = uint64_t(e0) << 56;
+      *out_size = 0u;
+    }
+    return;
   }
   // the padding words after the chunk table and the escape index
   for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kThreads) table[i] = 0u;
   if (tid == 0) {
-    const uint32_t e0 = d_e0[0];
-    const bool ok = e0 <= kMaxE0;
-    ws.ctrl->e0 = ok ? e0 : kBadE0;
-    ws.ctrl->n_err_slots = nchunks ? nchunks * kParts : 1u;
-    if (nchunks == 0u) ws.err[0] = ok ? 0u : uint32_t(CIERA_ERR_ARG);
     const uint32_t magic = B ? 0x52454943u /* "CIER" */ : 0x3350495Au /* "ZIP3" */;
-    hd[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(B ? 1u : 0u) << 48) | (uint64_t(ok ? e0 : 0u) << 56);
+    hd[0] = uint64_t(magic) | (1ull << 32) | (uint64_t(B ? 1u : 0u) << 48) | (uint64_t(e0) << 56);
     hd[1] = n;
     hd[2] = uint64_t(B) | (uint64_t(kChunk) << 32);
     hd[3] = nchunks;
@@ -1607,7 +1633,7 @@ __device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint32_t log2B, 
     }
     const uint64_t flag = st & ~kValMask;
     if (__ballot(flag == 0u) != 0u) {
-      if (++spins > kSpinLimit) return false;
+      if (++spins > ws.spin_limit) return false;
       __builtin_amdgcn_s_sleep(1);
       continue;
     }
@@ -1789,7 +1815,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     for (uint32_t spins = 0;; spins++) {
       w_l = (lane < kParts) ? load_relaxed(&ws.pcount[c * kPcountStride + lane]) : kPartReady;
       if (__ballot(!(w_l & kPartReady)) == 0u) break;
-      if (spins > kSpinLimit) {
+      if (spins > ws.spin_limit) {
         err = CIERA_ERR_INTERNAL;
         break;
       }
@@ -2352,7 +2378,7 @@ __device__ inline uint32_t part_granules(uint32_t h, uint32_t nc, uint32_t log2B
 // The block's ready flag and inclusive prefix or own size, as in the
 // single-read encode: kFlagSize | padded payload bytes, then kFlagIncl |
 // payload bytes of the parts up to and including it.
-__device__ inline bool part_lookback(const uint64_t* rstat, uint64_t p, uint64_t& before) {
+__device__ inline bool part_lookback(const uint64_t* rstat, uint64_t p, uint64_t& before, uint32_t limit) {
   const uint32_t lane = lane_id();
   before = 0;
   int64_t top = int64_t(p) - 1;
@@ -2362,7 +2388,7 @@ __device__ inline bool part_lookback(const uint64_t* rstat, uint64_t p, uint64_t
     const uint64_t st = (k >= 0) ? load_relaxed(&rstat[uint64_t(k) * kRstatStride]) : kFlagIncl;
     const uint64_t flag = st & ~kValMask;
     if (__ballot(flag == 0u) != 0u) {
-      if (++spins > kSpinLimit) return false;
+      if (++spins > limit) return false;
       __builtin_amdgcn_s_sleep(1);
       continue;
     }
@@ -2656,7 +2682,7 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
   if (tid == 0) store_relaxed(&ws.rstat[c * kRstatStride], kFlagSize | padded);
   if (wave == 0) {
     uint64_t before = 0;
-    const bool found = part_lookback(ws.rstat, c, before);
+    const bool found = part_lookback(ws.rstat, c, before, ws.spin_limit);
     if (lane == 0) {
       s_before = before;
       s_found = found ? 1u : 0u;
@@ -2831,14 +2857,16 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
       ok &= hd[1] == n;
       ok &= hd[2] == (uint64_t(B) | (uint64_t(kChunk) << 32));
       ok &= hd[3] == nchunks;
-      ok &= hd[4] == in_size;
+      // in_size is the buffer's size: the stream's own length may be less
+      const uint64_t total = hd[4];
+      ok &= total <= in_size;
       for (int i = 7; i < 16; i++) ok &= hd[i] == 0u;
       const uint64_t* table = reinterpret_cast<const uint64_t*>(in + kHeader);
-      ok &= table[0] == pay_pos && table[nchunks] == in_size;
+      ok &= table[0] == pay_pos && table[nchunks] == total;
       if (ok && nchunks > 0u) {
         a = table[c];
         b = table[c + 1u];
-        ok &= a >= pay_pos && a <= b && b <= in_size && ((a | b) & 127u) == 0u;
+        ok &= a >= pay_pos && a <= b && b <= total && ((a | b) & 127u) == 0u;
       }
     }
     s_ok = ok;
@@ -3173,6 +3201,7 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   uint64_t per = 0;
   uint32_t groups = 0;
   plan_shape(nchunks, plan_groups, per, groups);
+  launch(k_sums, dim3(groups), dim3(kPlanThreads), stream, nchunks, per, ws);
   if (hashed && B > kPartValues)
     launch(k_plan<true>, dim3(groups), dim3(kPlanThreads), stream, n, nchunks, per, B, e0_override, out, d_out_size,
            hcache, ws);
@@ -3182,10 +3211,10 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   if (nchunks) {
     if (ciera)
       launch(k_write<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, lb, out,
-             out_capacity, ws);
+             out_capacity, d_out_size, ws);
     else
       launch(k_write<false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, 0u, out,
-             out_capacity, ws);
+             out_capacity, d_out_size, ws);
   }
   return launch_status();
 }
@@ -3456,6 +3485,10 @@ ciera_status ciera_read_error(const void* d_ws, hipStream_t stream) {
       if (buf[i] > worst) worst = buf[i];
   }
   return ciera_status(worst);
+}
+
+uint32_t ciera_set_wait_limit(uint32_t polls) {
+  return g_wait_limit.exchange(polls ? polls : kSpinLimit, std::memory_order_relaxed);
 }
 
 ciera_status ciera_time_kernels(void* const* events, uint32_t n_pairs) {

@@ -162,10 +162,11 @@ def check_roundtrip(stream_bytes, x, B=0, cache=None):
     return c
 
 
-def gpu_encode_e0(x, e0_src, e0_offset=0):
+def gpu_encode_e0(x, e0_src, e0_offset=0, raw=False):
     """Single-read zip3 encode with the window base read from byte
     ``e0_offset`` of the uint8 device tensor ``e0_src``.  Returns (stream bytes
-    or None, device status)."""
+    or None, device status); with ``raw``, (whole output buffer, *out_size,
+    device status) whatever the status."""
     n = x.size
     xd = torch.from_numpy(x.view(np.int16)).cuda()
     cap = ciera.zip3_max_encoded_size(n)
@@ -177,6 +178,8 @@ def gpu_encode_e0(x, e0_src, e0_offset=0):
     status = ciera.ciera_read_error(ws)
     host = buf.cpu().numpy()
     _check_guards(host, cap, "stream")
+    if raw:
+        return host[GUARD:GUARD + cap].copy(), int(size.item()), status
     if status:
         return None, status
     sz = int(size.item())
@@ -324,8 +327,13 @@ def gpu_encode_rans(x, B=0, cache=None):
     return host[GUARD:GUARD + sz].copy(), new_cache
 
 
-def gpu_decode_rans(stream_bytes, n, B=0, cache=None):
-    """rANS-mode decode on the GPU.  Returns (values, cache after, status)."""
+def gpu_decode_rans(stream_bytes, n, B=0, cache=None, extra=0):
+    """rANS-mode decode on the GPU, from a buffer holding the stream and
+    ``extra`` more bytes (not part of it).  Returns (values, cache after,
+    status)."""
+    if extra:
+        tail = np.random.default_rng(extra).integers(0, 256, extra, dtype=np.uint8)
+        stream_bytes = np.concatenate([stream_bytes, tail])
     inp = torch.from_numpy(np.ascontiguousarray(stream_bytes)).cuda()
     ybuf, y = _guarded_bytes(2 * n)
     ws_n = ciera.ciera_workspace_size(n, B) if B else ciera.zip3_workspace_size(n)
@@ -363,7 +371,7 @@ def check_rans(x, B=0, cache=None):
                              f"(gpu size {g.size}): gpu {g[i:i + 16]} oracle {o[i:i + 16]}")
     if B:
         assert np.array_equal(gc, oc), "sender cache differs from the oracle's"
-    y, rc, st = gpu_decode_rans(g, x.size, B, cache.copy() if B else None)
+    y, rc, st = gpu_decode_rans(g, x.size, B, cache.copy() if B else None, extra=256)
     assert st == 0, f"rANS decode reported status {st}"
     if not np.array_equal(y, x):
         i = int(np.flatnonzero(y != x)[0])

@@ -102,6 +102,23 @@ def test_extreme_magnitudes():
     check_roundtrip(s, tiny)
 
 
+@pytest.mark.parametrize("k", [-40, -11, 30])
+def test_variance_on_a_window_threshold(k):
+    """Tensors whose exact variance equals K0 4^k, or misses it by a part in
+    about 2^130: the oracle (exact) and the GPU (FP64) may pick either
+    adjacent window base only here, and the rest of the stream must equal
+    the oracle's at the GPU's base (check_encode); every stream decodes."""
+    from test_oracle_exact import _threshold_tensor
+    s_ = min(40, k - 17 + 126)
+    for delta in (-1, 0, 1):
+        x = _threshold_tensor(k, delta, s_)  # 513 values: 64 units and a ragged tail
+        s, st = check_encode(x)
+        assert int(s[7]) in (126 + k, 127 + k)
+        check_roundtrip(s, x)
+        s, _ = check_encode(x, 64, np.zeros(x.size, np.uint8))
+        check_roundtrip(s, x, 64, np.zeros(x.size, np.uint8))
+
+
 def test_deterministic_and_stream_independent():
     rng = np.random.default_rng(77)
     x = wl.f32_to_bf16(rng.standard_normal(5_000_000, dtype=np.float32) * np.float32(0.02))

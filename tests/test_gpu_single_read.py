@@ -57,12 +57,23 @@ def test_single_read_window_from_previous_stream():
 
 
 def test_single_read_rejects_bad_window_base():
+    from gpu_util import CANARY
     x = np.arange(70000, dtype=np.uint16)
-    for bad in (250, 255):
-        g, st = gpu_encode_e0(x, torch.tensor([bad], dtype=torch.uint8, device="cuda"))
-        assert g is None and st == 1
-    g, st = gpu_encode_e0(np.zeros(0, np.uint16), torch.tensor([250], dtype=torch.uint8, device="cuda"))
-    assert g is None and st == 1
+    for n in (70000, 0):
+        for bad in (250, 255):
+            src = torch.tensor([bad], dtype=torch.uint8, device="cuda")
+            g, st = gpu_encode_e0(x[:n], src)
+            assert g is None and st == 1
+            # only the first header word is written, and its E0 byte keeps the
+            # bad value: a decoder rejects it, and so does a next single-read
+            # encode that takes its window base from byte 7
+            buf, size, st = gpu_encode_e0(x[:n], src, raw=True)
+            assert st == 1 and size == 0
+            assert buf[:8].tolist() == [0] * 7 + [bad]
+            assert (buf[8:] == CANARY).all(), "bytes written past the first header word"
+            chained = torch.from_numpy(buf[:16].copy()).cuda()
+            g, st = gpu_encode_e0(x[:n], chained, e0_offset=7)
+            assert g is None and st == 1
 
 
 def test_single_read_deterministic():
