@@ -281,6 +281,26 @@ ciera_status ciera_encode_e0(const void* d_x, uint64_t n, uint32_t B, uint8_t* d
  * CIERA_ERR_ARG for a null array or handle. */
 ciera_status ciera_time_kernels(void* const* events, uint32_t n_pairs);
 
+/* ciera_encode_noalloc: ciera_encode for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same kernels, stream, cache update
+ * and window, with the workspace taken from a 6 MiB array that the library
+ * holds in device memory (one per GPU it runs on, kept until the process
+ * ends) instead of a caller's buffer.  The call allocates and frees
+ * nothing; its first call on a device looks up that device's array.
+ *   d_x, n, B, d_prev_exp, d_out, out_capacity, d_out_size: as ciera_encode.
+ *   n <= CIERA_NOALLOC_MAX_N (2^27 values); a larger n returns
+ *   CIERA_ERR_WORKSPACE before anything is enqueued.
+ * Every call on one GPU uses that GPU's one array: calls that overlap on a
+ * GPU (two streams, or two host threads) race and corrupt each other's
+ * streams; order them.  The kernels clear what they need, so the array's
+ * contents from an earlier call do not matter.  There is no workspace for
+ * ciera_read_error: a wait that gave up shows as *d_out_size == 0 once the
+ * stream has completed (the header's state as after CIERA_ERR_INTERNAL). */
+#define CIERA_NOALLOC_MAX_N (1ull << 27)
+ciera_status ciera_encode_noalloc(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, void* d_out,
+                                  uint64_t out_capacity, uint64_t* d_out_size, hipStream_t stream);
+
 /* Test hook: the number of polls after which the next calls' waits on
  * other workgroups give up (CIERA_ERR_INTERNAL); 0 restores the default
  * (2^22).  Returns the previous value.  Tests lower it to drive the failure

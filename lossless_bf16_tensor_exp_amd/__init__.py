@@ -25,6 +25,7 @@ Same names as the C ABI::
     ciera_read_error(ws, stream=None)
     ciera_time_kernels(pairs)             (profiling: per-kernel start/stop events)
     ciera_set_wait_limit(polls)           (test hook: bound of the waits between workgroups)
+    ciera_encode_noalloc(x, B, prev_exp, out, out_size, stream=None)   (no workspace: allocates nothing)
 
 ``x``/``y`` are CUDA(HIP) tensors of dtype bfloat16, int16 or uint16 holding
 the BF16 patterns; ``out``/``inp``/``ws``/``prev_exp`` are uint8 tensors and
@@ -42,11 +43,12 @@ __all__ = [
     "zip3_encode_e0", "ciera_encode_e0", "ciera_encode_hashed", "ciera_hash_cache_size",
     "rans_max_encoded_size", "rans_workspace_size", "zip3_encode_rans", "zip3_decode_rans", "ciera_encode_rans",
     "ciera_decode_rans",
-    "bind", "ciera_time_kernels", "ciera_set_wait_limit",
+    "bind", "ciera_time_kernels", "ciera_set_wait_limit", "ciera_encode_noalloc", "NOALLOC_MAX_N",
     "CHUNK",
 ]
 
 CHUNK = 65536
+NOALLOC_MAX_N = 1 << 27
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libciera.so")
 _lib = None
@@ -98,6 +100,7 @@ def load_library():
         "ciera_decode_rans": [vp, u64, vp, u64, u32, vp, vp, u64, vp],
         "ciera_read_error": [vp, vp],
         "ciera_time_kernels": [ctypes.POINTER(vp), u32],
+        "ciera_encode_noalloc": [vp, u64, u32, vp, vp, u64, vp, vp],
     }
     for name, args in sigs.items():
         f = getattr(lib, name)
@@ -217,6 +220,20 @@ def ciera_encode(x, B: int, prev_exp, out, ws, out_size, e0_override: int = -1, 
                              ws.numel(), ctypes.c_void_p(out_size.data_ptr()), e0_override, plan_groups,
                              _stream(stream))
     _raise(st, "ciera_encode")
+
+
+def ciera_encode_noalloc(x, B: int, prev_exp, out, out_size, stream=None) -> None:
+    """ciera_encode with its workspace in the library's own device array
+    (nothing is allocated; n <= NOALLOC_MAX_N; calls on one GPU must not
+    overlap)."""
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(prev_exp, "prev_exp", x.numel())
+    _check_bytes(out, "out")
+    _check_size_slot(out_size)
+    st = lib.ciera_encode_noalloc(_ptr(x), x.numel(), B, _ptr(prev_exp), _ptr(out), out.numel(),
+                                  ctypes.c_void_p(out_size.data_ptr()), _stream(stream))
+    _raise(st, "ciera_encode_noalloc")
 
 
 def ciera_encode_e0(x, B: int, prev_exp, e0_src, out, ws, out_size, e0_offset: int = 0, stream=None) -> None:

@@ -38,6 +38,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "ciera.h"
@@ -3355,9 +3356,51 @@ ciera_status decode_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t
   return launch_status();
 }
 
+// ------------------------------------------------------------------ no-allocation entry point
+// ciera_encode_noalloc runs ciera_encode's kernels on a workspace that lives
+// in this array instead of a caller's buffer.  Each GPU holds its own copy;
+// host code must use the address hipGetSymbolAddress returns for the current
+// device, never the array's name (a host-side stand-in).
+constexpr uint64_t kScratchBytes = 6ull << 20;
+constexpr uint64_t kNoAllocMaxN = CIERA_NOALLOC_MAX_N;  // 2048 chunks: ws_layout needs about 5.5 MB
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+// The scratch array's device address on the current device, looked up once
+// per device (with that device current) and kept.
+ciera_status scratch_on_current_device(void** ptr_out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return CIERA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return CIERA_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *ptr_out = g_scratch_ptr[dev];
+  return CIERA_OK;
+}
+
 }  // namespace
 
 extern "C" {
+
+ciera_status ciera_encode_noalloc(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, void* d_out,
+                                  uint64_t out_capacity, uint64_t* d_out_size, hipStream_t stream) {
+  if (B == 0u || !valid_block(B)) return CIERA_ERR_ARG;
+  if (n > kNoAllocMaxN || ws_layout(cdiv(n, kChunk)).total > kScratchBytes) return CIERA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const ciera_status st = scratch_on_current_device(&ws);
+  if (st != CIERA_OK) return st;
+  return encode_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, ws, kScratchBytes, d_out_size, -1, 0u, stream);
+}
 
 uint64_t zip3_max_encoded_size(uint64_t n) { return n > kMaxN ? 0u : max_size(n, 0u); }
 
