@@ -3,20 +3,30 @@
 
 A step is one pass of the whole codec over one synthetic tensor already
 resident in HBM: encode (variance/change pass, window plan, pack) and decode.
-Default workload: the 64 Mi-value gradient-like tensor (N(0, 1e-3) with 0.1 %
-Student-t(3) outliers, 3-bit code only).  Other workloads (1, 3, 4, 5) use
-exponent reuse; their steps alternate between two consecutive iterations so
-the caches always hold the previous iteration.
+Default workload: the largest one, the 1e9-value stress buffer (mixed
+N(0, 0.02) / Student-t / constant regions with +-0, subnormals, Inf and NaN
+payloads, 1 % exponent flips between two iterations; exponent reuse with
+B = 512 plus the 3-bit code).  The reuse workloads' steps alternate between
+two consecutive iterations, so the caches always hold the previous one.
 
 Prints one JSON line.  ``value`` = 2 n K / (wall time of K steps), in GB/s of
 BF16 input (1 GB = 1e9 bytes).  A second pass of the same K steps times every
 kernel with HIP events recorded at the kernel's own start and end;
-``roofline`` describes the kernel with the longest average duration.  In
-the back-to-back steps, work that one call leaves in the 256 MB MALL (decode's
-output lines, still to be written back) is paid by the next call, so a third
-pass, ``isolated``, times encode alone and decode alone with the MALL swept by
-a 1 GiB read before every call.  ``cpu_baseline`` times the plain CPU oracle
-(single thread) on the same tensor.
+``roofline`` describes the streaming kernel with the longest average
+duration.  In the back-to-back steps, work that one call leaves in the
+256 MB MALL (decode's output lines, still to be written back) is paid by the
+next call, so a third pass, ``isolated``, times encode alone and decode alone
+with the MALL swept by a 1 GiB read before every call.
+
+Checks in the same run: the stream of the timed encode is compared byte for
+byte with the CPU oracle's for the same input and cache (``bit_exact_vs_oracle``;
+the run exits with status 1 when it differs), and the decoded tensor with the
+input.  ``cpu_baseline`` times that oracle on the host's cores: one thread,
+and chunk-parallel on all of them (the same bytes).  ``configs`` repeats the
+isolated measurement, the oracle check and both oracle legs for the other
+workloads (1: a 2^20-value shard, 2: the 64 Mi-value gradient tensor, 3: the
+OLMoE-like shard at B = 64 and 1024, 4: the DeepSeek-like chain's last
+iteration).
 """
 from __future__ import annotations
 
@@ -36,12 +46,17 @@ HBM_PEAK_GBPS = 8000.0
 # cycles): 614.4 G wave instructions/s.
 VALU_PEAK_WAVE_INSTR_PER_S = 256 * 4 * 2.4e9 / 4
 WORKLOAD_NAMES = {
-    1: "shard 1,048,576 BF16 ~N(0,0.02), iter t = iter t-1 + N(0,1e-4); exponent reuse B=256 + 3-bit code",
+    1: "shard 1,048,576 BF16 ~N(0,0.02), iter t = iter t-1 + N(0,1e-4); exponent reuse B={B} + 3-bit code",
     2: "gradient 67,108,864 BF16 ~N(0,1e-3) + 0.1% Student-t(3); 3-bit code only, 128-B chunks",
     3: "OLMoE-like layer shard W=4, 104,891,392 BF16 ~N(0,0.02), ~0.3% exponent flips; exponent reuse B={B}",
-    4: "DeepSeek-MoE-like layer shard W=8, 71,368,704 BF16 ~N(0,0.015), 0.5% flips in 20% of blocks; B=128",
-    5: "stress 1e9 BF16 mixed N/t/constant + specials, 1% flips; exponent reuse B=512",
+    4: "DeepSeek-MoE-like layer shard W=8, 71,368,704 BF16 ~N(0,0.015), 0.5% flips in 20% of blocks; B={B}",
+    5: "stress 1e9 BF16 mixed N/t/constant + specials, 1% flips; exponent reuse B={B}",
 }
+DEFAULT_B = {1: 256, 2: 0, 3: 64, 4: 128, 5: 512}
+# the encode's kernels, in launch order, then the decode's
+ENC_KERNELS = ["k_stats", "k_sums", "k_plan", "k_write"]
+DEC_KERNELS = ["k_decode"]
+STREAMING = ["k_stats", "k_write", "k_decode"]
 
 
 def source_hash() -> str:
@@ -49,7 +64,10 @@ def source_hash() -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-KERNELS = ["k_stats", "k_plan", "k_write", "k_decode"]
+def host_threads() -> int:
+    """Threads for the all-core oracle leg: the host's CPUs, at most 16 (a
+    one-GPU share of the box)."""
+    return max(1, min(16, os.cpu_count() or 1))
 
 
 class _Offset:
@@ -105,13 +123,13 @@ def changed_values(prev, cur, B):
     return int(sizes[blk].sum())
 
 
-def load_valu(kernel: str, workload: int, B: int):
-    """VALU wave instructions per launch (rocprofv3 SQ_INSTS_VALU, a device
-    total) from the ```json blocks of the instruction summaries in profiles/,
-    if they were taken on the current kernel source."""
+def _profile_record(kind: str, kernel: str, workload: int, B: int):
+    """A per-launch figure for kernel on (workload, B) from the ```json blocks
+    of the ``*{kind}*.md`` summaries in profiles/, if taken on the current
+    kernel source (else None)."""
     import glob
     import re
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*valu*.md"))):
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"*{kind}*.md"))):
         with open(path) as f:
             text = f.read()
         for block in re.findall(r"```json\n(.*?)```", text, flags=re.S):
@@ -122,6 +140,18 @@ def load_valu(kernel: str, workload: int, B: int):
             if hit is not None:
                 return hit
     return None
+
+
+def load_valu(kernel: str, workload: int, B: int):
+    """VALU wave instructions per launch (rocprofv3 SQ_INSTS_VALU, a device
+    total) from the instruction summaries in profiles/."""
+    return _profile_record("valu", kernel, workload, B)
+
+
+def load_traffic(kernel: str, workload: int, B: int):
+    """Counter-derived HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled
+    by a copy kernel of known size) from the traffic summaries in profiles/."""
+    return _profile_record("traffic", kernel, workload, B)
 
 
 def alu_roofline(kernel: str, key: str, workload: int, B: int, ms: float):
@@ -137,23 +167,141 @@ def alu_roofline(kernel: str, key: str, workload: int, B: int, ms: float):
             "valu_instr_per_launch": v, "avg_launch_ms": round(ms, 5)}
 
 
-def load_traffic(kernel: str, workload: int, B: int):
-    """Counter-derived HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled
-    by a copy kernel of known size) from the ```json blocks of the traffic
-    summaries in profiles/, if they were taken on the current kernel source."""
-    import glob
-    import re
-    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*traffic*.md"))):
-        with open(path) as f:
-            text = f.read()
-        for block in re.findall(r"```json\n(.*?)```", text, flags=re.S):
-            rec = json.loads(block)
-            if rec.get("source_hash") != source_hash():
-                continue
-            hit = rec.get("kernels", {}).get(f"{kernel}/w{workload}/B{B}")
-            if hit is not None:
-                return hit
-    return None
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Gpu:
+    """The device, stream, MALL sweep and isolated-call timer shared by the
+    measurements."""
+
+    def __init__(self, torch, ciera, K):
+        self.torch, self.ciera, self.K = torch, ciera, K
+        self.dev = torch.device("cuda:0")
+        self.stream = torch.cuda.current_stream()
+        self.sweep = torch.ones(1 << 28, dtype=torch.float32, device=self.dev)
+        self.sweep_out = torch.empty((), dtype=torch.float32, device=self.dev)
+
+    def isolated(self, call, restore=None):
+        """K + 1 calls, each preceded (outside its events) by restore() and a
+        1 GiB read that leaves only clean lines in the MALL; the first call
+        is a warm-up.  Returns (median ms, min ms)."""
+        torch = self.torch
+        marks = []
+        for _ in range(self.K + 1):
+            if restore is not None:
+                restore()
+            torch.sum(self.sweep, dim=0, out=self.sweep_out)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(self.stream)
+            call()
+            b.record(self.stream)
+            marks.append((a, b))
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in marks[1:])
+        return ms[len(ms) // 2], ms[0]
+
+
+def oracle_legs(oracle, np, x, B, prev_exps, threads):
+    """The CPU oracle on one input: one thread and `threads` threads, encode
+    then decode, each timed.  Returns (stream, timings dict)."""
+    res = {}
+    streams = []
+    for leg, nt in (("single", 0), ("all_cores", threads)):
+        cache = prev_exps.copy() if B else None
+        t = time.perf_counter()
+        s, _ = oracle.encode(x, B, cache, threads=nt)
+        t_enc = time.perf_counter() - t
+        rcache = prev_exps.copy() if B else None
+        t = time.perf_counter()
+        y = oracle.decode(s, x.size, B, rcache, threads=nt)
+        t_dec = time.perf_counter() - t
+        if not np.array_equal(y, x):
+            raise AssertionError(f"the oracle's own round trip failed ({leg})")
+        res[leg] = {"threads": max(1, nt), "encode_s": round(t_enc, 3), "decode_s": round(t_dec, 3),
+                    "encode_GBps": round(2 * x.size / t_enc / 1e9, 4),
+                    "decode_GBps": round(2 * x.size / t_dec / 1e9, 4),
+                    "GBps": round(2 * x.size / (t_enc + t_dec) / 1e9, 4)}
+        streams.append(s)
+    if streams[0].tobytes() != streams[1].tobytes():
+        raise AssertionError("the chunk-parallel oracle wrote other bytes than the single-threaded one")
+    return streams[0], res
+
+
+def stream_stats(s, n):
+    """Header fields of a stream: window base, changed blocks, escapes."""
+    import numpy as np
+    hd = s[:56].view(np.uint64)
+    return {"E0": int(s[7]), "changed_blocks": int(hd[5]), "escapes": int(hd[6])}
+
+
+def measure_config(gpu, oracle, np, wl, workload, B_pick, threads):
+    """One workload's isolated encode and decode on the GPU, its stream
+    against the oracle's, and both oracle legs."""
+    torch, ciera = gpu.torch, gpu.ciera
+    t0 = time.time()
+    d = wl.WORKLOADS[workload]()
+    iters, mode = d["iters"], d["mode"]
+    B = 0 if mode == "zip3" else B_pick
+    x = iters[-1]
+    prev = ((iters[-2] >> 7) & 0xFF).astype(np.uint8) if len(iters) >= 2 else None
+    n = x.size
+    log(f"config {workload} B={B} n={n} generated in {time.time() - t0:.1f}s")
+    dev = gpu.dev
+    xd = torch.from_numpy(x.view(np.int16)).to(dev)
+    if mode == "zip3":
+        cap, wsz = ciera.zip3_max_encoded_size(n), ciera.zip3_workspace_size(n)
+    else:
+        cap, wsz = ciera.ciera_max_encoded_size(n, B), ciera.ciera_workspace_size(n, B)
+    out = torch.empty(cap, dtype=torch.uint8, device=dev)
+    ws_e = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(wsz, dtype=torch.uint8, device=dev)
+    size = torch.zeros(1, dtype=torch.int64, device=dev)
+    y = torch.empty(n, dtype=torch.int16, device=dev)
+    pristine = send = recv = None
+    if mode != "zip3":
+        pristine = torch.from_numpy(prev).to(dev)
+        send, recv = pristine.clone(), pristine.clone()
+        enc = ciera.bind("ciera_encode", xd, n, B, send, out, cap, ws_e, wsz, size, stream=gpu.stream)
+    else:
+        enc = ciera.bind("zip3_encode", xd, n, out, cap, ws_e, wsz, size, stream=gpu.stream)
+    if send is not None:
+        send.copy_(pristine)
+    enc()
+    torch.cuda.synchronize()
+    assert ciera.ciera_read_error(ws_e) == 0
+    sz = int(size.item())
+    if mode == "zip3":
+        dec = ciera.bind("zip3_decode", out, sz, y, n, ws_d, wsz, stream=gpu.stream)
+    else:
+        dec = ciera.bind("ciera_decode", out, sz, y, n, B, recv, ws_d, wsz, stream=gpu.stream)
+    e_ms, e_min = gpu.isolated(enc, (lambda: send.copy_(pristine)) if send is not None else None)
+    d_ms, d_min = gpu.isolated(dec, (lambda: recv.copy_(pristine)) if recv is not None else None)
+    assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
+    roundtrip = bool(torch.equal(y, xd))
+    g_stream = out[:sz].cpu().numpy()
+    o_stream, legs = oracle_legs(oracle, np, x, B, prev, threads)
+    exact = g_stream.tobytes() == o_stream.tobytes()
+    ch = changed_values(iters[-2], x, B) if mode != "zip3" else 0
+    in_bytes = 2 * n
+    alg_enc = in_bytes + (n + ch if mode != "zip3" else 0) + in_bytes + sz
+    alg_dec = sz + in_bytes + (n if mode != "zip3" else 0)
+    st = stream_stats(g_stream, n)
+    nb = -(-n // B) if B else 0
+    res = {"workload": WORKLOAD_NAMES[workload].format(B=B), "n": n, "B": B, "mode": mode,
+           "encode_ms": round(e_ms, 5), "encode_min_ms": round(e_min, 5),
+           "encode_GBps": round(in_bytes / (e_ms * 1e-3) / 1e9, 1),
+           "encode_algorithmic_bytes": alg_enc,
+           "decode_ms": round(d_ms, 5), "decode_min_ms": round(d_min, 5),
+           "decode_GBps": round(in_bytes / (d_ms * 1e-3) / 1e9, 1),
+           "decode_algorithmic_bytes": alg_dec,
+           "compression_ratio": round(in_bytes / sz, 4), "stream_bytes": sz,
+           "E0": st["E0"], "escape_pct": round(100.0 * st["escapes"] / max(1, n), 3),
+           "reuse_pct": round(100.0 * (1 - st["changed_blocks"] / nb), 2) if nb else None,
+           "bit_exact_vs_oracle": exact, "roundtrip_ok": roundtrip, "oracle": legs}
+    del out, ws_e, ws_d, y, xd, send, recv, pristine
+    torch.cuda.empty_cache()
+    return res
 
 
 def main() -> int:
@@ -161,10 +309,13 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", type=int, default=2, choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--workload", type=int, default=5, choices=sorted(WORKLOAD_NAMES))
     ap.add_argument("--block", type=int, default=None, help="block size B for the reuse workloads")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--verify", action="store_true", help="check the last step's round trip on the host")
+    ap.add_argument("--configs", default="auto",
+                    help="extra workloads to measure isolated, as w or w:B, comma-separated; 'auto' = "
+                         "1,2,3:64,3:1024,4 with the default workload, none otherwise; '' = none")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle legs and the oracle check")
+    ap.add_argument("--verify", action="store_true", help="check the last step's round trip on the device")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="after timing, run a plain elementwise kernel that reads and writes MIB MiB each "
                          "(reference dispatch for calibrating hardware byte counters)")
@@ -186,20 +337,21 @@ def main() -> int:
         hip_build.build()
     ciera.load_library()
     assert torch.cuda.is_available(), "bench.py needs a GPU"
-    dev = torch.device("cuda:0")
+    gpu = Gpu(torch, ciera, args.steps)
+    dev = gpu.dev
+    K = args.steps
 
     t0 = time.time()
-    gen = wl.WORKLOADS[args.workload]
-    d = gen()
+    d = wl.WORKLOADS[args.workload]()
     iters = d["iters"]
     mode = d["mode"]
     B = 0 if mode == "zip3" else (args.block or d["B"][0])
     n = iters[0].size
-    print(f"[bench] workload {args.workload} n={n} B={B} generated in {time.time() - t0:.1f}s", file=sys.stderr,
-          flush=True)
+    log(f"workload {args.workload} n={n} B={B} generated in {time.time() - t0:.1f}s")
 
     # the two tensors a step alternates between (zip3: one tensor)
     pair = [iters[-2], iters[-1]] if len(iters) >= 2 else [iters[0], iters[0]]
+    del d, iters
     xs = [torch.from_numpy(a.view(np.int16)).to(dev) for a in pair]
     y = torch.empty(n, dtype=torch.int16, device=dev)
     if mode == "zip3":
@@ -210,11 +362,11 @@ def main() -> int:
     ws_e = torch.empty(wsz, dtype=torch.uint8, device=dev)
     ws_d = torch.empty(wsz, dtype=torch.uint8, device=dev)
     size = torch.zeros(1, dtype=torch.int64, device=dev)
-    send = recv = None
+    send = recv = e_prev = None
     if mode != "zip3":
         e_prev = torch.from_numpy(((pair[0] >> 7) & 0xFF).astype(np.uint8)).to(dev)
         send, recv = e_prev.clone(), e_prev.clone()
-    stream = torch.cuda.current_stream()
+    stream = gpu.stream
 
     # Pre-bound C calls (argument marshalling done once, outside the timing).
     if mode == "zip3":
@@ -251,8 +403,8 @@ def main() -> int:
         step(w)
     torch.cuda.synchronize()
 
-    K = args.steps
     # Pass 1, the headline number: K steps back to back, nothing between them.
+    log(f"pass 1: {K} steps back to back")
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for s in range(K):
@@ -261,11 +413,12 @@ def main() -> int:
     wall = time.perf_counter() - t_start
     # Pass 2, the same K steps with every kernel timed by HIP events that the
     # runtime records at the kernel's own start and end (hipExtLaunchKernel);
-    # a step launches encode's three kernels, then decode's one.
-    names = KERNELS
+    # a step launches encode's four kernels, then decode's one.
+    names = ENC_KERNELS + DEC_KERNELS
+    ne = len(ENC_KERNELS)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
           for _ in range(K)]
-    ciera.ciera_time_kernels([pair for row in ev for pair in row], stream=stream)
+    ciera.ciera_time_kernels([pair_ for row in ev for pair_ in row], stream=stream)
     torch.cuda.synchronize()
     t2 = time.perf_counter()
     for s in range(K):
@@ -276,50 +429,17 @@ def main() -> int:
     wall2 = time.perf_counter() - t2
     ciera.ciera_time_kernels([])
     kern_ms = {nm: sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(K)) / K for i, nm in enumerate(names)}
-    enc_ms = [ev[s][0][0].elapsed_time(ev[s][2][1]) for s in range(K)]  # k_stats start .. k_write end
-    dec_ms = [ev[s][3][0].elapsed_time(ev[s][3][1]) for s in range(K)]
+    enc_ms = [ev[s][0][0].elapsed_time(ev[s][ne - 1][1]) for s in range(K)]  # k_stats start .. k_write end
+    dec_ms = [ev[s][ne][0].elapsed_time(ev[s][ne][1]) for s in range(K)]
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
     if args.verify:
         klast = (2 * K) % 2 if mode != "zip3" else 0  # input of the last step, index 2K-1
         assert torch.equal(y, xs[klast]), "round trip failed"
 
-    # Single-read encode back to back (zip3): the window base comes from byte
-    # 7 of the stream the full encode just wrote, read on the device; K calls,
-    # each kernel timed by HIP events as above.
-    single = None
-    if mode == "zip3":
-        out1 = torch.empty(cap, dtype=torch.uint8, device=dev)
-        size1 = torch.zeros(1, dtype=torch.int64, device=dev)
-        ws1 = torch.empty(wsz, dtype=torch.uint8, device=dev)
-        enc1 = ciera.bind("zip3_encode_e0", xs[0], n, _Offset(out, 7), out1, cap, ws1, wsz, size1, stream=stream)
-        for _ in range(args.warmup):
-            enc1()
-        torch.cuda.synchronize()
-        ev1 = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
-               for _ in range(K)]
-        ciera.ciera_time_kernels([pair for row in ev1 for pair in row], stream=stream)
-        t1 = time.perf_counter()
-        for _ in range(K):
-            enc1()
-        torch.cuda.synchronize()
-        wall1 = time.perf_counter() - t1
-        ciera.ciera_time_kernels([])
-        assert ciera.ciera_read_error(ws1) == 0
-        sz1 = int(size1.item())
-        same = sz1 == sizes[0] and bool(torch.equal(out1[:sz1], out[:sz1]))
-        prep_ms = sum(ev1[s][0][0].elapsed_time(ev1[s][0][1]) for s in range(K)) / K
-        write_ms = sum(ev1[s][1][0].elapsed_time(ev1[s][1][1]) for s in range(K)) / K
-        call_ms = sum(ev1[s][0][0].elapsed_time(ev1[s][1][1]) for s in range(K)) / K
-        by1 = 2 * n + sz1
-        single = {"encode_GBps": round(2 * n / (call_ms * 1e-3) / 1e9, 2), "encode_ms": round(call_ms, 5),
-                  "wall_ms_per_call": round(wall1 * 1e3 / K, 4), "stream_equal_to_full_encode": same,
-                  "kernels": {"k_prep1": {"avg_ms": round(prep_ms, 5)},
-                              "k_write1": {"avg_ms": round(write_ms, 5), "algorithmic_bytes": by1,
-                                           "GBps": round(by1 / (write_ms * 1e-3) / 1e9, 1)}}}
-
     # Graph replay: the same steps captured once in a HIP graph (two steps
     # for the reuse workloads, so the caches keep alternating) and replayed;
-    # no host launch work per step.  Small tensors are launch-bound eagerly.
+    # no host launch work per step.
+    log("graph replay")
     g = torch.cuda.CUDAGraph()
     side = torch.cuda.Stream()
     side.wait_stream(stream)
@@ -350,52 +470,51 @@ def main() -> int:
              "GBps": round(2 * n * reps_g * steps_g / wall_g / 1e9, 2)}
     del g
 
-    # Pass 3: each direction on its own, K calls each.  Before every call the
-    # ciera caches are restored from a pristine copy and a 1 GiB read-only
-    # sum sweeps the 256 MB MALL (both outside the events), so that no call
-    # inherits another's dirty lines or finds its input cached.  Encode takes
-    # the step input of pass 1 against the other input's exponents; decode
-    # takes the stream that encode wrote.
+    # Pass 3: each direction on its own, K calls each (the ciera caches
+    # restored from a pristine copy and the MALL swept before every call,
+    # outside the events).  Encode takes the step input of pass 1 against
+    # the other input's exponents; decode takes the stream that encode wrote.
+    log("pass 3: isolated encode and decode")
     k_iso = 1 if mode != "zip3" else 0
-    sweep = torch.ones(1 << 28, dtype=torch.float32, device=dev)
-    sweep_out = torch.empty((), dtype=torch.float32, device=dev)
-
-    def isolated(call, cache):
-        marks = []
-        for _ in range(K + 1):
-            if cache is not None:
-                cache.copy_(e_prev)
-            torch.sum(sweep, dim=0, out=sweep_out)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            call()
-            b.record(stream)
-            marks.append((a, b))
-        torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in marks[1:])
-        return ms[len(ms) // 2], ms[0]
-
-    enc_iso, enc_iso_min = isolated(enc[k_iso], send)
-    dec_iso, dec_iso_min = isolated(dec[k_iso], recv)
+    restore_s = (lambda: send.copy_(e_prev)) if send is not None else None
+    restore_r = (lambda: recv.copy_(e_prev)) if recv is not None else None
+    enc_iso, enc_iso_min = gpu.isolated(enc[k_iso], restore_s)
+    g_stream = out[:sizes[k_iso]].cpu().numpy()  # the timed encode's stream, for the oracle check
+    dec_iso, dec_iso_min = gpu.isolated(dec[k_iso], restore_r)
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
+    iso_roundtrip = bool(torch.equal(y, xs[k_iso]))
 
     # Single-read encode, timed like pass 3: the window base is byte 7 of the
     # stream the full encode of the same input just wrote (read on the
     # device); x (and the sender cache) are read once.  Its stream must equal
-    # the full encode's.
+    # the full encode's.  Then its kernels once more with events.
+    log("single-read encode")
     out1 = torch.empty(cap, dtype=torch.uint8, device=dev)
     size1 = torch.zeros(1, dtype=torch.int64, device=dev)
     ws1 = torch.empty(wsz, dtype=torch.uint8, device=dev)
     if mode == "zip3":
-        enc1_iso = ciera.bind("zip3_encode_e0", xs[k_iso], n, _Offset(out, 7), out1, cap, ws1, wsz, size1,
-                              stream=stream)
+        enc1 = ciera.bind("zip3_encode_e0", xs[k_iso], n, _Offset(out, 7), out1, cap, ws1, wsz, size1,
+                          stream=stream)
     else:
-        enc1_iso = ciera.bind("ciera_encode_e0", xs[k_iso], n, B, send, _Offset(out, 7), out1, cap, ws1, wsz, size1,
-                              stream=stream)
-    sr_iso, sr_iso_min = isolated(enc1_iso, send)
+        enc1 = ciera.bind("ciera_encode_e0", xs[k_iso], n, B, send, _Offset(out, 7), out1, cap, ws1, wsz, size1,
+                          stream=stream)
+    sr_iso, sr_iso_min = gpu.isolated(enc1, restore_s)
     assert ciera.ciera_read_error(ws1) == 0
     sz_sr = int(size1.item())
     sr_same = sz_sr == sizes[k_iso] and bool(torch.equal(out1[:sz_sr], out[:sz_sr]))
+    ev1 = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(2)]
+           for _ in range(K)]
+    ciera.ciera_time_kernels([pr for row in ev1 for pr in row], stream=stream)
+    for _ in range(K):
+        if restore_s is not None:
+            restore_s()
+        torch.sum(gpu.sweep, dim=0, out=gpu.sweep_out)
+        enc1()
+    torch.cuda.synchronize()
+    ciera.ciera_time_kernels([])
+    assert ciera.ciera_read_error(ws1) == 0
+    prep_ms = sum(ev1[s][0][0].elapsed_time(ev1[s][0][1]) for s in range(K)) / K
+    write1_ms = sum(ev1[s][1][0].elapsed_time(ev1[s][1][1]) for s in range(K)) / K
     del out1, ws1
 
     # Hash sender (ciera workloads): the same encode with two 64-bit hashes
@@ -404,7 +523,9 @@ def main() -> int:
     # from a zeroed cache; timed like pass 3, and its stream compared with
     # the exact sender's.
     hashed = None
+    changed_vals = changed_values(pair[0], pair[1], B) if mode != "zip3" else 0
     if mode != "zip3":
+        log("hash sender")
         hsz = ciera.ciera_hash_cache_size(n, B)
         h_pristine = torch.zeros(hsz, dtype=torch.uint8, device=dev)
         h_cache = torch.empty_like(h_pristine)
@@ -413,41 +534,37 @@ def main() -> int:
         ciera.ciera_encode_hashed(xs[1 - k_iso], B, h_pristine, out_h, ws_e, size_h)
         enc_h = ciera.bind("ciera_encode_hashed", xs[k_iso], n, B, h_cache, out_h, cap, ws_e, wsz, size_h,
                            stream=stream)
-        marks = []
-        for i in range(K + 1):
-            h_cache.copy_(h_pristine)
-            torch.sum(sweep, dim=0, out=sweep_out)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            enc_h()
-            b.record(stream)
-            marks.append((a, b))
-        torch.cuda.synchronize()
-        ms = sorted(a.elapsed_time(b) for a, b in marks[1:])
+        h_ms, h_min = gpu.isolated(enc_h, lambda: h_cache.copy_(h_pristine))
         # the same calls once more with each kernel timed
-        evk = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(3)]
+        evk = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ENC_KERNELS]
                for _ in range(K)]
-        ciera.ciera_time_kernels([pair for row in evk for pair in row], stream=stream)
+        ciera.ciera_time_kernels([pr for row in evk for pr in row], stream=stream)
         for i in range(K):
             h_cache.copy_(h_pristine)
-            torch.sum(sweep, dim=0, out=sweep_out)
+            torch.sum(gpu.sweep, dim=0, out=gpu.sweep_out)
             enc_h()
         torch.cuda.synchronize()
         ciera.ciera_time_kernels([])
         assert ciera.ciera_read_error(ws_e) == 0
         szh = int(size_h.item())
         same = szh == sizes[k_iso] and bool(torch.equal(out_h[:szh], out[:szh]))
-        hk = [sum(evk[i][j][0].elapsed_time(evk[i][j][1]) for i in range(K)) / K for j in range(3)]
-        hashed = {"encode_ms": round(ms[len(ms) // 2], 5), "encode_min_ms": round(ms[0], 5),
-                  "cache_bytes": hsz, "stream_equal_to_exact_sender": same,
-                  "kernels": {"k_stats": round(hk[0], 5), "k_plan": round(hk[1], 5), "k_write": round(hk[2], 5)},
+        hk = {nm: sum(evk[i][j][0].elapsed_time(evk[i][j][1]) for i in range(K)) / K
+              for j, nm in enumerate(ENC_KERNELS)}
+        alg_h = 2 * n + hsz + 16 * (changed_vals // B) + 2 * n + sizes[k_iso]
+        hashed = {"encode_ms": round(h_ms, 5), "encode_min_ms": round(h_min, 5),
+                  "encode_GBps": round(2 * n / (h_ms * 1e-3) / 1e9, 2),
+                  "cache_bytes": hsz, "blocks": -(-n // B), "stream_equal_to_exact_sender": same,
+                  "encode_algorithmic_bytes": alg_h,
+                  "kernels": {nm: round(v, 5) for nm, v in hk.items()},
                   # its k_stats hashes every exponent word twice: VALU-bound
-                  "alu_roofline": alu_roofline("k_stats<true, true>", "k_stats_hash", args.workload, B, hk[0])}
+                  "alu_roofline": alu_roofline("k_stats<true, true>", "k_stats_hash", args.workload, B,
+                                               hk["k_stats"])}
         del h_pristine, h_cache, out_h
+
     # rANS modes: the same input and caches, the coded exponents range-ANS
     # coded instead of the 3-bit code; encode and decode timed like pass 3,
     # each kernel once more with events; the round trip checked on the GPU.
-    rans = None
+    log("rANS modes")
     rcap, rwsz = ciera.rans_max_encoded_size(n, B), ciera.rans_workspace_size(n, B)
     out_r = torch.empty(rcap, dtype=torch.uint8, device=dev)
     ws_r = torch.empty(rwsz, dtype=torch.uint8, device=dev)
@@ -457,8 +574,8 @@ def main() -> int:
         enc_r = ciera.bind("zip3_encode_rans", xs[k_iso], n, out_r, rcap, ws_r, rwsz, size_r, stream=stream)
     else:
         enc_r = ciera.bind("ciera_encode_rans", xs[k_iso], n, B, send, out_r, rcap, ws_r, rwsz, size_r, stream=stream)
-    if mode != "zip3":
-        send.copy_(e_prev)
+    if restore_s is not None:
+        restore_s()
     enc_r()
     torch.cuda.synchronize()
     assert ciera.ciera_read_error(ws_r) == 0
@@ -467,18 +584,18 @@ def main() -> int:
         dec_r = ciera.bind("zip3_decode_rans", out_r, szr, y_r, n, ws_d, wsz, stream=stream)
     else:
         dec_r = ciera.bind("ciera_decode_rans", out_r, szr, y_r, n, B, recv, ws_d, wsz, stream=stream)
-    r_enc, r_enc_min = isolated(enc_r, send)
-    r_dec, r_dec_min = isolated(dec_r, recv)
+    r_enc, r_enc_min = gpu.isolated(enc_r, restore_s)
+    r_dec, r_dec_min = gpu.isolated(dec_r, restore_r)
     assert ciera.ciera_read_error(ws_r) == 0 and ciera.ciera_read_error(ws_d) == 0
     r_ok = bool(torch.equal(y_r, xs[k_iso]))
     evr = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(4)]
            for _ in range(K)]
     ciera.ciera_time_kernels([pr for row in evr for pr in row], stream=stream)
     for i in range(K):
-        if mode != "zip3":
-            send.copy_(e_prev)
-            recv.copy_(e_prev)
-        torch.sum(sweep, dim=0, out=sweep_out)
+        if restore_s is not None:
+            restore_s()
+            restore_r()
+        torch.sum(gpu.sweep, dim=0, out=gpu.sweep_out)
         enc_r()
         dec_r()
     torch.cuda.synchronize()
@@ -487,6 +604,9 @@ def main() -> int:
     rans = {"encode_ms": round(r_enc, 5), "encode_min_ms": round(r_enc_min, 5),
             "decode_ms": round(r_dec, 5), "decode_min_ms": round(r_dec_min, 5),
             "stream_bytes": szr, "roundtrip_ok": r_ok,
+            "compression_ratio": round(2 * n / szr, 4),
+            "encode_GBps": round(2 * n / (r_enc * 1e-3) / 1e9, 2),
+            "decode_GBps": round(2 * n / (r_dec * 1e-3) / 1e9, 2),
             "kernels": {"k_stats": round(rk[0], 5), "k_rans_enc": round(rk[1], 5), "k_rans_finish": round(rk[2], 5),
                         "k_rans_dec": round(rk[3], 5)},
             # the coders are bound by their dependent steps, not by HBM:
@@ -494,7 +614,6 @@ def main() -> int:
             "alu_roofline": [alu_roofline("k_rans_enc", "k_rans_enc", args.workload, B, rk[1]),
                              alu_roofline("k_rans_dec", "k_rans_dec", args.workload, B, rk[3])]}
     del out_r, ws_r, y_r
-    del sweep
 
     if args.copy_probe:
         a = torch.full((args.copy_probe << 19,), 3, dtype=torch.int16, device=dev)
@@ -503,13 +622,15 @@ def main() -> int:
             torch.bitwise_not(a, out=b)
         torch.cuda.synchronize()
         del a, b
+    del out, ws_e, ws_d, y, xs, send, recv, e_prev
+    torch.cuda.empty_cache()
     bw_copy, bw_read = measured_bandwidth(torch, dev)
 
     in_bytes = 2 * n
     value = in_bytes * K / wall / 1e9
     enc_avg = sum(enc_ms) / K
     dec_avg = sum(dec_ms) / K
-    stream_bytes = sizes[1 if mode != "zip3" else 0]
+    stream_bytes = sizes[k_iso]
     ratio = in_bytes / stream_bytes
 
     # Algorithmic bytes per launch of each streaming kernel: what the method
@@ -517,15 +638,12 @@ def main() -> int:
     # exponents of changed blocks); k_write reads x and writes the stream;
     # k_decode reads the stream and writes y (+ the receiver cache: read for
     # unchanged blocks, written for changed ones, n bytes in total).
-    changed_vals = 0
-    if mode != "zip3":
-        changed_vals = changed_values(pair[0], pair[1], B)
     alg = {
         "k_stats": in_bytes + (n + changed_vals if mode != "zip3" else 0),
         "k_write": in_bytes + stream_bytes,
         "k_decode": stream_bytes + in_bytes + (n if mode != "zip3" else 0),
     }
-    dom = max(alg, key=lambda nm: kern_ms[nm])
+    dom = max(STREAMING, key=lambda nm: kern_ms[nm])
     dom_gbps = alg[dom] / (kern_ms[dom] * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(dom_gbps, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
@@ -536,35 +654,28 @@ def main() -> int:
     for nm, by in alg.items():
         kernels[nm]["algorithmic_bytes"] = by
         kernels[nm]["GBps"] = round(by / (kern_ms[nm] * 1e-3) / 1e9, 1)
+        kernels[nm]["frac_of_hbm_peak"] = round(by / (kern_ms[nm] * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)
 
     alg_enc = alg["k_stats"] + alg["k_write"]
     alg_dec = alg["k_decode"]
-    if hashed is not None:
-        nb = -(-n // B)
-        # k_stats reads x and the hash cache and rewrites the changed blocks' hashes
-        alg_h = in_bytes + hashed["cache_bytes"] + 16 * (changed_vals // B) + alg["k_write"]
-        hashed["encode_GBps"] = round(in_bytes / (hashed["encode_ms"] * 1e-3) / 1e9, 2)
-        hashed["encode_algorithmic_bytes"] = alg_h
-        hashed["encode_frac_of_measured_copy"] = round(alg_h / (hashed["encode_ms"] * 1e-3) / 1e9 / bw_copy, 4)
-        hashed["blocks"] = nb
-    rans["compression_ratio"] = round(in_bytes / rans["stream_bytes"], 4)
-    rans["encode_GBps"] = round(in_bytes / (rans["encode_ms"] * 1e-3) / 1e9, 2)
-    rans["decode_GBps"] = round(in_bytes / (rans["decode_ms"] * 1e-3) / 1e9, 2)
     iso = {"method": "each call alone, MALL swept by a 1 GiB read before it; median (min) of K calls",
            "encode_ms": round(enc_iso, 5), "encode_min_ms": round(enc_iso_min, 5),
            "encode_GBps": round(in_bytes / (enc_iso * 1e-3) / 1e9, 2),
            "encode_algorithmic_bytes": alg_enc,
+           "encode_frac_of_hbm_peak": round(alg_enc / (enc_iso * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
            "encode_frac_of_measured_copy": round(alg_enc / (enc_iso * 1e-3) / 1e9 / bw_copy, 4),
            "decode_ms": round(dec_iso, 5), "decode_min_ms": round(dec_iso_min, 5),
            "decode_GBps": round(in_bytes / (dec_iso * 1e-3) / 1e9, 2),
            "decode_algorithmic_bytes": alg_dec,
-           "decode_frac_of_measured_copy": round(alg_dec / (dec_iso * 1e-3) / 1e9 / bw_copy, 4)}
+           "decode_frac_of_hbm_peak": round(alg_dec / (dec_iso * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "decode_frac_of_measured_copy": round(alg_dec / (dec_iso * 1e-3) / 1e9 / bw_copy, 4),
+           "decode_roundtrip_ok": iso_roundtrip}
     # The same fractions with the bytes the HBM counters saw (FETCH_SIZE +
     # WRITE_SIZE per launch, from the traffic summaries taken on this kernel
     # source), null where no such record exists.
-    cnt = {nm: load_traffic(nm, args.workload, B) for nm in ("k_stats", "k_plan", "k_write", "k_decode")}
-    if all(v is not None for v in cnt.values()):
-        c_enc = cnt["k_stats"] + cnt["k_plan"] + cnt["k_write"]
+    cnt = {nm: load_traffic(nm, args.workload, B) for nm in ENC_KERNELS + DEC_KERNELS}
+    if all(cnt[nm] is not None for nm in STREAMING):
+        c_enc = sum(cnt[nm] or 0 for nm in ENC_KERNELS)
         iso["encode_counted_bytes"] = c_enc
         iso["encode_frac_counted"] = round(c_enc / (enc_iso * 1e-3) / 1e9 / bw_copy, 4)
         iso["decode_counted_bytes"] = cnt["k_decode"]
@@ -574,35 +685,59 @@ def main() -> int:
 
     # single-read: x once [+ the cache, read, and its changed values rewritten] + the stream
     alg_sr = in_bytes + (n + changed_vals if mode != "zip3" else 0) + stream_bytes
-    if single is None:
-        single = {}
-    single.update({"isolated_ms": round(sr_iso, 5), "isolated_min_ms": round(sr_iso_min, 5),
-                   "isolated_GBps": round(in_bytes / (sr_iso * 1e-3) / 1e9, 2),
-                   "isolated_algorithmic_bytes": alg_sr,
-                   "isolated_frac_of_measured_copy": round(alg_sr / (sr_iso * 1e-3) / 1e9 / bw_copy, 4),
-                   "isolated_stream_equal_to_full_encode": sr_same})
+    alg_w1 = in_bytes + (n + changed_vals if mode != "zip3" else 0) + stream_bytes
+    single = {"isolated_ms": round(sr_iso, 5), "isolated_min_ms": round(sr_iso_min, 5),
+              "isolated_GBps": round(in_bytes / (sr_iso * 1e-3) / 1e9, 2),
+              "isolated_algorithmic_bytes": alg_sr,
+              "isolated_frac_of_hbm_peak": round(alg_sr / (sr_iso * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+              "isolated_frac_of_measured_copy": round(alg_sr / (sr_iso * 1e-3) / 1e9 / bw_copy, 4),
+              "isolated_stream_equal_to_full_encode": sr_same,
+              "speedup_vs_two_pass_isolated": round(enc_iso / sr_iso, 3),
+              "kernels": {"k_prep1": {"avg_ms": round(prep_ms, 5)},
+                          "k_write1": {"avg_ms": round(write1_ms, 5), "algorithmic_bytes": alg_w1,
+                                       "GBps": round(alg_w1 / (write1_ms * 1e-3) / 1e9, 1),
+                                       "frac_of_hbm_peak": round(alg_w1 / (write1_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+                                                                 4)}}}
+    if hashed is not None:
+        hashed["encode_frac_of_measured_copy"] = round(hashed["encode_algorithmic_bytes"] /
+                                                       (hashed["encode_ms"] * 1e-3) / 1e9 / bw_copy, 4)
 
+    # The CPU oracle: the timed encode's stream against the oracle's (same
+    # input, same cache), then the oracle timed on one thread and on all the
+    # host's cores.
     cpu = None
+    exact = None
+    threads = host_threads()
     if not args.no_cpu_baseline:
         import oracle
-        x_host = pair[1] if mode != "zip3" else pair[0]
-        t = time.perf_counter()
-        if mode == "zip3":
-            s_o, _ = oracle.zip3_encode(x_host)
-        else:
-            c = ((pair[0] >> 7) & 0xFF).astype(np.uint8)
-            s_o, _ = oracle.ciera_encode(x_host, B, c)
-        t_enc = time.perf_counter() - t
-        t = time.perf_counter()
-        if mode == "zip3":
-            oracle.zip3_decode(s_o, n)
-        else:
-            oracle.ciera_decode(s_o, n, B, ((pair[0] >> 7) & 0xFF).astype(np.uint8))
-        t_dec = time.perf_counter() - t
-        cpu = {"value": round(in_bytes / (t_enc + t_dec) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-               "sample": f"the full {n}-value tensor, one encode + one decode (scalar C oracle, 1 thread)",
-               "encode_GBps": round(in_bytes / t_enc / 1e9, 4), "decode_GBps": round(in_bytes / t_dec / 1e9, 4),
-               "host_cpus": os.cpu_count()}
+        log(f"oracle: single thread and {threads} threads on the full tensor")
+        prev = ((pair[0] >> 7) & 0xFF).astype(np.uint8) if mode != "zip3" else None
+        o_stream, legs = oracle_legs(oracle, np, pair[k_iso], B, prev, threads)
+        exact = g_stream.tobytes() == o_stream.tobytes()
+        a = legs["all_cores"]
+        cpu = {"value": a["GBps"], "unit": "GB/s", "cores": a["threads"], "kind": "oracle",
+               "sample": f"the full {n}-value tensor, one encode + one decode: the scalar C oracle's "
+                         f"chunk-parallel driver on {a['threads']} threads (single_thread: the same on one)",
+               "encode_GBps": a["encode_GBps"], "decode_GBps": a["decode_GBps"],
+               "single_thread": legs["single"], "host_cpus": os.cpu_count()}
+        del o_stream
+    del g_stream
+
+    configs = []
+    spec = args.configs
+    if spec == "auto":
+        spec = "1,2,3:64,3:1024,4" if args.workload == 5 and not args.no_cpu_baseline else ""
+    if spec:
+        import oracle
+        for item in spec.split(","):
+            w, _, b = item.partition(":")
+            w = int(w)
+            c = measure_config(gpu, oracle, np, wl, w, int(b) if b else DEFAULT_B[w], threads)
+            c["encode_frac_of_measured_copy"] = round(c["encode_algorithmic_bytes"] / (c["encode_ms"] * 1e-3) / 1e9 /
+                                                      bw_copy, 4)
+            c["decode_frac_of_measured_copy"] = round(c["decode_algorithmic_bytes"] / (c["decode_ms"] * 1e-3) / 1e9 /
+                                                      bw_copy, 4)
+            configs.append(c)
 
     line = {
         "metric": "codec encode/decode GB/s of BF16 input (% HBM roofline) + compression ratio",
@@ -618,6 +753,7 @@ def main() -> int:
         "dtype": "u16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload].format(B=B), "n": n, "B": B, "mode": mode},
+        "bit_exact_vs_oracle": exact,
         "encode_GBps": round(in_bytes / (enc_avg * 1e-3) / 1e9, 2),
         "decode_GBps": round(in_bytes / (dec_avg * 1e-3) / 1e9, 2),
         "encode_ms": round(enc_avg, 5),
@@ -634,9 +770,15 @@ def main() -> int:
         "bw_measured_GBps": {"copy": round(bw_copy, 1), "read": round(bw_read, 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "configs": configs,
         "source_hash": source_hash(),
     }
     print(json.dumps(line), flush=True)
+    bad = exact is False or not iso_roundtrip or any(not c["bit_exact_vs_oracle"] or not c["roundtrip_ok"]
+                                                    for c in configs)
+    if bad:
+        log("FAILED: a GPU stream differs from the oracle's or a round trip failed")
+        return 1
     return 0
 
 
