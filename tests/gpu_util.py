@@ -39,6 +39,15 @@ def _check_guards(host, n, what):
     assert (host[GUARD + n:] == CANARY).all(), f"{what}: write after the buffer"
 
 
+def oracle_encode(x, B=0, cache=None, e0=-1):
+    """The oracle's 3-bit encode; from 2^24 values on, its chunk-parallel
+    driver on the host's cores (the same bytes as the single-threaded
+    encode, which the CPU tests pin)."""
+    import os
+    threads = min(16, os.cpu_count() or 1) if x.size >= (1 << 24) else 0
+    return oracle.encode(x, B, cache, e0, threads=threads)
+
+
 def window_tie(x, e0_a, e0_b):
     """Where the GPU (FP64 sums in its own order) and the oracle (exact) may
     pick different window bases: the exact variance lies within a relative
@@ -135,12 +144,12 @@ def check_encode(x, B=0, cache=None, e0=-1, stream=None, plan_groups=0):
     window base.  Returns (stream, oracle stats)."""
     g_stream, g_cache = gpu_encode(x, B, cache, e0, stream, plan_groups)
     o_cache = cache.copy() if B else None
-    o_stream, o_st = oracle.encode(x, B, o_cache, e0)
+    o_stream, o_st = oracle_encode(x, B, o_cache, e0)
     if g_stream.tobytes() != o_stream.tobytes() and e0 < 0 and int(g_stream[7]) != o_st["E0"]:
         assert window_tie(x, int(g_stream[7]), o_st["E0"]), \
             f"window base differs away from a threshold: gpu {g_stream[7]} oracle {o_st['E0']}"
         o_cache = cache.copy() if B else None
-        o_stream, o_st = oracle.encode(x, B, o_cache, int(g_stream[7]))
+        o_stream, o_st = oracle_encode(x, B, o_cache, int(g_stream[7]))
     if g_stream.tobytes() != o_stream.tobytes():
         i = _first_diff(g_stream, o_stream)
         raise AssertionError(f"stream differs from the oracle at byte {i} of {o_stream.size} "
@@ -193,7 +202,7 @@ def check_encode_e0(x, e0):
     src = torch.tensor([e0], dtype=torch.uint8, device="cuda")
     g, st = gpu_encode_e0(x, src)
     assert st == 0, f"single-read encode reported status {st}"
-    o, _ = oracle.encode(x, 0, None, e0)
+    o, _ = oracle_encode(x, 0, None, e0)
     if g.tobytes() != o.tobytes():
         i = _first_diff(g, o)
         raise AssertionError(f"single-read stream differs from the oracle at byte {i} of {o.size} "
@@ -237,7 +246,7 @@ def check_encode_e0_ciera(x, B, cache, e0):
     g, st, gc = gpu_encode_e0_ciera(x, B, cache.copy(), src)
     assert st == 0, f"single-read ciera encode reported status {st}"
     oc = cache.copy()
-    o, _ = oracle.encode(x, B, oc, e0)
+    o, _ = oracle_encode(x, B, oc, e0)
     if g.tobytes() != o.tobytes():
         i = _first_diff(g, o)
         raise AssertionError(f"single-read ciera stream differs from the oracle at byte {i} of {o.size} "
@@ -284,11 +293,11 @@ def check_encode_hashed(x, B, prev_exps):
     hc = oracle.block_hashes(exps_as_bf16(prev_exps), B)
     g, hc_after = gpu_encode_hashed(x, B, hc)
     o_cache = np.ascontiguousarray(prev_exps, dtype=np.uint8).copy()
-    o, st = oracle.encode(x, B, o_cache, -1)
+    o, st = oracle_encode(x, B, o_cache, -1)
     if g.tobytes() != o.tobytes() and int(g[7]) != st["E0"]:
         assert window_tie(x, int(g[7]), st["E0"]), f"window base: gpu {g[7]} oracle {st['E0']}"
         o_cache = np.ascontiguousarray(prev_exps, dtype=np.uint8).copy()
-        o, st = oracle.encode(x, B, o_cache, int(g[7]))
+        o, st = oracle_encode(x, B, o_cache, int(g[7]))
     if g.tobytes() != o.tobytes():
         i = _first_diff(g, o)
         raise AssertionError(f"hash-sender stream differs from the oracle at byte {i} of {o.size} "

@@ -7,7 +7,8 @@ hold the oracle's block hashes of the new tensor."""
 import numpy as np
 import pytest
 
-from gpu_util import check_encode_hashed, check_roundtrip, exps, gpu_encode, gpu_encode_hashed, require_gpu, say
+from gpu_util import (check_encode_hashed, check_roundtrip, exps, gpu_encode, gpu_encode_hashed, oracle_encode,
+                      require_gpu, say)
 from lossless_bf16_tensor_exp_amd import workloads as wl
 
 import oracle
@@ -75,19 +76,20 @@ def test_hash_sender_chain_equals_exact_cache_chain(B):
 
 
 def test_hash_sender_deepseek_like_layer():
-    """Workload 4 (71,368,704 values, B = 128), two iterations: the hash
-    sender's stream equals the exact sender's, and its cache the oracle's
-    block hashes."""
-    d = wl.workload4(iterations=2)
-    x0, x1, x2 = d["iters"][:3]
+    """Workload 4 (71,368,704 values, B = 128), the whole ten-iteration
+    chain from a zeroed hash cache: each stream equals the oracle's
+    exact-cache encode of that iteration, and the hash cache after each
+    equals the oracle's block hashes of the tensor just sent."""
+    d = wl.workload4()
+    it = d["iters"]
     B = 128
-    say(f"deepseek-like n={x0.size}")
-    hc = oracle.block_hashes(x0, B)
-    g, hc = gpu_encode_hashed(x1, B, hc)
-    e, _ = gpu_encode(x1, B, exps(x0))
-    assert g.tobytes() == e.tobytes()
-    assert np.array_equal(hc, oracle.block_hashes(x1, B))
-    g2, hc = gpu_encode_hashed(x2, B, hc)
-    e2, _ = gpu_encode(x2, B, exps(x1))
-    assert g2.tobytes() == e2.tobytes()
-    assert np.array_equal(hc, oracle.block_hashes(x2, B))
+    say(f"deepseek-like n={it[0].size} iterations={len(it) - 1}")
+    hc = np.zeros((-(-it[0].size // B), 2), dtype=np.uint64)
+    prev = np.zeros(it[0].size, dtype=np.uint8)
+    for t, x in enumerate(it):
+        g, hc = gpu_encode_hashed(x, B, hc)
+        o, st = oracle_encode(x, B, prev.copy())
+        assert g.tobytes() == o.tobytes(), t
+        assert np.array_equal(hc, oracle.block_hashes(x, B)), t
+        prev = exps(x)
+        say(f"  iter {t} changed={st['changed_blocks']}")
