@@ -305,6 +305,17 @@ __device__ inline void store_bytes8(uint8_t* __restrict__ p, uint32_t cnt, uint2
   }
 }
 
+// Cache rewrite by whole lines: m is the wave's ballot of "this lane's unit
+// differs from the cache", lane l holding unit u0 + l of 64 consecutive units
+// (u0 a multiple of 64), so lanes 16g .. 16g + 15 cover one aligned 128-byte
+// line of the cache.  Every lane of a line with some differing unit stores
+// its 8 bytes: HBM then sees whole lines.  Stores of only the differing
+// units' 8 bytes leave lines partly written; on the 10^9-value stress buffer
+// (1 % exponent flips, about 8 % of units differing) the statistics pass
+// took 756 us with those and 733 us with whole lines, although it then
+// writes 0.72 GB instead of 0.31 GB.
+__device__ inline bool line_has_change(uint64_t m) { return ((m >> (lane_id() & 48u)) & 0xFFFFu) != 0u; }
+
 // Exponent fields as 16-bit lanes: bits 0..7 = exponent of the low value,
 // bits 16..23 = exponent of the high value.
 __device__ inline uint32_t exp_pair(uint32_t w) { return (w >> 7) & 0x00FF00FFu; }
@@ -640,7 +651,9 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
     const uint32_t u = pu0 + j * kPartThreads + tid;
-    bool diff = false;
+    bool diff = false, live = false;
+    uint32_t ucnt = 0u;
+    uint2 ue = make_uint2(0u, 0u);
     if (full || u < nunits) {
       const uint32_t cnt = full ? 8u : min(8u, nc - 8u * u);
       if (cnt == 8u) {
@@ -663,11 +676,10 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
         if (kHash) {
           reinterpret_cast<uint64_t*>(s_hist)[j * kPartThreads + tid] = ((uint64_t(e.y) << 32) | e.x) & keep;
         } else {
-          const uint64_t d = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
-          if (d) {
-            store_bytes8(cache + start + 8ull * u, cnt, e);
-            diff = true;
-          }
+          diff = (((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep) != 0u;
+          live = true;
+          ucnt = cnt;
+          ue = e;
         }
       }
     } else if (kHash) {
@@ -676,6 +688,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     if (kCiera && !kHash) {
       const uint64_t m = __ballot(diff);
       if (m != 0u) {
+        if (live && line_has_change(m)) store_bytes8(cache + start + 8ull * u, ucnt, ue);
         // first block of the wave's units, relative to the part
         const uint32_t lbw = ((8u * (pu0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
         uint32_t bits = 0;
@@ -1738,18 +1751,17 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     for (uint32_t j = 0; j < kUPT; j++) {
       const uint32_t u = pu0 + j * kPartThreads + tid;
       bool diff = false;
+      uint32_t cnt = 0u;
+      uint2 e = make_uint2(0u, 0u);
       if (u < nunits) {
-        const uint32_t cnt = min(8u, nc - 8u * u);
-        const uint2 e = unit_exponents(v[j]);
+        cnt = min(8u, nc - 8u * u);
+        e = unit_exponents(v[j]);
         const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
-        const uint64_t d = ((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep;
-        if (d) {
-          store_bytes8(cache + start + 8ull * u, cnt, e);
-          diff = true;
-        }
+        diff = (((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep) != 0u;
       }
       const uint64_t m = __ballot(diff);
       if (m != 0u) {
+        if (u < nunits && line_has_change(m)) store_bytes8(cache + start + 8ull * u, cnt, e);
         const uint32_t lbw = (8u * (j * kPartThreads + 64u * wave)) >> lb;  // the wave's first block in the part
         uint32_t bits = 0;
         for (uint32_t k = 0; k < 64u / L; k++) bits |= ((m >> (k * L)) & gmask) ? (1u << k) : 0u;
