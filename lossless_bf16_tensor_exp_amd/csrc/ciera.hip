@@ -66,7 +66,7 @@ constexpr uint32_t kPartUnits = kPartThreads * kUPT;  // 2048 units = 16384 valu
 static_assert(kPartUnits * kParts == kUnitsPerChunk, "parts tile a chunk");
 static_assert(kUPT * kPartWaves <= 64u, "one scan entry per lane");
 constexpr uint32_t kStage = kPartUnits + 16u;  // LDS bytes per staged plane
-constexpr uint32_t kPartEscStage = 4096u;      // escape bytes staged in LDS per part
+constexpr uint32_t kPartEscStage = 16384u + 32u;  // a part's escapes (at most its 16,384 values) staged in LDS
 constexpr uint32_t kBins = 256u;               // exponent histogram bins
 constexpr uint32_t kHistCopies = 16u;          // interleaved LDS copies (by lane) to spread atomics
 static_assert(kPartThreads == kBins, "k_stats stores one bin per thread");
@@ -315,6 +315,50 @@ __device__ inline void store_bytes8(uint8_t* __restrict__ p, uint32_t cnt, uint2
 // took 756 us with those and 733 us with whole lines, although it then
 // writes 0.72 GB instead of 0.31 GB.
 __device__ inline bool line_has_change(uint64_t m) { return ((m >> (lane_id() & 48u)) & 0xFFFFu) != 0u; }
+
+// Bytes sh .. sh + 15 of the 32 bytes p, q (p first), sh < 16.
+__device__ inline uint4 shift_bytes(const uint4& p, const uint4& q, uint32_t sh) {
+  const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
+  const uint32_t r = sh & 3u;
+  uint32_t o[4];
+  switch (sh >> 2) {  // constant indices in each case (no private array)
+    case 0:
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r);
+      break;
+    case 1:
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 2], w[i + 1], r);
+      break;
+    case 2:
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 3], w[i + 2], r);
+      break;
+    default:
+#pragma unroll
+      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 4], w[i + 3], r);
+      break;
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// Copies len bytes from the 16-byte-aligned LDS buffer src to global memory
+// at dst with the nthreads threads of a workgroup: aligned 16-byte stores
+// over the middle (each built from the two aligned LDS blocks that cover it),
+// byte stores only for the unaligned head and tail, so that HBM sees whole
+// lines.  src must have 16 readable bytes past len.
+__device__ inline void lds_to_global(uint8_t* __restrict__ dst, const uint8_t* src, uint32_t len, uint32_t tid,
+                                     uint32_t nthreads) {
+  const uint32_t head = min(len, uint32_t((16u - (reinterpret_cast<uintptr_t>(dst) & 15u)) & 15u));
+  const uint32_t body = (len - head) / 16u;
+  for (uint32_t i = tid; i < head; i += nthreads) dst[i] = src[i];
+  for (uint32_t i = tid; i < body; i += nthreads) {
+    const uint32_t o = head + 16u * i;
+    const uint4* a = reinterpret_cast<const uint4*>(src + (o & ~15u));
+    *reinterpret_cast<uint4*>(dst + o) = shift_bytes(a[0], a[1], o & 15u);
+  }
+  for (uint32_t i = head + 16u * body + tid; i < len; i += nthreads) dst[i] = src[i];
+}
 
 // Exponent fields as 16-bit lanes: bits 0..7 = exponent of the low value,
 // bits 16..23 = exponent of the high value.
@@ -1316,6 +1360,25 @@ __device__ inline void stage_bitmap(uint32_t w, uint32_t* s_bits, uint32_t* s_ra
 // One part of a chunk.  Its stream offset, the escapes before it in its chunk
 // and the chunk's escape total all come from k_plan, so the part waits on
 // nothing: load, code, write.
+// A thread's escapes (the raw exponent bytes of its units' code-0 values) to
+// the part's LDS staging at their ranks base[j], in value order.
+__device__ inline void stage_escapes(const Unit (&v)[kUPT], const uint32_t (&emask)[kUPT], const uint32_t (&base)[kUPT],
+                                     uint8_t* s_esc) {
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    uint32_t em = emask[j];
+    if (em) {
+      const uint2 e = unit_exponents(v[j]);
+      uint32_t at = base[j];
+      while (em) {
+        const uint32_t k = __builtin_ctz(em);
+        em &= em - 1u;
+        s_esc[at++] = uint8_t(byte_of(e, k));
+      }
+    }
+  }
+}
+
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restrict__ x, uint64_t n,
                                                         uint32_t log2B, uint8_t* __restrict__ out,
@@ -1446,36 +1509,10 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   }
   // escapes of this part: [esc_before, esc_before + pesc) of the chunk's section
   const uint64_t esc_at = g.esc + esc_before;
-  if (esc_ok && pesc <= kPartEscStage) {
-#pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      uint32_t em = emask[j];
-      if (em) {
-        const uint2 e = unit_exponents(v[j]);
-        uint32_t at = base[j];
-        while (em) {
-          const uint32_t k = __builtin_ctz(em);
-          em &= em - 1u;
-          s_esc[at++] = uint8_t(byte_of(e, k));
-        }
-      }
-    }
+  if (esc_ok) {
+    stage_escapes(v, emask, base, s_esc);
     __syncthreads();
-    for (uint32_t i = tid; i < pesc; i += kPartThreads) out[esc_at + i] = s_esc[i];
-  } else if (esc_ok) {
-#pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      uint32_t em = emask[j];
-      if (em) {
-        const uint2 e = unit_exponents(v[j]);
-        uint64_t at = esc_at + base[j];
-        while (em) {
-          const uint32_t k = __builtin_ctz(em);
-          em &= em - 1u;
-          out[at++] = uint8_t(byte_of(e, k));
-        }
-      }
-    }
+    lds_to_global(out + esc_at, s_esc, pesc, tid, kPartThreads);
   }
   if (last_part) {
     // zero padding after each section's data, and the bitmap
@@ -1918,36 +1955,10 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   }
   // escapes of this part: [esc_before, esc_before + pesc) of the chunk's section
   const uint64_t esc_at = g.esc + esc_before;
-  if (coded_part && pesc <= kPartEscStage) {
-#pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      uint32_t em = emask[j];
-      if (em) {
-        const uint2 e = unit_exponents(v[j]);
-        uint32_t at = base[j];
-        while (em) {
-          const uint32_t k = __builtin_ctz(em);
-          em &= em - 1u;
-          s_esc[at++] = uint8_t(byte_of(e, k));
-        }
-      }
-    }
+  if (coded_part) {
+    stage_escapes(v, emask, base, s_esc);
     __syncthreads();
-    for (uint32_t i = tid; i < pesc; i += kPartThreads) out[esc_at + i] = s_esc[i];
-  } else if (coded_part) {
-#pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      uint32_t em = emask[j];
-      if (em) {
-        const uint2 e = unit_exponents(v[j]);
-        uint64_t at = esc_at + base[j];
-        while (em) {
-          const uint32_t k = __builtin_ctz(em);
-          em &= em - 1u;
-          out[at++] = uint8_t(byte_of(e, k));
-        }
-      }
-    }
+    lds_to_global(out + esc_at, s_esc, pesc, tid, kPartThreads);
   }
   if (kCiera) {
     // the chunk's bitmap: with B <= 512 each part writes its own words; else
@@ -2474,31 +2485,6 @@ __device__ inline uint32_t rans_push(uint32_t x, const RansEnt& e) {
   return uint32_t(__mul24(int32_t(q), e.nf)) + ((q << 12) + x + (e.cf & 0xFFFFu));
 }
 
-// Bytes sh .. sh + 15 of the 32 bytes p, q (p first), sh < 16.
-__device__ inline uint4 shift_bytes(const uint4& p, const uint4& q, uint32_t sh) {
-  const uint32_t w[8] = {p.x, p.y, p.z, p.w, q.x, q.y, q.z, q.w};
-  const uint32_t r = sh & 3u;
-  uint32_t o[4];
-  switch (sh >> 2) {  // constant indices in each case (no private array)
-    case 0:
-#pragma unroll
-      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 1], w[i], r);
-      break;
-    case 1:
-#pragma unroll
-      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 2], w[i + 1], r);
-      break;
-    case 2:
-#pragma unroll
-      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 3], w[i + 2], r);
-      break;
-    default:
-#pragma unroll
-      for (int i = 0; i < 4; i++) o[i] = __builtin_amdgcn_alignbyte(w[i + 4], w[i + 3], r);
-      break;
-  }
-  return make_uint4(o[0], o[1], o[2], o[3]);
-}
 
 template <bool kCiera>
 __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __restrict__ x, uint64_t n,
