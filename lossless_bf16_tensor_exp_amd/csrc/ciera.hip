@@ -1543,6 +1543,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
 // CIERA_ERR_INTERNAL.
 constexpr uint64_t kFlagSize = 1ull << 62;  // look-back only: a predecessor's size, not a prefix
 constexpr uint64_t kFlagIncl = 2ull << 62;
+constexpr uint64_t kFlagFail = 3ull << 62;  // the chunk's last part gave up a wait: no offset follows
 constexpr uint64_t kValMask = (1ull << 62) - 1u;
 constexpr uint32_t kBadE0 = ~0u;
 constexpr uint32_t kDoneShift = 40u;           // ctrl->done_esc: chunks << 40 | escapes
@@ -1659,30 +1660,20 @@ __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks
 }
 
 // Stream bytes of the chunks before c (wave 0, 64 predecessors at a time).
-// A predecessor contributes its inclusive prefix if its last part has
-// published one (and the search ends there), else its size, known as soon as
-// its four parts have published their words (every chunk before the last
-// holds 65,536 values).  Returns false if a wait did not end.
-template <bool kCiera>
-__device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint32_t log2B, uint64_t& pb) {
+// A predecessor's status word holds its inclusive prefix once its last part
+// has looked back (the search ends there), else its size as soon as one of
+// its parts knows it (all four parts' counts are in), else nothing yet.
+// Returns false if a wait did not end.
+__device__ inline bool chunk_lookback(const Ws& ws, uint64_t c, uint64_t& pb) {
   const uint32_t lane = lane_id();
   pb = 0;
   int64_t top = int64_t(c) - 1;
   uint32_t spins = 0;
   while (top >= 0) {
     const int64_t k = top - int64_t(lane);
-    uint64_t st = (k >= 0) ? load_relaxed(&ws.cstat[uint64_t(k) * kCstatStride]) : kFlagIncl;
-    if (k >= 0 && (st & ~kValMask) != kFlagIncl) {
-      uint32_t w[kParts], ready = 1u;
-#pragma unroll
-      for (uint32_t q = 0; q < kParts; q++) {
-        w[q] = load_relaxed(&ws.pcount[uint64_t(k) * kPcountStride + q]);
-        ready &= w[q] >> 31;
-      }
-      const ChunkCounts cc = chunk_counts(w, kCiera, log2B);
-      st = ready ? (kFlagSize | chunk_bytes(kChunk, kCiera, log2B, cc.nch, cc.esc)) : 0u;
-    }
+    const uint64_t st = (k >= 0) ? load_relaxed(&ws.cstat[uint64_t(k) * kCstatStride]) : kFlagIncl;
     const uint64_t flag = st & ~kValMask;
+    if (__ballot(flag == kFlagFail) != 0u) return false;
     if (__ballot(flag == 0u) != 0u) {
       if (++spins > ws.spin_limit) return false;
       __builtin_amdgcn_s_sleep(1);
@@ -1879,12 +1870,36 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     const uint64_t tbl = table_end(nchunks);
     uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
     uint64_t pb = 0;
-    // every part looks back for the chunk's offset; the last part publishes it
-    if (!err && !chunk_lookback<kCiera>(ws, c, log2B, pb)) err = CIERA_ERR_INTERNAL;
+    uint64_t* cst = &ws.cstat[c * kCstatStride];
+    // Every part publishes the chunk's size (the same value; the maximum
+    // keeps an inclusive prefix that is already there, its flag being the
+    // larger).  The last part looks back for the chunk's offset and publishes
+    // the inclusive prefix; the others wait for it on the chunk's own word.
+    if (!err && lane == 0u)
+      atomicMax(reinterpret_cast<unsigned long long*>(cst), (unsigned long long)(kFlagSize | size));
+    if (last_part) {
+      if (!err && !chunk_lookback(ws, c, pb)) err = CIERA_ERR_INTERNAL;
+    } else if (!err) {
+      // The last part publishes the inclusive prefix, or kFlagFail if it gave
+      // up a wait (its size may then come from incomplete counts and must not
+      // be subtracted from); a prefix below the chunk's own size is refused too.
+      uint64_t st = 0;
+      for (uint32_t spins = 0;; spins++) {
+        st = shfl_u64(load_relaxed(cst), 0u);  // lane 0's read: one decision for the wave
+        if ((st & ~kValMask) >= kFlagIncl) break;
+        if (spins > ws.spin_limit) break;
+        __builtin_amdgcn_s_sleep(1);
+      }
+      if ((st & ~kValMask) == kFlagIncl && (st & kValMask) >= size)
+        pb = (st & kValMask) - size;
+      else
+        err = CIERA_ERR_INTERNAL;
+    }
     if (last_part) {
       if (lane == 0u) {
-        // published even after a failed wait, so that no later wait lasts forever
-        store_relaxed(&ws.cstat[c * kCstatStride], kFlagIncl | (pb + size));
+        // published even after a failed wait (as a failure), so that no later
+        // wait lasts forever and no other part takes an offset from it
+        store_relaxed(cst, err ? kFlagFail : (kFlagIncl | (pb + size)));
         table[c] = tbl + pb;
         table[nchunks + 1u + c] = (uint64_t(cc.esc_before[1]) << 16) | (uint64_t(cc.esc_before[2]) << 32) |
                                   (uint64_t(cc.esc_before[3]) << 48);
