@@ -53,8 +53,11 @@ WORKLOAD_NAMES = {
     5: "stress 1e9 BF16 mixed N/t/constant + specials, 1% flips; exponent reuse B={B}",
 }
 DEFAULT_B = {1: 256, 2: 0, 3: 64, 4: 128, 5: 512}
-# the encode's kernels, in launch order, then the decode's
+# the encode's kernels, in launch order, then the decode's; a tensor of at most
+# SELF_PLAN_CHUNKS chunks is planned inside k_write (two launches)
 ENC_KERNELS = ["k_stats", "k_sums", "k_plan", "k_write"]
+ENC_KERNELS_SMALL = ["k_stats", "k_write"]
+SELF_PLAN_CHUNKS = 16
 DEC_KERNELS = ["k_decode"]
 STREAMING = ["k_stats", "k_write", "k_decode"]
 
@@ -414,8 +417,9 @@ def main() -> int:
     # Pass 2, the same K steps with every kernel timed by HIP events that the
     # runtime records at the kernel's own start and end (hipExtLaunchKernel);
     # a step launches encode's four kernels, then decode's one.
-    names = ENC_KERNELS + DEC_KERNELS
-    ne = len(ENC_KERNELS)
+    enc_names = ENC_KERNELS_SMALL if -(-n // 65536) <= SELF_PLAN_CHUNKS else ENC_KERNELS
+    names = enc_names + DEC_KERNELS
+    ne = len(enc_names)
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in names]
           for _ in range(K)]
     ciera.ciera_time_kernels([pair_ for row in ev for pair_ in row], stream=stream)
@@ -536,7 +540,7 @@ def main() -> int:
                            stream=stream)
         h_ms, h_min = gpu.isolated(enc_h, lambda: h_cache.copy_(h_pristine))
         # the same calls once more with each kernel timed
-        evk = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in ENC_KERNELS]
+        evk = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in enc_names]
                for _ in range(K)]
         ciera.ciera_time_kernels([pr for row in evk for pr in row], stream=stream)
         for i in range(K):
@@ -549,7 +553,7 @@ def main() -> int:
         szh = int(size_h.item())
         same = szh == sizes[k_iso] and bool(torch.equal(out_h[:szh], out[:szh]))
         hk = {nm: sum(evk[i][j][0].elapsed_time(evk[i][j][1]) for i in range(K)) / K
-              for j, nm in enumerate(ENC_KERNELS)}
+              for j, nm in enumerate(enc_names)}
         alg_h = 2 * n + hsz + 16 * (changed_vals // B) + 2 * n + sizes[k_iso]
         hashed = {"encode_ms": round(h_ms, 5), "encode_min_ms": round(h_min, 5),
                   "encode_GBps": round(2 * n / (h_ms * 1e-3) / 1e9, 2),
@@ -673,9 +677,9 @@ def main() -> int:
     # The same fractions with the bytes the HBM counters saw (FETCH_SIZE +
     # WRITE_SIZE per launch, from the traffic summaries taken on this kernel
     # source), null where no such record exists.
-    cnt = {nm: load_traffic(nm, args.workload, B) for nm in ENC_KERNELS + DEC_KERNELS}
+    cnt = {nm: load_traffic(nm, args.workload, B) for nm in enc_names + DEC_KERNELS}
     if all(cnt[nm] is not None for nm in STREAMING):
-        c_enc = sum(cnt[nm] or 0 for nm in ENC_KERNELS)
+        c_enc = sum(cnt[nm] or 0 for nm in enc_names)
         iso["encode_counted_bytes"] = c_enc
         iso["encode_frac_counted"] = round(c_enc / (enc_iso * 1e-3) / 1e9 / bw_copy, 4)
         iso["decode_counted_bytes"] = cnt["k_decode"]

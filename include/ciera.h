@@ -272,9 +272,10 @@ ciera_status ciera_encode_e0(const void* d_x, uint64_t n, uint32_t B, uint8_t* d
  * n_pairs (start, stop) pairs of hipEvent_t handles, created with timing
  * enabled and owned by the caller.  The next n_pairs kernel launches made by
  * the calling host thread through this library (any entry point: the
- * 3-bit encode launches three kernels and its decode one; the single-read
- * encode two; the rANS encode three and its decode one) each take the next
- * pair, which the HIP
+ * 3-bit encode launches four kernels, or two for a tensor of at most 16
+ * chunks, whose planning the write kernel does itself, unless plan_groups
+ * forces the planner; its decode one; the single-read encode two; the rANS
+ * encode three and its decode one) each take the next pair, which the HIP
  * runtime records at that kernel's start and end (hipExtLaunchKernel);
  * hipEventElapsedTime then gives the kernel's own duration.  The handles are
  * copied; a later call replaces the queue, n_pairs = 0 clears it.  Returns

@@ -108,3 +108,27 @@ def test_plan_most_groups():
     x = varied(n, 24)
     s, _ = check_encode(x)
     check_roundtrip(s, x)
+
+
+@pytest.mark.parametrize("nchunks,tail", [(1, 60000), (1, 0), (4, 777), (16, 0), (16, 1)])
+@pytest.mark.parametrize("B", [0, 64, 512, 32768])
+def test_self_planned_write_equals_the_planner(nchunks, tail, B):
+    """A tensor of at most 16 chunks is planned inside the write kernel
+    (no planner launches); the stream must equal the one the planner's path
+    writes for the same input (plan_groups = 1 forces that path), byte for
+    byte, and the oracle's."""
+    n = nchunks * C - tail
+    say(f"self-planned write n={n} B={B}")
+    rng = np.random.default_rng(nchunks * 7 + B)
+    x = varied(n, 11 + nchunks)
+    cache = None
+    if B:
+        cache = ((x >> 7) & 0xFF).astype(np.uint8)
+        cache[rng.random(n) < 0.002] ^= 1
+    s_self, c_self = gpu_encode(x, B, cache)
+    s_plan, c_plan = gpu_encode(x, B, cache, plan_groups=1)
+    assert s_self.tobytes() == s_plan.tobytes()
+    if B:
+        assert np.array_equal(c_self, c_plan)
+    check_encode(x, B, cache)
+    check_roundtrip(s_self, x, B, cache.copy() if B else None)
