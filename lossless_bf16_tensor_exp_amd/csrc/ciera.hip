@@ -1981,6 +1981,8 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   uint32_t field = 0u;
   if (kCiera) field = (B <= 512u) ? pnch : (B <= kPartValues ? s_pbits[0] : (s_pbits[0] & 1u));
   if (tid == 0) store_relaxed(&ws.pcount[c * kPcountStride + h], kPartReady | (field << kEscBits) | pesc);
+  // the escapes need no stream position: staged while the part waits for it
+  stage_escapes(v, emask, base, s_esc);
 
   // Stream position (wave 0).
   if (tid < 64u) {
@@ -2104,11 +2106,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   }
   // escapes of this part: [esc_before, esc_before + pesc) of the chunk's section
   const uint64_t esc_at = g.esc + esc_before;
-  if (coded_part) {
-    stage_escapes(v, emask, base, s_esc);
-    __syncthreads();
-    lds_to_global(out + esc_at, s_esc, pesc, tid, kPartThreads);
-  }
+  if (coded_part) lds_to_global(out + esc_at, s_esc, pesc, tid, kPartThreads);  // staged before the wait's barrier
   if (kCiera) {
     // the chunk's bitmap: with B <= 512 each part writes its own words; else
     // the last part assembles the (at most two) words, the others zero
