@@ -38,6 +38,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <type_traits>
 #include <mutex>
 #include <vector>
 
@@ -692,56 +693,65 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   uint32_t coded = kCiera ? 0u : 0xFFu;
   const uint32_t L = (B >= 512u) ? 64u : max(B / 8u, 8u);  // B >= 64 in ciera mode
   const uint64_t gmask = (L >= 64u) ? ~0ull : ((1ull << L) - 1u);
+  // One copy of the unit loop for a part of 16384 values, one for a short
+  // last part: the full copy carries no per-unit value counts.
+  auto units = [&](auto full_c) {
+    constexpr bool kF = decltype(full_c)::value;
 #pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
-    bool diff = false, live = false;
-    uint32_t ucnt = 0u;
-    uint2 ue = make_uint2(0u, 0u);
-    if (full || u < nunits) {
-      const uint32_t cnt = full ? 8u : min(8u, nc - 8u * u);
-      if (cnt == 8u) {
+    for (uint32_t j = 0; j < kUPT; j++) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
+      bool diff = false, live = false;
+      uint32_t ucnt = 0u;
+      uint2 ue = make_uint2(0u, 0u);
+      if (kF || u < nunits) {
+        const uint32_t cnt = kF ? 8u : min(8u, nc - 8u * u);
+        if (cnt == 8u) {
 #pragma unroll
-        for (int i = 0; i < 4; i++) {
-          const double lo = widen_hi(v[j].w[i] << 16) - shift;
-          const double hi = widen_hi(v[j].w[i] & 0xFFFF0000u) - shift;
-          s1 += lo;
-          s2 = fma(lo, lo, s2);
-          s1 += hi;
-          s2 = fma(hi, hi, s2);
-        }
-        nf += 8u;
-      } else {
-        stats_checked(v[j], cnt, shift, s1, s2, nf);
-      }
-      if (kCiera) {
-        const uint2 e = unit_exponents(v[j]);
-        const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
-        if (kHash) {
-          reinterpret_cast<uint64_t*>(s_hist)[j * kPartThreads + tid] = ((uint64_t(e.y) << 32) | e.x) & keep;
+          for (int i = 0; i < 4; i++) {
+            const double lo = widen_hi(v[j].w[i] << 16) - shift;
+            const double hi = widen_hi(v[j].w[i] & 0xFFFF0000u) - shift;
+            s1 += lo;
+            s2 = fma(lo, lo, s2);
+            s1 += hi;
+            s2 = fma(hi, hi, s2);
+          }
+          nf += 8u;
         } else {
-          diff = (((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep) != 0u;
-          live = true;
-          ucnt = cnt;
-          ue = e;
+          stats_checked(v[j], cnt, shift, s1, s2, nf);
+        }
+        if (kCiera) {
+          const uint2 e = unit_exponents(v[j]);
+          const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * (cnt & 7u))) - 1u);
+          if (kHash) {
+            reinterpret_cast<uint64_t*>(s_hist)[j * kPartThreads + tid] = ((uint64_t(e.y) << 32) | e.x) & keep;
+          } else {
+            diff = (((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep) != 0u;
+            live = true;
+            ucnt = cnt;
+            ue = e;
+          }
+        }
+      } else if (kHash) {
+        reinterpret_cast<uint64_t*>(s_hist)[j * kPartThreads + tid] = 0u;  // past the data
+      }
+      if (kCiera && !kHash) {
+        const uint64_t m = __ballot(diff);
+        if (m != 0u) {
+          if (live && line_has_change(m)) store_bytes8(cache + start + 8ull * u, ucnt, ue);
+          // first block of the wave's units, relative to the part
+          const uint32_t lbw = ((8u * (pu0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
+          uint32_t bits = 0;
+          for (uint32_t k = 0; k < 64u / L; k++) bits |= ((m >> (k * L)) & gmask) ? (1u << k) : 0u;
+          if (lane == 0u) atomicOr(&s_bits[lbw >> 5], bits << (lbw & 31u));
+          if (B <= 512u) coded |= ((m >> (lane & ~(L - 1u))) & gmask) ? (1u << j) : 0u;
         }
       }
-    } else if (kHash) {
-      reinterpret_cast<uint64_t*>(s_hist)[j * kPartThreads + tid] = 0u;  // past the data
     }
-    if (kCiera && !kHash) {
-      const uint64_t m = __ballot(diff);
-      if (m != 0u) {
-        if (live && line_has_change(m)) store_bytes8(cache + start + 8ull * u, ucnt, ue);
-        // first block of the wave's units, relative to the part
-        const uint32_t lbw = ((8u * (pu0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
-        uint32_t bits = 0;
-        for (uint32_t k = 0; k < 64u / L; k++) bits |= ((m >> (k * L)) & gmask) ? (1u << k) : 0u;
-        if (lane == 0u) atomicOr(&s_bits[lbw >> 5], bits << (lbw & 31u));
-        if (B <= 512u) coded |= ((m >> (lane & ~(L - 1u))) & gmask) ? (1u << j) : 0u;
-      }
-    }
-  }
+  };
+  if (full)
+    units(std::true_type{});
+  else
+    units(std::false_type{});
   if (!(__builtin_isfinite(s1) && __builtin_isfinite(s2))) {
     s1 = 0.0;
     s2 = 0.0;
@@ -1918,7 +1928,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
       if (u < nunits) {
         cnt = min(8u, nc - 8u * u);
         e = unit_exponents(v[j]);
-        const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * cnt)) - 1u);
+        const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * (cnt & 7u))) - 1u);
         diff = (((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep) != 0u;
       }
       const uint64_t m = __ballot(diff);
