@@ -1057,8 +1057,8 @@ constexpr uint32_t kRunRegs = 8u;
 // of its parts gets the block's flag (bit 0 of its bitmap word).
 template <bool kHashBlocks>
 __device__ inline uint64_t plan_chunk(uint64_t c, uint64_t n, uint32_t B, uint32_t e0, const Ws& ws,
-                                      uint64_t* __restrict__ hcache, uint32_t (&esc)[kParts], uint32_t& esc_total,
-                                      uint32_t& nch_out) {
+                                      const uint16_t* hist, uint64_t* __restrict__ hcache, uint32_t (&esc)[kParts],
+                                      uint32_t& esc_total, uint32_t& nch_out) {
   const uint32_t ppb = B > kPartValues ? B / kPartValues : 1u;  // parts per block when blocks span parts
   const uint32_t r0 = e0 & 7u;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
@@ -1070,7 +1070,7 @@ __device__ inline uint64_t plan_chunk(uint64_t c, uint64_t n, uint32_t B, uint32
   uint32_t inwin[kParts];
 #pragma unroll
   for (uint32_t h = 0; h < kParts; h++) {
-    const uint4* row = reinterpret_cast<const uint4*>(ws.hist + (c * kParts + h) * kBins) + (e0 >> 3);
+    const uint4* row = reinterpret_cast<const uint4*>(hist + (c * kParts + h) * kBins) + (e0 >> 3);
     const uint4 a = row[0], b = (e0 >> 3) < kBins / 8u - 1u ? row[1] : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
     uint32_t sum = 0;
@@ -1231,7 +1231,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
   // (2) sizes of the group's chunks, one per thread per round of 256.
   auto chunk_size = [&](uint64_t c, uint64_t& esc_out, uint64_t& nch_out) -> uint64_t {
     uint32_t esc[kParts], acc, nch;
-    const uint64_t size = plan_chunk<kHashBlocks>(c, n, B, e0, ws, hcache, esc, acc, nch);
+    const uint64_t size = plan_chunk<kHashBlocks>(c, n, B, e0, ws, ws.hist, hcache, esc, acc, nch);
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) ws.partesc[c * kParts + h] = esc[h];
     ws.chunkesc[c] = acc;
@@ -1431,7 +1431,8 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
   const uint32_t e0 = uint32_t(s_r[1]);
   uint32_t esc[kParts] = {0u, 0u, 0u, 0u}, esc_total = 0u, nch = 0u;
   uint64_t size = 0;
-  if (tid < nchunks) size = plan_chunk<false>(tid, n, B, e0, ws, nullptr, esc, esc_total, nch);
+  if (tid < nchunks)
+    size = plan_chunk<false>(tid, n, B, e0, ws, ws.hist, nullptr, esc, esc_total, nch);
   const uint64_t base = table_end(nchunks);
   uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
@@ -1543,6 +1544,9 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   uint64_t begin;
   uint32_t esc_before, esc_chunk, esc_part, e0;
   bool plan_failed = false;
+  // self-planned: the chunk's bitmap words are fetched with the plan's inputs
+  __shared__ uint32_t s_pw[kSelfPlan ? kBitmapWords : 1u];
+  const uint32_t pw_l = (kSelfPlan && kCiera && tid < kBitmapWords) ? ws.bitmap[uint64_t(c) * kBitmapWords + tid] : 0u;
   if (kSelfPlan) {
     const SelfPlan sp = self_plan(n, nchunks, c, h, wg, kCiera ? B : 0u, e0_override, out, out_size, ws);
     begin = sp.begin;
@@ -1579,9 +1583,13 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
 
   uint32_t nch = 0, nb = 0;
   if (kCiera) {
-    if (tid < 64u)
-      stage_bitmap((tid < kBitmapWords) ? chunk_bitmap_word(ws.bitmap + uint64_t(c) * kBitmapWords, tid, B) : 0u,
-                   s_bits, s_rank);
+    const uint32_t* pw = ws.bitmap + uint64_t(c) * kBitmapWords;
+    if (kSelfPlan) {
+      if (tid < kBitmapWords) s_pw[tid] = pw_l;
+      __syncthreads();
+      pw = s_pw;
+    }
+    if (tid < 64u) stage_bitmap((tid < kBitmapWords) ? chunk_bitmap_word(pw, tid, B) : 0u, s_bits, s_rank);
     nb = (nc + B - 1u) >> log2B;
   }
   __syncthreads();  // staging cleared, bitmap staged
@@ -2358,6 +2366,16 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
     if (in_size < base_off) {
       ok = 0u;
     } else {
+      // The table lies inside the stream once in_size >= base_off: its
+      // entries are read with the header, in one round trip, and used only
+      // if the header checks out.
+      const uint64_t* table = reinterpret_cast<const uint64_t*>(in + kHeader);
+      const uint64_t t_first = table[0], t_last = table[nchunks];
+      if (nchunks) {
+        begin = table[c];
+        end = table[c + 1u];
+        index = table[nchunks + 1u + c];
+      }
       const uint64_t h0 = hd[0];
       e0 = uint32_t(h0 >> 56);
       ok &= uint32_t(h0 & 0xFFFFFFFFu) == magic;
@@ -2370,19 +2388,16 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
       const uint64_t total = hd[4];
       ok &= total <= in_size;
       for (int i = 7; i < 16; i++) ok &= hd[i] == 0u;
-      const uint64_t* table = reinterpret_cast<const uint64_t*>(in + kHeader);
-      ok &= table[0] == base_off;
-      ok &= table[nchunks] == total;
+      ok &= t_first == base_off;
+      ok &= t_last == total;
       if (wg == 0u)  // the padding after the escape index is zero
         for (uint64_t i = 2u * nchunks + 1u; i < (base_off - kHeader) / 8u; i++) ok &= table[i] == 0u;
-      if (ok && nchunks) {
-        begin = table[c];
-        end = table[c + 1u];
-        index = table[nchunks + 1u + c];
+      if (nchunks) {
         ok &= begin >= base_off && begin <= end && end <= total;
         ok &= ((begin | end) & 127u) == 0u;
         ok &= (index & 0xFFFFu) == 0u;  // no escapes before the chunk's first value
       }
+      if (!ok) begin = end = index = 0u;
     }
     s_ok = ok;
     s_e0 = e0;
