@@ -158,6 +158,13 @@ struct WsLayout {
   uint64_t err, partial, bitmap, hist, partesc, chunkesc, pcount, cstat, plan, phash, total;
 };
 
+// Decoding tensors of at most kSliceChunks chunks: kSlices workgroups per
+// part, each decoding a slice of it (two units per thread instead of eight),
+// so that a shard-sized tensor keeps every CU busy instead of one per part.
+constexpr uint32_t kSlices = 4u;
+constexpr uint64_t kSliceChunks = 32u;
+static_assert(kUPT % kSlices == 0u && (kUPT / kSlices) % 2u == 0u, "unit pairs per thread in a slice");
+
 // Exponent histograms: per part one row of kBins u16 counts (a part holds at
 // most 16384 values) of its coded values by exponent field, rows in part
 // order, so that each part writes whole 128-byte lines.
@@ -168,7 +175,8 @@ __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   WsLayout l;
   const uint64_t slots = nchunks ? nchunks : 1u;
   l.err = sizeof(Ctrl);
-  l.partial = align256(l.err + 4u * kParts * slots);
+  const uint64_t err_slots = kParts * slots * (slots <= kSliceChunks ? kSlices : 1u);  // one per workgroup
+  l.partial = align256(l.err + 4u * err_slots);
   l.bitmap = align256(l.partial + sizeof(Partial) * kParts * slots);
   l.hist = align256(l.bitmap + 4u * kBitmapWords * slots);
   l.partesc = align256(l.hist + 2u * kBins * kParts * slots);
@@ -1325,16 +1333,40 @@ __device__ inline void zero_fill(uint8_t* __restrict__ p, uint64_t from, uint64_
   for (uint64_t i = from + threadIdx.x; i < to; i += nthreads) p[i] = 0u;
 }
 
+// Block-wide (256 threads) sum and inclusive scan of u32 values.
+__device__ inline uint32_t part_sum_u32(uint32_t v, uint32_t* s_w) {
+  v = wave_sum_u32(v);
+  __syncthreads();
+  if (lane_id() == 0u) s_w[threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t t = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPartWaves; w++) t += s_w[w];
+  return t;
+}
+__device__ inline uint32_t part_incl_scan_u32(uint32_t v, uint32_t* s_w) {
+  const uint32_t incl = wave_incl_scan(v);
+  __syncthreads();
+  if (lane_id() == 63u) s_w[threadIdx.x >> 6] = incl;
+  __syncthreads();
+  uint32_t before = 0;
+#pragma unroll
+  for (uint32_t w = 0; w < kPartWaves; w++) before += (w < (threadIdx.x >> 6)) ? s_w[w] : 0u;
+  return before + incl;
+}
+
 // Escape positions within a part: cnt[j] (0..8) per unit, units ordered
 // (j, wave, lane).  base[j] receives the escapes in earlier units of the part;
 // returns the part's total.  Every thread of the workgroup must call it.
-__device__ inline uint32_t part_escape_scan(const uint32_t (&cnt)[kUPT], uint32_t (&base)[kUPT],
-                                            uint32_t* s_tot /* kUPT * kPartWaves + 1 */) {
+template <uint32_t N>
+__device__ inline uint32_t part_escape_scan(const uint32_t (&cnt)[N], uint32_t (&base)[N],
+                                            uint32_t* s_tot /* N * kPartWaves + 1 */) {
+  static_assert(N % 2u == 0u && N <= kUPT, "unit pairs, at most kUPT per thread");
   const uint32_t lane = lane_id();
   const uint32_t wave = threadIdx.x >> 6;
   // two counts per 32-bit word (16-bit fields; a wave's sum is at most 512)
 #pragma unroll
-  for (uint32_t p = 0; p < kUPT / 2u; p++) {
+  for (uint32_t p = 0; p < N / 2u; p++) {
     const uint32_t packed = cnt[2 * p] | (cnt[2 * p + 1] << 16);
     const uint32_t incl = wave_incl_scan(packed);
     const uint32_t excl = incl - packed;
@@ -1346,7 +1378,7 @@ __device__ inline uint32_t part_escape_scan(const uint32_t (&cnt)[kUPT], uint32_
     }
   }
   __syncthreads();
-  constexpr uint32_t kEntries = kUPT * kPartWaves;
+  constexpr uint32_t kEntries = N * kPartWaves;
   if (wave == 0) {
     const uint32_t a = (lane < kEntries) ? s_tot[lane] : 0u;
     const uint32_t incl = wave_incl_scan(a);
@@ -1355,7 +1387,7 @@ __device__ inline uint32_t part_escape_scan(const uint32_t (&cnt)[kUPT], uint32_
   }
   __syncthreads();
 #pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) base[j] += s_tot[j * kPartWaves + wave];
+  for (uint32_t j = 0; j < N; j++) base[j] += s_tot[j * kPartWaves + wave];
   return s_tot[kEntries];
 }
 
@@ -2205,24 +2237,32 @@ struct DecodePart {
   uint32_t part;    // h: the part's quarter of the chunk
   uint64_t index;   // the chunk's escape index word (four u16)
   uint32_t before;  // escapes of the chunk before the part, from the index
+  uint32_t u0;      // the workgroup's first unit: the part's, or its slice's
+  uint32_t slot0;   // plane slot of unit u0 (zip3: u0)
+  bool final_units; // the workgroup holds the part's last units with data
 };
 
-// Decode one part.  kFull: every unit of the part holds 8 values, so no
-// per-unit tail handling.  Returns the part's status word.
-template <bool kCiera, bool kFull>
+// Decode the units [u0, u0 + kPartUnits / kS) of a part.  kS = 1: the whole
+// part.  kS > 1: one slice of it, whose first escape follows from the index
+// entry of the part and the code-0 values in the part's slots before u0.
+// kFull: every unit of the range holds 8 values, so no per-unit tail
+// handling.  Returns the workgroup's status word.
+template <bool kCiera, bool kFull, uint32_t kS>
 __device__ __attribute__((always_inline)) inline uint32_t decode_part(const DecodePart& p, const uint32_t* s_bits,
                                                                       const uint32_t* s_rank, uint8_t* s_planes,
                                                                       uint8_t* s_esc, uint32_t* s_tot) {
+  constexpr uint32_t kU = kUPT / kS;  // units per thread
+  __shared__ uint32_t s_zw[kPartWaves];
   const uint32_t tid = threadIdx.x;
   const uint8_t* __restrict__ in = p.in;
   const ChunkGeom& g = p.g;
   // Issue every load before using any: sign+mantissa and, for unchanged
-  // blocks, the receiver cache into registers; the part's plane bytes and
-  // escapes, staged in LDS.
-  uint2 smv[kUPT], ev[kUPT];
+  // blocks, the receiver cache into registers; the part's plane bytes (up to
+  // the end of the range) and escapes, staged in LDS.
+  uint2 smv[kU], ev[kU];
 #pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = p.pu0 + j * kPartThreads + tid;
+  for (uint32_t j = 0; j < kU; j++) {
+    const uint32_t u = p.u0 + j * kPartThreads + tid;
     smv[j] = make_uint2(0u, 0u);
     ev[j] = make_uint2(0u, 0u);
     if (kFull || u < p.nunits) {
@@ -2277,12 +2317,20 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   for (uint32_t i = tid + kEscRounds * kPartThreads; i < pieces; i += kPartThreads)
     reinterpret_cast<uint4*>(s_esc)[i] = *reinterpret_cast<const uint4*>(in + g.esc + esc_lo + 16u * i);
   __syncthreads();
-  const uint32_t before = p.before;
+  uint32_t zb = 0;  // code-0 values of the part before unit u0
+  if (kS > 1u) {
+    const uint32_t lim = p.slot0 - p.sbase;
+    uint32_t z = 0;
+    for (uint32_t i = tid; i < lim; i += kPartThreads)
+      z += __popc(~(uint32_t(s_planes[i]) | s_planes[kStage + i] | s_planes[2u * kStage + i]) & 0xFFu);
+    zb = part_sum_u32(z, s_zw);
+  }
+  const uint32_t before = p.before + zb;
 
-  uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
+  uint32_t cnt[kU], base[kU], emask[kU];
 #pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = p.pu0 + j * kPartThreads + tid;
+  for (uint32_t j = 0; j < kU; j++) {
+    const uint32_t u = p.u0 + j * kPartThreads + tid;
     cnt[j] = 0u;
     emask[j] = 0u;
     if (!kFull && u >= p.nunits) continue;
@@ -2308,19 +2356,21 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);
   // Every escape read stays inside the chunk's escape section and the staged
-  // bytes: the index entry after the part must equal before + pesc, and the
-  // part that holds the chunk's last values checks the section's padded
-  // length and the index entries of the quarters past the data.
+  // bytes: the range's escapes must end inside both; the workgroup with the
+  // part's last units checks the index entry after the part against before +
+  // pesc, and the one with the chunk's last values checks the section's
+  // padded length and the index entries of the quarters past the data.
   const uint32_t after = before + pesc;
-  bool bad = after > p.esc_len || (p.part + 1u < kParts && next != after);
+  bool bad = after > p.esc_len || after - esc_lo > 16u * pieces;
+  if (p.final_units && p.part + 1u < kParts) bad |= next != after;
   if (p.last_with_data) {
     bad |= pad128(after) != p.esc_len;
     for (uint32_t q = p.part + 1u; q < kParts; q++) bad |= (uint32_t(p.index >> (16u * q)) & 0xFFFFu) != after;
   }
   if (bad) return uint32_t(CIERA_ERR_FORMAT);  // uniform
 #pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = p.pu0 + j * kPartThreads + tid;
+  for (uint32_t j = 0; j < kU; j++) {
+    const uint32_t u = p.u0 + j * kPartThreads + tid;
     if (!kFull && u >= p.nunits) continue;
     const uint32_t valid = kFull ? 8u : min(8u, p.nc - 8u * u);
     // the unit's escapes are staged bytes [before + base - esc_lo, + cnt)
@@ -2334,9 +2384,9 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   return 0u;
 }
 
-// One part of a chunk; parts never wait on each other: the escape index gives
-// each part its first escape.
-template <bool kCiera>
+// One part of a chunk (kS = 1), or one of its kS slices; workgroups never
+// wait on each other: the escape index gives each part its first escape.
+template <bool kCiera, uint32_t kS>
 __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restrict__ in, uint64_t in_size,
                                                          uint16_t* __restrict__ y, uint64_t n, uint64_t nchunks,
                                                          uint32_t log2B, uint8_t* __restrict__ cache,
@@ -2353,8 +2403,9 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
   const uint32_t tid = threadIdx.x;
   const uint32_t wg = blockIdx.x;
-  const uint32_t c = wg / kParts;
-  const uint32_t h = wg % kParts;
+  const uint32_t c = wg / (kParts * kS);
+  const uint32_t h = (wg / kS) % kParts;
+  const uint32_t slice = wg % kS;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint64_t base_off = table_end(nchunks);
   if (tid == 0) {
@@ -2446,7 +2497,9 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
     if (tid == 0) err_slots[wg] = uint32_t(CIERA_ERR_FORMAT);
     return;
   }
-  if (pu0 >= nunits) {  // a part past the chunk's data
+  constexpr uint32_t kRange = kPartUnits / kS;  // units of the workgroup
+  const uint32_t u0 = pu0 + slice * kRange;
+  if (u0 >= nunits) {  // a range past the chunk's data
     if (tid == 0) err_slots[wg] = 0u;
     return;
   }
@@ -2454,10 +2507,12 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   const uint32_t esc_len = uint32_t(end - g.esc);
   const uint64_t index = s_index;
   const uint32_t s_h = kCiera ? coded_before(pu0, s_bits, s_rank, log2B, nb, nch) : pu0;
-  const bool last_with_data = pu0 + kPartUnits >= nunits;
-  // slots of the part's own units (a block may span several parts)
-  const uint32_t s_next = kCiera ? coded_before(pu0 + kPartUnits, s_bits, s_rank, log2B, nb, nch)
-                                 : min(pu0 + kPartUnits, nunits);
+  const uint32_t s_lo = kCiera ? coded_before(u0, s_bits, s_rank, log2B, nb, nch) : u0;
+  const bool last_with_data = u0 + kRange >= nunits;
+  // slots from the part's first unit to the end of the range (a block may
+  // span several parts)
+  const uint32_t s_next = kCiera ? coded_before(u0 + kRange, s_bits, s_rank, log2B, nb, nch)
+                                 : min(u0 + kRange, nunits);
   DecodePart p;
   p.in = in;
   p.y = y;
@@ -2479,11 +2534,14 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   p.part = h;
   p.index = index;
   p.before = uint32_t(index >> (16u * h)) & 0xFFFFu;
+  p.u0 = u0;
+  p.slot0 = s_lo;
+  p.final_units = slice + 1u == kS || last_with_data;
   uint32_t err;
-  if (8u * (pu0 + kPartUnits) <= nc)
-    err = decode_part<kCiera, true>(p, s_bits, s_rank, s_planes, s_esc, s_tot);
+  if (8u * (u0 + kRange) <= nc)
+    err = decode_part<kCiera, true, kS>(p, s_bits, s_rank, s_planes, s_esc, s_tot);
   else
-    err = decode_part<kCiera, false>(p, s_bits, s_rank, s_planes, s_esc, s_tot);
+    err = decode_part<kCiera, false, kS>(p, s_bits, s_rank, s_planes, s_esc, s_tot);
   if (tid == 0) err_slots[wg] = err;
 }
 
@@ -2598,28 +2656,6 @@ __device__ inline bool part_lookback(const uint64_t* rstat, uint64_t p, uint64_t
     top -= 64;
   }
   return true;
-}
-
-// Block-wide (256 threads) sum and inclusive scan of u32 values.
-__device__ inline uint32_t part_sum_u32(uint32_t v, uint32_t* s_w) {
-  v = wave_sum_u32(v);
-  __syncthreads();
-  if (lane_id() == 0u) s_w[threadIdx.x >> 6] = v;
-  __syncthreads();
-  uint32_t t = 0;
-#pragma unroll
-  for (uint32_t w = 0; w < kPartWaves; w++) t += s_w[w];
-  return t;
-}
-__device__ inline uint32_t part_incl_scan_u32(uint32_t v, uint32_t* s_w) {
-  const uint32_t incl = wave_incl_scan(v);
-  __syncthreads();
-  if (lane_id() == 63u) s_w[threadIdx.x >> 6] = incl;
-  __syncthreads();
-  uint32_t before = 0;
-#pragma unroll
-  for (uint32_t w = 0; w < kPartWaves; w++) before += (w < (threadIdx.x >> 6)) ? s_w[w] : 0u;
-  return before + incl;
 }
 
 // Encoder table entry of a symbol with frequency f >= 1 and cumulative
@@ -3525,15 +3561,24 @@ ciera_status decode_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t
   const uint64_t nchunks = cdiv(n, kChunk);
   if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
   const Ws ws = ws_bind(d_ws, nchunks);
-  const uint32_t grid = uint32_t(nchunks ? nchunks * kParts : 1u);
+  const bool sliced = nchunks <= kSliceChunks;
+  const uint32_t grid = uint32_t(nchunks ? nchunks * kParts * (sliced ? kSlices : 1u) : 1u);
   const uint8_t* in = static_cast<const uint8_t*>(d_in);
   uint16_t* y = static_cast<uint16_t*>(d_y);
+  const uint32_t lb = ciera ? log2u(B) : 0u;
+  uint8_t* cache = ciera ? d_cache : nullptr;
   (void)hipGetLastError();
-  if (ciera)
-    launch(k_decode<true>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, log2u(B), d_cache,
+  if (ciera && sliced)
+    launch(k_decode<true, kSlices>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, lb, cache,
+           &ws.ctrl->n_err_slots, ws.err);
+  else if (ciera)
+    launch(k_decode<true, 1u>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, lb, cache,
+           &ws.ctrl->n_err_slots, ws.err);
+  else if (sliced)
+    launch(k_decode<false, kSlices>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, lb, cache,
            &ws.ctrl->n_err_slots, ws.err);
   else
-    launch(k_decode<false>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, 0u, nullptr,
+    launch(k_decode<false, 1u>, dim3(grid), dim3(kPartThreads), stream, in, in_size, y, n, nchunks, lb, cache,
            &ws.ctrl->n_err_slots, ws.err);
   return launch_status();
 }
