@@ -1432,9 +1432,9 @@ struct SelfPlan {
   uint64_t begin;
   uint32_t e0, esc_before, esc_chunk, esc_part;
 };
-__device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, uint32_t h, uint32_t wg, uint32_t B,
-                                     int e0_override, uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
-                                     const Ws& ws) {
+__device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, uint32_t h, bool lead, uint32_t wg,
+                                     uint32_t B, int e0_override, uint8_t* __restrict__ out,
+                                     uint64_t* __restrict__ out_size, const Ws& ws) {
   __shared__ double s_f[kPlanWaves];
   __shared__ uint64_t s_u[kPlanWaves];
   __shared__ uint64_t s_r[4];
@@ -1480,7 +1480,7 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
       s_r[0] = base + incl - size;
       s_r[2] = eb;
       s_r[3] = esc_total | (uint64_t(en - eb) << 32);
-      if (h == 0u) {
+      if (lead) {
         table[c] = base + incl - size;
         table[nchunks + 1u + c] = uint64_t(esc[0]) | (uint64_t(esc[1]) << 16) | (uint64_t(esc[2]) << 32) |
                                   (uint64_t(esc[3]) << 48);
@@ -1503,7 +1503,7 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
         hd[6] = t_esc;
         for (int i = 7; i < 16; i++) hd[i] = 0u;
         ws.ctrl->e0 = e0;
-        ws.ctrl->n_err_slots = nchunks * kParts;
+        ws.ctrl->n_err_slots = gridDim.x;
       }
     }
   }
@@ -1521,10 +1521,11 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
 
 // A thread's escapes (the raw exponent bytes of its units' code-0 values) to
 // the part's LDS staging at their ranks base[j], in value order.
-__device__ inline void stage_escapes(const Unit (&v)[kUPT], const uint32_t (&emask)[kUPT], const uint32_t (&base)[kUPT],
+template <uint32_t N>
+__device__ inline void stage_escapes(const Unit (&v)[N], const uint32_t (&emask)[N], const uint32_t (&base)[N],
                                      uint8_t* s_esc) {
 #pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
+  for (uint32_t j = 0; j < N; j++) {
     uint32_t em = emask[j];
     if (em) {
       const uint2 e = unit_exponents(v[j]);
@@ -1538,38 +1539,69 @@ __device__ inline void stage_escapes(const Unit (&v)[kUPT], const uint32_t (&ema
   }
 }
 
-template <bool kCiera, bool kSelfPlan>
+// One part of a chunk (kS = 1) or one of its kS slices (self-planned
+// tensors only): a slice codes units [u0, u0 + kPartUnits / kS) and counts
+// the escapes of the part's units before u0 to place its own.
+template <bool kCiera, bool kSelfPlan, uint32_t kS>
 __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restrict__ x, uint64_t n,
                                                         uint32_t log2B, uint8_t* __restrict__ out,
                                                         uint64_t capacity, uint64_t* __restrict__ out_size,
                                                         int e0_override, Ws ws) {
+  static_assert(kS == 1u || kSelfPlan, "slices only for self-planned tensors");
+  constexpr uint32_t kU = kUPT / kS;             // units per thread
+  constexpr uint32_t kRange = kPartUnits / kS;   // units per workgroup
+  constexpr uint32_t kEarly = kUPT - kU;         // most units per thread before u0
   __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_esc[kPartEscStage];
   __shared__ uint32_t s_bits[kBitmapWords];
   __shared__ uint32_t s_rank[kBitmapWords];
   __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
+  __shared__ uint32_t s_zw[kPartWaves];
   const uint32_t tid = threadIdx.x;
   const uint32_t wg = blockIdx.x;
-  const uint32_t c = wg / kParts;
-  const uint32_t h = wg % kParts;
+  const uint32_t c = wg / (kParts * kS);
+  const uint32_t h = (wg / kS) % kParts;
+  const uint32_t slice = wg % kS;
   const bool last_part = h + 1u == kParts;
+  const bool final_slice = slice + 1u == kS;
   const uint32_t B = 1u << log2B;
   const uint64_t start = uint64_t(c) * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
   const uint32_t pu0 = h * kPartUnits;
+  const uint32_t u0 = pu0 + slice * kRange;
 
-  // Load the part first: all of a thread's 16-byte loads go out before any is used.
-  Unit v[kUPT];
-  if (8u * (pu0 + kPartUnits) <= nc) {
+  // Load the range first: all of a thread's 16-byte loads go out before any
+  // is used; a slice also loads the part's units before it.
+  Unit v[kU];
+  if (8u * (u0 + kRange) <= nc) {
 #pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) v[j] = load_unit(x, start + 8ull * (pu0 + j * kPartThreads + tid), 8u);
+    for (uint32_t j = 0; j < kU; j++) v[j] = load_unit(x, start + 8ull * (u0 + j * kPartThreads + tid), 8u);
   } else {
 #pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      const uint32_t u = pu0 + j * kPartThreads + tid;
+    for (uint32_t j = 0; j < kU; j++) {
+      const uint32_t u = u0 + j * kPartThreads + tid;
       v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
       if (u < nunits) v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+    }
+  }
+  // (thread t's units before u0 are pu0 + 256 k + t, k < slice * kU; all
+  // hold 8 values unless the data ends before u0)
+  Unit ve[kEarly > 0u ? kEarly : 1u];
+#pragma unroll
+  for (uint32_t k = 0; k < kEarly; k++) ve[k].w[0] = ve[k].w[1] = ve[k].w[2] = ve[k].w[3] = 0u;
+  if (kEarly > 0u) {
+    const uint32_t nearly = slice * kU;
+    if (8u * u0 <= nc) {
+#pragma unroll
+      for (uint32_t k = 0; k < kEarly; k++)
+        if (k < nearly) ve[k] = load_unit(x, start + 8ull * (pu0 + k * kPartThreads + tid), 8u);
+    } else {
+#pragma unroll
+      for (uint32_t k = 0; k < kEarly; k++) {
+        const uint32_t u = pu0 + k * kPartThreads + tid;
+        if (k < nearly && u < nunits) ve[k] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
+      }
     }
   }
   const uint64_t nchunks = cdiv(n, kChunk);
@@ -1580,7 +1612,8 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   __shared__ uint32_t s_pw[kSelfPlan ? kBitmapWords : 1u];
   const uint32_t pw_l = (kSelfPlan && kCiera && tid < kBitmapWords) ? ws.bitmap[uint64_t(c) * kBitmapWords + tid] : 0u;
   if (kSelfPlan) {
-    const SelfPlan sp = self_plan(n, nchunks, c, h, wg, kCiera ? B : 0u, e0_override, out, out_size, ws);
+    const SelfPlan sp = self_plan(n, nchunks, c, h, h == 0u && slice == 0u, wg, kCiera ? B : 0u, e0_override, out,
+                                  out_size, ws);
     begin = sp.begin;
     esc_before = sp.esc_before;
     esc_chunk = sp.esc_chunk;
@@ -1633,16 +1666,44 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   // ciera: the slots of the part's units in changed blocks, [S_h, S_next);
   // the last part also owns the padding after the chunk's last slot.  Every
   // bound is a multiple of 8.
-  const uint32_t s_h = kCiera ? coded_before(pu0, s_bits, s_rank, log2B, nb, nch) : pu0;
-  const uint32_t s_next = kCiera ? (!last_part ? coded_before(pu0 + kPartUnits, s_bits, s_rank, log2B, nb, nch)
-                                               : nch * (B / 8u))
-                                 : pu0 + kPartUnits;
+  // A slice owns the slots of its own units, [S(u0), S(u0 + kRange)).
+  const uint32_t s_h = kCiera ? coded_before(u0, s_bits, s_rank, log2B, nb, nch) : u0;
+  const uint32_t s_next = kCiera ? (!(last_part && final_slice) ? coded_before(u0 + kRange, s_bits, s_rank, log2B, nb, nch)
+                                                                : nch * (B / 8u))
+                                 : u0 + kRange;
+
+  // A slice's first escape: the part's escapes before u0 (values of coded
+  // units whose code is 0), counted from the units loaded above.
+  uint32_t zb = 0;
+  if (kS > 1u) {
+    uint32_t z = 0;
+#pragma unroll
+    for (uint32_t k = 0; k < kEarly; k++) {
+      const uint32_t u = pu0 + k * kPartThreads + tid;
+      if (u >= u0 || u >= nunits) continue;
+      bool coded = true;
+      if (kCiera) {
+        const uint32_t blk = (8u * u) >> log2B;
+        coded = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
+      }
+      if (coded) {
+        const uint32_t valid = min(8u, nc - 8u * u);
+        const uint32_t vmask = (valid == 8u) ? 0xFFu : ((1u << valid) - 1u);
+        uint32_t cp[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) cp[i] = code_pair(exp_pair(ve[k].w[i]), bias);
+        const uint32_t p = unit_planes(cp);
+        z += __popc(~(p | (p >> 8) | (p >> 16)) & vmask);
+      }
+    }
+    zb = part_sum_u32(z, s_zw);
+  }
 
   // Code every unit: sign+mantissa bytes straight to HBM, plane bytes into LDS.
-  uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
+  uint32_t cnt[kU], base[kU], emask[kU];
 #pragma unroll
-  for (uint32_t j = 0; j < kUPT; j++) {
-    const uint32_t u = pu0 + j * kPartThreads + tid;
+  for (uint32_t j = 0; j < kU; j++) {
+    const uint32_t u = u0 + j * kPartThreads + tid;
     cnt[j] = 0u;
     emask[j] = 0u;
     if (u < nunits) {
@@ -1671,10 +1732,11 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     }
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
-  // The count must match what k_plan read off the histogram; a mismatch
-  // would overrun the escape section, so no escapes are written and the error
-  // word reports it.
-  const bool esc_ok = pesc == esc_part;
+  // The count must match what the plan read off the histogram (a slice: its
+  // escapes and those before it stay within the part's, and the last slice's
+  // end where the part's do); a mismatch would overrun the escape section, so
+  // no escapes are written and the error word reports it.
+  const bool esc_ok = final_slice ? zb + pesc == esc_part : zb + pesc <= esc_part;
   if (tid == 0) ws.err[wg] = esc_ok ? 0u : uint32_t(CIERA_ERR_INTERNAL);
   // planes: LDS -> HBM in 8-byte pieces over the owned range, clipped to the
   // padded plane length
@@ -1686,14 +1748,14 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     const uint2 val = *reinterpret_cast<const uint2*>(s_planes + b * kStage + off);
     *reinterpret_cast<uint2*>(out + g.plane + b * pb + s_h + off) = val;
   }
-  // escapes of this part: [esc_before, esc_before + pesc) of the chunk's section
-  const uint64_t esc_at = g.esc + esc_before;
+  // escapes of this range: [esc_before + zb, + pesc) of the chunk's section
+  const uint64_t esc_at = g.esc + esc_before + zb;
   if (esc_ok) {
     stage_escapes(v, emask, base, s_esc);
     __syncthreads();
     lds_to_global(out + esc_at, s_esc, pesc, tid, kPartThreads);
   }
-  if (last_part) {
+  if (last_part && final_slice) {
     // zero padding after each section's data, and the bitmap
     zero_fill(out, g.sm + 8ull * nunits, g.bitmap, kPartThreads);
     if (kCiera && tid < kBitmapWords) *reinterpret_cast<uint32_t*>(out + g.bitmap + 4u * tid) = s_bits[tid];
@@ -3421,18 +3483,21 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
              d_out_size, nullptr, ws);
   }
   if (nchunks) {
+    // a self-planned tensor is small: kSlices workgroups per part
     const dim3 grid(uint32_t(nchunks * kParts));
+    const dim3 sgrid(uint32_t(nchunks * kParts * kSlices));
+    static_assert(kSelfPlanChunks <= kSliceChunks, "the workspace has an error slot per slice");
     if (ciera && self_plan)
-      launch(k_write<true, true>, grid, dim3(kPartThreads), stream, x, n, lb, out, out_capacity, d_out_size,
+      launch(k_write<true, true, kSlices>, sgrid, dim3(kPartThreads), stream, x, n, lb, out, out_capacity, d_out_size,
              e0_override, ws);
     else if (ciera)
-      launch(k_write<true, false>, grid, dim3(kPartThreads), stream, x, n, lb, out, out_capacity, d_out_size,
+      launch(k_write<true, false, 1u>, grid, dim3(kPartThreads), stream, x, n, lb, out, out_capacity, d_out_size,
              e0_override, ws);
     else if (self_plan)
-      launch(k_write<false, true>, grid, dim3(kPartThreads), stream, x, n, 0u, out, out_capacity, d_out_size,
-             e0_override, ws);
+      launch(k_write<false, true, kSlices>, sgrid, dim3(kPartThreads), stream, x, n, 0u, out, out_capacity,
+             d_out_size, e0_override, ws);
     else
-      launch(k_write<false, false>, grid, dim3(kPartThreads), stream, x, n, 0u, out, out_capacity, d_out_size,
+      launch(k_write<false, false, 1u>, grid, dim3(kPartThreads), stream, x, n, 0u, out, out_capacity, d_out_size,
              e0_override, ws);
   }
   return launch_status();
