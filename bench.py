@@ -487,6 +487,10 @@ def main() -> int:
     dec_iso, dec_iso_min = gpu.isolated(dec[k_iso], restore_r)
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
     iso_roundtrip = bool(torch.equal(y, xs[k_iso]))
+    # The floor of this method: one launch of a one-element fill, timed the
+    # same way (launch and event overhead, part of every isolated time).
+    one = torch.zeros(1, device=gpu.dev)
+    floor_ms, floor_min = gpu.isolated(lambda: one.zero_())
 
     # Single-read encode, timed like pass 3: the window base is byte 7 of the
     # stream the full encode of the same input just wrote (read on the
@@ -673,7 +677,9 @@ def main() -> int:
            "decode_algorithmic_bytes": alg_dec,
            "decode_frac_of_hbm_peak": round(alg_dec / (dec_iso * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
            "decode_frac_of_measured_copy": round(alg_dec / (dec_iso * 1e-3) / 1e9 / bw_copy, 4),
-           "decode_roundtrip_ok": iso_roundtrip}
+           "decode_roundtrip_ok": iso_roundtrip,
+           "floor_ms": round(floor_ms, 5), "floor_min_ms": round(floor_min, 5),
+           "floor_what": "one launch of a one-element fill timed the same way"}
     # The same fractions with the bytes the HBM counters saw (FETCH_SIZE +
     # WRITE_SIZE per launch, from the traffic summaries taken on this kernel
     # source), null where no such record exists.

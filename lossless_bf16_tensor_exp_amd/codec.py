@@ -8,7 +8,7 @@ from __future__ import annotations
 
 import torch
 
-from . import (ciera_decode, ciera_encode, ciera_encode_e0, ciera_max_encoded_size, ciera_read_error,
+from . import (CieraError, ciera_decode, ciera_encode, ciera_encode_e0, ciera_max_encoded_size, ciera_read_error,
                ciera_workspace_size, zip3_decode, zip3_encode, zip3_encode_e0, zip3_max_encoded_size,
                zip3_workspace_size)
 
@@ -81,3 +81,62 @@ class CieraCodec:
     def decode_error(self, stream=None) -> int:
         """Device status of the last decode."""
         return ciera_read_error(self.ws_dec, stream)
+
+
+# One-shot calls: allocate the stream and workspace with torch, run one
+# encode or decode on the current stream, and return the result.  Reading the
+# compressed size back synchronizes the stream; the classes above keep their
+# buffers and do not.
+
+def _raise_device_error(ws, what: str) -> None:
+    st = ciera_read_error(ws)
+    if st:
+        raise CieraError(st, what)
+
+
+def zip3_encode_tensor(x):
+    """3-bit code of the BF16 values x (a CUDA tensor, read as raw 16-bit
+    patterns).  Returns (stream bytes, size)."""
+    n = x.numel()
+    out = torch.empty(zip3_max_encoded_size(n), dtype=torch.uint8, device=x.device)
+    ws = torch.empty(zip3_workspace_size(n), dtype=torch.uint8, device=x.device)
+    size = torch.zeros(1, dtype=torch.int64, device=x.device)
+    zip3_encode(x, out, ws, size)
+    _raise_device_error(ws, "zip3_encode")
+    k = int(size.item())
+    return out[:k], k
+
+
+def zip3_decode_tensor(stream_bytes, n: int):
+    """Inverse of zip3_encode_tensor: the n values as an int16 tensor of raw patterns."""
+    y = torch.empty(n, dtype=torch.int16, device=stream_bytes.device)
+    ws = torch.empty(zip3_workspace_size(n), dtype=torch.uint8, device=stream_bytes.device)
+    zip3_decode(stream_bytes, stream_bytes.numel(), y, ws)
+    _raise_device_error(ws, "zip3_decode")
+    return y
+
+
+def ciera_encode_tensor(x, B: int, prev_exp):
+    """Exponent reuse against the sender cache prev_exp (n bytes, updated in
+    place) plus the 3-bit code.  Returns (stream bytes, size)."""
+    n = x.numel()
+    cap = ciera_max_encoded_size(n, B)
+    if cap == 0:
+        raise ValueError(f"invalid block size {B}")
+    out = torch.empty(cap, dtype=torch.uint8, device=x.device)
+    ws = torch.empty(ciera_workspace_size(n, B), dtype=torch.uint8, device=x.device)
+    size = torch.zeros(1, dtype=torch.int64, device=x.device)
+    ciera_encode(x, B, prev_exp, out, ws, size)
+    _raise_device_error(ws, "ciera_encode")
+    k = int(size.item())
+    return out[:k], k
+
+
+def ciera_decode_tensor(stream_bytes, n: int, B: int, prev_exp):
+    """Inverse of ciera_encode_tensor against the receiver cache prev_exp
+    (updated in place)."""
+    y = torch.empty(n, dtype=torch.int16, device=stream_bytes.device)
+    ws = torch.empty(ciera_workspace_size(n, B), dtype=torch.uint8, device=stream_bytes.device)
+    ciera_decode(stream_bytes, stream_bytes.numel(), y, B, prev_exp, ws)
+    _raise_device_error(ws, "ciera_decode")
+    return y
