@@ -1860,15 +1860,19 @@ __device__ inline uint64_t chunk_bytes(uint32_t nc, bool ciera, uint32_t log2B, 
 __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks, uint32_t B,
                                                     const uint8_t* __restrict__ d_e0, uint8_t* __restrict__ out,
                                                     uint64_t* __restrict__ out_size, Ws ws) {
+  // every workgroup clears its share of the look-back words; workgroup 0
+  // also writes the header and the control words
   const uint32_t tid = threadIdx.x;
+  const uint64_t first = uint64_t(blockIdx.x) * kThreads + tid, stride = uint64_t(gridDim.x) * kThreads;
   uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
   const uint64_t base = table_end(nchunks);
   const uint32_t e0 = d_e0[0];
   const bool ok = e0 <= kMaxE0;
-  for (uint64_t i = tid; i < nchunks * kParts; i += kThreads)
+  for (uint64_t i = first; i < nchunks * kParts; i += stride)
     ws.pcount[(i / kParts) * kPcountStride + i % kParts] = 0u;
-  for (uint64_t i = tid; i < nchunks; i += kThreads) ws.cstat[i * kCstatStride] = 0u;
+  for (uint64_t i = first; i < nchunks; i += stride) ws.cstat[i * kCstatStride] = 0u;
+  if (blockIdx.x != 0u) return;
   if (tid == 0) {
     ws.ctrl->done_esc = 0u;
     ws.ctrl->done_nch = 0u;
@@ -3520,7 +3524,9 @@ ciera_status encode_known_e0_impl(const void* d_x, uint64_t n, uint32_t B, uint8
   const uint16_t* x = static_cast<const uint16_t*>(d_x);
   uint8_t* out = static_cast<uint8_t*>(d_out);
   (void)hipGetLastError();
-  launch(k_prep1, dim3(1), dim3(kThreads), stream, n, nchunks, B, d_e0, out, d_out_size, ws);
+  const uint64_t prep_groups = cdiv(nchunks * kParts, kThreads);
+  launch(k_prep1, dim3(uint32_t(prep_groups < 1u ? 1u : (prep_groups > 1024u ? 1024u : prep_groups))), dim3(kThreads),
+         stream, n, nchunks, B, d_e0, out, d_out_size, ws);
   if (nchunks) {
     if (ciera)
       launch(k_write1<true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nchunks, log2u(B),
