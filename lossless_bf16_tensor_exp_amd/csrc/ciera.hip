@@ -175,11 +175,12 @@ __host__ inline WsLayout ws_layout(uint64_t nchunks) {
   WsLayout l;
   const uint64_t slots = nchunks ? nchunks : 1u;
   l.err = sizeof(Ctrl);
-  const uint64_t err_slots = kParts * slots * (slots <= kSliceChunks ? kSlices : 1u);  // one per workgroup
-  l.partial = align256(l.err + 4u * err_slots);
-  l.bitmap = align256(l.partial + sizeof(Partial) * kParts * slots);
-  l.hist = align256(l.bitmap + 4u * kBitmapWords * slots);
-  l.partesc = align256(l.hist + 2u * kBins * kParts * slots);
+  // one error word per workgroup; per-part records of k_stats, per slice for small tensors
+  const uint64_t recs = kParts * slots * (slots <= kSliceChunks ? kSlices : 1u);
+  l.partial = align256(l.err + 4u * recs);
+  l.bitmap = align256(l.partial + sizeof(Partial) * recs);
+  l.hist = align256(l.bitmap + 4u * kPartBitmapWords * recs);
+  l.partesc = align256(l.hist + 2u * kBins * recs);
   l.chunkesc = align256(l.partesc + 4u * kParts * slots);
   l.pcount = align256(l.chunkesc + 4u * slots);
   l.cstat = align256(l.pcount + 4u * kPcountStride * slots);
@@ -208,6 +209,7 @@ struct Ws {
   uint64_t* rinfo;
   uint8_t* rslot;
   uint32_t spin_limit;  // polls before a wait gives up (kSpinLimit unless a test lowers it)
+  uint32_t ss;          // k_stats records per part: 1, or kSlices (one per slice) for self-planned tensors
 };
 
 // The bound the next calls pass to their kernels (ciera_set_wait_limit).
@@ -232,6 +234,7 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.rinfo = nullptr;
   w.rslot = nullptr;
   w.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
+  w.ss = 1u;
   return w;
 }
 
@@ -558,21 +561,6 @@ __device__ inline void stats_checked(const Unit& v, uint32_t cnt, double shift, 
   }
 }
 
-// Changed blocks of a chunk from its parts' partials.  A part holds whole
-// blocks when B <= 16384 and counts them; a larger block spans B / 16384
-// parts, each of which records whether its own share changed.
-__device__ inline uint32_t chunk_changed_blocks(const Partial* part, uint32_t B) {
-  if (B <= kPartValues) return part[0].nch + part[1].nch + part[2].nch + part[3].nch;
-  const uint32_t ppb = B / kPartValues;
-  uint32_t nch = 0;
-  for (uint32_t first = 0; first < kParts; first += ppb) {
-    uint32_t any = 0;
-    for (uint32_t h = first; h < first + ppb; h++) any |= part[h].nch;
-    nch += any ? 1u : 0u;
-  }
-  return nch;
-}
-
 // Word t of a chunk's bitmap (bit j set = block j changed) from the words its
 // parts wrote (pw: kPartBitmapWords per part): part h keeps its own blocks'
 // bits from bit 0 of its first word, or, when a block spans several parts,
@@ -609,15 +597,19 @@ __device__ inline uint32_t stats_part_of(uint32_t b, uint32_t parts) {
   return (b % kXcds) * per + b / kXcds;
 }
 
-// One 256-thread workgroup per part (quarter chunk), units pu0 + 256 j + t.
-// Per part: FP64 variance partials; ciera: changed-block bits against the
+// One 256-thread workgroup per part (quarter chunk), units pu0 + 256 j + t;
+// for self-planned tensors (kS = kSlices) one per slice of a part, units
+// u0 + 256 j + t of the slice.  Per part (slice): FP64 variance partials; ciera: changed-block bits against the
 // sender cache and the cache update; an exponent histogram of the values to
 // code, and their count.  kHash: the sender cache is the block-hash cache
 // (two u64 per block) instead of the exponents.
-template <bool kCiera, bool kHash>
+template <bool kCiera, bool kHash, uint32_t kS>
 __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
                                                         uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
   static_assert(kCiera || !kHash, "the hash sender is a ciera mode");
+  static_assert(kS == 1u || !kHash, "the hash sender takes whole parts");
+  constexpr uint32_t kU = kUPT / kS;            // units per thread
+  constexpr uint32_t kRange = kPartUnits / kS;  // units per workgroup
   // hash sender: first the part's exponent words (2048 u64), then the histogram
   __shared__ __attribute__((aligned(16))) uint32_t s_hist[kHistCopies * kBins];
   __shared__ uint32_t s_bits[kPartBitmapWords];
@@ -626,20 +618,23 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   __shared__ uint64_t s_wh[2][kPartWaves];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = lane_id(), wave = tid >> 6;
-  const uint32_t wg = stats_part_of(blockIdx.x, gridDim.x);  // the part this workgroup takes
-  const uint64_t c = wg / kParts;
-  const uint32_t h = wg % kParts;
+  // the part (kS = 1) or slice this workgroup takes; its records sit at index wg
+  const uint32_t wg = stats_part_of(blockIdx.x, gridDim.x);
+  const uint64_t c = wg / (kParts * kS);
+  const uint32_t h = (wg / kS) % kParts;
+  const uint32_t slice = wg % kS;
   const uint64_t start = c * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
   const uint32_t pu0 = h * kPartUnits;
-  const bool full = 8u * (pu0 + kPartUnits) <= nc;
+  const uint32_t u0 = pu0 + slice * kRange;  // first unit of the workgroup
+  const bool full = 8u * (u0 + kRange) <= nc;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint32_t blk0 = kCiera ? ((8u * pu0) >> log2B) : 0u;  // first block of the part
   if (!kHash)
     for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
   if (tid < kPartBitmapWords) s_bits[tid] = 0u;
-  if (ws.rstat && tid == 0 && h == 0u) ws.rstat[c * kRstatStride] = 0u;  // rANS encode: the chunk's look-back word, not ready
+  if (ws.rstat && tid == 0 && h == 0u && slice == 0u) ws.rstat[c * kRstatStride] = 0u;  // rANS encode: the chunk's look-back word, not ready
   if (blockIdx.x == 0u) {
     // k_plan's slots: the count words not ready
     uint64_t* sw = reinterpret_cast<uint64_t*>(ws.plan);
@@ -664,20 +659,20 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   }
 
   // Load: all of a thread's 16-byte loads (and 8-byte cache loads) before use.
-  Unit v[kUPT];
-  uint2 old[kUPT];
+  Unit v[kU];
+  uint2 old[kU];
   if (full) {
 #pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) v[j] = load_unit(x, start + 8ull * (pu0 + j * kPartThreads + tid), 8u);
+    for (uint32_t j = 0; j < kU; j++) v[j] = load_unit(x, start + 8ull * (u0 + j * kPartThreads + tid), 8u);
     if (kCiera && !kHash) {
 #pragma unroll
-      for (uint32_t j = 0; j < kUPT; j++)
-        old[j] = *reinterpret_cast<const uint2*>(cache + start + 8ull * (pu0 + j * kPartThreads + tid));
+      for (uint32_t j = 0; j < kU; j++)
+        old[j] = *reinterpret_cast<const uint2*>(cache + start + 8ull * (u0 + j * kPartThreads + tid));
     }
   } else {
 #pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      const uint32_t u = pu0 + j * kPartThreads + tid;
+    for (uint32_t j = 0; j < kU; j++) {
+      const uint32_t u = u0 + j * kPartThreads + tid;
       v[j].w[0] = v[j].w[1] = v[j].w[2] = v[j].w[3] = 0u;
       old[j] = make_uint2(0u, 0u);
       if (u < nunits) {
@@ -706,8 +701,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   auto units = [&](auto full_c) {
     constexpr bool kF = decltype(full_c)::value;
 #pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      const uint32_t u = pu0 + j * kPartThreads + tid;
+    for (uint32_t j = 0; j < kU; j++) {
+      const uint32_t u = u0 + j * kPartThreads + tid;
       bool diff = false, live = false;
       uint32_t ucnt = 0u;
       uint2 ue = make_uint2(0u, 0u);
@@ -747,7 +742,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
         if (m != 0u) {
           if (live && line_has_change(m)) store_bytes8(cache + start + 8ull * u, ucnt, ue);
           // first block of the wave's units, relative to the part
-          const uint32_t lbw = ((8u * (pu0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
+          const uint32_t lbw = ((8u * (u0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
           uint32_t bits = 0;
           for (uint32_t k = 0; k < 64u / L; k++) bits |= ((m >> (k * L)) & gmask) ? (1u << k) : 0u;
           if (lane == 0u) atomicOr(&s_bits[lbw >> 5], bits << (lbw & 31u));
@@ -765,8 +760,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     s2 = 0.0;
     nf = 0;
 #pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      const uint32_t u = pu0 + j * kPartThreads + tid;
+    for (uint32_t j = 0; j < kU; j++) {
+      const uint32_t u = u0 + j * kPartThreads + tid;
       if (u < nunits) stats_checked(v[j], min(8u, nc - 8u * u), shift, s1, s2, nf);
     }
   }
@@ -852,8 +847,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       coded = 0xFFu;
     } else {
 #pragma unroll
-      for (uint32_t j = 0; j < kUPT; j++) {
-        const uint32_t lb = ((8u * (pu0 + j * kPartThreads + tid)) >> log2B) - blk0;
+      for (uint32_t j = 0; j < kU; j++) {
+        const uint32_t lb = ((8u * (u0 + j * kPartThreads + tid)) >> log2B) - blk0;
         coded |= ((s_bits[lb >> 5] >> (lb & 31u)) & 1u) << j;
       }
     }
@@ -868,8 +863,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     } else {
       const uint32_t w0 = s_bits[0];  // at most 16 blocks per part
 #pragma unroll
-      for (uint32_t j = 0; j < kUPT; j++) {
-        const uint32_t lb = ((8u * (pu0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
+      for (uint32_t j = 0; j < kU; j++) {
+        const uint32_t lb = ((8u * (u0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
         coded |= ((w0 >> lb) & 1u) << j;
       }
     }
@@ -887,7 +882,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     constexpr uint32_t kBinMask = 0xFFu << kBinShift;
     uint8_t* hb = reinterpret_cast<uint8_t*>(s_hist);
 #pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
+    for (uint32_t j = 0; j < kU; j++) {
       if (!((coded >> j) & 1u)) continue;
 #pragma unroll
       for (int i = 0; i < 4; i++) {
@@ -898,8 +893,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     }
   } else {
 #pragma unroll
-    for (uint32_t j = 0; j < kUPT; j++) {
-      const uint32_t u = pu0 + j * kPartThreads + tid;
+    for (uint32_t j = 0; j < kU; j++) {
+      const uint32_t u = u0 + j * kPartThreads + tid;
       if (u >= nunits || !((coded >> j) & 1u)) continue;
       const uint32_t cnt = min(8u, nc - 8u * u);
       const uint2 e = unit_exponents(v[j]);
@@ -928,7 +923,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     sum = wave_sum_u32(sum);
     if (lane == 0u) s_wtot[wave] = sum;
   }
-  if (kCiera && tid < kPartBitmapWords) ws.bitmap[(c * kParts + h) * kPartBitmapWords + tid] = s_bits[tid];
+  if (kCiera && tid < kPartBitmapWords) ws.bitmap[uint64_t(wg) * kPartBitmapWords + tid] = s_bits[tid];
   __syncthreads();
   if (tid == 0) {
     double a = 0.0, b = 0.0;
@@ -956,7 +951,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     p.nch = nch;
     p.coded = t;
     p.pad = 0u;
-    ws.partial[c * kParts + h] = p;
+    ws.partial[wg] = p;
   }
 }
 
@@ -1054,47 +1049,86 @@ __device__ inline double plan_sum_f64(double v, double* s_w) {
 // up to kRunRegs rounds (longer ones park them in the chunk table).
 constexpr uint32_t kRunRegs = 8u;
 
-// Chunk c's layout at window base e0: the escapes before each of its parts
-// (esc), its escapes (esc_total) and changed blocks (nch), and its stream
-// bytes.  A part's escapes are its coded values minus those with exponent in
-// [E0, E0 + 6], read off its histogram row.  A part inside a block that spans
-// several parts codes its values only if some part of the block saw a
-// change.  kHashBlocks: hash sender with blocks larger than a part, whose
-// change decision k_stats leaves to the planner: the block's hashes are the
-// sums of its parts' shares; a changed block's go to the hash cache, and each
-// of its parts gets the block's flag (bit 0 of its bitmap word).
-template <bool kHashBlocks>
-__device__ inline uint64_t plan_chunk(uint64_t c, uint64_t n, uint32_t B, uint32_t e0, const Ws& ws,
-                                      const uint16_t* hist, uint64_t* __restrict__ hcache, uint32_t (&esc)[kParts],
-                                      uint32_t& esc_total, uint32_t& nch_out) {
-  const uint32_t ppb = B > kPartValues ? B / kPartValues : 1u;  // parts per block when blocks span parts
+// Coded values of one histogram row (a part's, or a slice's) with exponent
+// in [E0, E0 + 6]: bins E0..E0+6 lie in the two 16-byte words q = E0 / 8 and
+// q + 1 of the row (only in word q when E0 >= 248, and q + 1 is then past the
+// row and not read), at u16 positions r .. r + 6, r = E0 mod 8.
+__device__ inline uint32_t row_in_window(const uint16_t* row_base, uint32_t e0) {
   const uint32_t r0 = e0 & 7u;
-  const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
-  const Partial* pp = ws.partial + c * kParts;
-  // Coded values with exponent in [E0, E0 + 6], per part: bins E0..E0+6
-  // lie in the two 16-byte words q = E0 / 8 and q + 1 of the part's row
-  // (only in word q when E0 >= 248, and q + 1 is then past the row and not
-  // read), at u16 positions r .. r + 6, r = E0 mod 8.
-  uint32_t inwin[kParts];
+  const uint4* row = reinterpret_cast<const uint4*>(row_base) + (e0 >> 3);
+  const uint4 a = row[0], b = (e0 >> 3) < kBins / 8u - 1u ? row[1] : make_uint4(0u, 0u, 0u, 0u);
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t sum = 0;
+#pragma unroll
+  for (uint32_t i = 0; i < 16u; i++) {
+    const uint32_t cnt = (w[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
+    sum += (i - r0 < 7u) ? cnt : 0u;  // r0 <= i <= r0 + 6
+  }
+  return sum;
+}
+
+// A chunk's layout from its parts' coded values, change fields (B <= 16384:
+// the part's changed blocks; larger B: whether the part's share of its block
+// changed) and coded values in the window: the escapes before each part
+// (esc), the chunk's escapes and changed blocks, and its stream bytes.  A
+// part's escapes are its coded values outside the window.  A part inside a
+// block that spans several parts codes its values only if some part of the
+// block saw a change.
+__device__ inline uint64_t chunk_layout(uint32_t nc, uint32_t B, const uint32_t (&coded)[kParts],
+                                        const uint32_t (&pnch)[kParts], const uint32_t (&inwin)[kParts],
+                                        uint32_t (&esc)[kParts], uint32_t& esc_total, uint32_t& nch_out) {
+  const uint32_t ppb = B > kPartValues ? B / kPartValues : 1u;  // parts per block when blocks span parts
+  uint32_t nch = 0;
+  if (B && B <= kPartValues) {
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) nch += pnch[h];
+  } else if (B) {
+    for (uint32_t first = 0; first < kParts; first += ppb) {
+      uint32_t any = 0;
+      for (uint32_t h = first; h < first + ppb; h++) any |= pnch[h];
+      nch += any ? 1u : 0u;
+    }
+  }
+  uint32_t acc = 0;
 #pragma unroll
   for (uint32_t h = 0; h < kParts; h++) {
-    const uint4* row = reinterpret_cast<const uint4*>(hist + (c * kParts + h) * kBins) + (e0 >> 3);
-    const uint4 a = row[0], b = (e0 >> 3) < kBins / 8u - 1u ? row[1] : make_uint4(0u, 0u, 0u, 0u);
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-    uint32_t sum = 0;
+    bool codes = true;
+    if (B > kPartValues) {
+      uint32_t any = 0;
 #pragma unroll
-    for (uint32_t i = 0; i < 16u; i++) {
-      const uint32_t cnt = (w[i >> 1] >> (16u * (i & 1u))) & 0xFFFFu;
-      sum += (i - r0 < 7u) ? cnt : 0u;  // r0 <= i <= r0 + 6
+      for (uint32_t k = 0; k < kParts; k++) any |= (k / ppb == h / ppb) ? pnch[k] : 0u;
+      codes = any != 0u;
     }
-    inwin[h] = sum;
+    esc[h] = acc;
+    acc += codes ? coded[h] - inwin[h] : 0u;
   }
-  uint32_t nchp[kParts] = {1u, 1u, 1u, 1u};
-  uint32_t nch = 0;
+  esc_total = acc;
+  nch_out = nch;
+  const uint64_t planes = B ? uint64_t(nch) * B / 8u : cdiv(nc, 8u);
+  return pad128(nc) + (B ? 128u : 0u) + 3u * pad128(planes) + pad128(acc);
+}
+
+// Chunk c's layout at window base e0 (one thread), from its parts' records
+// in the workspace (one per part).  kHashBlocks: hash sender with blocks
+// larger than a part, whose change decision k_stats leaves to the planner:
+// the block's hashes are the sums of its parts' shares; a changed block's go
+// to the hash cache, and each of its parts gets the block's flag (bit 0 of
+// its bitmap word).
+template <bool kHashBlocks>
+__device__ inline uint64_t plan_chunk(uint64_t c, uint64_t n, uint32_t B, uint32_t e0, const Ws& ws,
+                                      uint64_t* __restrict__ hcache, uint32_t (&esc)[kParts], uint32_t& esc_total,
+                                      uint32_t& nch_out) {
+  const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - c * kChunk));
+  const Partial* pp = ws.partial + c * kParts;
+  uint32_t coded[kParts], pnch[kParts], inwin[kParts];
+#pragma unroll
+  for (uint32_t h = 0; h < kParts; h++) {
+    coded[h] = pp[h].coded;
+    pnch[h] = pp[h].nch;
+    inwin[h] = row_in_window(ws.hist + (c * kParts + h) * kBins, e0);
+  }
   if (kHashBlocks) {
-    // hash sender, blocks spanning ppb parts: the block's hashes are the
-    // sums of its parts' shares; a changed block's go to the cache, and
-    // each of its parts gets the block's flag (bit 0 of its bitmap word)
+    const uint32_t ppb = B / kPartValues;
     for (uint32_t q = 0; q < kChunk / B; q++) {
       const uint64_t blk = c * (kChunk / B) + q;
       bool changed = false;
@@ -1111,35 +1145,12 @@ __device__ inline uint64_t plan_chunk(uint64_t c, uint64_t n, uint32_t B, uint32
               make_uint4(uint32_t(s0), uint32_t(s0 >> 32), uint32_t(s1), uint32_t(s1 >> 32));
       }
       for (uint32_t h = q * ppb; h < (q + 1u) * ppb; h++) {
-        nchp[h] = changed ? 1u : 0u;
+        pnch[h] = changed ? 1u : 0u;
         ws.bitmap[(c * kParts + h) * kPartBitmapWords] = changed ? 1u : 0u;
       }
-      nch += changed ? 1u : 0u;
     }
-  } else {
-    if (B > kPartValues) {
-#pragma unroll
-      for (uint32_t h = 0; h < kParts; h++) nchp[h] = pp[h].nch;
-    }
-    nch = B ? chunk_changed_blocks(pp, B) : 0u;
   }
-  uint32_t acc = 0;
-#pragma unroll
-  for (uint32_t h = 0; h < kParts; h++) {
-    bool codes = true;
-    if (B > kPartValues) {
-      uint32_t any = 0;
-#pragma unroll
-      for (uint32_t k = 0; k < kParts; k++) any |= (k / ppb == h / ppb) ? nchp[k] : 0u;
-      codes = any != 0u;
-    }
-    esc[h] = acc;
-    acc += codes ? pp[h].coded - inwin[h] : 0u;
-  }
-  esc_total = acc;
-  nch_out = nch;
-  const uint64_t planes = B ? uint64_t(nch) * B / 8u : cdiv(nc, 8u);
-  return pad128(nc) + (B ? 128u : 0u) + 3u * pad128(planes) + pad128(acc);
+  return chunk_layout(nc, B, coded, pnch, inwin, esc, esc_total, nch_out);
 }
 
 // The planner's groups: group g of G takes chunks [g per, (g + 1) per).
@@ -1239,7 +1250,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
   // (2) sizes of the group's chunks, one per thread per round of 256.
   auto chunk_size = [&](uint64_t c, uint64_t& esc_out, uint64_t& nch_out) -> uint64_t {
     uint32_t esc[kParts], acc, nch;
-    const uint64_t size = plan_chunk<kHashBlocks>(c, n, B, e0, ws, ws.hist, hcache, esc, acc, nch);
+    const uint64_t size = plan_chunk<kHashBlocks>(c, n, B, e0, ws, hcache, esc, acc, nch);
 #pragma unroll
     for (uint32_t h = 0; h < kParts; h++) ws.partesc[c * kParts + h] = esc[h];
     ws.chunkesc[c] = acc;
@@ -1422,10 +1433,13 @@ __device__ inline void stage_bitmap(uint32_t w, uint32_t* s_bits, uint32_t* s_ra
 // nothing: load, code, write.
 // Tensors of at most kSelfPlanChunks chunks are planned by one group; the
 // write kernel then plans for itself instead (two launches fewer for a
-// shard-sized tensor): every workgroup adds the parts' variance sums as that
-// group would (the same bits, so the same window base), sizes every chunk and
-// scans the sizes in one wave.  Workgroup 0 writes the header and totals,
-// part 0 of each chunk its table and escape-index entries.
+// shard-sized tensor): every workgroup adds the variance sums of k_stats'
+// records in the one-group planner's order, sizes every chunk and scans the
+// sizes in one wave.  With one record per part that gives the planner's bits
+// and window base; with one per slice (ws.ss > 1) the sums round in another
+// order, which can move the window base only where the variance lies within
+// that rounding of a threshold.  Workgroup 0 writes the header and totals,
+// the first slice of part 0 of each chunk its table and escape-index entries.
 constexpr uint64_t kSelfPlanChunks = kPlanMinChunks;
 static_assert(kSelfPlanChunks <= 64u, "one wave scans every chunk");
 struct SelfPlan {
@@ -1438,15 +1452,23 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
   __shared__ double s_f[kPlanWaves];
   __shared__ uint64_t s_u[kPlanWaves];
   __shared__ uint64_t s_r[4];
+  __shared__ uint32_t s_pc[kSelfPlanChunks * kParts], s_pn[kSelfPlanChunks * kParts], s_pi[kSelfPlanChunks * kParts];
   static_assert(kPartThreads == kPlanThreads, "the planner's reduction order");
+  static_assert(kSelfPlanChunks * kParts * kSlices <= kPlanThreads, "one record per thread");
   const uint32_t tid = threadIdx.x;
+  const uint32_t ss = ws.ss;
+  const uint32_t nrec = uint32_t(kParts * nchunks) * ss;
+  // thread t takes record t, as the one-group planner's k_sums takes part t
   double a = 0.0, b = 0.0;
   uint64_t m = 0;
-  for (uint64_t i = tid; i < kParts * nchunks; i += kPlanThreads) {
-    const Partial& p = ws.partial[i];
+  uint32_t r_coded = 0u, r_nch = 0u;
+  if (tid < nrec) {
+    const Partial& p = ws.partial[tid];
     a += p.s1;
     b += p.s2;
     m += p.nf;
+    r_coded = p.coded;
+    r_nch = p.nch;
   }
   a = plan_sum_f64(a, s_f);
   b = plan_sum_f64(b, s_f);
@@ -1461,10 +1483,35 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
   }
   __syncthreads();
   const uint32_t e0 = uint32_t(s_r[1]);
+  // Each record's coded values in the window; a part's records (ss
+  // consecutive lanes of one wave) added by lane exchanges; then one thread
+  // per chunk lays the chunk out.
+  uint32_t r_in = 0u;
+  if (tid < nrec) r_in = row_in_window(ws.hist + uint64_t(tid) * kBins, e0);
+  for (uint32_t off = 1u; off < ss; off <<= 1) {
+    r_coded += uint32_t(__shfl_xor(int(r_coded), int(off)));
+    r_nch += uint32_t(__shfl_xor(int(r_nch), int(off)));
+    r_in += uint32_t(__shfl_xor(int(r_in), int(off)));
+  }
+  if (tid < nrec && tid % ss == 0u) {
+    s_pc[tid / ss] = r_coded;
+    s_pn[tid / ss] = r_nch;
+    s_pi[tid / ss] = r_in;
+  }
+  __syncthreads();
   uint32_t esc[kParts] = {0u, 0u, 0u, 0u}, esc_total = 0u, nch = 0u;
   uint64_t size = 0;
-  if (tid < nchunks)
-    size = plan_chunk<false>(tid, n, B, e0, ws, ws.hist, nullptr, esc, esc_total, nch);
+  if (tid < nchunks) {
+    uint32_t coded[kParts], pnch[kParts], inwin[kParts];
+#pragma unroll
+    for (uint32_t h = 0; h < kParts; h++) {
+      coded[h] = s_pc[kParts * tid + h];
+      pnch[h] = s_pn[kParts * tid + h];
+      inwin[h] = s_pi[kParts * tid + h];
+    }
+    const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - uint64_t(tid) * kChunk));
+    size = chunk_layout(nc, B, coded, pnch, inwin, esc, esc_total, nch);
+  }
   const uint64_t base = table_end(nchunks);
   uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
@@ -1610,7 +1657,12 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   bool plan_failed = false;
   // self-planned: the chunk's bitmap words are fetched with the plan's inputs
   __shared__ uint32_t s_pw[kSelfPlan ? kBitmapWords : 1u];
-  const uint32_t pw_l = (kSelfPlan && kCiera && tid < kBitmapWords) ? ws.bitmap[uint64_t(c) * kBitmapWords + tid] : 0u;
+  uint32_t pw_l = 0u;
+  if (kSelfPlan && kCiera && tid < kBitmapWords) {
+    // word tid % 8 of part tid / 8: the OR of the part's records (one per slice)
+    const uint64_t rec0 = (uint64_t(c) * kParts + tid / kPartBitmapWords) * ws.ss;
+    for (uint32_t sl = 0; sl < ws.ss; sl++) pw_l |= ws.bitmap[(rec0 + sl) * kPartBitmapWords + tid % kPartBitmapWords];
+  }
   if (kSelfPlan) {
     const SelfPlan sp = self_plan(n, nchunks, c, h, h == 0u && slice == 0u, wg, kCiera ? B : 0u, e0_override, out,
                                   out_size, ws);
@@ -3454,26 +3506,34 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   if (out_capacity < max_size(n, B)) return CIERA_ERR_CAPACITY;
   const uint64_t nchunks = cdiv(n, kChunk);
   if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
-  const Ws ws = ws_bind(d_ws, nchunks);
+  // A tensor of at most kSelfPlanChunks chunks (one planning group) is
+  // planned by the write kernel itself, unless a planner shape is forced.
+  // Its k_stats then runs one workgroup per slice of a part (kSlices per
+  // part, one record each), except for the hash sender and for blocks that
+  // span slices.
+  const bool self_plan = plan_groups == 0u && nchunks >= 1u && nchunks <= kSelfPlanChunks && !(hashed && B > kPartValues);
+  const bool stats_sliced = self_plan && !hashed && (!ciera || B <= 8u * (kPartUnits / kSlices));
+  static_assert(kSelfPlanChunks <= kSliceChunks, "the workspace has a record per slice");
+  Ws ws = ws_bind(d_ws, nchunks);
+  ws.ss = stats_sliced ? kSlices : 1u;
   const uint32_t lb = ciera ? log2u(B) : 0u;
   uint64_t* hcache = static_cast<uint64_t*>(d_hash);
   const uint16_t* x = static_cast<const uint16_t*>(d_x);
   uint8_t* out = static_cast<uint8_t*>(d_out);
   (void)hipGetLastError();
   if (nchunks) {
+    const dim3 grid(uint32_t(nchunks * kParts)), sgrid(uint32_t(nchunks * kParts * kSlices));
     if (hashed)
-      launch(k_stats<true, true>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n,
-             static_cast<uint8_t*>(d_hash), lb, ws);
+      launch(k_stats<true, true, 1u>, grid, dim3(kPartThreads), stream, x, n, static_cast<uint8_t*>(d_hash), lb, ws);
+    else if (ciera && stats_sliced)
+      launch(k_stats<true, false, kSlices>, sgrid, dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
     else if (ciera)
-      launch(k_stats<true, false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, d_cache, lb,
-             ws);
+      launch(k_stats<true, false, 1u>, grid, dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
+    else if (stats_sliced)
+      launch(k_stats<false, false, kSlices>, sgrid, dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
     else
-      launch(k_stats<false, false>, dim3(uint32_t(nchunks * kParts)), dim3(kPartThreads), stream, x, n, nullptr, 0u,
-             ws);
+      launch(k_stats<false, false, 1u>, grid, dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
   }
-  // A tensor of at most kSelfPlanChunks chunks (one planning group) is
-  // planned by the write kernel itself, unless a planner shape is forced.
-  const bool self_plan = plan_groups == 0u && nchunks >= 1u && nchunks <= kSelfPlanChunks && !(hashed && B > kPartValues);
   if (!self_plan) {
     uint64_t per = 0;
     uint32_t groups = 0;
@@ -3490,7 +3550,6 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
     // a self-planned tensor is small: kSlices workgroups per part
     const dim3 grid(uint32_t(nchunks * kParts));
     const dim3 sgrid(uint32_t(nchunks * kParts * kSlices));
-    static_assert(kSelfPlanChunks <= kSliceChunks, "the workspace has an error slot per slice");
     if (ciera && self_plan)
       launch(k_write<true, true, kSlices>, sgrid, dim3(kPartThreads), stream, x, n, lb, out, out_capacity, d_out_size,
              e0_override, ws);
@@ -3586,10 +3645,10 @@ ciera_status encode_rans_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* 
   (void)hipGetLastError();
   if (nchunks) {
     if (ciera) {
-      launch(k_stats<true, false>, dim3(parts), dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
+      launch(k_stats<true, false, 1u>, dim3(parts), dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
       launch(k_rans_enc<true>, dim3(uint32_t(nchunks)), dim3(kPartThreads), stream, x, n, nchunks, lb, out, ws);
     } else {
-      launch(k_stats<false, false>, dim3(parts), dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
+      launch(k_stats<false, false, 1u>, dim3(parts), dim3(kPartThreads), stream, x, n, nullptr, 0u, ws);
       launch(k_rans_enc<false>, dim3(uint32_t(nchunks)), dim3(kPartThreads), stream, x, n, nchunks, 0u, out, ws);
     }
   }
