@@ -792,13 +792,13 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     // The block's sum (mod 2^64) over its threads, in its last thread: a wave
     // scan minus the scan before the block's first lane, or, for blocks (or
     // a part's share of a block) wider than a wave, the waves' totals.
-    uint64_t s0 = p0, s1 = p1;
+    uint64_t hs0 = p0, hs1 = p1;
     if (hb_threads > 1u) {
       const uint64_t i0 = wave_incl_scan_u64(p0), i1 = wave_incl_scan_u64(p1);
       if (hb_threads <= 64u) {
-        const uint32_t first = lane & ~(hb_threads - 1u);
-        s0 = i0 - shfl_u64(i0 - p0, first);
-        s1 = i1 - shfl_u64(i1 - p1, first);
+        const uint32_t lead = lane & ~(hb_threads - 1u);
+        hs0 = i0 - shfl_u64(i0 - p0, lead);
+        hs1 = i1 - shfl_u64(i1 - p1, lead);
       } else {
         if (lane == 63u) {
           s_wh[0][wave] = i0;
@@ -806,10 +806,10 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
         }
         __syncthreads();
         const uint32_t wpb = hb_threads / 64u, wfirst = (wave / wpb) * wpb;
-        s0 = s1 = 0u;
+        hs0 = hs1 = 0u;
         for (uint32_t q = 0; q < wpb; q++) {
-          s0 += s_wh[0][wfirst + q];
-          s1 += s_wh[1][wfirst + q];
+          hs0 += s_wh[0][wfirst + q];
+          hs1 += s_wh[1][wfirst + q];
         }
       }
     }
@@ -817,10 +817,10 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       // decide: a changed block's new hashes go to the cache and its bit to s_bits
       bool changed = false;
       if (decider) {
-        changed = s0 != hc0 || s1 != hc1;
+        changed = hs0 != hc0 || hs1 != hc1;
         if (changed)
           *reinterpret_cast<uint4*>(hcache + 2u * hblk) =
-              make_uint4(uint32_t(s0), uint32_t(s0 >> 32), uint32_t(s1), uint32_t(s1 >> 32));
+              make_uint4(uint32_t(hs0), uint32_t(hs0 >> 32), uint32_t(hs1), uint32_t(hs1 >> 32));
       }
       if (hb_threads <= 64u) {
         const uint64_t m = __ballot(changed);  // set only at the blocks' last lanes
@@ -838,8 +838,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       }
     } else if (tid == kPartThreads - 1u) {
       // a block spans several parts: k_plan adds the parts' shares and decides
-      ws.phash[2u * wg] = s0;
-      ws.phash[2u * wg + 1u] = s1;
+      ws.phash[2u * wg] = hs0;
+      ws.phash[2u * wg + 1u] = hs1;
     }
     __syncthreads();  // the exponent words are no longer read; s_bits complete
     for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
@@ -1445,14 +1445,18 @@ static_assert(kSelfPlanChunks <= 64u, "one wave scans every chunk");
 struct SelfPlan {
   uint64_t begin;
   uint32_t e0, esc_before, esc_chunk, esc_part;
+  // one record per slice (ws.ss > 1): the escapes of slice `slice` of the
+  // part and those of the part's slices before it
+  uint32_t esc_slice, esc_slice_before;
 };
-__device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, uint32_t h, bool lead, uint32_t wg,
-                                     uint32_t B, int e0_override, uint8_t* __restrict__ out,
+__device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, uint32_t h, uint32_t slice, bool lead,
+                                     uint32_t wg, uint32_t B, int e0_override, uint8_t* __restrict__ out,
                                      uint64_t* __restrict__ out_size, const Ws& ws) {
   __shared__ double s_f[kPlanWaves];
   __shared__ uint64_t s_u[kPlanWaves];
-  __shared__ uint64_t s_r[4];
+  __shared__ uint64_t s_r[5];
   __shared__ uint32_t s_pc[kSelfPlanChunks * kParts], s_pn[kSelfPlanChunks * kParts], s_pi[kSelfPlanChunks * kParts];
+  __shared__ uint32_t s_re[kPlanThreads];  // each record's escapes
   static_assert(kPartThreads == kPlanThreads, "the planner's reduction order");
   static_assert(kSelfPlanChunks * kParts * kSlices <= kPlanThreads, "one record per thread");
   const uint32_t tid = threadIdx.x;
@@ -1488,6 +1492,9 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
   // per chunk lays the chunk out.
   uint32_t r_in = 0u;
   if (tid < nrec) r_in = row_in_window(ws.hist + uint64_t(tid) * kBins, e0);
+  // a record's escapes (used with one record per slice, where no block spans
+  // slices, so that all of a record's coded values are written)
+  s_re[tid] = r_coded - r_in;
   for (uint32_t off = 1u; off < ss; off <<= 1) {
     r_coded += uint32_t(__shfl_xor(int(r_coded), int(off)));
     r_nch += uint32_t(__shfl_xor(int(r_nch), int(off)));
@@ -1504,10 +1511,10 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
   if (tid < nchunks) {
     uint32_t coded[kParts], pnch[kParts], inwin[kParts];
 #pragma unroll
-    for (uint32_t h = 0; h < kParts; h++) {
-      coded[h] = s_pc[kParts * tid + h];
-      pnch[h] = s_pn[kParts * tid + h];
-      inwin[h] = s_pi[kParts * tid + h];
+    for (uint32_t q = 0; q < kParts; q++) {
+      coded[q] = s_pc[kParts * tid + q];
+      pnch[q] = s_pn[kParts * tid + q];
+      inwin[q] = s_pi[kParts * tid + q];
     }
     const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - uint64_t(tid) * kChunk));
     size = chunk_layout(nc, B, coded, pnch, inwin, esc, esc_total, nch);
@@ -1556,6 +1563,12 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
   }
   if (wg == 0u)  // the padding words after the chunk table and the escape index
     for (uint64_t i = 2u * nchunks + 1u + tid; i < (base - kHeader) / 8u; i += kPartThreads) table[i] = 0u;
+  if (tid == 0u) {
+    const uint32_t rec0 = uint32_t(c * kParts + h) * ss;
+    uint32_t before = 0u;
+    for (uint32_t q = 0; q < slice && q < ss; q++) before += s_re[rec0 + q];
+    s_r[4] = (uint64_t(slice < ss ? s_re[rec0 + slice] : 0u) << 32) | before;
+  }
   __syncthreads();
   SelfPlan r;
   r.begin = s_r[0];
@@ -1563,6 +1576,8 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
   r.esc_before = uint32_t(s_r[2]);
   r.esc_chunk = uint32_t(s_r[3]);
   r.esc_part = uint32_t(s_r[3] >> 32);
+  r.esc_slice_before = uint32_t(s_r[4]);
+  r.esc_slice = uint32_t(s_r[4] >> 32);
   return r;
 }
 
@@ -1619,7 +1634,10 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   const uint32_t u0 = pu0 + slice * kRange;
 
   // Load the range first: all of a thread's 16-byte loads go out before any
-  // is used; a slice also loads the part's units before it.
+  // is used.  A slice whose escapes the plan does not count per slice (the
+  // statistics kept one record per part) also loads the part's units before
+  // it, to count their escapes.
+  const bool counted = kS > 1u && ws.ss == kS;  // the plan has this slice's escapes
   Unit v[kU];
   if (8u * (u0 + kRange) <= nc) {
 #pragma unroll
@@ -1637,7 +1655,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   Unit ve[kEarly > 0u ? kEarly : 1u];
 #pragma unroll
   for (uint32_t k = 0; k < kEarly; k++) ve[k].w[0] = ve[k].w[1] = ve[k].w[2] = ve[k].w[3] = 0u;
-  if (kEarly > 0u) {
+  if (kEarly > 0u && !counted) {
     const uint32_t nearly = slice * kU;
     if (8u * u0 <= nc) {
 #pragma unroll
@@ -1654,6 +1672,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   const uint64_t nchunks = cdiv(n, kChunk);
   uint64_t begin;
   uint32_t esc_before, esc_chunk, esc_part, e0;
+  uint32_t esc_slice = 0u, esc_slice_before = 0u;
   bool plan_failed = false;
   // self-planned: the chunk's bitmap words are fetched with the plan's inputs
   __shared__ uint32_t s_pw[kSelfPlan ? kBitmapWords : 1u];
@@ -1664,12 +1683,14 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     for (uint32_t sl = 0; sl < ws.ss; sl++) pw_l |= ws.bitmap[(rec0 + sl) * kPartBitmapWords + tid % kPartBitmapWords];
   }
   if (kSelfPlan) {
-    const SelfPlan sp = self_plan(n, nchunks, c, h, h == 0u && slice == 0u, wg, kCiera ? B : 0u, e0_override, out,
-                                  out_size, ws);
+    const SelfPlan sp = self_plan(n, nchunks, c, h, slice, h == 0u && slice == 0u, wg, kCiera ? B : 0u, e0_override,
+                                  out, out_size, ws);
     begin = sp.begin;
     esc_before = sp.esc_before;
     esc_chunk = sp.esc_chunk;
     esc_part = sp.esc_part;
+    esc_slice = sp.esc_slice;
+    esc_slice_before = sp.esc_slice_before;
     e0 = sp.e0;
   } else {
     begin = reinterpret_cast<const uint64_t*>(out + kHeader)[c];
@@ -1725,9 +1746,12 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
                                  : u0 + kRange;
 
   // A slice's first escape: the part's escapes before u0 (values of coded
-  // units whose code is 0), counted from the units loaded above.
+  // units whose code is 0), from the plan, or counted from the units loaded
+  // above.
   uint32_t zb = 0;
-  if (kS > 1u) {
+  if (counted) {
+    zb = esc_slice_before;
+  } else if (kS > 1u) {
     uint32_t z = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kEarly; k++) {
@@ -1784,11 +1808,12 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     }
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
-  // The count must match what the plan read off the histogram (a slice: its
-  // escapes and those before it stay within the part's, and the last slice's
-  // end where the part's do); a mismatch would overrun the escape section, so
-  // no escapes are written and the error word reports it.
-  const bool esc_ok = final_slice ? zb + pesc == esc_part : zb + pesc <= esc_part;
+  // The count must match what the plan read off the histograms (a slice: its
+  // escapes and those before it stay within the part's, the last slice's end
+  // where the part's do, and one the plan counted has its planned count); a
+  // mismatch would overrun the escape section, so no escapes are written and
+  // the error word reports it.
+  const bool esc_ok = (final_slice ? zb + pesc == esc_part : zb + pesc <= esc_part) && (!counted || pesc == esc_slice);
   if (tid == 0) ws.err[wg] = esc_ok ? 0u : uint32_t(CIERA_ERR_INTERNAL);
   // planes: LDS -> HBM in 8-byte pieces over the owned range, clipped to the
   // padded plane length
@@ -3077,9 +3102,9 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_enc(const uint16_t* __res
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (uint32_t i = 0; i < 8u; i++) {
-          const uint32_t d = d0 + 2u * i;
-          if (d >= d_lo && d < d_lo + d_len)
-            *reinterpret_cast<uint16_t*>(pay + d) = uint16_t(w[i / 2u] >> (16u * (i % 2u)));
+          const uint32_t di = d0 + 2u * i;
+          if (di >= d_lo && di < d_lo + d_len)
+            *reinterpret_cast<uint16_t*>(pay + di) = uint16_t(w[i / 2u] >> (16u * (i % 2u)));
         }
       }
     }
