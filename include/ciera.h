@@ -246,7 +246,10 @@ ciera_status ciera_read_error(const void* d_ws, hipStream_t stream);
  * limited to 2^39 (CIERA_ERR_ARG above); the stream equals zip3_encode_ex's
  * with e0_override = *d_e0.  Within the call, workgroups
  * wait on each other through the workspace (bounded waits; a wait that does
- * not end is reported as CIERA_ERR_INTERNAL by ciera_read_error). */
+ * not end is reported as CIERA_ERR_INTERNAL by ciera_read_error).  A tensor
+ * of at most 16 chunks (2^20 values; its 2 MiB stay in the GPU's last-level
+ * cache) is encoded by the two launches of zip3_encode with the given window
+ * base instead: x is read twice there, and no workgroup waits. */
 ciera_status zip3_encode_e0(const void* d_x, uint64_t n, const uint8_t* d_e0, void* d_out, uint64_t out_capacity,
                             void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream);
 
@@ -263,7 +266,9 @@ ciera_status zip3_encode_e0(const void* d_x, uint64_t n, const uint8_t* d_e0, vo
  * equal ciera_encode_ex's with e0_override = *d_e0.  A *d_e0 above 249 leaves
  * the cache as it was and the stream and *d_out_size as zip3_encode_e0 does
  * (CIERA_ERR_ARG).  Workgroups wait on each other through the
- * workspace as in zip3_encode_e0. */
+ * workspace as in zip3_encode_e0, and a tensor of at most 16 chunks is
+ * encoded by ciera_encode's two launches with the given window base, as
+ * there. */
 ciera_status ciera_encode_e0(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, const uint8_t* d_e0,
                              void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
                              hipStream_t stream);

@@ -53,6 +53,7 @@ constexpr uint32_t kBitmapWords = 32u;  // 1024 blocks per chunk at B = 64
 constexpr uint64_t kMaxN = 1ull << 40;
 constexpr uint64_t kHeader = 128u;
 constexpr uint32_t kMaxE0 = 249u;
+constexpr uint32_t kBadE0 = ~0u;  // control-block E0 of a call whose given window base is out of range
 // 16383 / (28 ln 2) as a double: the variance threshold of window base k is
 // kK0 * 4^k.
 constexpr double kK0 = 0x1.a610ca4a234eep+9;
@@ -210,6 +211,7 @@ struct Ws {
   uint8_t* rslot;
   uint32_t spin_limit;  // polls before a wait gives up (kSpinLimit unless a test lowers it)
   uint32_t ss;          // k_stats records per part: 1, or kSlices (one per slice) for self-planned tensors
+  const uint8_t* e0_src;  // self-planned encode with a known window base: its byte in device memory, else null
 };
 
 // The bound the next calls pass to their kernels (ciera_set_wait_limit).
@@ -235,6 +237,7 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.rslot = nullptr;
   w.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
   w.ss = 1u;
+  w.e0_src = nullptr;
   return w;
 }
 
@@ -643,6 +646,9 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   }
   const uint32_t first = x[0];
   const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
+  // a window base given in device memory that is out of range: the encode
+  // writes nothing, so the sender cache is left as it was
+  const bool keep_cache = ws.e0_src != nullptr && ws.e0_src[0] > kMaxE0;
 
   // Hash sender, blocks within the part: the hash phase gives each block
   // hb_threads consecutive threads (8 units each); the last of them decides
@@ -740,7 +746,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       if (kCiera && !kHash) {
         const uint64_t m = __ballot(diff);
         if (m != 0u) {
-          if (live && line_has_change(m)) store_bytes8(cache + start + 8ull * u, ucnt, ue);
+          if (live && !keep_cache && line_has_change(m)) store_bytes8(cache + start + 8ull * u, ucnt, ue);
           // first block of the wave's units, relative to the part
           const uint32_t lbw = ((8u * (u0 + j * kPartThreads + 64u * wave)) >> log2B) - blk0;
           uint32_t bits = 0;
@@ -1483,10 +1489,25 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
       var = (b - a * a / double(m)) / double(m - 1u);
       if (!(var > 0.0)) var = 0.0;
     }
-    s_r[1] = (e0_override >= 0) ? uint32_t(e0_override) : window_base(var, m);
+    s_r[1] = ws.e0_src ? uint32_t(ws.e0_src[0])
+                       : ((e0_override >= 0) ? uint32_t(e0_override) : window_base(var, m));
   }
   __syncthreads();
   const uint32_t e0 = uint32_t(s_r[1]);
+  if (e0 > kMaxE0) {
+    // only from device memory: the stream gets its first header word alone,
+    // whose E0 byte keeps the bad value (a decoder refuses it, and so does a
+    // next encode taking its window base from that byte), and no size
+    if (wg == 0u && tid == 0u) {
+      *reinterpret_cast<uint64_t*>(out) = uint64_t(e0) << 56;
+      *out_size = 0u;
+      ws.ctrl->e0 = kBadE0;
+      ws.ctrl->n_err_slots = gridDim.x;
+    }
+    SelfPlan bad{};
+    bad.e0 = kBadE0;
+    return bad;
+  }
   // Each record's coded values in the window; a part's records (ss
   // consecutive lanes of one wave) added by lane exchanges; then one thread
   // per chunk lays the chunk out.
@@ -1692,6 +1713,10 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     esc_slice = sp.esc_slice;
     esc_slice_before = sp.esc_slice_before;
     e0 = sp.e0;
+    if (e0 == kBadE0) {  // the same for every workgroup
+      if (tid == 0) ws.err[wg] = uint32_t(CIERA_ERR_ARG);
+      return;
+    }
   } else {
     begin = reinterpret_cast<const uint64_t*>(out + kHeader)[c];
     esc_before = ws.partesc[c * kParts + h];
@@ -1863,7 +1888,6 @@ constexpr uint64_t kFlagSize = 1ull << 62;  // look-back only: a predecessor's s
 constexpr uint64_t kFlagIncl = 2ull << 62;
 constexpr uint64_t kFlagFail = 3ull << 62;  // the chunk's last part gave up a wait: no offset follows
 constexpr uint64_t kValMask = (1ull << 62) - 1u;
-constexpr uint32_t kBadE0 = ~0u;
 constexpr uint32_t kDoneShift = 40u;           // ctrl->done_esc: chunks << 40 | escapes
 constexpr uint64_t kMaxSingleReadN = 1ull << 39;  // keeps both fields of done_esc in range
 
@@ -3515,9 +3539,12 @@ void launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t stream, A..
 
 // d_hash non-null: ciera mode with the block-hash sender state instead of the
 // exponent cache (d_cache unused).
+// d_e0: a window base in device memory (the single-read entry points on
+// tensors of at most kSelfPlanChunks chunks), else null.
 ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cache, void* d_out,
                          uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
-                         int e0_override, uint32_t plan_groups, hipStream_t stream, void* d_hash = nullptr) {
+                         int e0_override, uint32_t plan_groups, hipStream_t stream, void* d_hash = nullptr,
+                         const uint8_t* d_e0 = nullptr) {
   const bool ciera = B != 0u;
   const bool hashed = d_hash != nullptr;
   if (n > kMaxN) return CIERA_ERR_ARG;
@@ -3539,8 +3566,10 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   const bool self_plan = plan_groups == 0u && nchunks >= 1u && nchunks <= kSelfPlanChunks && !(hashed && B > kPartValues);
   const bool stats_sliced = self_plan && !hashed && (!ciera || B <= 8u * (kPartUnits / kSlices));
   static_assert(kSelfPlanChunks <= kSliceChunks, "the workspace has a record per slice");
+  if (d_e0 && (!self_plan || hashed || e0_override >= 0)) return CIERA_ERR_ARG;
   Ws ws = ws_bind(d_ws, nchunks);
   ws.ss = stats_sliced ? kSlices : 1u;
+  ws.e0_src = d_e0;
   const uint32_t lb = ciera ? log2u(B) : 0u;
   uint64_t* hcache = static_cast<uint64_t*>(d_hash);
   const uint16_t* x = static_cast<const uint16_t*>(d_x);
@@ -3604,6 +3633,12 @@ ciera_status encode_known_e0_impl(const void* d_x, uint64_t n, uint32_t B, uint8
   if (out_capacity < max_size(n, B)) return CIERA_ERR_CAPACITY;
   const uint64_t nchunks = cdiv(n, kChunk);
   if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
+  // A tensor of at most kSelfPlanChunks chunks (2 MiB of input, which the
+  // MALL holds) runs the self-planned two-launch encode with the given
+  // window base: faster there than one read with waits between workgroups.
+  if (nchunks >= 1u && nchunks <= kSelfPlanChunks)
+    return encode_impl(d_x, n, B, d_cache, d_out, out_capacity, d_ws, ws_bytes, d_out_size, -1, 0u, stream, nullptr,
+                       d_e0);
   const Ws ws = ws_bind(d_ws, nchunks);
   const uint16_t* x = static_cast<const uint16_t*>(d_x);
   uint8_t* out = static_cast<uint8_t*>(d_out);
