@@ -1,6 +1,6 @@
 // ciera.hip -- HIP kernels and C ABI of the lossless BF16 codec, gfx950.
 //
-// Encode is three kernels on the caller's stream:
+// Encode is four kernels on the caller's stream:
 //   k_stats   one workgroup per quarter chunk ("part", 16,384 values), one
 //             pass over the input: FP64 partial sums for the tensor's
 //             variance (ZipCCL research digest, section 3.1: sigma from one
@@ -8,26 +8,35 @@
 //             against the sender's exponent cache and the cache update (CIERA
 //             page, section 3.1); and an exponent histogram of the values to
 //             be coded.
-//   k_plan    up to 256 workgroups over ranges of chunks: reduce the partial
-//             sums in a fixed order and pick the window base E0 (integer
-//             nearest x_opt = log2 sigma + 0.5 log2(14 ln2 / 16383), digest
-//             section 3.1, evaluated as var >= K0 4^k); each part's escape
-//             count is its number of coded values outside [E0, E0+6], read
-//             off the histogram, so chunk sizes follow exactly and a scan
-//             turns them into the chunk table (the size exchange of the
-//             digest's Figure 1, done on one GPU).
+//   k_sums    per planning group (a range of chunks), the parts' partial
+//             sums added in a fixed order.
+//   k_plan    the same groups (up to 256): add the groups' sums in a fixed
+//             order and pick the window base E0 (integer nearest x_opt =
+//             log2 sigma + 0.5 log2(14 ln2 / 16383), digest section 3.1,
+//             evaluated as var >= K0 4^k); each part's escape count is its
+//             number of coded values outside [E0, E0+6], read off the
+//             histogram, so chunk sizes follow exactly and a scan turns them
+//             into the chunk table (the size exchange of the digest's
+//             Figure 1, done on one GPU).
 //   k_write   one workgroup per part, no synchronisation with any other:
 //             splits values into sign+mantissa bytes and 3-bit codes and
 //             writes the 128-byte-aligned sections at offsets k_plan fixed
 //             (digest, section 3.1 last paragraph).
+// A tensor of at most 16 chunks is two kernels: k_stats, then k_write,
+// which plans for itself.
 // Decode is one kernel, k_decode, one workgroup per part; parts are
-// independent because the chunk table holds every chunk offset and a part
-// finds its first escape by counting code-0 slots in the planes before it.
+// independent because the chunk table holds every chunk offset and the
+// escape index each part's first escape.
+// The single-read encodes (window base given) are k_prep1 + k_write1; the
+// rANS modes k_stats + k_rans_enc + k_rans_finish, and k_rans_dec.
 //
 // Work mapping: a "unit" is 8 consecutive values (one 16-byte load).  A chunk
 // has 8192 units.  In k_stats, k_write and k_decode part h covers units
 // [2048h, 2048h + 2048) and thread t of its 256 handles unit 2048h + 256j + t
-// (j = 0..7), so each wave instruction moves 1 KiB of contiguous input.
+// (j = 0..7), so each wave instruction moves 1 KiB of contiguous input.  For
+// tensors of at most 16 chunks (k_stats, k_write) or 32 (k_decode) each part
+// is split into four slices of 512 units, one workgroup each, so that a
+// shard-sized tensor spreads over every CU.
 // Blocks (B >= 64) never split a unit, and chunks never split a block.  All
 // data movement is integer: sign, NaN payloads, subnormals and -0 never pass
 // through floating-point registers.
