@@ -569,7 +569,7 @@ def main() -> int:
                   "encode_algorithmic_bytes": alg_h,
                   "kernels": {nm: round(v, 5) for nm, v in hk.items()},
                   # its k_stats hashes every exponent word twice: VALU-bound
-                  "alu_roofline": alu_roofline("k_stats<true, true>", "k_stats_hash", args.workload, B,
+                  "alu_roofline": alu_roofline("k_stats<true, true, 1u>", "k_stats_hash", args.workload, B,
                                                hk["k_stats"])}
         del h_pristine, h_cache, out_h
 
