@@ -1384,7 +1384,10 @@ __device__ inline uint32_t part_incl_scan_u32(uint32_t v, uint32_t* s_w) {
 // Escape positions within a part: cnt[j] (0..8) per unit, units ordered
 // (j, wave, lane).  base[j] receives the escapes in earlier units of the part;
 // returns the part's total.  Every thread of the workgroup must call it.
-template <uint32_t N>
+// kSettle: base[] is computed before the first barrier, so the scan's partial
+// sums die there; otherwise the compiler may keep them (a dozen registers)
+// until the totals come back, which measured faster for k_write alone.
+template <uint32_t N, bool kSettle = true>
 __device__ inline uint32_t part_escape_scan(const uint32_t (&cnt)[N], uint32_t (&base)[N],
                                             uint32_t* s_tot /* N * kPartWaves + 1 */) {
   static_assert(N % 2u == 0u && N <= kUPT, "unit pairs, at most kUPT per thread");
@@ -1395,7 +1398,8 @@ __device__ inline uint32_t part_escape_scan(const uint32_t (&cnt)[N], uint32_t (
   for (uint32_t p = 0; p < N / 2u; p++) {
     const uint32_t packed = cnt[2 * p] | (cnt[2 * p + 1] << 16);
     const uint32_t incl = wave_incl_scan(packed);
-    const uint32_t excl = incl - packed;
+    uint32_t excl = incl - packed;
+    if (kSettle) __asm__ volatile("" : "+v"(excl));  // opaque: the partial sums end here
     base[2 * p] = excl & 0xFFFFu;
     base[2 * p + 1] = excl >> 16;
     if (lane == 63u) {
@@ -1631,6 +1635,23 @@ __device__ inline void stage_escapes(const Unit (&v)[N], const uint32_t (&emask)
   }
 }
 
+// The same from the units' exponent bytes, with the escape masks packed four
+// to a word (unit j's in byte j % 4 of em4[j / 4]).
+template <uint32_t N>
+__device__ inline void stage_escapes_ex(const uint2 (&ex)[N], const uint32_t (&em4)[N / 4u], const uint32_t (&base)[N],
+                                        uint8_t* s_esc) {
+#pragma unroll
+  for (uint32_t j = 0; j < N; j++) {
+    uint32_t em = (em4[j / 4u] >> (8u * (j % 4u))) & 0xFFu;
+    uint32_t at = base[j];
+    while (em) {
+      const uint32_t k = __builtin_ctz(em);
+      em &= em - 1u;
+      s_esc[at++] = uint8_t(byte_of(ex[j], k));
+    }
+  }
+}
+
 // One part of a chunk (kS = 1) or one of its kS slices (self-planned
 // tensors only): a slice codes units [u0, u0 + kPartUnits / kS) and counts
 // the escapes of the part's units before u0 to place its own.
@@ -1841,7 +1862,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
       }
     }
   }
-  const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
+  const uint32_t pesc = part_escape_scan<kU, false>(cnt, base, s_tot);  // its barriers also complete the plane staging
   // The count must match what the plan read off the histograms (a slice: its
   // escapes and those before it stay within the part's, the last slice's end
   // where the part's do, and one the plan counted has its planned count); a
@@ -2120,6 +2141,14 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
       }
     }
   }
+  // From here on a unit lives as its exponent bytes and its sign+mantissa
+  // bytes (half the registers of the loaded words, held until the stores).
+  uint2 ex[kUPT], smb[kUPT];
+#pragma unroll
+  for (uint32_t j = 0; j < kUPT; j++) {
+    ex[j] = unit_exponents(v[j]);
+    smb[j] = unit_sm(v[j]);
+  }
   const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
   for (uint32_t i = tid; i < 3u * kStage / 16u; i += kPartThreads)
     reinterpret_cast<uint4*>(s_planes)[i] = make_uint4(0u, 0u, 0u, 0u);
@@ -2143,7 +2172,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
       uint2 e = make_uint2(0u, 0u);
       if (u < nunits) {
         cnt = min(8u, nc - 8u * u);
-        e = unit_exponents(v[j]);
+        e = ex[j];
         const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * (cnt & 7u))) - 1u);
         diff = (((uint64_t(e.y ^ old[j].y) << 32) | (e.x ^ old[j].x)) & keep) != 0u;
       }
@@ -2158,34 +2187,31 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
     }
     __syncthreads();  // s_pbits complete
   }
-  // the part's changed blocks, and those before each bitmap word
-  uint32_t pnch = 0, prank[kPartBitmapWords];
+  // the part's changed blocks; lane k < kPartBitmapWords holds those before
+  // bitmap word k
+  uint32_t pnch = 0, prank_l = 0;
   if (kCiera) {
-#pragma unroll
-    for (uint32_t k = 0; k < kPartBitmapWords; k++) {
-      prank[k] = pnch;
-      pnch += __popc(s_pbits[k]);
-    }
+    const uint32_t pc = lane < kPartBitmapWords ? uint32_t(__popc(s_pbits[lane])) : 0u;
+    const uint32_t incl = wave_incl_scan(pc);
+    prank_l = incl - pc;
+    pnch = uint32_t(__builtin_amdgcn_readlane(int(incl), int(kPartBitmapWords - 1u)));
   }
 
   // Code every unit that is coded: plane bytes into LDS at the unit's plane
   // byte within the part's slots (zip3: the unit's own byte), escape masks.
-  uint32_t cnt[kUPT], base[kUPT], emask[kUPT];
+  uint32_t cnt[kUPT], base[kUPT], em4[kUPT / 4u] = {};  // escape masks, unit j in byte j % 4 of em4[j / 4]
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
     const uint32_t u = pu0 + j * kPartThreads + tid;
     const uint32_t ul = u - pu0;
     cnt[j] = 0u;
-    emask[j] = 0u;
     bool coded = true;
     uint32_t at = ul;
     if (kCiera && B <= kPartValues) {
       const uint32_t upb_log = log2B - 3u;  // units per block
       const uint32_t blk = ul >> upb_log;
       const uint32_t word = s_pbits[blk >> 5];
-      uint32_t before = 0;  // changed blocks in the words before blk's (constant indices: no private array)
-#pragma unroll
-      for (uint32_t k = 0; k < kPartBitmapWords; k++) before = (k == (blk >> 5)) ? prank[k] : before;
+      const uint32_t before = uint32_t(__shfl(int(prank_l), int(blk >> 5)));  // changed blocks in the words before blk's
       coded = (word >> (blk & 31u)) & 1u;
       at = ((before + __popc(word & ((1u << (blk & 31u)) - 1u))) << upb_log) + (ul & ((1u << upb_log) - 1u));
     }
@@ -2194,13 +2220,15 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
       const uint32_t vmask = (valid == 8u) ? 0xFFu : ((1u << valid) - 1u);
       uint32_t cp[4];
 #pragma unroll
-      for (int i = 0; i < 4; i++) cp[i] = code_pair(exp_pair(v[j].w[i]), bias);
+      for (int i = 0; i < 4; i++)
+        cp[i] = code_pair(perm(0u, i < 2 ? ex[j].x : ex[j].y, (i & 1) ? 0x0C030C02u : 0x0C010C00u), bias);
       const uint32_t p = unit_planes(cp) & (vmask * 0x010101u);
       s_planes[at] = uint8_t(p);
       s_planes[kStage + at] = uint8_t(p >> 8);
       s_planes[2u * kStage + at] = uint8_t(p >> 16);
-      emask[j] = ~(p | (p >> 8) | (p >> 16)) & vmask;
-      cnt[j] = __popc(emask[j]);
+      const uint32_t em = ~(p | (p >> 8) | (p >> 16)) & vmask;
+      em4[j / 4u] |= em << (8u * (j % 4u));
+      cnt[j] = __popc(em);
     }
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);  // its barriers also complete the plane staging
@@ -2208,7 +2236,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   if (kCiera) field = (B <= 512u) ? pnch : (B <= kPartValues ? s_pbits[0] : (s_pbits[0] & 1u));
   if (tid == 0) store_relaxed(&ws.pcount[c * kPcountStride + h], kPartReady | (field << kEscBits) | pesc);
   // the escapes need no stream position: staged while the part waits for it
-  stage_escapes(v, emask, base, s_esc);
+  stage_escapes_ex(ex, em4, base, s_esc);
 
   // Stream position (wave 0).
   if (tid < 64u) {
@@ -2316,7 +2344,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
     const uint32_t u = pu0 + j * kPartThreads + tid;
-    if (u < nunits) *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
+    if (u < nunits) *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = smb[j];
   }
   // planes: the part's plane bytes [slot0, slot0 + own) of each plane, clipped
   // to the padded plane length (zip3: bytes [pu0, pu0 + kPartUnits))
@@ -2441,8 +2469,20 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
     const uint32_t u = p.u0 + j * kPartThreads + tid;
     smv[j] = make_uint2(0u, 0u);
     ev[j] = make_uint2(0u, 0u);
-    if (kFull || u < p.nunits) {
-      const uint32_t valid = kFull ? 8u : min(8u, p.nc - 8u * u);
+    if (kFull) {
+      smv[j] = *reinterpret_cast<const uint2*>(in + g.sm + 8ull * u);
+      if (kCiera) {
+        // Unchanged blocks read their cache bytes; the units of changed
+        // blocks, whose ev the codes replace, read the chunk's first cache
+        // bytes instead (one line for the wave).  With the load taken on
+        // every path it needs no copy afterwards, and so no wait before the
+        // next loads go out.
+        const uint32_t blk = (8u * u) >> p.log2B;
+        const bool changed = (s_bits[blk >> 5] >> (blk & 31u)) & 1u;
+        ev[j] = *reinterpret_cast<const uint2*>(p.cache + p.start + (changed ? 0ull : 8ull * u));
+      }
+    } else if (u < p.nunits) {
+      const uint32_t valid = min(8u, p.nc - 8u * u);
       smv[j] = load_bytes8(in + g.sm + 8ull * u, valid);
       if (kCiera) {
         const uint32_t blk = (8u * u) >> p.log2B;
@@ -2456,7 +2496,7 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   for (uint32_t r = 0; r < kPlaneRounds; r++) {
     const uint32_t i = tid + r * kPartThreads;
     if (i < 3u * np) {
-      const uint32_t b = i / np;
+      const uint32_t b = uint32_t(i >= np) + uint32_t(i >= 2u * np);  // i < 3 np
       st[r] = *reinterpret_cast<const uint2*>(in + g.plane + b * p.pb + p.sbase + 8u * (i - b * np));
     }
   }
@@ -2481,7 +2521,7 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   for (uint32_t r = 0; r < kPlaneRounds; r++) {
     const uint32_t i = tid + r * kPartThreads;
     if (i < 3u * np) {
-      const uint32_t b = i / np;
+      const uint32_t b = uint32_t(i >= np) + uint32_t(i >= 2u * np);  // i < 3 np
       *reinterpret_cast<uint2*>(s_planes + b * kStage + 8u * (i - b * np)) = st[r];
     }
   }
@@ -2503,12 +2543,11 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   }
   const uint32_t before = p.before + zb;
 
-  uint32_t cnt[kU], base[kU], emask[kU];
+  uint32_t cnt[kU], base[kU], em4[(kU + 3u) / 4u] = {};  // unit j's escape mask in byte j % 4 of em4[j / 4]
 #pragma unroll
   for (uint32_t j = 0; j < kU; j++) {
     const uint32_t u = p.u0 + j * kPartThreads + tid;
     cnt[j] = 0u;
-    emask[j] = 0u;
     if (!kFull && u >= p.nunits) continue;
     bool coded = true;
     uint32_t pbyte = u;
@@ -2526,8 +2565,9 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
                                                                            : ((1u << (p.nc - 8u * u)) - 1u));
       const uint2 codes = codes_from_planes(p0, p1, p2);
       ev[j] = make_uint2(exps_from_codes(codes.x, p.e0), exps_from_codes(codes.y, p.e0));
-      emask[j] = ~(p0 | p1 | p2) & vmask;
-      cnt[j] = __popc(emask[j]);
+      const uint32_t em = ~(p0 | p1 | p2) & vmask;
+      em4[j / 4u] |= em << (8u * (j % 4u));
+      cnt[j] = __popc(em);
     }
   }
   const uint32_t pesc = part_escape_scan(cnt, base, s_tot);
@@ -2550,7 +2590,8 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
     if (!kFull && u >= p.nunits) continue;
     const uint32_t valid = kFull ? 8u : min(8u, p.nc - 8u * u);
     // the unit's escapes are staged bytes [before + base - esc_lo, + cnt)
-    const uint2 e = merge_escapes(ev[j], emask[j], s_esc, before + base[j] - esc_lo);
+    const uint32_t em = (em4[j / 4u] >> (8u * (j % 4u))) & 0xFFu;
+    const uint2 e = merge_escapes(ev[j], em, s_esc, before + base[j] - esc_lo);
     store_unit(p.y, p.start + 8ull * u, valid, unit_join(smv[j], e));
     if (kCiera) {
       const uint32_t blk = (8u * u) >> p.log2B;
