@@ -3327,16 +3327,53 @@ __global__ __launch_bounds__(kPartThreads) void k_rans_dec(const uint8_t* __rest
     for (uint32_t u0 = 0; u0 < nunits; u0 += kSpanUnits * kPartThreads) {
       uint2 smv[kSpanUnits], ev[kSpanUnits];
       uint32_t keep = 0;
+      if (8u * (u0 + kSpanUnits * kPartThreads) <= nc) {
+        // Every unit of the span holds 8 values.  No load sits under a
+        // per-lane condition (the compiler would copy its result into place
+        // after a wait for all loads before it): from B = 512 on, a wave's 64
+        // units lie in one block, so the wave loads them or skips them
+        // together; below, a unit of a changed block reads the chunk's first
+        // bytes instead.  Units of changed blocks are not stored.
+        if (log2B >= 9u) {
 #pragma unroll
-      for (uint32_t j = 0; j < kSpanUnits; j++) {
-        const uint32_t u = u0 + j * kPartThreads + tid;
-        const uint32_t blk = (8u * u) >> log2B;
-        smv[j] = ev[j] = make_uint2(0u, 0u);
-        if (u < nunits && !((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) {
-          const uint32_t k = min(8u, nc - 8u * u);
-          smv[j] = load_bytes8(in + sm_pos + start + 8ull * u, k);
-          ev[j] = load_bytes8(cache + start + 8ull * u, k);
-          keep |= 1u << j;
+          for (uint32_t j = 0; j < kSpanUnits; j++) {
+            const uint32_t u = u0 + j * kPartThreads + tid;
+            const uint32_t blk = (8u * u) >> log2B;
+            const bool kept = !((s_bits[blk >> 5] >> (blk & 31u)) & 1u);
+            // any value where the wave skips: none of its units is stored
+            uint64_t sv = __builtin_nondeterministic_value(sv), cv = __builtin_nondeterministic_value(cv);
+            if (__ballot(kept) != 0u) {
+              sv = *reinterpret_cast<const uint64_t*>(in + sm_pos + start + 8ull * u);
+              cv = *reinterpret_cast<const uint64_t*>(cache + start + 8ull * u);
+            }
+            smv[j] = make_uint2(uint32_t(sv), uint32_t(sv >> 32));
+            ev[j] = make_uint2(uint32_t(cv), uint32_t(cv >> 32));
+            keep |= uint32_t(kept) << j;
+          }
+        } else {
+#pragma unroll
+          for (uint32_t j = 0; j < kSpanUnits; j++) {
+            const uint32_t u = u0 + j * kPartThreads + tid;
+            const uint32_t blk = (8u * u) >> log2B;
+            const bool kept = !((s_bits[blk >> 5] >> (blk & 31u)) & 1u);
+            const uint64_t off = kept ? 8ull * u : 0ull;
+            smv[j] = *reinterpret_cast<const uint2*>(in + sm_pos + start + off);
+            ev[j] = *reinterpret_cast<const uint2*>(cache + start + off);
+            keep |= uint32_t(kept) << j;
+          }
+        }
+      } else {
+#pragma unroll
+        for (uint32_t j = 0; j < kSpanUnits; j++) {
+          const uint32_t u = u0 + j * kPartThreads + tid;
+          const uint32_t blk = (8u * u) >> log2B;
+          smv[j] = ev[j] = make_uint2(0u, 0u);
+          if (u < nunits && !((s_bits[blk >> 5] >> (blk & 31u)) & 1u)) {
+            const uint32_t k = min(8u, nc - 8u * u);
+            smv[j] = load_bytes8(in + sm_pos + start + 8ull * u, k);
+            ev[j] = load_bytes8(cache + start + 8ull * u, k);
+            keep |= 1u << j;
+          }
         }
       }
 #pragma unroll
