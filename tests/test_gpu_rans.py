@@ -29,7 +29,7 @@ def test_zip3_rans_small(n):
         check_rans(wl.mixed_small(rng, n))
 
 
-@pytest.mark.parametrize("B", [64, 256, 4096, 32768, 65536])
+@pytest.mark.parametrize("B", [64, 256, 512, 1024, 4096, 32768, 65536])
 @pytest.mark.parametrize("n", SMALL_N)
 def test_ciera_rans_small(n, B):
     say(f"ciera rans n={n} B={B}")
