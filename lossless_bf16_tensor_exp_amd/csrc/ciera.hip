@@ -40,6 +40,12 @@
 // Blocks (B >= 64) never split a unit, and chunks never split a block.  All
 // data movement is integer: sign, NaN payloads, subnormals and -0 never pass
 // through floating-point registers.
+// Loads: a thread issues all loads of a full range before it uses any, and
+// none sits under a per-lane condition: the compiler would copy such a
+// load's result into place only after waiting for every load issued before
+// it, one round trip per load.  A lane that needs no data (a unit of a
+// changed block in the decoders) reads the chunk's first bytes instead, one
+// line for all such lanes of the wave.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
