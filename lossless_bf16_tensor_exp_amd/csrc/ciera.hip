@@ -1074,10 +1074,12 @@ constexpr uint32_t kRunRegs = 8u;
 // in [E0, E0 + 6]: bins E0..E0+6 lie in the two 16-byte words q = E0 / 8 and
 // q + 1 of the row (only in word q when E0 >= 248, and q + 1 is then past the
 // row and not read), at u16 positions r .. r + 6, r = E0 mod 8.
-__device__ inline uint32_t row_in_window(const uint16_t* row_base, uint32_t e0) {
+// The coded values of a histogram row inside [E0, E0 + 6], from the row's 16
+// counts starting at bin E0 & ~7: a = bins (E0 & ~7) + 0..7, b = the next 8
+// (ignored past the row's end).
+__device__ inline uint32_t window_count(uint4 a, uint4 b, uint32_t e0) {
   const uint32_t r0 = e0 & 7u;
-  const uint4* row = reinterpret_cast<const uint4*>(row_base) + (e0 >> 3);
-  const uint4 a = row[0], b = (e0 >> 3) < kBins / 8u - 1u ? row[1] : make_uint4(0u, 0u, 0u, 0u);
+  if ((e0 >> 3) == kBins / 8u - 1u) b = make_uint4(0u, 0u, 0u, 0u);
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   uint32_t sum = 0;
 #pragma unroll
@@ -1086,6 +1088,12 @@ __device__ inline uint32_t row_in_window(const uint16_t* row_base, uint32_t e0) 
     sum += (i - r0 < 7u) ? cnt : 0u;  // r0 <= i <= r0 + 6
   }
   return sum;
+}
+
+__device__ inline uint32_t row_in_window(const uint16_t* row_base, uint32_t e0) {
+  const uint4* row = reinterpret_cast<const uint4*>(row_base) + (e0 >> 3);
+  const uint4 b = (e0 >> 3) < kBins / 8u - 1u ? row[1] : make_uint4(0u, 0u, 0u, 0u);
+  return window_count(row[0], b, e0);
 }
 
 // A chunk's layout from its parts' coded values, change fields (B <= 16384:
@@ -1474,30 +1482,40 @@ struct SelfPlan {
   // part and those of the part's slices before it
   uint32_t esc_slice, esc_slice_before;
 };
-__device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, uint32_t h, uint32_t slice, bool lead,
-                                     uint32_t wg, uint32_t B, int e0_override, uint8_t* __restrict__ out,
-                                     uint64_t* __restrict__ out_size, const Ws& ws) {
+// The self-plan in two steps, so that the workgroup codes its values while
+// the histogram windows are on their way.  Step one: the window base from the
+// statistics records (thread t adds record t), then the loads of each
+// record's histogram counts around the window, issued and not waited for.
+// Both loads are taken on every path (record 0 stands in for threads past
+// the records, the row's last 16 bytes for the 16 past its end), so that no
+// later load waits for them.
+struct PlanStart {
+  uint32_t e0;  // kBadE0: the given window base is out of range
+  uint32_t r_coded, r_nch;
+  uint4 wa, wb;
+};
+__device__ inline PlanStart self_plan_start(uint64_t nchunks, uint32_t wg, int e0_override,
+                                            uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
+                                            const Ws& ws) {
   __shared__ double s_f[kPlanWaves];
   __shared__ uint64_t s_u[kPlanWaves];
-  __shared__ uint64_t s_r[5];
-  __shared__ uint32_t s_pc[kSelfPlanChunks * kParts], s_pn[kSelfPlanChunks * kParts], s_pi[kSelfPlanChunks * kParts];
-  __shared__ uint32_t s_re[kPlanThreads];  // each record's escapes
+  __shared__ uint32_t s_e0;
   static_assert(kPartThreads == kPlanThreads, "the planner's reduction order");
   static_assert(kSelfPlanChunks * kParts * kSlices <= kPlanThreads, "one record per thread");
   const uint32_t tid = threadIdx.x;
-  const uint32_t ss = ws.ss;
-  const uint32_t nrec = uint32_t(kParts * nchunks) * ss;
+  const uint32_t nrec = uint32_t(kParts * nchunks) * ws.ss;
   // thread t takes record t, as the one-group planner's k_sums takes part t
   double a = 0.0, b = 0.0;
   uint64_t m = 0;
-  uint32_t r_coded = 0u, r_nch = 0u;
+  PlanStart r;
+  r.r_coded = r.r_nch = 0u;
   if (tid < nrec) {
     const Partial& p = ws.partial[tid];
     a += p.s1;
     b += p.s2;
     m += p.nf;
-    r_coded = p.coded;
-    r_nch = p.nch;
+    r.r_coded = p.coded;
+    r.r_nch = p.nch;
   }
   a = plan_sum_f64(a, s_f);
   b = plan_sum_f64(b, s_f);
@@ -1508,11 +1526,11 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
       var = (b - a * a / double(m)) / double(m - 1u);
       if (!(var > 0.0)) var = 0.0;
     }
-    s_r[1] = ws.e0_src ? uint32_t(ws.e0_src[0])
-                       : ((e0_override >= 0) ? uint32_t(e0_override) : window_base(var, m));
+    s_e0 = ws.e0_src ? uint32_t(ws.e0_src[0]) : ((e0_override >= 0) ? uint32_t(e0_override) : window_base(var, m));
   }
   __syncthreads();
-  const uint32_t e0 = uint32_t(s_r[1]);
+  const uint32_t e0 = s_e0;
+  r.e0 = e0;
   if (e0 > kMaxE0) {
     // only from device memory: the stream gets its first header word alone,
     // whose E0 byte keeps the bad value (a decoder refuses it, and so does a
@@ -1523,15 +1541,34 @@ __device__ inline SelfPlan self_plan(uint64_t n, uint64_t nchunks, uint64_t c, u
       ws.ctrl->e0 = kBadE0;
       ws.ctrl->n_err_slots = gridDim.x;
     }
-    SelfPlan bad{};
-    bad.e0 = kBadE0;
-    return bad;
+    r.e0 = kBadE0;
+    return r;
   }
+  const uint4* row = reinterpret_cast<const uint4*>(ws.hist + uint64_t(tid < nrec ? tid : 0u) * kBins) + (e0 >> 3);
+  r.wa = row[0];
+  r.wb = row[(e0 >> 3) < kBins / 8u - 1u ? 1 : 0];
+  return r;
+}
+
+// Step two: each record's coded values in the window, the chunks' layout and
+// offsets, the chunk table, the header; the workgroup's part and slice
+// entries.
+__device__ inline SelfPlan self_plan_finish(uint64_t n, uint64_t nchunks, uint64_t c, uint32_t h, uint32_t slice,
+                                            bool lead, uint32_t wg, uint32_t B, const PlanStart& ps,
+                                            uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
+                                            const Ws& ws) {
+  __shared__ uint64_t s_r[5];
+  __shared__ uint32_t s_pc[kSelfPlanChunks * kParts], s_pn[kSelfPlanChunks * kParts], s_pi[kSelfPlanChunks * kParts];
+  __shared__ uint32_t s_re[kPlanThreads];  // each record's escapes
+  const uint32_t tid = threadIdx.x;
+  const uint32_t ss = ws.ss;
+  const uint32_t nrec = uint32_t(kParts * nchunks) * ss;
+  const uint32_t e0 = ps.e0;
+  uint32_t r_coded = ps.r_coded, r_nch = ps.r_nch;
   // Each record's coded values in the window; a part's records (ss
   // consecutive lanes of one wave) added by lane exchanges; then one thread
   // per chunk lays the chunk out.
-  uint32_t r_in = 0u;
-  if (tid < nrec) r_in = row_in_window(ws.hist + uint64_t(tid) * kBins, e0);
+  uint32_t r_in = tid < nrec ? window_count(ps.wa, ps.wb, e0) : 0u;
   // a record's escapes (used with one record per slice, where no block spans
   // slices, so that all of a record's coded values are written)
   s_re[tid] = r_coded - r_in;
@@ -1727,10 +1764,9 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     }
   }
   const uint64_t nchunks = cdiv(n, kChunk);
-  uint64_t begin;
-  uint32_t esc_before, esc_chunk, esc_part, e0;
+  uint64_t begin = 0;
+  uint32_t esc_before = 0u, esc_chunk = 0u, esc_part = 0u, e0;
   uint32_t esc_slice = 0u, esc_slice_before = 0u;
-  bool plan_failed = false;
   // self-planned: the chunk's bitmap words are fetched with the plan's inputs
   __shared__ uint32_t s_pw[kSelfPlan ? kBitmapWords : 1u];
   uint32_t pw_l = 0u;
@@ -1739,16 +1775,18 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     const uint64_t rec0 = (uint64_t(c) * kParts + tid / kPartBitmapWords) * ws.ss;
     for (uint32_t sl = 0; sl < ws.ss; sl++) pw_l |= ws.bitmap[(rec0 + sl) * kPartBitmapWords + tid % kPartBitmapWords];
   }
+  // Nothing is written unless the plan is complete and puts the chunk inside
+  // the output buffer.
+  auto plan_ok = [&](bool plan_failed) {
+    return !(plan_failed || begin < table_end(nchunks) || (begin & 127u) != 0u || begin > capacity ||
+             capacity - begin < chunk_max_bytes(nc, kCiera ? B : 0u) || esc_chunk > nc || esc_before > esc_chunk ||
+             esc_part > esc_chunk - esc_before);
+  };
+  PlanStart ps;
   if (kSelfPlan) {
-    const SelfPlan sp = self_plan(n, nchunks, c, h, slice, h == 0u && slice == 0u, wg, kCiera ? B : 0u, e0_override,
-                                  out, out_size, ws);
-    begin = sp.begin;
-    esc_before = sp.esc_before;
-    esc_chunk = sp.esc_chunk;
-    esc_part = sp.esc_part;
-    esc_slice = sp.esc_slice;
-    esc_slice_before = sp.esc_slice_before;
-    e0 = sp.e0;
+    // the window base now; the chunks' offsets after the values are coded
+    ps = self_plan_start(nchunks, wg, e0_override, out, out_size, ws);
+    e0 = ps.e0;
     if (e0 == kBadE0) {  // the same for every workgroup
       if (tid == 0) ws.err[wg] = uint32_t(CIERA_ERR_ARG);
       return;
@@ -1759,22 +1797,18 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     esc_chunk = ws.chunkesc[c];
     esc_part = (last_part ? esc_chunk : ws.partesc[c * kParts + h + 1u]) - esc_before;
     e0 = ws.ctrl->e0;
-    plan_failed = ws.ctrl->plan_fail != 0u;
-  }
-  // Nothing is written unless the plan is complete and puts the chunk inside
-  // the output buffer.
-  if (plan_failed || begin < table_end(nchunks) || (begin & 127u) != 0u || begin > capacity ||
-      capacity - begin < chunk_max_bytes(nc, kCiera ? B : 0u) || esc_chunk > nc || esc_before > esc_chunk ||
-      esc_part > esc_chunk - esc_before) {
-    if (tid == 0) {
-      ws.err[wg] = uint32_t(CIERA_ERR_INTERNAL);
-      // after a failed plan the stream must not pass for one: no size, no magic
-      if (plan_failed && wg == 0u) {
-        *out_size = 0u;
-        *reinterpret_cast<uint64_t*>(out) = 0u;
+    const bool plan_failed = ws.ctrl->plan_fail != 0u;
+    if (!plan_ok(plan_failed)) {
+      if (tid == 0) {
+        ws.err[wg] = uint32_t(CIERA_ERR_INTERNAL);
+        // after a failed plan the stream must not pass for one: no size, no magic
+        if (plan_failed && wg == 0u) {
+          *out_size = 0u;
+          *reinterpret_cast<uint64_t*>(out) = 0u;
+        }
       }
+      return;
     }
-    return;
   }
   const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
   for (uint32_t i = tid; i < 3u * kStage / 16u; i += kPartThreads)
@@ -1793,7 +1827,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   }
   __syncthreads();  // staging cleared, bitmap staged
   if (kCiera) nch = s_rank[kBitmapWords - 1] + __popc(s_bits[kBitmapWords - 1]);
-  const ChunkGeom g = chunk_geom(begin, nc, kCiera, nch, B);
+  ChunkGeom g = chunk_geom(begin, nc, kCiera, nch, B);  // self-planned: recomputed once the offset is known
   const uint32_t pb = uint32_t(g.plane_bytes);
   // Plane bytes this part stages and writes.  zip3: one byte per unit, so the
   // part owns bytes [pu0, pu0 + kPartUnits) of each plane (padding included).
@@ -1807,12 +1841,10 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
                                  : u0 + kRange;
 
   // A slice's first escape: the part's escapes before u0 (values of coded
-  // units whose code is 0), from the plan, or counted from the units loaded
-  // above.
+  // units whose code is 0), from the plan (below), or counted from the units
+  // loaded above.
   uint32_t zb = 0;
-  if (counted) {
-    zb = esc_slice_before;
-  } else if (kS > 1u) {
+  if (kS > 1u && !counted) {
     uint32_t z = 0;
 #pragma unroll
     for (uint32_t k = 0; k < kEarly; k++) {
@@ -1836,15 +1868,18 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     zb = part_sum_u32(z, s_zw);
   }
 
-  // Code every unit: sign+mantissa bytes straight to HBM, plane bytes into LDS.
+  // Code every unit: sign+mantissa bytes straight to HBM (self-planned: held
+  // until the offset is known), plane bytes into LDS.
   uint32_t cnt[kU], base[kU], emask[kU];
+  uint2 smb[kSelfPlan ? kU : 1u];
 #pragma unroll
   for (uint32_t j = 0; j < kU; j++) {
     const uint32_t u = u0 + j * kPartThreads + tid;
     cnt[j] = 0u;
     emask[j] = 0u;
+    if (kSelfPlan) smb[j] = unit_sm(v[j]);
     if (u < nunits) {
-      *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
+      if (!kSelfPlan) *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = unit_sm(v[j]);
       bool coded = true;
       uint32_t pbyte = u;
       if (kCiera) {
@@ -1869,6 +1904,30 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
     }
   }
   const uint32_t pesc = part_escape_scan<kU, false>(cnt, base, s_tot);  // its barriers also complete the plane staging
+  if (kSelfPlan) {
+    // The escapes need no stream position: staged now; the plan's second
+    // step (its barriers complete the staging) gives the offsets.
+    stage_escapes(v, emask, base, s_esc);
+    const SelfPlan sp = self_plan_finish(n, nchunks, c, h, slice, h == 0u && slice == 0u, wg, kCiera ? B : 0u, ps,
+                                         out, out_size, ws);
+    begin = sp.begin;
+    esc_before = sp.esc_before;
+    esc_chunk = sp.esc_chunk;
+    esc_part = sp.esc_part;
+    esc_slice = sp.esc_slice;
+    esc_slice_before = sp.esc_slice_before;
+    if (counted) zb = esc_slice_before;
+    if (!plan_ok(false)) {
+      if (tid == 0) ws.err[wg] = uint32_t(CIERA_ERR_INTERNAL);
+      return;
+    }
+    g = chunk_geom(begin, nc, kCiera, nch, B);
+#pragma unroll
+    for (uint32_t j = 0; j < kU; j++) {
+      const uint32_t u = u0 + j * kPartThreads + tid;
+      if (u < nunits) *reinterpret_cast<uint2*>(out + g.sm + 8ull * u) = smb[j];
+    }
+  }
   // The count must match what the plan read off the histograms (a slice: its
   // escapes and those before it stay within the part's, the last slice's end
   // where the part's do, and one the plan counted has its planned count); a
@@ -1889,8 +1948,10 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   // escapes of this range: [esc_before + zb, + pesc) of the chunk's section
   const uint64_t esc_at = g.esc + esc_before + zb;
   if (esc_ok) {
-    stage_escapes(v, emask, base, s_esc);
-    __syncthreads();
+    if (!kSelfPlan) {
+      stage_escapes(v, emask, base, s_esc);
+      __syncthreads();
+    }
     lds_to_global(out + esc_at, s_esc, pesc, tid, kPartThreads);
   }
   if (last_part && final_slice) {
