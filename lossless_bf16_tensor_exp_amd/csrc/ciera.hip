@@ -1504,19 +1504,18 @@ __device__ inline PlanStart self_plan_start(uint64_t nchunks, uint32_t wg, int e
   static_assert(kSelfPlanChunks * kParts * kSlices <= kPlanThreads, "one record per thread");
   const uint32_t tid = threadIdx.x;
   const uint32_t nrec = uint32_t(kParts * nchunks) * ws.ss;
-  // thread t takes record t, as the one-group planner's k_sums takes part t
-  double a = 0.0, b = 0.0;
-  uint64_t m = 0;
+  // a window base given in device memory, read with the records
+  const uint32_t e0_given = ws.e0_src ? uint32_t(ws.e0_src[0]) : 0u;
+  // Thread t takes record t, as the one-group planner's k_sums takes part t.
+  // The load is taken on every path (the last record stands in past the
+  // records and adds nothing), so it goes out with the loads before it.
+  const Partial p = ws.partial[min(tid, nrec - 1u)];
+  const bool own = tid < nrec;
+  double a = own ? p.s1 : 0.0, b = own ? p.s2 : 0.0;
+  uint64_t m = own ? p.nf : 0u;
   PlanStart r;
-  r.r_coded = r.r_nch = 0u;
-  if (tid < nrec) {
-    const Partial& p = ws.partial[tid];
-    a += p.s1;
-    b += p.s2;
-    m += p.nf;
-    r.r_coded = p.coded;
-    r.r_nch = p.nch;
-  }
+  r.r_coded = own ? p.coded : 0u;
+  r.r_nch = own ? p.nch : 0u;
   a = plan_sum_f64(a, s_f);
   b = plan_sum_f64(b, s_f);
   m = plan_sum_u64(m, s_u);
@@ -1526,7 +1525,7 @@ __device__ inline PlanStart self_plan_start(uint64_t nchunks, uint32_t wg, int e
       var = (b - a * a / double(m)) / double(m - 1u);
       if (!(var > 0.0)) var = 0.0;
     }
-    s_e0 = ws.e0_src ? uint32_t(ws.e0_src[0]) : ((e0_override >= 0) ? uint32_t(e0_override) : window_base(var, m));
+    s_e0 = ws.e0_src ? e0_given : ((e0_override >= 0) ? uint32_t(e0_override) : window_base(var, m));
   }
   __syncthreads();
   const uint32_t e0 = s_e0;
@@ -1769,11 +1768,18 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   uint32_t esc_slice = 0u, esc_slice_before = 0u;
   // self-planned: the chunk's bitmap words are fetched with the plan's inputs
   __shared__ uint32_t s_pw[kSelfPlan ? kBitmapWords : 1u];
-  uint32_t pw_l = 0u;
-  if (kSelfPlan && kCiera && tid < kBitmapWords) {
-    // word tid % 8 of part tid / 8: the OR of the part's records (one per slice)
-    const uint64_t rec0 = (uint64_t(c) * kParts + tid / kPartBitmapWords) * ws.ss;
-    for (uint32_t sl = 0; sl < ws.ss; sl++) pw_l |= ws.bitmap[(rec0 + sl) * kPartBitmapWords + tid % kPartBitmapWords];
+  // Word t % 8 of part t / 8 (t < 32) is the OR of the part's records (one
+  // per slice).  The loads are taken on every path and ORed only where the
+  // words are staged, so that they go out with the plan's loads (with fewer
+  // records the last is read again, which the OR absorbs; threads past the
+  // 32 words read those of thread 31).
+  uint32_t pwr[kSelfPlan && kCiera ? kSlices : 1u];
+  if (kSelfPlan && kCiera) {
+    const uint32_t t = min(tid, kBitmapWords - 1u);
+    const uint64_t rec0 = (uint64_t(c) * kParts + t / kPartBitmapWords) * ws.ss;
+#pragma unroll
+    for (uint32_t sl = 0; sl < kSlices; sl++)
+      pwr[sl] = ws.bitmap[(rec0 + min(sl, ws.ss - 1u)) * kPartBitmapWords + t % kPartBitmapWords];
   }
   // Nothing is written unless the plan is complete and puts the chunk inside
   // the output buffer.
@@ -1818,6 +1824,9 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   if (kCiera) {
     const uint32_t* pw = ws.bitmap + uint64_t(c) * kBitmapWords;
     if (kSelfPlan) {
+      uint32_t pw_l = 0u;
+#pragma unroll
+      for (uint32_t sl = 0; sl < kSlices; sl++) pw_l |= pwr[sl];
       if (tid < kBitmapWords) s_pw[tid] = pw_l;
       __syncthreads();
       pw = s_pw;
