@@ -659,12 +659,6 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     for (uint32_t i = tid; i < kPlanMaxGroups * 8u; i += kPartThreads) sw[i] = 0u;
     if (tid == 0) ws.ctrl->plan_fail = 0u;
   }
-  const uint32_t first = x[0];
-  const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
-  // a window base given in device memory that is out of range: the encode
-  // writes nothing, so the sender cache is left as it was
-  const bool keep_cache = ws.e0_src != nullptr && ws.e0_src[0] > kMaxE0;
-
   // Hash sender, blocks within the part: the hash phase gives each block
   // hb_threads consecutive threads (8 units each); the last of them decides
   // and fetches the block's stored hashes now.
@@ -702,6 +696,12 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       }
     }
   }
+  // read after the part's loads are out, so that they do not wait for these
+  const uint32_t first = x[0];
+  const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
+  // a window base given in device memory that is out of range: the encode
+  // writes nothing, so the sender cache is left as it was
+  const bool keep_cache = ws.e0_src != nullptr && ws.e0_src[0] > kMaxE0;
   __syncthreads();  // LDS cleared
 
   // Variance sums with no finite test per value: a non-finite input makes the
