@@ -696,12 +696,15 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       }
     }
   }
-  // read after the part's loads are out, so that they do not wait for these
+  // x[0] (the shift of the variance sums) and the given window byte, if any
+  // (else x's first byte stands in): read after the part's loads are out,
+  // both on every path, so that they share the part's round trip
   const uint32_t first = x[0];
+  const uint32_t e0_byte = *(ws.e0_src ? ws.e0_src : reinterpret_cast<const uint8_t*>(x));
   const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
   // a window base given in device memory that is out of range: the encode
   // writes nothing, so the sender cache is left as it was
-  const bool keep_cache = ws.e0_src != nullptr && ws.e0_src[0] > kMaxE0;
+  const bool keep_cache = ws.e0_src != nullptr && e0_byte > kMaxE0;
   __syncthreads();  // LDS cleared
 
   // Variance sums with no finite test per value: a non-finite input makes the
