@@ -625,7 +625,6 @@ template <bool kCiera, bool kHash, uint32_t kS>
 __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
                                                         uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
   static_assert(kCiera || !kHash, "the hash sender is a ciera mode");
-  static_assert(kS == 1u || !kHash, "the hash sender takes whole parts");
   constexpr uint32_t kU = kUPT / kS;            // units per thread
   constexpr uint32_t kRange = kPartUnits / kS;  // units per workgroup
   // hash sender: first the part's exponent words (2048 u64), then the histogram
@@ -659,12 +658,13 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     for (uint32_t i = tid; i < kPlanMaxGroups * 8u; i += kPartThreads) sw[i] = 0u;
     if (tid == 0) ws.ctrl->plan_fail = 0u;
   }
-  // Hash sender, blocks within the part: the hash phase gives each block
-  // hb_threads consecutive threads (8 units each); the last of them decides
-  // and fetches the block's stored hashes now.
+  // Hash sender, blocks within the part (a slice: within the slice): the hash
+  // phase gives each block hb_threads consecutive threads (kU units each);
+  // the last of them decides and fetches the block's stored hashes now.
   uint64_t* hcache = reinterpret_cast<uint64_t*>(cache);
-  const uint32_t hb_threads = (kHash && B <= kPartValues) ? B / 64u : kPartThreads;
-  const uint64_t hblk = kHash ? c * (kChunk >> log2B) + blk0 + tid / hb_threads : 0u;  // global block
+  const uint32_t hb_threads = (kHash && B <= kPartValues) ? B / (8u * kU) : kPartThreads;
+  const uint32_t sblk0 = kCiera ? ((8u * u0) >> log2B) - blk0 : 0u;  // the workgroup's first block in the part
+  const uint64_t hblk = kHash ? c * (kChunk >> log2B) + blk0 + sblk0 + tid / hb_threads : 0u;  // global block
   const bool decider = kHash && B <= kPartValues && tid % hb_threads == hb_threads - 1u && (hblk << log2B) < n;
   uint64_t hc0 = 0, hc1 = 0;
   if (decider) {
@@ -790,22 +790,24 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
     }
   }
   if (kHash) {
-    // The part's exponent words are in LDS; thread t hashes units 8t .. 8t+7
-    // of the part (64 values), word k of its block being unit k of it.
+    // The range's exponent words are in LDS; thread t hashes units kU t ..
+    // kU t + kU - 1 of the range (8 kU values), word k of its block being
+    // unit k of it.
+    static_assert(kU % 2u == 0u, "two words per 16-byte read");
     __syncthreads();
-    const uint4* se = reinterpret_cast<const uint4*>(s_hist) + 4u * tid;
-    uint64_t w[8];
+    const uint4* se = reinterpret_cast<const uint4*>(s_hist) + (kU / 2u) * tid;
+    uint64_t w[kU];
 #pragma unroll
-    for (uint32_t i = 0; i < 4u; i++) {
+    for (uint32_t i = 0; i < kU / 2u; i++) {
       const uint4 q = se[i];
       w[2u * i] = (uint64_t(q.y) << 32) | q.x;
       w[2u * i + 1u] = (uint64_t(q.w) << 32) | q.z;
     }
-    const uint64_t k1 = uint64_t(((pu0 + 8u * tid) & ((B >> 3) - 1u)) + 1u);  // k + 1 of the first word
+    const uint64_t k1 = uint64_t(((u0 + kU * tid) & ((B >> 3) - 1u)) + 1u);  // k + 1 of the first word
     uint64_t key0 = kHashSeed0 + k1 * kHashGamma0, key1 = kHashSeed1 + k1 * kHashGamma1;
     uint64_t p0 = 0, p1 = 0;
 #pragma unroll
-    for (uint32_t i = 0; i < 8u; i++) {
+    for (uint32_t i = 0; i < kU; i++) {
       if (w[i]) {
         p0 += splitmix64_out(w[i] + key0);
         p1 += splitmix64_out(w[i] + key1);
@@ -852,12 +854,12 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
           const uint32_t per = 64u / hb_threads;  // blocks of this wave
           uint64_t bits = 0;
           for (uint32_t i = 0; i < per; i++) bits |= ((m >> (i * hb_threads + hb_threads - 1u)) & 1u) << i;
-          const uint32_t b0 = wave * per;
+          const uint32_t b0 = sblk0 + wave * per;  // a multiple of per (sblk0 is one of 4 per)
           atomicOr(&s_bits[b0 >> 5], uint32_t(bits) << (b0 & 31u));
           if (per > 32u) atomicOr(&s_bits[(b0 >> 5) + 1u], uint32_t(bits >> 32));
         }
       } else if (changed) {
-        const uint32_t b = tid / hb_threads;
+        const uint32_t b = sblk0 + tid / hb_threads;
         atomicOr(&s_bits[b >> 5], 1u << (b & 31u));
       }
     } else if (tid == kPartThreads - 1u) {
@@ -3727,10 +3729,9 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   // A tensor of at most kSelfPlanChunks chunks (one planning group) is
   // planned by the write kernel itself, unless a planner shape is forced.
   // Its k_stats then runs one workgroup per slice of a part (kSlices per
-  // part, one record each), except for the hash sender and for blocks that
-  // span slices.
+  // part, one record each), except for blocks that span slices.
   const bool self_plan = plan_groups == 0u && nchunks >= 1u && nchunks <= kSelfPlanChunks && !(hashed && B > kPartValues);
-  const bool stats_sliced = self_plan && !hashed && (!ciera || B <= 8u * (kPartUnits / kSlices));
+  const bool stats_sliced = self_plan && (!ciera || B <= 8u * (kPartUnits / kSlices));
   static_assert(kSelfPlanChunks <= kSliceChunks, "the workspace has a record per slice");
   if (d_e0 && (!self_plan || hashed || e0_override >= 0)) return CIERA_ERR_ARG;
   Ws ws = ws_bind(d_ws, nchunks);
@@ -3743,7 +3744,10 @@ ciera_status encode_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cac
   (void)hipGetLastError();
   if (nchunks) {
     const dim3 grid(uint32_t(nchunks * kParts)), sgrid(uint32_t(nchunks * kParts * kSlices));
-    if (hashed)
+    if (hashed && stats_sliced)
+      launch(k_stats<true, true, kSlices>, sgrid, dim3(kPartThreads), stream, x, n, static_cast<uint8_t*>(d_hash), lb,
+             ws);
+    else if (hashed)
       launch(k_stats<true, true, 1u>, grid, dim3(kPartThreads), stream, x, n, static_cast<uint8_t*>(d_hash), lb, ws);
     else if (ciera && stats_sliced)
       launch(k_stats<true, false, kSlices>, sgrid, dim3(kPartThreads), stream, x, n, d_cache, lb, ws);
