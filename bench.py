@@ -238,6 +238,35 @@ def stream_stats(s, n):
     return {"E0": int(s[7]), "changed_blocks": int(hd[5]), "escapes": int(hd[6])}
 
 
+# Shard-sized tensors also time the batch decode of BATCH_PEERS streams (the
+# W - 1 = 3 peer shards a rank of a 4-way sharded all-gather receives).
+BATCH_MAX_N = 1 << 22
+BATCH_PEERS = 3
+
+
+def measure_decode_batch(gpu, out, sz, n, B, pristine, xd, single_ms):
+    """BATCH_PEERS copies of one stream decoded in one batch call (each into
+    its own output, against its own receiver cache), timed like the isolated
+    calls, against BATCH_PEERS single decodes."""
+    torch, ciera = gpu.torch, gpu.ciera
+    k = BATCH_PEERS
+    ys = [torch.empty(n, dtype=torch.int16, device=gpu.dev) for _ in range(k)]
+    caches = [pristine.clone() for _ in range(k)] if B else None
+    ws = torch.empty(ciera.decode_batch_workspace_size(n, k), dtype=torch.uint8, device=gpu.dev)
+    inps, sizes = [out] * k, [sz] * k
+    if B:
+        call = lambda: ciera.ciera_decode_batch(inps, sizes, ys, B, caches, ws, stream=gpu.stream)  # noqa: E731
+        restore = lambda: [c.copy_(pristine) for c in caches]  # noqa: E731
+    else:
+        call = lambda: ciera.zip3_decode_batch(inps, sizes, ys, ws, stream=gpu.stream)  # noqa: E731
+        restore = None
+    ms, ms_min = gpu.isolated(call, restore)
+    ok = ciera.ciera_read_error(ws) == 0 and all(bool(torch.equal(y, xd)) for y in ys)
+    return {"streams": k, "ms": round(ms, 5), "min_ms": round(ms_min, 5),
+            "GBps": round(2 * n * k / (ms * 1e-3) / 1e9, 1),
+            "speedup_vs_single_decodes": round(k * single_ms / ms, 3), "roundtrip_ok": ok}
+
+
 def measure_config(gpu, oracle, np, wl, workload, B_pick, threads):
     """One workload's isolated encode and decode on the GPU, its stream
     against the oracle's, and both oracle legs."""
@@ -282,6 +311,7 @@ def measure_config(gpu, oracle, np, wl, workload, B_pick, threads):
     d_ms, d_min = gpu.isolated(dec, (lambda: recv.copy_(pristine)) if recv is not None else None)
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
     roundtrip = bool(torch.equal(y, xd))
+    batch = measure_decode_batch(gpu, out, sz, n, B, pristine, xd, d_ms) if n <= BATCH_MAX_N else None
     g_stream = out[:sz].cpu().numpy()
     o_stream, legs = oracle_legs(oracle, np, x, B, prev, threads)
     exact = g_stream.tobytes() == o_stream.tobytes()
@@ -302,6 +332,8 @@ def measure_config(gpu, oracle, np, wl, workload, B_pick, threads):
            "E0": st["E0"], "escape_pct": round(100.0 * st["escapes"] / max(1, n), 3),
            "reuse_pct": round(100.0 * (1 - st["changed_blocks"] / nb), 2) if nb else None,
            "bit_exact_vs_oracle": exact, "roundtrip_ok": roundtrip, "oracle": legs}
+    if batch is not None:
+        res["decode_batch"] = batch
     del out, ws_e, ws_d, y, xd, send, recv, pristine
     torch.cuda.empty_cache()
     return res

@@ -223,6 +223,34 @@ ciera_status ciera_decode_rans(const void* d_in, uint64_t in_size, void* d_y, ui
 ciera_status ciera_decode(const void* d_in, uint64_t in_size, void* d_y, uint64_t n, uint32_t B,
                           uint8_t* d_prev_exp, void* d_ws, uint64_t ws_bytes, hipStream_t stream);
 
+/* zip3_decode_batch, ciera_decode_batch: k streams of the same n (and B)
+ * decoded in one launch, e.g. the peer shards a rank receives in a sharded
+ * all-gather: the CIERA page's receivers decompress each peer's message
+ * against that peer's receiver cache (section 3.1; the pipelining of section
+ * 3.3 puts this decompression on the critical path).  Stream i is decoded
+ * exactly as zip3_decode / ciera_decode would decode it alone.
+ *   k           1..CIERA_DECODE_BATCH_MAX
+ *   d_in[i], in_size[i]  stream i and its buffer's size (as in_size of the
+ *                        single decode); host arrays of k entries, read
+ *                        during the call
+ *   d_y[i]      output i, n u16, 16-B aligned; the k outputs must not overlap
+ *   d_prev_exp[i]  (ciera) receiver cache of stream i's sender, n bytes,
+ *                  in/out as in ciera_decode; the k caches must not overlap
+ *   d_ws        workspace of decode_batch_workspace_size(n, k) bytes: one
+ *               status word per workgroup of all k streams
+ * Argument errors (k out of range, k * n above 2^40, a null or misaligned
+ * pointer, a small workspace) return before any launch.  A malformed stream
+ * makes ciera_read_error report CIERA_ERR_FORMAT (without saying which
+ * stream); that stream's output and cache are then unspecified, the other
+ * streams are decoded in full. */
+#define CIERA_DECODE_BATCH_MAX 16u
+uint64_t decode_batch_workspace_size(uint64_t n, uint32_t k);
+ciera_status zip3_decode_batch(uint32_t k, const void* const* d_in, const uint64_t* in_size, void* const* d_y,
+                               uint64_t n, void* d_ws, uint64_t ws_bytes, hipStream_t stream);
+ciera_status ciera_decode_batch(uint32_t k, const void* const* d_in, const uint64_t* in_size, void* const* d_y,
+                                uint64_t n, uint32_t B, uint8_t* const* d_prev_exp, void* d_ws, uint64_t ws_bytes,
+                                hipStream_t stream);
+
 /* Synchronise `stream` and return the device-side status of the last call
  * that used d_ws: CIERA_OK, CIERA_ERR_FORMAT (decode saw a malformed
  * stream), CIERA_ERR_INTERNAL, or CIERA_ERR_HIP if the copy fails. */

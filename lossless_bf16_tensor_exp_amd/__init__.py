@@ -22,6 +22,9 @@ Same names as the C ABI::
     zip3_encode_rans / zip3_decode_rans / ciera_encode_rans / ciera_decode_rans   (rANS-coded exponents)
     rans_max_encoded_size(n, B), rans_workspace_size(n, B)
     ciera_decode(inp, in_size, y, B, prev_exp, ws, stream=None)
+    zip3_decode_batch(inps, in_sizes, ys, ws, stream=None)     (several streams of one n, one launch)
+    ciera_decode_batch(inps, in_sizes, ys, B, prev_exps, ws, stream=None)
+    decode_batch_workspace_size(n, k)
     ciera_read_error(ws, stream=None)
     ciera_time_kernels(pairs)             (profiling: per-kernel start/stop events)
     ciera_set_wait_limit(polls)           (test hook: bound of the waits between workgroups)
@@ -44,11 +47,13 @@ __all__ = [
     "rans_max_encoded_size", "rans_workspace_size", "zip3_encode_rans", "zip3_decode_rans", "ciera_encode_rans",
     "ciera_decode_rans",
     "bind", "ciera_time_kernels", "ciera_set_wait_limit", "ciera_encode_noalloc", "NOALLOC_MAX_N",
+    "decode_batch_workspace_size", "zip3_decode_batch", "ciera_decode_batch", "DECODE_BATCH_MAX",
     "CHUNK",
 ]
 
 CHUNK = 65536
 NOALLOC_MAX_N = 1 << 27
+DECODE_BATCH_MAX = 16
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libciera.so")
 _lib = None
@@ -105,6 +110,11 @@ def load_library():
     for name, args in sigs.items():
         f = getattr(lib, name)
         f.argtypes, f.restype = args, i32
+    pvp, pu64 = ctypes.POINTER(vp), ctypes.POINTER(u64)
+    lib.decode_batch_workspace_size.argtypes, lib.decode_batch_workspace_size.restype = [u64, u32], u64
+    lib.zip3_decode_batch.argtypes, lib.zip3_decode_batch.restype = [u32, pvp, pu64, pvp, u64, vp, u64, vp], i32
+    lib.ciera_decode_batch.argtypes = [u32, pvp, pu64, pvp, u64, u32, pvp, vp, u64, vp]
+    lib.ciera_decode_batch.restype = i32
     lib.ciera_status_string.argtypes, lib.ciera_status_string.restype = [i32], ctypes.c_char_p
     lib.ciera_set_wait_limit.argtypes, lib.ciera_set_wait_limit.restype = [u32], u32
     _lib = lib
@@ -330,6 +340,54 @@ def ciera_decode(inp, in_size: int, y, B: int, prev_exp, ws, stream=None) -> Non
     st = lib.ciera_decode(_ptr(inp), in_size, _ptr(y), y.numel(), B, _ptr(prev_exp), _ptr(ws), ws.numel(),
                           _stream(stream))
     _raise(st, "ciera_decode")
+
+
+def decode_batch_workspace_size(n: int, k: int) -> int:
+    return load_library().decode_batch_workspace_size(n, k)
+
+
+def _batch_arrays(inps, in_sizes, ys, prev_exps=None):
+    """Host arrays of device pointers and sizes for the batch decodes."""
+    k = len(inps)
+    if not (len(in_sizes) == len(ys) == k) or (prev_exps is not None and len(prev_exps) != k):
+        raise ValueError("one input size, output (and cache) per stream")
+    if not 1 <= k <= DECODE_BATCH_MAX:
+        raise ValueError(f"1 to {DECODE_BATCH_MAX} streams per batch, got {k}")
+    n = ys[0].numel()
+    for i in range(k):
+        _check_bytes(inps[i], f"inps[{i}]", in_sizes[i])
+        _check_values(ys[i], f"ys[{i}]")
+        if ys[i].numel() != n:
+            raise ValueError("every output of a batch holds the same number of values")
+        if prev_exps is not None:
+            _check_bytes(prev_exps[i], f"prev_exps[{i}]", n)
+    arr = ctypes.c_void_p * k
+    ins = arr(*[inp.data_ptr() for inp in inps])
+    sizes = (ctypes.c_uint64 * k)(*in_sizes)
+    outs = arr(*[y.data_ptr() if n else None for y in ys])
+    caches = arr(*[c.data_ptr() if n else None for c in prev_exps]) if prev_exps is not None else None
+    return k, n, ins, sizes, outs, caches
+
+
+def zip3_decode_batch(inps, in_sizes, ys, ws, stream=None) -> None:
+    """Decode len(inps) zip3 streams of the same n in one launch: stream i
+    (in_sizes[i] bytes of inps[i]) into ys[i]."""
+    lib = load_library()
+    k, n, ins, sizes, outs, _ = _batch_arrays(inps, in_sizes, ys)
+    _check_bytes(ws, "ws")
+    st = lib.zip3_decode_batch(k, ins, sizes, outs, n, _ptr(ws), ws.numel(), _stream(stream))
+    _raise(st, "zip3_decode_batch")
+
+
+def ciera_decode_batch(inps, in_sizes, ys, B: int, prev_exps, ws, stream=None) -> None:
+    """Decode len(inps) ciera streams of the same n and B in one launch:
+    stream i against receiver cache prev_exps[i] (updated in place) into
+    ys[i]."""
+    lib = load_library()
+    k, n, ins, sizes, outs, caches = _batch_arrays(inps, in_sizes, ys, prev_exps)
+    _check_bytes(ws, "ws")
+    st = lib.ciera_decode_batch(k, ins, sizes, outs, n, B, caches, _ptr(ws), ws.numel(), _stream(stream))
+    _raise(st, "ciera_decode_batch")
 
 
 def bind(name: str, *args, stream=None):

@@ -26,7 +26,8 @@
 // which plans for itself.
 // Decode is one kernel, k_decode, one workgroup per part; parts are
 // independent because the chunk table holds every chunk offset and the
-// escape index each part's first escape.
+// escape index each part's first escape.  k_decode_batch runs the same
+// workgroups for several streams of one size in one launch.
 // The single-read encodes (window base given) are k_prep1 + k_write1; the
 // rANS modes k_stats + k_rans_enc + k_rans_finish, and k_rans_dec.
 //
@@ -2487,6 +2488,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
 // most 15 bytes of earlier parts').  The LDS array has 16 spare bytes for the
 // 12-byte reads of merge_escapes.
 constexpr uint32_t kEscStage = kPartUnits * 8u + 16u;
+constexpr uint32_t kDecodeBatchMax = CIERA_DECODE_BATCH_MAX;  // streams per batch decode
 static_assert(kEscStage % 16u == 0u, "escape staging");
 
 // Put a unit's escape bytes into e: the k-th set bit of emask (a code-0
@@ -2682,14 +2684,15 @@ __device__ __attribute__((always_inline)) inline uint32_t decode_part(const Deco
   return 0u;
 }
 
-// One part of a chunk (kS = 1), or one of its kS slices; workgroups never
-// wait on each other: the escape index gives each part its first escape.
+// Workgroup wg of one stream's decode: one part of a chunk (kS = 1), or one
+// of its kS slices; workgroups never wait on each other, as the escape index
+// gives each part its first escape.  It stores its status in *status.
 template <bool kCiera, uint32_t kS>
-__global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restrict__ in, uint64_t in_size,
-                                                         uint16_t* __restrict__ y, uint64_t n, uint64_t nchunks,
-                                                         uint32_t log2B, uint8_t* __restrict__ cache,
-                                                         uint64_t* __restrict__ n_err_slots,
-                                                         uint32_t* __restrict__ err_slots) {
+__device__ __attribute__((always_inline)) inline void decode_workgroup(const uint8_t* __restrict__ in,
+                                                                       uint64_t in_size, uint16_t* __restrict__ y,
+                                                                       uint64_t n, uint64_t nchunks, uint32_t log2B,
+                                                                       uint8_t* __restrict__ cache, uint32_t wg,
+                                                                       uint32_t* __restrict__ status) {
   __shared__ __attribute__((aligned(16))) uint8_t s_planes[3u * kStage];
   __shared__ __attribute__((aligned(16))) uint8_t s_esc[kEscStage + 16u];
   __shared__ uint32_t s_ok;    // header and table entries are consistent
@@ -2700,7 +2703,6 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   __shared__ uint32_t s_rank[kBitmapWords];
   __shared__ uint32_t s_tot[kUPT * kPartWaves + 1];
   const uint32_t tid = threadIdx.x;
-  const uint32_t wg = blockIdx.x;
   const uint32_t c = wg / (kParts * kS);
   const uint32_t h = (wg / kS) % kParts;
   const uint32_t slice = wg % kS;
@@ -2753,11 +2755,10 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
     s_begin = begin;
     s_end = end;
     s_index = index;
-    if (wg == 0u) *n_err_slots = gridDim.x;
   }
   __syncthreads();
   if (!s_ok || nchunks == 0u) {
-    if (tid == 0) err_slots[wg] = s_ok ? 0u : uint32_t(CIERA_ERR_FORMAT);
+    if (tid == 0) *status = s_ok ? 0u : uint32_t(CIERA_ERR_FORMAT);
     return;
   }
   const uint32_t e0 = s_e0;
@@ -2792,13 +2793,13 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
   const uint32_t bitmap_fits = s_fits;
   const ChunkGeom g = chunk_geom(begin, nc, kCiera, nch, B);
   if (!bitmap_fits || g.esc > end) {
-    if (tid == 0) err_slots[wg] = uint32_t(CIERA_ERR_FORMAT);
+    if (tid == 0) *status = uint32_t(CIERA_ERR_FORMAT);
     return;
   }
   constexpr uint32_t kRange = kPartUnits / kS;  // units of the workgroup
   const uint32_t u0 = pu0 + slice * kRange;
   if (u0 >= nunits) {  // a range past the chunk's data
-    if (tid == 0) err_slots[wg] = 0u;
+    if (tid == 0) *status = 0u;
     return;
   }
   const uint32_t pb = uint32_t(g.plane_bytes);
@@ -2840,7 +2841,38 @@ __global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restri
     err = decode_part<kCiera, true, kS>(p, s_bits, s_rank, s_planes, s_esc, s_tot);
   else
     err = decode_part<kCiera, false, kS>(p, s_bits, s_rank, s_planes, s_esc, s_tot);
-  if (tid == 0) err_slots[wg] = err;
+  if (tid == 0) *status = err;
+}
+
+// One stream: workgroup b decodes its piece b.
+template <bool kCiera, uint32_t kS>
+__global__ __launch_bounds__(kPartThreads) void k_decode(const uint8_t* __restrict__ in, uint64_t in_size,
+                                                         uint16_t* __restrict__ y, uint64_t n, uint64_t nchunks,
+                                                         uint32_t log2B, uint8_t* __restrict__ cache,
+                                                         uint64_t* __restrict__ n_err_slots,
+                                                         uint32_t* __restrict__ err_slots) {
+  if (blockIdx.x == 0u && threadIdx.x == 0u) *n_err_slots = gridDim.x;
+  decode_workgroup<kCiera, kS>(in, in_size, y, n, nchunks, log2B, cache, blockIdx.x, err_slots + blockIdx.x);
+}
+
+// Several streams of the same n and B in one launch (a rank's received peer
+// shards): workgroup b decodes piece b % per of stream b / per, with that
+// stream's input, output and receiver cache, and status word b.
+struct DecodeStreams {
+  const uint8_t* in[kDecodeBatchMax];
+  uint64_t in_size[kDecodeBatchMax];
+  uint16_t* y[kDecodeBatchMax];
+  uint8_t* cache[kDecodeBatchMax];
+};
+template <bool kCiera, uint32_t kS>
+__global__ __launch_bounds__(kPartThreads) void k_decode_batch(DecodeStreams st, uint32_t per, uint64_t n,
+                                                               uint64_t nchunks, uint32_t log2B,
+                                                               uint64_t* __restrict__ n_err_slots,
+                                                               uint32_t* __restrict__ err_slots) {
+  const uint32_t i = blockIdx.x / per;  // uniform: the workgroup's stream
+  if (blockIdx.x == 0u && threadIdx.x == 0u) *n_err_slots = gridDim.x;
+  decode_workgroup<kCiera, kS>(st.in[i], st.in_size[i], st.y[i], n, nchunks, log2B, st.cache[i], blockIdx.x - i * per,
+                               err_slots + blockIdx.x);
 }
 
 // ------------------------------------------------------------------ rANS modes
@@ -3943,6 +3975,56 @@ ciera_status decode_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t
   return launch_status();
 }
 
+// Batch decode: k streams of one n and B in one launch of k_decode_batch,
+// each stream with the single decode's workgroups, their status words one
+// after the other after the control block.
+uint64_t decode_workgroups(uint64_t nchunks) {
+  return nchunks ? nchunks * kParts * (nchunks <= kSliceChunks ? kSlices : 1u) : 1u;
+}
+uint64_t decode_batch_ws_bytes(uint64_t nchunks, uint32_t k) {
+  return align256(sizeof(Ctrl) + 4u * uint64_t(k) * decode_workgroups(nchunks));
+}
+
+ciera_status decode_batch_impl(uint32_t k, const void* const* d_in, const uint64_t* in_size, void* const* d_y,
+                               uint64_t n, uint32_t B, uint8_t* const* d_cache, void* d_ws, uint64_t ws_bytes,
+                               hipStream_t stream) {
+  const bool ciera = B != 0u;
+  if (k == 0u || k > kDecodeBatchMax || !d_in || !in_size || !d_y) return CIERA_ERR_ARG;
+  if (n > kMaxN / k) return CIERA_ERR_ARG;
+  if (ciera && (!valid_block(B) || !d_cache)) return CIERA_ERR_ARG;
+  if (!d_ws || !aligned16(d_ws)) return CIERA_ERR_ARG;
+  DecodeStreams st;
+  memset(&st, 0, sizeof(st));
+  for (uint32_t i = 0; i < k; i++) {
+    if (!d_in[i] || !aligned16(d_in[i])) return CIERA_ERR_ARG;
+    if (n > 0 && (!d_y[i] || !aligned16(d_y[i]))) return CIERA_ERR_ARG;
+    if (ciera && n > 0 && (!d_cache[i] || !aligned16(d_cache[i]))) return CIERA_ERR_ARG;
+    st.in[i] = static_cast<const uint8_t*>(d_in[i]);
+    st.in_size[i] = in_size[i];
+    st.y[i] = static_cast<uint16_t*>(d_y[i]);
+    st.cache[i] = ciera ? d_cache[i] : nullptr;
+  }
+  const uint64_t nchunks = cdiv(n, kChunk);
+  if (ws_bytes < decode_batch_ws_bytes(nchunks, k)) return CIERA_ERR_WORKSPACE;
+  uint64_t* n_err_slots = &static_cast<Ctrl*>(d_ws)->n_err_slots;
+  uint32_t* err = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(d_ws) + sizeof(Ctrl));
+  const uint32_t per = uint32_t(decode_workgroups(nchunks));
+  const dim3 grid(k * per);
+  const bool sliced = nchunks <= kSliceChunks;
+  const uint32_t lb = ciera ? log2u(B) : 0u;
+  (void)hipGetLastError();
+  if (ciera && sliced)
+    launch(k_decode_batch<true, kSlices>, grid, dim3(kPartThreads), stream, st, per, n, nchunks, lb, n_err_slots, err);
+  else if (ciera)
+    launch(k_decode_batch<true, 1u>, grid, dim3(kPartThreads), stream, st, per, n, nchunks, lb, n_err_slots, err);
+  else if (sliced)
+    launch(k_decode_batch<false, kSlices>, grid, dim3(kPartThreads), stream, st, per, n, nchunks, lb, n_err_slots,
+           err);
+  else
+    launch(k_decode_batch<false, 1u>, grid, dim3(kPartThreads), stream, st, per, n, nchunks, lb, n_err_slots, err);
+  return launch_status();
+}
+
 // ------------------------------------------------------------------ no-allocation entry point
 // ciera_encode_noalloc runs ciera_encode's kernels on a workspace that lives
 // in this array instead of a caller's buffer.  Each GPU holds its own copy;
@@ -3987,6 +4069,22 @@ ciera_status ciera_encode_noalloc(const void* d_x, uint64_t n, uint32_t B, uint8
   const ciera_status st = scratch_on_current_device(&ws);
   if (st != CIERA_OK) return st;
   return encode_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, ws, kScratchBytes, d_out_size, -1, 0u, stream);
+}
+
+uint64_t decode_batch_workspace_size(uint64_t n, uint32_t k) {
+  return (k == 0u || k > kDecodeBatchMax || n > kMaxN / k) ? 0u : decode_batch_ws_bytes(cdiv(n, kChunk), k);
+}
+
+ciera_status zip3_decode_batch(uint32_t k, const void* const* d_in, const uint64_t* in_size, void* const* d_y,
+                               uint64_t n, void* d_ws, uint64_t ws_bytes, hipStream_t stream) {
+  return decode_batch_impl(k, d_in, in_size, d_y, n, 0u, nullptr, d_ws, ws_bytes, stream);
+}
+
+ciera_status ciera_decode_batch(uint32_t k, const void* const* d_in, const uint64_t* in_size, void* const* d_y,
+                                uint64_t n, uint32_t B, uint8_t* const* d_prev_exp, void* d_ws, uint64_t ws_bytes,
+                                hipStream_t stream) {
+  if (B == 0u) return CIERA_ERR_ARG;
+  return decode_batch_impl(k, d_in, in_size, d_y, n, B, d_prev_exp, d_ws, ws_bytes, stream);
 }
 
 uint64_t zip3_max_encoded_size(uint64_t n) { return n > kMaxN ? 0u : max_size(n, 0u); }

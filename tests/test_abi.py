@@ -98,6 +98,40 @@ def test_argument_errors_return_before_any_launch(lib):
     assert lib.ciera_time_kernels(None, 0) == 0
 
 
+def test_batch_decode_sizes_and_argument_errors(lib):
+    # one status word per workgroup of every stream after the 256-byte
+    # control block: a 2^20-value stream has 16 chunks x 4 parts x 4 slices
+    # workgroups, a 2^26-value one 1024 chunks x 4 parts
+    assert lib.decode_batch_workspace_size(1 << 20, 3) == 256 + 4 * 3 * 256
+    assert lib.decode_batch_workspace_size(1 << 26, 2) == 256 + 4 * 2 * 4096
+    assert lib.decode_batch_workspace_size(0, 1) == 512
+    assert lib.decode_batch_workspace_size(10, 0) == 0
+    assert lib.decode_batch_workspace_size(10, 17) == 0
+    assert lib.decode_batch_workspace_size(1 << 39, 3) == 0  # k n above 2^40
+    # every case fails a host-side check, so no HIP call is made
+    two = (ctypes.c_void_p * 2)(16 * 1024, 32 * 1024)
+    mis = (ctypes.c_void_p * 2)(16 * 1024, 32 * 1024 + 8)
+    nul = (ctypes.c_void_p * 2)(16 * 1024, None)
+    sizes = (ctypes.c_uint64 * 2)(1 << 20, 1 << 20)
+    p = ctypes.c_void_p(64 * 1024)
+    ws = 1 << 20
+    assert lib.zip3_decode_batch(0, two, sizes, two, 10, p, ws, None) == 1
+    assert lib.zip3_decode_batch(17, two, sizes, two, 10, p, ws, None) == 1
+    assert lib.zip3_decode_batch(2, None, sizes, two, 10, p, ws, None) == 1
+    assert lib.zip3_decode_batch(2, two, None, two, 10, p, ws, None) == 1
+    assert lib.zip3_decode_batch(2, mis, sizes, two, 10, p, ws, None) == 1
+    assert lib.zip3_decode_batch(2, two, sizes, mis, 10, p, ws, None) == 1
+    assert lib.zip3_decode_batch(2, two, sizes, nul, 10, p, ws, None) == 1
+    assert lib.zip3_decode_batch(2, two, sizes, two, 10, ctypes.c_void_p(64 * 1024 + 8), ws, None) == 1
+    assert lib.zip3_decode_batch(2, two, sizes, two, 1 << 40, p, 1 << 40, None) == 1
+    assert lib.zip3_decode_batch(2, two, sizes, two, 10, p, 16, None) == 3
+    assert lib.ciera_decode_batch(2, two, sizes, two, 10, 0, two, p, ws, None) == 1
+    assert lib.ciera_decode_batch(2, two, sizes, two, 10, 96, two, p, ws, None) == 1
+    assert lib.ciera_decode_batch(2, two, sizes, two, 10, 64, None, p, ws, None) == 1
+    assert lib.ciera_decode_batch(2, two, sizes, two, 10, 64, mis, p, ws, None) == 1
+    assert lib.ciera_decode_batch(2, two, sizes, two, 10, 64, two, p, 16, None) == 3
+
+
 def test_status_strings(lib):
     assert lib.ciera_status_string(0) == b"ok"
     assert lib.ciera_status_string(5) == b"malformed stream"
