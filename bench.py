@@ -519,6 +519,8 @@ def main() -> int:
     dec_iso, dec_iso_min = gpu.isolated(dec[k_iso], restore_r)
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
     iso_roundtrip = bool(torch.equal(y, xs[k_iso]))
+    batch = (measure_decode_batch(gpu, out, sizes[k_iso], n, B, e_prev, xs[k_iso], dec_iso)
+             if n <= BATCH_MAX_N else None)
     # The floor of this method: one launch of a one-element fill, timed the
     # same way (launch and event overhead, part of every isolated time).
     one = torch.zeros(1, device=gpu.dev)
@@ -813,6 +815,7 @@ def main() -> int:
         "kernels": kernels,
         "graph_replay": graph,
         "isolated": iso,
+        **({"decode_batch": batch} if batch is not None else {}),
         "hash_sender": hashed,
         "rans": rans,
         "single_read_encode": single,
@@ -823,8 +826,9 @@ def main() -> int:
         "source_hash": source_hash(),
     }
     print(json.dumps(line), flush=True)
-    bad = exact is False or not iso_roundtrip or any(not c["bit_exact_vs_oracle"] or not c["roundtrip_ok"]
-                                                    for c in configs)
+    batches = [b for b in [batch] + [c.get("decode_batch") for c in configs] if b is not None]
+    bad = (exact is False or not iso_roundtrip or any(not b["roundtrip_ok"] for b in batches)
+           or any(not c["bit_exact_vs_oracle"] or not c["roundtrip_ok"] for c in configs))
     if bad:
         log("FAILED: a GPU stream differs from the oracle's or a round trip failed")
         return 1
