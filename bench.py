@@ -59,6 +59,8 @@ ENC_KERNELS = ["k_stats", "k_sums", "k_plan", "k_write"]
 ENC_KERNELS_SMALL = ["k_stats", "k_write"]
 SELF_PLAN_CHUNKS = 16
 DEC_KERNELS = ["k_decode"]
+# the speculative encode's launches (tensors of more than SELF_PLAN_CHUNKS chunks)
+SPEC_KERNELS = ["k_prep1", "k_write1", "k_sums", "k_check", "k_stats", "k_plan", "k_write"]
 STREAMING = ["k_stats", "k_write", "k_decode"]
 
 
@@ -307,11 +309,30 @@ def measure_config(gpu, oracle, np, wl, workload, B_pick, threads):
         dec = ciera.bind("zip3_decode", out, sz, y, n, ws_d, wsz, stream=gpu.stream)
     else:
         dec = ciera.bind("ciera_decode", out, sz, y, n, B, recv, ws_d, wsz, stream=gpu.stream)
-    e_ms, e_min = gpu.isolated(enc, (lambda: send.copy_(pristine)) if send is not None else None)
+    restore_s = (lambda: send.copy_(pristine)) if send is not None else None
+    e_ms, e_min = gpu.isolated(enc, restore_s)
     d_ms, d_min = gpu.isolated(dec, (lambda: recv.copy_(pristine)) if recv is not None else None)
     assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
     roundtrip = bool(torch.equal(y, xd))
     batch = measure_decode_batch(gpu, out, sz, n, B, pristine, xd, d_ms) if n <= BATCH_MAX_N else None
+    spec = None
+    if -(-n // 65536) > SELF_PLAN_CHUNKS:
+        # the speculative encode hinted by this stream's window byte (a right
+        # hint), into its own buffer: its time and its stream against this one
+        out_s = torch.empty(cap, dtype=torch.uint8, device=dev)
+        size_s = torch.zeros(1, dtype=torch.int64, device=dev)
+        hint = out[7:8].clone()
+        if mode == "zip3":
+            enc_s = ciera.bind("zip3_encode_spec", xd, n, hint, out_s, cap, ws_e, wsz, size_s, stream=gpu.stream)
+        else:
+            enc_s = ciera.bind("ciera_encode_spec", xd, n, B, send, hint, out_s, cap, ws_e, wsz, size_s,
+                               stream=gpu.stream)
+        s_ms, s_min = gpu.isolated(enc_s, restore_s)
+        ok = ciera.ciera_read_error(ws_e) == 0 and int(size_s.item()) == sz and bool(torch.equal(out_s[:sz], out[:sz]))
+        spec = {"encode_ms": round(s_ms, 5), "encode_min_ms": round(s_min, 5),
+                "encode_GBps": round(2 * n / (s_ms * 1e-3) / 1e9, 1), "speedup_vs_two_pass": round(e_ms / s_ms, 3),
+                "stream_equal_to_full_encode": ok}
+        del out_s
     g_stream = out[:sz].cpu().numpy()
     o_stream, legs = oracle_legs(oracle, np, x, B, prev, threads)
     exact = g_stream.tobytes() == o_stream.tobytes()
@@ -334,6 +355,8 @@ def measure_config(gpu, oracle, np, wl, workload, B_pick, threads):
            "bit_exact_vs_oracle": exact, "roundtrip_ok": roundtrip, "oracle": legs}
     if batch is not None:
         res["decode_batch"] = batch
+    if spec is not None:
+        res["speculative_encode"] = spec
     del out, ws_e, ws_d, y, xd, send, recv, pristine
     torch.cuda.empty_cache()
     return res
@@ -562,6 +585,83 @@ def main() -> int:
     prep_ms = sum(ev1[s][0][0].elapsed_time(ev1[s][0][1]) for s in range(K)) / K
     write1_ms = sum(ev1[s][1][0].elapsed_time(ev1[s][1][1]) for s in range(K)) / K
     del out1, ws1
+
+    # Speculative encode (tensors of more than SELF_PLAN_CHUNKS chunks): the
+    # regular encode's stream and cache from one read of x when the hinted
+    # window base is the one the variance gives.  Timed like pass 3 with a
+    # right hint (byte 7 of the regular encode's stream of the same input) and
+    # with one a binade off (the fallback), each stream compared with the
+    # regular encode's; its kernels once more with events; then K steps back
+    # to back like pass 1, each encode hinted by the byte 7 that the previous
+    # step left in the output buffer it writes.
+    spec_leg = None
+    if -(-n // 65536) > SELF_PLAN_CHUNKS:
+        log("speculative encode")
+        out_s = torch.empty(cap, dtype=torch.uint8, device=dev)
+        size_s = torch.zeros(1, dtype=torch.int64, device=dev)
+        e0_right = int(out[7].item())
+        wrong = torch.tensor([e0_right + 1 if e0_right < 249 else e0_right - 1], dtype=torch.uint8, device=dev)
+
+        def spec_call(xk, hint, dst, sz_t):
+            if mode == "zip3":
+                return ciera.bind("zip3_encode_spec", xk, n, hint, dst, cap, ws_e, wsz, sz_t, stream=stream)
+            return ciera.bind("ciera_encode_spec", xk, n, B, send, hint, dst, cap, ws_e, wsz, sz_t, stream=stream)
+
+        def same_stream():
+            sz = int(size_s.item())
+            return sz == sizes[k_iso] and bool(torch.equal(out_s[:sz], out[:sz]))
+
+        right_call = spec_call(xs[k_iso], _Offset(out, 7), out_s, size_s)
+        sp_ms, sp_min = gpu.isolated(right_call, restore_s)
+        assert ciera.ciera_read_error(ws_e) == 0
+        sp_same = same_stream()
+        evs = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in SPEC_KERNELS] for _ in range(K)]
+        ciera.ciera_time_kernels([pr for row in evs for pr in row], stream=stream)
+        for _ in range(K):
+            if restore_s is not None:
+                restore_s()
+            torch.sum(gpu.sweep, dim=0, out=gpu.sweep_out)
+            right_call()
+        torch.cuda.synchronize()
+        ciera.ciera_time_kernels([])
+        sk = {nm: round(sum(evs[i][j][0].elapsed_time(evs[i][j][1]) for i in range(K)) / K, 5)
+              for j, nm in enumerate(SPEC_KERNELS)}
+        sw_ms, sw_min = gpu.isolated(spec_call(xs[k_iso], wrong, out_s, size_s), restore_s)
+        assert ciera.ciera_read_error(ws_e) == 0
+        sw_same = same_stream()
+        enc_sp = [spec_call(xs[k], _Offset(out, 7), out, size) for k in (0, 1)]
+        if send is not None:
+            send.copy_(e_prev)
+            recv.copy_(e_prev)
+
+        def step_spec(s_):
+            k = (s_ + 1) % 2 if mode != "zip3" else 0
+            enc_sp[k]()
+            dec[k]()
+
+        for w in range(2 * args.warmup):
+            step_spec(w)
+        torch.cuda.synchronize()
+        t_sp = time.perf_counter()
+        for s_ in range(K):
+            step_spec(s_)
+        torch.cuda.synchronize()
+        wall_sp = time.perf_counter() - t_sp
+        assert ciera.ciera_read_error(ws_e) == 0 and ciera.ciera_read_error(ws_d) == 0
+        klast = K % 2 if mode != "zip3" else 0  # input of the last step, index K-1
+        sp_roundtrip = bool(torch.equal(y, xs[klast]))
+        spec_leg = {"isolated_ms": round(sp_ms, 5), "isolated_min_ms": round(sp_min, 5),
+                "isolated_GBps": round(2 * n / (sp_ms * 1e-3) / 1e9, 2),
+                "speedup_vs_two_pass_isolated": round(enc_iso / sp_ms, 3),
+                "stream_equal_to_full_encode": sp_same,
+                "kernels": sk,
+                "wrong_hint_ms": round(sw_ms, 5), "wrong_hint_stream_equal_to_full_encode": sw_same,
+                "steps": K, "ms_per_step": round(wall_sp * 1e3 / K, 4),
+                "GBps": round(2 * n * K / wall_sp / 1e9, 2), "step_roundtrip_ok": sp_roundtrip,
+                "path": "k_prep1 + k_write1 with the variance sums, k_sums, k_check; k_stats, k_plan, k_write "
+                        "return at once on a right hint and encode again on a wrong one"}
+        del out_s
 
     # Hash sender (ciera workloads): the same encode with two 64-bit hashes
     # per block as the sender state.  Its starting cache (the hashes of the
@@ -819,6 +919,7 @@ def main() -> int:
         "hash_sender": hashed,
         "rans": rans,
         "single_read_encode": single,
+        "speculative_encode": spec_leg,
         "bw_measured_GBps": {"copy": round(bw_copy, 1), "read": round(bw_read, 1)},
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -827,7 +928,11 @@ def main() -> int:
     }
     print(json.dumps(line), flush=True)
     batches = [b for b in [batch] + [c.get("decode_batch") for c in configs] if b is not None]
-    bad = (exact is False or not iso_roundtrip or any(not b["roundtrip_ok"] for b in batches)
+    spec_bad = spec_leg is not None and not (spec_leg["stream_equal_to_full_encode"] and spec_leg["step_roundtrip_ok"]
+                                             and spec_leg["wrong_hint_stream_equal_to_full_encode"])
+    spec_bad = spec_bad or any(not c["speculative_encode"]["stream_equal_to_full_encode"]
+                               for c in configs if "speculative_encode" in c)
+    bad = (exact is False or not iso_roundtrip or spec_bad or any(not b["roundtrip_ok"] for b in batches)
            or any(not c["bit_exact_vs_oracle"] or not c["roundtrip_ok"] for c in configs))
     if bad:
         log("FAILED: a GPU stream differs from the oracle's or a round trip failed")

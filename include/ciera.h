@@ -301,6 +301,36 @@ ciera_status ciera_encode_e0(const void* d_x, uint64_t n, uint32_t B, uint8_t* d
                              void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
                              hipStream_t stream);
 
+/* zip3_encode_spec, ciera_encode_spec: zip3_encode / ciera_encode with the
+ * same stream, cache and *d_out_size for every input, but x (and the sender
+ * cache) read once when a hint names the right window base.  The window rule
+ * of the ZipCCL digest (section 3.1) takes E0 from the current tensor's
+ * sigma; sigma moves little from one training iteration to the next, so the
+ * previous iteration's E0 (byte 7 of its stream) is usually the same.  The
+ * call writes the stream in one pass with the hinted window while it adds
+ * the variance sums, then checks on the device that the variance gives that
+ * window; if not (or the hint is above 249, or a wait between workgroups did
+ * not end), it encodes again with the two-pass kernels, taking the changed
+ * blocks it recorded in the first pass (CIERA page, section 3.1), so the
+ * result is still ciera_encode's.
+ *   d_hint  in  device pointer to one byte, the hinted window base, read
+ *               when the encode runs (it may be the previous stream's byte 7
+ *               in the same output buffer)
+ * Other arguments, sizes, workspace (zip3/ciera_workspace_size) and errors
+ * as zip3_encode / ciera_encode.  A tensor of at most 16 chunks, or of more
+ * than 2^39 values, is encoded by zip3_encode / ciera_encode without the
+ * hint.  A right hint costs the single-read encode plus three small kernels
+ * and three launches that return at once; a wrong one the single-read pass
+ * plus the two-pass encode.  If a wait of the two-pass kernels then does not
+ * end either, the call ends as ciera_encode does after CIERA_ERR_INTERNAL
+ * (*d_out_size 0, the header's first word cleared; the sender cache holds
+ * x's exponents, so both caches are zeroed before the next iteration). */
+ciera_status zip3_encode_spec(const void* d_x, uint64_t n, const uint8_t* d_hint, void* d_out, uint64_t out_capacity,
+                              void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream);
+ciera_status ciera_encode_spec(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, const uint8_t* d_hint,
+                               void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                               hipStream_t stream);
+
 /* Kernel timing, a profiling aid (not part of the codec).  events holds
  * n_pairs (start, stop) pairs of hipEvent_t handles, created with timing
  * enabled and owned by the caller.  The next n_pairs kernel launches made by

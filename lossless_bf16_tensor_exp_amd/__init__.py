@@ -17,6 +17,8 @@ Same names as the C ABI::
     zip3_encode_e0(x, e0_src, out, ws, out_size, e0_offset=0, stream=None)
     ciera_encode(x, B, prev_exp, out, ws, out_size, e0_override=-1, stream=None, plan_groups=0)
     ciera_encode_e0(x, B, prev_exp, e0_src, out, ws, out_size, e0_offset=0, stream=None)
+    zip3_encode_spec(x, hint_src, out, ws, out_size, hint_offset=0, stream=None)   (one read of x if the hinted window is right)
+    ciera_encode_spec(x, B, prev_exp, hint_src, out, ws, out_size, hint_offset=0, stream=None)
     ciera_encode_hashed(x, B, hash_cache, out, ws, out_size, stream=None)
     ciera_hash_cache_size(n, B)
     zip3_encode_rans / zip3_decode_rans / ciera_encode_rans / ciera_decode_rans   (rANS-coded exponents)
@@ -48,6 +50,7 @@ __all__ = [
     "ciera_decode_rans",
     "bind", "ciera_time_kernels", "ciera_set_wait_limit", "ciera_encode_noalloc", "NOALLOC_MAX_N",
     "decode_batch_workspace_size", "zip3_decode_batch", "ciera_decode_batch", "DECODE_BATCH_MAX",
+    "zip3_encode_spec", "ciera_encode_spec",
     "CHUNK",
 ]
 
@@ -94,6 +97,8 @@ def load_library():
         "zip3_encode_ex": [vp, u64, vp, u64, vp, u64, vp, i32, u32, vp],
         "zip3_encode_e0": [vp, u64, vp, vp, u64, vp, u64, vp, vp],
         "ciera_encode_e0": [vp, u64, u32, vp, vp, vp, u64, vp, u64, vp, vp],
+        "zip3_encode_spec": [vp, u64, vp, vp, u64, vp, u64, vp, vp],
+        "ciera_encode_spec": [vp, u64, u32, vp, vp, vp, u64, vp, u64, vp, vp],
         "zip3_decode": [vp, u64, vp, u64, vp, u64, vp],
         "ciera_encode": [vp, u64, u32, vp, vp, u64, vp, u64, vp, vp],
         "ciera_encode_ex": [vp, u64, u32, vp, vp, u64, vp, u64, vp, i32, u32, vp],
@@ -260,6 +265,38 @@ def ciera_encode_e0(x, B: int, prev_exp, e0_src, out, ws, out_size, e0_offset: i
                              _ptr(out), out.numel(), _ptr(ws), ws.numel(), ctypes.c_void_p(out_size.data_ptr()),
                              _stream(stream))
     _raise(st, "ciera_encode_e0")
+
+
+def zip3_encode_spec(x, hint_src, out, ws, out_size, hint_offset: int = 0, stream=None) -> None:
+    """zip3_encode's stream, reading x once when the window base hinted by
+    byte ``hint_offset`` of the uint8 device tensor ``hint_src`` (e.g. byte 7
+    of the previous iteration's stream) is the one x's sigma gives."""
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(hint_src, "hint_src", hint_offset + 1)
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.zip3_encode_spec(_ptr(x), x.numel(), ctypes.c_void_p(hint_src.data_ptr() + hint_offset), _ptr(out),
+                              out.numel(), _ptr(ws), ws.numel(), ctypes.c_void_p(out_size.data_ptr()), _stream(stream))
+    _raise(st, "zip3_encode_spec")
+
+
+def ciera_encode_spec(x, B: int, prev_exp, hint_src, out, ws, out_size, hint_offset: int = 0, stream=None) -> None:
+    """ciera_encode's stream and cache update, reading x and the sender cache
+    once when the hinted window base (byte ``hint_offset`` of ``hint_src``)
+    is the one x's sigma gives."""
+    lib = load_library()
+    _check_values(x, "x")
+    _check_bytes(prev_exp, "prev_exp", x.numel())
+    _check_bytes(hint_src, "hint_src", hint_offset + 1)
+    _check_bytes(out, "out")
+    _check_bytes(ws, "ws")
+    _check_size_slot(out_size)
+    st = lib.ciera_encode_spec(_ptr(x), x.numel(), B, _ptr(prev_exp), ctypes.c_void_p(hint_src.data_ptr() + hint_offset),
+                               _ptr(out), out.numel(), _ptr(ws), ws.numel(), ctypes.c_void_p(out_size.data_ptr()),
+                               _stream(stream))
+    _raise(st, "ciera_encode_spec")
 
 
 def ciera_hash_cache_size(n: int, B: int) -> int:

@@ -29,7 +29,10 @@
 // escape index each part's first escape.  k_decode_batch runs the same
 // workgroups for several streams of one size in one launch.
 // The single-read encodes (window base given) are k_prep1 + k_write1; the
-// rANS modes k_stats + k_rans_enc + k_rans_finish, and k_rans_dec.
+// rANS modes k_stats + k_rans_enc + k_rans_finish, and k_rans_dec.  The
+// speculative encodes (window base hinted) run k_prep1 + k_write1 with the
+// variance sums, k_sums and k_check, then k_stats (recorded change bits),
+// k_plan and k_write, which return at once when the hint was right.
 //
 // Work mapping: a "unit" is 8 consecutive values (one 16-byte load).  A chunk
 // has 8192 units.  In k_stats, k_write and k_decode part h covers units
@@ -130,7 +133,9 @@ struct Ctrl {
   uint64_t n_err_slots;
   uint64_t done_esc;  // single-read encode: chunks finished << 40 | their escapes
   uint64_t done_nch;  // single-read ciera encode: the finished chunks' changed blocks
-  uint64_t reserved[28];
+  uint32_t spec;       // speculative encode: kSpecHit once k_check found the hinted window right
+  uint32_t spec_fail;  // speculative encode: set by a write workgroup that did not finish the stream
+  uint64_t reserved[27];
 };
 static_assert(sizeof(Ctrl) == 256, "control block is 256 bytes");
 
@@ -228,7 +233,9 @@ struct Ws {
   uint32_t spin_limit;  // polls before a wait gives up (kSpinLimit unless a test lowers it)
   uint32_t ss;          // k_stats records per part: 1, or kSlices (one per slice) for self-planned tensors
   const uint8_t* e0_src;  // self-planned encode with a known window base: its byte in device memory, else null
+  uint32_t spec;          // a speculative encode's fallback launch: do nothing if ctrl->spec == kSpecHit
 };
+constexpr uint32_t kSpecHit = 1u;
 
 // The bound the next calls pass to their kernels (ciera_set_wait_limit).
 std::atomic<uint32_t> g_wait_limit{kSpinLimit};
@@ -254,6 +261,7 @@ __host__ inline Ws ws_bind(void* base, uint64_t nchunks) {
   w.spin_limit = g_wait_limit.load(std::memory_order_relaxed);
   w.ss = 1u;
   w.e0_src = nullptr;
+  w.spec = 0u;
   return w;
 }
 
@@ -580,6 +588,33 @@ __device__ inline void stats_checked(const Unit& v, uint32_t cnt, double shift, 
   }
 }
 
+// One unit's share of the variance sums, its values in order: no finiteness
+// test for a full unit (a non-finite input makes the sums non-finite, and
+// the thread then redoes its units with stats_checked).  k_stats and the
+// speculative single-read write both add their units through this, so they
+// produce the same bits.
+__device__ inline void stats_unit(const Unit& v, uint32_t cnt, double shift, double& s1, double& s2, uint32_t& nf) {
+  if (cnt == 8u) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const double lo = widen_hi(v.w[i] << 16) - shift;
+      const double hi = widen_hi(v.w[i] & 0xFFFF0000u) - shift;
+      s1 += lo;
+      s2 = fma(lo, lo, s2);
+      s1 += hi;
+      s2 = fma(hi, hi, s2);
+    }
+    nf += 8u;
+  } else {
+    stats_checked(v, cnt, shift, s1, s2, nf);
+  }
+}
+
+// The shift of the variance sums: x[0], or 0 if x[0] is not finite.
+__device__ inline double stats_shift(uint32_t first) {
+  return (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
+}
+
 // Word t of a chunk's bitmap (bit j set = block j changed) from the words its
 // parts wrote (pw: kPartBitmapWords per part): part h keeps its own blocks'
 // bits from bit 0 of its first word, or, when a block spans several parts,
@@ -622,10 +657,17 @@ __device__ inline uint32_t stats_part_of(uint32_t b, uint32_t parts) {
 // sender cache and the cache update; an exponent histogram of the values to
 // code, and their count.  kHash: the sender cache is the block-hash cache
 // (two u64 per block) instead of the exponents.
-template <bool kCiera, bool kHash, uint32_t kS>
+// kGiven: the fallback pass of a speculative encode (ws.spec), which returns
+// at once if the speculation hit; else it takes each part's change bits from
+// the records the speculative write left (no cache read, compare or write),
+// and it clears only the planner slots' count words, keeping the variance
+// sums k_sums wrote there.
+template <bool kCiera, bool kHash, uint32_t kS, bool kGiven = false>
 __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restrict__ x, uint64_t n,
                                                         uint8_t* __restrict__ cache, uint32_t log2B, Ws ws) {
   static_assert(kCiera || !kHash, "the hash sender is a ciera mode");
+  static_assert(!kGiven || (!kHash && kS == 1u), "the speculative fallback is the exact sender's, one part each");
+  if (kGiven && ws.ctrl->spec == kSpecHit) return;
   constexpr uint32_t kU = kUPT / kS;            // units per thread
   constexpr uint32_t kRange = kPartUnits / kS;  // units per workgroup
   // hash sender: first the part's exponent words (2048 u64), then the histogram
@@ -651,12 +693,14 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   const uint32_t blk0 = kCiera ? ((8u * pu0) >> log2B) : 0u;  // first block of the part
   if (!kHash)
     for (uint32_t i = tid; i < kHistCopies * kBins; i += kPartThreads) s_hist[i] = 0u;
-  if (tid < kPartBitmapWords) s_bits[tid] = 0u;
+  if (tid < kPartBitmapWords) s_bits[tid] = (kGiven && kCiera) ? ws.bitmap[uint64_t(wg) * kPartBitmapWords + tid] : 0u;
   if (ws.rstat && tid == 0 && h == 0u && slice == 0u) ws.rstat[c * kRstatStride] = 0u;  // rANS encode: the chunk's look-back word, not ready
   if (blockIdx.x == 0u) {
-    // k_plan's slots: the count words not ready
+    // k_plan's slots: the count words not ready (words 3.. of each slot;
+    // the fallback keeps words 0..2, the sums)
     uint64_t* sw = reinterpret_cast<uint64_t*>(ws.plan);
-    for (uint32_t i = tid; i < kPlanMaxGroups * 8u; i += kPartThreads) sw[i] = 0u;
+    for (uint32_t i = tid; i < kPlanMaxGroups * 8u; i += kPartThreads)
+      if (!kGiven || (i & 7u) >= 3u) sw[i] = 0u;
     if (tid == 0) ws.ctrl->plan_fail = 0u;
   }
   // Hash sender, blocks within the part (a slice: within the slice): the hash
@@ -680,7 +724,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   if (full) {
 #pragma unroll
     for (uint32_t j = 0; j < kU; j++) v[j] = load_unit(x, start + 8ull * (u0 + j * kPartThreads + tid), 8u);
-    if (kCiera && !kHash) {
+    if (kCiera && !kHash && !kGiven) {
 #pragma unroll
       for (uint32_t j = 0; j < kU; j++)
         old[j] = *reinterpret_cast<const uint2*>(cache + start + 8ull * (u0 + j * kPartThreads + tid));
@@ -693,7 +737,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       old[j] = make_uint2(0u, 0u);
       if (u < nunits) {
         v[j] = load_unit(x, start + 8ull * u, min(8u, nc - 8u * u));
-        if (kCiera && !kHash) old[j] = load_bytes8(cache + start + 8ull * u, min(8u, nc - 8u * u));
+        if (kCiera && !kHash && !kGiven) old[j] = load_bytes8(cache + start + 8ull * u, min(8u, nc - 8u * u));
       }
     }
   }
@@ -702,7 +746,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
   // both on every path, so that they share the part's round trip
   const uint32_t first = x[0];
   const uint32_t e0_byte = *(ws.e0_src ? ws.e0_src : reinterpret_cast<const uint8_t*>(x));
-  const double shift = (((first >> 7) & 0xFFu) != 0xFFu) ? widen_hi(first << 16) : 0.0;
+  const double shift = stats_shift(first);
   // a window base given in device memory that is out of range: the encode
   // writes nothing, so the sender cache is left as it was
   const bool keep_cache = ws.e0_src != nullptr && e0_byte > kMaxE0;
@@ -733,21 +777,8 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       uint2 ue = make_uint2(0u, 0u);
       if (kF || u < nunits) {
         const uint32_t cnt = kF ? 8u : min(8u, nc - 8u * u);
-        if (cnt == 8u) {
-#pragma unroll
-          for (int i = 0; i < 4; i++) {
-            const double lo = widen_hi(v[j].w[i] << 16) - shift;
-            const double hi = widen_hi(v[j].w[i] & 0xFFFF0000u) - shift;
-            s1 += lo;
-            s2 = fma(lo, lo, s2);
-            s1 += hi;
-            s2 = fma(hi, hi, s2);
-          }
-          nf += 8u;
-        } else {
-          stats_checked(v[j], cnt, shift, s1, s2, nf);
-        }
-        if (kCiera) {
+        stats_unit(v[j], cnt, shift, s1, s2, nf);
+        if (kCiera && !kGiven) {
           const uint2 e = unit_exponents(v[j]);
           const uint64_t keep = (cnt == 8u) ? ~0ull : ((1ull << (8u * (cnt & 7u))) - 1u);
           if (kHash) {
@@ -762,7 +793,7 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       } else if (kHash) {
         reinterpret_cast<uint64_t*>(s_hist)[j * kPartThreads + tid] = 0u;  // past the data
       }
-      if (kCiera && !kHash) {
+      if (kCiera && !kHash && !kGiven) {
         const uint64_t m = __ballot(diff);
         if (m != 0u) {
           if (live && !keep_cache && line_has_change(m)) store_bytes8(cache + start + 8ull * u, ucnt, ue);
@@ -880,6 +911,17 @@ __global__ __launch_bounds__(kPartThreads) void k_stats(const uint16_t* __restri
       }
     }
     __syncthreads();  // histogram cleared
+  } else if (kCiera && kGiven) {
+    // the part's recorded bits (in s_bits since before the first barrier)
+    if (B > kPartValues) {
+      coded = 0xFFu;
+    } else {
+#pragma unroll
+      for (uint32_t j = 0; j < kU; j++) {
+        const uint32_t lb = ((8u * (u0 + j * kPartThreads + tid)) >> log2B) - blk0;
+        coded |= ((s_bits[lb >> 5] >> (lb & 31u)) & 1u) << j;
+      }
+    }
   } else if (kCiera && B > 512u) {
     // a block spans several waves: its bit is complete after the barrier.  A
     // part inside a block that spans several parts counts all of its values
@@ -1188,6 +1230,29 @@ __device__ inline uint64_t plan_chunk(uint64_t c, uint64_t n, uint32_t B, uint32
   return chunk_layout(nc, B, coded, pnch, inwin, esc, esc_total, nch_out);
 }
 
+// The window base from the G planner groups' variance sums (k_sums wrote
+// them), added in group order: every thread of every caller gets the same
+// bits, and so the same window base.
+__device__ inline uint32_t plan_e0(const PlanSlot* slot, uint32_t G, double* s_f, uint64_t* s_u) {
+  const uint32_t tid = threadIdx.x;
+  double ga = 0.0, gb = 0.0;
+  uint64_t gm = 0;
+  if (tid < G) {
+    ga = from_bits(slot[tid].s1);
+    gb = from_bits(slot[tid].s2);
+    gm = slot[tid].nf;
+  }
+  const double s1 = plan_sum_f64(ga, s_f);
+  const double s2 = plan_sum_f64(gb, s_f);
+  const uint64_t nf = plan_sum_u64(gm, s_u);
+  double var = 0.0;
+  if (nf >= 2u) {
+    var = (s2 - s1 * s1 / double(nf)) / double(nf - 1u);
+    if (!(var > 0.0)) var = 0.0;
+  }
+  return window_base(var, nf);
+}
+
 // The planner's groups: group g of G takes chunks [g per, (g + 1) per).
 // k_sums: each group adds up its parts' variance partials in a fixed order
 // and stores them in its slot.  Nothing waits; k_plan, the next launch,
@@ -1213,6 +1278,19 @@ __global__ __launch_bounds__(kPlanThreads) void k_sums(uint64_t nchunks, uint64_
     ws.plan[g].s2 = as_bits(b);
     ws.plan[g].nf = m;
   }
+}
+
+// Speculative encode: the window base from the variance, by k_plan's own
+// first step, against the hinted one the single-read write used (ctrl->e0).
+// One workgroup; ctrl->spec = kSpecHit when they agree and every write
+// workgroup finished, so that the fallback launches (k_stats with the
+// recorded change bits, k_plan, k_write) return at once.
+__global__ __launch_bounds__(kPlanThreads) void k_check(uint32_t G, Ws ws) {
+  __shared__ double s_f[kPlanWaves];
+  __shared__ uint64_t s_u[kPlanWaves];
+  const uint32_t e0 = plan_e0(ws.plan, G, s_f, s_u);
+  if (threadIdx.x == 0)
+    ws.ctrl->spec = (ws.ctrl->spec_fail == 0u && ws.ctrl->e0 == e0) ? kSpecHit : 0u;
 }
 
 // k_plan, the same groups: (1) every group adds the G groups' sums in group
@@ -1243,6 +1321,8 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
   uint64_t* hd = reinterpret_cast<uint64_t*>(out);
   uint64_t* table = reinterpret_cast<uint64_t*>(out + kHeader);
   const uint64_t base = table_end(nchunks);
+  // a speculative encode whose hinted window was right: nothing to plan
+  if (ws.spec && ws.ctrl->spec == kSpecHit) return;
   PlanSlot* slot = ws.plan;
   if (g == 0u) {
     if (tid == 0) ws.ctrl->n_err_slots = nchunks * kParts;
@@ -1251,23 +1331,9 @@ __global__ __launch_bounds__(kPlanThreads) void k_plan(uint64_t n, uint64_t nchu
   }
 
   // (1) the variance from every group's sums (k_sums wrote them)
-  double ga = 0.0, gb = 0.0;
-  uint64_t gm = 0;
-  if (tid < G) {
-    ga = from_bits(slot[tid].s1);
-    gb = from_bits(slot[tid].s2);
-    gm = slot[tid].nf;
-  }
-  const double s1 = plan_sum_f64(ga, s_f);
-  const double s2 = plan_sum_f64(gb, s_f);
-  const uint64_t nf = plan_sum_u64(gm, s_u);
+  const uint32_t e0_sigma = plan_e0(slot, G, s_f, s_u);
   if (tid == 0) {
-    double var = 0.0;
-    if (nf >= 2u) {
-      var = (s2 - s1 * s1 / double(nf)) / double(nf - 1u);
-      if (!(var > 0.0)) var = 0.0;
-    }
-    const uint32_t e0 = (e0_override >= 0) ? uint32_t(e0_override) : window_base(var, nf);
+    const uint32_t e0 = (e0_override >= 0) ? uint32_t(e0_override) : e0_sigma;
     s_e0 = e0;
     if (g == 0u) {
       ws.ctrl->e0 = e0;
@@ -1726,6 +1792,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write(const uint16_t* __restri
   const bool last_part = h + 1u == kParts;
   const bool final_slice = slice + 1u == kS;
   const uint32_t B = 1u << log2B;
+  if (ws.spec && ws.ctrl->spec == kSpecHit) return;  // a speculative encode that hit: the stream is written
   const uint64_t start = uint64_t(c) * kChunk;
   const uint32_t nc = uint32_t(min(uint64_t(kChunk), n - start));
   const uint32_t nunits = (nc + 7u) / 8u;
@@ -2089,6 +2156,8 @@ __global__ __launch_bounds__(kThreads) void k_prep1(uint64_t n, uint64_t nchunks
   if (tid == 0) {
     ws.ctrl->done_esc = 0u;
     ws.ctrl->done_nch = 0u;
+    ws.ctrl->spec = 0u;
+    ws.ctrl->spec_fail = 0u;
     ws.ctrl->e0 = ok ? e0 : kBadE0;
     ws.ctrl->n_err_slots = nchunks ? nchunks * kParts : 1u;
     if (nchunks == 0u) ws.err[0] = ok ? 0u : uint32_t(CIERA_ERR_ARG);
@@ -2168,7 +2237,13 @@ __device__ inline uint32_t single_part_of(uint32_t b, uint32_t nchunks) {
 // the sender cache, rewrites the units that differ, and codes only the
 // values of its changed blocks (a block that spans several parts: once the
 // chunk's words show some part of it changed).
-template <bool kCiera>
+// kSigma: the speculative encode's write, with the window base a hint (e.g.
+// the previous iteration's): the part also adds its variance sums exactly as
+// k_stats does and leaves k_stats' records (sums, change bits), so that
+// k_sums and k_check can tell whether the hint is the window the variance
+// gives, and the fallback launches can redo the encode if not; with an
+// out-of-range hint it writes only those records and the cache.
+template <bool kCiera, bool kSigma = false>
 __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restrict__ x, uint64_t n, uint64_t nchunks,
                                                          uint32_t log2B, uint8_t* __restrict__ cache,
                                                          uint8_t* __restrict__ out, uint64_t* __restrict__ out_size,
@@ -2179,6 +2254,8 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   __shared__ uint32_t s_pbits[kPartBitmapWords];  // ciera: the part's block bits (B > 16384: bit 0, its share)
   __shared__ uint64_t s_begin;
   __shared__ uint32_t s_before, s_slot0, s_nch, s_coded, s_err;
+  __shared__ double s_vs1[kSigma ? kPartWaves : 1u], s_vs2[kSigma ? kPartWaves : 1u];
+  __shared__ uint32_t s_vnf[kSigma ? kPartWaves : 1u];
   const uint32_t tid = threadIdx.x;
   const uint32_t lane = lane_id(), wave = tid >> 6;
   // Workgroups are dealt round-robin over the chip's 8 XCDs; the four parts of
@@ -2194,7 +2271,7 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   const uint32_t pu0 = h * kPartUnits;
   const uint32_t B = kCiera ? (1u << log2B) : 0u;
   const uint32_t e0 = ws.ctrl->e0;
-  if (e0 == kBadE0) {  // the same for every workgroup: none waits on another
+  if (!kSigma && e0 == kBadE0) {  // the same for every workgroup: none waits on another
     if (tid == 0) ws.err[wg] = uint32_t(CIERA_ERR_ARG);
     return;
   }
@@ -2223,13 +2300,34 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
       }
     }
   }
+  // kSigma: the variance sums' shift, read after the part's loads are out
+  const double shift = kSigma ? stats_shift(x[0]) : 0.0;
   // From here on a unit lives as its exponent bytes and its sign+mantissa
   // bytes (half the registers of the loaded words, held until the stores).
+  // kSigma: each unit first adds to the variance sums, as in k_stats.
   uint2 ex[kUPT], smb[kUPT];
+  double s1 = 0.0, s2 = 0.0;
+  uint32_t nf = 0;
 #pragma unroll
   for (uint32_t j = 0; j < kUPT; j++) {
+    if (kSigma) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
+      if (full || u < nunits) stats_unit(v[j], full ? 8u : min(8u, nc - 8u * u), shift, s1, s2, nf);
+    }
     ex[j] = unit_exponents(v[j]);
     smb[j] = unit_sm(v[j]);
+  }
+  if (kSigma && !(__builtin_isfinite(s1) && __builtin_isfinite(s2))) {
+    // a non-finite value: the units again with the finiteness test, the
+    // values rebuilt from their bytes
+    s1 = 0.0;
+    s2 = 0.0;
+    nf = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kUPT; j++) {
+      const uint32_t u = pu0 + j * kPartThreads + tid;
+      if (u < nunits) stats_checked(unit_join(smb[j], ex[j]), min(8u, nc - 8u * u), shift, s1, s2, nf);
+    }
   }
   const uint32_t bias = ((1u - e0) & 0xFFFFu) * 0x00010001u;
   for (uint32_t i = tid; i < 3u * kStage / 16u; i += kPartThreads)
@@ -2268,6 +2366,45 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
       }
     }
     __syncthreads();  // s_pbits complete
+  }
+  if (kSigma) {
+    // the part's records in k_stats' form: variance sums (waves in order)
+    // and change bits
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    nf = wave_sum_u32(nf);
+    if (lane == 0u) {
+      s_vs1[wave] = s1;
+      s_vs2[wave] = s2;
+      s_vnf[wave] = nf;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double a = 0.0, bsum = 0.0;
+      uint32_t m = 0;
+#pragma unroll
+      for (uint32_t w = 0; w < kPartWaves; w++) {
+        a += s_vs1[w];
+        bsum += s_vs2[w];
+        m += s_vnf[w];
+      }
+      Partial p;
+      p.s1 = a;
+      p.s2 = bsum;
+      p.nf = m;
+      p.nch = 0u;
+      p.coded = 0u;
+      p.pad = 0u;
+      ws.partial[wg] = p;
+    }
+    if (kCiera && tid < kPartBitmapWords) ws.bitmap[uint64_t(wg) * kPartBitmapWords + tid] = s_pbits[tid];
+    if (e0 == kBadE0) {  // the same for every workgroup: the fallback writes the stream
+      if (tid == 0) {
+        ws.err[wg] = 0u;
+        ws.ctrl->spec_fail = 1u;
+      }
+      return;
+    }
   }
   // the part's changed blocks; lane k < kPartBitmapWords holds those before
   // bitmap word k
@@ -2413,7 +2550,10 @@ __global__ __launch_bounds__(kPartThreads) void k_write1(const uint16_t* __restr
   }
   __syncthreads();
   if (s_err) {
-    if (tid == 0) ws.err[wg] = s_err;
+    if (tid == 0) {
+      ws.err[wg] = s_err;
+      if (kSigma) ws.ctrl->spec_fail = 1u;  // the fallback redoes the encode
+    }
     return;
   }
   const uint64_t begin = s_begin;
@@ -3975,6 +4115,64 @@ ciera_status decode_impl(const void* d_in, uint64_t in_size, void* d_y, uint64_t
   return launch_status();
 }
 
+// Speculative encode: the single-read write with a hinted window base that
+// also keeps k_stats' records, then k_sums and k_check (the window the
+// variance gives, against the hint), then the two-pass encode's k_stats (with
+// the recorded change bits), k_plan and k_write, which return at once when
+// the hint was right.  Either way the stream, the cache and *d_out_size are
+// those of the regular encode.  Tensors of at most kSelfPlanChunks chunks, or
+// above the single-read limit, take the regular encode.
+ciera_status encode_spec_impl(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_cache, const uint8_t* d_hint,
+                              void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                              hipStream_t stream) {
+  const bool ciera = B != 0u;
+  if (!d_hint) return CIERA_ERR_ARG;
+  const uint64_t nchunks = cdiv(n, kChunk);
+  if (nchunks <= kSelfPlanChunks || n > kMaxSingleReadN)
+    return encode_impl(d_x, n, B, d_cache, d_out, out_capacity, d_ws, ws_bytes, d_out_size, -1, 0u, stream);
+  if (ciera && !valid_block(B)) return CIERA_ERR_ARG;
+  if (!d_out || !d_ws || !d_out_size || !aligned16(d_out) || !aligned16(d_ws)) return CIERA_ERR_ARG;
+  if ((reinterpret_cast<uintptr_t>(d_out_size) & 7u) != 0u) return CIERA_ERR_ARG;
+  if (!d_x || !aligned16(d_x)) return CIERA_ERR_ARG;
+  if (ciera && (!d_cache || !aligned16(d_cache))) return CIERA_ERR_ARG;
+  if (out_capacity < max_size(n, B)) return CIERA_ERR_CAPACITY;
+  if (ws_bytes < ws_layout(nchunks).total) return CIERA_ERR_WORKSPACE;
+  const Ws ws = ws_bind(d_ws, nchunks);
+  Ws wsf = ws;
+  wsf.spec = 1u;  // the fallback launches
+  const uint16_t* x = static_cast<const uint16_t*>(d_x);
+  uint8_t* out = static_cast<uint8_t*>(d_out);
+  const uint32_t lb = ciera ? log2u(B) : 0u;
+  const dim3 grid(uint32_t(nchunks * kParts));
+  uint64_t per = 0;
+  uint32_t groups = 0;
+  plan_shape(nchunks, 0u, per, groups);
+  (void)hipGetLastError();
+  const uint64_t prep_groups = cdiv(nchunks * kParts, kThreads);
+  launch(k_prep1, dim3(uint32_t(prep_groups > 1024u ? 1024u : prep_groups)), dim3(kThreads), stream, n, nchunks, B,
+         d_hint, out, d_out_size, ws);
+  if (ciera)
+    launch(k_write1<true, true>, grid, dim3(kPartThreads), stream, x, n, nchunks, lb, d_cache, out, d_out_size, ws);
+  else
+    launch(k_write1<false, true>, grid, dim3(kPartThreads), stream, x, n, nchunks, 0u, nullptr, out, d_out_size, ws);
+  launch(k_sums, dim3(groups), dim3(kPlanThreads), stream, nchunks, per, ws);
+  launch(k_check, dim3(1), dim3(kPlanThreads), stream, groups, ws);
+  if (ciera) {
+    launch(k_stats<true, false, 1u, true>, grid, dim3(kPartThreads), stream, x, n, d_cache, lb, wsf);
+    launch(k_plan<false>, dim3(groups), dim3(kPlanThreads), stream, n, nchunks, per, B, -1, out, d_out_size, nullptr,
+           wsf);
+    launch(k_write<true, false, 1u>, grid, dim3(kPartThreads), stream, x, n, lb, out, out_capacity, d_out_size, -1,
+           wsf);
+  } else {
+    launch(k_stats<false, false, 1u, true>, grid, dim3(kPartThreads), stream, x, n, nullptr, 0u, wsf);
+    launch(k_plan<false>, dim3(groups), dim3(kPlanThreads), stream, n, nchunks, per, 0u, -1, out, d_out_size, nullptr,
+           wsf);
+    launch(k_write<false, false, 1u>, grid, dim3(kPartThreads), stream, x, n, 0u, out, out_capacity, d_out_size, -1,
+           wsf);
+  }
+  return launch_status();
+}
+
 // Batch decode: k streams of one n and B in one launch of k_decode_batch,
 // each stream with the single decode's workgroups, their status words one
 // after the other after the control block.
@@ -4069,6 +4267,19 @@ ciera_status ciera_encode_noalloc(const void* d_x, uint64_t n, uint32_t B, uint8
   const ciera_status st = scratch_on_current_device(&ws);
   if (st != CIERA_OK) return st;
   return encode_impl(d_x, n, B, d_prev_exp, d_out, out_capacity, ws, kScratchBytes, d_out_size, -1, 0u, stream);
+}
+
+ciera_status zip3_encode_spec(const void* d_x, uint64_t n, const uint8_t* d_hint, void* d_out, uint64_t out_capacity,
+                              void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size, hipStream_t stream) {
+  if (n > kMaxN) return CIERA_ERR_ARG;
+  return encode_spec_impl(d_x, n, 0u, nullptr, d_hint, d_out, out_capacity, d_ws, ws_bytes, d_out_size, stream);
+}
+
+ciera_status ciera_encode_spec(const void* d_x, uint64_t n, uint32_t B, uint8_t* d_prev_exp, const uint8_t* d_hint,
+                               void* d_out, uint64_t out_capacity, void* d_ws, uint64_t ws_bytes, uint64_t* d_out_size,
+                               hipStream_t stream) {
+  if (B == 0u || n > kMaxN) return CIERA_ERR_ARG;
+  return encode_spec_impl(d_x, n, B, d_prev_exp, d_hint, d_out, out_capacity, d_ws, ws_bytes, d_out_size, stream);
 }
 
 uint64_t decode_batch_workspace_size(uint64_t n, uint32_t k) {
