@@ -1,7 +1,8 @@
 """Calls on two HIP streams at once, each with its own workspace and
 buffers: every encode of a batch is enqueued before any finishes (3-bit
-two-pass, single-read, hash sender and rANS encodes, whose kernels wait on
-other workgroups of their own launch), then every decode.  Each stream
+two-pass, single-read, speculative (right and wrong hint), hash sender and
+rANS encodes, whose kernels wait on other workgroups of their own launch),
+then every decode.  Each stream
 and each decoded tensor must equal what the same call gives alone on the
 default stream; those single calls are checked against the oracle by the
 other GPU tests."""
@@ -56,12 +57,15 @@ class Job:
             # the hashes of x0's exponents, from one hashed encode of x0
             x0d = torch.from_numpy(x0.view(np.int16)).to(dev)
             ciera.ciera_encode_hashed(x0d, B, self.hcache, self.out, self.ws, self.size)
-        if kind == "single":
-            # the window base from a full encode of the same tensor
+        if kind == "single" or kind.startswith("spec"):
+            # the window base from a full encode of the same tensor (a wrong
+            # hint for "spec_miss": one binade up)
             self.e0 = torch.zeros(16, dtype=torch.uint8, device=dev)
             ciera.zip3_encode(self.x, self.out, self.ws, self.size)
             torch.cuda.synchronize()
             self.e0.copy_(self.out[:16])
+            if kind == "spec_miss":
+                self.e0[7] += 1
         torch.cuda.synchronize()
         self.hcache0 = self.hcache.clone() if kind == "hashed" else None
 
@@ -80,6 +84,11 @@ class Job:
             ciera.zip3_encode_e0(self.x, self.e0, self.out, self.ws, self.size, e0_offset=7, stream=stream)
         elif k == "hashed":
             ciera.ciera_encode_hashed(self.x, B, self.hcache, self.out, self.ws, self.size, stream=stream)
+        elif k == "spec" and B:
+            ciera.ciera_encode_spec(self.x, B, self.send, self.e0, self.out, self.ws, self.size, hint_offset=7,
+                                    stream=stream)
+        elif k in ("spec", "spec_miss"):
+            ciera.zip3_encode_spec(self.x, self.e0, self.out, self.ws, self.size, hint_offset=7, stream=stream)
         elif k == "rans_zip3":
             ciera.zip3_encode_rans(self.x, self.out, self.ws, self.size, stream=stream)
         elif k == "rans_ciera":
@@ -87,9 +96,9 @@ class Job:
 
     def decode(self, stream, sz):
         k, B = self.kind, self.B
-        if k in ("zip3", "single"):
+        if k in ("zip3", "single", "spec_miss") or (k == "spec" and not B):
             ciera.zip3_decode(self.out, sz, self.y, self.dws, stream=stream)
-        elif k in ("ciera", "hashed"):
+        elif k in ("ciera", "hashed", "spec"):
             ciera.ciera_decode(self.out, sz, self.y, B, self.recv, self.dws, stream=stream)
         elif k == "rans_zip3":
             ciera.zip3_decode_rans(self.out, sz, self.y, self.dws, stream=stream)
@@ -98,7 +107,7 @@ class Job:
 
 
 KINDS = [("zip3", 0), ("ciera", 64), ("single", 0), ("hashed", 256), ("rans_zip3", 0), ("rans_ciera", 128),
-         ("ciera", 1024), ("zip3", 0)]
+         ("ciera", 1024), ("zip3", 0), ("spec", 256), ("spec_miss", 0)]
 
 
 def test_two_streams_overlapping_calls():
