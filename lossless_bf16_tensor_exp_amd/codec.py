@@ -8,9 +8,9 @@ from __future__ import annotations
 
 import torch
 
-from . import (CieraError, ciera_decode, ciera_encode, ciera_encode_e0, ciera_max_encoded_size, ciera_read_error,
-               ciera_workspace_size, zip3_decode, zip3_encode, zip3_encode_e0, zip3_max_encoded_size,
-               zip3_workspace_size)
+from . import (CieraError, ciera_decode, ciera_encode, ciera_encode_e0, ciera_encode_spec, ciera_max_encoded_size,
+               ciera_read_error, ciera_workspace_size, zip3_decode, zip3_encode, zip3_encode_e0, zip3_encode_spec,
+               zip3_max_encoded_size, zip3_workspace_size)
 
 
 class Zip3Codec:
@@ -31,6 +31,12 @@ class Zip3Codec:
         ``out`` (its header byte 7, read on the device before it is
         rewritten); the previous call must have been an encode."""
         zip3_encode_e0(x, self.out, self.out, self.ws, self.size, 7, stream)
+
+    def encode_spec(self, x, stream=None):
+        """``encode``'s stream, with x read once when the previous stream's
+        window base (its header byte 7 in ``out``) is still the one x's sigma
+        gives; the previous call must have been an encode."""
+        zip3_encode_spec(x, self.out, self.out, self.ws, self.size, 7, stream)
 
     def decode(self, stream_bytes, in_size: int, y, stream=None):
         zip3_decode(stream_bytes, in_size, y, self.ws, stream)
@@ -67,6 +73,13 @@ class CieraCodec:
         read on the device before it is rewritten); the previous call must
         have been an encode."""
         ciera_encode_e0(x, self.B, self.send_cache, self.out, self.out, self.ws, self.size, 7, stream)
+
+    def encode_spec(self, x, stream=None):
+        """``encode``'s stream and cache update, with x and the sender cache
+        read once when the previous stream's window base (its header byte 7
+        in ``out``) is still the one x's sigma gives; the previous call must
+        have been an encode."""
+        ciera_encode_spec(x, self.B, self.send_cache, self.out, self.out, self.ws, self.size, 7, stream)
 
     def decode(self, stream_bytes, in_size: int, y, stream=None):
         ciera_decode(stream_bytes, in_size, y, self.B, self.recv_cache, self.ws_dec, stream)

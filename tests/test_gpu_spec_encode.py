@@ -191,3 +191,39 @@ def test_spec_encode_after_waits_that_give_up(B):
     got = out[:int(size.item())].cpu().numpy()
     assert got.tobytes() == want.tobytes()
     check_roundtrip(got, x, B, zero.copy() if B else None)
+
+
+def test_codec_encode_spec_equals_encode():
+    """Codec objects: after a full encode, encode_spec takes its hint from
+    byte 7 of the previous stream in the same output buffer and writes what
+    the oracle (and so encode) writes, over iterations whose window stays and
+    one whose window moves."""
+    from lossless_bf16_tensor_exp_amd.codec import CieraCodec, Zip3Codec
+    rng = np.random.default_rng(45)
+    n = 3 * 65536 + 999
+    xs = [wl.f32_to_bf16(rng.standard_normal(n, dtype=np.float32) * np.float32(0.02))]
+    for scale in (1.0, 1.0, 16.0):  # the last step moves the window
+        x = wl.f32_to_bf16(wl.bf16_to_f32(xs[-1]) * np.float32(scale))
+        wl.flip(x, rng.choice(n, size=3000, replace=False))
+        xs.append(x)
+    dev = [torch.from_numpy(x.view(np.int16)).cuda() for x in xs]
+    say(f"codec encode_spec n={n}")
+    z = Zip3Codec(n)
+    z.encode(dev[0])
+    for x, d in zip(xs[1:], dev[1:]):
+        z.encode_spec(d)
+        torch.cuda.synchronize()
+        assert z.error() == 0
+        o, _ = oracle.encode(x, 0, None)
+        assert z.out[:z.nbytes()].cpu().numpy().tobytes() == o.tobytes()
+    c = CieraCodec(n, 256)
+    cache = np.zeros(n, np.uint8)
+    c.encode(dev[0])
+    oracle.encode(xs[0], 256, cache)
+    for x, d in zip(xs[1:], dev[1:]):
+        c.encode_spec(d)
+        torch.cuda.synchronize()
+        assert c.error() == 0
+        o, _ = oracle.encode(x, 256, cache)
+        assert c.out[:c.nbytes()].cpu().numpy().tobytes() == o.tobytes()
+        assert np.array_equal(c.send_cache[:n].cpu().numpy(), cache)
