@@ -630,7 +630,15 @@ def main() -> int:
         sw_ms, sw_min = gpu.isolated(spec_call(xs[k_iso], wrong, out_s, size_s), restore_s)
         assert ciera.ciera_read_error(ws_e) == 0
         sw_same = same_stream()
-        enc_sp = [spec_call(xs[k], _Offset(out, 7), out, size) for k in (0, 1)]
+        # the steps write out_s (which now holds the regular encode's stream
+        # of xs[k_iso], so its byte 7 is a right first hint) and decode it;
+        # out keeps that stream for the hash sender's comparison below
+        enc_sp = [spec_call(xs[k], _Offset(out_s, 7), out_s, size_s) for k in (0, 1)]
+        if mode == "zip3":
+            dec_sp = {k: ciera.bind("zip3_decode", out_s, sizes[k], y, n, ws_d, wsz, stream=stream) for k in sizes}
+        else:
+            dec_sp = {k: ciera.bind("ciera_decode", out_s, sizes[k], y, n, B, recv, ws_d, wsz, stream=stream)
+                      for k in sizes}
         if send is not None:
             send.copy_(e_prev)
             recv.copy_(e_prev)
@@ -638,7 +646,7 @@ def main() -> int:
         def step_spec(s_):
             k = (s_ + 1) % 2 if mode != "zip3" else 0
             enc_sp[k]()
-            dec[k]()
+            dec_sp[k]()
 
         for w in range(2 * args.warmup):
             step_spec(w)
@@ -661,7 +669,7 @@ def main() -> int:
                 "GBps": round(2 * n * K / wall_sp / 1e9, 2), "step_roundtrip_ok": sp_roundtrip,
                 "path": "k_prep1 + k_write1 with the variance sums, k_sums, k_check; k_stats, k_plan, k_write "
                         "return at once on a right hint and encode again on a wrong one"}
-        del out_s
+        del out_s, enc_sp, dec_sp
 
     # Hash sender (ciera workloads): the same encode with two 64-bit hashes
     # per block as the sender state.  Its starting cache (the hashes of the
@@ -932,10 +940,14 @@ def main() -> int:
                                              and spec_leg["wrong_hint_stream_equal_to_full_encode"])
     spec_bad = spec_bad or any(not c["speculative_encode"]["stream_equal_to_full_encode"]
                                for c in configs if "speculative_encode" in c)
-    bad = (exact is False or not iso_roundtrip or spec_bad or any(not b["roundtrip_ok"] for b in batches)
+    # the other modes' streams: the hash sender's equals the exact sender's,
+    # the single-read encode's the full encode's, the rANS round trip holds
+    modes_bad = ((hashed is not None and not hashed["stream_equal_to_exact_sender"])
+                 or not sr_same or not rans["roundtrip_ok"])
+    bad = (exact is False or not iso_roundtrip or spec_bad or modes_bad or any(not b["roundtrip_ok"] for b in batches)
            or any(not c["bit_exact_vs_oracle"] or not c["roundtrip_ok"] for c in configs))
     if bad:
-        log("FAILED: a GPU stream differs from the oracle's or a round trip failed")
+        log("FAILED: a GPU stream differs from the oracle's or from the regular encode's, or a round trip failed")
         return 1
     return 0
 
