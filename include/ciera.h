@@ -338,8 +338,10 @@ ciera_status ciera_encode_spec(const void* d_x, uint64_t n, uint32_t B, uint8_t*
  * 3-bit encode launches four kernels, or two for a tensor of at most 16
  * chunks, whose planning the write kernel does itself, unless plan_groups
  * forces the planner; its decode one; the single-read encode two; the rANS
- * encode three and its decode one) each take the next pair, which the HIP
- * runtime records at that kernel's start and end (hipExtLaunchKernel);
+ * encode three and its decode one; the speculative encode seven on a tensor
+ * of more than 16 chunks, whatever the hint; the batch decode one) each take
+ * the next pair, which the HIP runtime records at that kernel's start and end
+ * (hipExtLaunchKernel);
  * hipEventElapsedTime then gives the kernel's own duration.  The handles are
  * copied; a later call replaces the queue, n_pairs = 0 clears it.  Returns
  * CIERA_ERR_ARG for a null array or handle. */
